@@ -1,0 +1,245 @@
+"""Float64 CPU oracle for the STCA forward hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: it is used by ``tests/``, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of ``bench.py``.  It shares no code, table or
+constant with the HIP implementation; both sides only consume the seeded
+arrays drawn by ``recsys_ultra_long_amd.inputs``.
+
+What it computes is the plain definition of the method, evaluated in float64
+per user and per target, with a two-pass softmax (max, then exp-sum) and no
+splitting, blocking or online rescaling.  Page citations use these short
+names for the pages this work is built from:
+
+* [WeChat]   "视频号推荐超长序列技术演进：从端到端到 Cross-Mask Transformer"
+* [Notes]    "超长序列建模 —— STCA 精读笔记" (STCA reading notes)
+* [Review]   "Make It Long, Keep It Fast: End-to-End 10K Long User Behavior
+             Sequence Modeling for Billion-Scale Douyin Recommendation"
+             (paper review)
+* [HyFormer] "HyFormer：重新审视序列建模和特征交互在 CTR 预测中的作用"
+             (translation)
+
+Readings taken where the pages are silent (each one is listed in the design doc):
+
+* SwiGLU(x) = (SiLU(x W1) * (x W3)) W2 with SiLU(u) = u * sigmoid(u), no
+  biases ([Notes] §STCA and [Review] §四 name the block but never define it).
+* LN is LayerNorm over the model width, biased variance, eps = 1e-5, with a
+  gain and a bias.
+* History side, layer i: K = LN(SwiGLU_i(X)) W_K, V = LN(SwiGLU_i(X)) W_V, with
+  X the raw embedding rows for every layer ([Notes] §STCA, layers i > 1).
+  HyFormer mode drops the LN ([HyFormer] eq. (7), (8)).
+* First query q1 = LN(SwiGLU_q1(x_t)) ([Notes] §STCA, first layer).
+* Heads are column slices of width d_h of one d x d matrix; the score scale is
+  1/sqrt(d_h) ([Review] architecture tree; the formula for alpha).
+* Fusion: q_{i+1} = LN(SwiGLU_{i+1}([o_1 | ... | o_i | x_t] W_C^{i+1})) with
+  o_k the post-W_O layer outputs ([Review] 核心公式, inter-layer fusion).
+* Final: z = SwiGLU_Z([o_1 | ... | o_M | x_t] W_Z) ([Review] architecture
+  tree), optionally followed by LN (the [Notes] wording: z is the last
+  updated query).
+* ReLU-scored variant: w_j = max(0, s_j), o = sum_j w_j v_j, and the active
+  count is #{j : s_j > 0} ([WeChat] §1.2: a key is active when its score is
+  above zero).
+* Empty history: attention output 0, active count 0.
+* HyFormer linear mode: Q_{l+1} = O_l R_l, output O_M ([HyFormer] eq. (9),
+  (16), with the boosting block replaced by a fixed linear map).
+
+Parity pins: every function below is pinned by a closed form, an invariant,
+a brute-force enumeration or an independent library routine in
+``tests/test_oracle_pins.py``.  The absolute values of a whole multi-layer
+forward (fusion chain, z) have no external anchor: they are pinned only
+compositionally (parity unpinned as a whole; each step is pinned).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+LN_EPS = 1e-5
+
+
+def stored_to_f64(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    """Stored values -> float64, exactly.  uint16 arrays hold raw bf16 bits."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        bits = a.astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- blocks
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(u) = u * sigmoid(u) (the gate of the SwiGLU FFN)."""
+    return x / (1.0 + np.exp(-x))
+
+
+def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = LN_EPS) -> np.ndarray:
+    """LayerNorm over the last axis: biased variance, gain g, bias b."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def swiglu(x: np.ndarray, w: dict) -> np.ndarray:
+    """Dimension-preserving SwiGLU FFN: (SiLU(x W1) * (x W3)) W2."""
+    return (silu(x @ w["w1"]) * (x @ w["w3"])) @ w["w2"]
+
+
+def ffn_ln(x: np.ndarray, w: dict, ln: bool) -> np.ndarray:
+    y = swiglu(x, w)
+    return layer_norm(y, w["ln_g"], w["ln_b"]) if ln else y
+
+
+# ---------------------------------------------------------------- attention
+def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
+                     scale: Optional[float] = None):
+    """One target (query row ``Q`` of width d, already multiplied by W_Q)
+    against one user's keys K and values V ([L, d] each).
+
+    Per head eta (columns eta*d_h .. (eta+1)*d_h):
+      s_j   = Q_eta . K_{j,eta} / sqrt(d_h)
+      softmax: a_eta = sum_j exp(s_j - max s) V_{j,eta} / sum_j exp(s_j - max s)
+      relu:    a_eta = sum_j max(0, s_j) V_{j,eta};  cnt_eta = #{j : s_j > 0}
+    ([Review] formula for alpha and o; [WeChat] §1.2 for the ReLU form.)
+
+    ``scale`` defaults to 1/sqrt(d_h); pass 1.0 when ``Q`` already carries it.
+
+    Returns (a [d], cnt [H], amb [H]) where ``amb`` counts the scores whose
+    sign an fp32 evaluation of the same operands could flip:
+    |s_j| <= d_h * 2^-23 * scale * sum_k |Q_k K_jk|.
+    """
+    d = Q.shape[0]
+    dh = d // H
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    a = np.zeros(d)
+    cnt = np.zeros(H, dtype=np.int64)
+    amb = np.zeros(H, dtype=np.int64)
+    L = K.shape[0]
+    if L == 0:
+        return a, cnt, amb
+    for eta in range(H):
+        cols = slice(eta * dh, (eta + 1) * dh)
+        q = Q[cols]
+        s = (K[:, cols] @ q) * scale
+        if score == "softmax":
+            p = np.exp(s - s.max())
+            a[cols] = (p @ V[:, cols]) / p.sum()
+        elif score == "relu":
+            w = np.maximum(s, 0.0)
+            a[cols] = w @ V[:, cols]
+            cnt[eta] = int(np.count_nonzero(s > 0.0))
+            bound = dh * 2.0 ** -23 * (np.abs(K[:, cols]) @ np.abs(q)) * scale
+            amb[eta] = int(np.count_nonzero(np.abs(s) <= bound))
+        else:
+            raise ValueError(score)
+    return a, cnt, amb
+
+
+def attention_core(Qs: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
+                   scale: Optional[float] = None):
+    """Every target of one user: rows of ``Qs`` handled one at a time."""
+    m, d = Qs.shape
+    attn = np.zeros((m, d))
+    cnt = np.zeros((m, H), dtype=np.int64)
+    amb = np.zeros((m, H), dtype=np.int64)
+    for t in range(m):
+        attn[t], cnt[t], amb[t] = attention_target(Qs[t], K, V, H, score, scale)
+    return attn, cnt, amb
+
+
+# ---------------------------------------------------------------- weights
+def weights_f64(layers, z=None, wz=None):
+    """Upcast stored weights (bf16 bits or fp32) to float64 dictionaries."""
+    def conv(w):
+        if w is None:
+            return None
+        if isinstance(w, dict):
+            return {k: conv(v) for k, v in w.items()}
+        return stored_to_f64(w)
+    return [conv(l) for l in layers], conv(z), conv(wz)
+
+
+# ---------------------------------------------------------------- forward
+def encode_history(X: np.ndarray, lw: dict, kv_ln: bool):
+    """History side of one layer: K = Xt W_K, V = Xt W_V with
+    Xt = LN(SwiGLU(X)) ([Notes] §STCA; [HyFormer] eq. (7)-(8) without LN)."""
+    xt = ffn_ln(X, lw["kv"], kv_ln)
+    return xt @ lw["wk"], xt @ lw["wv"]
+
+
+def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=None, wz=None,
+            tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q")):
+    """The STCA forward for the users in ``users`` (default: all).
+
+    cfg: dict with d, H, M, score ("softmax"|"relu"), qmode ("fusion"|"linear"),
+         kv_ln, z_ln.
+    rows_f64: callable ids -> float64 table rows [len(ids), d].
+    layers/z/wz: float64 weights (see ``weights_f64``).
+    Returns a dict of float64 arrays indexed by global target index:
+      z [T, d], o [M, T, d], attn [M, T, d], active [M, T, H], amb [M, T, H],
+      qs [M, T, d] (the query rows after W_Q, before the 1/sqrt(d_h) scale).
+    Rows of targets whose user is not in ``users`` stay zero.
+    """
+    d, H, M = cfg["d"], cfg["H"], cfg["M"]
+    score, qmode = cfg["score"], cfg["qmode"]
+    ho = np.asarray(hist_offsets, dtype=np.int64)
+    to = np.asarray(tgt_offsets, dtype=np.int64)
+    B = len(ho) - 1
+    T = int(to[-1])
+    out = {"z": np.zeros((T, d)), "o": np.zeros((M, T, d)), "attn": np.zeros((M, T, d)),
+           "active": np.zeros((M, T, H), dtype=np.int64), "amb": np.zeros((M, T, H), np.int64),
+           "qs": np.zeros((M, T, d))}
+    if users is None:
+        users = range(B)
+    for u in users:
+        ids = np.asarray(hist_ids[ho[u]:ho[u + 1]])
+        X = rows_f64(ids) if len(ids) else np.zeros((0, d))
+        # Request Level Batching: the user's K/V of every layer is computed
+        # once and serves all of the user's targets ([Notes] §RLB).
+        KV = [encode_history(X, layers[i], cfg["kv_ln"]) for i in range(M)]
+        for t in range(int(to[u]), int(to[u + 1])):
+            if qmode == "fusion":
+                x_t = rows_f64(np.asarray([tgt_ids[t]]))[0]
+                q = ffn_ln(x_t, layers[0]["q"], True)
+            else:
+                q = np.asarray(q0[t], dtype=np.float64)
+            outs = []
+            for i in range(M):
+                Q = q @ layers[i]["wq"]
+                K, V = KV[i]
+                a, c, amb = attention_target(Q, K, V, H, score)
+                o = a @ layers[i]["wo"]
+                outs.append(o)
+                out["qs"][i, t] = Q
+                out["attn"][i, t] = a
+                out["active"][i, t] = c
+                out["amb"][i, t] = amb
+                out["o"][i, t] = o
+                if i + 1 < M:
+                    if qmode == "fusion":
+                        cat = np.concatenate(outs + [x_t])
+                        q = ffn_ln(cat @ layers[i + 1]["wc"], layers[i + 1]["q"], True)
+                    else:
+                        q = o @ layers[i]["r"]
+            if qmode == "fusion":
+                cat = np.concatenate(outs + [x_t])
+                out["z"][t] = ffn_ln(cat @ wz, z, cfg["z_ln"])
+            else:
+                out["z"][t] = outs[-1]
+    return out
+
+
+def forward_problem(p, users=None):
+    """Convenience wrapper over a ``recsys_ultra_long_amd.inputs.Problem``
+    (a plain data container: only its arrays are read)."""
+    sp = p.spec
+    layers, z, wz = weights_f64(p.layers, p.z, p.wz)
+    cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode,
+               kv_ln=sp.kv_ln, z_ln=sp.z_ln)
+    return forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets,
+                   lambda ids: stored_to_f64(p.rows(ids)), layers, z, wz,
+                   tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users)
