@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""STCA forward throughput on one MI355X.
+
+One step = one full STCA forward (every row of the hot path: planning, the
+history gather + SwiGLU FFN + LN + W_K/W_V of every layer, the query chain,
+the m-target multi-head cross attention with its split-L merge, W_O, the
+fusion update and z) over the RLB long-history workload: 32 users with
+10,240-item histories, 64 targets per user sharing the user's K/V, a
+4,000,000 x 256 bf16 table with Zipf(1.1) ids, d = 256, 8 heads, SwiGLU
+hidden 512, 4 stacked layers.  Inputs are synthetic, seeded, and resident in
+HBM before the timed region.
+
+Prints one JSON line.  ``value`` = history tokens per second per STCA layer
+(sum of history lengths x layers / time per forward).  The roofline block
+covers the dominant kernel (per-launch duration from HIP events recorded by
+the library at stage boundaries on its own stream); the attention kernel's HBM
+roofline is reported beside it.  ``cpu_baseline`` times the float64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload(name):
+    from recsys_ultra_long_amd import inputs as I
+    if name == "rlb-long":
+        return I.spec(3)
+    if name == "single-target":
+        return I.spec(2)
+    if name == "ragged":
+        return I.spec(4)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(p, seconds):
+    """Float64 oracle on whole users of the same workload until `seconds` pass."""
+    import numpy as np
+    from oracle import stca_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    sp = p.spec
+    layers, z, wz = O.weights_f64(p.layers, p.z, p.wz)
+    cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode, kv_ln=sp.kv_ln,
+               z_ln=sp.z_ln)
+    rows = lambda ids: O.stored_to_f64(p.rows(ids))
+    t0 = time.perf_counter()
+    users, toks, tgts = 0, 0, 0
+    q0 = O.stored_to_f64(p.q0) if p.q0 is not None else None
+    while users < sp.B:
+        O.forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets, rows, layers, z, wz,
+                  tgt_ids=p.tgt_ids, q0=q0, users=[users])
+        toks += int(p.hist_offsets[users + 1] - p.hist_offsets[users])
+        tgts += int(p.tgt_offsets[users + 1] - p.tgt_offsets[users])
+        users += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": toks * sp.M / dt, "unit": "history tokens/s per STCA layer",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{users} of {sp.B} users ({toks} history tokens, {tgts} targets, "
+                      f"{sp.M} layers) in {dt:.1f} s, float64 numpy",
+            "target_scores_per_s": tgts / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="rlb-long")
+    ap.add_argument("--path", default="staged", choices=["staged", "fused"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the STCA forward "
+              "shards by user with no exchange, so throughput at N GPUs is N times this "
+              "figure by construction and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from recsys_ultra_long_amd import inputs as I
+    from recsys_ultra_long_amd import stca
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stca.load()
+    sp = workload(args.workload)
+    t = time.time()
+    p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
+    log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} "
+        f"n_tgt={p.n_tgt} table={sp.table_rows}x{sp.d} {sp.dtype}")
+    dp = stca.upload(p, path=args.path)
+    torch.cuda.synchronize()
+    log("uploaded")
+    M = sp.M
+    nev = stca.n_stage_events(M)
+    evs = [stca.StageEvents(nev) for _ in range(args.steps)]
+    f = stca.Forward(dp, want=(), dumps=())
+    for _ in range(args.warmup):
+        f()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        f.out.stage_events = evs[k].ptr
+        f.out.n_stage_events = nev
+        f()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    st = int(f.status[0].item())
+    if st != 0:
+        raise SystemExit(f"device status flagged: {st}")
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    # per-stage durations from the library's boundary events
+    def stage(a, b):
+        return float(np.mean([e.elapsed(a, b) for e in evs]))
+    prep = stage(0, 1)
+    hist = [stage(1 + i, 2 + i) for i in range(M)]
+    query, part, merge, wo = [], [], [], []
+    for i in range(M):
+        prev = 1 + M if i == 0 else 5 + M + 4 * (i - 1)
+        query.append(stage(prev, 2 + M + 4 * i))
+        part.append(stage(2 + M + 4 * i, 3 + M + 4 * i))
+        merge.append(stage(3 + M + 4 * i, 4 + M + 4 * i))
+        wo.append(stage(4 + M + 4 * i, 5 + M + 4 * i))
+    zt = stage(5 + M + 4 * (M - 1), 2 + 5 * M)
+
+    d, h, H = sp.d, sp.hidden, sp.H
+    n_hist, T = p.n_hist, p.n_tgt
+    flops_hist = n_hist * (6 * d * h + 4 * d * d)            # per layer launch
+    bytes_attn = n_hist * 4 * d + T * 2 * d                  # K,V bf16 read once + Q
+    t_hist = float(np.mean(hist)) * 1e-3
+    t_attn = float(np.mean(part)) * 1e-3
+    hist_tf = flops_hist / t_hist / 1e12
+    attn_gbs = bytes_attn / t_attn / 1e9
+    roof_hist = {"kernel": "history chain (gather+SwiGLU+LN+W_K|W_V)", "bound": "mfma",
+                 "achieved": round(hist_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(hist_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                 "launch_ms": round(t_hist * 1e3, 4),
+                 "per_launch": f"{n_hist} tokens x {6 * d * h + 4 * d * d} flop"}
+    roof_attn = {"kernel": "m-target cross attention (split-L partials)", "bound": "hbm",
+                 "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                 "launch_ms": round(t_attn * 1e3, 4),
+                 "per_launch": f"{n_hist} tokens x {4 * d} B + {T} targets x {2 * d} B"}
+    dominant = roof_hist if sum(hist) >= sum(part) else roof_attn
+
+    value = n_hist * M / (ms * 1e-3)
+    res = {
+        "metric": "history tokens/s + target scores/s per STCA layer at L=10K; % of HBM/MFMA peak",
+        "value": round(value, 1),
+        "unit": "history tokens/s per STCA layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{sp.name}: B={sp.B} users, L={sp.L}, m={sp.m} targets/user (RLB), "
+                               f"table {sp.table_rows}x{d} bf16 Zipf({sp.zipf_s}) ids, d={d}, H={H}, "
+                               f"hidden={h}, M={M} layers, softmax, path={args.path}",
+                   "global_batch": sp.B, "seq_len": sp.L, "targets": T, "parallelism": "single GPU"},
+        "target_scores_per_s_per_layer": round(T * M / (ms * 1e-3), 1),
+        "target_scores_per_s": round(T / (ms * 1e-3), 1),
+        "history_tokens_per_s": round(n_hist / (ms * 1e-3), 1),
+        "roofline": dominant,
+        "roofline_attention": roof_attn,
+        "roofline_history": roof_hist,
+        "stages_ms": {"prep_plan": round(prep, 4), "history": [round(x, 4) for x in hist],
+                      "query": [round(x, 4) for x in query], "attn_partial": [round(x, 4) for x in part],
+                      "attn_merge": [round(x, 4) for x in merge], "w_o": [round(x, 4) for x in wo],
+                      "z": round(zt, 4)},
+    }
+    for e in evs:
+        e.close()
+    if not args.no_cpu_baseline:
+        log(f"timing the float64 oracle for ~{args.cpu_seconds:.0f}s")
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

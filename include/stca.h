@@ -1,0 +1,211 @@
+/*
+ * stca.h -- C ABI of the STCA forward library for MI355X (gfx950).
+ *
+ * The library computes the forward hot path of Stacked Target-to-History
+ * Cross Attention (STCA) over ragged user histories, with Request Level
+ * Batching (every target of a user reads that user's keys and values once
+ * per layer) and, on the fused path, the embedding gather fused with the
+ * attention ("lookup while computing").
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [Notes]    "超长序列建模 —— STCA 精读笔记": §STCA (layer definition:
+ *              history FFN+LN feeding W_K/W_V, query from the target, heads
+ *              concatenated then W_O), §Request Level Batching.
+ *   [Review]   "Make It Long, Keep It Fast: End-to-End 10K Long User Behavior
+ *              Sequence Modeling for Billion-Scale Douyin Recommendation"
+ *              (paper review): architecture tree and 核心公式 (alpha, o,
+ *              fusion q^(i+1), final z).
+ *   [WeChat]   "视频号推荐超长序列技术演进：从端到端到 Cross-Mask Transformer":
+ *              §1.1 显存优化 (lookup fused with target attention, no [B,L,D]
+ *              KV tensor), §1.2 (ReLU-activated target attention, active keys
+ *              are those with score > 0).
+ *   [HyFormer] "HyFormer：重新审视序列建模和特征交互在 CTR 预测中的作用":
+ *              eq. (7)-(9) and (16) (per-layer SwiGLU encoding without LN,
+ *              multi-query cross attention), §3.7 (one query set per sequence).
+ *
+ * Conventions
+ *   - Row vectors: y = x W with W stored [in, out] row-major.
+ *   - Every data pointer below is a DEVICE pointer unless marked "host".
+ *     The caller allocates and owns every buffer, including the workspace;
+ *     the library keeps no pointer after a call returns.
+ *   - Calls are asynchronous on the given HIP stream (hipStream_t passed as
+ *     void*; NULL = the null stream).  The library never synchronises.
+ *   - bf16 arrays hold raw bf16 bits (uint16).  fp32 arrays are IEEE float.
+ *   - All device pointers must be 16-byte aligned.
+ *
+ * Errors
+ *   Host-side validation is synchronous: a negative stca_status is returned,
+ *   nothing is enqueued, and stca_last_error() gives a thread-local message.
+ *   Conditions only visible on the device (inconsistent CSR offsets, a user
+ *   with more targets than max_tgt_per_user, ids outside [0, table_rows))
+ *   never cause an out-of-bounds access: the offending rows are treated as
+ *   zero rows / empty users, and if outputs->dev_status is non-NULL a nonzero
+ *   bit mask (STCA_DEV_*) is OR-ed into it; the caller reads it after the
+ *   stream has completed.  No exception crosses the ABI and nothing aborts.
+ */
+#ifndef STCA_H_
+#define STCA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STCA_OK = 0,
+  STCA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or mode   */
+  STCA_ERR_UNSUPPORTED = -2,   /* valid request this build does not implement */
+  STCA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required  */
+  STCA_ERR_HIP = -4            /* a HIP launch or runtime call failed         */
+} stca_status;
+
+enum { STCA_F32 = 0, STCA_BF16 = 1 };                  /* stca_config.dtype  */
+enum { STCA_SCORE_SOFTMAX = 0, STCA_SCORE_RELU = 1 };  /* stca_config.score  */
+enum { STCA_Q_FUSION = 0, STCA_Q_LINEAR = 1 };         /* stca_config.qmode  */
+enum { STCA_PATH_STAGED = 0, STCA_PATH_FUSED = 1 };    /* stca_config.path   */
+enum {                                                 /* stca_config.flags  */
+  STCA_FLAG_KV_LN = 1,  /* LN after the history FFN (STCA); clear for HyFormer eq. (7) */
+  STCA_FLAG_Z_LN = 2    /* LN on the final z ([Notes] wording); default is [Review]'s z */
+};
+enum {                                                 /* dev_status bits     */
+  STCA_DEV_BAD_HIST_OFFSETS = 1,  /* hist_offsets not monotone / not ending at n_hist: all users empty */
+  STCA_DEV_BAD_TGT_OFFSETS = 2,   /* tgt_offsets inconsistent or m_u > max_tgt_per_user: no targets  */
+  STCA_DEV_BAD_ID = 4             /* an id outside [0, table_rows): that row reads as zeros           */
+};
+
+/* Model and launch configuration (host struct). */
+typedef struct {
+  int32_t B;            /* users in the batch                                     */
+  int32_t d;            /* model width; bf16: 128, 256 or 512; fp32: 32..512 (x32) */
+  int32_t H;            /* heads; d_h = d / H must be 32 or 64                    */
+  int32_t hidden;       /* SwiGLU hidden width h; multiple of 128 (bf16) / 32     */
+  int32_t M;            /* stacked layers, 1..16                                  */
+  int64_t table_rows;   /* rows N of the embedding table                          */
+  int32_t dtype;        /* STCA_F32 or STCA_BF16: table, weights, K/V, queries    */
+  int32_t score;        /* STCA_SCORE_*                                           */
+  int32_t qmode;        /* STCA_Q_*                                               */
+  int32_t path;         /* STCA_PATH_*                                            */
+  int32_t flags;        /* STCA_FLAG_*                                            */
+  int32_t chunk_keys;   /* keys per split-L chunk (multiple of 32); 0 = automatic  */
+} stca_config;
+
+/* One batch of requests: ragged histories and targets in CSR form.
+ * User u owns history tokens [hist_offsets[u], hist_offsets[u+1]) and targets
+ * [tgt_offsets[u], tgt_offsets[u+1]) ([Notes] §RLB: the targets of one request
+ * share the user's encoding).  Histories may be empty. */
+typedef struct {
+  const int32_t *hist_offsets;  /* [B+1], hist_offsets[0] = 0, last = n_hist       */
+  const int32_t *hist_ids;      /* [n_hist] table rows of the history items         */
+  const int32_t *tgt_offsets;   /* [B+1], tgt_offsets[0] = 0, last = n_tgt          */
+  const int32_t *tgt_ids;       /* [n_tgt] table rows of the targets (STCA_Q_FUSION) */
+  const void *q0;               /* [n_tgt, d] first-layer queries (STCA_Q_LINEAR)   */
+  const void *table;            /* [table_rows, d] embedding table                  */
+  int64_t n_hist;               /* host: total history tokens, < 2^31               */
+  int64_t n_tgt;                /* host: total targets, < 2^31                      */
+  int32_t max_tgt_per_user;     /* host: upper bound on any m_u, 1..4096            */
+} stca_batch;
+
+/* SwiGLU FFN d -> h -> d, optionally followed by LayerNorm (eps 1e-5):
+ * y = (SiLU(x W1) * (x W3)) W2;  LN(y) = (y - mean) / sqrt(var + eps) * ln_g + ln_b.
+ * Matrices in the config dtype; ln_g / ln_b are always fp32 [d]. */
+typedef struct {
+  const void *w1;     /* [d, h] */
+  const void *w3;     /* [d, h] */
+  const void *w2;     /* [h, d] */
+  const float *ln_g;  /* [d] (NULL when the LN is not applied) */
+  const float *ln_b;  /* [d] */
+} stca_ffn;
+
+/* Weights of layer i (0-based).  Heads are column slices of width d_h of
+ * W_Q, W_K, W_V; W_O acts on the concatenated heads ([Notes] §STCA). */
+typedef struct {
+  stca_ffn kv;        /* history FFN (+LN if STCA_FLAG_KV_LN): Xt = LN(SwiGLU(X))   */
+  stca_ffn q;         /* query FFN+LN (STCA_Q_FUSION): q1 = LN(SwiGLU(x_t)) at i = 0,
+                         q_{i+1} = LN(SwiGLU([o_1|..|o_i|x_t] W_C)) at i > 0          */
+  const void *wk, *wv, *wq, *wo;   /* [d, d] each                                   */
+  const void *wc;     /* [(i+1) d, d] fusion matrix (STCA_Q_FUSION, i > 0; else NULL) */
+  const void *r;      /* [d, d] next-query map Q_{i+1} = O_i R_i (STCA_Q_LINEAR,
+                         i < M-1; else ignored)                                      */
+} stca_layer;
+
+typedef struct {
+  const stca_layer *layers;  /* host array [M]                                      */
+  stca_ffn z;                /* final SwiGLU (+LN with STCA_FLAG_Z_LN), STCA_Q_FUSION */
+  const void *wz;            /* [(M+1) d, d] final concat map, STCA_Q_FUSION          */
+} stca_weights;
+
+typedef struct {
+  float *z;            /* [n_tgt, d] required: z (fusion) or O_M (linear)           */
+  float *o_layers;     /* [M, n_tgt, d] optional: o^(i) after W_O                    */
+  float *attn;         /* [M, n_tgt, d] optional: heads concatenated, before W_O     */
+  int32_t *active;     /* [M, n_tgt, H] optional, STCA_SCORE_RELU: #{j : s_j > 0}    */
+  void *q_dump;        /* [M, n_tgt, d] optional: query rows as the attention reads
+                          them (after W_Q and the 1/sqrt(d_h) scale), config dtype   */
+  void *kv_dump;       /* [M, 2, n_hist, d] optional: K then V rows of every layer as
+                          the attention reads them, config dtype (staged path only)  */
+  void *x_dump;        /* [n_hist, d] optional: gathered history rows (table dtype)  */
+  int32_t *dev_status; /* optional: STCA_DEV_* bits OR-ed in on the device           */
+  /* Optional stage timing: host array of caller-created hipEvent_t handles.  The
+   * library records (hipEventRecord on the call's stream, no synchronisation) up
+   * to n_stage_events of these boundaries, in this order:
+   *   0            start of the call
+   *   1            weights prepared and batch planned
+   *   2 + i        history encoding (gather, FFN, LN, W_K|W_V) of layer i done, i < M
+   *   2 + M + 4i   query of layer i done
+   *   3 + M + 4i   attention partials of layer i done
+   *   4 + M + 4i   partial merge of layer i done
+   *   5 + M + 4i   output projection (and next-query map) of layer i done
+   *   2 + 5M       final z done                     (5M + 3 events in all) */
+  void *const *stage_events;
+  int32_t n_stage_events;
+} stca_outputs;
+
+/* Workspace bytes stca_forward needs for this configuration and batch.
+ * With STCA_PATH_FUSED the size does not grow with n_hist * d (no K/V buffer). */
+int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t *bytes);
+
+/* The full forward: every layer's history encoding (gather, SwiGLU FFN, LN,
+ * W_K/W_V), the query chain, the m-target multi-head cross attention of every
+ * user, W_O, the fusion update and z.  Returns STCA_OK once everything is
+ * enqueued on `hip_stream`. */
+int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                 const stca_outputs *out, void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* The attention core alone on caller-provided operands ([Review] formula for
+ * alpha and o; [WeChat] §1.2 for the ReLU form): for every user u, target t of
+ * u and head eta,
+ *   s_j = q_t[eta] . k_j[eta]                (q rows already carry 1/sqrt(d_h))
+ *   softmax: attn_t[eta] = sum_j exp(s_j - max) v_j[eta] / sum_j exp(s_j - max)
+ *   relu:    attn_t[eta] = sum_j max(0, s_j) v_j[eta], active = #{j : s_j > 0}
+ * over the user's history rows j.  An empty history gives zeros. */
+typedef struct {
+  int32_t B, d, H;          /* host                                                  */
+  int32_t dtype;            /* STCA_F32 / STCA_BF16 for q, k, v                       */
+  int32_t score;            /* STCA_SCORE_*                                           */
+  int32_t chunk_keys;       /* as in stca_config                                      */
+  const int32_t *hist_offsets;  /* [B+1] */
+  const int32_t *tgt_offsets;   /* [B+1] */
+  int64_t n_hist, n_tgt;    /* host */
+  int32_t max_tgt_per_user; /* host */
+  const void *q;            /* [n_tgt, d] */
+  const void *k, *v;        /* [n_hist, d] each */
+  float *attn;              /* [n_tgt, d] output */
+  int32_t *active;          /* [n_tgt, H] output, ReLU only (optional) */
+  int32_t *dev_status;      /* optional */
+} stca_attn_args;
+
+int stca_attention_workspace_size(const stca_attn_args *a, size_t *bytes);
+int stca_attention(const stca_attn_args *a, void *workspace, size_t ws_bytes, void *hip_stream);
+
+const char *stca_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *stca_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int stca_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STCA_H_ */

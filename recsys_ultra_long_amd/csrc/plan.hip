@@ -1,0 +1,89 @@
+// plan.hip -- batch planner (a1): validates the CSR offsets on the device and
+// builds the padded K/V block offsets and the split-L chunk offsets.
+//
+// Each user's history is padded to whole 32-key blocks so that a block never
+// mixes users ([Notes] §RLB: a user's encoding is shared by all of that
+// user's targets and by no one else).  Chunks group `nb` consecutive blocks of
+// one user; every (chunk, head, target group) is one attention workgroup.
+#include "stca_internal.h"
+
+namespace stca {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ int block_exclusive_scan(int v, int *sh, int &total) {
+  // Hillis-Steele inclusive scan in shared memory, then shift to exclusive.
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    int x = (t >= o) ? sh[t - o] : 0;
+    __syncthreads();
+    sh[t] += x;
+    __syncthreads();
+  }
+  int incl = sh[t];
+  total = sh[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(
+    const int *__restrict__ hist_off, const int *__restrict__ tgt_off, int B, long long n_hist,
+    long long n_tgt, int max_tgt, int nb, Plan plan, int *status) {
+  __shared__ int sh[kPlanThreads];
+  __shared__ int bad_h, bad_t;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    bad_h = (hist_off[0] != 0) || ((long long)hist_off[B] != n_hist);
+    bad_t = (tgt_off[0] != 0) || ((long long)tgt_off[B] != n_tgt);
+  }
+  __syncthreads();
+  for (int u = t; u < B; u += kPlanThreads) {
+    int lh = hist_off[u + 1] - hist_off[u];
+    int lt = tgt_off[u + 1] - tgt_off[u];
+    if (lh < 0) atomicOr(&bad_h, 1);
+    if (lt < 0 || lt > max_tgt) atomicOr(&bad_t, 1);
+  }
+  __syncthreads();
+  const bool bh = bad_h != 0, bt = bad_t != 0;
+  if (t == 0) {
+    if (bh) set_status(status, 1);
+    if (bt) set_status(status, 2);
+  }
+  int carry_b = 0, carry_c = 0;
+  for (int base = 0; base <= B; base += kPlanThreads) {
+    const int u = base + t;
+    int nbk = 0, nch = 0;
+    if (u < B) {
+      int lh = bh ? 0 : hist_off[u + 1] - hist_off[u];
+      nbk = (lh + 31) >> 5;
+      nch = (nbk + nb - 1) / nb;
+    }
+    int tb, tc;
+    int eb = block_exclusive_scan(nbk, sh, tb);
+    int ec = block_exclusive_scan(nch, sh, tc);
+    if (u <= B) {
+      plan.pblk[u] = carry_b + eb;
+      plan.coff[u] = carry_c + ec;
+      plan.hoff[u] = bh ? 0 : hist_off[u];
+      plan.toff[u] = bt ? 0 : tgt_off[u];
+    }
+    carry_b += tb;
+    carry_c += tc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
+                       int64_t n_tgt, int max_tgt, int nb, Plan plan, int *status,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, hist_off, tgt_off, B,
+                     (long long)n_hist, (long long)n_tgt, max_tgt, nb, plan, status);
+  return hipGetLastError();
+}
+
+}  // namespace stca

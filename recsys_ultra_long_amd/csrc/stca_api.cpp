@@ -1,0 +1,690 @@
+// stca_api.cpp -- the C ABI (include/stca.h): argument validation, workspace
+// planning and the per-layer launch sequence of the STCA forward.
+//
+// Launch sequence of stca_forward (bf16 shown; fp32 is the same without the
+// weight preparation):
+//   1. weight preparation: every matrix transposed to [out, in] bf16 (one
+//      batched launch) so MFMA operands are k-contiguous 16-byte loads;
+//   2. planner: CSR validation, padded block offsets, split-L chunk offsets;
+//   3. history side of every layer (gather -> SwiGLU FFN -> LN -> W_K | W_V)
+//      into the blocked K/V buffers.  The history side never depends on the
+//      query ([Notes] §STCA: each layer's FFN reads the raw rows), so all M
+//      layers are encoded before the query chain starts;
+//   4. per layer: query (q1 from x_t, or the fusion of [o_1..o_i | x_t]),
+//      Q = q W_Q / sqrt(d_h); attention partials and merge; o = attn W_O;
+//   5. z = SwiGLU([o_1 | .. | o_M | x_t] W_Z) [+ LN]   (linear mode: z = O_M).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/stca.h"
+#include "stca_internal.h"
+
+using namespace stca;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(STCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off += up(bytes);
+    return o;
+  }
+};
+
+// Offsets (elements) of the prepared (transposed) bf16 weights of one layer.
+struct PrepLayer {
+  size_t kv_w1, kv_w3, kv_w2, wkv, q_w1, q_w3, q_w2, wq, wo, wc, r;
+};
+
+struct Layout {
+  int nb = 1;              // blocks per chunk
+  int64_t max_blocks = 0;  // host bound
+  int64_t max_chunks = 0;
+  size_t esize = 2;
+  size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0;
+  size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
+  std::vector<PrepLayer> pl;
+  size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
+};
+
+int choose_nb(int chunk_keys, int64_t n_hist, int B, int H, int max_tgt) {
+  if (chunk_keys > 0) return chunk_keys / 32;
+  const int64_t blocks = max_blocks(n_hist, B);
+  const int groups = (max_tgt + 63) / 64;
+  const int64_t want_chunks = std::max<int64_t>(1, 2048 / ((int64_t)H * groups));
+  int64_t nb = (blocks + want_chunks - 1) / want_chunks;
+  nb = std::max<int64_t>(nb, std::max(4, std::min(max_tgt, 64)));
+  nb = (nb + 3) / 4 * 4;
+  return (int)std::min<int64_t>(nb, 1 << 20);
+}
+
+int validate_cfg(const stca_config *c) {
+  if (!c) return fail(STCA_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->B < 0) return fail(STCA_ERR_INVALID_ARG, "B must be >= 0 (got %d)", c->B);
+  if (c->H <= 0 || c->d <= 0 || c->d % c->H)
+    return fail(STCA_ERR_INVALID_ARG, "d (%d) must be a positive multiple of H (%d)", c->d, c->H);
+  const int dh = c->d / c->H;
+  if (dh != 32 && dh != 64) return fail(STCA_ERR_UNSUPPORTED, "d_h = %d unsupported (32 or 64)", dh);
+  if (c->M < 1 || c->M > 16) return fail(STCA_ERR_INVALID_ARG, "M = %d outside 1..16", c->M);
+  if (c->dtype != STCA_F32 && c->dtype != STCA_BF16)
+    return fail(STCA_ERR_INVALID_ARG, "dtype %d unknown", c->dtype);
+  if (c->score != STCA_SCORE_SOFTMAX && c->score != STCA_SCORE_RELU)
+    return fail(STCA_ERR_INVALID_ARG, "score %d unknown", c->score);
+  if (c->qmode != STCA_Q_FUSION && c->qmode != STCA_Q_LINEAR)
+    return fail(STCA_ERR_INVALID_ARG, "qmode %d unknown", c->qmode);
+  if (c->path != STCA_PATH_STAGED && c->path != STCA_PATH_FUSED)
+    return fail(STCA_ERR_INVALID_ARG, "path %d unknown", c->path);
+  if (c->path == STCA_PATH_FUSED) return fail(STCA_ERR_UNSUPPORTED, "fused path not built yet");
+  if (c->flags & ~(STCA_FLAG_KV_LN | STCA_FLAG_Z_LN))
+    return fail(STCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
+  if (c->chunk_keys < 0 || c->chunk_keys % 32)
+    return fail(STCA_ERR_INVALID_ARG, "chunk_keys %d must be a multiple of 32", c->chunk_keys);
+  if (c->table_rows <= 0 || c->table_rows >= (1ll << 31))
+    return fail(STCA_ERR_INVALID_ARG, "table_rows %lld outside [1, 2^31)", (long long)c->table_rows);
+  if (c->dtype == STCA_BF16) {
+    if (c->d != 128 && c->d != 256 && c->d != 512)
+      return fail(STCA_ERR_UNSUPPORTED, "bf16 supports d in {128, 256, 512} (got %d)", c->d);
+    if (c->hidden <= 0 || c->hidden % 128)
+      return fail(STCA_ERR_UNSUPPORTED, "bf16 needs hidden a positive multiple of 128 (got %d)", c->hidden);
+  } else {
+    if (c->d > 512 || c->d % 32)
+      return fail(STCA_ERR_UNSUPPORTED, "fp32 supports d a multiple of 32 up to 512 (got %d)", c->d);
+    if (c->hidden <= 0 || c->hidden % 32)
+      return fail(STCA_ERR_UNSUPPORTED, "fp32 needs hidden a positive multiple of 32 (got %d)", c->hidden);
+  }
+  return STCA_OK;
+}
+
+int validate_batch(const stca_config *c, const stca_batch *b) {
+  if (!b) return fail(STCA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->n_hist < 0 || b->n_hist >= (1ll << 31))
+    return fail(STCA_ERR_INVALID_ARG, "n_hist %lld outside [0, 2^31)", (long long)b->n_hist);
+  if (b->n_tgt < 0 || b->n_tgt >= (1ll << 31))
+    return fail(STCA_ERR_INVALID_ARG, "n_tgt %lld outside [0, 2^31)", (long long)b->n_tgt);
+  if (b->max_tgt_per_user < 1 || b->max_tgt_per_user > 4096)
+    return fail(STCA_ERR_INVALID_ARG, "max_tgt_per_user %d outside 1..4096", b->max_tgt_per_user);
+  if (c->B == 0 && (b->n_hist || b->n_tgt))
+    return fail(STCA_ERR_INVALID_ARG, "B = 0 with n_hist = %lld, n_tgt = %lld", (long long)b->n_hist,
+                (long long)b->n_tgt);
+  if (c->B > 0 && (!b->hist_offsets || !b->tgt_offsets))
+    return fail(STCA_ERR_INVALID_ARG, "hist_offsets / tgt_offsets must not be NULL");
+  if (b->n_hist > 0 && !b->hist_ids) return fail(STCA_ERR_INVALID_ARG, "hist_ids is NULL");
+  if (!b->table) return fail(STCA_ERR_INVALID_ARG, "table is NULL");
+  if (c->qmode == STCA_Q_FUSION && b->n_tgt > 0 && !b->tgt_ids)
+    return fail(STCA_ERR_INVALID_ARG, "tgt_ids is NULL (fusion mode)");
+  if (c->qmode == STCA_Q_LINEAR && b->n_tgt > 0 && !b->q0)
+    return fail(STCA_ERR_INVALID_ARG, "q0 is NULL (linear mode)");
+  const void *ptrs[] = {b->hist_offsets, b->hist_ids, b->tgt_offsets, b->tgt_ids, b->q0, b->table};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
+  return STCA_OK;
+}
+
+int check_ffn(const stca_ffn &f, bool ln, const char *name, int layer) {
+  if (!f.w1 || !f.w3 || !f.w2) return fail(STCA_ERR_INVALID_ARG, "%s FFN matrix NULL (layer %d)", name, layer);
+  if (ln && (!f.ln_g || !f.ln_b)) return fail(STCA_ERR_INVALID_ARG, "%s LN params NULL (layer %d)", name, layer);
+  const void *ptrs[] = {f.w1, f.w3, f.w2, f.ln_g, f.ln_b};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "%s weight not 16-byte aligned (layer %d)", name, layer);
+  return STCA_OK;
+}
+
+int validate_weights(const stca_config *c, const stca_weights *w) {
+  if (!w || !w->layers) return fail(STCA_ERR_INVALID_ARG, "weights / weights->layers is NULL");
+  const bool kvln = c->flags & STCA_FLAG_KV_LN;
+  for (int i = 0; i < c->M; ++i) {
+    const stca_layer &l = w->layers[i];
+    int r = check_ffn(l.kv, kvln, "kv", i);
+    if (r) return r;
+    const void *mats[] = {l.wk, l.wv, l.wq, l.wo};
+    for (const void *p : mats) {
+      if (!p) return fail(STCA_ERR_INVALID_ARG, "W_K/W_V/W_Q/W_O NULL (layer %d)", i);
+      if (!aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "layer %d weight not 16-byte aligned", i);
+    }
+    if (c->qmode == STCA_Q_FUSION) {
+      if ((r = check_ffn(l.q, true, "q", i))) return r;
+      if (i > 0 && !l.wc) return fail(STCA_ERR_INVALID_ARG, "W_C NULL (layer %d)", i);
+      if (l.wc && !aligned16(l.wc)) return fail(STCA_ERR_INVALID_ARG, "W_C not aligned (layer %d)", i);
+    } else if (i + 1 < c->M) {
+      if (!l.r) return fail(STCA_ERR_INVALID_ARG, "R NULL (layer %d, linear mode)", i);
+      if (!aligned16(l.r)) return fail(STCA_ERR_INVALID_ARG, "R not aligned (layer %d)", i);
+    }
+  }
+  if (c->qmode == STCA_Q_FUSION) {
+    int r = check_ffn(w->z, c->flags & STCA_FLAG_Z_LN, "z", c->M);
+    if (r) return r;
+    if (!w->wz) return fail(STCA_ERR_INVALID_ARG, "W_Z is NULL");
+    if (!aligned16(w->wz)) return fail(STCA_ERR_INVALID_ARG, "W_Z not aligned");
+  }
+  return STCA_OK;
+}
+
+Layout make_layout(const stca_config *c, const stca_batch *b) {
+  Layout L;
+  const int64_t d = c->d, h = c->hidden, T = b->n_tgt;
+  const int dh = c->d / c->H;
+  L.esize = c->dtype == STCA_BF16 ? 2 : 4;
+  L.nb = choose_nb(c->chunk_keys, b->n_hist, c->B, c->H, b->max_tgt_per_user);
+  L.max_blocks = max_blocks(b->n_hist, c->B);
+  L.max_chunks = max_chunks(b->n_hist, c->B, L.nb);
+  Carver cv;
+  L.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
+  if (c->dtype == STCA_BF16) {
+    size_t e = 0;
+    L.pl.resize(c->M);
+    for (int i = 0; i < c->M; ++i) {
+      PrepLayer &p = L.pl[i];
+      p.kv_w1 = e; e += h * d;
+      p.kv_w3 = e; e += h * d;
+      p.kv_w2 = e; e += h * d;
+      p.wkv = e; e += 2 * d * d;
+      p.wq = e; e += d * d;
+      p.wo = e; e += d * d;
+      if (c->qmode == STCA_Q_FUSION) {
+        p.q_w1 = e; e += h * d;
+        p.q_w3 = e; e += h * d;
+        p.q_w2 = e; e += h * d;
+        if (i > 0) { p.wc = e; e += d * (i + 1) * d; }
+      } else {
+        p.r = e; e += d * d;
+      }
+    }
+    if (c->qmode == STCA_Q_FUSION) {
+      L.z_w1 = e; e += h * d;
+      L.z_w3 = e; e += h * d;
+      L.z_w2 = e; e += h * d;
+      L.wz = e; e += d * (c->M + 1) * d;
+    }
+    L.prep_elems = e;
+    L.prep = cv.take(e * 2);
+  }
+  L.kv_layer = (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
+  L.kv = cv.take(2 * L.kv_layer * c->M);
+  const size_t np = (size_t)L.max_chunks * c->H * b->max_tgt_per_user;
+  L.part_ml = cv.take(np * 2 * sizeof(float));
+  L.part_acc = cv.take(np * dh * sizeof(float));
+  L.part_cnt = cv.take(np * sizeof(int));
+  L.xt = cv.take(T * d * L.esize);
+  L.ocat = cv.take(T * d * c->M * L.esize);
+  L.qs = cv.take(T * d * L.esize);
+  L.attn32 = cv.take(T * d * sizeof(float));
+  L.attnlo = cv.take(T * d * L.esize);
+  L.qcur = cv.take(T * d * L.esize);
+  L.total = cv.off;
+  return L;
+}
+
+template <typename T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>((char *)ws + off); }
+
+}  // namespace
+
+extern "C" {
+
+int stca_version(void) { return 100; }
+
+const char *stca_status_string(int s) {
+  switch (s) {
+    case STCA_OK: return "STCA_OK";
+    case STCA_ERR_INVALID_ARG: return "STCA_ERR_INVALID_ARG";
+    case STCA_ERR_UNSUPPORTED: return "STCA_ERR_UNSUPPORTED";
+    case STCA_ERR_WORKSPACE: return "STCA_ERR_WORKSPACE";
+    case STCA_ERR_HIP: return "STCA_ERR_HIP";
+    default: return "STCA_ERR_UNKNOWN";
+  }
+}
+
+const char *stca_last_error(void) { return g_err; }
+
+int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(STCA_ERR_INVALID_ARG, "bytes is NULL");
+  int r = validate_cfg(cfg);
+  if (r) return r;
+  if ((r = validate_batch(cfg, batch))) return r;
+  *bytes = make_layout(cfg, batch).total;
+  return STCA_OK;
+}
+
+int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                 const stca_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  int r = validate_cfg(cfg);
+  if (r) return r;
+  if ((r = validate_batch(cfg, batch))) return r;
+  if ((r = validate_weights(cfg, w))) return r;
+  if (!out || !out->z) return fail(STCA_ERR_INVALID_ARG, "outputs->z is required");
+  {
+    const void *ptrs[] = {out->z, out->o_layers, out->attn, out->active, out->q_dump, out->kv_dump,
+                          out->x_dump, out->dev_status};
+    for (const void *p : ptrs)
+      if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return fail(STCA_ERR_INVALID_ARG, "output pointer %p misaligned", p);
+    const void *p16[] = {out->z, out->o_layers, out->attn, out->q_dump, out->x_dump};
+    for (const void *p : p16)
+      if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "output pointer %p not 16-byte aligned", p);
+  }
+  const Layout L = make_layout(cfg, batch);
+  if (!ws && L.total > 0) return fail(STCA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total)
+    return fail(STCA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  if (ws && !aligned16(ws)) return fail(STCA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int B = cfg->B, d = cfg->d, H = cfg->H, M = cfg->M, dh = d / H;
+  if (out->n_stage_events < 0 || (out->n_stage_events > 0 && !out->stage_events))
+    return fail(STCA_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+  auto rec = [&](int k) -> hipError_t {
+    if (k < out->n_stage_events && out->stage_events[k])
+      return hipEventRecord(reinterpret_cast<hipEvent_t>(out->stage_events[k]), s);
+    return hipSuccess;
+  };
+  const int64_t T = batch->n_tgt;
+  const bool bf = cfg->dtype == STCA_BF16;
+  const size_t es = L.esize;
+  const bool fusion = cfg->qmode == STCA_Q_FUSION;
+  const float qscale = 1.0f / std::sqrt((float)dh);
+  hipError_t e = hipSuccess;
+
+  Plan plan;
+  plan.hoff = at<int>(ws, L.plan);
+  plan.toff = plan.hoff + (B + 1);
+  plan.pblk = plan.toff + (B + 1);
+  plan.coff = plan.pblk + (B + 1);
+
+  if ((e = rec(0))) return hip_fail(e, "stage event");
+  // ---- 1. weight preparation (bf16): transposes into the workspace
+  bf16_t *prep = bf ? at<bf16_t>(ws, L.prep) : nullptr;
+  if (bf) {
+    TransposeBatch tb;
+    int n = 0;
+    auto add = [&](const void *src, int rows, int cols, size_t dst, int ld, int col0) -> hipError_t {
+      tb.m[n++] = TransposeDesc{(const bf16_t *)src, prep + dst, rows, cols, ld, col0};
+      if (n == kMaxTransposes) {
+        hipError_t er = launch_transpose_batch(tb, n, s);
+        n = 0;
+        return er;
+      }
+      return hipSuccess;
+    };
+    const int hd = cfg->hidden;
+    for (int i = 0; i < M; ++i) {
+      const stca_layer &l = w->layers[i];
+      const PrepLayer &p = L.pl[i];
+      if ((e = add(l.kv.w1, d, hd, p.kv_w1, d, 0))) break;
+      if ((e = add(l.kv.w3, d, hd, p.kv_w3, d, 0))) break;
+      if ((e = add(l.kv.w2, hd, d, p.kv_w2, hd, 0))) break;
+      if ((e = add(l.wk, d, d, p.wkv, d, 0))) break;
+      if ((e = add(l.wv, d, d, p.wkv + (size_t)d * d, d, 0))) break;
+      if ((e = add(l.wq, d, d, p.wq, d, 0))) break;
+      if ((e = add(l.wo, d, d, p.wo, d, 0))) break;
+      if (fusion) {
+        if ((e = add(l.q.w1, d, hd, p.q_w1, d, 0))) break;
+        if ((e = add(l.q.w3, d, hd, p.q_w3, d, 0))) break;
+        if ((e = add(l.q.w2, hd, d, p.q_w2, hd, 0))) break;
+        if (i > 0 && (e = add(l.wc, (i + 1) * d, d, p.wc, (i + 1) * d, 0))) break;
+      } else if (i + 1 < M) {
+        if ((e = add(l.r, d, d, p.r, d, 0))) break;
+      }
+    }
+    if (!e && fusion) {
+      e = add(w->z.w1, d, hd, L.z_w1, d, 0);
+      if (!e) e = add(w->z.w3, d, hd, L.z_w3, d, 0);
+      if (!e) e = add(w->z.w2, hd, d, L.z_w2, hd, 0);
+      if (!e) e = add(w->wz, (M + 1) * d, d, L.wz, (M + 1) * d, 0);
+    }
+    if (!e && n) e = launch_transpose_batch(tb, n, s);
+    if (e) return hip_fail(e, "weight preparation");
+  }
+
+  // ---- 2. planner
+  if (B > 0) {
+    e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, batch->n_hist, T,
+                    batch->max_tgt_per_user, L.nb, plan, out->dev_status, s);
+    if (e) return hip_fail(e, "planner");
+  }
+  if ((e = rec(1))) return hip_fail(e, "stage event");
+  if (B == 0 || (batch->n_hist == 0 && T == 0)) return STCA_OK;
+
+  auto chain = [&](const ChainArgs &a) { return bf ? launch_chain_bf16(a, s) : launch_chain_f32(a, s); };
+  auto base_args = [&]() {
+    ChainArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.d = d;
+    a.hidden = cfg->hidden;
+    a.table = batch->table;
+    a.table_rows = cfg->table_rows;
+    a.plan = plan;
+    a.B = B;
+    a.H = H;
+    a.scale = 1.0f;
+    a.status = out->dev_status;
+    return a;
+  };
+
+  // ---- 3. history side of every layer -> blocked K/V
+  char *kvbase = at<char>(ws, L.kv);
+  auto kbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i) * L.kv_layer); };
+  auto vbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i + 1) * L.kv_layer); };
+  const bool kvln = cfg->flags & STCA_FLAG_KV_LN;
+  for (int i = 0; i < M && batch->n_hist > 0; ++i) {
+    const stca_layer &l = w->layers[i];
+    ChainArgs a = base_args();
+    a.in_mode = IN_GATHER_CSR;
+    a.out_mode = OUT_KV;
+    a.ffn = true;
+    a.ln = kvln;
+    a.proj = true;
+    a.n_rows = L.max_blocks * 32;
+    a.ids = batch->hist_ids;
+    a.in_dump = i == 0 ? out->x_dump : nullptr;
+    if (bf) {
+      const PrepLayer &p = L.pl[i];
+      a.w1 = prep + p.kv_w1;
+      a.w3 = prep + p.kv_w3;
+      a.w2 = prep + p.kv_w2;
+      a.wp = prep + p.wkv;
+    } else {
+      a.w1 = l.kv.w1;
+      a.w3 = l.kv.w3;
+      a.w2 = l.kv.w2;
+      a.wp = l.wk;
+      a.wp2 = l.wv;
+    }
+    a.ln_g = l.kv.ln_g;
+    a.ln_b = l.kv.ln_b;
+    a.pn = 2 * d;
+    a.kbuf = kbuf(i);
+    a.vbuf = vbuf(i);
+    if ((e = chain(a))) return hip_fail(e, "history encoding");
+    if (out->kv_dump) {
+      char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;
+      char *vd = kd + (size_t)batch->n_hist * d * es;
+      e = launch_kv_relayout(cfg->dtype, kd, vd, kbuf(i), vbuf(i), plan, B, L.max_blocks, d, H, false, s);
+      if (e) return hip_fail(e, "kv dump");
+    }
+    if ((e = rec(2 + i))) return hip_fail(e, "stage event");
+  }
+  if (T == 0) return STCA_OK;
+
+  // ---- 4. query chain and attention, layer by layer
+  void *xt = at<void>(ws, L.xt);
+  char *ocat = at<char>(ws, L.ocat);
+  void *qs = at<void>(ws, L.qs);
+  void *qcur = at<void>(ws, L.qcur);
+  void *attnlo = at<void>(ws, L.attnlo);
+  for (int i = 0; i < M; ++i) {
+    const stca_layer &l = w->layers[i];
+    const PrepLayer *p = bf ? &L.pl[i] : nullptr;
+    void *qdst = out->q_dump ? (void *)((char *)out->q_dump + (size_t)i * T * d * es) : qs;
+    {  // Q = q W_Q / sqrt(d_h)
+      ChainArgs a = base_args();
+      a.out_mode = OUT_ROWS;
+      a.proj = true;
+      a.n_rows = T;
+      a.pn = d;
+      a.scale = qscale;
+      a.wp = bf ? (const void *)(prep + p->wq) : l.wq;
+      a.out = qdst;
+      a.ldo = d;
+      if (fusion) {
+        a.ffn = true;
+        a.ln = true;
+        a.ln_g = l.q.ln_g;
+        a.ln_b = l.q.ln_b;
+        a.w1 = bf ? (const void *)(prep + p->q_w1) : l.q.w1;
+        a.w3 = bf ? (const void *)(prep + p->q_w3) : l.q.w3;
+        a.w2 = bf ? (const void *)(prep + p->q_w2) : l.q.w2;
+        if (i == 0) {  // q1 = LN(SwiGLU(x_t)); x_t kept for the fusion concat
+          a.in_mode = IN_GATHER_IDS;
+          a.ids = batch->tgt_ids;
+          a.in_dump = xt;
+        } else {  // q = LN(SwiGLU([o_1..o_i | x_t] W_C))
+          a.in_mode = IN_PREGEMM;
+          a.a = ocat;
+          a.lda = M * d;
+          a.k1 = i * d;
+          a.a2 = xt;
+          a.lda2 = d;
+          a.k2 = d;
+          a.wpre = bf ? (const void *)(prep + p->wc) : l.wc;
+        }
+      } else {
+        a.in_mode = IN_DENSE;
+        a.a = i == 0 ? batch->q0 : qcur;
+        a.lda = d;
+      }
+      if ((e = chain(a))) return hip_fail(e, "query");
+    }
+    if ((e = rec(2 + M + 4 * i))) return hip_fail(e, "stage event");
+    {  // attention partials + merge
+      AttnArgs at_;
+      std::memset(&at_, 0, sizeof(at_));
+      at_.dtype = cfg->dtype;
+      at_.score = cfg->score;
+      at_.d = d;
+      at_.H = H;
+      at_.dh = dh;
+      at_.nb = L.nb;
+      at_.max_tgt = batch->max_tgt_per_user;
+      at_.grid_chunks = L.max_chunks;
+      at_.plan = plan;
+      at_.kbuf = kbuf(i);
+      at_.vbuf = vbuf(i);
+      at_.q = qdst;
+      at_.n_tgt = T;
+      at_.part_ml = at<float>(ws, L.part_ml);
+      at_.part_acc = at<float>(ws, L.part_acc);
+      at_.part_cnt = at<int>(ws, L.part_cnt);
+      at_.attn = out->attn ? out->attn + (size_t)i * T * d : at<float>(ws, L.attn32);
+      at_.attn_lo = attnlo;
+      at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
+      at_.B = B;
+      if (batch->n_hist == 0) at_.grid_chunks = 0;
+      if ((e = launch_attn_partial(at_, s))) return hip_fail(e, "attention");
+      if ((e = rec(3 + M + 4 * i))) return hip_fail(e, "stage event");
+      if ((e = launch_attn_merge(at_, s))) return hip_fail(e, "attention merge");
+      if ((e = rec(4 + M + 4 * i))) return hip_fail(e, "stage event");
+    }
+    const bool last = i + 1 == M;
+    {  // o = attn W_O -> fp32 output and the concat buffer
+      ChainArgs a = base_args();
+      a.in_mode = IN_DENSE;
+      a.out_mode = OUT_ROWS;
+      a.proj = true;
+      a.n_rows = T;
+      a.a = attnlo;
+      a.lda = d;
+      a.pn = d;
+      a.wp = bf ? (const void *)(prep + p->wo) : l.wo;
+      a.out = ocat + (size_t)i * d * es;
+      a.ldo = M * d;
+      if (out->o_layers) {
+        a.out32 = out->o_layers + (size_t)i * T * d;
+        a.ldo32 = d;
+      } else if (!fusion && last) {
+        a.out32 = out->z;
+        a.ldo32 = d;
+      }
+      if ((e = chain(a))) return hip_fail(e, "output projection");
+      if (!fusion && last && out->o_layers) {  // z = O_M
+        e = hipMemcpy2DAsync(out->z, d * sizeof(float), out->o_layers + (size_t)i * T * d,
+                             d * sizeof(float), d * sizeof(float), T, hipMemcpyDeviceToDevice, s);
+        if (e) return hip_fail(e, "z copy");
+      }
+    }
+    if (!fusion && !last) {  // Q_{i+1} = O_i R_i
+      ChainArgs a = base_args();
+      a.in_mode = IN_DENSE;
+      a.out_mode = OUT_ROWS;
+      a.proj = true;
+      a.n_rows = T;
+      a.a = ocat + (size_t)i * d * es;
+      a.lda = M * d;
+      a.pn = d;
+      a.wp = bf ? (const void *)(prep + p->r) : l.r;
+      a.out = qcur;
+      a.ldo = d;
+      if ((e = chain(a))) return hip_fail(e, "next-query map");
+    }
+    if ((e = rec(5 + M + 4 * i))) return hip_fail(e, "stage event");
+  }
+
+  // ---- 5. z = SwiGLU([o_1 .. o_M | x_t] W_Z) [+ LN]
+  if (fusion) {
+    ChainArgs a = base_args();
+    a.in_mode = IN_PREGEMM;
+    a.out_mode = OUT_ROWS;
+    a.ffn = true;
+    a.ln = cfg->flags & STCA_FLAG_Z_LN;
+    a.proj = false;
+    a.n_rows = T;
+    a.a = ocat;
+    a.lda = M * d;
+    a.k1 = M * d;
+    a.a2 = xt;
+    a.lda2 = d;
+    a.k2 = d;
+    a.wpre = bf ? (const void *)(prep + L.wz) : w->wz;
+    a.w1 = bf ? (const void *)(prep + L.z_w1) : w->z.w1;
+    a.w3 = bf ? (const void *)(prep + L.z_w3) : w->z.w3;
+    a.w2 = bf ? (const void *)(prep + L.z_w2) : w->z.w2;
+    a.ln_g = w->z.ln_g;
+    a.ln_b = w->z.ln_b;
+    a.out32 = out->z;
+    a.ldo32 = d;
+    if ((e = chain(a))) return hip_fail(e, "final z");
+  }
+  if ((e = rec(2 + 5 * M))) return hip_fail(e, "stage event");
+  return STCA_OK;
+}
+
+// ---------------------------------------------------------------- attention only
+static int attn_validate(const stca_attn_args *a) {
+  if (!a) return fail(STCA_ERR_INVALID_ARG, "args is NULL");
+  if (a->B < 0) return fail(STCA_ERR_INVALID_ARG, "B must be >= 0");
+  if (a->H <= 0 || a->d <= 0 || a->d % a->H) return fail(STCA_ERR_INVALID_ARG, "d must be a multiple of H");
+  const int dh = a->d / a->H;
+  if (dh != 32 && dh != 64) return fail(STCA_ERR_UNSUPPORTED, "d_h = %d unsupported", dh);
+  if (a->dtype != STCA_F32 && a->dtype != STCA_BF16) return fail(STCA_ERR_INVALID_ARG, "dtype unknown");
+  if (a->score != STCA_SCORE_SOFTMAX && a->score != STCA_SCORE_RELU)
+    return fail(STCA_ERR_INVALID_ARG, "score unknown");
+  if (a->chunk_keys < 0 || a->chunk_keys % 32) return fail(STCA_ERR_INVALID_ARG, "chunk_keys must be a multiple of 32");
+  if (a->n_hist < 0 || a->n_hist >= (1ll << 31) || a->n_tgt < 0 || a->n_tgt >= (1ll << 31))
+    return fail(STCA_ERR_INVALID_ARG, "n_hist / n_tgt outside [0, 2^31)");
+  if (a->max_tgt_per_user < 1 || a->max_tgt_per_user > 4096)
+    return fail(STCA_ERR_INVALID_ARG, "max_tgt_per_user outside 1..4096");
+  if (a->B > 0 && (!a->hist_offsets || !a->tgt_offsets)) return fail(STCA_ERR_INVALID_ARG, "offsets NULL");
+  if (a->n_tgt > 0 && (!a->q || !a->attn)) return fail(STCA_ERR_INVALID_ARG, "q / attn NULL");
+  if (a->n_hist > 0 && (!a->k || !a->v)) return fail(STCA_ERR_INVALID_ARG, "k / v NULL");
+  const void *ptrs[] = {a->hist_offsets, a->tgt_offsets, a->q, a->k, a->v, a->attn, a->active};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "pointer %p not 16-byte aligned", p);
+  return STCA_OK;
+}
+
+struct AttnLayout {
+  int nb;
+  int64_t mb, mc;
+  size_t plan, kv, kvl, ml, acc, cnt, total;
+};
+
+static AttnLayout attn_layout(const stca_attn_args *a) {
+  AttnLayout L;
+  const size_t es = a->dtype == STCA_BF16 ? 2 : 4;
+  L.nb = choose_nb(a->chunk_keys, a->n_hist, a->B, a->H, a->max_tgt_per_user);
+  L.mb = max_blocks(a->n_hist, a->B);
+  L.mc = max_chunks(a->n_hist, a->B, L.nb);
+  Carver cv;
+  L.plan = cv.take(4 * sizeof(int) * (size_t)(a->B + 1));
+  L.kvl = (size_t)L.mb * 32 * a->d * es;
+  L.kv = cv.take(2 * L.kvl);
+  const size_t np = (size_t)L.mc * a->H * a->max_tgt_per_user;
+  L.ml = cv.take(np * 2 * sizeof(float));
+  L.acc = cv.take(np * (a->d / a->H) * sizeof(float));
+  L.cnt = cv.take(np * sizeof(int));
+  L.total = cv.off;
+  return L;
+}
+
+int stca_attention_workspace_size(const stca_attn_args *a, size_t *bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(STCA_ERR_INVALID_ARG, "bytes is NULL");
+  int r = attn_validate(a);
+  if (r) return r;
+  *bytes = attn_layout(a).total;
+  return STCA_OK;
+}
+
+int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *stream) {
+  g_err[0] = 0;
+  int r = attn_validate(a);
+  if (r) return r;
+  const AttnLayout L = attn_layout(a);
+  if (ws_bytes < L.total || (!ws && L.total))
+    return fail(STCA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  if (ws && !aligned16(ws)) return fail(STCA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  if (a->B == 0 || a->n_tgt == 0) return STCA_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Plan plan;
+  plan.hoff = at<int>(ws, L.plan);
+  plan.toff = plan.hoff + (a->B + 1);
+  plan.pblk = plan.toff + (a->B + 1);
+  plan.coff = plan.pblk + (a->B + 1);
+  hipError_t e = launch_plan(a->hist_offsets, a->tgt_offsets, a->B, a->n_hist, a->n_tgt,
+                             a->max_tgt_per_user, L.nb, plan, a->dev_status, s);
+  if (e) return hip_fail(e, "planner");
+  char *kv = at<char>(ws, L.kv);
+  if (a->n_hist > 0) {
+    e = launch_kv_relayout(a->dtype, a->k, a->v, kv, kv + L.kvl, plan, a->B, L.mb, a->d, a->H, true, s);
+    if (e) return hip_fail(e, "relayout");
+  }
+  AttnArgs at_;
+  std::memset(&at_, 0, sizeof(at_));
+  at_.dtype = a->dtype;
+  at_.score = a->score;
+  at_.d = a->d;
+  at_.H = a->H;
+  at_.dh = a->d / a->H;
+  at_.nb = L.nb;
+  at_.max_tgt = a->max_tgt_per_user;
+  at_.grid_chunks = a->n_hist > 0 ? L.mc : 0;
+  at_.plan = plan;
+  at_.kbuf = kv;
+  at_.vbuf = kv + L.kvl;
+  at_.q = a->q;
+  at_.n_tgt = a->n_tgt;
+  at_.part_ml = at<float>(ws, L.ml);
+  at_.part_acc = at<float>(ws, L.acc);
+  at_.part_cnt = at<int>(ws, L.cnt);
+  at_.attn = a->attn;
+  at_.active = a->active;
+  at_.B = a->B;
+  if ((e = launch_attention(at_, s))) return hip_fail(e, "attention");
+  return STCA_OK;
+}
+
+}  // extern "C"

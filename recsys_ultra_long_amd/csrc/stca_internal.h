@@ -1,0 +1,126 @@
+// stca_internal.h -- host-side launcher interface between the C ABI layer
+// (stca_api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace stca {
+
+// Device-side batch plan written by the planner kernel (all int32):
+//   hoff[B+1]  sanitised history offsets (all zero when the CSR is bad)
+//   toff[B+1]  sanitised target offsets
+//   pblk[B+1]  first 32-key block of each user in the padded K/V layout
+//   coff[B+1]  first split-L chunk of each user
+struct Plan {
+  int *hoff, *toff, *pblk, *coff;
+};
+
+// Upper bound (host) on the padded blocks / chunks of a batch.
+inline int64_t max_blocks(int64_t n_hist, int B) { return (n_hist + 31) / 32 + B; }
+inline int64_t max_chunks(int64_t n_hist, int B, int nb) {
+  return (max_blocks(n_hist, B) + nb - 1) / nb + B;
+}
+
+hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
+                       int64_t n_tgt, int max_tgt, int nb, Plan plan, int *status,
+                       hipStream_t s);
+
+// ------------------------------------------------------------ row chain
+// One launch computes, for a set of rows,
+//   input -> [SwiGLU FFN] -> [LN] -> [projection (scaled)] -> output
+// Input modes:
+enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3 };
+// Output modes:
+enum OutMode { OUT_KV = 0, OUT_ROWS = 1 };
+
+struct ChainArgs {
+  int in_mode, out_mode;
+  bool ffn, ln, proj;
+  int d, hidden;
+  int64_t n_rows;           // IN_GATHER_IDS / DENSE / PREGEMM: rows; CSR: max blocks * 32
+  // gather
+  const void *table;
+  int64_t table_rows;
+  const int *ids;           // per-row ids (IDS) or history ids (CSR)
+  Plan plan;
+  int B;
+  // dense / pre-GEMM input (config dtype)
+  const void *a;            // dense rows, or pre-GEMM segment 1
+  int lda;
+  const void *a2;           // pre-GEMM segment 2 (x_t rows)
+  int lda2;
+  int k1, k2;               // pre-GEMM segment widths (multiples of 32)
+  const void *wpre;         // pre-GEMM weight [k1+k2, d] (bf16: prepared [d, k1+k2])
+  void *in_dump;            // optional copy of the input rows (IDS: [n_rows, d]; CSR: per token)
+  // FFN (bf16: prepared transposed matrices)
+  const void *w1, *w3, *w2;
+  const float *ln_g, *ln_b;
+  // projection
+  const void *wp;           // [d, pn] (bf16: prepared [pn, d]; OUT_KV: [W_K|W_V]^T)
+  const void *wp2;          // fp32 OUT_KV: W_V (wp is W_K)
+  int pn;
+  float scale;
+  // outputs
+  void *out;                // OUT_ROWS, config dtype [n_rows, ldo]
+  int ldo;
+  float *out32;             // OUT_ROWS optional fp32 copy [n_rows, ldo32]
+  int ldo32;
+  void *kbuf, *vbuf;        // OUT_KV blocked layout
+  int H;
+  int *status;
+};
+
+hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s);
+hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
+
+// Batched bf16 transpose: src [rows, cols] -> dst[c][dst_col0 + r] with row
+// pitch ld_dst (so several transposes can fill one prepared matrix).
+struct TransposeDesc {
+  const bf16_t *src;
+  bf16_t *dst;
+  int rows, cols, ld_dst, dst_col0;
+};
+constexpr int kMaxTransposes = 48;
+struct TransposeBatch {
+  TransposeDesc m[kMaxTransposes];
+};
+hipError_t launch_transpose_batch(const TransposeBatch &tb, int n, hipStream_t s);
+
+// ------------------------------------------------------------ attention
+struct AttnArgs {
+  int dtype;                // 0 fp32, 1 bf16
+  int score;                // 0 softmax, 1 relu
+  int d, H, dh;
+  int nb;                   // blocks per chunk
+  int max_tgt;
+  int64_t grid_chunks;      // host bound on chunks
+  Plan plan;
+  const void *kbuf, *vbuf;  // blocked K/V of one layer
+  const void *q;            // [n_tgt, d] scaled queries
+  int64_t n_tgt;
+  float *part_ml;           // [chunks, H, max_tgt, 2]
+  float *part_acc;          // [chunks, H, max_tgt, dh]
+  int *part_cnt;            // [chunks, H, max_tgt]
+  float *attn;              // [n_tgt, d] fp32 (required)
+  void *attn_lo;            // [n_tgt, d] config dtype copy (optional)
+  int *active;              // [n_tgt, H] (optional)
+  int B;
+};
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);  // partials + merge
+hipError_t launch_attn_partial(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s);
+
+// Row-major K, V ([n_hist, d]) -> blocked K/V layout (for stca_attention) and
+// the reverse (for kv_dump).
+hipError_t launch_kv_relayout(int dtype, const void *k, const void *v, void *kbuf, void *vbuf,
+                              Plan plan, int B, int64_t max_blocks, int d, int H, bool to_blocked,
+                              hipStream_t s);
+
+hipError_t launch_copy_rows(int dtype, const void *src, int lds, void *dst, int ldd,
+                            int64_t rows, int cols, hipStream_t s);
+
+}  // namespace stca

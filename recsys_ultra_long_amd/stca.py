@@ -1,0 +1,327 @@
+"""Thin Python binding of ``libstca.so`` (C ABI in ``include/stca.h``).
+
+Argument marshalling only: every step of the forward runs in the HIP
+library.  PyTorch supplies device memory and the current HIP stream.  There
+is no fallback: if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libstca.so")
+
+# enums (mirror include/stca.h)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+SCORE = {"softmax": 0, "relu": 1}
+QMODE = {"fusion": 0, "linear": 1}
+PATH = {"staged": 0, "fused": 1}
+FLAG_KV_LN, FLAG_Z_LN = 1, 2
+DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
+
+EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
+           "stca_attention", "stca_status_string", "stca_last_error", "stca_version")
+
+_vp = C.c_void_p
+
+
+class Config(C.Structure):
+    _fields_ = [("B", C.c_int32), ("d", C.c_int32), ("H", C.c_int32), ("hidden", C.c_int32),
+                ("M", C.c_int32), ("table_rows", C.c_int64), ("dtype", C.c_int32),
+                ("score", C.c_int32), ("qmode", C.c_int32), ("path", C.c_int32),
+                ("flags", C.c_int32), ("chunk_keys", C.c_int32)]
+
+
+class Batch(C.Structure):
+    _fields_ = [("hist_offsets", _vp), ("hist_ids", _vp), ("tgt_offsets", _vp), ("tgt_ids", _vp),
+                ("q0", _vp), ("table", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
+                ("max_tgt_per_user", C.c_int32)]
+
+
+class Ffn(C.Structure):
+    _fields_ = [("w1", _vp), ("w3", _vp), ("w2", _vp), ("ln_g", _vp), ("ln_b", _vp)]
+
+
+class Layer(C.Structure):
+    _fields_ = [("kv", Ffn), ("q", Ffn), ("wk", _vp), ("wv", _vp), ("wq", _vp), ("wo", _vp),
+                ("wc", _vp), ("r", _vp)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("layers", C.POINTER(Layer)), ("z", Ffn), ("wz", _vp)]
+
+
+class Outputs(C.Structure):
+    _fields_ = [("z", _vp), ("o_layers", _vp), ("attn", _vp), ("active", _vp), ("q_dump", _vp),
+                ("kv_dump", _vp), ("x_dump", _vp), ("dev_status", _vp),
+                ("stage_events", C.POINTER(_vp)), ("n_stage_events", C.c_int32)]
+
+
+class AttnArgs(C.Structure):
+    _fields_ = [("B", C.c_int32), ("d", C.c_int32), ("H", C.c_int32), ("dtype", C.c_int32),
+                ("score", C.c_int32), ("chunk_keys", C.c_int32), ("hist_offsets", _vp),
+                ("tgt_offsets", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
+                ("max_tgt_per_user", C.c_int32), ("q", _vp), ("k", _vp), ("v", _vp),
+                ("attn", _vp), ("active", _vp), ("dev_status", _vp)]
+
+
+_LIB = None
+
+
+class StcaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{status_string(code)}: {msg}")
+        self.code = code
+
+
+def load() -> C.CDLL:
+    """Load libstca.so from the package directory (raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m recsys_ultra_long_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        lib.stca_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(C.c_size_t)]
+        lib.stca_forward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights),
+                                     C.POINTER(Outputs), _vp, C.c_size_t, _vp]
+        lib.stca_attention_workspace_size.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
+        lib.stca_attention.argtypes = [C.POINTER(AttnArgs), _vp, C.c_size_t, _vp]
+        lib.stca_status_string.restype = C.c_char_p
+        lib.stca_status_string.argtypes = [C.c_int]
+        lib.stca_last_error.restype = C.c_char_p
+        lib.stca_version.restype = C.c_int
+        for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
+                  "stca_attention"):
+            getattr(lib, f).restype = C.c_int
+        _LIB = lib
+    return _LIB
+
+
+def status_string(code: int) -> str:
+    return load().stca_status_string(code).decode()
+
+
+def last_error() -> str:
+    return load().stca_last_error().decode()
+
+
+def _check(code: int):
+    if code != OK:
+        raise StcaError(code, last_error())
+
+
+# ---------------------------------------------------------------- device data
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class DeviceProblem:
+    """A problem's arrays on the GPU (torch tensors; bf16 kept as raw int16 bits)."""
+    cfg: Config
+    hist_offsets: object
+    hist_ids: object
+    tgt_offsets: object
+    tgt_ids: object
+    q0: object
+    table: object
+    layers: list          # per layer dict of device tensors (same keys as inputs.Problem)
+    z: Optional[dict]
+    wz: object
+    n_hist: int
+    n_tgt: int
+    max_tgt: int
+
+
+def _dev(a, device):
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def upload(p, device="cuda", table=None, path="staged", chunk_keys=0) -> DeviceProblem:
+    """Copy an ``inputs.Problem`` to the device.  ``table`` may be a device
+    tensor already holding the embedding table (avoids a second copy)."""
+    import torch
+    sp = p.spec
+    flags = (FLAG_KV_LN if sp.kv_ln else 0) | (FLAG_Z_LN if sp.z_ln else 0)
+    cfg = Config(B=sp.B, d=sp.d, H=sp.H, hidden=sp.hidden, M=sp.M, table_rows=sp.table_rows,
+                 dtype=BF16 if sp.dtype == "bf16" else F32, score=SCORE[sp.score],
+                 qmode=QMODE[sp.qmode], path=PATH[path], flags=flags, chunk_keys=chunk_keys)
+
+    def conv(w):
+        if w is None:
+            return None
+        if isinstance(w, dict):
+            return {k: conv(v) for k, v in w.items()}
+        return _dev(w, device)
+    if table is None:
+        table = _dev(p.table, device)
+    m = np.diff(p.tgt_offsets)
+    return DeviceProblem(cfg, _dev(p.hist_offsets, device), _dev(p.hist_ids, device),
+                         _dev(p.tgt_offsets, device), _dev(p.tgt_ids, device), _dev(p.q0, device),
+                         table, [conv(l) for l in p.layers], conv(p.z), _dev(p.wz, device),
+                         p.n_hist, p.n_tgt, max(1, int(m.max()) if len(m) else 1))
+
+
+def _ffn(f) -> Ffn:
+    if f is None:
+        return Ffn()
+    return Ffn(_ptr(f["w1"]), _ptr(f["w3"]), _ptr(f["w2"]), _ptr(f.get("ln_g")), _ptr(f.get("ln_b")))
+
+
+def _structs(dp: DeviceProblem):
+    layers = (Layer * len(dp.layers))()
+    for i, l in enumerate(dp.layers):
+        layers[i] = Layer(_ffn(l["kv"]), _ffn(l.get("q")), _ptr(l["wk"]), _ptr(l["wv"]),
+                          _ptr(l["wq"]), _ptr(l["wo"]), _ptr(l.get("wc")), _ptr(l.get("r")))
+    w = Weights(layers, _ffn(dp.z), _ptr(dp.wz))
+    b = Batch(_ptr(dp.hist_offsets), _ptr(dp.hist_ids), _ptr(dp.tgt_offsets), _ptr(dp.tgt_ids),
+              _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt)
+    return b, w, layers
+
+
+def workspace_bytes(dp: DeviceProblem) -> int:
+    lib = load()
+    b, _, _ = _structs(dp)
+    n = C.c_size_t(0)
+    _check(lib.stca_workspace_size(C.byref(dp.cfg), C.byref(b), C.byref(n)))
+    return n.value
+
+
+class StageEvents:
+    """hipEvent_t handles for the stage-boundary timing of ``stca_forward``
+    (created with the HIP runtime directly so they live on the same stream as
+    the library's kernels; read with ``elapsed`` after the stream completes)."""
+
+    def __init__(self, n: int):
+        self.hip = C.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(_vp)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), _vp, _vp]
+        self.hip.hipEventDestroy.argtypes = [_vp]
+        self.n = n
+        self.arr = (_vp * n)()
+        for i in range(n):
+            ev = _vp()
+            if self.hip.hipEventCreate(C.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = ev
+        self.ptr = C.cast(self.arr, C.POINTER(_vp))
+
+    def elapsed(self, i: int, j: int) -> float:
+        """Milliseconds between boundary i and boundary j (after synchronisation)."""
+        ms = C.c_float(0)
+        r = self.hip.hipEventElapsedTime(C.byref(ms), self.arr[i], self.arr[j])
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime({i},{j}) failed: {r}")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            if self.arr[i]:
+                self.hip.hipEventDestroy(self.arr[i])
+                self.arr[i] = None
+
+
+def n_stage_events(M: int) -> int:
+    return 5 * M + 3
+
+
+class Forward:
+    """Reusable forward call: outputs and workspace are allocated once."""
+
+    def __init__(self, dp: DeviceProblem, want=("o", "attn", "active"), dumps=(), stream=None,
+                 events: Optional[StageEvents] = None):
+        import torch
+        self.dp = dp
+        self.lib = load()
+        cfg = dp.cfg
+        dev = dp.table.device
+        T, d, M, H = dp.n_tgt, cfg.d, cfg.M, cfg.H
+        lo = torch.int16 if cfg.dtype == BF16 else torch.float32
+        self.z = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.o = torch.empty((M, T, d), dtype=torch.float32, device=dev) if "o" in want else None
+        self.attn = torch.empty((M, T, d), dtype=torch.float32, device=dev) if "attn" in want else None
+        self.active = (torch.empty((M, T, H), dtype=torch.int32, device=dev)
+                       if ("active" in want and cfg.score == 1) else None)
+        self.q_dump = torch.empty((M, T, d), dtype=lo, device=dev) if "q" in dumps else None
+        self.kv_dump = (torch.empty((M, 2, dp.n_hist, d), dtype=lo, device=dev)
+                        if "kv" in dumps else None)
+        self.x_dump = torch.empty((dp.n_hist, d), dtype=lo, device=dev) if "x" in dumps else None
+        self.status = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.b, self.w, self._layers = _structs(dp)
+        self.out = Outputs(_ptr(self.z), _ptr(self.o), _ptr(self.attn), _ptr(self.active),
+                           _ptr(self.q_dump), _ptr(self.kv_dump), _ptr(self.x_dump),
+                           _ptr(self.status))
+        if events is not None:
+            self.out.stage_events = events.ptr
+            self.out.n_stage_events = events.n
+        n = C.c_size_t(0)
+        _check(self.lib.stca_workspace_size(C.byref(cfg), C.byref(self.b), C.byref(n)))
+        self.ws_bytes = n.value
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.stream = stream
+
+    def __call__(self):
+        import torch
+        s = self.stream if self.stream is not None else torch.cuda.current_stream()
+        _check(self.lib.stca_forward(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
+                                     C.byref(self.out), self.ws.data_ptr(), self.ws_bytes,
+                                     s.cuda_stream))
+        return self
+
+    def results(self) -> dict:
+        r = {"z": self.z, "o": self.o, "attn": self.attn, "active": self.active,
+             "q": self.q_dump, "kv": self.kv_dump, "x": self.x_dump, "status": self.status}
+        return {k: v for k, v in r.items() if v is not None}
+
+
+def forward(dp: DeviceProblem, want=("o", "attn", "active"), dumps=()) -> dict:
+    return Forward(dp, want, dumps)().results()
+
+
+def attention(q, k, v, hist_offsets, tgt_offsets, H: int, score: str = "softmax",
+              max_tgt: Optional[int] = None, chunk_keys: int = 0):
+    """The attention core alone (``stca_attention``) on device tensors.
+    q: [T, d] (already scaled by 1/sqrt(d_h)), k/v: [n_hist, d]; fp32, or
+    bf16 bits as int16.  Returns (attn fp32 [T, d], active int32 [T, H] or None,
+    dev_status)."""
+    import torch
+    lib = load()
+    T, d = q.shape
+    dtype = BF16 if q.dtype in (torch.int16, torch.bfloat16) else F32
+    B = hist_offsets.numel() - 1
+    if max_tgt is None:
+        max_tgt = max(1, int((tgt_offsets[1:] - tgt_offsets[:-1]).max().item())) if B > 0 else 1
+    attn = torch.empty((T, d), dtype=torch.float32, device=q.device)
+    active = torch.empty((T, H), dtype=torch.int32, device=q.device) if score == "relu" else None
+    status = torch.zeros(4, dtype=torch.int32, device=q.device)
+    a = AttnArgs(B=B, d=d, H=H, dtype=dtype, score=SCORE[score], chunk_keys=chunk_keys,
+                 hist_offsets=_ptr(hist_offsets), tgt_offsets=_ptr(tgt_offsets),
+                 n_hist=k.shape[0], n_tgt=T, max_tgt_per_user=max_tgt, q=_ptr(q), k=_ptr(k),
+                 v=_ptr(v), attn=_ptr(attn), active=_ptr(active), dev_status=_ptr(status))
+    n = C.c_size_t(0)
+    _check(lib.stca_attention_workspace_size(C.byref(a), C.byref(n)))
+    ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=q.device)
+    _check(lib.stca_attention(C.byref(a), ws.data_ptr(), n.value,
+                              torch.cuda.current_stream().cuda_stream))
+    return attn, active, status
+
+
+def to_numpy_stored(t) -> np.ndarray:
+    """Device tensor -> numpy in the stored convention (bf16 bits as uint16)."""
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    return a
