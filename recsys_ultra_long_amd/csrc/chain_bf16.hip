@@ -15,6 +15,8 @@
 // prepared transposes ([out, in], k contiguous) straight from L2 into MFMA
 // operand registers.  All contractions are 32x32x16 bf16 MFMA with fp32
 // accumulation; LN statistics are fp32.
+#include <algorithm>
+
 #include "stca_internal.h"
 
 namespace stca {
@@ -25,19 +27,19 @@ constexpr int kThreads = 256; // 4 waves
 constexpr int kHC = 128;      // hidden columns per chunk
 constexpr int kPad = 8;       // bf16 elements of row padding in LDS (16 bytes)
 
-// acc[i][j] += A(rows of tile i) * B(cols of tile j)^T over k in [0, K).
-// ar[i] / br[j] point at the lane's row (A) / column (B) already offset by
-// the lane's 16-element k group; each 32-wide k block is two MFMAs.
+// acc[i][j] += A(tile i) * B(tile j)^T over k in [0, K) with A a packed
+// weight (ar[i]: the lane's fragment of tile i at the first k block) and B
+// plain rows (br[j]: the lane's row, already offset by its 16-element k group).
 template <int RT, int CT>
-DEV void mma(f32x16 (&acc)[RT][CT], const bf16_t *const (&ar)[RT], const bf16_t *const (&br)[CT],
-             int K) {
+DEV void mma_packed_a(f32x16 (&acc)[RT][CT], const bf16_t *const (&ar)[RT],
+                      const bf16_t *const (&br)[CT], int K) {
 #pragma unroll 1
   for (int k0 = 0; k0 < K; k0 += 32) {
     bf16x8 a[RT][2], b[CT][2];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      a[i][0] = ld8(ar[i] + k0);
-      a[i][1] = ld8(ar[i] + k0 + 8);
+      a[i][0] = ld8(ar[i] + k0 * 32);
+      a[i][1] = ld8(ar[i] + k0 * 32 + 512);
     }
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
@@ -45,12 +47,88 @@ DEV void mma(f32x16 (&acc)[RT][CT], const bf16_t *const (&ar)[RT], const bf16_t 
       b[j][1] = ld8(br[j] + k0 + 8);
     }
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < CT; ++j) {
-        acc[i][j] = mfma32(a[i][0], b[j][0], acc[i][j]);
-        acc[i][j] = mfma32(a[i][1], b[j][1], acc[i][j]);
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) acc[i][j] = mfma32(a[i][h], b[j][h], acc[i][j]);
+  }
+}
+
+// ---------------------------------------------------------------- weight ring
+// The weights of a tile are consumed as a fixed sequence of phases (hidden
+// chunk c: W1|W3 rows, then W2 columns; then the projection).  Their 32-wide
+// k blocks stream through a 4-slot register ring that is always filled three
+// blocks ahead -- across phase boundaries too, so the first blocks of the next
+// phase are already in flight while a phase finishes, its epilogue runs and
+// the workgroup synchronises.  Every phase has a multiple of 4 blocks, so a
+// phase always starts at ring slot 0 and all slot indices are compile time.
+struct Ring {
+  bf16x8 v[4][2][2];  // [slot][tile][half]
+};
+
+// p[t]: the lane's fragment of tile t at the phase's first k block (packed
+// weights: the two halves of a k block are 512 elements apart, blocks 1024).
+template <int NG>
+DEV void ring_load(Ring &r, int slot, const bf16_t *const (&p)[NG], int kb) {
+#pragma unroll
+  for (int t = 0; t < NG; ++t) {
+    r.v[slot][t][0] = ld8(p[t] + kb * 1024);
+    r.v[slot][t][1] = ld8(p[t] + kb * 1024 + 512);
+  }
+}
+
+// Prime the ring with blocks 0..2 of the first phase.
+template <int NG>
+DEV void ring_prime(Ring &r, const bf16_t *const (&p)[NG]) {
+#pragma unroll
+  for (int kb = 0; kb < 3; ++kb) ring_load<NG>(r, kb, p, kb);
+}
+
+// acc[i][j] += A_i B_j^T over NK blocks.  GA: A is the streamed (global)
+// operand, else B is.  `lp` are the LDS operand's tile pointers.  While the
+// last three blocks are consumed, blocks 0..2 of the next phase (pointers
+// `np`, two tiles; NGN = 0 when nothing follows) are loaded into the ring.
+template <int RT, int CT, int NK, bool GA, int NGN>
+DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ? RT : CT],
+               const bf16_t *const (&lp)[GA ? CT : RT], const bf16_t *const (&np)[2]) {
+  static_assert(NK % 4 == 0 && NK >= 4, "phase length must be a multiple of 4 blocks");
+  constexpr int NG = GA ? RT : CT;
+  constexpr int NL = GA ? CT : RT;
+  bf16x8 lo[2][NL][2];  // LDS operand, double-buffered one block ahead
+#pragma unroll
+  for (int t = 0; t < NL; ++t) {
+    lo[0][t][0] = ld8(lp[t]);
+    lo[0][t][1] = ld8(lp[t] + 8);
+  }
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) {
+    const int nb = kb + 3;
+    if (nb < NK) {
+      ring_load<NG>(ring, nb % 4, gp, nb);
+    } else if (NGN > 0) {
+      ring_load<2>(ring, nb % 4, np, nb - NK);
+    }
+    if (kb + 1 < NK) {
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        lo[(kb + 1) & 1][t][0] = ld8(lp[t] + (kb + 1) * 32);
+        lo[(kb + 1) & 1][t][1] = ld8(lp[t] + (kb + 1) * 32 + 8);
       }
+    }
+    // keep the prefetches issued ahead of this block's matrix work
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+          const bf16x8 av = GA ? ring.v[kb % 4][i][h] : lo[kb & 1][i][h];
+          const bf16x8 bv = GA ? lo[kb & 1][j][h] : ring.v[kb % 4][j][h];
+          acc[i][j] = mfma32(av, bv, acc[i][j]);
+        }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -65,10 +143,14 @@ DEV void zero(f32x16 (&acc)[RT][CT]) {
 }
 
 template <int D, int IN, bool FFN, bool LN, bool PROJ, int OUT>
-__global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
+__global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(ChainArgs a) {
+  // Every contraction is computed "feature-major": MFMA rows are output
+  // features, MFMA columns are the 64 rows (tokens) of the tile.  A lane then
+  // holds 4 consecutive features of one token, so LDS / global stores are
+  // 8 or 16 bytes and the LN statistics of a token are mostly an in-lane sum.
   constexpr int XLD = D + kPad;
   constexpr int GLD = kHC + kPad;
-  constexpr int CTY = D / 128;  // 32-col tiles per wave for d-wide outputs
+  constexpr int FT = D / 128;  // 32-feature tiles per wave for d-wide outputs
   __shared__ __attribute__((aligned(16))) bf16_t xs[kRows * XLD];
   __shared__ __attribute__((aligned(16))) bf16_t gs[FFN ? 2 : 1][FFN ? kRows * GLD : 8];
   __shared__ float red[2][4][kRows];
@@ -78,9 +160,55 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
-  const int kg = (lane >> 5) * 16;  // lane's k offset inside a 32-wide k block
+  const int hi = lane >> 5;         // which half of the wave
+  const int kg = hi * 16;           // lane's k offset inside a 32-wide k block
   const int64_t row0 = (int64_t)blockIdx.x * kRows;
   const bf16_t *table = (const bf16_t *)a.table;
+  // MFMA-column (token) operands read from LDS rows
+  const bf16_t *bx[2] = {xs + l32 * XLD + kg, xs + (32 + l32) * XLD + kg};
+
+  // weight rows streamed through the ring (each pointer: this lane's row + kg)
+  constexpr int YT = FT < 2 ? FT : 2;  // weight tiles per phase
+  constexpr int NSP = FT / YT;         // phases per d-wide contraction
+  const bf16_t *w1 = (const bf16_t *)a.w1, *w3 = (const bf16_t *)a.w3, *w2 = (const bf16_t *)a.w2;
+  const bf16_t *wp = (const bf16_t *)a.wp;
+  const int nkD = D / 32, nkH = a.hidden / 32;
+  auto g_ptrs = [&](int hc, const bf16_t *(&o)[2]) {
+    const int rt = hc * (kHC / 32) + w;
+    o[0] = w1 + frag_off(rt, 0, nkD, 0, lane);
+    o[1] = w3 + frag_off(rt, 0, nkD, 0, lane);
+  };
+  auto y_ptrs = [&](int hc, int sp, auto &o) {
+#pragma unroll
+    for (int t = 0; t < (int)(sizeof(o) / sizeof(o[0])); ++t) {
+      const int tt = t < YT ? t : YT - 1;
+      o[t] = w2 + frag_off(w * FT + sp * YT + tt, hc * (kHC / 32), nkH, 0, lane);
+    }
+  };
+  // projection weight tiles: rows [tile0 * 32, ...) of the packed W^T
+  auto proj_ptrs = [&](int sp, int tile0, const bf16_t *(&o)[YT]) {
+#pragma unroll
+    for (int t = 0; t < YT; ++t) o[t] = wp + frag_off(tile0 + w * FT + sp * YT + t, 0, nkD, 0, lane);
+  };
+  auto proj_ptrs2 = [&](int sp, int tile0, const bf16_t *(&o)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int tt = t < YT ? t : YT - 1;
+      o[t] = wp + frag_off(tile0 + w * FT + sp * YT + tt, 0, nkD, 0, lane);
+    }
+  };
+  auto first_proj_ptrs = [&](const bf16_t *(&o)[2]) {
+    if (PROJ) proj_ptrs2(0, 0, o);
+    else o[0] = o[1] = w1;  // nothing follows: harmless valid address
+  };
+  Ring ring;
+  // the weights do not depend on the rows: start streaming them before the gather
+  if (IN != IN_PREGEMM) {
+    const bf16_t *p0[2];
+    if (FFN) g_ptrs(0, p0);
+    else first_proj_ptrs(p0);
+    ring_prime<2>(ring, p0);
+  }
 
   int total_blocks = 0;
   if (IN == IN_GATHER_CSR) {
@@ -136,161 +264,185 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       if (row0 + r < a.n_rows) v = *reinterpret_cast<const u32x4 *>(src + (row0 + r) * a.lda + c);
       *reinterpret_cast<u32x4 *>(xs + r * XLD + c) = v;
     }
-  } else {  // IN_PREGEMM: xs = bf16([seg1 | seg2] W_pre)
-    f32x16 acc[2][CTY];
+  } else {  // IN_PREGEMM: xs = bf16([seg1 | seg2] W_pre), computed as W_pre^T [seg1|seg2]^T
+    f32x16 acc[FT][2];
     zero(acc);
     const bf16_t *wpre = (const bf16_t *)a.wpre;
-    const int kt = a.k1 + a.k2;
-    const bf16_t *br[CTY];
+    const int nkt = (a.k1 + a.k2) / 32;
+    const bf16_t *aw[FT];
 #pragma unroll
-    for (int j = 0; j < CTY; ++j) br[j] = wpre + (int64_t)(w * (D / 4) + j * 32 + l32) * kt + kg;
-    const bf16_t *ar[2];
+    for (int i = 0; i < FT; ++i) aw[i] = wpre + frag_off(w * FT + i, 0, nkt, 0, lane);
     int64_t rr[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rr[i] = row0 + i * 32 + l32;
-      if (rr[i] >= a.n_rows) rr[i] = a.n_rows - 1;  // clamp: result discarded
+    for (int j = 0; j < 2; ++j) {
+      rr[j] = row0 + j * 32 + l32;
+      if (rr[j] >= a.n_rows) rr[j] = a.n_rows - 1;  // clamp: result discarded
     }
+    const bf16_t *bt[2];
     if (a.k1 > 0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) ar[i] = (const bf16_t *)a.a + rr[i] * a.lda + kg;
-      mma<2, CTY>(acc, ar, br, a.k1);
+      for (int j = 0; j < 2; ++j) bt[j] = (const bf16_t *)a.a + rr[j] * a.lda + kg;
+      mma_packed_a<FT, 2>(acc, aw, bt, a.k1);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ar[i] = (const bf16_t *)a.a2 + rr[i] * a.lda2 + kg;
+    for (int j = 0; j < 2; ++j) bt[j] = (const bf16_t *)a.a2 + rr[j] * a.lda2 + kg;
 #pragma unroll
-    for (int j = 0; j < CTY; ++j) br[j] += a.k1;
-    mma<2, CTY>(acc, ar, br, a.k2);
+    for (int i = 0; i < FT; ++i) aw[i] += (int64_t)(a.k1 / 32) * 1024;
+    mma_packed_a<FT, 2>(acc, aw, bt, a.k2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FT; ++i)
 #pragma unroll
-      for (int j = 0; j < CTY; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          xs[(i * 32 + c32_row(lane, e)) * XLD + w * (D / 4) + j * 32 + l32] = f2bf(acc[i][j][e]);
+        for (int q = 0; q < 4; ++q) {
+          const int f = w * (D / 4) + i * 32 + 8 * q + 4 * hi;
+          u32x2 v = {pack_bf2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                     pack_bf2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+          *reinterpret_cast<u32x2 *>(xs + (j * 32 + l32) * XLD + f) = v;
+        }
+    const bf16_t *p0[2];
+    if (FFN) g_ptrs(0, p0);
+    else first_proj_ptrs(p0);
+    ring_prime<2>(ring, p0);
   }
   __syncthreads();
 
   // ------------------------------------------------------------ SwiGLU FFN
   if (FFN) {
-    f32x16 y[2][CTY];
-    zero(y);
-    const bf16_t *w1 = (const bf16_t *)a.w1, *w3 = (const bf16_t *)a.w3, *w2 = (const bf16_t *)a.w2;
-    const bf16_t *ax[2] = {xs + l32 * XLD + kg, xs + (32 + l32) * XLD + kg};
+    f32x16 y[NSP][YT][2];  // Y^T: this wave's D/4 features x 64 tokens
+#pragma unroll
+    for (int sp = 0; sp < NSP; ++sp) zero(y[sp]);
     const int nchunk = a.hidden / kHC;
     for (int hc = 0; hc < nchunk; ++hc) {
       bf16_t *g = gs[hc & 1];
-      {  // g = SiLU(X W1) * (X W3) for this wave's 32 hidden columns
+      {  // G^T = SiLU(W1^T X^T) * (W3^T X^T) for this wave's 32 hidden units
         f32x16 acc[2][2];
         zero(acc);
-        const int col = hc * kHC + w * 32 + l32;
-        const bf16_t *br[2] = {w1 + (int64_t)col * D + kg, w3 + (int64_t)col * D + kg};
-        mma<2, 2>(acc, ax, br, D);
+        const bf16_t *gp[2], *nx[2];
+        g_ptrs(hc, gp);
+        y_ptrs(hc, 0, nx);
+        phase<2, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            g[(i * 32 + c32_row(lane, e)) * GLD + w * 32 + l32] =
-                f2bf(silu_fast(acc[i][0][e]) * acc[i][1][e]);
+          for (int q = 0; q < 4; ++q) {
+            float gv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              gv[r] = silu_fast(acc[0][j][4 * q + r]) * acc[1][j][4 * q + r];
+            u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
+            *reinterpret_cast<u32x2 *>(g + (j * 32 + l32) * GLD + w * 32 + 8 * q + 4 * hi) = v;
+          }
       }
       __syncthreads();
-      {  // y += g W2[chunk rows]
-        const bf16_t *ag[2] = {g + l32 * GLD + kg, g + (32 + l32) * GLD + kg};
-        const bf16_t *br[CTY];
+      {  // Y^T += W2^T[features, chunk] G^T[chunk, tokens]
+        const bf16_t *bg[2] = {g + l32 * GLD + kg, g + (32 + l32) * GLD + kg};
 #pragma unroll
-        for (int j = 0; j < CTY; ++j)
-          br[j] = w2 + (int64_t)(w * (D / 4) + j * 32 + l32) * a.hidden + hc * kHC + kg;
-        mma<2, CTY>(y, ag, br, kHC);
+        for (int sp = 0; sp < NSP; ++sp) {
+          const bf16_t *gp[YT], *nx[2];
+          y_ptrs(hc, sp, gp);
+          if (sp + 1 < NSP) y_ptrs(hc, sp + 1, nx);
+          else if (hc + 1 < nchunk) g_ptrs(hc + 1, nx);
+          else first_proj_ptrs(nx);
+          phase<YT, 2, kHC / 32, true, 2>(y[sp], ring, gp, bg, nx);
+        }
       }
     }
     // -------------------------------------------------------- LayerNorm
-    float mean[2][16], rstd[2][16];
+    // lane holds features w*D/4 + (sp*YT+t)*32 + 8q + 4*hi + r of tokens j*32 + l32
+    float mean[2] = {0.f, 0.f}, rstd[2] = {1.f, 1.f};
     if (LN) {
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
-        float s[2][16];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+          float v = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            float v = 0.f;
+          for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
-            for (int j = 0; j < CTY; ++j) {
-              const float x = y[i][j][e];
-              v += pass == 0 ? x : (x - mean[i][e]) * (x - mean[i][e]);
-            }
+            for (int t = 0; t < YT; ++t)
 #pragma unroll
-            for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o);
-            s[i][e] = v;
-          }
-        if (l32 == 0) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) red[pass][w][i * 32 + c32_row(lane, e)] = s[i][e];
+              for (int e = 0; e < 16; ++e) {
+                const float x = y[sp][t][j][e];
+                v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
+              }
+          v += __shfl_xor(v, 32);
+          if (hi == 0) red[pass][w][j * 32 + l32] = v;
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int r = i * 32 + c32_row(lane, e);
-            const float t = red[pass][0][r] + red[pass][1][r] + red[pass][2][r] + red[pass][3][r];
-            if (pass == 0) mean[i][e] = t * (1.0f / D);
-            else rstd[i][e] = rsqrtf(t * (1.0f / D) + 1e-5f);
-          }
+        for (int j = 0; j < 2; ++j) {
+          const int t = j * 32 + l32;
+          const float tot = red[pass][0][t] + red[pass][1][t] + red[pass][2][t] + red[pass][3][t];
+          if (pass == 0) mean[j] = tot * (1.0f / D);
+          else rstd[j] = rsqrtf(tot * (1.0f / D) + 1e-5f);
+        }
       }
     }
-    // normalised (or plain) FFN output -> xs (bf16) or straight to out32
 #pragma unroll
-    for (int j = 0; j < CTY; ++j) {
-      const int c = w * (D / 4) + j * 32 + l32;
-      const float gg = LN ? a.ln_g[c] : 1.f, bb = LN ? a.ln_b[c] : 0.f;
+    for (int sp = 0; sp < NSP; ++sp)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int ti = 0; ti < YT; ++ti)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = i * 32 + c32_row(lane, e);
-          float v = y[i][j][e];
-          if (LN) v = (v - mean[i][e]) * rstd[i][e] * gg + bb;
-          if (PROJ) {
-            xs[r * XLD + c] = f2bf(v);
-          } else if (row0 + r < a.n_rows) {
-            if (a.out32) a.out32[(row0 + r) * a.ldo32 + c] = v;
-            if (a.out) ((bf16_t *)a.out)[(row0 + r) * a.ldo + c] = f2bf(v);
+        for (int q = 0; q < 4; ++q) {
+          const int f = w * (D / 4) + (sp * YT + ti) * 32 + 8 * q + 4 * hi;
+          f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
+          if (LN) {
+            gg = *reinterpret_cast<const f32x4 *>(a.ln_g + f);
+            bb = *reinterpret_cast<const f32x4 *>(a.ln_b + f);
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = y[sp][ti][j][4 * q + r];
+              if (LN) v[r] = (v[r] - mean[j]) * rstd[j] * gg[r] + bb[r];
+            }
+            const int t = j * 32 + l32;
+            if (PROJ) {
+              u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+              *reinterpret_cast<u32x2 *>(xs + t * XLD + f) = pv;
+            } else if (row0 + t < a.n_rows) {
+              if (a.out32) {
+                f32x4 ov = {v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(a.out32 + (row0 + t) * a.ldo32 + f) = ov;
+              }
+              if (a.out) {
+                u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>((bf16_t *)a.out + (row0 + t) * a.ldo + f) = pv;
+              }
+            }
           }
         }
-    }
     if (!PROJ) return;
     __syncthreads();
   }
 
   // ------------------------------------------------------------ projection
   if (PROJ) {
-    const bf16_t *wp = (const bf16_t *)a.wp;
-    const bf16_t *bx[2] = {xs + l32 * XLD + kg, xs + (32 + l32) * XLD + kg};
     if (OUT == OUT_KV) {
       const int H = a.H;
-      constexpr int DH_LOG_MIN = 5;
-      (void)DH_LOG_MIN;
       const int DH = D / H;
       bf16_t *kb = (bf16_t *)a.kbuf, *vb = (bf16_t *)a.vbuf;
-      {  // K^T = W_K^T Xt^T: lane gets 4 consecutive features of one token
-        f32x16 acc[CTY][2];
-        zero(acc);
-        const bf16_t *ar[CTY];
 #pragma unroll
-        for (int i = 0; i < CTY; ++i) ar[i] = wp + (int64_t)(w * (D / 4) + i * 32 + l32) * D + kg;
-        mma<CTY, 2>(acc, ar, bx, D);
+      for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T: 4 consecutive features / token
+        f32x16 acc[YT][2];
+        zero(acc);
+        const bf16_t *gp[YT], *nx[2];
+        proj_ptrs(sp, 0, gp);
+        if (sp + 1 < NSP) proj_ptrs2(sp + 1, 0, nx);
+        else proj_ptrs2(0, nkD, nx);
+        phase<YT, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int blk = (int)(row0 >> 5) + t;
           if (blk >= total_blocks) continue;
 #pragma unroll
-          for (int i = 0; i < CTY; ++i)
+          for (int i = 0; i < YT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int f = w * (D / 4) + i * 32 + 8 * q + 4 * (lane >> 5);
+              const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
               const int h = f / DH, dh = f % DH;
               u32x2 v = {pack_bf2(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
                          pack_bf2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
@@ -298,24 +450,29 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
             }
         }
       }
-      {  // V = Xt W_V: lane gets 4 consecutive tokens of one feature -> V^T rows
-        f32x16 acc[2][CTY];
-        zero(acc);
-        const bf16_t *br[CTY];
 #pragma unroll
-        for (int j = 0; j < CTY; ++j) br[j] = wp + (int64_t)(D + w * (D / 4) + j * 32 + l32) * D + kg;
-        mma<2, CTY>(acc, bx, br, D);
+      for (int sp = 0; sp < NSP; ++sp) {  // V = Xt W_V: 4 consecutive tokens / feature -> V^T
+        f32x16 acc[2][YT];
+        zero(acc);
+        const bf16_t *gp[YT], *nx[2];
+        proj_ptrs(sp, nkD, gp);
+        if (sp + 1 < NSP) {
+          proj_ptrs2(sp + 1, nkD, nx);
+          phase<2, YT, D / 32, false, 2>(acc, ring, gp, bx, nx);
+        } else {
+          phase<2, YT, D / 32, false, 0>(acc, ring, gp, bx, nx);
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int blk = (int)(row0 >> 5) + t;
           if (blk >= total_blocks) continue;
 #pragma unroll
-          for (int j = 0; j < CTY; ++j) {
-            const int f = w * (D / 4) + j * 32 + l32;
+          for (int j = 0; j < YT; ++j) {
+            const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
             const int h = f / DH, dh = f % DH;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int key = 8 * q + 4 * (lane >> 5);
+              const int key = 8 * q + 4 * hi;
               u32x2 v = {pack_bf2(acc[t][j][4 * q], acc[t][j][4 * q + 1]),
                          pack_bf2(acc[t][j][4 * q + 2], acc[t][j][4 * q + 3])};
               *reinterpret_cast<u32x2 *>(vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
@@ -323,29 +480,28 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
           }
         }
       }
-    } else {  // OUT_ROWS: out^T = Wp^T Xt^T, pn/4 features per wave in tiles of 32
-      const int per_wave = a.pn / 4;
-      for (int f0 = 0; f0 < per_wave; f0 += 32 * CTY) {
-        f32x16 acc[CTY][2];
-        zero(acc);
-        const bf16_t *ar[CTY];
+    } else {  // OUT_ROWS (pn == d): out^T = Wp^T Xt^T, D/4 features per wave
 #pragma unroll
-        for (int i = 0; i < CTY; ++i) {
-          int f = w * per_wave + f0 + i * 32 + l32;
-          if (f0 + i * 32 >= per_wave) f = w * per_wave;  // beyond this wave's slice: dummy
-          ar[i] = wp + (int64_t)f * D + kg;
+      for (int sp = 0; sp < NSP; ++sp) {
+        f32x16 acc[YT][2];
+        zero(acc);
+        const bf16_t *gp[YT], *nx[2];
+        proj_ptrs(sp, 0, gp);
+        if (sp + 1 < NSP) {
+          proj_ptrs2(sp + 1, 0, nx);
+          phase<YT, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
+        } else {
+          phase<YT, 2, D / 32, true, 0>(acc, ring, gp, bx, nx);
         }
-        mma<CTY, 2>(acc, ar, bx, D);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int64_t row = row0 + t * 32 + l32;
           if (row >= a.n_rows) continue;
 #pragma unroll
-          for (int i = 0; i < CTY; ++i) {
-            if (f0 + i * 32 >= per_wave) continue;
+          for (int i = 0; i < YT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int f = w * per_wave + f0 + i * 32 + 8 * q + 4 * (lane >> 5);
+              const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
               const float v0 = acc[i][t][4 * q] * a.scale, v1 = acc[i][t][4 * q + 1] * a.scale;
               const float v2 = acc[i][t][4 * q + 2] * a.scale, v3 = acc[i][t][4 * q + 3] * a.scale;
               if (a.out) {
@@ -357,7 +513,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
                 *reinterpret_cast<f32x4 *>(a.out32 + row * a.ldo32 + f) = v;
               }
             }
-          }
         }
       }
     }
@@ -399,23 +554,22 @@ hipError_t dispatch_d(const ChainArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void transpose_batch_kernel(TransposeBatch tb) {
-  const TransposeDesc &t = tb.m[blockIdx.y];
-  const int tiles_c = (t.cols + 31) / 32;
-  const int tile = blockIdx.x;
-  if (tile >= tiles_c * ((t.rows + 31) / 32)) return;
-  __shared__ bf16_t sh[32][33];
-  const int bx = (tile % tiles_c) * 32, by = (tile / tiles_c) * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int j = ty; j < 32; j += 8) {
-    const int r = by + j, c = bx + tx;
-    sh[j][tx] = (r < t.rows && c < t.cols) ? t.src[(int64_t)r * t.cols + c] : (bf16_t)0;
-  }
-  __syncthreads();
-  for (int j = ty; j < 32; j += 8) {
-    const int r = bx + j, c = by + tx;  // dst[src col][src row]
-    if (r < t.cols && c < t.rows) t.dst[(int64_t)r * t.ld_dst + t.dst_col0 + c] = sh[tx][j];
-  }
+__global__ __launch_bounds__(256) void pack_batch_kernel(PackBatch pb) {
+  const PackDesc &t = pb.m[blockIdx.y];
+  // one thread = 8 consecutive k of one output n (a 16-byte fragment piece)
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int groups = t.K / 8;
+  if (idx >= (int64_t)t.N * groups) return;
+  const int n = (int)(idx % t.N), k0 = (int)(idx / t.N) * 8;
+  const int ng = t.row_tile0 * 32 + n;
+  const int kk = k0 % 32;
+  const int lane = 32 * (kk / 16) + ng % 32;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = t.src[(int64_t)(k0 + e) * t.N + n];
+  const u32x4 pk = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+  bf16_t *d = t.dst + frag_off(ng / 32, k0 / 32, t.K / 32, (kk % 16) / 8, lane);
+  *reinterpret_cast<u32x4 *>(d) = pk;
 }
 
 }  // namespace
@@ -430,14 +584,11 @@ hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s) {
   }
 }
 
-hipError_t launch_transpose_batch(const TransposeBatch &tb, int n, hipStream_t s) {
+hipError_t launch_pack_batch(const PackBatch &pb, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int max_tiles = 1;
-  for (int i = 0; i < n; ++i) {
-    const int t = ((tb.m[i].rows + 31) / 32) * ((tb.m[i].cols + 31) / 32);
-    if (t > max_tiles) max_tiles = t;
-  }
-  hipLaunchKernelGGL(transpose_batch_kernel, dim3(max_tiles, n), dim3(256), 0, s, tb);
+  int64_t most = 1;
+  for (int i = 0; i < n; ++i) most = std::max<int64_t>(most, (int64_t)pb.m[i].N * (pb.m[i].K / 8));
+  hipLaunchKernelGGL(pack_batch_kernel, dim3((unsigned)((most + 255) / 256), n), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 

@@ -20,17 +20,16 @@ static constexpr int kBlockKeys = 32;  // keys per K/V block of the staged layou
 // ---------------------------------------------------------------- bf16
 DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bf16, round to nearest, ties to even (from the definition of the
-// format: add half an ulp of the kept part, plus the kept lsb for ties).
-DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;  // NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float -> bf16, round to nearest, ties to even: the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32, RNE under the default rounding mode; NaN
+// stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 DEV uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> DEV float to_f(T x);
@@ -70,7 +69,7 @@ DEV float wave_sum(float v) {
   return v;
 }
 
-DEV float silu_fast(float x) { return x * __frcp_rn(1.0f + __expf(-x)); }
+DEV float silu_fast(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 DEV float silu_exact(float x) { return x / (1.0f + expf(-x)); }
 
 // Largest u with off[u] <= key (off ascending, off[0] = 0), over [0, n).

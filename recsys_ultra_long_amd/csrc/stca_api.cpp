@@ -3,8 +3,8 @@
 //
 // Launch sequence of stca_forward (bf16 shown; fp32 is the same without the
 // weight preparation):
-//   1. weight preparation: every matrix transposed to [out, in] bf16 (one
-//      batched launch) so MFMA operands are k-contiguous 16-byte loads;
+//   1. weight preparation: every matrix re-laid as W^T in MFMA fragment order
+//      (one batched launch) so each operand fragment is one contiguous 1 KB load;
 //   2. planner: CSR validation, padded block offsets, split-L chunk offsets;
 //   3. history side of every layer (gather -> SwiGLU FFN -> LN -> W_K | W_V)
 //      into the blocked K/V buffers.  The history side never depends on the
@@ -56,7 +56,7 @@ struct Carver {
   }
 };
 
-// Offsets (elements) of the prepared (transposed) bf16 weights of one layer.
+// Offsets (elements) of the prepared (fragment-packed) bf16 weights of one layer.
 struct PrepLayer {
   size_t kv_w1, kv_w3, kv_w2, wkv, q_w1, q_w3, q_w2, wq, wo, wc, r;
 };
@@ -316,15 +316,16 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   plan.coff = plan.pblk + (B + 1);
 
   if ((e = rec(0))) return hip_fail(e, "stage event");
-  // ---- 1. weight preparation (bf16): transposes into the workspace
+  // ---- 1. weight preparation (bf16): fragment-packed W^T into the workspace
   bf16_t *prep = bf ? at<bf16_t>(ws, L.prep) : nullptr;
   if (bf) {
-    TransposeBatch tb;
+    PackBatch pb;
     int n = 0;
-    auto add = [&](const void *src, int rows, int cols, size_t dst, int ld, int col0) -> hipError_t {
-      tb.m[n++] = TransposeDesc{(const bf16_t *)src, prep + dst, rows, cols, ld, col0};
-      if (n == kMaxTransposes) {
-        hipError_t er = launch_transpose_batch(tb, n, s);
+    // W [K, N] -> packed W^T fragments at `dst` (+ row tile offset)
+    auto add = [&](const void *src, int K, int N, size_t dst, int tile0) -> hipError_t {
+      pb.m[n++] = PackDesc{(const bf16_t *)src, prep + dst, K, N, tile0};
+      if (n == kMaxPacks) {
+        hipError_t er = launch_pack_batch(pb, n, s);
         n = 0;
         return er;
       }
@@ -334,29 +335,29 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (int i = 0; i < M; ++i) {
       const stca_layer &l = w->layers[i];
       const PrepLayer &p = L.pl[i];
-      if ((e = add(l.kv.w1, d, hd, p.kv_w1, d, 0))) break;
-      if ((e = add(l.kv.w3, d, hd, p.kv_w3, d, 0))) break;
-      if ((e = add(l.kv.w2, hd, d, p.kv_w2, hd, 0))) break;
-      if ((e = add(l.wk, d, d, p.wkv, d, 0))) break;
-      if ((e = add(l.wv, d, d, p.wkv + (size_t)d * d, d, 0))) break;
-      if ((e = add(l.wq, d, d, p.wq, d, 0))) break;
-      if ((e = add(l.wo, d, d, p.wo, d, 0))) break;
+      if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0))) break;
+      if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0))) break;
+      if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
+      if ((e = add(l.wk, d, d, p.wkv, 0))) break;
+      if ((e = add(l.wv, d, d, p.wkv, d / 32))) break;
+      if ((e = add(l.wq, d, d, p.wq, 0))) break;
+      if ((e = add(l.wo, d, d, p.wo, 0))) break;
       if (fusion) {
-        if ((e = add(l.q.w1, d, hd, p.q_w1, d, 0))) break;
-        if ((e = add(l.q.w3, d, hd, p.q_w3, d, 0))) break;
-        if ((e = add(l.q.w2, hd, d, p.q_w2, hd, 0))) break;
-        if (i > 0 && (e = add(l.wc, (i + 1) * d, d, p.wc, (i + 1) * d, 0))) break;
+        if ((e = add(l.q.w1, d, hd, p.q_w1, 0))) break;
+        if ((e = add(l.q.w3, d, hd, p.q_w3, 0))) break;
+        if ((e = add(l.q.w2, hd, d, p.q_w2, 0))) break;
+        if (i > 0 && (e = add(l.wc, (i + 1) * d, d, p.wc, 0))) break;
       } else if (i + 1 < M) {
-        if ((e = add(l.r, d, d, p.r, d, 0))) break;
+        if ((e = add(l.r, d, d, p.r, 0))) break;
       }
     }
     if (!e && fusion) {
-      e = add(w->z.w1, d, hd, L.z_w1, d, 0);
-      if (!e) e = add(w->z.w3, d, hd, L.z_w3, d, 0);
-      if (!e) e = add(w->z.w2, hd, d, L.z_w2, hd, 0);
-      if (!e) e = add(w->wz, (M + 1) * d, d, L.wz, (M + 1) * d, 0);
+      e = add(w->z.w1, d, hd, L.z_w1, 0);
+      if (!e) e = add(w->z.w3, d, hd, L.z_w3, 0);
+      if (!e) e = add(w->z.w2, hd, d, L.z_w2, 0);
+      if (!e) e = add(w->wz, (M + 1) * d, d, L.wz, 0);
     }
-    if (!e && n) e = launch_transpose_batch(tb, n, s);
+    if (!e && n) e = launch_pack_batch(pb, n, s);
     if (e) return hip_fail(e, "weight preparation");
   }
 

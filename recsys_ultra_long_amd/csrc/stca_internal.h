@@ -53,13 +53,13 @@ struct ChainArgs {
   const void *a2;           // pre-GEMM segment 2 (x_t rows)
   int lda2;
   int k1, k2;               // pre-GEMM segment widths (multiples of 32)
-  const void *wpre;         // pre-GEMM weight [k1+k2, d] (bf16: prepared [d, k1+k2])
+  const void *wpre;         // pre-GEMM weight [k1+k2, d] (bf16: packed W^T)
   void *in_dump;            // optional copy of the input rows (IDS: [n_rows, d]; CSR: per token)
-  // FFN (bf16: prepared transposed matrices)
+  // FFN (bf16: packed W^T fragments, see PackDesc)
   const void *w1, *w3, *w2;
   const float *ln_g, *ln_b;
   // projection
-  const void *wp;           // [d, pn] (bf16: prepared [pn, d]; OUT_KV: [W_K|W_V]^T)
+  const void *wp;           // [d, pn] (bf16: packed; OUT_KV: W_K then W_V tiles)
   const void *wp2;          // fp32 OUT_KV: W_V (wp is W_K)
   int pn;
   float scale;
@@ -76,18 +76,30 @@ struct ChainArgs {
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s);
 hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 
-// Batched bf16 transpose: src [rows, cols] -> dst[c][dst_col0 + r] with row
-// pitch ld_dst (so several transposes can fill one prepared matrix).
-struct TransposeDesc {
+// Weight preparation (bf16): a matrix W [K, N] (row-major, y = x W) is stored
+// as W^T in MFMA fragment order.  Rows of W^T (outputs n) are grouped in
+// tiles of 32, k in blocks of 32; the 2 KB of a (tile, k block) hold the two
+// 32x32x16 operand fragments (half h = 0, 1) lane by lane:
+//   element (n, k) -> ((rt * NK + kb) * 2 + h) * 512 + lane * 8 + e
+//   rt = n / 32, kb = k / 32, lane = 32 * ((k % 32) / 16) + n % 32,
+//   h = (k % 16) / 8, e = k % 8, NK = K / 32.
+// so one fragment load is a single contiguous 1 KB read.  row_tile0 places
+// the matrix at a tile offset of the destination (W_K and W_V share one).
+struct PackDesc {
   const bf16_t *src;
   bf16_t *dst;
-  int rows, cols, ld_dst, dst_col0;
+  int K, N, row_tile0;
 };
-constexpr int kMaxTransposes = 48;
-struct TransposeBatch {
-  TransposeDesc m[kMaxTransposes];
+constexpr int kMaxPacks = 48;
+struct PackBatch {
+  PackDesc m[kMaxPacks];
 };
-hipError_t launch_transpose_batch(const TransposeBatch &tb, int n, hipStream_t s);
+hipError_t launch_pack_batch(const PackBatch &pb, int n, hipStream_t s);
+
+// Offset (elements) of the lane's half-h fragment of (tile rt, block kb).
+__host__ __device__ inline int64_t frag_off(int rt, int kb, int nk, int h, int lane) {
+  return (((int64_t)rt * nk + kb) * 2 + h) * 512 + lane * 8;
+}
 
 // ------------------------------------------------------------ attention
 struct AttnArgs {
