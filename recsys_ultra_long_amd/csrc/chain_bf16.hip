@@ -22,7 +22,6 @@
 namespace stca {
 namespace {
 
-constexpr int kRows = 64;     // rows per workgroup
 constexpr int kThreads = 256; // 4 waves
 constexpr int kHC = 128;      // hidden columns per chunk
 constexpr int kPad = 8;       // bf16 elements of row padding in LDS (16 bytes)
@@ -95,12 +94,6 @@ DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ?
   static_assert(NK % 4 == 0 && NK >= 4, "phase length must be a multiple of 4 blocks");
   constexpr int NG = GA ? RT : CT;
   constexpr int NL = GA ? CT : RT;
-  bf16x8 lo[2][NL][2];  // LDS operand, double-buffered one block ahead
-#pragma unroll
-  for (int t = 0; t < NL; ++t) {
-    lo[0][t][0] = ld8(lp[t]);
-    lo[0][t][1] = ld8(lp[t] + 8);
-  }
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) {
     const int nb = kb + 3;
@@ -109,12 +102,11 @@ DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ?
     } else if (NGN > 0) {
       ring_load<2>(ring, nb % 4, np, nb - NK);
     }
-    if (kb + 1 < NK) {
+    bf16x8 lo[NL][2];  // LDS operand of this block
 #pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        lo[(kb + 1) & 1][t][0] = ld8(lp[t] + (kb + 1) * 32);
-        lo[(kb + 1) & 1][t][1] = ld8(lp[t] + (kb + 1) * 32 + 8);
-      }
+    for (int t = 0; t < NL; ++t) {
+      lo[t][0] = ld8(lp[t] + kb * 32);
+      lo[t][1] = ld8(lp[t] + kb * 32 + 8);
     }
     // keep the prefetches issued ahead of this block's matrix work
     __builtin_amdgcn_sched_barrier(0);
@@ -124,8 +116,8 @@ DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ?
       for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-          const bf16x8 av = GA ? ring.v[kb % 4][i][h] : lo[kb & 1][i][h];
-          const bf16x8 bv = GA ? lo[kb & 1][j][h] : ring.v[kb % 4][j][h];
+          const bf16x8 av = GA ? ring.v[kb % 4][i][h] : lo[i][h];
+          const bf16x8 bv = GA ? lo[j][h] : ring.v[kb % 4][j][h];
           acc[i][j] = mfma32(av, bv, acc[i][j]);
         }
     __builtin_amdgcn_sched_barrier(0);
@@ -142,8 +134,9 @@ DEV void zero(f32x16 (&acc)[RT][CT]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-template <int D, int IN, bool FFN, bool LN, bool PROJ, int OUT>
-__global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(ChainArgs a) {
+template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT>
+__global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void chain_kernel(ChainArgs a) {
+  constexpr int R = 32 * TT;  // rows (tokens) per workgroup
   // Every contraction is computed "feature-major": MFMA rows are output
   // features, MFMA columns are the 64 rows (tokens) of the tile.  A lane then
   // holds 4 consecutive features of one token, so LDS / global stores are
@@ -151,10 +144,10 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
   constexpr int XLD = D + kPad;
   constexpr int GLD = kHC + kPad;
   constexpr int FT = D / 128;  // 32-feature tiles per wave for d-wide outputs
-  __shared__ __attribute__((aligned(16))) bf16_t xs[kRows * XLD];
-  __shared__ __attribute__((aligned(16))) bf16_t gs[FFN ? 2 : 1][FFN ? kRows * GLD : 8];
-  __shared__ float red[2][4][kRows];
-  __shared__ int s_id[kRows], s_tok[kRows];
+  __shared__ __attribute__((aligned(16))) bf16_t xs[R * XLD];
+  __shared__ __attribute__((aligned(16))) bf16_t gs[FFN ? 2 : 1][FFN ? R * GLD : 8];
+  __shared__ float red[2][4][R];
+  __shared__ int s_id[R], s_tok[R];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,10 +155,12 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
   const int l32 = lane & 31;
   const int hi = lane >> 5;         // which half of the wave
   const int kg = hi * 16;           // lane's k offset inside a 32-wide k block
-  const int64_t row0 = (int64_t)blockIdx.x * kRows;
+  const int64_t row0 = (int64_t)blockIdx.x * R;
   const bf16_t *table = (const bf16_t *)a.table;
   // MFMA-column (token) operands read from LDS rows
-  const bf16_t *bx[2] = {xs + l32 * XLD + kg, xs + (32 + l32) * XLD + kg};
+  const bf16_t *bx[TT];
+#pragma unroll
+  for (int j = 0; j < TT; ++j) bx[j] = xs + (j * 32 + l32) * XLD + kg;
 
   // weight rows streamed through the ring (each pointer: this lane's row + kg)
   constexpr int YT = FT < 2 ? FT : 2;  // weight tiles per phase
@@ -220,7 +215,7 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
 
   // ------------------------------------------------------------ input rows
   if (IN == IN_GATHER_CSR || IN == IN_GATHER_IDS) {
-    if (tid < kRows) {
+    if (tid < R) {
       int id = -1, tok = -1;
       const int64_t p = row0 + tid;
       if (IN == IN_GATHER_CSR) {
@@ -246,7 +241,7 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
     }
     __syncthreads();
     constexpr int C8 = D / 8;
-    for (int e = tid; e < kRows * C8; e += kThreads) {
+    for (int e = tid; e < R * C8; e += kThreads) {
       const int r = e / C8, c = (e % C8) * 8;
       const int id = s_id[r];
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -258,41 +253,41 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
   } else if (IN == IN_DENSE) {
     constexpr int C8 = D / 8;
     const bf16_t *src = (const bf16_t *)a.a;
-    for (int e = tid; e < kRows * C8; e += kThreads) {
+    for (int e = tid; e < R * C8; e += kThreads) {
       const int r = e / C8, c = (e % C8) * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (row0 + r < a.n_rows) v = *reinterpret_cast<const u32x4 *>(src + (row0 + r) * a.lda + c);
       *reinterpret_cast<u32x4 *>(xs + r * XLD + c) = v;
     }
   } else {  // IN_PREGEMM: xs = bf16([seg1 | seg2] W_pre), computed as W_pre^T [seg1|seg2]^T
-    f32x16 acc[FT][2];
+    f32x16 acc[FT][TT];
     zero(acc);
     const bf16_t *wpre = (const bf16_t *)a.wpre;
     const int nkt = (a.k1 + a.k2) / 32;
     const bf16_t *aw[FT];
 #pragma unroll
     for (int i = 0; i < FT; ++i) aw[i] = wpre + frag_off(w * FT + i, 0, nkt, 0, lane);
-    int64_t rr[2];
+    int64_t rr[TT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < TT; ++j) {
       rr[j] = row0 + j * 32 + l32;
       if (rr[j] >= a.n_rows) rr[j] = a.n_rows - 1;  // clamp: result discarded
     }
-    const bf16_t *bt[2];
+    const bf16_t *bt[TT];
     if (a.k1 > 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bt[j] = (const bf16_t *)a.a + rr[j] * a.lda + kg;
-      mma_packed_a<FT, 2>(acc, aw, bt, a.k1);
+      for (int j = 0; j < TT; ++j) bt[j] = (const bf16_t *)a.a + rr[j] * a.lda + kg;
+      mma_packed_a<FT, TT>(acc, aw, bt, a.k1);
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bt[j] = (const bf16_t *)a.a2 + rr[j] * a.lda2 + kg;
+    for (int j = 0; j < TT; ++j) bt[j] = (const bf16_t *)a.a2 + rr[j] * a.lda2 + kg;
 #pragma unroll
     for (int i = 0; i < FT; ++i) aw[i] += (int64_t)(a.k1 / 32) * 1024;
-    mma_packed_a<FT, 2>(acc, aw, bt, a.k2);
+    mma_packed_a<FT, TT>(acc, aw, bt, a.k2);
 #pragma unroll
     for (int i = 0; i < FT; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TT; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int f = w * (D / 4) + i * 32 + 8 * q + 4 * hi;
@@ -309,21 +304,21 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
 
   // ------------------------------------------------------------ SwiGLU FFN
   if (FFN) {
-    f32x16 y[NSP][YT][2];  // Y^T: this wave's D/4 features x 64 tokens
+    f32x16 y[NSP][YT][TT];  // Y^T: this wave's D/4 features x R tokens
 #pragma unroll
     for (int sp = 0; sp < NSP; ++sp) zero(y[sp]);
     const int nchunk = a.hidden / kHC;
     for (int hc = 0; hc < nchunk; ++hc) {
       bf16_t *g = gs[hc & 1];
       {  // G^T = SiLU(W1^T X^T) * (W3^T X^T) for this wave's 32 hidden units
-        f32x16 acc[2][2];
+        f32x16 acc[2][TT];
         zero(acc);
         const bf16_t *gp[2], *nx[2];
         g_ptrs(hc, gp);
         y_ptrs(hc, 0, nx);
-        phase<2, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
+        phase<2, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TT; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float gv[4];
@@ -336,7 +331,9 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
       }
       __syncthreads();
       {  // Y^T += W2^T[features, chunk] G^T[chunk, tokens]
-        const bf16_t *bg[2] = {g + l32 * GLD + kg, g + (32 + l32) * GLD + kg};
+        const bf16_t *bg[TT];
+#pragma unroll
+        for (int j = 0; j < TT; ++j) bg[j] = g + (j * 32 + l32) * GLD + kg;
 #pragma unroll
         for (int sp = 0; sp < NSP; ++sp) {
           const bf16_t *gp[YT], *nx[2];
@@ -344,18 +341,23 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
           if (sp + 1 < NSP) y_ptrs(hc, sp + 1, nx);
           else if (hc + 1 < nchunk) g_ptrs(hc + 1, nx);
           else first_proj_ptrs(nx);
-          phase<YT, 2, kHC / 32, true, 2>(y[sp], ring, gp, bg, nx);
+          phase<YT, TT, kHC / 32, true, 2>(y[sp], ring, gp, bg, nx);
         }
       }
     }
     // -------------------------------------------------------- LayerNorm
     // lane holds features w*D/4 + (sp*YT+t)*32 + 8q + 4*hi + r of tokens j*32 + l32
-    float mean[2] = {0.f, 0.f}, rstd[2] = {1.f, 1.f};
+    float mean[TT], rstd[TT];
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      mean[j] = 0.f;
+      rstd[j] = 1.f;
+    }
     if (LN) {
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TT; ++j) {
           float v = 0.f;
 #pragma unroll
           for (int sp = 0; sp < NSP; ++sp)
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TT; ++j) {
           const int t = j * 32 + l32;
           const float tot = red[pass][0][t] + red[pass][1][t] + red[pass][2][t] + red[pass][3][t];
           if (pass == 0) mean[j] = tot * (1.0f / D);
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
             bb = *reinterpret_cast<const f32x4 *>(a.ln_b + f);
           }
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < TT; ++j) {
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -427,15 +429,15 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
       bf16_t *kb = (bf16_t *)a.kbuf, *vb = (bf16_t *)a.vbuf;
 #pragma unroll
       for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T: 4 consecutive features / token
-        f32x16 acc[YT][2];
+        f32x16 acc[YT][TT];
         zero(acc);
         const bf16_t *gp[YT], *nx[2];
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) proj_ptrs2(sp + 1, 0, nx);
         else proj_ptrs2(0, nkD, nx);
-        phase<YT, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
+        phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
           if (blk >= total_blocks) continue;
 #pragma unroll
@@ -452,18 +454,18 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
       }
 #pragma unroll
       for (int sp = 0; sp < NSP; ++sp) {  // V = Xt W_V: 4 consecutive tokens / feature -> V^T
-        f32x16 acc[2][YT];
+        f32x16 acc[TT][YT];
         zero(acc);
         const bf16_t *gp[YT], *nx[2];
         proj_ptrs(sp, nkD, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, nkD, nx);
-          phase<2, YT, D / 32, false, 2>(acc, ring, gp, bx, nx);
+          phase<TT, YT, D / 32, false, 2>(acc, ring, gp, bx, nx);
         } else {
-          phase<2, YT, D / 32, false, 0>(acc, ring, gp, bx, nx);
+          phase<TT, YT, D / 32, false, 0>(acc, ring, gp, bx, nx);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
           if (blk >= total_blocks) continue;
 #pragma unroll
@@ -483,18 +485,18 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
     } else {  // OUT_ROWS (pn == d): out^T = Wp^T Xt^T, D/4 features per wave
 #pragma unroll
       for (int sp = 0; sp < NSP; ++sp) {
-        f32x16 acc[YT][2];
+        f32x16 acc[YT][TT];
         zero(acc);
         const bf16_t *gp[YT], *nx[2];
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, 0, nx);
-          phase<YT, 2, D / 32, true, 2>(acc, ring, gp, bx, nx);
+          phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
         } else {
-          phase<YT, 2, D / 32, true, 0>(acc, ring, gp, bx, nx);
+          phase<YT, TT, D / 32, true, 0>(acc, ring, gp, bx, nx);
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TT; ++t) {
           const int64_t row = row0 + t * 32 + l32;
           if (row >= a.n_rows) continue;
 #pragma unroll
@@ -519,32 +521,37 @@ __global__ __launch_bounds__(kThreads, (D <= 256 ? 2 : 1)) void chain_kernel(Cha
   }
 }
 
+// History rows: 64-token tiles (two 4-wave workgroups per CU at d <= 256;
+// 128-token tiles with one workgroup per CU measured slower).  Query-side
+// rows (a few thousand targets): 32-token tiles for more workgroups.
 template <int D>
 hipError_t dispatch_d(const ChainArgs &a, hipStream_t s) {
-  int64_t rows = a.n_rows;
-  const dim3 grid((unsigned)((rows + kRows - 1) / kRows)), block(kThreads);
-#define CH(IN, FFN, LN, PROJ, OUT) \
-  hipLaunchKernelGGL((chain_kernel<D, IN, FFN, LN, PROJ, OUT>), grid, block, 0, s, a)
+  constexpr int TTH = 2;
+  constexpr int TTQ = 1;
   const bool f = a.ffn, l = a.ln, p = a.proj;
+  auto grid = [&](int tt) { return dim3((unsigned)((a.n_rows + 32 * tt - 1) / (32 * tt))); };
+  const dim3 block(kThreads);
+#define CH(TT, IN, FFN, LN, PROJ, OUT) \
+  hipLaunchKernelGGL((chain_kernel<D, TT, IN, FFN, LN, PROJ, OUT>), grid(TT), block, 0, s, a)
   switch (a.in_mode) {
     case IN_GATHER_CSR:  // history: FFN (+LN) then K/V
       if (!(f && p && a.out_mode == OUT_KV)) return hipErrorInvalidValue;
-      if (l) CH(IN_GATHER_CSR, true, true, true, OUT_KV);
-      else CH(IN_GATHER_CSR, true, false, true, OUT_KV);
+      if (l) CH(TTH, IN_GATHER_CSR, true, true, true, OUT_KV);
+      else CH(TTH, IN_GATHER_CSR, true, false, true, OUT_KV);
       break;
     case IN_GATHER_IDS:  // first query: FFN + LN + W_Q
       if (!(f && l && p)) return hipErrorInvalidValue;
-      CH(IN_GATHER_IDS, true, true, true, OUT_ROWS);
+      CH(TTQ, IN_GATHER_IDS, true, true, true, OUT_ROWS);
       break;
     case IN_DENSE:  // projections only (W_Q, W_O, R)
       if (f || l || !p) return hipErrorInvalidValue;
-      CH(IN_DENSE, false, false, true, OUT_ROWS);
+      CH(TTQ, IN_DENSE, false, false, true, OUT_ROWS);
       break;
     case IN_PREGEMM:  // fusion (FFN + LN + W_Q) or z (FFN [+LN], no projection)
       if (!f) return hipErrorInvalidValue;
-      if (p && l) CH(IN_PREGEMM, true, true, true, OUT_ROWS);
-      else if (!p && l) CH(IN_PREGEMM, true, true, false, OUT_ROWS);
-      else if (!p && !l) CH(IN_PREGEMM, true, false, false, OUT_ROWS);
+      if (p && l) CH(TTQ, IN_PREGEMM, true, true, true, OUT_ROWS);
+      else if (!p && l) CH(TTQ, IN_PREGEMM, true, true, false, OUT_ROWS);
+      else if (!p && !l) CH(TTQ, IN_PREGEMM, true, false, false, OUT_ROWS);
       else return hipErrorInvalidValue;
       break;
     default:
