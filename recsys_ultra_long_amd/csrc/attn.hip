@@ -7,19 +7,27 @@
 //   softmax: o = sum_j exp(s_j - max) V_j[eta] / sum_j exp(s_j - max)
 //   relu:    o = sum_j max(0, s_j) V_j[eta],   active = #{j : s_j > 0}
 //
-// Request Level Batching ([Notes] §RLB): one workgroup streams a chunk of the
-// user's K/V blocks once and serves up to 64 of the user's targets with it.
-// The history is split into chunks of `nb` 32-key blocks (the single-GPU form
-// of the per-device partial attention of [WeChat] §1.1; the blocked tiling
-// follows the SRAM tiling idea of [WeChat] §3.3.1): each chunk writes a
-// partial (running max, running sum, accumulator) per (target, head), and a
-// second pass merges a user's partials in chunk order -- no float atomics, so
-// results do not depend on scheduling.
+// Request Level Batching ([Notes] §RLB): a workgroup streams a user's K/V
+// blocks once and serves up to 64 of the user's targets with them.
+//
+// Scheduling ("stream-K"): the work is the sequence of units
+//   ((user, target group, head), 128-key unit)      in that order,
+// and a persistent grid (one workgroup per occupancy slot) takes equal
+// contiguous ranges of it.  A workgroup carries the online-softmax state
+// across the units of one (user, group, head) and writes one partial
+// (running max, running sum, accumulator) when that pair ends or its range
+// ends -- the single-GPU form of the per-device partial attention of [WeChat]
+// §1.1, with the blocked tiling of [WeChat] §3.3.1.  Ragged histories stay
+// balanced, and the partial traffic is set by the grid, not by the length.
+// A second pass folds a pair's partials in workgroup order: no float atomics,
+// so results do not depend on scheduling.
 //
 // K/V layout (written by the history chain): per 32-key block b and head h,
 //   K[b][h][key 0..31][d_h]   (row of a key contiguous)
 //   V[b][h][d_h][key 0..31]   (transposed: a feature's 32 keys contiguous)
 // so every MFMA operand fragment is one 16-byte load.
+#include <algorithm>
+
 #include "stca_internal.h"
 
 namespace stca {
@@ -30,266 +38,327 @@ constexpr float kNegBig = -1.0e30f;
 
 DEV float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Position of global unit `unit` in the sequence: user u, pair index within
+// the user (group * H + head), first unit of the pair, units of the pair.
+struct UnitPos {
+  int u, pair, first, nc;
+};
+DEV UnitPos decode_unit(const Plan &P, int B, int HG, int unit) {
+  UnitPos r;
+  r.u = upper_index(P.coff, B, unit / HG);
+  r.nc = P.coff[r.u + 1] - P.coff[r.u];
+  const int rem = unit - P.coff[r.u] * HG;
+  r.pair = rem / r.nc;
+  r.first = P.coff[r.u] * HG + r.pair * r.nc;
+  return r;
+}
+
+// Units per workgroup of the persistent grid.
+DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
+
 // ------------------------------------------------------------------ bf16 / MFMA
 // S^T = K Q^T (16 keys x 16 targets per MFMA), online softmax in registers,
 // O^T += V^T P^T (16 features x 16 targets per MFMA).  The key order inside a
 // 32-key block is permuted when K is loaded so that the score tile's lane
 // layout is exactly the B-operand layout P^T needs: lane l (g = l/16) holds the
-// scores of keys 8g..8g+7 for target l%16.
+// scores of keys 8g..8g+7 for target l%16.  The four waves of a workgroup take
+// alternate blocks of a pair's range and merge in LDS when the pair ends.
 template <int DH, int NT, int SCORE>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
   constexpr int DT = DH / 16;  // feature tiles of the output
-  constexpr int TG = NT * 16;  // targets per workgroup
+  constexpr int TG = NT * 16;  // targets per group
   __shared__ float sm_m[4][TG], sm_l[4][TG];
   __shared__ int sm_c[4][TG];
   __shared__ float sm_o[4][TG][DH + 1];
 
-  const int c = blockIdx.x, h = blockIdx.y;
   const Plan P = a.plan;
-  if (c >= P.coff[a.B]) return;
-  const int u = upper_index(P.coff, a.B, c);
-  const int tbase = P.toff[u];
-  const int m_u = P.toff[u + 1] - tbase;
-  const int t0 = blockIdx.z * TG;
-  if (t0 >= m_u) return;
-  const int L = P.hoff[u + 1] - P.hoff[u];
-  const int cl = c - P.coff[u];
-  const int b_begin = P.pblk[u] + cl * a.nb;
-  const int b_end = min(P.pblk[u + 1], b_begin + a.nb);
-  const int key0 = cl * a.nb * 32;  // user-local index of the chunk's first key
+  const int H = a.H, G = a.groups, HG = H * G;
+  const int total = P.coff[a.B] * HG;
+  const int per = units_per_wg(total, gridDim.x);
+  int unit = blockIdx.x * per;
+  const int unit_end = min(total, unit + per);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int H = a.H;
+  const int g16 = lane >> 4, c16 = lane & 15;
   const bf16_t *Q = (const bf16_t *)a.q;
   const bf16_t *Kb = (const bf16_t *)a.kbuf, *Vb = (const bf16_t *)a.vbuf;
+  const int kr0 = 8 * (c16 >> 2) + (c16 & 3);  // permuted key row of score tile 0
 
-  bf16x8 qf[NT][KS];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int tl = t0 + n * 16 + c16;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      if (tl < m_u) {
-        qf[n][k] = ld8(Q + (int64_t)(tbase + tl) * a.d + h * DH + k * 32 + g * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[n][k][e] = 0;
-      }
-    }
-  }
-  float mrun[NT], lrun[NT];
-  int cnt[NT];
-  f32x4 o[DT][NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    mrun[n] = kNegBig;
-    lrun[n] = 0.f;
-    cnt[n] = 0;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // key row this lane loads for score tile kt (a permutation of the block)
-  const int kr0 = 8 * (c16 >> 2) + (c16 & 3);
+  while (unit < unit_end) {
+    const UnitPos pos = decode_unit(P, a.B, HG, unit);
+    const int seg_end = min(unit_end, pos.first + pos.nc);
+    const int u = pos.u, grp = pos.pair / H, h = pos.pair % H;
+    const int tbase = P.toff[u];
+    const int m_u = P.toff[u + 1] - tbase;
+    const int t0 = grp * TG;
+    if (t0 < m_u) {
+      const int L = P.hoff[u + 1] - P.hoff[u];
+      const int cl = unit - (pos.first);  // first unit of this segment within the pair
+      const int b0 = P.pblk[u] + cl * a.nb;
+      const int b1 = min(P.pblk[u + 1], P.pblk[u] + (cl + seg_end - unit) * a.nb);
 
-  for (int b = b_begin + w; b < b_end; b += 4) {
-    const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
-    const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
-    bf16x8 kf[2][KS], vf[DT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int k = 0; k < KS; ++k) kf[kt][k] = ld8(kb + (kr0 + 4 * kt) * DH + k * 32 + g * 8);
-#pragma unroll
-    for (int t = 0; t < DT; ++t) vf[t] = ld8(vb + (t * 16 + c16) * 32 + g * 8);
-
-    f32x4 st[2][NT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      bf16x8 qf[NT][KS];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        st[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tl = t0 + n * 16 + c16;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) st[kt][n] = mfma16(kf[kt][k], qf[n][k], st[kt][n]);
-      }
-    // keys of this lane: 8g + 4kt + r; valid while below the user's length
-    const int nvalid = L - (key0 + (b - b_begin) * 32);
-    bf16x8 pk[NT];
+        for (int k = 0; k < KS; ++k) {
+          if (tl < m_u) {
+            qf[n][k] = ld8(Q + (int64_t)(tbase + tl) * a.d + h * DH + k * 32 + g16 * 8);
+          } else {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      if (SCORE == 0) {
-        float mx = kNegBig;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (8 * g + 4 * kt + r < nvalid) mx = fmaxf(mx, st[kt][n][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(mrun[n], mx);
-        const float corr = ex2((mrun[n] - mnew) * kLog2e);
-        mrun[n] = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p = 0.f;
-            if (8 * g + 4 * kt + r < nvalid) p = ex2((st[kt][n][r] - mnew) * kLog2e);
-            const bf16_t pb = f2bf(p);
-            psum += bf2f(pb);
-            pk[n][4 * kt + r] = (short)pb;
+            for (int e = 0; e < 8; ++e) qf[n][k][e] = 0;
           }
-        lrun[n] = lrun[n] * corr + psum;
+        }
+      }
+      float mrun[NT], lrun[NT];
+      int cnt[NT];
+      f32x4 o[DT][NT];
 #pragma unroll
-        for (int t = 0; t < DT; ++t) o[t][n] *= corr;
-      } else {
+      for (int n = 0; n < NT; ++n) {
+        mrun[n] = kNegBig;
+        lrun[n] = 0.f;
+        cnt[n] = 0;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      bf16x8 kf[2][KS], vf[DT];
+      auto load_kv = [&](int b, bf16x8 (&kk)[2][KS], bf16x8 (&vv)[DT]) {
+        const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
+        const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float s = st[kt][n][r];
-            const bool on = (8 * g + 4 * kt + r < nvalid) && s > 0.f;
-            cnt[n] += on ? 1 : 0;
-            pk[n][4 * kt + r] = (short)f2bf(on ? s : 0.f);
+          for (int k = 0; k < KS; ++k) kk[kt][k] = ld8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vv[t] = ld8(vb + (t * 16 + c16) * 32 + g16 * 8);
+      };
+      if (b0 + w < b1) load_kv(b0 + w, kf, vf);
+      for (int b = b0 + w; b < b1; b += 4) {
+        bf16x8 kn[2][KS], vn[DT];
+        if (b + 4 < b1) load_kv(b + 4, kn, vn);  // next block of this wave
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 st[2][NT];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            st[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) st[kt][n] = mfma16(kf[kt][k], qf[n][k], st[kt][n]);
           }
+        // keys of this lane: 8g + 4kt + r; valid while below the user's length
+        const int nvalid = L - (b - P.pblk[u]) * 32;
+        bf16x8 pk[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (SCORE == 0) {
+            float mx = kNegBig;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (8 * g16 + 4 * kt + r < nvalid) mx = fmaxf(mx, st[kt][n][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mnew = fmaxf(mrun[n], mx);
+            const float corr = ex2((mrun[n] - mnew) * kLog2e);
+            mrun[n] = mnew;
+            const float mb = mnew * kLog2e;
+            float psum = 0.f;
+            float pv[8];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                float p = 0.f;
+                if (8 * g16 + 4 * kt + r < nvalid) p = ex2(fmaf(st[kt][n][r], kLog2e, -mb));
+                pv[4 * kt + r] = p;
+              }
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
+              pk[n][e] = (short)(pr & 0xffff);
+              pk[n][e + 1] = (short)(pr >> 16);
+              psum += bf2f((bf16_t)(pr & 0xffff)) + bf2f((bf16_t)(pr >> 16));
+            }
+            lrun[n] = lrun[n] * corr + psum;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) o[t][n] *= corr;
+          } else {
+            float pv[8];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float sc = st[kt][n][r];
+                const bool on = (8 * g16 + 4 * kt + r < nvalid) && sc > 0.f;
+                cnt[n] += on ? 1 : 0;
+                pv[4 * kt + r] = on ? sc : 0.f;
+              }
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
+              pk[n][e] = (short)(pr & 0xffff);
+              pk[n][e + 1] = (short)(pr >> 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o[t][n] = mfma16(vf[t], pk[n], o[t][n]);
+        if (b + 4 < b1) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) kf[kt][k] = kn[kt][k];
+#pragma unroll
+          for (int t = 0; t < DT; ++t) vf[t] = vn[t];
+        }
       }
-    }
-#pragma unroll
-    for (int t = 0; t < DT; ++t)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) o[t][n] = mfma16(vf[t], pk[n], o[t][n]);
-  }
 
-  // ---- merge the four waves in LDS, then write this chunk's partial
+      // ---- merge the four waves in LDS, write this segment's partial
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float l = lrun[n];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    int cn = cnt[n];
-    cn += __shfl_xor(cn, 16);
-    cn += __shfl_xor(cn, 32);
-    if (g == 0) {
-      sm_m[w][n * 16 + c16] = mrun[n];
-      sm_l[w][n * 16 + c16] = l;
-      sm_c[w][n * 16 + c16] = cn;
-    }
+      for (int n = 0; n < NT; ++n) {
+        float l = lrun[n];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        int cn = cnt[n];
+        cn += __shfl_xor(cn, 16);
+        cn += __shfl_xor(cn, 32);
+        if (g16 == 0) {
+          sm_m[w][n * 16 + c16] = mrun[n];
+          sm_l[w][n * 16 + c16] = l;
+          sm_c[w][n * 16 + c16] = cn;
+        }
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g + r] = o[t][n][r];
-  }
-  __syncthreads();
-  const int64_t pbase = ((int64_t)c * H + h) * a.max_tgt + t0;
-  for (int e = tid; e < TG * DH; e += 256) {
-    const int tl = e / DH, dh = e % DH;
-    if (t0 + tl >= m_u) continue;
-    if (SCORE == 0) {
-      const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
-      float acc = 0.f, l = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float f = ex2((sm_m[q][tl] - M) * kLog2e);
-        acc += sm_o[q][tl][dh] * f;
-        l += sm_l[q][tl] * f;
+          for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = o[t][n][r];
       }
-      a.part_acc[(pbase + tl) * DH + dh] = acc;
-      if (dh == 0) {
-        a.part_ml[(pbase + tl) * 2] = M;
-        a.part_ml[(pbase + tl) * 2 + 1] = l;
+      __syncthreads();
+      const int64_t pbase = (int64_t)unit * a.tgs;
+      for (int e = tid; e < TG * DH; e += 256) {
+        const int tl = e / DH, dh = e % DH;
+        if (t0 + tl >= m_u) continue;
+        if (SCORE == 0) {
+          const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
+          float acc = 0.f, l = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float f = ex2((sm_m[q][tl] - M) * kLog2e);
+            acc += sm_o[q][tl][dh] * f;
+            l += sm_l[q][tl] * f;
+          }
+          a.part_acc[(pbase + tl) * DH + dh] = acc;
+          if (dh == 0) {
+            a.part_ml[(pbase + tl) * 2] = M;
+            a.part_ml[(pbase + tl) * 2 + 1] = l;
+          }
+        } else {
+          a.part_acc[(pbase + tl) * DH + dh] =
+              sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
+          if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
+        }
       }
-    } else {
-      a.part_acc[(pbase + tl) * DH + dh] =
-          sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
-      if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
+      __syncthreads();  // LDS reused by the next segment
     }
+    unit = seg_end;
   }
 }
 
 // ------------------------------------------------------------------ fp32
-// One wave per (chunk, head, 64 targets); lane = target; keys streamed one at
-// a time.  The fp32 configuration is the precision reference of the library
-// (small shapes), so scores and sums are accumulated in fp64: the ReLU-scored
-// sum is unnormalised and cancels heavily, and fp32 accumulation alone would
-// cost most of a 1e-5 error budget.
+// One wave per workgroup, lane = target, keys streamed one at a time over the
+// same unit ranges.  The fp32 configuration is the precision reference of the
+// library (small shapes), so scores and sums are accumulated in fp64: the
+// ReLU-scored sum is unnormalised and cancels heavily, and fp32 accumulation
+// alone would cost most of a 1e-5 error budget.
 template <int DH, int SCORE>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
-  const int c = blockIdx.x, h = blockIdx.y;
   const Plan P = a.plan;
-  if (c >= P.coff[a.B]) return;
-  const int u = upper_index(P.coff, a.B, c);
-  const int tbase = P.toff[u];
-  const int m_u = P.toff[u + 1] - tbase;
-  const int t0 = blockIdx.z * 64;
-  if (t0 >= m_u) return;
-  const int L = P.hoff[u + 1] - P.hoff[u];
-  const int cl = c - P.coff[u];
-  const int b_begin = P.pblk[u] + cl * a.nb;
-  const int b_end = min(P.pblk[u + 1], b_begin + a.nb);
-  const int key0 = cl * a.nb * 32;
-  const int H = a.H;
-  const int tl = t0 + threadIdx.x;
-  const bool act = tl < m_u;
+  const int H = a.H, G = a.groups, HG = H * G;
+  const int total = P.coff[a.B] * HG;
+  const int per = units_per_wg(total, gridDim.x);
+  int unit = blockIdx.x * per;
+  const int unit_end = min(total, unit + per);
   const float *Q = (const float *)a.q;
   const float *Kb = (const float *)a.kbuf, *Vb = (const float *)a.vbuf;
-  double q[DH], acc[DH];
+  while (unit < unit_end) {
+    const UnitPos pos = decode_unit(P, a.B, HG, unit);
+    const int seg_end = min(unit_end, pos.first + pos.nc);
+    const int u = pos.u, grp = pos.pair / H, h = pos.pair % H;
+    const int tbase = P.toff[u];
+    const int m_u = P.toff[u + 1] - tbase;
+    const int tl = grp * 64 + threadIdx.x;
+    if (grp * 64 < m_u) {
+      const bool act = tl < m_u;
+      const int L = P.hoff[u + 1] - P.hoff[u];
+      const int cl = unit - pos.first;
+      const int b0 = P.pblk[u] + cl * a.nb;
+      const int b1 = min(P.pblk[u + 1], P.pblk[u] + (cl + seg_end - unit) * a.nb);
+      double q[DH], acc[DH];
 #pragma unroll
-  for (int i = 0; i < DH; ++i) {
-    q[i] = act ? (double)Q[(int64_t)(tbase + tl) * a.d + h * DH + i] : 0.0;
-    acc[i] = 0.0;
-  }
-  double mrun = -1.0e300, lrun = 0.0;
-  int cnt = 0;
-  for (int b = b_begin; b < b_end; ++b) {
-    const float *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
-    const float *vb = Vb + ((int64_t)b * H + h) * DH * 32;
-    const int nvalid = min(32, L - (key0 + (b - b_begin) * 32));
-    for (int j = 0; j < nvalid; ++j) {
-      double s = 0.0;
-#pragma unroll
-      for (int i = 0; i < DH; ++i) s = fma(q[i], (double)kb[j * DH + i], s);
-      double p;
-      if (SCORE == 0) {
-        const double mnew = fmax(mrun, s);
-        const double corr = exp(mrun - mnew);
-        p = exp(s - mnew);
-        lrun = lrun * corr + p;
-#pragma unroll
-        for (int i = 0; i < DH; ++i) acc[i] *= corr;
-        mrun = mnew;
-      } else {
-        p = s > 0.0 ? s : 0.0;
-        cnt += s > 0.0 ? 1 : 0;
+      for (int i = 0; i < DH; ++i) {
+        q[i] = act ? (double)Q[(int64_t)(tbase + tl) * a.d + h * DH + i] : 0.0;
+        acc[i] = 0.0;
       }
+      double mrun = -1.0e300, lrun = 0.0;
+      int cnt = 0;
+      for (int b = b0; b < b1; ++b) {
+        const float *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
+        const float *vb = Vb + ((int64_t)b * H + h) * DH * 32;
+        const int nvalid = min(32, L - (b - P.pblk[u]) * 32);
+        for (int j = 0; j < nvalid; ++j) {
+          double sc = 0.0;
 #pragma unroll
-      for (int i = 0; i < DH; ++i) acc[i] = fma(p, (double)vb[i * 32 + j], acc[i]);
+          for (int i = 0; i < DH; ++i) sc = fma(q[i], (double)kb[j * DH + i], sc);
+          double p;
+          if (SCORE == 0) {
+            const double mnew = fmax(mrun, sc);
+            const double corr = exp(mrun - mnew);
+            p = exp(sc - mnew);
+            lrun = lrun * corr + p;
+#pragma unroll
+            for (int i = 0; i < DH; ++i) acc[i] *= corr;
+            mrun = mnew;
+          } else {
+            p = sc > 0.0 ? sc : 0.0;
+            cnt += sc > 0.0 ? 1 : 0;
+          }
+#pragma unroll
+          for (int i = 0; i < DH; ++i) acc[i] = fma(p, (double)vb[i * 32 + j], acc[i]);
+        }
+      }
+      if (act) {
+        const int64_t pi = (int64_t)unit * a.tgs + (tl - grp * 64);
+        // softmax partials are stored normalised by their own running sum
+        // (a convex combination, no cancellation), the sum separately
+        if (SCORE == 0) {
+          const double inv = lrun > 0.0 ? 1.0 / lrun : 0.0;
+#pragma unroll
+          for (int i = 0; i < DH; ++i) a.part_acc[pi * DH + i] = (float)(acc[i] * inv);
+          a.part_ml[pi * 2] = (float)mrun;
+          a.part_ml[pi * 2 + 1] = (float)lrun;
+        } else {
+#pragma unroll
+          for (int i = 0; i < DH; ++i) a.part_acc[pi * DH + i] = (float)acc[i];
+          a.part_cnt[pi] = cnt;
+        }
+      }
     }
-  }
-  if (!act) return;
-  const int64_t pi = ((int64_t)c * H + h) * a.max_tgt + tl;
-  // fp32 partials: the softmax accumulator is stored normalised by its own
-  // running sum (a convex combination, no cancellation), the sum separately.
-  if (SCORE == 0) {
-    const double inv = lrun > 0.0 ? 1.0 / lrun : 0.0;
-#pragma unroll
-    for (int i = 0; i < DH; ++i) a.part_acc[pi * DH + i] = (float)(acc[i] * inv);
-    a.part_ml[pi * 2] = (float)mrun;
-    a.part_ml[pi * 2 + 1] = (float)lrun;
-  } else {
-#pragma unroll
-    for (int i = 0; i < DH; ++i) a.part_acc[pi * DH + i] = (float)acc[i];
-    a.part_cnt[pi] = cnt;
+    unit = seg_end;
   }
 }
 
 // ------------------------------------------------------------------ merge
-// One thread per (target, feature): fold the user's chunk partials in chunk
-// order.  attn = sum_c acc_c e^{m_c - M} / sum_c l_c e^{m_c - M}; ReLU: sums.
+// One thread per (target, feature): fold the partials of the target's
+// (user, group, head) pair in workgroup order.
+//   softmax: attn = sum_w acc_w e^{m_w - M} / sum_w l_w e^{m_w - M};  ReLU: sums.
 template <int SCORE>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  const int d = a.d, DH = a.dh, H = a.H;
+  const int d = a.d, DH = a.dh, H = a.H, G = a.groups, HG = H * G;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= a.n_tgt * d) return;
   const int t = (int)(e / d), f = (int)(e % d);
@@ -297,47 +366,49 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const Plan P = a.plan;
   float out = 0.f;
   int cnt = 0;
-  if (t < P.toff[a.B]) {
+  if (t < P.toff[a.B] && a.grid > 0) {
     const int u = upper_index(P.toff, a.B, t);
     const int tl = t - P.toff[u];
-    const int c0 = P.coff[u], c1 = P.coff[u + 1];
-    if (SCORE == 0 && a.dtype) {
-      float M = kNegBig;
-      for (int c = c0; c < c1; ++c) M = fmaxf(M, a.part_ml[(((int64_t)c * H + h) * a.max_tgt + tl) * 2]);
-      float acc = 0.f, l = 0.f;
-      for (int c = c0; c < c1; ++c) {
-        const int64_t pi = ((int64_t)c * H + h) * a.max_tgt + tl;
-        const float fct = ex2((a.part_ml[pi * 2] - M) * kLog2e);
-        acc += a.part_acc[pi * DH + dh] * fct;
-        l += a.part_ml[pi * 2 + 1] * fct;
+    const int grp = G > 1 ? tl / 64 : 0;
+    const int tg = tl - grp * 64;
+    const int nc = P.coff[u + 1] - P.coff[u];
+    if (nc > 0) {
+      const int per = units_per_wg(P.coff[a.B] * HG, a.grid);
+      const int first = P.coff[u] * HG + (grp * H + h) * nc;
+      const int w0 = first / per, w1 = (first + nc - 1) / per;
+      if (SCORE == 0 && a.dtype) {
+        float M = kNegBig;
+        for (int wg = w0; wg <= w1; ++wg)
+          M = fmaxf(M, a.part_ml[((int64_t)max(first, wg * per) * a.tgs + tg) * 2]);
+        float acc = 0.f, l = 0.f;
+        for (int wg = w0; wg <= w1; ++wg) {
+          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          const float fct = ex2((a.part_ml[pi * 2] - M) * kLog2e);
+          acc += a.part_acc[pi * DH + dh] * fct;
+          l += a.part_ml[pi * 2 + 1] * fct;
+        }
+        out = l > 0.f ? acc / l : 0.f;
+      } else if (SCORE == 0) {  // fp32 path: normalised partials, fp64 fold
+        double M = -1.0e300;
+        for (int wg = w0; wg <= w1; ++wg)
+          M = fmax(M, (double)a.part_ml[((int64_t)max(first, wg * per) * a.tgs + tg) * 2]);
+        double acc = 0.0, l = 0.0;
+        for (int wg = w0; wg <= w1; ++wg) {
+          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          const double wgt = (double)a.part_ml[pi * 2 + 1] * exp((double)a.part_ml[pi * 2] - M);
+          acc += (double)a.part_acc[pi * DH + dh] * wgt;
+          l += wgt;
+        }
+        out = l > 0.0 ? (float)(acc / l) : 0.f;
+      } else {
+        double acc = 0.0;
+        for (int wg = w0; wg <= w1; ++wg) {
+          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          acc += (double)a.part_acc[pi * DH + dh];
+          if (dh == 0) cnt += a.part_cnt[pi];
+        }
+        out = (float)acc;
       }
-      out = l > 0.f ? acc / l : 0.f;
-    } else if (SCORE == 0) {  // fp32 path: normalised partials, fp64 fold
-      double M = -1.0e300;
-      for (int c = c0; c < c1; ++c)
-        M = fmax(M, (double)a.part_ml[(((int64_t)c * H + h) * a.max_tgt + tl) * 2]);
-      double acc = 0.0, l = 0.0;
-      for (int c = c0; c < c1; ++c) {
-        const int64_t pi = ((int64_t)c * H + h) * a.max_tgt + tl;
-        const double wgt = (double)a.part_ml[pi * 2 + 1] * exp((double)a.part_ml[pi * 2] - M);
-        acc += (double)a.part_acc[pi * DH + dh] * wgt;
-        l += wgt;
-      }
-      out = l > 0.0 ? (float)(acc / l) : 0.f;
-    } else if (a.dtype) {
-      for (int c = c0; c < c1; ++c) {
-        const int64_t pi = ((int64_t)c * H + h) * a.max_tgt + tl;
-        out += a.part_acc[pi * DH + dh];
-        if (dh == 0) cnt += a.part_cnt[pi];
-      }
-    } else {
-      double acc = 0.0;
-      for (int c = c0; c < c1; ++c) {
-        const int64_t pi = ((int64_t)c * H + h) * a.max_tgt + tl;
-        acc += (double)a.part_acc[pi * DH + dh];
-        if (dh == 0) cnt += a.part_cnt[pi];
-      }
-      out = (float)acc;
     }
   }
   a.attn[e] = out;
@@ -375,42 +446,56 @@ __global__ void relayout_kernel(const T *k, const T *v, T *kb, T *vb, Plan P, in
   }
 }
 
+
+template <typename K>
+int persistent_grid(K kernel, int threads, int64_t units) {
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * per_cu));
+}
+
 template <int DH, int SCORE>
-hipError_t launch_bf16(const AttnArgs &a, hipStream_t s) {
-  const int groups = (a.max_tgt + 63) / 64;
-  const int nt = a.max_tgt >= 64 ? 4 : (a.max_tgt + 15) / 16;
+hipError_t launch_bf16(AttnArgs &a, hipStream_t s) {
+  const int nt = a.groups > 1 ? 4 : (a.max_tgt + 15) / 16;
   const dim3 block(256);
-  if (nt == 4 || groups > 1) {
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 4, SCORE>), dim3(a.grid_chunks, a.H, groups), block, 0, s, a);
-  } else if (nt == 3) {
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 3, SCORE>), dim3(a.grid_chunks, a.H, 1), block, 0, s, a);
-  } else if (nt == 2) {
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 2, SCORE>), dim3(a.grid_chunks, a.H, 1), block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, 1, SCORE>), dim3(a.grid_chunks, a.H, 1), block, 0, s, a);
+#define GO(NT)                                                                         \
+  {                                                                                    \
+    auto k = attn_bf16_kernel<DH, NT, SCORE>;                                          \
+    a.grid = persistent_grid(k, 256, a.max_units);                                     \
+    hipLaunchKernelGGL(k, dim3(a.grid), block, 0, s, a);                               \
   }
+  if (nt >= 4) GO(4) else if (nt == 3) GO(3) else if (nt == 2) GO(2) else GO(1)
+#undef GO
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_partial(const AttnArgs &a, hipStream_t s) {
-  if (a.grid_chunks <= 0 || a.n_tgt <= 0) return hipSuccess;
+hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
+  a.grid = 0;
+  if (a.max_units <= 0 || a.n_tgt <= 0) return hipSuccess;
   if (a.dtype == 1) {
     if (a.dh == 32) return a.score ? launch_bf16<32, 1>(a, s) : launch_bf16<32, 0>(a, s);
     if (a.dh == 64) return a.score ? launch_bf16<64, 1>(a, s) : launch_bf16<64, 0>(a, s);
     return hipErrorInvalidValue;
   }
-  const dim3 grid(a.grid_chunks, a.H, (a.max_tgt + 63) / 64), block(64);
+#define GO(DH, SC)                                                   \
+  {                                                                  \
+    auto k = attn_f32_kernel<DH, SC>;                                \
+    a.grid = persistent_grid(k, 64, a.max_units);                    \
+    hipLaunchKernelGGL(k, dim3(a.grid), dim3(64), 0, s, a);          \
+  }
   if (a.dh == 32) {
-    if (a.score) hipLaunchKernelGGL((attn_f32_kernel<32, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<32, 0>), grid, block, 0, s, a);
+    if (a.score) GO(32, 1) else GO(32, 0)
   } else if (a.dh == 64) {
-    if (a.score) hipLaunchKernelGGL((attn_f32_kernel<64, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_f32_kernel<64, 0>), grid, block, 0, s, a);
+    if (a.score) GO(64, 1) else GO(64, 0)
   } else {
     return hipErrorInvalidValue;
   }
+#undef GO
   return hipGetLastError();
 }
 
@@ -423,7 +508,7 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
+hipError_t launch_attention(AttnArgs &a, hipStream_t s) {
   hipError_t e = launch_attn_partial(a, s);
   if (e != hipSuccess) return e;
   return launch_attn_merge(a, s);

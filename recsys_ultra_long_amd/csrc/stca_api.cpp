@@ -72,15 +72,17 @@ struct Layout {
   size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
 };
 
-int choose_nb(int chunk_keys, int64_t n_hist, int B, int H, int max_tgt) {
-  if (chunk_keys > 0) return chunk_keys / 32;
-  const int64_t blocks = max_blocks(n_hist, B);
+// 32-key blocks per attention scheduling unit.  Units only set how finely
+// the persistent grid's ranges can be cut (the partial count is set by the
+// grid, not by the unit), so they are small: 128 keys.
+int choose_nb(int chunk_keys) { return chunk_keys > 0 ? chunk_keys / 32 : 4; }
+
+// Partial slots of the attention: one per unit, each with room for the
+// targets of one group.
+size_t partial_slots(int64_t max_chunks, int H, int max_tgt) {
   const int groups = (max_tgt + 63) / 64;
-  const int64_t want_chunks = std::max<int64_t>(1, 2048 / ((int64_t)H * groups));
-  int64_t nb = (blocks + want_chunks - 1) / want_chunks;
-  nb = std::max<int64_t>(nb, std::max(4, std::min(max_tgt, 64)));
-  nb = (nb + 3) / 4 * 4;
-  return (int)std::min<int64_t>(nb, 1 << 20);
+  const int tgs = groups > 1 ? 64 : max_tgt;
+  return (size_t)max_chunks * H * groups * tgs;
 }
 
 int validate_cfg(const stca_config *c) {
@@ -189,7 +191,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   const int64_t d = c->d, h = c->hidden, T = b->n_tgt;
   const int dh = c->d / c->H;
   L.esize = c->dtype == STCA_BF16 ? 2 : 4;
-  L.nb = choose_nb(c->chunk_keys, b->n_hist, c->B, c->H, b->max_tgt_per_user);
+  L.nb = choose_nb(c->chunk_keys);
   L.max_blocks = max_blocks(b->n_hist, c->B);
   L.max_chunks = max_chunks(b->n_hist, c->B, L.nb);
   Carver cv;
@@ -225,7 +227,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   }
   L.kv_layer = (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
   L.kv = cv.take(2 * L.kv_layer * c->M);
-  const size_t np = (size_t)L.max_chunks * c->H * b->max_tgt_per_user;
+  const size_t np = partial_slots(L.max_chunks, c->H, b->max_tgt_per_user);
   L.part_ml = cv.take(np * 2 * sizeof(float));
   L.part_acc = cv.take(np * dh * sizeof(float));
   L.part_cnt = cv.take(np * sizeof(int));
@@ -491,7 +493,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       at_.dh = dh;
       at_.nb = L.nb;
       at_.max_tgt = batch->max_tgt_per_user;
-      at_.grid_chunks = L.max_chunks;
+      attn_shape(at_, L.max_chunks);
       at_.plan = plan;
       at_.kbuf = kbuf(i);
       at_.vbuf = vbuf(i);
@@ -504,7 +506,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       at_.attn_lo = attnlo;
       at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
       at_.B = B;
-      if (batch->n_hist == 0) at_.grid_chunks = 0;
+      if (batch->n_hist == 0) at_.max_units = 0;
       if ((e = launch_attn_partial(at_, s))) return hip_fail(e, "attention");
       if ((e = rec(3 + M + 4 * i))) return hip_fail(e, "stage event");
       if ((e = launch_attn_merge(at_, s))) return hip_fail(e, "attention merge");
@@ -616,14 +618,14 @@ struct AttnLayout {
 static AttnLayout attn_layout(const stca_attn_args *a) {
   AttnLayout L;
   const size_t es = a->dtype == STCA_BF16 ? 2 : 4;
-  L.nb = choose_nb(a->chunk_keys, a->n_hist, a->B, a->H, a->max_tgt_per_user);
+  L.nb = choose_nb(a->chunk_keys);
   L.mb = max_blocks(a->n_hist, a->B);
   L.mc = max_chunks(a->n_hist, a->B, L.nb);
   Carver cv;
   L.plan = cv.take(4 * sizeof(int) * (size_t)(a->B + 1));
   L.kvl = (size_t)L.mb * 32 * a->d * es;
   L.kv = cv.take(2 * L.kvl);
-  const size_t np = (size_t)L.mc * a->H * a->max_tgt_per_user;
+  const size_t np = partial_slots(L.mc, a->H, a->max_tgt_per_user);
   L.ml = cv.take(np * 2 * sizeof(float));
   L.acc = cv.take(np * (a->d / a->H) * sizeof(float));
   L.cnt = cv.take(np * sizeof(int));
@@ -672,7 +674,8 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   at_.dh = a->d / a->H;
   at_.nb = L.nb;
   at_.max_tgt = a->max_tgt_per_user;
-  at_.grid_chunks = a->n_hist > 0 ? L.mc : 0;
+  attn_shape(at_, L.mc);
+  if (a->n_hist == 0) at_.max_units = 0;
   at_.plan = plan;
   at_.kbuf = kv;
   at_.vbuf = kv + L.kvl;

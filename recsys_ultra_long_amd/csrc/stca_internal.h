@@ -106,25 +106,35 @@ struct AttnArgs {
   int dtype;                // 0 fp32, 1 bf16
   int score;                // 0 softmax, 1 relu
   int d, H, dh;
-  int nb;                   // blocks per chunk
+  int nb;                   // 32-key blocks per scheduling unit
   int max_tgt;
-  int64_t grid_chunks;      // host bound on chunks
+  int groups;               // target groups of 64 (1 when max_tgt <= 64)
+  int tgs;                  // target slots per partial (max_tgt if one group, else 64)
+  int64_t max_units;        // host bound on units (chunks x H x groups); 0: nothing to do
+  int grid;                 // persistent workgroups (set by launch_attn_partial)
   Plan plan;
   const void *kbuf, *vbuf;  // blocked K/V of one layer
   const void *q;            // [n_tgt, d] scaled queries
   int64_t n_tgt;
-  float *part_ml;           // [chunks, H, max_tgt, 2]
-  float *part_acc;          // [chunks, H, max_tgt, dh]
-  int *part_cnt;            // [chunks, H, max_tgt]
+  float *part_ml;           // [units, tgs, 2]
+  float *part_acc;          // [units, tgs, dh]
+  int *part_cnt;            // [units, tgs]
   float *attn;              // [n_tgt, d] fp32 (required)
   void *attn_lo;            // [n_tgt, d] config dtype copy (optional)
   int *active;              // [n_tgt, H] (optional)
   int B;
 };
 
-hipError_t launch_attention(const AttnArgs &a, hipStream_t s);  // partials + merge
-hipError_t launch_attn_partial(const AttnArgs &a, hipStream_t s);
+// Partials + merge.  launch_attn_partial fills a.grid, which the merge reads.
+hipError_t launch_attention(AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s);
+
+inline void attn_shape(AttnArgs &a, int64_t max_chunks) {
+  a.groups = (a.max_tgt + 63) / 64;
+  a.tgs = a.groups > 1 ? 64 : a.max_tgt;
+  a.max_units = max_chunks * a.H * a.groups;
+}
 
 // Row-major K, V ([n_hist, d]) -> blocked K/V layout (for stca_attention) and
 // the reverse (for kv_dump).
