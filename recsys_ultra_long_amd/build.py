@@ -28,8 +28,8 @@ COMMON = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+def sources(src_dir: str = CSRC):
+    return sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir)
                   if f.endswith((".hip", ".cpp")))
 
 
@@ -40,8 +40,8 @@ def _hipcc() -> str:
     return h
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, obj_dir: str) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *COMMON, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stderr or "").splitlines()
@@ -53,21 +53,26 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra=None, jobs: int = 8) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = True, extra=None, jobs: int = 8, out=None, src_dir=None) -> str:
+    """Compile every source of ``src_dir`` (default csrc/) and link ``out``
+    (default the in-tree libstca.so)."""
+    src_dir = src_dir or CSRC
+    lib_path = out or LIB
+    obj_dir = OUT_DIR if src_dir == CSRC else os.path.join(OUT_DIR, "v_" + str(abs(hash(src_dir))))
+    os.makedirs(obj_dir, exist_ok=True)
     extra = list(extra or [])
-    srcs = sources()
+    srcs = sources(src_dir)
     with ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, obj_dir), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -21,7 +21,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/stca.h"
+#include "stca.h"
 #include "stca_internal.h"
 
 using namespace stca;

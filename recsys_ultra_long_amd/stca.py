@@ -81,13 +81,15 @@ class StcaError(RuntimeError):
 
 
 def load() -> C.CDLL:
-    """Load libstca.so from the package directory (raises if it is not built)."""
+    """Load libstca.so from the package directory (or the path in the
+    STCA_LIBRARY environment variable); raises if it is not built."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = os.environ.get("STCA_LIBRARY", LIB_PATH)
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m recsys_ultra_long_amd.build`")
-        lib = C.CDLL(LIB_PATH)
+        lib = C.CDLL(path)
         lib.stca_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(C.c_size_t)]
         lib.stca_forward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights),
                                      C.POINTER(Outputs), _vp, C.c_size_t, _vp]

@@ -231,7 +231,14 @@ def test_permutation_invariance_gpu():
 
 def test_rlb_equals_single_target_runs():
     """P4 on the device: m targets sharing a user's K/V equal m single-target
-    users with the same history (bitwise with a fixed chunk size)."""
+    users with the same history.  The K/V side and the first layer's queries
+    are computed identically (bitwise).  The persistent attention grid cuts a
+    user's history into partials according to the whole batch; each partial
+    scales its probabilities against its own running max before they are
+    rounded to bf16 for the PV product, so first-layer attention agrees at that
+    quantisation level (2^-9 per weight, a few 1e-4 per row), not bitwise.
+    Deeper layers carry the difference through bf16 roundings of attn and o, so
+    end to end the bar is the bf16 tolerance."""
     p = I.make_problem(_small(3, B=2, L=500, m=20))
     B, m = p.spec.B, p.spec.m
     ho, to = p.hist_offsets, p.tgt_offsets
@@ -244,10 +251,17 @@ def test_rlb_equals_single_target_runs():
     q = I.Problem(replace(p.spec, B=B * m, m=1), np.asarray(hoff, np.int32),
                   np.concatenate(hid).astype(np.int32), np.asarray(toff, np.int32),
                   p.tgt_ids, p.q0, p.table, p.layers, p.z, p.wz)
-    g1 = gpu_run(p, chunk_keys=128)
-    g2 = gpu_run(q, chunk_keys=128)
+    g1 = gpu_run(p, chunk_keys=128, dumps=("kv", "q"))
+    g2 = gpu_run(q, chunk_keys=128, dumps=("kv", "q"))
+    for i in range(p.spec.M):
+        for u in range(B):
+            a, b = ho[u], ho[u + 1]
+            for t in range(to[u], to[u + 1]):
+                assert np.array_equal(g1["kv"][i, :, a:b], g2["kv"][i, :, hoff[t]:hoff[t + 1]])
+    assert np.array_equal(g1["q"][0], g2["q"][0])
+    assert row_rel_err(g2["attn"][0], g1["attn"][0]) < 2e-3
     for k in ("z", "o", "attn"):
-        assert np.array_equal(g1[k], g2[k]), k
+        assert row_rel_err(g2[k], g1[k]) < TOL["bf16"], k
 
 
 def test_deterministic_rerun():
