@@ -89,7 +89,21 @@ def main():
     ap.add_argument("--path", default="staged", choices=["staged", "fused"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 1 GiB (x5), to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the STCA forward "
               "shards by user with no exchange, so throughput at N GPUs is N times this "
@@ -167,6 +181,16 @@ def main():
                  "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                  "launch_ms": round(t_attn * 1e3, 4),
                  "per_launch": f"{n_hist} tokens x {4 * d} B + {T} targets x {2 * d} B"}
+    # HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    # was taken on the current kernel sources
+    from recsys_ultra_long_amd import profiling
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.md"))
+    if tr is not None:
+        for roof, pick in ((roof_hist, lambda k: k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k),
+                           (roof_attn, lambda k: k.startswith("attn_bf16_kernel<"))):
+            hits = [v["hbm_bytes"] for k, v in tr["kernels"].items() if pick(k)]
+            if hits:
+                roof["traffic"] = round(max(hits))
     dominant = roof_hist if sum(hist) >= sum(part) else roof_attn
 
     value = n_hist * M / (ms * 1e-3)

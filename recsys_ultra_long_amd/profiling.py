@@ -1,0 +1,119 @@
+"""rocprofv3 output -> short text summaries under profiles/.
+
+    python -m recsys_ultra_long_amd.profiling kernels  <stats.csv> <out.md> <command...>
+    python -m recsys_ultra_long_amd.profiling traffic  <fetch.csv> <write.csv> \
+        <copy_fetch.csv> <copy_write.csv> <copy_bytes> <out.md> <command...>
+
+``kernels`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
+average duration).  ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of the profiled
+kernels, each scaled by what the same counter reads for a plain device copy
+of known size (``bench.py --copy-calibration``).  The traffic summary carries
+a hash of the kernel sources; ``bench.py`` reports the figures only while the
+sources are unchanged.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    k = re.sub(r"stca::\(anonymous namespace\)::", "", kernel)
+    k = re.sub(r"\(stca::\w+\)$", "", k)
+    return k.replace("void ", "").strip()
+
+
+def kernel_stats(path: str):
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        calls = int(float(r.get("Calls", 0)))
+        total = float(r.get("TotalDurationNs", 0))
+        avg = float(r.get("AverageNs", total / max(calls, 1)))
+        out.append((short_name(name), calls, total, avg, float(r.get("Percentage", 0))))
+    out.sort(key=lambda x: -x[2])
+    return out
+
+
+def pmc_per_kernel(path: str, counter: str):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            agg[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def write_kernels(stats_csv: str, out: str, command: str):
+    st = kernel_stats(stats_csv)
+    lines = [f"# rocprofv3 kernel trace summary", "", f"Command: `{command}`", "",
+             "| kernel | calls | avg us | total us | % |", "|---|---|---|---|---|"]
+    for name, calls, total, avg, pct in st:
+        lines.append(f"| `{name}` | {calls} | {avg / 1e3:.2f} | {total / 1e3:.1f} | {pct:.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def write_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out, command):
+    fetch = pmc_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = pmc_per_kernel(write_csv, "WRITE_SIZE")
+    cf = pmc_per_kernel(cfetch_csv, "FETCH_SIZE")
+    cw = pmc_per_kernel(cwrite_csv, "WRITE_SIZE")
+    copy_kernel = max(cf, key=lambda k: cf[k])            # the big copy dispatch
+    copy_bytes = float(copy_bytes)
+    f_scale = copy_bytes / (cf[copy_kernel] * 1024.0)
+    w_scale = copy_bytes / (cw.get(copy_kernel, max(cw.values())) * 1024.0)
+    data = {"source_hash": source_hash(), "copy_kernel": copy_kernel, "copy_bytes": copy_bytes,
+            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for k in fetch:
+        data["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0),
+                              "hbm_bytes": fetch[k] * 1024 * f_scale + write.get(k, 0.0) * 1024 * w_scale}
+    lines = ["# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE)", "",
+             f"Command: `{command}`", "",
+             f"Calibration: a device copy of {copy_bytes:.0f} bytes (`{copy_kernel}`) reads "
+             f"FETCH_SIZE x {f_scale:.3f} and WRITE_SIZE x {w_scale:.3f} of its true bytes.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes |", "|---|---|---|---|"]
+    for k, v in sorted(data["kernels"].items(), key=lambda kv: -kv[1]["hbm_bytes"]):
+        lines.append(f"| `{k}` | {v['fetch_kib']:.0f} | {v['write_kib']:.0f} | {v['hbm_bytes']:.4g} |")
+    lines += ["", "```json", json.dumps(data, indent=1), "```", ""]
+    open(out, "w").write("\n".join(lines))
+
+
+def read_traffic(path: str):
+    """The JSON block of a traffic summary, or None if missing or stale."""
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    return data if data.get("source_hash") == source_hash() else None
+
+
+if __name__ == "__main__":
+    cmd = sys.argv[1]
+    if cmd == "kernels":
+        write_kernels(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif cmd == "traffic":
+        write_traffic(*sys.argv[2:8], " ".join(sys.argv[8:]))
+    elif cmd == "hash":
+        print(source_hash())
+    else:
+        raise SystemExit(__doc__)
