@@ -86,7 +86,11 @@ typedef struct {
   int32_t dtype;        /* STCA_F32 or STCA_BF16: table, weights, K/V, queries    */
   int32_t score;        /* STCA_SCORE_*                                           */
   int32_t qmode;        /* STCA_Q_*                                               */
-  int32_t path;         /* STCA_PATH_*                                            */
+  int32_t path;         /* STCA_PATH_*.  STCA_PATH_FUSED ([WeChat] §1.1): per layer
+                           one kernel gathers, encodes and attends 64 keys at a time
+                           and no K/V tensor is kept; bf16 only, d = 256 (d_h 32
+                           or 64) or d = 128 (d_h 32), STCA_FLAG_KV_LN set, at most
+                           64 targets per user; otherwise STCA_ERR_UNSUPPORTED     */
   int32_t flags;        /* STCA_FLAG_*                                            */
   int32_t chunk_keys;   /* keys per split-L chunk (multiple of 32); 0 = automatic  */
 } stca_config;
@@ -137,7 +141,7 @@ typedef struct {
 } stca_weights;
 
 typedef struct {
-  float *z;            /* [n_tgt, d] required: z (fusion) or O_M (linear)           */
+  float *z;            /* [n_tgt, d] z (fusion) or O_M (linear); required if n_tgt > 0 */
   float *o_layers;     /* [M, n_tgt, d] optional: o^(i) after W_O                    */
   float *attn;         /* [M, n_tgt, d] optional: heads concatenated, before W_O     */
   int32_t *active;     /* [M, n_tgt, H] optional, STCA_SCORE_RELU: #{j : s_j > 0}    */
@@ -145,7 +149,8 @@ typedef struct {
                           them (after W_Q and the 1/sqrt(d_h) scale), config dtype   */
   void *kv_dump;       /* [M, 2, n_hist, d] optional: K then V rows of every layer as
                           the attention reads them, config dtype (staged path only)  */
-  void *x_dump;        /* [n_hist, d] optional: gathered history rows (table dtype)  */
+  void *x_dump;        /* [n_hist, d] optional: gathered history rows (table dtype).
+                          Fused path: written with layer 0's encoding            */
   int32_t *dev_status; /* optional: STCA_DEV_* bits OR-ed in on the device           */
   /* Optional stage timing: host array of caller-created hipEvent_t handles.  The
    * library records (hipEventRecord on the call's stream, no synchronisation) up
@@ -153,6 +158,8 @@ typedef struct {
    *   0            start of the call
    *   1            weights prepared and batch planned
    *   2 + i        history encoding (gather, FFN, LN, W_K|W_V) of layer i done, i < M
+   *                (fused path: all M recorded right after event 1; the
+   *                encoding is then part of each layer's attention partials)
    *   2 + M + 4i   query of layer i done
    *   3 + M + 4i   attention partials of layer i done
    *   4 + M + 4i   partial merge of layer i done

@@ -28,15 +28,15 @@
 // so every MFMA operand fragment is one 16-byte load.
 #include <algorithm>
 
+#include "attn_block.h"
 #include "stca_internal.h"
 
 namespace stca {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;
-
-DEV float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float kLog2e = kAttnLog2e;
+constexpr float kNegBig = kAttnNegBig;
+DEV float ex2(float x) { return attn_ex2(x); }
 
 // Position of global unit `unit` in the sequence: user u, pair index within
 // the user (group * H + head), first unit of the pair, units of the pair.
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int g16 = lane >> 4, c16 = lane & 15;
   const bf16_t *Q = (const bf16_t *)a.q;
   const bf16_t *Kb = (const bf16_t *)a.kbuf, *Vb = (const bf16_t *)a.vbuf;
-  const int kr0 = 8 * (c16 >> 2) + (c16 & 3);  // permuted key row of score tile 0
+  const int kr0 = attn_key_row(lane);  // permuted key row of score tile 0
 
   while (unit < unit_end) {
     const UnitPos pos = decode_unit(P, a.B, HG, unit);
@@ -98,31 +98,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       const int b0 = P.pblk[u] + cl * a.nb;
       const int b1 = min(P.pblk[u + 1], P.pblk[u] + (cl + seg_end - unit) * a.nb);
 
-      bf16x8 qf[NT][KS];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int tl = t0 + n * 16 + c16;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          if (tl < m_u) {
-            qf[n][k] = ld8(Q + (int64_t)(tbase + tl) * a.d + h * DH + k * 32 + g16 * 8);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[n][k][e] = 0;
-          }
-        }
-      }
-      float mrun[NT], lrun[NT];
-      int cnt[NT];
-      f32x4 o[DT][NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        mrun[n] = kNegBig;
-        lrun[n] = 0.f;
-        cnt[n] = 0;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      AttnState<DH, NT> st;
+      attn_reset(st);
+      attn_load_q(st, Q, a.d, h, tbase, t0, m_u, lane);
       bf16x8 kf[2][KS], vf[DT];
       auto load_kv = [&](int b, bf16x8 (&kk)[2][KS], bf16x8 (&vv)[DT]) {
         const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
@@ -139,76 +117,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         bf16x8 kn[2][KS], vn[DT];
         if (b + 4 < b1) load_kv(b + 4, kn, vn);  // next block of this wave
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 st[2][NT];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            st[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < KS; ++k) st[kt][n] = mfma16(kf[kt][k], qf[n][k], st[kt][n]);
-          }
         // keys of this lane: 8g + 4kt + r; valid while below the user's length
-        const int nvalid = L - (b - P.pblk[u]) * 32;
-        bf16x8 pk[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (SCORE == 0) {
-            float mx = kNegBig;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (8 * g16 + 4 * kt + r < nvalid) mx = fmaxf(mx, st[kt][n][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrun[n], mx);
-            const float corr = ex2((mrun[n] - mnew) * kLog2e);
-            mrun[n] = mnew;
-            const float mb = mnew * kLog2e;
-            float psum = 0.f;
-            float pv[8];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                float p = 0.f;
-                if (8 * g16 + 4 * kt + r < nvalid) p = ex2(fmaf(st[kt][n][r], kLog2e, -mb));
-                pv[4 * kt + r] = p;
-              }
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
-              pk[n][e] = (short)(pr & 0xffff);
-              pk[n][e + 1] = (short)(pr >> 16);
-              psum += bf2f((bf16_t)(pr & 0xffff)) + bf2f((bf16_t)(pr >> 16));
-            }
-            lrun[n] = lrun[n] * corr + psum;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) o[t][n] *= corr;
-          } else {
-            float pv[8];
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float sc = st[kt][n][r];
-                const bool on = (8 * g16 + 4 * kt + r < nvalid) && sc > 0.f;
-                cnt[n] += on ? 1 : 0;
-                pv[4 * kt + r] = on ? sc : 0.f;
-              }
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
-              pk[n][e] = (short)(pr & 0xffff);
-              pk[n][e + 1] = (short)(pr >> 16);
-            }
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) o[t][n] = mfma16(vf[t], pk[n], o[t][n]);
+        attn_block<DH, NT, SCORE>(st, kf, vf, L - (b - P.pblk[u]) * 32, lane);
         if (b + 4 < b1) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
@@ -222,21 +132,21 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       // ---- merge the four waves in LDS, write this segment's partial
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        float l = lrun[n];
+        float l = st.lrun[n];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        int cn = cnt[n];
+        int cn = st.cnt[n];
         cn += __shfl_xor(cn, 16);
         cn += __shfl_xor(cn, 32);
         if (g16 == 0) {
-          sm_m[w][n * 16 + c16] = mrun[n];
+          sm_m[w][n * 16 + c16] = st.mrun[n];
           sm_l[w][n * 16 + c16] = l;
           sm_c[w][n * 16 + c16] = cn;
         }
 #pragma unroll
         for (int t = 0; t < DT; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = o[t][n][r];
+          for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = st.o[t][n][r];
       }
       __syncthreads();
       const int64_t pbase = (int64_t)unit * a.tgs;
@@ -354,8 +264,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 // ------------------------------------------------------------------ merge
 // One thread per (target, feature): fold the partials of the target's
-// (user, group, head) pair in workgroup order.
+// (user, group, head) in workgroup order.
 //   softmax: attn = sum_w acc_w e^{m_w - M} / sum_w l_w e^{m_w - M};  ReLU: sums.
+// Streaming partials: a workgroup's segment of a pair is stored at the
+// segment's first unit.  Fused partials (one per workgroup and user, all
+// heads): slot workgroup + user, units = the user's 64-key tiles.
 template <int SCORE>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int d = a.d, DH = a.dh, H = a.H, G = a.groups, HG = H * G;
@@ -371,18 +284,28 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int tl = t - P.toff[u];
     const int grp = G > 1 ? tl / 64 : 0;
     const int tg = tl - grp * 64;
-    const int nc = P.coff[u + 1] - P.coff[u];
-    if (nc > 0) {
-      const int per = units_per_wg(P.coff[a.B] * HG, a.grid);
-      const int first = P.coff[u] * HG + (grp * H + h) * nc;
-      const int w0 = first / per, w1 = (first + nc - 1) / per;
+    int first, nu, per;
+    if (a.fused) {
+      first = P.pblk[u] / 2;
+      nu = (P.pblk[u + 1] - P.pblk[u]) / 2;
+      per = units_per_wg(P.pblk[a.B] / 2, a.grid);
+    } else {
+      nu = P.coff[u + 1] - P.coff[u];
+      first = P.coff[u] * HG + (grp * H + h) * nu;
+      per = units_per_wg(P.coff[a.B] * HG, a.grid);
+    }
+    auto pidx = [&](int wg) -> int64_t {
+      if (a.fused) return partial_index(wg + u, H, h, a.tgs, tg);
+      return (int64_t)max(first, wg * per) * a.tgs + tg;
+    };
+    if (nu > 0) {
+      const int w0 = first / per, w1 = (first + nu - 1) / per;
       if (SCORE == 0 && a.dtype) {
         float M = kNegBig;
-        for (int wg = w0; wg <= w1; ++wg)
-          M = fmaxf(M, a.part_ml[((int64_t)max(first, wg * per) * a.tgs + tg) * 2]);
+        for (int wg = w0; wg <= w1; ++wg) M = fmaxf(M, a.part_ml[pidx(wg) * 2]);
         float acc = 0.f, l = 0.f;
         for (int wg = w0; wg <= w1; ++wg) {
-          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          const int64_t pi = pidx(wg);
           const float fct = ex2((a.part_ml[pi * 2] - M) * kLog2e);
           acc += a.part_acc[pi * DH + dh] * fct;
           l += a.part_ml[pi * 2 + 1] * fct;
@@ -390,11 +313,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
         out = l > 0.f ? acc / l : 0.f;
       } else if (SCORE == 0) {  // fp32 path: normalised partials, fp64 fold
         double M = -1.0e300;
-        for (int wg = w0; wg <= w1; ++wg)
-          M = fmax(M, (double)a.part_ml[((int64_t)max(first, wg * per) * a.tgs + tg) * 2]);
+        for (int wg = w0; wg <= w1; ++wg) M = fmax(M, (double)a.part_ml[pidx(wg) * 2]);
         double acc = 0.0, l = 0.0;
         for (int wg = w0; wg <= w1; ++wg) {
-          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          const int64_t pi = pidx(wg);
           const double wgt = (double)a.part_ml[pi * 2 + 1] * exp((double)a.part_ml[pi * 2] - M);
           acc += (double)a.part_acc[pi * DH + dh] * wgt;
           l += wgt;
@@ -403,7 +325,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       } else {
         double acc = 0.0;
         for (int wg = w0; wg <= w1; ++wg) {
-          const int64_t pi = (int64_t)max(first, wg * per) * a.tgs + tg;
+          const int64_t pi = pidx(wg);
           acc += (double)a.part_acc[pi * DH + dh];
           if (dh == 0) cnt += a.part_cnt[pi];
         }
@@ -450,8 +372,9 @@ __global__ void relayout_kernel(const T *k, const T *v, T *kb, T *vb, Plan P, in
 template <typename K>
 int persistent_grid(K kernel, int threads, int64_t units) {
   int dev = 0, cus = 256, per_cu = 1;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   return (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * per_cu));

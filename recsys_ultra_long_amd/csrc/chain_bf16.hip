@@ -17,6 +17,7 @@
 // accumulation; LN statistics are fp32.
 #include <algorithm>
 
+#include "attn_block.h"
 #include "stca_internal.h"
 
 namespace stca {
@@ -134,8 +135,31 @@ DEV void zero(f32x16 (&acc)[RT][CT]) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 }
 
-template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT>
-__global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void chain_kernel(ChainArgs a) {
+// LDS of one row-chain workgroup.
+template <int D, int TT, bool FFN>
+struct ChainSmem {
+  static constexpr int R = 32 * TT;
+  static constexpr int XLD = D + kPad;
+  static constexpr int GLD = kHC + kPad;
+  __attribute__((aligned(16))) bf16_t xs[R * XLD];
+  __attribute__((aligned(16))) bf16_t gs[FFN ? 2 : 1][FFN ? R * GLD : 8];
+  float red[2][4][R];
+  int s_id[R], s_tok[R];
+};
+
+// Fused-path K/V staging of one wave: its HW heads' K [hh][key 0..63][d_h]
+// and V^T [hh][d_h][key 0..63] for the 64 keys of the tile (rows padded).
+template <int FDH>
+struct FusedStage {
+  static constexpr int LDK = FDH + 8;
+  static constexpr int LDV = 64 + 8;
+};
+
+// One tile of rows (64 for the history, 32 on the query side) through the
+// chain; OUT_KV writes blocked K/V to HBM, OUT_ROWS rows, OUT_FUSED stages
+// this wave's K/V features in `kvs` (FDH = head width) for the fused attention.
+template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT, int FDH = 0>
+DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN> &sm, bf16_t *kvs) {
   constexpr int R = 32 * TT;  // rows (tokens) per workgroup
   // Every contraction is computed "feature-major": MFMA rows are output
   // features, MFMA columns are the 64 rows (tokens) of the tile.  A lane then
@@ -144,10 +168,11 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
   constexpr int XLD = D + kPad;
   constexpr int GLD = kHC + kPad;
   constexpr int FT = D / 128;  // 32-feature tiles per wave for d-wide outputs
-  __shared__ __attribute__((aligned(16))) bf16_t xs[R * XLD];
-  __shared__ __attribute__((aligned(16))) bf16_t gs[FFN ? 2 : 1][FFN ? R * GLD : 8];
-  __shared__ float red[2][4][R];
-  __shared__ int s_id[R], s_tok[R];
+  bf16_t *const xs = sm.xs;
+  auto &gs = sm.gs;
+  auto &red = sm.red;
+  int *const s_id = sm.s_id;
+  int *const s_tok = sm.s_tok;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -155,7 +180,6 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
   const int l32 = lane & 31;
   const int hi = lane >> 5;         // which half of the wave
   const int kg = hi * 16;           // lane's k offset inside a 32-wide k block
-  const int64_t row0 = (int64_t)blockIdx.x * R;
   const bf16_t *table = (const bf16_t *)a.table;
   // MFMA-column (token) operands read from LDS rows
   const bf16_t *bx[TT];
@@ -423,10 +447,14 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
 
   // ------------------------------------------------------------ projection
   if (PROJ) {
-    if (OUT == OUT_KV) {
+    if (OUT == OUT_KV || OUT == OUT_FUSED) {
       const int H = a.H;
       const int DH = D / H;
       bf16_t *kb = (bf16_t *)a.kbuf, *vb = (bf16_t *)a.vbuf;
+      constexpr int LDK = FusedStage<FDH>::LDK, LDV = FusedStage<FDH>::LDV;
+      constexpr int HW = FDH > 0 ? (D / 4) / FDH : 1;  // heads per wave (fused)
+      bf16_t *const kst = kvs;                           // [HW][64][LDK]
+      bf16_t *const vst = kvs + HW * 64 * LDK;           // [HW][FDH][LDV]
 #pragma unroll
       for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T: 4 consecutive features / token
         f32x16 acc[YT][TT];
@@ -439,16 +467,21 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
-          if (blk >= total_blocks) continue;
+          if (OUT == OUT_KV && blk >= total_blocks) continue;
 #pragma unroll
           for (int i = 0; i < YT; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
-              const int h = f / DH, dh = f % DH;
               u32x2 v = {pack_bf2(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
                          pack_bf2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
-              *reinterpret_cast<u32x2 *>(kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh) = v;
+              if constexpr (OUT == OUT_FUSED) {
+                const int fl = (sp * YT + i) * 32 + 8 * q + 4 * hi;  // wave-local feature
+                *reinterpret_cast<u32x2 *>(kst + ((fl / FDH) * 64 + t * 32 + l32) * LDK + fl % FDH) = v;
+              } else {
+                const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
+                const int h = f / DH, dh = f % DH;
+                *reinterpret_cast<u32x2 *>(kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh) = v;
+              }
             }
         }
       }
@@ -467,17 +500,22 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
-          if (blk >= total_blocks) continue;
+          if (OUT == OUT_KV && blk >= total_blocks) continue;
 #pragma unroll
           for (int j = 0; j < YT; ++j) {
-            const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
-            const int h = f / DH, dh = f % DH;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int key = 8 * q + 4 * hi;
               u32x2 v = {pack_bf2(acc[t][j][4 * q], acc[t][j][4 * q + 1]),
                          pack_bf2(acc[t][j][4 * q + 2], acc[t][j][4 * q + 3])};
-              *reinterpret_cast<u32x2 *>(vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
+              if constexpr (OUT == OUT_FUSED) {
+                const int fl = (sp * YT + j) * 32 + l32;
+                *reinterpret_cast<u32x2 *>(vst + ((fl / FDH) * FDH + fl % FDH) * LDV + t * 32 + key) = v;
+              } else {
+                const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
+                const int h = f / DH, dh = f % DH;
+                *reinterpret_cast<u32x2 *>(vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
+              }
             }
           }
         }
@@ -519,6 +557,157 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
       }
     }
   }
+}
+
+template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT>
+__global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void chain_kernel(ChainArgs a) {
+  __shared__ ChainSmem<D, TT, FFN> sm;
+  chain_tile<D, TT, IN, FFN, LN, PROJ, OUT>(a, (int64_t)blockIdx.x * (32 * TT), sm, nullptr);
+}
+
+// ---------------------------------------------------------------- fused path
+// "Lookup while computing" ([WeChat] §1.1): a persistent workgroup walks a
+// contiguous range of 64-key tiles (every user padded to whole tiles).  For
+// each tile it gathers the embedding rows, runs the history FFN, LN and
+// W_K | W_V, keeps the tile's K/V in LDS -- each wave has produced exactly
+// the features of its own heads, so the staging is wave-private -- and folds
+// those keys at once into the online-softmax (or ReLU) state of the user's
+// targets for its heads, held in registers across the user's tiles.  No K/V
+// tensor exists in HBM.  A partial is written when the user changes or the
+// range ends, into slot (workgroup + user): ranges are contiguous and users
+// ordered, so along the sequence of (workgroup, user) segments both indices
+// only grow and each step raises one of them -- the slots are distinct and
+// fewer than grid + B.
+template <int D, int DH, int NT, int SCORE>
+__global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChainArgs a, AttnArgs at) {
+  constexpr int HW = (D / 4) / DH;  // heads per wave
+  constexpr int KS = DH / 32, DT = DH / 16;
+  constexpr int LDK = FusedStage<DH>::LDK, LDV = FusedStage<DH>::LDV;
+  constexpr int KVW = HW * 64 * LDK + HW * DH * LDV;
+  __shared__ ChainSmem<D, 2, true> sm;
+  __shared__ __attribute__((aligned(16))) bf16_t kvs_all[4][KVW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int kr0 = attn_key_row(lane);
+  bf16_t *const kvs = kvs_all[w];
+  const bf16_t *const vst = kvs + HW * 64 * LDK;
+  const Plan P = at.plan;
+  const int H = at.H;
+  const int tiles = P.pblk[at.B] / 2;
+  const int per = (tiles + (int)gridDim.x - 1) / (int)gridDim.x;
+  int tile = (int)blockIdx.x * per;
+  const int tend = min(tiles, tile + per);
+  const bf16_t *Q = (const bf16_t *)at.q;
+  AttnState<DH, NT> st[HW];
+  int cur_u = -1;
+
+  auto flush = [&](int u) {
+    const int m_u = P.toff[u + 1] - P.toff[u];
+    const int slot = (int)blockIdx.x + u;
+#pragma unroll
+    for (int hh = 0; hh < HW; ++hh) {
+      const int h = w * HW + hh;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float l = st[hh].lrun[n];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        int cn = st[hh].cnt[n];
+        cn += __shfl_xor(cn, 16);
+        cn += __shfl_xor(cn, 32);
+        const int tl = n * 16 + c16;
+        if (tl < m_u) {
+          const int64_t idx = partial_index(slot, H, h, at.tgs, tl);
+          if (g16 == 0) {
+            if (SCORE == 0) {
+              at.part_ml[idx * 2] = st[hh].mrun[n];
+              at.part_ml[idx * 2 + 1] = l;
+            } else {
+              at.part_cnt[idx] = cn;
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            const f32x4 v = st[hh].o[t][n];
+            *reinterpret_cast<f32x4 *>(at.part_acc + idx * DH + t * 16 + 4 * g16) = v;
+          }
+        }
+      }
+    }
+  };
+
+  for (; tile < tend; ++tile) {
+    const int u = upper_index(P.pblk, at.B, tile * 2);
+    const int tbase = P.toff[u];
+    const int m_u = P.toff[u + 1] - tbase;
+    // a user without targets needs no K/V (only the optional input dump)
+    if (m_u == 0 && !a.in_dump) continue;
+    if (u != cur_u) {
+      if (cur_u >= 0) flush(cur_u);
+      cur_u = u;
+#pragma unroll
+      for (int hh = 0; hh < HW; ++hh) {
+        attn_reset(st[hh]);
+        attn_load_q(st[hh], Q, at.d, w * HW + hh, tbase, 0, m_u, lane);
+      }
+    }
+    __syncthreads();  // every wave is done with the previous tile's rows
+    chain_tile<D, 2, IN_GATHER_CSR, true, true, true, OUT_FUSED, DH>(a, (int64_t)tile * 64, sm, kvs);
+    // the staging was written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (m_u == 0) continue;
+    const int L = P.hoff[u + 1] - P.hoff[u];
+    const int kbase = (tile * 2 - P.pblk[u]) * 32;  // user-local index of the tile's first key
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int nvalid = L - (kbase + blk * 32);
+      if (nvalid <= 0) break;
+#pragma unroll
+      for (int hh = 0; hh < HW; ++hh) {
+        bf16x8 kf[2][KS], vf[DT];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int k = 0; k < KS; ++k)
+            kf[kt][k] = ld8(kvs + (hh * 64 + blk * 32 + kr0 + 4 * kt) * LDK + k * 32 + g16 * 8);
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          vf[t] = ld8(vst + (hh * DH + t * 16 + c16) * LDV + blk * 32 + g16 * 8);
+        attn_block<DH, NT, SCORE>(st[hh], kf, vf, nvalid, lane);
+      }
+    }
+  }
+  if (cur_u >= 0) flush(cur_u);
+}
+
+template <int D, int DH, int NT, int SCORE>
+hipError_t launch_fused_t(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s) {
+  auto k = fused_kernel<D, DH, NT, SCORE>;
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int64_t g = std::min<int64_t>(max_tiles, (int64_t)cus * per_cu);
+  g = std::max<int64_t>(1, std::min<int64_t>(g, at.max_grid));
+  at.grid = (int)g;
+  hipLaunchKernelGGL(k, dim3(at.grid), dim3(kThreads), 0, s, a, at);
+  return hipGetLastError();
+}
+
+template <int D, int DH>
+hipError_t launch_fused_d(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s) {
+  const int nt = (at.max_tgt + 15) / 16;
+  if (at.score) {
+    if (nt <= 1) return launch_fused_t<D, DH, 1, 1>(a, at, max_tiles, s);
+    if (nt <= 2) return launch_fused_t<D, DH, 2, 1>(a, at, max_tiles, s);
+    return launch_fused_t<D, DH, 4, 1>(a, at, max_tiles, s);
+  }
+  if (nt <= 1) return launch_fused_t<D, DH, 1, 0>(a, at, max_tiles, s);
+  if (nt <= 2) return launch_fused_t<D, DH, 2, 0>(a, at, max_tiles, s);
+  return launch_fused_t<D, DH, 4, 0>(a, at, max_tiles, s);
 }
 
 // History rows: 64-token tiles (two 4-wave workgroups per CU at d <= 256;
@@ -580,6 +769,16 @@ __global__ __launch_bounds__(256) void pack_batch_kernel(PackBatch pb) {
 }
 
 }  // namespace
+
+hipError_t launch_fused(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s) {
+  at.grid = 0;
+  if (max_tiles <= 0 || (at.n_tgt <= 0 && !a.in_dump)) return hipSuccess;
+  if (at.max_tgt > 64 || !a.ln || at.max_grid < 1) return hipErrorInvalidValue;
+  if (a.d == 256 && at.dh == 32) return launch_fused_d<256, 32>(a, at, max_tiles, s);
+  if (a.d == 256 && at.dh == 64) return launch_fused_d<256, 64>(a, at, max_tiles, s);
+  if (a.d == 128 && at.dh == 32) return launch_fused_d<128, 32>(a, at, max_tiles, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;

@@ -32,7 +32,7 @@ __device__ int block_exclusive_scan(int v, int *sh, int &total) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int *__restrict__ hist_off, const int *__restrict__ tgt_off, int B, long long n_hist,
-    long long n_tgt, int max_tgt, int nb, Plan plan, int *status) {
+    long long n_tgt, int max_tgt, int nb, int align, Plan plan, int *status) {
   __shared__ int sh[kPlanThreads];
   __shared__ int bad_h, bad_t;
   const int t = threadIdx.x;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     int nbk = 0, nch = 0;
     if (u < B) {
       int lh = bh ? 0 : hist_off[u + 1] - hist_off[u];
-      nbk = (lh + 31) >> 5;
+      nbk = (lh + 32 * align - 1) / (32 * align) * align;
       nch = (nbk + nb - 1) / nb;
     }
     int tb, tc;
@@ -79,10 +79,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 }  // namespace
 
 hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
-                       int64_t n_tgt, int max_tgt, int nb, Plan plan, int *status,
+                       int64_t n_tgt, int max_tgt, int nb, int align, Plan plan, int *status,
                        hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, hist_off, tgt_off, B,
-                     (long long)n_hist, (long long)n_tgt, max_tgt, nb, plan, status);
+                     (long long)n_hist, (long long)n_tgt, max_tgt, nb, align, plan, status);
   return hipGetLastError();
 }
 

@@ -13,6 +13,9 @@
 //   4. per layer: query (q1 from x_t, or the fusion of [o_1..o_i | x_t]),
 //      Q = q W_Q / sqrt(d_h); attention partials and merge; o = attn W_O;
 //   5. z = SwiGLU([o_1 | .. | o_M | x_t] W_Z) [+ LN]   (linear mode: z = O_M).
+// On the fused path (bf16) step 3 disappears: per layer, after the query, one
+// persistent kernel gathers, encodes and attends tile by tile, and no K/V
+// buffer exists; the merge and W_O follow as above.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -62,9 +65,12 @@ struct PrepLayer {
 };
 
 struct Layout {
+  bool fused = false;
   int nb = 1;              // blocks per chunk
   int64_t max_blocks = 0;  // host bound
   int64_t max_chunks = 0;
+  int64_t max_tiles = 0;   // fused: 64-key tiles (host bound)
+  int fused_grid = 0;      // fused: partial buffers hold this many workgroups
   size_t esize = 2;
   size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
@@ -101,7 +107,6 @@ int validate_cfg(const stca_config *c) {
     return fail(STCA_ERR_INVALID_ARG, "qmode %d unknown", c->qmode);
   if (c->path != STCA_PATH_STAGED && c->path != STCA_PATH_FUSED)
     return fail(STCA_ERR_INVALID_ARG, "path %d unknown", c->path);
-  if (c->path == STCA_PATH_FUSED) return fail(STCA_ERR_UNSUPPORTED, "fused path not built yet");
   if (c->flags & ~(STCA_FLAG_KV_LN | STCA_FLAG_Z_LN))
     return fail(STCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
   if (c->chunk_keys < 0 || c->chunk_keys % 32)
@@ -119,6 +124,21 @@ int validate_cfg(const stca_config *c) {
     if (c->hidden <= 0 || c->hidden % 32)
       return fail(STCA_ERR_UNSUPPORTED, "fp32 needs hidden a positive multiple of 32 (got %d)", c->hidden);
   }
+  return STCA_OK;
+}
+
+// What the fused kernel is built for.
+int validate_fused(const stca_config *c, const stca_batch *b) {
+  if (c->path != STCA_PATH_FUSED) return STCA_OK;
+  const int dh = c->d / c->H;
+  if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "fused path is bf16 only");
+  if (!((c->d == 256 && (dh == 32 || dh == 64)) || (c->d == 128 && dh == 32)))
+    return fail(STCA_ERR_UNSUPPORTED, "fused path supports d = 256 (d_h 32, 64) or d = 128 (d_h 32); got d = %d, d_h = %d",
+                c->d, dh);
+  if (!(c->flags & STCA_FLAG_KV_LN))
+    return fail(STCA_ERR_UNSUPPORTED, "fused path needs STCA_FLAG_KV_LN (LN after the history FFN)");
+  if (b && b->max_tgt_per_user > 64)
+    return fail(STCA_ERR_UNSUPPORTED, "fused path serves at most 64 targets per user (got %d)", b->max_tgt_per_user);
   return STCA_OK;
 }
 
@@ -144,7 +164,7 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
   const void *ptrs[] = {b->hist_offsets, b->hist_ids, b->tgt_offsets, b->tgt_ids, b->q0, b->table};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
-  return STCA_OK;
+  return validate_fused(c, b);
 }
 
 int check_ffn(const stca_ffn &f, bool ln, const char *name, int layer) {
@@ -191,9 +211,12 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   const int64_t d = c->d, h = c->hidden, T = b->n_tgt;
   const int dh = c->d / c->H;
   L.esize = c->dtype == STCA_BF16 ? 2 : 4;
+  L.fused = c->path == STCA_PATH_FUSED;
   L.nb = choose_nb(c->chunk_keys);
-  L.max_blocks = max_blocks(b->n_hist, c->B);
+  L.max_blocks = max_blocks(b->n_hist, c->B, L.fused ? 2 : 1);
   L.max_chunks = max_chunks(b->n_hist, c->B, L.nb);
+  L.max_tiles = fused_max_tiles(b->n_hist, c->B);
+  L.fused_grid = (int)fused_grid_bound(L.max_tiles);
   Carver cv;
   L.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
   if (c->dtype == STCA_BF16) {
@@ -225,9 +248,12 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
     L.prep_elems = e;
     L.prep = cv.take(e * 2);
   }
-  L.kv_layer = (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
+  // staged: blocked K/V of every layer; fused: none (the point of that path)
+  L.kv_layer = L.fused ? 0 : (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
   L.kv = cv.take(2 * L.kv_layer * c->M);
-  const size_t np = partial_slots(L.max_chunks, c->H, b->max_tgt_per_user);
+  size_t np = partial_slots(L.max_chunks, c->H, b->max_tgt_per_user);
+  if (L.fused)  // one slot per (workgroup, user): independent of the history length
+    np = (size_t)(L.fused_grid + c->B) * c->H * b->max_tgt_per_user;
   L.part_ml = cv.take(np * 2 * sizeof(float));
   L.part_acc = cv.take(np * dh * sizeof(float));
   L.part_cnt = cv.take(np * sizeof(int));
@@ -279,7 +305,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   if (r) return r;
   if ((r = validate_batch(cfg, batch))) return r;
   if ((r = validate_weights(cfg, w))) return r;
-  if (!out || !out->z) return fail(STCA_ERR_INVALID_ARG, "outputs->z is required");
+  if (!out) return fail(STCA_ERR_INVALID_ARG, "outputs is NULL");
+  if (!out->z && batch->n_tgt > 0) return fail(STCA_ERR_INVALID_ARG, "outputs->z is required");
   {
     const void *ptrs[] = {out->z, out->o_layers, out->attn, out->active, out->q_dump, out->kv_dump,
                           out->x_dump, out->dev_status};
@@ -289,6 +316,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (const void *p : p16)
       if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "output pointer %p not 16-byte aligned", p);
   }
+  if (cfg->path == STCA_PATH_FUSED && out->kv_dump)
+    return fail(STCA_ERR_UNSUPPORTED, "kv_dump needs the staged path (the fused path keeps no K/V)");
   const Layout L = make_layout(cfg, batch);
   if (!ws && L.total > 0) return fail(STCA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
   if (ws_bytes < L.total)
@@ -366,7 +395,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   // ---- 2. planner
   if (B > 0) {
     e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, batch->n_hist, T,
-                    batch->max_tgt_per_user, L.nb, plan, out->dev_status, s);
+                    batch->max_tgt_per_user, L.nb, L.fused ? 2 : 1, plan, out->dev_status, s);
     if (e) return hip_fail(e, "planner");
   }
   if ((e = rec(1))) return hip_fail(e, "stage event");
@@ -388,16 +417,13 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     return a;
   };
 
-  // ---- 3. history side of every layer -> blocked K/V
-  char *kvbase = at<char>(ws, L.kv);
-  auto kbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i) * L.kv_layer); };
-  auto vbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i + 1) * L.kv_layer); };
   const bool kvln = cfg->flags & STCA_FLAG_KV_LN;
-  for (int i = 0; i < M && batch->n_hist > 0; ++i) {
+  // history-side chain arguments of layer i (gather -> FFN -> LN -> W_K | W_V)
+  auto hist_args = [&](int i) {
     const stca_layer &l = w->layers[i];
     ChainArgs a = base_args();
     a.in_mode = IN_GATHER_CSR;
-    a.out_mode = OUT_KV;
+    a.out_mode = L.fused ? OUT_FUSED : OUT_KV;
     a.ffn = true;
     a.ln = kvln;
     a.proj = true;
@@ -420,6 +446,55 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     a.ln_g = l.kv.ln_g;
     a.ln_b = l.kv.ln_b;
     a.pn = 2 * d;
+    return a;
+  };
+  auto attn_args = [&](int i, const void *q) {
+    AttnArgs at_;
+    std::memset(&at_, 0, sizeof(at_));
+    at_.dtype = cfg->dtype;
+    at_.score = cfg->score;
+    at_.d = d;
+    at_.H = H;
+    at_.dh = dh;
+    at_.nb = L.nb;
+    at_.max_tgt = batch->max_tgt_per_user;
+    attn_shape(at_, L.max_chunks);
+    at_.fused = L.fused ? 1 : 0;
+    at_.max_grid = L.fused_grid;
+    at_.plan = plan;
+    at_.q = q;
+    at_.n_tgt = T;
+    at_.part_ml = at<float>(ws, L.part_ml);
+    at_.part_acc = at<float>(ws, L.part_acc);
+    at_.part_cnt = at<int>(ws, L.part_cnt);
+    at_.attn = out->attn ? out->attn + (size_t)i * T * d : at<float>(ws, L.attn32);
+    at_.attn_lo = at<void>(ws, L.attnlo);
+    at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
+    at_.B = B;
+    if (batch->n_hist == 0) at_.max_units = 0;
+    return at_;
+  };
+
+  if (L.fused) {
+    // no separate history stage: its events mark the same instant
+    for (int i = 0; i < M; ++i)
+      if ((e = rec(2 + i))) return hip_fail(e, "stage event");
+    if (T == 0) {  // nothing attends; only the optional input dump is produced
+      if (out->x_dump && batch->n_hist > 0) {
+        AttnArgs at_ = attn_args(0, nullptr);
+        ChainArgs a = hist_args(0);
+        if ((e = launch_fused(a, at_, L.max_tiles, s))) return hip_fail(e, "fused encoding");
+      }
+      return STCA_OK;
+    }
+  }
+
+  // ---- 3. history side of every layer -> blocked K/V (staged path)
+  char *kvbase = at<char>(ws, L.kv);
+  auto kbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i) * L.kv_layer); };
+  auto vbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i + 1) * L.kv_layer); };
+  for (int i = 0; i < M && batch->n_hist > 0 && !L.fused; ++i) {
+    ChainArgs a = hist_args(i);
     a.kbuf = kbuf(i);
     a.vbuf = vbuf(i);
     if ((e = chain(a))) return hip_fail(e, "history encoding");
@@ -483,31 +558,18 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       if ((e = chain(a))) return hip_fail(e, "query");
     }
     if ((e = rec(2 + M + 4 * i))) return hip_fail(e, "stage event");
-    {  // attention partials + merge
-      AttnArgs at_;
-      std::memset(&at_, 0, sizeof(at_));
-      at_.dtype = cfg->dtype;
-      at_.score = cfg->score;
-      at_.d = d;
-      at_.H = H;
-      at_.dh = dh;
-      at_.nb = L.nb;
-      at_.max_tgt = batch->max_tgt_per_user;
-      attn_shape(at_, L.max_chunks);
-      at_.plan = plan;
-      at_.kbuf = kbuf(i);
-      at_.vbuf = vbuf(i);
-      at_.q = qdst;
-      at_.n_tgt = T;
-      at_.part_ml = at<float>(ws, L.part_ml);
-      at_.part_acc = at<float>(ws, L.part_acc);
-      at_.part_cnt = at<int>(ws, L.part_cnt);
-      at_.attn = out->attn ? out->attn + (size_t)i * T * d : at<float>(ws, L.attn32);
-      at_.attn_lo = attnlo;
-      at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
-      at_.B = B;
-      if (batch->n_hist == 0) at_.max_units = 0;
-      if ((e = launch_attn_partial(at_, s))) return hip_fail(e, "attention");
+    {  // attention partials (fused: with the history encoding) + merge
+      AttnArgs at_ = attn_args(i, qdst);
+      if (L.fused) {
+        if (batch->n_hist > 0) {
+          ChainArgs a = hist_args(i);
+          if ((e = launch_fused(a, at_, L.max_tiles, s))) return hip_fail(e, "fused encoding + attention");
+        }
+      } else {
+        at_.kbuf = kbuf(i);
+        at_.vbuf = vbuf(i);
+        if ((e = launch_attn_partial(at_, s))) return hip_fail(e, "attention");
+      }
       if ((e = rec(3 + M + 4 * i))) return hip_fail(e, "stage event");
       if ((e = launch_attn_merge(at_, s))) return hip_fail(e, "attention merge");
       if ((e = rec(4 + M + 4 * i))) return hip_fail(e, "stage event");
@@ -658,7 +720,7 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   plan.pblk = plan.toff + (a->B + 1);
   plan.coff = plan.pblk + (a->B + 1);
   hipError_t e = launch_plan(a->hist_offsets, a->tgt_offsets, a->B, a->n_hist, a->n_tgt,
-                             a->max_tgt_per_user, L.nb, plan, a->dev_status, s);
+                             a->max_tgt_per_user, L.nb, 1, plan, a->dev_status, s);
   if (e) return hip_fail(e, "planner");
   char *kv = at<char>(ws, L.kv);
   if (a->n_hist > 0) {

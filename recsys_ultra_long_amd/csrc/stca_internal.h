@@ -19,13 +19,17 @@ struct Plan {
 };
 
 // Upper bound (host) on the padded blocks / chunks of a batch.
-inline int64_t max_blocks(int64_t n_hist, int B) { return (n_hist + 31) / 32 + B; }
+inline int64_t max_blocks(int64_t n_hist, int B, int align = 1) {
+  return (n_hist + 31) / 32 + (int64_t)B * align;
+}
 inline int64_t max_chunks(int64_t n_hist, int B, int nb) {
   return (max_blocks(n_hist, B) + nb - 1) / nb + B;
 }
 
+// align: every user is padded to a multiple of `align` 32-key blocks (2 on
+// the fused path, whose tiles hold 64 keys).
 hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
-                       int64_t n_tgt, int max_tgt, int nb, Plan plan, int *status,
+                       int64_t n_tgt, int max_tgt, int nb, int align, Plan plan, int *status,
                        hipStream_t s);
 
 // ------------------------------------------------------------ row chain
@@ -34,7 +38,7 @@ hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n
 // Input modes:
 enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3 };
 // Output modes:
-enum OutMode { OUT_KV = 0, OUT_ROWS = 1 };
+enum OutMode { OUT_KV = 0, OUT_ROWS = 1, OUT_FUSED = 2 };
 
 struct ChainArgs {
   int in_mode, out_mode;
@@ -111,7 +115,9 @@ struct AttnArgs {
   int groups;               // target groups of 64 (1 when max_tgt <= 64)
   int tgs;                  // target slots per partial (max_tgt if one group, else 64)
   int64_t max_units;        // host bound on units (chunks x H x groups); 0: nothing to do
-  int grid;                 // persistent workgroups (set by launch_attn_partial)
+  int grid;                 // persistent workgroups (set by the partial launch)
+  int max_grid;             // fused: bound on the grid the partial buffers hold
+  int fused;                // partials come from the fused kernel (slot = workgroup + user)
   Plan plan;
   const void *kbuf, *vbuf;  // blocked K/V of one layer
   const void *q;            // [n_tgt, d] scaled queries
@@ -135,6 +141,19 @@ inline void attn_shape(AttnArgs &a, int64_t max_chunks) {
   a.tgs = a.groups > 1 ? 64 : a.max_tgt;
   a.max_units = max_chunks * a.H * a.groups;
 }
+
+// ------------------------------------------------------------ fused path
+// History chain + attention of one layer in one persistent kernel (bf16;
+// d 128 or 256 with d_h 32, or d 256 with d_h 64; LN after the history FFN;
+// at most 64 targets per user).  Users are padded to 64-key tiles (planner
+// align = 2).  Partials: one slot per (workgroup, user), H heads x max_tgt
+// targets each, at most fused_grid_bound(tiles) + B slots.  Sets at.grid.
+constexpr int kFusedMaxGrid = 1024;
+inline int64_t fused_max_tiles(int64_t n_hist, int B) { return (n_hist + 63) / 64 + B; }
+inline int64_t fused_grid_bound(int64_t max_tiles) {
+  return max_tiles < kFusedMaxGrid ? max_tiles : kFusedMaxGrid;
+}
+hipError_t launch_fused(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s);
 
 // Row-major K, V ([n_hist, d]) -> blocked K/V layout (for stca_attention) and
 // the reverse (for kv_dump).

@@ -153,3 +153,43 @@ def test_attention_validation():
     assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.ERR_INVALID_ARG
     a.k = FAKE
     assert lib.stca_attention(C.byref(a), FAKE, 0, None) == stca.ERR_WORKSPACE
+
+
+# ------------------------------------------------------------------ fused path
+@pytest.mark.parametrize("over,bover,code", [
+    (dict(), dict(), stca.OK),                                   # d 256, d_h 32
+    (dict(H=4), dict(), stca.OK),                                # d 256, d_h 64
+    (dict(d=128, H=4, hidden=256), dict(), stca.OK),             # d 128, d_h 32
+    (dict(d=128, H=2, hidden=256), dict(), stca.ERR_UNSUPPORTED),  # d 128, d_h 64
+    (dict(d=512, H=8, hidden=1024), dict(), stca.ERR_UNSUPPORTED),
+    (dict(dtype=stca.F32), dict(), stca.ERR_UNSUPPORTED),
+    (dict(flags=0), dict(), stca.ERR_UNSUPPORTED),               # no LN after the history FFN
+    (dict(), dict(max_tgt_per_user=65), stca.ERR_UNSUPPORTED),
+    (dict(), dict(max_tgt_per_user=64), stca.OK),
+])
+def test_fused_validation(over, bover, code):
+    r, _ = ws_size(cfg(path=1, **over), batch(**bover))
+    assert r == code, stca.last_error()
+
+
+def test_fused_workspace_does_not_grow_with_history():
+    """The fused path keeps no K/V: beyond a bounded partial buffer (one slot
+    per workgroup and user) its workspace does not depend on n_hist."""
+    b = lambda n: batch(n_hist=n, n_tgt=64 * 32, max_tgt_per_user=64)
+    _, f1 = ws_size(cfg(path=1, B=32), b(32 * 10_240))
+    _, f2 = ws_size(cfg(path=1, B=32), b(32 * 100_000))
+    _, f3 = ws_size(cfg(path=1, B=32), b(2**31 - 1))
+    _, s1 = ws_size(cfg(path=0, B=32), b(32 * 10_240))
+    assert f1 == f2 == f3
+    # staged: 4 layers x K, V x 327,680 tokens x 256 x 2 bytes of K/V alone
+    assert s1 >= 4 * 2 * 32 * 10_240 * 256 * 2
+    assert f1 < s1 / 4
+
+
+def test_fused_rejects_kv_dump():
+    c, b = cfg(path=1), batch()
+    w, keep = _weights()
+    _, need = ws_size(c, b)
+    out = stca.Outputs(z=FAKE, kv_dump=FAKE)
+    assert _forward(c, b, w, out, need) == stca.ERR_UNSUPPORTED
+    assert "staged" in stca.last_error()
