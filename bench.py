@@ -166,6 +166,9 @@ def main():
     d, h, H = sp.d, sp.hidden, sp.H
     n_hist, T = p.n_hist, p.n_tgt
     flops_hist = n_hist * (6 * d * h + 4 * d * d)            # per layer launch
+    # attention flops: 4 d per (history token, target of the same user) pair
+    pairs = int(np.sum(np.diff(p.hist_offsets).astype(np.int64) * np.diff(p.tgt_offsets)))
+    flops_attn = 4 * d * pairs
     bytes_attn = n_hist * 4 * d + T * 2 * d                  # K,V bf16 read once + Q
     t_hist = float(np.mean(hist)) * 1e-3
     t_attn = float(np.mean(part)) * 1e-3
@@ -184,14 +187,30 @@ def main():
     # HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     # was taken on the current kernel sources
     from recsys_ultra_long_amd import profiling
-    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.md"))
+    roofs = {"history": roof_hist, "attention": roof_attn}
+    if args.path == "fused":
+        # one kernel per layer: gather, history FFN + LN, W_K | W_V and the
+        # attention; K/V never leave the chip, so it is bound by the MFMA
+        fused_tf = (flops_hist + flops_attn) / t_attn / 1e12
+        roofs = {"fused": {"kernel": "fused gather+SwiGLU+LN+W_K|W_V+attention", "bound": "mfma",
+                           "achieved": round(fused_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(fused_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "launch_ms": round(t_attn * 1e3, 4),
+                           "per_launch": f"{n_hist} tokens x {6 * d * h + 4 * d * d} flop + "
+                                         f"{pairs} (token, target) pairs x {4 * d} flop"}}
+    picks = {"history": lambda k: k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k,
+             "attention": lambda k: k.startswith("attn_bf16_kernel<"),
+             "fused": lambda k: k.startswith(f"fused_kernel<{d},")}
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{args.path}.md"))
     if tr is not None:
-        for roof, pick in ((roof_hist, lambda k: k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k),
-                           (roof_attn, lambda k: k.startswith("attn_bf16_kernel<"))):
-            hits = [v["hbm_bytes"] for k, v in tr["kernels"].items() if pick(k)]
+        for name, roof in roofs.items():
+            hits = [v["hbm_bytes"] for k, v in tr["kernels"].items() if picks[name](k)]
             if hits:
                 roof["traffic"] = round(max(hits))
-    dominant = roof_hist if sum(hist) >= sum(part) else roof_attn
+    if args.path == "fused":
+        dominant = roofs["fused"]
+    else:
+        dominant = roof_hist if sum(hist) >= sum(part) else roof_attn
 
     value = n_hist * M / (ms * 1e-3)
     res = {
@@ -210,10 +229,12 @@ def main():
         "target_scores_per_s": round(T / (ms * 1e-3), 1),
         "history_tokens_per_s": round(n_hist / (ms * 1e-3), 1),
         "roofline": dominant,
-        "roofline_attention": roof_attn,
-        "roofline_history": roof_hist,
-        "stages_ms": {"prep_plan": round(prep, 4), "history": [round(x, 4) for x in hist],
-                      "query": [round(x, 4) for x in query], "attn_partial": [round(x, 4) for x in part],
+        **({"roofline_attention": roof_attn, "roofline_history": roof_hist}
+           if args.path == "staged" else {}),
+        "stages_ms": {"prep_plan": round(prep, 4),
+                      **({"history": [round(x, 4) for x in hist]} if args.path == "staged" else {}),
+                      "query": [round(x, 4) for x in query],
+                      ("attn_partial" if args.path == "staged" else "fused"): [round(x, 4) for x in part],
                       "attn_merge": [round(x, 4) for x in merge], "w_o": [round(x, 4) for x in wo],
                       "z": round(zt, 4)},
     }

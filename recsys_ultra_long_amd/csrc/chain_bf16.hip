@@ -147,19 +147,39 @@ struct ChainSmem {
   int s_id[R], s_tok[R];
 };
 
-// Fused-path K/V staging of one wave: its HW heads' K [hh][key 0..63][d_h]
-// and V^T [hh][d_h][key 0..63] for the 64 keys of the tile (rows padded).
-template <int FDH>
-struct FusedStage {
-  static constexpr int LDK = FDH + 8;
-  static constexpr int LDV = 64 + 8;
+// Fused-path K/V staging of one 64-key tile, placed over LDS the chain no
+// longer needs once the projection runs.  Wave w (features w d/4 .. of both
+// K and V, i.e. heads w HW ..) keeps
+//   K   [hh][key 0..63][d_h]  over the FFN's G buffer (free after the last
+//                             W2 phase, which every wave finished before LN);
+//   V^T [hh][d_h][key 0..63]  over the input rows (free once every wave has
+//                             finished the V projection).
+template <int D, int TT>
+DEV bf16_t *fused_k_stage(ChainSmem<D, TT, true> &sm, int w) {
+  static_assert(sizeof(sm.gs) >= sizeof(bf16_t) * D * 64, "K staging exceeds the G buffer");
+  return &sm.gs[0][0] + w * (D / 4) * 64;
+}
+template <int D, int TT>
+DEV bf16_t *fused_v_stage(ChainSmem<D, TT, true> &sm, int w) {
+  static_assert(sizeof(sm.xs) >= sizeof(bf16_t) * D * 64, "V staging exceeds the row buffer");
+  return sm.xs + w * (D / 4) * 64;
+}
+
+struct NoHook {
+  DEV void operator()() const {}
 };
 
 // One tile of rows (64 for the history, 32 on the query side) through the
-// chain; OUT_KV writes blocked K/V to HBM, OUT_ROWS rows, OUT_FUSED stages
-// this wave's K/V features in `kvs` (FDH = head width) for the fused attention.
-template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT, int FDH = 0>
-DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN> &sm, bf16_t *kvs) {
+// chain; OUT_KV writes blocked K/V to HBM, OUT_ROWS rows, OUT_FUSED leaves
+// the tile's K/V in LDS (fused_k_stage / fused_v_stage, head width FDH).
+// IN_STAGED: the caller has already written the input rows to sm.xs and
+// synchronised.  pre_ln / pre_proj run (all threads) just before the LN and
+// just before the projection: a persistent caller prefetches its next tile's
+// input there, while the chain's own memory traffic is light.
+template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT, int FDH = 0,
+          class PreLn = NoHook, class PreProj = NoHook>
+DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN> &sm,
+                    PreLn pre_ln = PreLn{}, PreProj pre_proj = PreProj{}) {
   constexpr int R = 32 * TT;  // rows (tokens) per workgroup
   // Every contraction is computed "feature-major": MFMA rows are output
   // features, MFMA columns are the 64 rows (tokens) of the tile.  A lane then
@@ -174,7 +194,10 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
   int *const s_id = sm.s_id;
   int *const s_tok = sm.s_tok;
 
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  // inside the fused kernel's tile loop: keep per-lane address arithmetic
+  // from being hoisted out of the loop (see fused_kernel)
+  if constexpr (OUT == OUT_FUSED) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
@@ -230,7 +253,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
   }
 
   int total_blocks = 0;
-  if (IN == IN_GATHER_CSR) {
+  if (IN == IN_GATHER_CSR || IN == IN_STAGED) {
     total_blocks = a.plan.pblk[a.B];
     if (row0 >= (int64_t)total_blocks * 32) return;
   } else {
@@ -242,7 +265,11 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
     if (tid < R) {
       int id = -1, tok = -1;
       const int64_t p = row0 + tid;
-      if (IN == IN_GATHER_CSR) {
+      if (IN == IN_GATHER_CSR && a.plan.prow && !a.in_dump) {
+        // padded-row ids from the planner (already validated): one load
+        id = a.plan.prow[p];
+        tok = id;  // only its sign is used below
+      } else if (IN == IN_GATHER_CSR) {
         const int blk = (int)(p >> 5);
         if (blk < total_blocks) {
           const int u = upper_index(a.plan.pblk, a.B, blk);
@@ -324,7 +351,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
     else first_proj_ptrs(p0);
     ring_prime<2>(ring, p0);
   }
-  __syncthreads();
+  if (IN != IN_STAGED) __syncthreads();
 
   // ------------------------------------------------------------ SwiGLU FFN
   if (FFN) {
@@ -369,6 +396,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         }
       }
     }
+    pre_ln();
     // -------------------------------------------------------- LayerNorm
     // lane holds features w*D/4 + (sp*YT+t)*32 + 8q + 4*hi + r of tokens j*32 + l32
     float mean[TT], rstd[TT];
@@ -447,14 +475,18 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
 
   // ------------------------------------------------------------ projection
   if (PROJ) {
+    pre_proj();
     if (OUT == OUT_KV || OUT == OUT_FUSED) {
       const int H = a.H;
       const int DH = D / H;
       bf16_t *kb = (bf16_t *)a.kbuf, *vb = (bf16_t *)a.vbuf;
-      constexpr int LDK = FusedStage<FDH>::LDK, LDV = FusedStage<FDH>::LDV;
-      constexpr int HW = FDH > 0 ? (D / 4) / FDH : 1;  // heads per wave (fused)
-      bf16_t *const kst = kvs;                           // [HW][64][LDK]
-      bf16_t *const vst = kvs + HW * 64 * LDK;           // [HW][FDH][LDV]
+      static_assert(OUT != OUT_FUSED || (FFN && TT == 2 && NSP == 1 && FDH > 0 && (D / 4) % FDH == 0),
+                    "fused staging: 64-row tiles, one projection phase, whole heads per wave");
+      bf16_t *kst = nullptr, *vst = nullptr;
+      if constexpr (OUT == OUT_FUSED) {
+        kst = fused_k_stage(sm, w);
+        vst = fused_v_stage(sm, w);
+      }
 #pragma unroll
       for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T: 4 consecutive features / token
         f32x16 acc[YT][TT];
@@ -476,7 +508,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
                          pack_bf2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
               if constexpr (OUT == OUT_FUSED) {
                 const int fl = (sp * YT + i) * 32 + 8 * q + 4 * hi;  // wave-local feature
-                *reinterpret_cast<u32x2 *>(kst + ((fl / FDH) * 64 + t * 32 + l32) * LDK + fl % FDH) = v;
+                *reinterpret_cast<u32x2 *>(kst + ((fl / FDH) * 64 + t * 32 + l32) * FDH + fl % FDH) = v;
               } else {
                 const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
                 const int h = f / DH, dh = f % DH;
@@ -497,6 +529,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         } else {
           phase<TT, YT, D / 32, false, 0>(acc, ring, gp, bx, nx);
         }
+        if constexpr (OUT == OUT_FUSED) __syncthreads();  // V^T goes over rows other waves read
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
@@ -510,7 +543,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
                          pack_bf2(acc[t][j][4 * q + 2], acc[t][j][4 * q + 3])};
               if constexpr (OUT == OUT_FUSED) {
                 const int fl = (sp * YT + j) * 32 + l32;
-                *reinterpret_cast<u32x2 *>(vst + ((fl / FDH) * FDH + fl % FDH) * LDV + t * 32 + key) = v;
+                *reinterpret_cast<u32x2 *>(vst + fl * 64 + t * 32 + key) = v;
               } else {
                 const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
                 const int h = f / DH, dh = f % DH;
@@ -562,35 +595,66 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
 template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT>
 __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void chain_kernel(ChainArgs a) {
   __shared__ ChainSmem<D, TT, FFN> sm;
-  chain_tile<D, TT, IN, FFN, LN, PROJ, OUT>(a, (int64_t)blockIdx.x * (32 * TT), sm, nullptr);
+  const int64_t row0 = (int64_t)blockIdx.x * (32 * TT);
+  if constexpr (IN == IN_GATHER_CSR && OUT == OUT_KV && TT == 2) {
+    if (a.plan.prow && a.pf_stride > 0) {
+      // History tiles: the gather opens every tile with a wait on table rows
+      // (mostly HBM / infinity-cache latency).  While this tile is in its LN
+      // and projection, touch the rows of the tile pf_stride workgroups
+      // ahead -- the one that takes this workgroup's place on the same XCD --
+      // one dword per 128-byte line, so that its gather finds them in cache.
+      const int64_t r = (row0 + (int64_t)a.pf_stride * 64) + (threadIdx.x >> 2);
+      const bf16_t *table = (const bf16_t *)a.table;
+      int id = -1;
+      unsigned sink = 0;
+      chain_tile<D, TT, IN, FFN, LN, PROJ, OUT>(
+          a, row0, sm,
+          [&] {
+            if (r < a.n_rows) id = a.plan.prow[r];
+          },
+          [&] {
+            if (id >= 0) sink = *reinterpret_cast<const unsigned *>(table + (int64_t)id * D + (threadIdx.x & 3) * 64);
+          });
+      // keeps the touch load (its value is irrelevant; the test is false in practice)
+      if (sink == 0x7fc00123u) atomicOr(a.status, 0);
+      return;
+    }
+  }
+  chain_tile<D, TT, IN, FFN, LN, PROJ, OUT>(a, row0, sm);
 }
 
 // ---------------------------------------------------------------- fused path
 // "Lookup while computing" ([WeChat] §1.1): a persistent workgroup walks a
 // contiguous range of 64-key tiles (every user padded to whole tiles).  For
 // each tile it gathers the embedding rows, runs the history FFN, LN and
-// W_K | W_V, keeps the tile's K/V in LDS -- each wave has produced exactly
-// the features of its own heads, so the staging is wave-private -- and folds
-// those keys at once into the online-softmax (or ReLU) state of the user's
-// targets for its heads, held in registers across the user's tiles.  No K/V
-// tensor exists in HBM.  A partial is written when the user changes or the
-// range ends, into slot (workgroup + user): ranges are contiguous and users
+// W_K | W_V (chain_tile), which leaves the tile's K/V in LDS -- each wave has
+// produced exactly the features of its own heads -- and the wave folds those
+// keys at once into the online-softmax (or ReLU) state of the user's targets
+// for its heads.  No K/V tensor exists in HBM.
+//
+// Two workgroups share a CU (LDS: the chain's 71 KB, the staging overlays
+// it), so the per-head state does not stay in registers across the chain:
+// between tiles of one user it lives in the workgroup's own state area
+// (at.fstate, each lane reading back only what it wrote), loaded and stored
+// one head at a time.  At a user's last tile in the range the state becomes
+// a partial in slot (workgroup + user): ranges are contiguous and users
 // ordered, so along the sequence of (workgroup, user) segments both indices
 // only grow and each step raises one of them -- the slots are distinct and
 // fewer than grid + B.
+template <int DH, int NT>
+struct FusedRec {
+  static constexpr int DT = DH / 16;
+  static constexpr int N = DT * NT + 3;  // f32x4 per lane: o, then m, l, count
+};
+
 template <int D, int DH, int NT, int SCORE>
-__global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChainArgs a, AttnArgs at) {
+__global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArgs at) {
   constexpr int HW = (D / 4) / DH;  // heads per wave
   constexpr int KS = DH / 32, DT = DH / 16;
-  constexpr int LDK = FusedStage<DH>::LDK, LDV = FusedStage<DH>::LDV;
-  constexpr int KVW = HW * 64 * LDK + HW * DH * LDV;
+  constexpr int REC = FusedRec<DH, NT>::N;
+  static_assert(NT <= 4, "state record holds at most 4 target tiles");
   __shared__ ChainSmem<D, 2, true> sm;
-  __shared__ __attribute__((aligned(16))) bf16_t kvs_all[4][KVW];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g16 = lane >> 4, c16 = lane & 15;
-  const int kr0 = attn_key_row(lane);
-  bf16_t *const kvs = kvs_all[w];
-  const bf16_t *const vst = kvs + HW * 64 * LDK;
+  const int w = threadIdx.x >> 6;
   const Plan P = at.plan;
   const int H = at.H;
   const int tiles = P.pblk[at.B] / 2;
@@ -598,43 +662,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChainArgs a, AttnArg
   int tile = (int)blockIdx.x * per;
   const int tend = min(tiles, tile + per);
   const bf16_t *Q = (const bf16_t *)at.q;
-  AttnState<DH, NT> st[HW];
   int cur_u = -1;
-
-  auto flush = [&](int u) {
-    const int m_u = P.toff[u + 1] - P.toff[u];
-    const int slot = (int)blockIdx.x + u;
-#pragma unroll
-    for (int hh = 0; hh < HW; ++hh) {
-      const int h = w * HW + hh;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float l = st[hh].lrun[n];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        int cn = st[hh].cnt[n];
-        cn += __shfl_xor(cn, 16);
-        cn += __shfl_xor(cn, 32);
-        const int tl = n * 16 + c16;
-        if (tl < m_u) {
-          const int64_t idx = partial_index(slot, H, h, at.tgs, tl);
-          if (g16 == 0) {
-            if (SCORE == 0) {
-              at.part_ml[idx * 2] = st[hh].mrun[n];
-              at.part_ml[idx * 2 + 1] = l;
-            } else {
-              at.part_cnt[idx] = cn;
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const f32x4 v = st[hh].o[t][n];
-            *reinterpret_cast<f32x4 *>(at.part_acc + idx * DH + t * 16 + 4 * g16) = v;
-          }
-        }
-      }
-    }
-  };
 
   for (; tile < tend; ++tile) {
     const int u = upper_index(P.pblk, at.B, tile * 2);
@@ -642,43 +670,114 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChainArgs a, AttnArg
     const int m_u = P.toff[u + 1] - tbase;
     // a user without targets needs no K/V (only the optional input dump)
     if (m_u == 0 && !a.in_dump) continue;
-    if (u != cur_u) {
-      if (cur_u >= 0) flush(cur_u);
-      cur_u = u;
-#pragma unroll
-      for (int hh = 0; hh < HW; ++hh) {
-        attn_reset(st[hh]);
-        attn_load_q(st[hh], Q, at.d, w * HW + hh, tbase, 0, m_u, lane);
-      }
-    }
-    __syncthreads();  // every wave is done with the previous tile's rows
-    chain_tile<D, 2, IN_GATHER_CSR, true, true, true, OUT_FUSED, DH>(a, (int64_t)tile * 64, sm, kvs);
+    const bool first = u != cur_u;                                   // user's first tile here
+    const bool last = tile + 1 == tend || (tile + 1) * 2 >= P.pblk[u + 1];  // ... and last
+    cur_u = u;
+    __syncthreads();  // every wave is done with the previous tile's LDS
+    // The weight and LN-parameter addresses are the same for every tile;
+    // hiding them from the optimiser once per tile keeps it from hoisting the
+    // chain's address arithmetic and LN parameter loads out of this loop and
+    // holding them in registers throughout.
+    ChainArgs ta = a;
+    asm volatile("" : "+s"(ta.w1), "+s"(ta.w3), "+s"(ta.w2), "+s"(ta.wp), "+s"(ta.ln_g), "+s"(ta.ln_b));
+    chain_tile<D, 2, IN_GATHER_CSR, true, true, true, OUT_FUSED, DH>(ta, (int64_t)tile * 64, sm);
+    if (m_u == 0) continue;
     // the staging was written by other lanes of this wave
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    if (m_u == 0) continue;
+    // lane quantities derived here, not before the loop, so that none of
+    // them is held in registers across the chain
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int g16 = lane >> 4, c16 = lane & 15;
+    const int kr0 = attn_key_row(lane);
+    f32x4 *const fst =
+        reinterpret_cast<f32x4 *>(at.fstate) + ((int64_t)blockIdx.x * 4 + w) * HW * REC * 64 + lane;
+    const bf16_t *kst = fused_k_stage(sm, w);
+    const bf16_t *vst = fused_v_stage(sm, w);
     const int L = P.hoff[u + 1] - P.hoff[u];
     const int kbase = (tile * 2 - P.pblk[u]) * 32;  // user-local index of the tile's first key
+#pragma unroll 1
+    for (int hh = 0; hh < HW; ++hh) {
+      const int h = w * HW + hh;
+      f32x4 *rec = fst + hh * REC * 64;
+      AttnState<DH, NT> st;
+      if (first) {
+        attn_reset(st);
+      } else {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int nvalid = L - (kbase + blk * 32);
-      if (nvalid <= 0) break;
+        for (int t = 0; t < DT; ++t)
 #pragma unroll
-      for (int hh = 0; hh < HW; ++hh) {
+          for (int n = 0; n < NT; ++n) st.o[t][n] = rec[(t * NT + n) * 64];
+        const f32x4 m4 = rec[(DT * NT) * 64], l4 = rec[(DT * NT + 1) * 64], c4 = rec[(DT * NT + 2) * 64];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          st.mrun[n] = m4[n];
+          st.lrun[n] = l4[n];
+          st.cnt[n] = __float_as_int(c4[n]);
+        }
+      }
+      attn_load_q(st, Q, at.d, h, tbase, 0, m_u, lane);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int nvalid = L - (kbase + blk * 32);
+        if (nvalid <= 0) break;
         bf16x8 kf[2][KS], vf[DT];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int k = 0; k < KS; ++k)
-            kf[kt][k] = ld8(kvs + (hh * 64 + blk * 32 + kr0 + 4 * kt) * LDK + k * 32 + g16 * 8);
+            kf[kt][k] = ld8(kst + (hh * 64 + blk * 32 + kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) vf[t] = ld8(vst + (hh * DH + t * 16 + c16) * 64 + blk * 32 + g16 * 8);
+        attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, lane);
+      }
+      if (!last) {
 #pragma unroll
         for (int t = 0; t < DT; ++t)
-          vf[t] = ld8(vst + (hh * DH + t * 16 + c16) * LDV + blk * 32 + g16 * 8);
-        attn_block<DH, NT, SCORE>(st[hh], kf, vf, nvalid, lane);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) rec[(t * NT + n) * 64] = st.o[t][n];
+        f32x4 m4 = {0.f, 0.f, 0.f, 0.f}, l4 = m4, c4 = m4;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          m4[n] = st.mrun[n];
+          l4[n] = st.lrun[n];
+          c4[n] = __int_as_float(st.cnt[n]);
+        }
+        rec[(DT * NT) * 64] = m4;
+        rec[(DT * NT + 1) * 64] = l4;
+        rec[(DT * NT + 2) * 64] = c4;
+        continue;
+      }
+      // the user's last tile in this range: write the partial
+      const int slot = (int)blockIdx.x + u;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float l = st.lrun[n];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        int cn = st.cnt[n];
+        cn += __shfl_xor(cn, 16);
+        cn += __shfl_xor(cn, 32);
+        const int tl = n * 16 + c16;
+        if (tl < m_u) {
+          const int64_t idx = partial_index(slot, H, h, at.tgs, tl);
+          if (g16 == 0) {
+            if (SCORE == 0) {
+              at.part_ml[idx * 2] = st.mrun[n];
+              at.part_ml[idx * 2 + 1] = l;
+            } else {
+              at.part_cnt[idx] = cn;
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+            *reinterpret_cast<f32x4 *>(at.part_acc + idx * DH + t * 16 + 4 * g16) = st.o[t][n];
+        }
       }
     }
   }
-  if (cur_u >= 0) flush(cur_u);
 }
 
 template <int D, int DH, int NT, int SCORE>
@@ -719,14 +818,26 @@ hipError_t dispatch_d(const ChainArgs &a, hipStream_t s) {
   constexpr int TTQ = 1;
   const bool f = a.ffn, l = a.ln, p = a.proj;
   auto grid = [&](int tt) { return dim3((unsigned)((a.n_rows + 32 * tt - 1) / (32 * tt))); };
+  ChainArgs ah = a;  // history tiles: prefetch distance = resident workgroups
+  if (a.in_mode == IN_GATHER_CSR && a.plan.prow) {
+    int dev = 0, cus = 256, per_cu = 2;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    auto k = a.ln ? chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>
+                  : chain_kernel<D, TTH, IN_GATHER_CSR, true, false, true, OUT_KV>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 1;
+    ah.pf_stride = cus * per_cu;
+  }
   const dim3 block(kThreads);
 #define CH(TT, IN, FFN, LN, PROJ, OUT) \
   hipLaunchKernelGGL((chain_kernel<D, TT, IN, FFN, LN, PROJ, OUT>), grid(TT), block, 0, s, a)
   switch (a.in_mode) {
     case IN_GATHER_CSR:  // history: FFN (+LN) then K/V
       if (!(f && p && a.out_mode == OUT_KV)) return hipErrorInvalidValue;
-      if (l) CH(TTH, IN_GATHER_CSR, true, true, true, OUT_KV);
-      else CH(TTH, IN_GATHER_CSR, true, false, true, OUT_KV);
+      if (l) hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>), grid(TTH), block, 0, s, ah);
+      else hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, true, false, true, OUT_KV>), grid(TTH), block, 0, s, ah);
       break;
     case IN_GATHER_IDS:  // first query: FFN + LN + W_Q
       if (!(f && l && p)) return hipErrorInvalidValue;

@@ -76,7 +76,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   }
 }
 
+// One thread per padded row: which user's block, which item, which id.
+__global__ __launch_bounds__(256) void padded_ids_kernel(Plan plan, int B, const int *__restrict__ ids,
+                                                         long long table_rows, long long rows,
+                                                         int *status) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  int id = -1;
+  const int blk = (int)(r >> 5);
+  if (blk < plan.pblk[B]) {
+    const int u = upper_index(plan.pblk, B, blk);
+    const int j = (int)(r - (long long)plan.pblk[u] * 32);
+    if (j < plan.hoff[u + 1] - plan.hoff[u]) {
+      id = ids[plan.hoff[u] + j];
+      if (id < 0 || (long long)id >= table_rows) {
+        set_status(status, 4);
+        id = -1;
+      }
+    }
+  }
+  plan.prow[r] = id;
+}
+
 }  // namespace
+
+hipError_t launch_padded_ids(const Plan &plan, int B, const int *hist_ids, int64_t table_rows,
+                             int64_t max_blocks, int *status, hipStream_t s) {
+  const int64_t rows = prow_rows(max_blocks);
+  hipLaunchKernelGGL(padded_ids_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, plan, B,
+                     hist_ids, (long long)table_rows, (long long)rows, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
                        int64_t n_tgt, int max_tgt, int nb, int align, Plan plan, int *status,

@@ -72,7 +72,8 @@ struct Layout {
   int64_t max_tiles = 0;   // fused: 64-key tiles (host bound)
   int fused_grid = 0;      // fused: partial buffers hold this many workgroups
   size_t esize = 2;
-  size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0;
+  size_t prow = 0;         // staged bf16: padded-row id map (0 = none)
+  size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0, fstate = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
   std::vector<PrepLayer> pl;
   size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
@@ -219,6 +220,8 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   L.fused_grid = (int)fused_grid_bound(L.max_tiles);
   Carver cv;
   L.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
+  if (c->dtype == STCA_BF16 && !L.fused && b->n_hist > 0)
+    L.prow = cv.take(sizeof(int) * (size_t)prow_rows(L.max_blocks));
   if (c->dtype == STCA_BF16) {
     size_t e = 0;
     L.pl.resize(c->M);
@@ -257,6 +260,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   L.part_ml = cv.take(np * 2 * sizeof(float));
   L.part_acc = cv.take(np * dh * sizeof(float));
   L.part_cnt = cv.take(np * sizeof(int));
+  if (L.fused) L.fstate = cv.take(fused_state_bytes(c->d, dh, L.fused_grid));
   L.xt = cv.take(T * d * L.esize);
   L.ocat = cv.take(T * d * c->M * L.esize);
   L.qs = cv.take(T * d * L.esize);
@@ -345,6 +349,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   plan.toff = plan.hoff + (B + 1);
   plan.pblk = plan.toff + (B + 1);
   plan.coff = plan.pblk + (B + 1);
+  plan.prow = L.prow ? at<int>(ws, L.prow) : nullptr;
 
   if ((e = rec(0))) return hip_fail(e, "stage event");
   // ---- 1. weight preparation (bf16): fragment-packed W^T into the workspace
@@ -397,6 +402,10 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, batch->n_hist, T,
                     batch->max_tgt_per_user, L.nb, L.fused ? 2 : 1, plan, out->dev_status, s);
     if (e) return hip_fail(e, "planner");
+    if (plan.prow) {
+      e = launch_padded_ids(plan, B, batch->hist_ids, cfg->table_rows, L.max_blocks, out->dev_status, s);
+      if (e) return hip_fail(e, "padded ids");
+    }
   }
   if ((e = rec(1))) return hip_fail(e, "stage event");
   if (B == 0 || (batch->n_hist == 0 && T == 0)) return STCA_OK;
@@ -467,6 +476,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     at_.part_ml = at<float>(ws, L.part_ml);
     at_.part_acc = at<float>(ws, L.part_acc);
     at_.part_cnt = at<int>(ws, L.part_cnt);
+    at_.fstate = L.fused ? at<float>(ws, L.fstate) : nullptr;
     at_.attn = out->attn ? out->attn + (size_t)i * T * d : at<float>(ws, L.attn32);
     at_.attn_lo = at<void>(ws, L.attnlo);
     at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
@@ -719,6 +729,7 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   plan.toff = plan.hoff + (a->B + 1);
   plan.pblk = plan.toff + (a->B + 1);
   plan.coff = plan.pblk + (a->B + 1);
+  plan.prow = nullptr;
   hipError_t e = launch_plan(a->hist_offsets, a->tgt_offsets, a->B, a->n_hist, a->n_tgt,
                              a->max_tgt_per_user, L.nb, 1, plan, a->dev_status, s);
   if (e) return hip_fail(e, "planner");

@@ -14,8 +14,12 @@ namespace stca {
 //   toff[B+1]  sanitised target offsets
 //   pblk[B+1]  first 32-key block of each user in the padded K/V layout
 //   coff[B+1]  first split-L chunk of each user
+//   prow[]     optional (staged bf16 history): per padded row, the table id
+//              of its history item, or -1 for padding and for ids outside the
+//              table (prow_rows(max_blocks) entries)
 struct Plan {
   int *hoff, *toff, *pblk, *coff;
+  int *prow;
 };
 
 // Upper bound (host) on the padded blocks / chunks of a batch.
@@ -25,6 +29,13 @@ inline int64_t max_blocks(int64_t n_hist, int B, int align = 1) {
 inline int64_t max_chunks(int64_t n_hist, int B, int nb) {
   return (max_blocks(n_hist, B) + nb - 1) / nb + B;
 }
+
+// Padded-row id map (Plan::prow) after the planner: entries for every row of
+// the 64-row tiles over max_blocks blocks.  Ids outside [0, table_rows) set
+// status bit 4 and read as -1.
+inline int64_t prow_rows(int64_t max_blocks) { return (max_blocks + 2) * 32; }
+hipError_t launch_padded_ids(const Plan &plan, int B, const int *hist_ids, int64_t table_rows,
+                             int64_t max_blocks, int *status, hipStream_t s);
 
 // align: every user is padded to a multiple of `align` 32-key blocks (2 on
 // the fused path, whose tiles hold 64 keys).
@@ -36,7 +47,7 @@ hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n
 // One launch computes, for a set of rows,
 //   input -> [SwiGLU FFN] -> [LN] -> [projection (scaled)] -> output
 // Input modes:
-enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3 };
+enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3, IN_STAGED = 4 };
 // Output modes:
 enum OutMode { OUT_KV = 0, OUT_ROWS = 1, OUT_FUSED = 2 };
 
@@ -75,6 +86,7 @@ struct ChainArgs {
   void *kbuf, *vbuf;        // OUT_KV blocked layout
   int H;
   int *status;
+  int pf_stride;            // history tiles: touch the rows of tile + pf_stride (0: off)
 };
 
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s);
@@ -125,6 +137,7 @@ struct AttnArgs {
   float *part_ml;           // [units, tgs, 2]
   float *part_acc;          // [units, tgs, dh]
   int *part_cnt;            // [units, tgs]
+  float *fstate;            // fused: per-workgroup attention state between tiles
   float *attn;              // [n_tgt, d] fp32 (required)
   void *attn_lo;            // [n_tgt, d] config dtype copy (optional)
   int *active;              // [n_tgt, H] (optional)
@@ -147,8 +160,14 @@ inline void attn_shape(AttnArgs &a, int64_t max_chunks) {
 // d 128 or 256 with d_h 32, or d 256 with d_h 64; LN after the history FFN;
 // at most 64 targets per user).  Users are padded to 64-key tiles (planner
 // align = 2).  Partials: one slot per (workgroup, user), H heads x max_tgt
-// targets each, at most fused_grid_bound(tiles) + B slots.  Sets at.grid.
-constexpr int kFusedMaxGrid = 1024;
+// targets each, at most fused_grid_bound(tiles) + B slots; between tiles each
+// workgroup keeps its heads' state in fused_state_bytes / grid bytes of
+// at.fstate.  Sets at.grid.
+constexpr int kFusedMaxGrid = 512;
+inline size_t fused_state_bytes(int d, int dh, int64_t grid) {
+  const int heads_per_wave = (d / 4) / dh, rec = (dh / 16) * 4 + 3;  // f32x4 per lane, <= 64 targets
+  return (size_t)grid * 4 * heads_per_wave * rec * 64 * 16;
+}
 inline int64_t fused_max_tiles(int64_t n_hist, int B) { return (n_hist + 63) / 64 + B; }
 inline int64_t fused_grid_bound(int64_t max_tiles) {
   return max_tiles < kFusedMaxGrid ? max_tiles : kFusedMaxGrid;

@@ -31,9 +31,9 @@ def _target_rows(p, users):
     return np.concatenate([np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users])
 
 
-def _check_sampled(p, dumps=()):
-    print(f"[fullsize] {p.spec.name} B={p.spec.B} n_hist={p.n_hist} n_tgt={p.n_tgt}", flush=True)
-    g = gpu_run(p, dumps=dumps)
+def _check_sampled(p, dumps=(), path="staged"):
+    print(f"[fullsize] {p.spec.name} {path} B={p.spec.B} n_hist={p.n_hist} n_tgt={p.n_tgt}", flush=True)
+    g = gpu_run(p, dumps=dumps, path=path)
     assert int(g["status"][0]) == 0
     users = _sample_users(p)
     o = oracle_run(p, users=users)
@@ -80,4 +80,12 @@ def test_fullsize_ragged_relu_stepwise():
 def test_fullsize_hyformer(seq):
     p = I.make_problem(I.spec(5)[seq], threads=16)
     _, _, errs, _ = _check_sampled(p)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_fullsize_fused(k):
+    """The fused path (no K/V in HBM) at full size, sampled users."""
+    p = I.make_problem(I.spec(k), threads=16)
+    _, _, errs, _ = _check_sampled(p, path="fused")
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
