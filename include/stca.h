@@ -158,8 +158,10 @@ typedef struct {
    *   0            start of the call
    *   1            weights prepared and batch planned
    *   2 + i        history encoding (gather, FFN, LN, W_K|W_V) of layer i done, i < M
-   *                (fused path: all M recorded right after event 1; the
-   *                encoding is then part of each layer's attention partials)
+   *                (bf16 staged at d <= 256: one launch encodes every layer,
+   *                so all M are recorded after it and 2 + 0 spans it all;
+   *                fused path: all M recorded right after event 1, the
+   *                encoding being part of each layer's attention partials)
    *   2 + M + 4i   query of layer i done
    *   3 + M + 4i   attention partials of layer i done
    *   4 + M + 4i   partial merge of layer i done

@@ -64,7 +64,7 @@ DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
 // scores of keys 8g..8g+7 for target l%16.  The four waves of a workgroup take
 // alternate blocks of a pair's range and merge in LDS when the pair ends.
 template <int DH, int NT, int SCORE>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
   constexpr int DT = DH / 16;  // feature tiles of the output
   constexpr int TG = NT * 16;  // targets per group
@@ -112,29 +112,35 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < DT; ++t) vv[t] = ld8(vb + (t * 16 + c16) * 32 + g16 * 8);
       };
+      // two blocks of this wave in flight ahead of the one being used: the
+      // loads, not the arithmetic, set the pace once the block step is lean
+      bf16x8 k1[2][KS], v1[DT];
       if (b0 + w < b1) load_kv(b0 + w, kf, vf);
+      if (b0 + w + 4 < b1) load_kv(b0 + w + 4, k1, v1);
       for (int b = b0 + w; b < b1; b += 4) {
-        bf16x8 kn[2][KS], vn[DT];
-        if (b + 4 < b1) load_kv(b + 4, kn, vn);  // next block of this wave
+        bf16x8 k2[2][KS], v2[DT];
+        if (b + 8 < b1) load_kv(b + 8, k2, v2);
         __builtin_amdgcn_sched_barrier(0);
         // keys of this lane: 8g + 4kt + r; valid while below the user's length
         attn_block<DH, NT, SCORE>(st, kf, vf, L - (b - P.pblk[u]) * 32, lane);
-        if (b + 4 < b1) {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kf[kt][k] = kn[kt][k];
+          for (int k = 0; k < KS; ++k) {
+            kf[kt][k] = k1[kt][k];
+            k1[kt][k] = k2[kt][k];
+          }
 #pragma unroll
-          for (int t = 0; t < DT; ++t) vf[t] = vn[t];
+        for (int t = 0; t < DT; ++t) {
+          vf[t] = v1[t];
+          v1[t] = v2[t];
         }
       }
 
       // ---- merge the four waves in LDS, write this segment's partial
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        float l = st.lrun[n];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = st.l[n][0];  // already the whole block range's sum
         int cn = st.cnt[n];
         cn += __shfl_xor(cn, 16);
         cn += __shfl_xor(cn, 32);

@@ -28,8 +28,9 @@ struct AttnState {
   static constexpr int KS = DH / 32;  // k-steps of the score MFMA
   static constexpr int DT = DH / 16;  // feature tiles of the output
   bf16x8 qf[NT][KS];
-  float mrun[NT], lrun[NT];
-  int cnt[NT];
+  float mrun[NT];  // running max (natural units) the weights are taken against
+  f32x4 l[NT];     // softmax: running sum of the (rounded) weights, in every row
+  int cnt[NT];     // relu: keys with a positive score (this lane's share)
   f32x4 o[DT][NT];
 };
 
@@ -44,7 +45,7 @@ DEV void attn_reset(AttnState<DH, NT> &s) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     s.mrun[n] = kAttnNegBig;
-    s.lrun[n] = 0.f;
+    s.l[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     s.cnt[n] = 0;
 #pragma unroll
     for (int t = 0; t < AttnState<DH, NT>::DT; ++t) s.o[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -72,6 +73,13 @@ DEV void attn_load_q(AttnState<DH, NT> &s, const bf16_t *Q, int d, int h, int64_
   }
 }
 
+// Softmax weights are taken against a running max that is only raised when
+// some target's block max exceeds it by more than kAttnLazy (natural units,
+// a factor 2^8): weights then stay below 256, well inside bf16 and fp32, and
+// o and l are always scaled against the same max, so the normalised result
+// is unchanged -- only the rescaling work is skipped for most blocks.
+constexpr float kAttnLazy = 8.0f / kAttnLog2e;
+
 // One block: kf = K fragments (score tiles 0/1, k-steps), vf = V^T fragments
 // (feature tiles); keys at or beyond nvalid (block-local) are masked.
 template <int DH, int NT, int SCORE>
@@ -79,6 +87,7 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
                     int nvalid, int lane) {
   constexpr int KS = DH / 32, DT = DH / 16;
   const int g = lane >> 4;
+  const bool full = nvalid >= 32;  // uniform: only a user's last block is partial
   f32x4 st[2][NT];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -89,49 +98,63 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
       for (int k = 0; k < KS; ++k) st[kt][n] = mfma16(kf[kt][k], s.qf[n][k], st[kt][n]);
     }
   bf16x8 pk[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    float pv[8];
-    if (SCORE == 0) {
-      float mx = kAttnNegBig;
+  if (SCORE == 0) {
+    if (!full) {  // masked keys score -inf
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (8 * g + 4 * kt + r < nvalid) mx = fmaxf(mx, st[kt][n][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(s.mrun[n], mx);
-      const float corr = attn_ex2((s.mrun[n] - mnew) * kAttnLog2e);
-      s.mrun[n] = mnew;
-      const float mb = mnew * kAttnLog2e;
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (8 * g + 4 * kt + r >= nvalid) st[kt][n][r] = kAttnNegBig;
+    }
+    float mx[NT];
+    bool raise = false;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float m = fmaxf(fmaxf(fmaxf(st[0][n][0], st[0][n][1]), fmaxf(st[0][n][2], st[0][n][3])),
+                      fmaxf(fmaxf(st[1][n][0], st[1][n][1]), fmaxf(st[1][n][2], st[1][n][3])));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      mx[n] = m;
+      raise |= m > s.mrun[n] + kAttnLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float mnew = fmaxf(s.mrun[n], mx[n]);
+        const float corr = attn_ex2((s.mrun[n] - mnew) * kAttnLog2e);
+        s.mrun[n] = mnew;
+        s.l[n] *= corr;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) s.o[t][n] *= corr;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float mb = s.mrun[n] * kAttnLog2e;
+      float pv[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = 0.f;
-          if (8 * g + 4 * kt + r < nvalid) p = attn_ex2(fmaf(st[kt][n][r], kAttnLog2e, -mb));
-          pv[4 * kt + r] = p;
-        }
-      float psum = 0.f;
+        for (int r = 0; r < 4; ++r) pv[4 * kt + r] = attn_ex2(fmaf(st[kt][n][r], kAttnLog2e, -mb));
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
         pk[n][e] = (short)(pr & 0xffff);
         pk[n][e + 1] = (short)(pr >> 16);
-        // the sum uses the rounded weights the PV product sees
-        psum += bf2f((bf16_t)(pr & 0xffff)) + bf2f((bf16_t)(pr >> 16));
       }
-      s.lrun[n] = s.lrun[n] * corr + psum;
+    }
+  } else {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) s.o[t][n] *= corr;
-    } else {
+    for (int n = 0; n < NT; ++n) {
+      float pv[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sc = st[kt][n][r];
-          const bool on = (8 * g + 4 * kt + r < nvalid) && sc > 0.f;
+          const bool on = (full || 8 * g + 4 * kt + r < nvalid) && sc > 0.f;
           s.cnt[n] += on ? 1 : 0;
           pv[4 * kt + r] = on ? sc : 0.f;
         }
@@ -147,6 +170,15 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int n = 0; n < NT; ++n) s.o[t][n] = mfma16(vf[t], pk[n], s.o[t][n]);
+  if (SCORE == 0) {
+    // l += sum of this block's weights as rounded for the PV product: an
+    // all-ones A operand makes every output row that column sum
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (short)0x3f80;  // bf16 1.0
+#pragma unroll
+    for (int n = 0; n < NT; ++n) s.l[n] = mfma16(ones, pk[n], s.l[n]);
+  }
 }
 
 // Partial-slot indexing shared by the attention kernels and the merge: the

@@ -173,10 +173,13 @@ struct NoHook {
 // chain; OUT_KV writes blocked K/V to HBM, OUT_ROWS rows, OUT_FUSED leaves
 // the tile's K/V in LDS (fused_k_stage / fused_v_stage, head width FDH).
 // IN_STAGED: the caller has already written the input rows to sm.xs and
-// synchronised.  pre_ln / pre_proj run (all threads) just before the LN and
-// just before the projection: a persistent caller prefetches its next tile's
-// input there, while the chain's own memory traffic is light.
-template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT, int FDH = 0,
+// synchronised.  XT_GS: the LN output goes to the G buffer (sm.gs, row stride
+// D + kPad) instead of over the input rows, which stay intact for the next
+// layer's FFN (the caller synchronises before that FFN writes sm.gs again).
+// pre_ln / pre_proj run (all threads) just before the LN and just before the
+// projection: a caller can prefetch there, while the chain's own memory
+// traffic is light.
+template <int D, int TT, int IN, bool FFN, bool LN, bool PROJ, int OUT, int FDH = 0, bool XT_GS = false,
           class PreLn = NoHook, class PreProj = NoHook>
 DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN> &sm,
                     PreLn pre_ln = PreLn{}, PreProj pre_proj = PreProj{}) {
@@ -195,9 +198,9 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
   int *const s_tok = sm.s_tok;
 
   int tid = threadIdx.x;
-  // inside the fused kernel's tile loop: keep per-lane address arithmetic
+  // inside a loop over tiles or layers: keep per-lane address arithmetic
   // from being hoisted out of the loop (see fused_kernel)
-  if constexpr (OUT == OUT_FUSED) asm volatile("" : "+v"(tid));
+  if constexpr (OUT == OUT_FUSED || IN == IN_STAGED) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
@@ -205,9 +208,15 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
   const int kg = hi * 16;           // lane's k offset inside a 32-wide k block
   const bf16_t *table = (const bf16_t *)a.table;
   // MFMA-column (token) operands read from LDS rows
-  const bf16_t *bx[TT];
+  static_assert(!XT_GS || (FFN && PROJ && OUT == OUT_KV), "XT_GS: history chain writing K/V");
+  bf16_t *const xt = XT_GS ? &sm.gs[0][0] : xs;  // where the LN output (projection input) lives
+  static_assert(!XT_GS || sizeof(sm.gs) >= sizeof(bf16_t) * 32 * TT * (D + kPad), "LN output exceeds G buffer");
+  const bf16_t *bx[TT], *bp[TT];
 #pragma unroll
-  for (int j = 0; j < TT; ++j) bx[j] = xs + (j * 32 + l32) * XLD + kg;
+  for (int j = 0; j < TT; ++j) {
+    bx[j] = xs + (j * 32 + l32) * XLD + kg;
+    bp[j] = xt + (j * 32 + l32) * XLD + kg;
+  }
 
   // weight rows streamed through the ring (each pointer: this lane's row + kg)
   constexpr int YT = FT < 2 ? FT : 2;  // weight tiles per phase
@@ -310,7 +319,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
       if (row0 + r < a.n_rows) v = *reinterpret_cast<const u32x4 *>(src + (row0 + r) * a.lda + c);
       *reinterpret_cast<u32x4 *>(xs + r * XLD + c) = v;
     }
-  } else {  // IN_PREGEMM: xs = bf16([seg1 | seg2] W_pre), computed as W_pre^T [seg1|seg2]^T
+  } else if (IN == IN_PREGEMM) {  // xs = bf16([seg1 | seg2] W_pre), computed as W_pre^T [seg1|seg2]^T
     f32x16 acc[FT][TT];
     zero(acc);
     const bf16_t *wpre = (const bf16_t *)a.wpre;
@@ -456,7 +465,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
             const int t = j * 32 + l32;
             if (PROJ) {
               u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-              *reinterpret_cast<u32x2 *>(xs + t * XLD + f) = pv;
+              *reinterpret_cast<u32x2 *>(xt + t * XLD + f) = pv;
             } else if (row0 + t < a.n_rows) {
               if (a.out32) {
                 f32x4 ov = {v[0], v[1], v[2], v[3]};
@@ -495,7 +504,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) proj_ptrs2(sp + 1, 0, nx);
         else proj_ptrs2(0, nkD, nx);
-        phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
+        phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bp, nx);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
@@ -525,9 +534,9 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, nkD, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, nkD, nx);
-          phase<TT, YT, D / 32, false, 2>(acc, ring, gp, bx, nx);
+          phase<TT, YT, D / 32, false, 2>(acc, ring, gp, bp, nx);
         } else {
-          phase<TT, YT, D / 32, false, 0>(acc, ring, gp, bx, nx);
+          phase<TT, YT, D / 32, false, 0>(acc, ring, gp, bp, nx);
         }
         if constexpr (OUT == OUT_FUSED) __syncthreads();  // V^T goes over rows other waves read
 #pragma unroll
@@ -562,9 +571,9 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, 0, nx);
-          phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
+          phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bp, nx);
         } else {
-          phase<YT, TT, D / 32, true, 0>(acc, ring, gp, bx, nx);
+          phase<YT, TT, D / 32, true, 0>(acc, ring, gp, bp, nx);
         }
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
@@ -621,6 +630,45 @@ __global__ __launch_bounds__(kThreads, (TT >= 4 ? 1 : (D <= 256 ? 2 : 1))) void 
     }
   }
   chain_tile<D, TT, IN, FFN, LN, PROJ, OUT>(a, row0, sm);
+}
+
+// ---------------------------------------------------------------- history
+// Every layer's history FFN reads the same raw rows ([Notes] §STCA), so one
+// launch encodes all M layers: a 64-row tile is gathered once into LDS and
+// stays there while each layer runs SwiGLU FFN [+ LN] (its output goes to the
+// G buffer) and W_K | W_V on it, writing that layer's blocked K/V.
+template <int D, bool LN>
+__global__ __launch_bounds__(kThreads, 2) void hist_layers_kernel(ChainArgs a, HistLayers hl) {
+  __shared__ ChainSmem<D, 2, true> sm;
+  const int64_t row0 = (int64_t)blockIdx.x * 64;
+  ChainArgs ta = a;
+  ta.w1 = hl.w1[0];
+  ta.w3 = hl.w3[0];
+  ta.w2 = hl.w2[0];
+  ta.wp = hl.wp[0];
+  ta.ln_g = hl.ln_g[0];
+  ta.ln_b = hl.ln_b[0];
+  ta.kbuf = hl.kbuf[0];
+  ta.vbuf = hl.vbuf[0];
+  if (row0 >= (int64_t)a.plan.pblk[a.B] * 32) return;
+  chain_tile<D, 2, IN_GATHER_CSR, true, LN, true, OUT_KV, 0, true>(ta, row0, sm);
+#pragma unroll 1
+  for (int i = 1; i < hl.M; ++i) {
+    __syncthreads();  // the previous layer's projection is done with the G buffer
+    ChainArgs tb = a;
+    tb.w1 = hl.w1[i];
+    tb.w3 = hl.w3[i];
+    tb.w2 = hl.w2[i];
+    tb.wp = hl.wp[i];
+    tb.ln_g = hl.ln_g[i];
+    tb.ln_b = hl.ln_b[i];
+    tb.kbuf = hl.kbuf[i];
+    tb.vbuf = hl.vbuf[i];
+    tb.in_dump = nullptr;
+    // no weight address arithmetic hoisted out of this loop (see fused_kernel)
+    asm volatile("" : "+s"(tb.w1), "+s"(tb.w3), "+s"(tb.w2), "+s"(tb.wp), "+s"(tb.ln_g), "+s"(tb.ln_b));
+    chain_tile<D, 2, IN_STAGED, true, LN, true, OUT_KV, 0, true>(tb, row0, sm);
+  }
 }
 
 // ---------------------------------------------------------------- fused path
@@ -714,7 +762,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArg
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           st.mrun[n] = m4[n];
-          st.lrun[n] = l4[n];
+          st.l[n] = f32x4{l4[n], l4[n], l4[n], l4[n]};
           st.cnt[n] = __float_as_int(c4[n]);
         }
       }
@@ -742,7 +790,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArg
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           m4[n] = st.mrun[n];
-          l4[n] = st.lrun[n];
+          l4[n] = st.l[n][0];
           c4[n] = __int_as_float(st.cnt[n]);
         }
         rec[(DT * NT) * 64] = m4;
@@ -754,9 +802,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArg
       const int slot = (int)blockIdx.x + u;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        float l = st.lrun[n];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = st.l[n][0];
         int cn = st.cnt[n];
         cn += __shfl_xor(cn, 16);
         cn += __shfl_xor(cn, 32);
@@ -889,6 +935,25 @@ hipError_t launch_fused(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hip
   if (a.d == 256 && at.dh == 64) return launch_fused_d<256, 64>(a, at, max_tiles, s);
   if (a.d == 128 && at.dh == 32) return launch_fused_d<128, 32>(a, at, max_tiles, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_hist_layers(const ChainArgs &a, const HistLayers &hl, hipStream_t s) {
+  if (a.n_rows <= 0 || hl.M <= 0) return hipSuccess;
+  if (hl.M > kMaxLayers || a.in_mode != IN_GATHER_CSR || !a.ffn || !a.proj) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n_rows + 63) / 64)), block(kThreads);
+  switch (a.d) {
+    case 128:
+      if (a.ln) hipLaunchKernelGGL((hist_layers_kernel<128, true>), grid, block, 0, s, a, hl);
+      else hipLaunchKernelGGL((hist_layers_kernel<128, false>), grid, block, 0, s, a, hl);
+      break;
+    case 256:
+      if (a.ln) hipLaunchKernelGGL((hist_layers_kernel<256, true>), grid, block, 0, s, a, hl);
+      else hipLaunchKernelGGL((hist_layers_kernel<256, false>), grid, block, 0, s, a, hl);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s) {

@@ -9,7 +9,8 @@
 //   3. history side of every layer (gather -> SwiGLU FFN -> LN -> W_K | W_V)
 //      into the blocked K/V buffers.  The history side never depends on the
 //      query ([Notes] §STCA: each layer's FFN reads the raw rows), so all M
-//      layers are encoded before the query chain starts;
+//      layers are encoded before the query chain starts -- for bf16 at
+//      d <= 256 in one launch that gathers each tile once for all layers;
 //   4. per layer: query (q1 from x_t, or the fusion of [o_1..o_i | x_t]),
 //      Q = q W_Q / sqrt(d_h); attention partials and merge; o = attn W_O;
 //   5. z = SwiGLU([o_1 | .. | o_M | x_t] W_Z) [+ LN]   (linear mode: z = O_M).
@@ -503,7 +504,36 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   char *kvbase = at<char>(ws, L.kv);
   auto kbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i) * L.kv_layer); };
   auto vbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i + 1) * L.kv_layer); };
-  for (int i = 0; i < M && batch->n_hist > 0 && !L.fused; ++i) {
+  // bf16, d <= 256: all layers in one launch that gathers each tile once
+  const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers;
+  if (multi) {
+    ChainArgs a = hist_args(0);
+    HistLayers hl;
+    std::memset(&hl, 0, sizeof(hl));
+    hl.M = M;
+    for (int i = 0; i < M; ++i) {
+      const PrepLayer &p = L.pl[i];
+      hl.w1[i] = prep + p.kv_w1;
+      hl.w3[i] = prep + p.kv_w3;
+      hl.w2[i] = prep + p.kv_w2;
+      hl.wp[i] = prep + p.wkv;
+      hl.ln_g[i] = w->layers[i].kv.ln_g;
+      hl.ln_b[i] = w->layers[i].kv.ln_b;
+      hl.kbuf[i] = kbuf(i);
+      hl.vbuf[i] = vbuf(i);
+    }
+    if ((e = launch_hist_layers(a, hl, s))) return hip_fail(e, "history encoding");
+    for (int i = 0; i < M; ++i) {
+      if (out->kv_dump) {
+        char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;
+        char *vd = kd + (size_t)batch->n_hist * d * es;
+        e = launch_kv_relayout(cfg->dtype, kd, vd, kbuf(i), vbuf(i), plan, B, L.max_blocks, d, H, false, s);
+        if (e) return hip_fail(e, "kv dump");
+      }
+      if ((e = rec(2 + i))) return hip_fail(e, "stage event");
+    }
+  }
+  for (int i = 0; i < M && batch->n_hist > 0 && !L.fused && !multi; ++i) {
     ChainArgs a = hist_args(i);
     a.kbuf = kbuf(i);
     a.vbuf = vbuf(i);

@@ -90,6 +90,18 @@ struct ChainArgs {
 };
 
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s);
+
+// All M layers' history encodings in one launch (bf16, d 128 or 256): the
+// gathered rows of a tile are reused by every layer.  `a` carries the batch,
+// plan, flags and in_dump; the per-layer weights and K/V buffers come from hl.
+constexpr int kMaxLayers = 16;
+struct HistLayers {
+  const void *w1[kMaxLayers], *w3[kMaxLayers], *w2[kMaxLayers], *wp[kMaxLayers];
+  const float *ln_g[kMaxLayers], *ln_b[kMaxLayers];
+  void *kbuf[kMaxLayers], *vbuf[kMaxLayers];
+  int M;
+};
+hipError_t launch_hist_layers(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
 hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 
 // Weight preparation (bf16): a matrix W [K, N] (row-major, y = x W) is stored
