@@ -916,12 +916,18 @@ __global__ __launch_bounds__(256) void pack_batch_kernel(PackBatch pb) {
   const int n = (int)(idx % t.N), k0 = (int)(idx / t.N) * 8;
   const int ng = t.row_tile0 * 32 + n;
   const int kk = k0 % 32;
-  const int lane = 32 * (kk / 16) + ng % 32;
   uint32_t v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = t.src[(int64_t)(k0 + e) * t.N + n];
   const u32x4 pk = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
-  bf16_t *d = t.dst + frag_off(ng / 32, k0 / 32, t.K / 32, (kk % 16) / 8, lane);
+  bf16_t *d;
+  if (t.fmt == 1) {  // 16x16x32 A operand
+    const int lane = 16 * (kk / 8) + ng % 16;
+    d = t.dst + (((int64_t)(ng / 16) * (t.K / 32) + k0 / 32) * 64 + lane) * 8;
+  } else {
+    const int lane = 32 * (kk / 16) + ng % 32;
+    d = t.dst + frag_off(ng / 32, k0 / 32, t.K / 32, (kk % 16) / 8, lane);
+  }
   *reinterpret_cast<u32x4 *>(d) = pk;
 }
 

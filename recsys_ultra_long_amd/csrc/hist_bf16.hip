@@ -1,0 +1,380 @@
+// hist_bf16.hip -- history encoder for d = 256 (bf16): every layer's
+//   X~ = [LN](SwiGLU(X)) = [LN]((SiLU(X W1) * (X W3)) W2),  K = X~ W_K, V = X~ W_V
+// ([Notes] §STCA; [Review] architecture tree) over 128-row tiles of the
+// padded history, all M layers per launch on one gathered tile.
+//
+// Why this shape.  The encoder's weights (1 MB per layer) do not fit on chip,
+// so every row tile streams all of them from L2; with 64-row tiles that
+// stream is the bound (the vector-memory data path, not the matrix cores).
+// Here a workgroup of 8 waves (one per CU, two per SIMD) takes 128 rows and
+// splits the *outputs* of each contraction over its waves, so every weight
+// fragment a wave loads feeds all 128 rows:
+//   G   = SiLU(X W1) * (X W3)  : wave w owns hidden units 16w .. 16w+15 of each
+//                                128-unit chunk (16x16x32 MFMA, 8 row tiles)
+//   Y^T += W2^T G^T            : wave w owns features 32w .. 32w+31 (32x32x16)
+//   K^T  = W_K^T X~^T, V = X~ W_V : wave w owns features 32w .. 32w+31
+// Weights are consumed as a fixed chain of phases whose 32-wide k blocks
+// stream through a 4-slot register ring kept three blocks ahead, across phase
+// (and layer) boundaries.  LDS: the raw rows (kept for all layers), two G
+// chunk buffers which, after the FFN, hold the LN output for the projection.
+#include <algorithm>
+
+#include "stca_internal.h"
+
+namespace stca {
+namespace {
+
+constexpr int kD = 256;
+constexpr int kT = 512;          // threads: 8 waves
+constexpr int kR = 128;          // rows per tile
+constexpr int kHC = 128;         // hidden units per chunk (16 per wave)
+constexpr int kXLD = kD + 8;     // LDS row stride of X / X~ (elements)
+constexpr int kGLD = kHC + 8;    // LDS row stride of a G chunk
+
+struct Smem {
+  __attribute__((aligned(16))) bf16_t xs[kR * kXLD];
+  __attribute__((aligned(16))) bf16_t gs[2][kR * kGLD];
+  float red[2][8][kR];
+  int s_id[kR], s_tok[kR];
+};
+static_assert(sizeof(Smem::gs) >= sizeof(bf16_t) * kR * kXLD, "LN output must fit the G buffers");
+
+// Two 16-byte fragments per k block: (W1, W3) of a 16-row tile in the G
+// phase, the two k halves of a 32-row tile elsewhere.
+struct Src {
+  const bf16_t *p0, *p1;
+  int stride;  // elements per k block
+};
+struct Ring {
+  bf16x8 v[4][2];
+};
+DEV void ring_load(Ring &r, int slot, const Src &s, int kb) {
+  r.v[slot][0] = ld8(s.p0 + kb * s.stride);
+  r.v[slot][1] = ld8(s.p1 + kb * s.stride);
+}
+
+// Per-wave weight sources of each phase.  W1/W3 are packed for the 16x16x32
+// A operand (frag16), W2 and W_K|W_V for the 32x32x16 A operand (frag_off).
+struct Layer {
+  const bf16_t *w1, *w3, *w2, *wp;
+  const float *ln_g, *ln_b;
+  bf16_t *kb, *vb;
+};
+DEV Src src_g(const Layer &L, int hc, int w, int lane) {
+  const int64_t o = (int64_t)((hc * 8 + w) * (kD / 32)) * 512 + lane * 8;
+  return Src{L.w1 + o, L.w3 + o, 512};
+}
+DEV Src src_y(const Layer &L, int hc, int w, int lane, int nkh) {
+  const bf16_t *p = L.w2 + frag_off(w, hc * (kHC / 32), nkh, 0, lane);
+  return Src{p, p + 512, 1024};
+}
+DEV Src src_proj(const Layer &L, int tile, int lane) {
+  const bf16_t *p = L.wp + frag_off(tile, 0, kD / 32, 0, lane);
+  return Src{p, p + 512, 1024};
+}
+
+// The NK blocks of one phase; `mma(kb, slot)` does the block's matrix work.
+// Block kb + 3 is loaded while block kb is used (from the next phase once this
+// one runs out; `more` = whether there is a next phase).
+template <int NK, class F>
+DEV void run_phase(Ring &ring, const Src &cur, const Src &nxt, bool more, F mma) {
+  static_assert(NK % 4 == 0, "phase length must be a multiple of 4 blocks");
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) {
+    const int nb = kb + 3;
+    if (nb < NK) ring_load(ring, nb % 4, cur, nb);
+    else if (more) ring_load(ring, nb % 4, nxt, nb - NK);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(kb, kb % 4);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int N>
+DEV void zero4(f32x4 (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+template <int N>
+DEV void zero16(f32x16 (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a[i][e] = 0.f;
+}
+
+template <bool LN>
+__global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers hl) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;     // 32x32 operand / output roles
+  const int c16 = lane & 15, g16 = lane >> 4;    // 16x16 roles
+  const int64_t row0 = (int64_t)blockIdx.x * kR;
+  const int total_blocks = a.plan.pblk[a.B];
+  if (row0 >= (int64_t)total_blocks * 32) return;
+  const int nkh = a.hidden / 32, nchunk = a.hidden / kHC;
+  const int H = a.H, DH = kD / a.H;
+  auto layer = [&](int i) {
+    Layer L;
+    L.w1 = (const bf16_t *)hl.w1[i];
+    L.w3 = (const bf16_t *)hl.w3[i];
+    L.w2 = (const bf16_t *)hl.w2[i];
+    L.wp = (const bf16_t *)hl.wp[i];
+    L.ln_g = hl.ln_g[i];
+    L.ln_b = hl.ln_b[i];
+    L.kb = (bf16_t *)hl.kbuf[i];
+    L.vb = (bf16_t *)hl.vbuf[i];
+    return L;
+  };
+
+  Ring ring;
+  {
+    const Layer L0 = layer(0);
+    const Src s0 = src_g(L0, 0, w, lane);
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) ring_load(ring, kb, s0, kb);
+  }
+
+  // ---------------------------------------------------------------- gather
+  if (tid < kR) {
+    const int64_t p = row0 + tid;
+    int id = -1, tok = -1;
+    const int blk = (int)(p >> 5);
+    if (a.plan.prow && !a.in_dump) {
+      id = a.plan.prow[p];  // planner-validated id of this padded row
+    } else if (blk < total_blocks) {
+      const int u = upper_index(a.plan.pblk, a.B, blk);
+      const int j = (int)(p - (int64_t)a.plan.pblk[u] * 32);
+      if (j < a.plan.hoff[u + 1] - a.plan.hoff[u]) {
+        tok = a.plan.hoff[u] + j;
+        id = a.ids[tok];
+        if (id < 0 || (int64_t)id >= a.table_rows) {
+          set_status(a.status, 4);
+          id = -1;
+        }
+      }
+    }
+    sm.s_id[tid] = id;
+    sm.s_tok[tid] = tok;
+  }
+  __syncthreads();
+  {
+    const bf16_t *table = (const bf16_t *)a.table;
+    constexpr int C8 = kD / 8;
+#pragma unroll
+    for (int k = 0; k < kR * C8 / kT; ++k) {
+      const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
+      const int id = sm.s_id[r];
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * kD + c);
+      *reinterpret_cast<u32x4 *>(sm.xs + r * kXLD + c) = v;
+      if (a.in_dump && sm.s_tok[r] >= 0)
+        *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)sm.s_tok[r] * kD + c) = v;
+    }
+  }
+  __syncthreads();
+
+  bf16_t *const xt = &sm.gs[0][0];  // LN output, row stride kXLD
+#pragma unroll 1
+  for (int li = 0; li < hl.M; ++li) {
+    // lane quantities re-derived per layer so none is held across layers
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    const int lane = ltid & 63;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int c16 = lane & 15, g16 = lane >> 4;
+    const bf16_t *const xrow = sm.xs + c16 * kXLD + g16 * 8;  // G-phase operand base
+    Layer L = layer(li);
+    // the weight addresses stay loop-variant (no hoisting across layers)
+    asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
+    if (li > 0) __syncthreads();  // the previous layer's projection is done with X~
+
+    // ------------------------------------------------------------ SwiGLU FFN
+    f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
+    zero16(y);
+#pragma unroll 1
+    for (int hc = 0; hc < nchunk; ++hc) {
+      bf16_t *g = sm.gs[hc & 1];
+      {  // G^T tiles: W1 and W3 rows of this wave's 16 hidden units x 128 tokens
+        f32x4 acc[2][8];
+        zero4(acc[0]);
+        zero4(acc[1]);
+        const Src cur = src_g(L, hc, w, lane), nxt = src_y(L, hc, w, lane, nkh);
+        run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+#pragma unroll
+          for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
+            bf16x8 bx[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXLD + kb * 32);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
+          }
+        });
+        // lane: hidden rows 4 g16 + i of token 16 t + c16
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          float gv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i] = silu_fast(acc[0][t][i]) * acc[1][t][i];
+          u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
+          *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
+        }
+      }
+      __syncthreads();
+      {  // Y^T += W2^T[features 32w.., chunk] G^T[chunk, tokens]
+        Src nxt;
+        bool more = true;
+        if (hc + 1 < nchunk) nxt = src_g(L, hc + 1, w, lane);
+        else nxt = src_proj(L, w, lane);
+        const Src cur = src_y(L, hc, w, lane, nkh);
+        run_phase<kHC / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bf16x8 bg[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
+          }
+        });
+      }
+    }
+
+    // ------------------------------------------------------------ LayerNorm
+    // lane: features 32w + c32_row(lane, i) of tokens 32j + l32
+    float mean[4], rstd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mean[j] = 0.f;
+      rstd[j] = 1.f;
+    }
+    if (LN) {
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = y[j][i];
+            v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
+          }
+          v += __shfl_xor(v, 32);
+          if (hi == 0) sm.red[pass][w][j * 32 + l32] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = j * 32 + l32;
+          float tot = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) tot += sm.red[pass][q][t];
+          if (pass == 0) mean[j] = tot * (1.0f / kD);
+          else rstd[j] = rsqrtf(tot * (1.0f / kD) + 1e-5f);
+        }
+      }
+    } else {
+      __syncthreads();  // every wave is done reading the last G chunk
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = w * 32 + 8 * q + 4 * hi;
+      f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
+      if (LN) {
+        gg = *reinterpret_cast<const f32x4 *>(L.ln_g + f);
+        bb = *reinterpret_cast<const f32x4 *>(L.ln_b + f);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = y[j][4 * q + r];
+          if (LN) v[r] = (v[r] - mean[j]) * rstd[j] * gg[r] + bb[r];
+        }
+        u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+        *reinterpret_cast<u32x2 *>(xt + (j * 32 + l32) * kXLD + f) = pv;
+      }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ W_K | W_V
+    {  // K^T = W_K^T X~^T: 4 consecutive features of one key per lane
+      f32x16 acc[4];
+      zero16(acc);
+      const Src cur = src_proj(L, w, lane), nxt = src_proj(L, kD / 32 + w, lane);
+      run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bx[j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = mfma32(ring.v[slot][h], bx[j], acc[j]);
+        }
+      });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = (int)(row0 >> 5) + j;
+        if (blk >= total_blocks) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = w * 32 + 8 * q + 4 * hi;
+          const int h = f / DH, dh = f % DH;
+          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
+          *reinterpret_cast<u32x2 *>(L.kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh) = v;
+        }
+      }
+    }
+    {  // V = X~ W_V with keys as MFMA rows: 4 consecutive keys of one feature per lane
+      f32x16 acc[4];
+      zero16(acc);
+      const bool more = li + 1 < hl.M;
+      Src nxt = src_proj(L, w, lane);  // any valid address when nothing follows
+      if (more) {
+        const Layer Ln = layer(li + 1);
+        nxt = src_g(Ln, 0, w, lane);
+      }
+      const Src cur = src_proj(L, kD / 32 + w, lane);
+      run_phase<kD / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bx[j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = mfma32(bx[j], ring.v[slot][h], acc[j]);
+        }
+      });
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = (int)(row0 >> 5) + j;
+        if (blk >= total_blocks) continue;
+        const int f = w * 32 + l32;
+        const int h = f / DH, dh = f % DH;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int key = 8 * q + 4 * hi;
+          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
+          *reinterpret_cast<u32x2 *>(L.vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t s) {
+  if (a.n_rows <= 0 || hl.M <= 0) return hipSuccess;
+  if (a.d != kD || hl.M > kMaxLayers || a.hidden % kHC || a.in_mode != IN_GATHER_CSR)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n_rows + kR - 1) / kR)), block(kT);
+  if (a.ln) hipLaunchKernelGGL(hist256_kernel<true>, grid, block, 0, s, a, hl);
+  else hipLaunchKernelGGL(hist256_kernel<false>, grid, block, 0, s, a, hl);
+  return hipGetLastError();
+}
+
+}  // namespace stca

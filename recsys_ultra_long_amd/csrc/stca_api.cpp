@@ -359,8 +359,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     PackBatch pb;
     int n = 0;
     // W [K, N] -> packed W^T fragments at `dst` (+ row tile offset)
-    auto add = [&](const void *src, int K, int N, size_t dst, int tile0) -> hipError_t {
-      pb.m[n++] = PackDesc{(const bf16_t *)src, prep + dst, K, N, tile0};
+    auto add = [&](const void *src, int K, int N, size_t dst, int tile0, int fmt = 0) -> hipError_t {
+      pb.m[n++] = PackDesc{(const bf16_t *)src, prep + dst, K, N, tile0, fmt};
       if (n == kMaxPacks) {
         hipError_t er = launch_pack_batch(pb, n, s);
         n = 0;
@@ -372,8 +372,10 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (int i = 0; i < M; ++i) {
       const stca_layer &l = w->layers[i];
       const PrepLayer &p = L.pl[i];
-      if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0))) break;
-      if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0))) break;
+      // the d = 256 staged history encoder reads W1 / W3 as 16-row tiles
+      const int f13 = (d == 256 && !L.fused) ? 1 : 0;
+      if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
+      if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
       if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
       if ((e = add(l.wk, d, d, p.wkv, 0))) break;
       if ((e = add(l.wv, d, d, p.wkv, d / 32))) break;
@@ -522,7 +524,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       hl.kbuf[i] = kbuf(i);
       hl.vbuf[i] = vbuf(i);
     }
-    if ((e = launch_hist_layers(a, hl, s))) return hip_fail(e, "history encoding");
+    e = d == 256 ? launch_hist256(a, hl, s) : launch_hist_layers(a, hl, s);
+    if (e) return hip_fail(e, "history encoding");
     for (int i = 0; i < M; ++i) {
       if (out->kv_dump) {
         char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;

@@ -33,7 +33,7 @@ inline int64_t max_chunks(int64_t n_hist, int B, int nb) {
 // Padded-row id map (Plan::prow) after the planner: entries for every row of
 // the 64-row tiles over max_blocks blocks.  Ids outside [0, table_rows) set
 // status bit 4 and read as -1.
-inline int64_t prow_rows(int64_t max_blocks) { return (max_blocks + 2) * 32; }
+inline int64_t prow_rows(int64_t max_blocks) { return (max_blocks + 4) * 32; }
 hipError_t launch_padded_ids(const Plan &plan, int B, const int *hist_ids, int64_t table_rows,
                              int64_t max_blocks, int *status, hipStream_t s);
 
@@ -102,6 +102,8 @@ struct HistLayers {
   int M;
 };
 hipError_t launch_hist_layers(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
+// d = 256: 128-row tiles on 8 waves (W1, W3 packed with fmt 1).
+hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
 hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 
 // Weight preparation (bf16): a matrix W [K, N] (row-major, y = x W) is stored
@@ -113,10 +115,14 @@ hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 //   h = (k % 16) / 8, e = k % 8, NK = K / 32.
 // so one fragment load is a single contiguous 1 KB read.  row_tile0 places
 // the matrix at a tile offset of the destination (W_K and W_V share one).
+// fmt 1 packs for the 16x16x32 A operand instead (16-row tiles):
+//   element (n, k) -> ((n / 16 * NK + kb) * 64 + lane) * 8 + e,
+//   lane = 16 * ((k % 32) / 8) + n % 16,  e = k % 8.
 struct PackDesc {
   const bf16_t *src;
   bf16_t *dst;
   int K, N, row_tile0;
+  int fmt;
 };
 constexpr int kMaxPacks = 48;
 struct PackBatch {
