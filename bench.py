@@ -204,7 +204,7 @@ def main():
                            "launch_ms": round(t_attn * 1e3, 4),
                            "per_launch": f"{n_hist} tokens x {6 * d * h + 4 * d * d} flop + "
                                          f"{pairs} (token, target) pairs x {4 * d} flop"}}
-    picks = {"history": lambda k: (k.startswith(f"hist_layers_kernel<{d},") or
+    picks = {"history": lambda k: (k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
                                    (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
              "attention": lambda k: k.startswith("attn_bf16_kernel<"),
              "fused": lambda k: k.startswith(f"fused_kernel<{d},")}
