@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 //   softmax: attn = sum_w acc_w e^{m_w - M} / sum_w l_w e^{m_w - M};  ReLU: sums.
 // Streaming partials: a workgroup's segment of a pair is stored at the
 // segment's first unit.  Fused partials (one per workgroup and user, all
-// heads): slot workgroup + user, units = the user's 64-key tiles.
+// heads): slot workgroup + user, units = the user's key tiles.
 template <int SCORE>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int d = a.d, DH = a.dh, H = a.H, G = a.groups, HG = H * G;
@@ -292,9 +292,10 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
     const int tg = tl - grp * 64;
     int first, nu, per;
     if (a.fused) {
-      first = P.pblk[u] / 2;
-      nu = (P.pblk[u + 1] - P.pblk[u]) / 2;
-      per = units_per_wg(P.pblk[a.B] / 2, a.grid);
+      const int tb = a.tile_blocks;
+      first = P.pblk[u] / tb;
+      nu = (P.pblk[u + 1] - P.pblk[u]) / tb;
+      per = units_per_wg(P.pblk[a.B] / tb, a.grid);
     } else {
       nu = P.coff[u + 1] - P.coff[u];
       first = P.coff[u] * HG + (grp * H + h) * nu;

@@ -19,6 +19,7 @@
 // chunk buffers which, after the FFN, hold the LN output for the projection.
 #include <algorithm>
 
+#include "attn_block.h"
 #include "stca_internal.h"
 
 namespace stca {
@@ -103,6 +104,170 @@ DEV void zero16(f32x16 (&a)[N]) {
     for (int e = 0; e < 16; ++e) a[i][e] = 0.f;
 }
 
+// Gather the 128 table rows of a tile into sm.xs (zeros for padding rows and
+// for ids outside the table), with the optional copy by history token.
+// `use_prow`: take the planner's padded-row ids when present.  Ends synchronised.
+DEV void gather_tile(const ChainArgs &a, Smem &sm, int64_t row0, int total_blocks, int tid, bool use_prow) {
+  if (tid < kR) {
+    const int64_t p = row0 + tid;
+    int id = -1, tok = -1;
+    const int blk = (int)(p >> 5);
+    if (use_prow && a.plan.prow && !a.in_dump) {
+      id = a.plan.prow[p];  // planner-validated id of this padded row
+    } else if (blk < total_blocks) {
+      const int u = upper_index(a.plan.pblk, a.B, blk);
+      const int j = (int)(p - (int64_t)a.plan.pblk[u] * 32);
+      if (j < a.plan.hoff[u + 1] - a.plan.hoff[u]) {
+        tok = a.plan.hoff[u] + j;
+        id = a.ids[tok];
+        if (id < 0 || (int64_t)id >= a.table_rows) {
+          set_status(a.status, 4);
+          id = -1;
+        }
+      }
+    }
+    sm.s_id[tid] = id;
+    sm.s_tok[tid] = tok;
+  }
+  __syncthreads();
+  const bf16_t *table = (const bf16_t *)a.table;
+  constexpr int C8 = kD / 8;
+#pragma unroll
+  for (int k = 0; k < kR * C8 / kT; ++k) {
+    const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
+    const int id = sm.s_id[r];
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * kD + c);
+    *reinterpret_cast<u32x4 *>(sm.xs + r * kXLD + c) = v;
+    if (a.in_dump && sm.s_tok[r] >= 0)
+      *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)sm.s_tok[r] * kD + c) = v;
+  }
+  __syncthreads();
+}
+
+// SwiGLU FFN [+ LN] of one layer over the 128 rows in sm.xs; X~ goes to
+// `xt` (row stride kXLD: over the rows themselves, or into the G buffers when
+// the rows must survive for another layer).  The ring enters holding the
+// first blocks of G chunk 0 and leaves holding those of the W_K phase; X~ is
+// visible to every thread on return.
+template <bool LN>
+DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lane, int nkh, int nchunk) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int c16 = lane & 15, g16 = lane >> 4;
+  const bf16_t *const xrow = sm.xs + c16 * kXLD + g16 * 8;  // G-phase operand base
+  // ------------------------------------------------------------ SwiGLU FFN
+  f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
+  zero16(y);
+#pragma unroll 1
+  for (int hc = 0; hc < nchunk; ++hc) {
+    bf16_t *g = sm.gs[hc & 1];
+    {  // G^T tiles: W1 and W3 rows of this wave's 16 hidden units x 128 tokens
+      f32x4 acc[2][8];
+      zero4(acc[0]);
+      zero4(acc[1]);
+      const Src cur = src_g(L, hc, w, lane), nxt = src_y(L, hc, w, lane, nkh);
+      run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
+          bf16x8 bx[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXLD + kb * 32);
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
+        }
+      });
+      // lane: hidden rows 4 g16 + i of token 16 t + c16
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float gv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gv[i] = silu_fast(acc[0][t][i]) * acc[1][t][i];
+        u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
+        *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
+      }
+    }
+    __syncthreads();
+    {  // Y^T += W2^T[features 32w.., chunk] G^T[chunk, tokens]
+      Src nxt;
+      bool more = true;
+      if (hc + 1 < nchunk) nxt = src_g(L, hc + 1, w, lane);
+      else nxt = src_proj(L, w, lane);
+      const Src cur = src_y(L, hc, w, lane, nkh);
+      run_phase<kHC / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 bg[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
+        }
+      });
+    }
+  }
+
+  // ------------------------------------------------------------ LayerNorm
+  // lane: features 32w + c32_row(lane, i) of tokens 32j + l32
+  float mean[4], rstd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mean[j] = 0.f;
+    rstd[j] = 1.f;
+  }
+  if (LN) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float x = y[j][i];
+          v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
+        }
+        v += __shfl_xor(v, 32);
+        if (hi == 0) sm.red[pass][w][j * 32 + l32] = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = j * 32 + l32;
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tot += sm.red[pass][q][t];
+        if (pass == 0) mean[j] = tot * (1.0f / kD);
+        else rstd[j] = rsqrtf(tot * (1.0f / kD) + 1e-5f);
+      }
+    }
+  } else {
+    __syncthreads();  // every wave is done reading the last G chunk
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int f = w * 32 + 8 * q + 4 * hi;
+    f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
+    if (LN) {
+      gg = *reinterpret_cast<const f32x4 *>(L.ln_g + f);
+      bb = *reinterpret_cast<const f32x4 *>(L.ln_b + f);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = y[j][4 * q + r];
+        if (LN) v[r] = (v[r] - mean[j]) * rstd[j] * gg[r] + bb[r];
+      }
+      u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      *reinterpret_cast<u32x2 *>(xt + (j * 32 + l32) * kXLD + f) = pv;
+    }
+  }
+  __syncthreads();
+
+}
+
 template <bool LN>
 __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers hl) {
   __shared__ Smem sm;
@@ -135,44 +300,7 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     for (int kb = 0; kb < 3; ++kb) ring_load(ring, kb, s0, kb);
   }
 
-  // ---------------------------------------------------------------- gather
-  if (tid < kR) {
-    const int64_t p = row0 + tid;
-    int id = -1, tok = -1;
-    const int blk = (int)(p >> 5);
-    if (a.plan.prow && !a.in_dump) {
-      id = a.plan.prow[p];  // planner-validated id of this padded row
-    } else if (blk < total_blocks) {
-      const int u = upper_index(a.plan.pblk, a.B, blk);
-      const int j = (int)(p - (int64_t)a.plan.pblk[u] * 32);
-      if (j < a.plan.hoff[u + 1] - a.plan.hoff[u]) {
-        tok = a.plan.hoff[u] + j;
-        id = a.ids[tok];
-        if (id < 0 || (int64_t)id >= a.table_rows) {
-          set_status(a.status, 4);
-          id = -1;
-        }
-      }
-    }
-    sm.s_id[tid] = id;
-    sm.s_tok[tid] = tok;
-  }
-  __syncthreads();
-  {
-    const bf16_t *table = (const bf16_t *)a.table;
-    constexpr int C8 = kD / 8;
-#pragma unroll
-    for (int k = 0; k < kR * C8 / kT; ++k) {
-      const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
-      const int id = sm.s_id[r];
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * kD + c);
-      *reinterpret_cast<u32x4 *>(sm.xs + r * kXLD + c) = v;
-      if (a.in_dump && sm.s_tok[r] >= 0)
-        *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)sm.s_tok[r] * kD + c) = v;
-    }
-  }
-  __syncthreads();
+  gather_tile(a, sm, row0, total_blocks, tid, true);
 
   bf16_t *const xt = &sm.gs[0][0];  // LN output, row stride kXLD
 #pragma unroll 1
@@ -183,122 +311,12 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     const int lane = ltid & 63;
     const int l32 = lane & 31, hi = lane >> 5;
     const int c16 = lane & 15, g16 = lane >> 4;
-    const bf16_t *const xrow = sm.xs + c16 * kXLD + g16 * 8;  // G-phase operand base
     Layer L = layer(li);
     // the weight addresses stay loop-variant (no hoisting across layers)
     asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
     if (li > 0) __syncthreads();  // the previous layer's projection is done with X~
 
-    // ------------------------------------------------------------ SwiGLU FFN
-    f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
-    zero16(y);
-#pragma unroll 1
-    for (int hc = 0; hc < nchunk; ++hc) {
-      bf16_t *g = sm.gs[hc & 1];
-      {  // G^T tiles: W1 and W3 rows of this wave's 16 hidden units x 128 tokens
-        f32x4 acc[2][8];
-        zero4(acc[0]);
-        zero4(acc[1]);
-        const Src cur = src_g(L, hc, w, lane), nxt = src_y(L, hc, w, lane, nkh);
-        run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
-#pragma unroll
-          for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
-            bf16x8 bx[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXLD + kb * 32);
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-              for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
-          }
-        });
-        // lane: hidden rows 4 g16 + i of token 16 t + c16
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          float gv[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = silu_fast(acc[0][t][i]) * acc[1][t][i];
-          u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
-          *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
-        }
-      }
-      __syncthreads();
-      {  // Y^T += W2^T[features 32w.., chunk] G^T[chunk, tokens]
-        Src nxt;
-        bool more = true;
-        if (hc + 1 < nchunk) nxt = src_g(L, hc + 1, w, lane);
-        else nxt = src_proj(L, w, lane);
-        const Src cur = src_y(L, hc, w, lane, nkh);
-        run_phase<kHC / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            bf16x8 bg[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
-          }
-        });
-      }
-    }
-
-    // ------------------------------------------------------------ LayerNorm
-    // lane: features 32w + c32_row(lane, i) of tokens 32j + l32
-    float mean[4], rstd[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mean[j] = 0.f;
-      rstd[j] = 1.f;
-    }
-    if (LN) {
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x = y[j][i];
-            v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
-          }
-          v += __shfl_xor(v, 32);
-          if (hi == 0) sm.red[pass][w][j * 32 + l32] = v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = j * 32 + l32;
-          float tot = 0.f;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) tot += sm.red[pass][q][t];
-          if (pass == 0) mean[j] = tot * (1.0f / kD);
-          else rstd[j] = rsqrtf(tot * (1.0f / kD) + 1e-5f);
-        }
-      }
-    } else {
-      __syncthreads();  // every wave is done reading the last G chunk
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int f = w * 32 + 8 * q + 4 * hi;
-      f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
-      if (LN) {
-        gg = *reinterpret_cast<const f32x4 *>(L.ln_g + f);
-        bb = *reinterpret_cast<const f32x4 *>(L.ln_b + f);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = y[j][4 * q + r];
-          if (LN) v[r] = (v[r] - mean[j]) * rstd[j] * gg[r] + bb[r];
-        }
-        u32x2 pv = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-        *reinterpret_cast<u32x2 *>(xt + (j * 32 + l32) * kXLD + f) = pv;
-      }
-    }
-    __syncthreads();
+    ffn_ln<LN>(ring, L, sm, xt, w, lane, nkh, nchunk);
 
     // ------------------------------------------------------------ W_K | W_V
     {  // K^T = W_K^T X~^T: 4 consecutive features of one key per lane
@@ -365,7 +383,249 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
   }
 }
 
+
+// ---------------------------------------------------------------- fused path
+// "Lookup while computing" ([WeChat] §1.1) on the same 128-row structure: a
+// persistent workgroup (one per CU) walks a contiguous range of 128-key tiles
+// (users padded to whole tiles).  Per tile: gather, SwiGLU FFN, LN (over the
+// rows), W_K into LDS over the G buffers (K rows padded), W_V into LDS over
+// the rows once every wave has read them (V^T rows of 128 keys, the 16-byte
+// chunks of row f XOR-swizzled by f mod 16 so that 16 consecutive features
+// read at one key offset hit different banks), then each wave folds the
+// tile's keys into the online-softmax (or ReLU) state of one head: d_h = 32,
+// wave w = head w, all targets; d_h = 64, waves 2h and 2h + 1 = head h,
+// targets 0..31 and 32..63.  No K/V tensor exists in HBM.  Between tiles of
+// one user the state goes through the workgroup's state area (each lane reads
+// back only what it wrote); at the user's last tile in the range it becomes a
+// partial in slot (workgroup + user) -- distinct slots, fewer than grid + B,
+// because ranges are contiguous and users ordered.
+template <int DH, int NT, int SCORE, bool LN>
+__global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs at) {
+  constexpr int H = kD / DH;
+  constexpr int WPH = 8 / H;            // waves per head
+  constexpr int TPW = 64 / WPH;         // targets per wave
+  constexpr int KS = DH / 32, DT = DH / 16;
+  constexpr int REC = DT * NT + 3;      // f32x4 per lane: o, then m, l, count
+  static_assert(NT * 16 <= TPW, "target tiles exceed the wave's share");
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, w = tid >> 6;
+  const Plan P = at.plan;
+  const int tiles = P.pblk[at.B] / 4;
+  const int per = (tiles + (int)gridDim.x - 1) / (int)gridDim.x;
+  int tile = (int)blockIdx.x * per;
+  const int tend = min(tiles, tile + per);
+  const int nkh = a.hidden / 32, nchunk = a.hidden / kHC;
+  const int head = w / WPH, t0 = (w % WPH) * TPW;
+  const bf16_t *Q = (const bf16_t *)at.q;
+  Ring ring;
+  if (tile < tend) {
+    Layer L0{(const bf16_t *)a.w1, (const bf16_t *)a.w3, (const bf16_t *)a.w2, (const bf16_t *)a.wp,
+             a.ln_g, a.ln_b, nullptr, nullptr};
+    const Src s0 = src_g(L0, 0, w, tid & 63);
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) ring_load(ring, kb, s0, kb);
+  }
+  int cur_u = -1;
+  for (; tile < tend; ++tile) {
+    const int u = upper_index(P.pblk, at.B, tile * 4);
+    const int tbase = P.toff[u];
+    const int m_u = P.toff[u + 1] - tbase;
+    // a user without targets needs no K/V (only the optional input dump)
+    if (m_u == 0 && !a.in_dump) continue;
+    const bool first = u != cur_u;                                   // user's first tile here
+    const bool last = tile + 1 == tend || (tile + 1) * 4 >= P.pblk[u + 1];  // ... and last
+    cur_u = u;
+    // per-tile lane quantities and weight addresses (nothing held across tiles)
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    const int lane = ltid & 63;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int c16 = lane & 15, g16 = lane >> 4;
+    Layer L{(const bf16_t *)a.w1, (const bf16_t *)a.w3, (const bf16_t *)a.w2, (const bf16_t *)a.wp,
+            a.ln_g, a.ln_b, nullptr, nullptr};
+    asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
+    __syncthreads();  // the previous tile's attention is done with the staging
+    const int64_t row0 = (int64_t)tile * kR;
+    gather_tile(a, sm, row0, P.pblk[at.B], ltid, false);
+    ffn_ln<LN>(ring, L, sm, sm.xs, w, lane, nkh, nchunk);
+
+    bf16_t *const kst = &sm.gs[0][0];  // K: [key][feature], row stride kXLD
+    bf16_t *const vst = sm.xs;         // V^T: [feature][128 keys], swizzled chunks
+    {  // K^T = W_K^T X~^T
+      f32x16 acc[4];
+      zero16(acc);
+      const Src cur = src_proj(L, w, lane), nxt = src_proj(L, kD / 32 + w, lane);
+      run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bx[j] = ld8(sm.xs + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = mfma32(ring.v[slot][h], bx[j], acc[j]);
+        }
+      });
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int f = w * 32 + 8 * q + 4 * hi;
+          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
+          *reinterpret_cast<u32x2 *>(kst + (j * 32 + l32) * kXLD + f) = v;
+        }
+    }
+    {  // V = X~ W_V, keys as MFMA rows
+      f32x16 acc[4];
+      zero16(acc);
+      const bool more = tile + 1 < tend;  // then the next tile's first G blocks follow
+      const Src cur = src_proj(L, kD / 32 + w, lane), nxt = src_g(L, 0, w, lane);
+      run_phase<kD / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x8 bx[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bx[j] = ld8(sm.xs + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] = mfma32(bx[j], ring.v[slot][h], acc[j]);
+        }
+      });
+      __syncthreads();  // every wave has read X~: V^T goes over it
+      const int f = w * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = (j * 4 + q) ^ (f & 15);
+          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
+          *reinterpret_cast<u32x2 *>(vst + f * kR + chunk * 8 + 4 * hi) = v;
+        }
+    }
+    __syncthreads();  // the tile's K and V are staged
+    if (m_u == 0 || t0 >= m_u) continue;
+
+    const int Lu = P.hoff[u + 1] - P.hoff[u];
+    const int kbase = (tile * 4 - P.pblk[u]) * 32;  // user-local index of the tile's first key
+    const int kr0 = attn_key_row(lane);
+    f32x4 *const rec = reinterpret_cast<f32x4 *>(at.fstate) + ((int64_t)blockIdx.x * 8 + w) * REC * 64 + lane;
+    AttnState<DH, NT> st;
+    if (first) {
+      attn_reset(st);
+    } else {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) st.o[t][n] = rec[(t * NT + n) * 64];
+      const f32x4 m4 = rec[(DT * NT) * 64], l4 = rec[(DT * NT + 1) * 64], c4 = rec[(DT * NT + 2) * 64];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        st.mrun[n] = m4[n];
+        st.l[n] = f32x4{l4[n], l4[n], l4[n], l4[n]};
+        st.cnt[n] = __float_as_int(c4[n]);
+      }
+    }
+    attn_load_q(st, Q, at.d, head, tbase, t0, m_u, lane);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int nvalid = Lu - (kbase + blk * 32);
+      if (nvalid <= 0) break;
+      bf16x8 kf[2][KS], vf[DT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          kf[kt][k] = ld8(kst + (blk * 32 + kr0 + 4 * kt) * kXLD + head * DH + k * 32 + g16 * 8);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int f = head * DH + t * 16 + c16;
+        vf[t] = ld8(vst + f * kR + (((blk * 4 + g16) ^ (f & 15)) * 8));
+      }
+      attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, lane);
+    }
+    if (!last) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) rec[(t * NT + n) * 64] = st.o[t][n];
+      f32x4 m4 = {0.f, 0.f, 0.f, 0.f}, l4 = m4, c4 = m4;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        m4[n] = st.mrun[n];
+        l4[n] = st.l[n][0];
+        c4[n] = __int_as_float(st.cnt[n]);
+      }
+      rec[(DT * NT) * 64] = m4;
+      rec[(DT * NT + 1) * 64] = l4;
+      rec[(DT * NT + 2) * 64] = c4;
+      continue;
+    }
+    // the user's last tile in this range: write the partial
+    const int slot = (int)blockIdx.x + u;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      int cn = st.cnt[n];
+      cn += __shfl_xor(cn, 16);
+      cn += __shfl_xor(cn, 32);
+      const int tl = t0 + n * 16 + c16;
+      if (tl < m_u) {
+        const int64_t idx = partial_index(slot, H, head, at.tgs, tl);
+        if (g16 == 0) {
+          if (SCORE == 0) {
+            at.part_ml[idx * 2] = st.mrun[n];
+            at.part_ml[idx * 2 + 1] = st.l[n][0];
+          } else {
+            at.part_cnt[idx] = cn;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+          *reinterpret_cast<f32x4 *>(at.part_acc + idx * DH + t * 16 + 4 * g16) = st.o[t][n];
+      }
+    }
+  }
+}
+
+template <int DH, int NT, int SCORE>
+hipError_t launch_fused256_t(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s) {
+  auto k = a.ln ? fused256_kernel<DH, NT, SCORE, true> : fused256_kernel<DH, NT, SCORE, false>;
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  int64_t g = std::min<int64_t>(max_tiles, (int64_t)cus);
+  g = std::max<int64_t>(1, std::min<int64_t>(g, at.max_grid));
+  at.grid = (int)g;
+  hipLaunchKernelGGL(k, dim3(at.grid), dim3(kT), 0, s, a, at);
+  return hipGetLastError();
+}
 }  // namespace
+
+hipError_t launch_fused256(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s) {
+  at.grid = 0;
+  if (max_tiles <= 0 || (at.n_tgt <= 0 && !a.in_dump)) return hipSuccess;
+  if (a.d != kD || at.max_tgt > 64 || at.max_grid < 1 || a.hidden % kHC) return hipErrorInvalidValue;
+  const int mt = at.max_tgt;
+  if (at.dh == 32) {
+    const int nt = (mt + 15) / 16;
+    if (at.score) {
+      if (nt <= 1) return launch_fused256_t<32, 1, 1>(a, at, max_tiles, s);
+      if (nt <= 2) return launch_fused256_t<32, 2, 1>(a, at, max_tiles, s);
+      return launch_fused256_t<32, 4, 1>(a, at, max_tiles, s);
+    }
+    if (nt <= 1) return launch_fused256_t<32, 1, 0>(a, at, max_tiles, s);
+    if (nt <= 2) return launch_fused256_t<32, 2, 0>(a, at, max_tiles, s);
+    return launch_fused256_t<32, 4, 0>(a, at, max_tiles, s);
+  }
+  if (at.dh == 64) {  // each wave of a head's pair serves up to 32 targets
+    const int nt = (std::min(mt, 32) + 15) / 16;
+    if (at.score) {
+      if (nt <= 1) return launch_fused256_t<64, 1, 1>(a, at, max_tiles, s);
+      return launch_fused256_t<64, 2, 1>(a, at, max_tiles, s);
+    }
+    if (nt <= 1) return launch_fused256_t<64, 1, 0>(a, at, max_tiles, s);
+    return launch_fused256_t<64, 2, 0>(a, at, max_tiles, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t s) {
   if (a.n_rows <= 0 || hl.M <= 0) return hipSuccess;

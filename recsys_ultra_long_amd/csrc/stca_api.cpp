@@ -70,7 +70,8 @@ struct Layout {
   int nb = 1;              // blocks per chunk
   int64_t max_blocks = 0;  // host bound
   int64_t max_chunks = 0;
-  int64_t max_tiles = 0;   // fused: 64-key tiles (host bound)
+  int tile_blocks = 1;     // users padded to this many 32-key blocks (fused: its tile)
+  int64_t max_tiles = 0;   // fused: key tiles (host bound)
   int fused_grid = 0;      // fused: partial buffers hold this many workgroups
   size_t esize = 2;
   size_t prow = 0;         // staged bf16: padded-row id map (0 = none)
@@ -215,9 +216,10 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   L.esize = c->dtype == STCA_BF16 ? 2 : 4;
   L.fused = c->path == STCA_PATH_FUSED;
   L.nb = choose_nb(c->chunk_keys);
-  L.max_blocks = max_blocks(b->n_hist, c->B, L.fused ? 2 : 1);
+  L.tile_blocks = L.fused ? fused_tile_blocks(c->d) : 1;
+  L.max_blocks = max_blocks(b->n_hist, c->B, L.tile_blocks);
   L.max_chunks = max_chunks(b->n_hist, c->B, L.nb);
-  L.max_tiles = fused_max_tiles(b->n_hist, c->B);
+  L.max_tiles = fused_max_tiles(b->n_hist, c->B, L.fused ? L.tile_blocks : 2);
   L.fused_grid = (int)fused_grid_bound(L.max_tiles);
   Carver cv;
   L.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
@@ -372,8 +374,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (int i = 0; i < M; ++i) {
       const stca_layer &l = w->layers[i];
       const PrepLayer &p = L.pl[i];
-      // the d = 256 staged history encoder reads W1 / W3 as 16-row tiles
-      const int f13 = (d == 256 && !L.fused) ? 1 : 0;
+      // the d = 256 history encoders (staged and fused) read W1 / W3 as 16-row tiles
+      const int f13 = d == 256 ? 1 : 0;
       if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
       if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
       if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
@@ -403,7 +405,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   // ---- 2. planner
   if (B > 0) {
     e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, batch->n_hist, T,
-                    batch->max_tgt_per_user, L.nb, L.fused ? 2 : 1, plan, out->dev_status, s);
+                    batch->max_tgt_per_user, L.nb, L.tile_blocks, plan, out->dev_status, s);
     if (e) return hip_fail(e, "planner");
     if (plan.prow) {
       e = launch_padded_ids(plan, B, batch->hist_ids, cfg->table_rows, L.max_blocks, out->dev_status, s);
@@ -472,6 +474,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     at_.max_tgt = batch->max_tgt_per_user;
     attn_shape(at_, L.max_chunks);
     at_.fused = L.fused ? 1 : 0;
+    at_.tile_blocks = L.tile_blocks;
     at_.max_grid = L.fused_grid;
     at_.plan = plan;
     at_.q = q;
@@ -496,7 +499,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       if (out->x_dump && batch->n_hist > 0) {
         AttnArgs at_ = attn_args(0, nullptr);
         ChainArgs a = hist_args(0);
-        if ((e = launch_fused(a, at_, L.max_tiles, s))) return hip_fail(e, "fused encoding");
+        e = d == 256 ? launch_fused256(a, at_, L.max_tiles, s) : launch_fused(a, at_, L.max_tiles, s);
+        if (e) return hip_fail(e, "fused encoding");
       }
       return STCA_OK;
     }
@@ -606,7 +610,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       if (L.fused) {
         if (batch->n_hist > 0) {
           ChainArgs a = hist_args(i);
-          if ((e = launch_fused(a, at_, L.max_tiles, s))) return hip_fail(e, "fused encoding + attention");
+          e = d == 256 ? launch_fused256(a, at_, L.max_tiles, s) : launch_fused(a, at_, L.max_tiles, s);
+          if (e) return hip_fail(e, "fused encoding + attention");
         }
       } else {
         at_.kbuf = kbuf(i);

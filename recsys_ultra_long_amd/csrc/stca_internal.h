@@ -148,6 +148,7 @@ struct AttnArgs {
   int grid;                 // persistent workgroups (set by the partial launch)
   int max_grid;             // fused: bound on the grid the partial buffers hold
   int fused;                // partials come from the fused kernel (slot = workgroup + user)
+  int tile_blocks;          // fused: 32-key blocks per tile (2: d = 128, 4: d = 256)
   Plan plan;
   const void *kbuf, *vbuf;  // blocked K/V of one layer
   const void *q;            // [n_tgt, d] scaled queries
@@ -182,15 +183,25 @@ inline void attn_shape(AttnArgs &a, int64_t max_chunks) {
 // workgroup keeps its heads' state in fused_state_bytes / grid bytes of
 // at.fstate.  Sets at.grid.
 constexpr int kFusedMaxGrid = 512;
-inline size_t fused_state_bytes(int d, int dh, int64_t grid) {
-  const int heads_per_wave = (d / 4) / dh, rec = (dh / 16) * 4 + 3;  // f32x4 per lane, <= 64 targets
-  return (size_t)grid * 4 * heads_per_wave * rec * 64 * 16;
+// d = 256 runs 128-key tiles on 8 waves (launch_fused256), d = 128 64-key
+// tiles on 4 waves (launch_fused); users are padded to whole tiles.
+inline int fused_tile_blocks(int d) { return d == 256 ? 4 : 2; }
+inline int64_t fused_max_tiles(int64_t n_hist, int B, int tile_blocks) {
+  const int64_t keys = 32 * (int64_t)tile_blocks;
+  return (n_hist + keys - 1) / keys + B;
 }
-inline int64_t fused_max_tiles(int64_t n_hist, int B) { return (n_hist + 63) / 64 + B; }
 inline int64_t fused_grid_bound(int64_t max_tiles) {
   return max_tiles < kFusedMaxGrid ? max_tiles : kFusedMaxGrid;
 }
+// Per workgroup: every wave keeps one record of at most 11 f32x4 per lane per
+// head it serves (o for <= 64 targets, then m, l, count).
+inline size_t fused_state_bytes(int d, int dh, int64_t grid) {
+  const int waves = d == 256 ? 8 : 4;
+  const int heads_per_wave = d == 256 ? 1 : (d / 4) / dh;
+  return (size_t)grid * waves * heads_per_wave * 11 * 64 * 16;
+}
 hipError_t launch_fused(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s);
+hipError_t launch_fused256(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s);
 
 // Row-major K, V ([n_hist, d]) -> blocked K/V layout (for stca_attention) and
 // the reverse (for kv_dump).
