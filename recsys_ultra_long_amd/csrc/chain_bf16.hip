@@ -73,8 +73,8 @@ template <int NG>
 DEV void ring_load(Ring &r, int slot, const bf16_t *const (&p)[NG], int kb) {
 #pragma unroll
   for (int t = 0; t < NG; ++t) {
-    r.v[slot][t][0] = ld8(p[t] + kb * 1024);
-    r.v[slot][t][1] = ld8(p[t] + kb * 1024 + 512);
+    r.v[slot][t][0] = ldg8(p[t] + kb * 1024);
+    r.v[slot][t][1] = ldg8(p[t] + kb * 1024 + 512);
   }
 }
 
@@ -451,8 +451,8 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
           const int f = w * (D / 4) + (sp * YT + ti) * 32 + 8 * q + 4 * hi;
           f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
           if (LN) {
-            gg = *reinterpret_cast<const f32x4 *>(a.ln_g + f);
-            bb = *reinterpret_cast<const f32x4 *>(a.ln_b + f);
+            gg = ldg4(a.ln_g + f);
+            bb = ldg4(a.ln_b + f);
           }
 #pragma unroll
           for (int j = 0; j < TT; ++j) {

@@ -57,6 +57,16 @@ DEV int c32_row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 
 
 DEV bf16x8 ld8(const bf16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
+// Loads through pointers known to address global memory.  A pointer whose
+// origin the optimiser cannot see (for instance one passed through an empty
+// asm to keep address arithmetic inside a loop) otherwise becomes a flat
+// access, which also counts against the LDS wait counter: every wait for an
+// LDS operand would then drain the weight prefetches as well.
+typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
+typedef __attribute__((address_space(1))) const f32x4 gf32x4;
+DEV bf16x8 ldg8(const bf16_t *p) { return *(gbf16x8 *)p; }
+DEV f32x4 ldg4(const float *p) { return *(gf32x4 *)p; }
+
 // ---------------------------------------------------------------- misc
 DEV float wave_max(float v) {
 #pragma unroll

@@ -50,8 +50,8 @@ struct Ring {
   bf16x8 v[4][2];
 };
 DEV void ring_load(Ring &r, int slot, const Src &s, int kb) {
-  r.v[slot][0] = ld8(s.p0 + kb * s.stride);
-  r.v[slot][1] = ld8(s.p1 + kb * s.stride);
+  r.v[slot][0] = ldg8(s.p0 + kb * s.stride);
+  r.v[slot][1] = ldg8(s.p1 + kb * s.stride);
 }
 
 // Per-wave weight sources of each phase.  W1/W3 are packed for the 16x16x32
@@ -249,8 +249,8 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
     const int f = w * 32 + 8 * q + 4 * hi;
     f32x4 gg = {1.f, 1.f, 1.f, 1.f}, bb = {0.f, 0.f, 0.f, 0.f};
     if (LN) {
-      gg = *reinterpret_cast<const f32x4 *>(L.ln_g + f);
-      bb = *reinterpret_cast<const f32x4 *>(L.ln_b + f);
+      gg = ldg4(L.ln_g + f);
+      bb = ldg4(L.ln_b + f);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
