@@ -86,7 +86,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="rlb-long")
-    ap.add_argument("--path", default="staged", choices=["staged", "fused"])
+    ap.add_argument("--path", default="fused", choices=["staged", "fused"],
+                    help="fused (default, the faster complete path here) or staged")
+    ap.add_argument("--no-other-path", action="store_true",
+                    help="skip timing the other path for comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -247,6 +250,24 @@ def main():
     }
     for e in evs:
         e.close()
+    if not args.no_other_path:  # the same workload on the other path, same step count
+        other = "staged" if args.path == "fused" else "fused"
+        del f
+        dpo = stca.upload(p, path=other, table=dp.table)
+        fo = stca.Forward(dpo, want=(), dumps=())
+        for _ in range(args.warmup):
+            fo()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            fo()
+        end.record()
+        torch.cuda.synchronize()
+        mso = start.elapsed_time(end) / args.steps
+        res["other_path"] = {"path": other, "ms_per_step": round(mso, 4),
+                             "value": round(n_hist * M / (mso * 1e-3), 1)}
+        log(f"other path ({other}): {mso:.3f} ms/step")
+        del fo, dpo
     if not args.no_cpu_baseline:
         log(f"timing the float64 oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
