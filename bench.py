@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--workload", default="rlb-long")
     ap.add_argument("--path", default="fused", choices=["staged", "fused"],
                     help="fused (default, the faster complete path here) or staged")
+    ap.add_argument("--dedup", action="store_true",
+                    help="staged path with unique-id dedup of the history encoding "
+                         "(bit-identical results; valid because a row's encoding depends on its id alone)")
     ap.add_argument("--no-other-path", action="store_true",
                     help="skip timing the other path for comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -120,12 +123,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     stca.load()
+    if args.dedup:
+        args.path = "staged"
     sp = workload(args.workload)
     t = time.time()
     p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
     log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} "
         f"n_tgt={p.n_tgt} table={sp.table_rows}x{sp.d} {sp.dtype}")
-    dp = stca.upload(p, path=args.path)
+    dp = stca.upload(p, path=args.path, dedup=args.dedup)
+    n_unique = int(len(np.unique(p.hist_ids))) if args.dedup else None
     torch.cuda.synchronize()
     log("uploaded")
     M = sp.M
@@ -168,7 +174,8 @@ def main():
 
     d, h, H = sp.d, sp.hidden, sp.H
     n_hist, T = p.n_hist, p.n_tgt
-    flops_hist = n_hist * (6 * d * h + 4 * d * d)            # per layer launch
+    enc_rows = n_unique if args.dedup else n_hist              # rows the encoder processes
+    flops_hist = enc_rows * (6 * d * h + 4 * d * d)           # per layer
     # attention flops: 4 d per (history token, target of the same user) pair
     pairs = int(np.sum(np.diff(p.hist_offsets).astype(np.int64) * np.diff(p.tgt_offsets)))
     flops_attn = 4 * d * pairs
@@ -186,8 +193,8 @@ def main():
                  "achieved": round(hist_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(hist_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                  "launch_ms": round(t_hist * hist_layers_per_launch * 1e3, 4),
-                 "per_launch": f"{n_hist} tokens x {hist_layers_per_launch} layer(s) x "
-                               f"{6 * d * h + 4 * d * d} flop"}
+                 "per_launch": f"{enc_rows} {'unique rows' if args.dedup else 'tokens'} x "
+                               f"{hist_layers_per_launch} layer(s) x {6 * d * h + 4 * d * d} flop"}
     roof_attn = {"kernel": "m-target cross attention (split-L partials)", "bound": "hbm",
                  "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
@@ -233,7 +240,8 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{sp.name}: B={sp.B} users, L={sp.L}, m={sp.m} targets/user (RLB), "
                                f"table {sp.table_rows}x{d} bf16 Zipf({sp.zipf_s}) ids, d={d}, H={H}, "
-                               f"hidden={h}, M={M} layers, softmax, path={args.path}",
+                               f"hidden={h}, M={M} layers, softmax, path={args.path}"
+                               + (f", unique-id dedup ({n_unique} unique of {n_hist})" if args.dedup else ""),
                    "global_batch": sp.B, "seq_len": sp.L, "targets": T, "parallelism": "single GPU"},
         "target_scores_per_s_per_layer": round(T * M / (ms * 1e-3), 1),
         "target_scores_per_s": round(T / (ms * 1e-3), 1),
@@ -250,7 +258,7 @@ def main():
     }
     for e in evs:
         e.close()
-    if not args.no_other_path:  # the same workload on the other path, same step count
+    if not args.no_other_path and not args.dedup:  # the other path on the same inputs
         other = "staged" if args.path == "fused" else "fused"
         del f
         dpo = stca.upload(p, path=other, table=dp.table)

@@ -67,7 +67,11 @@ enum { STCA_Q_FUSION = 0, STCA_Q_LINEAR = 1 };         /* stca_config.qmode  */
 enum { STCA_PATH_STAGED = 0, STCA_PATH_FUSED = 1 };    /* stca_config.path   */
 enum {                                                 /* stca_config.flags  */
   STCA_FLAG_KV_LN = 1,  /* LN after the history FFN (STCA); clear for HyFormer eq. (7) */
-  STCA_FLAG_Z_LN = 2    /* LN on the final z ([Notes] wording); default is [Review]'s z */
+  STCA_FLAG_Z_LN = 2,   /* LN on the final z ([Notes] wording); default is [Review]'s z */
+  STCA_FLAG_DEDUP = 4   /* encode each distinct history id of the batch once and copy its
+                           K/V to every token carrying it (a row's encoding depends on its
+                           id alone, [Notes] §STCA); results are bit-identical to the plain
+                           path.  bf16, staged path only; not with x_dump. */
 };
 enum {                                                 /* dev_status bits     */
   STCA_DEV_BAD_HIST_OFFSETS = 1,  /* hist_offsets not monotone / not ending at n_hist: all users empty */

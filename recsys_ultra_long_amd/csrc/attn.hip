@@ -63,14 +63,22 @@ DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
 // layout is exactly the B-operand layout P^T needs: lane l (g = l/16) holds the
 // scores of keys 8g..8g+7 for target l%16.  The four waves of a workgroup take
 // alternate blocks of a pair's range and merge in LDS when the pair ends.
-template <int DH, int NT, int SCORE>
+//
+// IND (unique-id dedup): K/V are not per token but per distinct history id;
+// a token's row is found through a.tok2u.  K rows are read from the unique
+// rows' blocked K (16 bytes per lane, as above); the V rows of a block are
+// read row-major (a.vrows) and written transposed into a wave-private LDS
+// tile, from which the V^T fragments are read.
+template <int DH, int NT, int SCORE, bool IND>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
   constexpr int DT = DH / 16;  // feature tiles of the output
   constexpr int TG = NT * 16;  // targets per group
+  constexpr int LDT = 32 + 8;  // row stride of the transposed V tile
   __shared__ float sm_m[4][TG], sm_l[4][TG];
   __shared__ int sm_c[4][TG];
   __shared__ float sm_o[4][TG][DH + 1];
+  __shared__ __attribute__((aligned(16))) bf16_t sm_vt[IND ? 4 : 1][IND ? DH * LDT : 8];
 
   const Plan P = a.plan;
   const int H = a.H, G = a.groups, HG = H * G;
@@ -102,27 +110,99 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       attn_reset(st);
       attn_load_q(st, Q, a.d, h, tbase, t0, m_u, lane);
       bf16x8 kf[2][KS], vf[DT];
+      // IND: the V rows of a block come as DT 16-byte chunks per lane: chunk
+      // lane + 64 i = (key, part) with DH / 8 parts of 8 features per key
+      constexpr int PARTS = DH / 8;
+      const int64_t tok0 = (int64_t)P.hoff[u] - (int64_t)P.pblk[u] * 32;  // token of padded row 0
+      auto uid_of = [&](int b, int key) -> int {  // unique row of key `key` of block b (-1: padding)
+        const int j = (b - P.pblk[u]) * 32 + key;
+        return j < L ? a.tok2u[tok0 + (int64_t)b * 32 + key] : -1;
+      };
+      // IND: the unique rows of this lane's keys in a block (K: 2, V: DT),
+      // looked up one pipeline stage before the rows themselves are loaded
+      struct Uids {
+        int k[2], v[DT];
+      };
+      auto load_uids = [&](int b, Uids &U) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) U.k[kt] = uid_of(b, kr0 + 4 * kt);
+#pragma unroll
+        for (int i = 0; i < DT; ++i) U.v[i] = uid_of(b, (lane + 64 * i) / PARTS);
+      };
+      Uids U8;  // uids of the block two ahead of the one in use
       auto load_kv = [&](int b, bf16x8 (&kk)[2][KS], bf16x8 (&vv)[DT]) {
-        const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
-        const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
+        if constexpr (IND) {
+          const bf16_t *Vr = (const bf16_t *)a.vrows;
+          Uids U;
+          if (b < b0 + w + 8) load_uids(b, U);  // pipeline start
+          else U = U8;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt) {
+            const int ui = U.k[kt];
 #pragma unroll
-          for (int k = 0; k < KS; ++k) kk[kt][k] = ld8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+            for (int k = 0; k < KS; ++k) {
+              bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+              kk[kt][k] = ui < 0 ? z
+                                 : ld8(Kb + ((((int64_t)(ui >> 5)) * H + h) * 32 + (ui & 31)) * DH + k * 32 + g16 * 8);
+            }
+          }
 #pragma unroll
-        for (int t = 0; t < DT; ++t) vv[t] = ld8(vb + (t * 16 + c16) * 32 + g16 * 8);
+          for (int i = 0; i < DT; ++i) {
+            const int part = (lane + 64 * i) % PARTS;
+            const int ui = U.v[i];
+            bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+            vv[i] = ui < 0 ? z : ld8(Vr + (int64_t)ui * a.d + h * DH + part * 8);
+          }
+        } else {
+          const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
+          const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int k = 0; k < KS; ++k) kk[kt][k] = ld8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) vv[t] = ld8(vb + (t * 16 + c16) * 32 + g16 * 8);
+        }
+      };
+      // IND: V row chunks -> transposed wave-private tile -> V^T fragments
+      auto v_fragments = [&](const bf16x8 (&raw)[DT], bf16x8 (&out)[DT]) {
+        if constexpr (IND) {
+          bf16_t *vt = sm_vt[w];
+#pragma unroll
+          for (int i = 0; i < DT; ++i) {
+            const int c = lane + 64 * i, key = c / PARTS, part = c % PARTS;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vt[(part * 8 + e) * LDT + key] = (bf16_t)raw[i][e];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int t = 0; t < DT; ++t) out[t] = ld8(vt + (t * 16 + c16) * LDT + g16 * 8);
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+        } else {
+#pragma unroll
+          for (int t = 0; t < DT; ++t) out[t] = raw[t];
+        }
       };
       // two blocks of this wave in flight ahead of the one being used: the
       // loads, not the arithmetic, set the pace once the block step is lean
       bf16x8 k1[2][KS], v1[DT];
       if (b0 + w < b1) load_kv(b0 + w, kf, vf);
       if (b0 + w + 4 < b1) load_kv(b0 + w + 4, k1, v1);
+      if (IND && b0 + w + 8 < b1) load_uids(b0 + w + 8, U8);
       for (int b = b0 + w; b < b1; b += 4) {
         bf16x8 k2[2][KS], v2[DT];
+        Uids U12;
+        // uids first: waiting for them later does not wait for the rows below
+        if (IND && b + 12 < b1) load_uids(b + 12, U12);
         if (b + 8 < b1) load_kv(b + 8, k2, v2);
+        if (IND) U8 = U12;
         __builtin_amdgcn_sched_barrier(0);
         // keys of this lane: 8g + 4kt + r; valid while below the user's length
-        attn_block<DH, NT, SCORE>(st, kf, vf, L - (b - P.pblk[u]) * 32, lane);
+        bf16x8 vuse[DT];
+        v_fragments(vf, vuse);
+        attn_block<DH, NT, SCORE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, lane);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -387,13 +467,13 @@ int persistent_grid(K kernel, int threads, int64_t units) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * per_cu));
 }
 
-template <int DH, int SCORE>
+template <int DH, int SCORE, bool IND>
 hipError_t launch_bf16(AttnArgs &a, hipStream_t s) {
   const int nt = a.groups > 1 ? 4 : (a.max_tgt + 15) / 16;
   const dim3 block(256);
 #define GO(NT)                                                                         \
   {                                                                                    \
-    auto k = attn_bf16_kernel<DH, NT, SCORE>;                                          \
+    auto k = attn_bf16_kernel<DH, NT, SCORE, IND>;                                     \
     a.grid = persistent_grid(k, 256, a.max_units);                                     \
     hipLaunchKernelGGL(k, dim3(a.grid), block, 0, s, a);                               \
   }
@@ -408,8 +488,13 @@ hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
   a.grid = 0;
   if (a.max_units <= 0 || a.n_tgt <= 0) return hipSuccess;
   if (a.dtype == 1) {
-    if (a.dh == 32) return a.score ? launch_bf16<32, 1>(a, s) : launch_bf16<32, 0>(a, s);
-    if (a.dh == 64) return a.score ? launch_bf16<64, 1>(a, s) : launch_bf16<64, 0>(a, s);
+    if (a.tok2u) {
+      if (a.dh == 32) return a.score ? launch_bf16<32, 1, true>(a, s) : launch_bf16<32, 0, true>(a, s);
+      if (a.dh == 64) return a.score ? launch_bf16<64, 1, true>(a, s) : launch_bf16<64, 0, true>(a, s);
+      return hipErrorInvalidValue;
+    }
+    if (a.dh == 32) return a.score ? launch_bf16<32, 1, false>(a, s) : launch_bf16<32, 0, false>(a, s);
+    if (a.dh == 64) return a.score ? launch_bf16<64, 1, false>(a, s) : launch_bf16<64, 0, false>(a, s);
     return hipErrorInvalidValue;
   }
 #define GO(DH, SC)                                                   \

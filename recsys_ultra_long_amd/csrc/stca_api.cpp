@@ -75,6 +75,10 @@ struct Layout {
   int fused_grid = 0;      // fused: partial buffers hold this many workgroups
   size_t esize = 2;
   size_t prow = 0;         // staged bf16: padded-row id map (0 = none)
+  bool dedup = false;      // STCA_FLAG_DEDUP: encoder over the unique ids
+  int64_t drows = 0, dslots = 0;
+  size_t d_keys = 0, d_slot = 0, d_bcnt = 0, d_boff = 0, d_uniq = 0, d_tok2u = 0, d_small = 0;
+  size_t ukv = 0, ukv_layer = 0, vrows = 0;
   size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0, fstate = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
   std::vector<PrepLayer> pl;
@@ -110,7 +114,7 @@ int validate_cfg(const stca_config *c) {
     return fail(STCA_ERR_INVALID_ARG, "qmode %d unknown", c->qmode);
   if (c->path != STCA_PATH_STAGED && c->path != STCA_PATH_FUSED)
     return fail(STCA_ERR_INVALID_ARG, "path %d unknown", c->path);
-  if (c->flags & ~(STCA_FLAG_KV_LN | STCA_FLAG_Z_LN))
+  if (c->flags & ~(STCA_FLAG_KV_LN | STCA_FLAG_Z_LN | STCA_FLAG_DEDUP))
     return fail(STCA_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
   if (c->chunk_keys < 0 || c->chunk_keys % 32)
     return fail(STCA_ERR_INVALID_ARG, "chunk_keys %d must be a multiple of 32", c->chunk_keys);
@@ -131,6 +135,13 @@ int validate_cfg(const stca_config *c) {
 }
 
 // What the fused kernel is built for.
+int validate_dedup(const stca_config *c) {
+  if (!(c->flags & STCA_FLAG_DEDUP)) return STCA_OK;
+  if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "STCA_FLAG_DEDUP is bf16 only");
+  if (c->path != STCA_PATH_STAGED) return fail(STCA_ERR_UNSUPPORTED, "STCA_FLAG_DEDUP needs the staged path");
+  return STCA_OK;
+}
+
 int validate_fused(const stca_config *c, const stca_batch *b) {
   if (c->path != STCA_PATH_FUSED) return STCA_OK;
   const int dh = c->d / c->H;
@@ -167,6 +178,8 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
   const void *ptrs[] = {b->hist_offsets, b->hist_ids, b->tgt_offsets, b->tgt_ids, b->q0, b->table};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
+  int r = validate_dedup(c);
+  if (r) return r;
   return validate_fused(c, b);
 }
 
@@ -223,8 +236,23 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   L.fused_grid = (int)fused_grid_bound(L.max_tiles);
   Carver cv;
   L.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
-  if (c->dtype == STCA_BF16 && !L.fused && b->n_hist > 0)
+  L.dedup = (c->flags & STCA_FLAG_DEDUP) && b->n_hist > 0;
+  if (c->dtype == STCA_BF16 && !L.fused && b->n_hist > 0 && !L.dedup)
     L.prow = cv.take(sizeof(int) * (size_t)prow_rows(L.max_blocks));
+  if (L.dedup) {
+    L.drows = dedup_rows(b->n_hist);
+    L.dslots = dedup_slots(b->n_hist);
+    L.d_keys = cv.take(sizeof(int) * (size_t)L.dslots);
+    L.d_slot = cv.take(sizeof(int) * (size_t)L.dslots);
+    L.d_bcnt = cv.take(sizeof(int) * (size_t)(L.dslots / 256));
+    L.d_boff = cv.take(sizeof(int) * (size_t)(L.dslots / 256));
+    L.d_uniq = cv.take(sizeof(int) * (size_t)L.drows);
+    L.d_tok2u = cv.take(sizeof(int) * (size_t)b->n_hist);
+    L.d_small = cv.take(sizeof(int) * 8);
+    L.ukv_layer = (size_t)L.drows * d * 2;  // K or V of the unique rows, one layer
+    L.ukv = cv.take(2 * L.ukv_layer * c->M);
+    L.vrows = cv.take(L.ukv_layer * c->M);  // each layer's unique V, row-major
+  }
   if (c->dtype == STCA_BF16) {
     size_t e = 0;
     L.pl.resize(c->M);
@@ -323,6 +351,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (const void *p : p16)
       if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "output pointer %p not 16-byte aligned", p);
   }
+  if ((cfg->flags & STCA_FLAG_DEDUP) && out->x_dump)
+    return fail(STCA_ERR_UNSUPPORTED, "x_dump is not available with STCA_FLAG_DEDUP (the encoder gathers unique rows)");
   if (cfg->path == STCA_PATH_FUSED && out->kv_dump)
     return fail(STCA_ERR_UNSUPPORTED, "kv_dump needs the staged path (the fused path keeps no K/V)");
   const Layout L = make_layout(cfg, batch);
@@ -510,10 +540,77 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   char *kvbase = at<char>(ws, L.kv);
   auto kbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i) * L.kv_layer); };
   auto vbuf = [&](int i) { return (void *)(kvbase + (size_t)(2 * i + 1) * L.kv_layer); };
+  // STCA_FLAG_DEDUP: the encoder runs over the batch's distinct ids (a
+  // one-user plan whose padded rows are those ids); each layer's token K/V is
+  // then expanded from the unique rows
+  Plan uplan = plan;
+  int *n_unique = nullptr, *tok2u = nullptr;
+  char *ukvbase = L.dedup ? at<char>(ws, L.ukv) : nullptr;
+  auto ukbuf = [&](int i) { return (void *)(ukvbase + (size_t)(2 * i) * L.ukv_layer); };
+  auto uvbuf = [&](int i) { return (void *)(ukvbase + (size_t)(2 * i + 1) * L.ukv_layer); };
+  if (L.dedup) {
+    int *small = at<int>(ws, L.d_small);
+    DedupArgs da;
+    std::memset(&da, 0, sizeof(da));
+    da.ids = batch->hist_ids;
+    da.n_hist = batch->n_hist;
+    da.table_rows = cfg->table_rows;
+    da.keys = at<int>(ws, L.d_keys);
+    da.slot_uid = at<int>(ws, L.d_slot);
+    da.mask = (uint32_t)(L.dslots - 1);
+    da.block_cnt = at<int>(ws, L.d_bcnt);
+    da.block_off = at<int>(ws, L.d_boff);
+    da.uniq_rows = at<int>(ws, L.d_uniq);
+    da.tok2u = at<int>(ws, L.d_tok2u);
+    da.n_unique = small;
+    da.uplan_hoff = small + 1;
+    da.uplan_toff = small + 3;
+    da.uplan_pblk = small + 5;
+    da.status = out->dev_status;
+    if ((e = launch_dedup(da, s))) return hip_fail(e, "id dedup");
+    uplan.hoff = da.uplan_hoff;
+    uplan.toff = da.uplan_toff;
+    uplan.pblk = da.uplan_pblk;
+    uplan.coff = da.uplan_toff;
+    uplan.prow = da.uniq_rows;
+    n_unique = da.n_unique;
+    tok2u = da.tok2u;
+  }
+  // the encoder's view of the rows: the batch, or the unique ids
+  auto enc_args = [&](int i) {
+    ChainArgs a = hist_args(i);
+    if (L.dedup) {
+      a.plan = uplan;
+      a.B = 1;
+      a.n_rows = L.drows;
+      a.in_dump = nullptr;
+    }
+    return a;
+  };
+  auto enc_k = [&](int i) { return L.dedup ? ukbuf(i) : kbuf(i); };
+  auto enc_v = [&](int i) { return L.dedup ? uvbuf(i) : vbuf(i); };
+  auto vrows = [&](int i) { return at<bf16_t>(ws, L.vrows) + (size_t)i * L.drows * d; };
+  auto finish_layer = [&](int i) -> hipError_t {  // dedup V rows, K/V dump, stage event
+    hipError_t er = hipSuccess;
+    if (L.dedup) {
+      er = launch_vrows((const bf16_t *)uvbuf(i), vrows(i), n_unique, L.drows, d, H, s);
+      if (!er && out->kv_dump)  // the dump is per token: expand the unique rows
+        er = launch_expand_kv((const bf16_t *)ukbuf(i), vrows(i), (bf16_t *)kbuf(i), (bf16_t *)vbuf(i), tok2u,
+                              plan, B, L.max_blocks, d, H, s);
+    }
+    if (!er && out->kv_dump) {
+      char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;
+      char *vd = kd + (size_t)batch->n_hist * d * es;
+      er = launch_kv_relayout(cfg->dtype, kd, vd, kbuf(i), vbuf(i), plan, B, L.max_blocks, d, H, false, s);
+    }
+    if (!er) er = rec(2 + i);
+    return er;
+  };
+
   // bf16, d <= 256: all layers in one launch that gathers each tile once
   const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers;
   if (multi) {
-    ChainArgs a = hist_args(0);
+    ChainArgs a = enc_args(0);
     HistLayers hl;
     std::memset(&hl, 0, sizeof(hl));
     hl.M = M;
@@ -525,33 +622,20 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
       hl.wp[i] = prep + p.wkv;
       hl.ln_g[i] = w->layers[i].kv.ln_g;
       hl.ln_b[i] = w->layers[i].kv.ln_b;
-      hl.kbuf[i] = kbuf(i);
-      hl.vbuf[i] = vbuf(i);
+      hl.kbuf[i] = enc_k(i);
+      hl.vbuf[i] = enc_v(i);
     }
     e = d == 256 ? launch_hist256(a, hl, s) : launch_hist_layers(a, hl, s);
     if (e) return hip_fail(e, "history encoding");
-    for (int i = 0; i < M; ++i) {
-      if (out->kv_dump) {
-        char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;
-        char *vd = kd + (size_t)batch->n_hist * d * es;
-        e = launch_kv_relayout(cfg->dtype, kd, vd, kbuf(i), vbuf(i), plan, B, L.max_blocks, d, H, false, s);
-        if (e) return hip_fail(e, "kv dump");
-      }
-      if ((e = rec(2 + i))) return hip_fail(e, "stage event");
-    }
+    for (int i = 0; i < M; ++i)
+      if ((e = finish_layer(i))) return hip_fail(e, "history K/V");
   }
   for (int i = 0; i < M && batch->n_hist > 0 && !L.fused && !multi; ++i) {
-    ChainArgs a = hist_args(i);
-    a.kbuf = kbuf(i);
-    a.vbuf = vbuf(i);
+    ChainArgs a = enc_args(i);
+    a.kbuf = enc_k(i);
+    a.vbuf = enc_v(i);
     if ((e = chain(a))) return hip_fail(e, "history encoding");
-    if (out->kv_dump) {
-      char *kd = (char *)out->kv_dump + (size_t)i * 2 * batch->n_hist * d * es;
-      char *vd = kd + (size_t)batch->n_hist * d * es;
-      e = launch_kv_relayout(cfg->dtype, kd, vd, kbuf(i), vbuf(i), plan, B, L.max_blocks, d, H, false, s);
-      if (e) return hip_fail(e, "kv dump");
-    }
-    if ((e = rec(2 + i))) return hip_fail(e, "stage event");
+    if ((e = finish_layer(i))) return hip_fail(e, "history K/V");
   }
   if (T == 0) return STCA_OK;
 
@@ -614,8 +698,12 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
           if (e) return hip_fail(e, "fused encoding + attention");
         }
       } else {
-        at_.kbuf = kbuf(i);
+        at_.kbuf = L.dedup ? ukbuf(i) : kbuf(i);
         at_.vbuf = vbuf(i);
+        if (L.dedup) {  // K/V through the token -> unique row map
+          at_.tok2u = tok2u;
+          at_.vrows = vrows(i);
+        }
         if ((e = launch_attn_partial(at_, s))) return hip_fail(e, "attention");
       }
       if ((e = rec(3 + M + 4 * i))) return hip_fail(e, "stage event");

@@ -157,6 +157,8 @@ struct AttnArgs {
   float *part_acc;          // [units, tgs, dh]
   int *part_cnt;            // [units, tgs]
   float *fstate;            // fused: per-workgroup attention state between tiles
+  const int *tok2u;         // dedup: token -> unique row (kbuf = unique rows' blocked K)
+  const void *vrows;        // dedup: unique rows' V, row-major [rows][d]
   float *attn;              // [n_tgt, d] fp32 (required)
   void *attn_lo;            // [n_tgt, d] config dtype copy (optional)
   int *active;              // [n_tgt, H] (optional)
@@ -202,6 +204,37 @@ inline size_t fused_state_bytes(int d, int dh, int64_t grid) {
 }
 hipError_t launch_fused(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s);
 hipError_t launch_fused256(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, hipStream_t s);
+
+// ------------------------------------------------------------ id dedup
+// Unique-id deduplication of the history encoding (dedup.hip).  The encoder
+// then runs on a one-user plan over the unique ids (uplan_*, prow =
+// uniq_rows, padded with -1 to whole 128-row tiles), and each layer's K/V of
+// the tokens is expanded from the unique rows.
+struct DedupArgs {
+  const int *ids;
+  int64_t n_hist, table_rows;
+  int *keys, *slot_uid;      // hash set: [mask + 1] slots
+  uint32_t mask;
+  int *block_cnt, *block_off;  // [(mask + 1) / 256]
+  int *uniq_rows;            // [dedup_rows(n_hist)]
+  int *tok2u;                // [n_hist]
+  int *n_unique;             // [1]
+  int *uplan_hoff, *uplan_toff, *uplan_pblk;  // [2] each
+  int *status;
+};
+inline int64_t dedup_rows(int64_t n_hist) { return ((n_hist + 127) / 128 + 1) * 128; }
+inline int64_t dedup_slots(int64_t n_hist) {
+  int64_t s = 256;
+  while (s < 2 * n_hist) s <<= 1;
+  return s;
+}
+hipError_t launch_dedup(DedupArgs &d, hipStream_t s);
+// The unique rows' V (blocked, transposed per 32 rows) -> row-major [rows][d].
+hipError_t launch_vrows(const bf16_t *uv, bf16_t *vrows, const int *n_unique, int64_t max_unique, int d, int H,
+                        hipStream_t s);
+// Token K/V (blocked, per the batch plan) from the unique rows (for K/V dumps).
+hipError_t launch_expand_kv(const bf16_t *uk, const bf16_t *vrows, bf16_t *k, bf16_t *v, const int *tok2u,
+                            const Plan &plan, int B, int64_t max_blocks, int d, int H, hipStream_t s);
 
 // Row-major K, V ([n_hist, d]) -> blocked K/V layout (for stca_attention) and
 // the reverse (for kv_dump).

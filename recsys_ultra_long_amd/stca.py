@@ -22,7 +22,7 @@ F32, BF16 = 0, 1
 SCORE = {"softmax": 0, "relu": 1}
 QMODE = {"fusion": 0, "linear": 1}
 PATH = {"staged": 0, "fused": 1}
-FLAG_KV_LN, FLAG_Z_LN = 1, 2
+FLAG_KV_LN, FLAG_Z_LN, FLAG_DEDUP = 1, 2, 4
 DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
@@ -152,12 +152,12 @@ def _dev(a, device):
     return torch.from_numpy(a).to(device)
 
 
-def upload(p, device="cuda", table=None, path="staged", chunk_keys=0) -> DeviceProblem:
+def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=False) -> DeviceProblem:
     """Copy an ``inputs.Problem`` to the device.  ``table`` may be a device
     tensor already holding the embedding table (avoids a second copy)."""
     import torch
     sp = p.spec
-    flags = (FLAG_KV_LN if sp.kv_ln else 0) | (FLAG_Z_LN if sp.z_ln else 0)
+    flags = (FLAG_KV_LN if sp.kv_ln else 0) | (FLAG_Z_LN if sp.z_ln else 0) | (FLAG_DEDUP if dedup else 0)
     cfg = Config(B=sp.B, d=sp.d, H=sp.H, hidden=sp.hidden, M=sp.M, table_rows=sp.table_rows,
                  dtype=BF16 if sp.dtype == "bf16" else F32, score=SCORE[sp.score],
                  qmode=QMODE[sp.qmode], path=PATH[path], flags=flags, chunk_keys=chunk_keys)

@@ -22,10 +22,10 @@ def row_rel_err(g: np.ndarray, o: np.ndarray) -> float:
     return float((num / den).max())
 
 
-def gpu_run(p, path="staged", chunk_keys=0, dumps=(), table=None):
+def gpu_run(p, path="staged", chunk_keys=0, dumps=(), table=None, dedup=False):
     import torch
     from recsys_ultra_long_amd import stca
-    dp = stca.upload(p, table=table, path=path, chunk_keys=chunk_keys)
+    dp = stca.upload(p, table=table, path=path, chunk_keys=chunk_keys, dedup=dedup)
     f = stca.Forward(dp, want=("o", "attn", "active"), dumps=dumps)
     f()
     torch.cuda.synchronize()

@@ -193,3 +193,26 @@ def test_fused_rejects_kv_dump():
     out = stca.Outputs(z=FAKE, kv_dump=FAKE)
     assert _forward(c, b, w, out, need) == stca.ERR_UNSUPPORTED
     assert "staged" in stca.last_error()
+
+
+# ------------------------------------------------------------------ id dedup
+@pytest.mark.parametrize("over,code", [
+    (dict(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP), stca.OK),
+    (dict(flags=stca.FLAG_DEDUP), stca.OK),                                   # HyFormer-style, no LN
+    (dict(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP, path=1), stca.ERR_UNSUPPORTED),
+    (dict(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP, dtype=stca.F32), stca.ERR_UNSUPPORTED),
+])
+def test_dedup_validation(over, code):
+    r, _ = ws_size(cfg(**over), batch())
+    assert r == code, stca.last_error()
+
+
+def test_dedup_workspace_and_x_dump():
+    b = batch(n_hist=100_000, n_tgt=64, max_tgt_per_user=32)
+    _, plain = ws_size(cfg(), b)
+    _, dd = ws_size(cfg(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP), b)
+    assert dd > plain          # hash set, maps and the unique rows' K/V
+    c = cfg(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP)
+    w, keep = _weights()
+    out = stca.Outputs(z=FAKE, x_dump=FAKE)
+    assert _forward(c, b, w, out, dd) == stca.ERR_UNSUPPORTED

@@ -1,0 +1,80 @@
+"""Unique-id dedup of the history encoding (STCA_FLAG_DEDUP): each distinct
+history id of the batch is encoded once and its K/V copied to every token
+carrying it.  A row's K/V depends on its id alone and the encoder's per-row
+arithmetic does not depend on which rows share its tile, so the whole forward
+must equal the plain staged path bit for bit -- every output and dump."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from recsys_ultra_long_amd import inputs as I
+
+from parity_util import gpu_run
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU visible")]
+
+
+def _small(k, **over):
+    base = {
+        2: dict(B=4, L=300, table_rows=5000),
+        3: dict(B=2, L=700, m=64, table_rows=20000),
+        4: dict(B=6, L_max=1200, table_rows=20000),
+    }[k]
+    base.update(over)
+    return I.spec(k, **base)
+
+
+def _same(p, dumps=("q", "kv")):
+    g0 = gpu_run(p, dumps=dumps)
+    g1 = gpu_run(p, dumps=dumps, dedup=True)
+    n_u = len(np.unique(p.hist_ids))
+    print(f"[dedup] {p.spec.name} n_hist={p.n_hist} unique={n_u} ({n_u / max(1, p.n_hist):.1%})", flush=True)
+    for key in ("z", "o", "attn", "active", "status") + tuple(dumps):
+        a, b = g0.get(key), g1.get(key)
+        if a is None:  # not produced for this configuration (e.g. counts of softmax runs)
+            assert b is None, key
+            continue
+        assert a.shape == b.shape, key
+        assert np.array_equal(a, b), key
+    return g0, g1
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_dedup_bitwise_equal(k):
+    _same(I.make_problem(_small(k)))
+
+
+def test_dedup_relu_bitwise_equal():
+    _same(I.make_problem(_small(4, score="relu")))
+
+
+def test_dedup_hyformer_d512_bitwise_equal():
+    sp = I.spec(5)["feed"]
+    _same(I.make_problem(replace(sp, B=3, L=400, table_rows=3000)))
+
+
+def test_dedup_out_of_range_ids_and_empty_users():
+    from recsys_ultra_long_amd import stca
+    p = I.make_problem(_small(2, B=3, L=64))
+    p.hist_offsets = np.array([0, 0, 64, 64], np.int32)
+    p.hist_ids = p.hist_ids[:64].copy()
+    p.hist_ids[5] = p.spec.table_rows + 9
+    p.hist_ids[9] = -3
+    g0, g1 = _same(p)
+    assert int(g1["status"][0]) & stca.DEV_BAD_ID
+
+
+def test_dedup_all_ids_equal():
+    p = I.make_problem(_small(3, B=2, L=300))
+    p.hist_ids[:] = 17
+    _same(p)
+
+
+def test_dedup_fullsize_rlb_long():
+    p = I.make_problem(I.spec(3), threads=16)
+    _same(p, dumps=())
