@@ -258,24 +258,31 @@ def main():
     }
     for e in evs:
         e.close()
-    if not args.no_other_path and not args.dedup:  # the other path on the same inputs
-        other = "staged" if args.path == "fused" else "fused"
+    if not args.no_other_path and not args.dedup:
+        # the same inputs through the other path, and through the staged path
+        # with unique-id dedup (bit-identical outputs, valid because a history
+        # row here depends on its id alone)
         del f
-        dpo = stca.upload(p, path=other, table=dp.table)
-        fo = stca.Forward(dpo, want=(), dumps=())
-        for _ in range(args.warmup):
-            fo()
-        torch.cuda.synchronize()
-        start.record()
-        for _ in range(args.steps):
-            fo()
-        end.record()
-        torch.cuda.synchronize()
-        mso = start.elapsed_time(end) / args.steps
-        res["other_path"] = {"path": other, "ms_per_step": round(mso, 4),
-                             "value": round(n_hist * M / (mso * 1e-3), 1)}
-        log(f"other path ({other}): {mso:.3f} ms/step")
-        del fo, dpo
+        others = [("staged" if args.path == "fused" else "fused", False), ("staged", True)]
+        res["other_paths"] = []
+        for other, dd in others:
+            dpo = stca.upload(p, path=other, table=dp.table, dedup=dd)
+            fo = stca.Forward(dpo, want=(), dumps=())
+            for _ in range(args.warmup):
+                fo()
+            torch.cuda.synchronize()
+            start.record()
+            for _ in range(args.steps):
+                fo()
+            end.record()
+            torch.cuda.synchronize()
+            mso = start.elapsed_time(end) / args.steps
+            if int(fo.status[0].item()) != 0:
+                raise SystemExit(f"device status flagged on path {other}")
+            res["other_paths"].append({"path": other + ("+dedup" if dd else ""), "ms_per_step": round(mso, 4),
+                                       "value": round(n_hist * M / (mso * 1e-3), 1)})
+            log(f"other path ({other}{'+dedup' if dd else ''}): {mso:.3f} ms/step")
+            del fo, dpo
     if not args.no_cpu_baseline:
         log(f"timing the float64 oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
