@@ -173,6 +173,10 @@ typedef struct {
    *   2 + 5M       final z done                     (5M + 3 events in all) */
   void *const *stage_events;
   int32_t n_stage_events;
+  float *lse;          /* [M, n_tgt, H] optional, STCA_SCORE_SOFTMAX: log of each (target,
+                          head)'s softmax denominator, ln sum_j exp(s_j) (the max plus the
+                          log of the rescaled sum; 0 for an empty history).  The backward
+                          recomputes the weights exp(s_j - lse) from it. */
 } stca_outputs;
 
 /* Workspace bytes stca_forward needs for this configuration and batch.
@@ -211,6 +215,60 @@ typedef struct {
 
 int stca_attention_workspace_size(const stca_attn_args *a, size_t *bytes);
 int stca_attention(const stca_attn_args *a, void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* ---------------------------------------------------------------- training step
+ * Gradients of a loss through z.  The pages train the same model as they serve
+ * ([Review] 核心公式, "RLB 损失函数": the per-user loss is the mean BCE over the
+ * user's m targets, L_u = (1/m) sum_k BCE(y_hat(u, t_k), y_k); [Notes]
+ * "短序列训练，长序列推理": training runs on shorter, Beta-sampled lengths).  The
+ * head from z to y_hat (RankMixer, sigmoid) is not part of this library: the
+ * caller passes dz = dL/dz and receives the gradient of every STCA weight and of
+ * every embedding row the forward read, by the chain rule through the forward
+ * of stca_forward (recomputed inside the call from the same inputs: nothing is
+ * kept between calls).  Supported: bf16, STCA_Q_FUSION, d_h 32 or 64,
+ * max_tgt_per_user <= 64, softmax or ReLU scores, with or without the history
+ * and z LayerNorms (cfg->path and STCA_FLAG_DEDUP are ignored: the recompute
+ * runs the staged path).
+ *
+ * Weight gradients are fp32, shaped like the weights ([in, out] row-major), and
+ * ACCUMULATED (+=) into the caller's buffers: zero them for a fresh step.  The
+ * ReLU score takes derivative 0 at s = 0.  Rows read through an id outside the
+ * table get no gradient. */
+typedef struct {
+  float *w1, *w3;     /* [d, h] */
+  float *w2;          /* [h, d] */
+  float *ln_g, *ln_b; /* [d]; required where the forward applies that LN */
+} stca_ffn_grad;
+
+typedef struct {
+  stca_ffn_grad kv, q;
+  float *wk, *wv, *wq, *wo;  /* [d, d] */
+  float *wc;                 /* [(i+1) d, d]; NULL at i = 0 */
+} stca_layer_grad;
+
+typedef struct {
+  const stca_layer_grad *layers;  /* host array [M]; every pointer required */
+  stca_ffn_grad z;
+  float *wz;           /* [(M+1) d, d] */
+  float *table;        /* [table_rows, d] optional: += the gradient of every row read by a
+                          history item or a target (atomic adds: the summation order of a
+                          row shared by several items is not fixed) */
+  float *d_hist;       /* [n_hist, d] optional: gradient per history item (overwritten) */
+  float *d_tgt;        /* [n_tgt, d] optional: gradient per target row x_t (overwritten) */
+  float *z_out;        /* [n_tgt, d] optional: z of the recomputed forward */
+  float *dq_dump;      /* [M, n_tgt, d] optional: gradient w.r.t. each layer's query rows
+                          as the attention reads them (after the 1/sqrt(d_h) scale) */
+  float *da_dump;      /* [M, n_tgt, d] optional: gradient w.r.t. each layer's attention
+                          output (heads concatenated, before W_O) */
+  void *dkv_dump;      /* [M, n_hist, 2d] optional, bf16: each layer's dK | dV rows */
+  int32_t *dev_status; /* optional: STCA_DEV_* bits, as for stca_forward */
+} stca_grads;
+
+int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t *bytes);
+
+/* dz: [n_tgt, d] fp32 device array, the upstream gradient of z. */
+int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const float *dz,
+                  const stca_grads *grads, void *workspace, size_t ws_bytes, void *hip_stream);
 
 const char *stca_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -363,7 +363,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int t = (int)(e / d), f = (int)(e % d);
   const int h = f / DH, dh = f % DH;
   const Plan P = a.plan;
-  float out = 0.f;
+  float out = 0.f, lse_v = 0.f;
   int cnt = 0;
   if (t < P.toff[a.B] && a.grid > 0) {
     const int u = upper_index(P.toff, a.B, t);
@@ -398,6 +398,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
           l += a.part_ml[pi * 2 + 1] * fct;
         }
         out = l > 0.f ? acc / l : 0.f;
+        lse_v = l > 0.f ? M + logf(l) : 0.f;
       } else if (SCORE == 0) {  // fp32 path: normalised partials, fp64 fold
         double M = -1.0e300;
         for (int wg = w0; wg <= w1; ++wg) M = fmax(M, (double)a.part_ml[pidx(wg) * 2]);
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
           l += wgt;
         }
         out = l > 0.0 ? (float)(acc / l) : 0.f;
+        lse_v = l > 0.0 ? (float)(M + log(l)) : 0.f;
       } else {
         double acc = 0.0;
         for (int wg = w0; wg <= w1; ++wg) {
@@ -420,6 +422,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       }
     }
   }
+  if (SCORE == 0 && a.lse && dh == 0) a.lse[(int64_t)t * H + h] = lse_v;
   a.attn[e] = out;
   if (a.attn_lo) {
     if (a.dtype) ((bf16_t *)a.attn_lo)[e] = f2bf(out);

@@ -1,0 +1,275 @@
+// grad_ops.hip -- row-wise and element-wise steps of the backward pass.
+//
+// The derivatives written out here are those of the forward's blocks:
+//   SwiGLU  y = (SiLU(x W1) * (x W3)) W2,  SiLU(u) = u * sigmoid(u),
+//           SiLU'(u) = sigmoid(u) * (1 + u * (1 - sigmoid(u)));
+//   LayerNorm y = xhat * g + b, xhat = (x - mean) * rstd (biased variance,
+//           eps 1e-5): dx = rstd * (gy - mean(gy) - xhat * mean(gy * xhat))
+//           with gy = dy * g; dg = sum over rows of dy * xhat, db = sum dy.
+// ([Notes] §STCA names the SwiGLU FFN + LN block of every layer; the forms
+// above are the readings the forward uses.)  Column sums over rows (dg, db)
+// go through per-block partials folded in block order: no atomics decide a
+// floating-point result here, except the table scatter, whose adds into a
+// shared row are atomic by nature.
+#include "grad_internal.h"
+
+namespace stca {
+namespace {
+
+constexpr int kT = 256;
+constexpr float kLnEps = 1e-5f;
+
+DEV float sigm(float u) { return 1.0f / (1.0f + expf(-u)); }
+
+template <typename T> DEV void store(void *p, int64_t i, float v) { ((T *)p)[i] = from_f<T>(v); }
+
+__global__ __launch_bounds__(kT) void gather_kernel(const bf16_t *__restrict__ table, int64_t table_rows,
+                                                    const int *__restrict__ ids, int64_t R, int d, void *out,
+                                                    bool out_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= R * d) return;
+  const int64_t r = e / d;
+  const int f = (int)(e % d);
+  const int id = ids[r];
+  const float v = (id >= 0 && (int64_t)id < table_rows) ? bf2f(table[(int64_t)id * d + f]) : 0.f;
+  if (out_bf16) store<bf16_t>(out, e, v);
+  else store<float>(out, e, v);
+}
+
+__global__ __launch_bounds__(kT) void swiglu_fwd_kernel(const float *__restrict__ h13, int64_t R, int h, void *g,
+                                                        bool g_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= R * h) return;
+  const int64_t r = e / h;
+  const int j = (int)(e % h);
+  const float u = h13[r * 2 * h + j], v = h13[r * 2 * h + h + j];
+  const float y = u * sigm(u) * v;
+  if (g_bf16) store<bf16_t>(g, e, y);
+  else store<float>(g, e, y);
+}
+
+__global__ __launch_bounds__(kT) void swiglu_bwd_kernel(const float *__restrict__ dg, const float *__restrict__ h13,
+                                                        int64_t R, int h, void *dh13, bool out_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= R * h) return;
+  const int64_t r = e / h;
+  const int j = (int)(e % h);
+  const float u = h13[r * 2 * h + j], v = h13[r * 2 * h + h + j];
+  const float sg = sigm(u);
+  const float gg = dg[e];
+  const float d1 = gg * v * sg * (1.0f + u * (1.0f - sg));
+  const float d3 = gg * u * sg;
+  const int64_t o1 = r * 2 * h + j, o3 = o1 + h;
+  if (out_bf16) {
+    store<bf16_t>(dh13, o1, d1);
+    store<bf16_t>(dh13, o3, d3);
+  } else {
+    store<float>(dh13, o1, d1);
+    store<float>(dh13, o3, d3);
+  }
+}
+
+// One wave per row (d <= 1024: each lane handles d / 64 features).
+constexpr int kLnRowsPerBlock = 4;
+
+__global__ __launch_bounds__(kT) void ln_fwd_kernel(const float *__restrict__ y, int64_t R, int d,
+                                                    const float *__restrict__ g, const float *__restrict__ b, void *out,
+                                                    bool out_bf16, float *stats) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float *yr = y + r * d;
+  float s = 0.f;
+  for (int f = lane; f < d; f += 64) s += yr[f];
+  const float mu = wave_sum(s) / d;
+  float q = 0.f;
+  for (int f = lane; f < d; f += 64) {
+    const float c = yr[f] - mu;
+    q += c * c;
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / d + kLnEps);
+  for (int f = lane; f < d; f += 64) {
+    const float v = (yr[f] - mu) * rstd * g[f] + b[f];
+    if (out_bf16) store<bf16_t>(out, r * d + f, v);
+    else store<float>(out, r * d + f, v);
+  }
+  if (lane == 0) {
+    stats[2 * r] = mu;
+    stats[2 * r + 1] = rstd;
+  }
+}
+
+__global__ __launch_bounds__(kT) void copy_rows_kernel(const float *__restrict__ y, int64_t n, void *out,
+                                                       bool out_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= n) return;
+  if (out_bf16) store<bf16_t>(out, e, y[e]);
+  else store<float>(out, e, y[e]);
+}
+
+// rows per LN-backward block, and its partial sums of dg, db
+constexpr int kLnBwdRows = 64;
+
+__global__ __launch_bounds__(kT) void ln_bwd_kernel(const float *__restrict__ dout, const float *__restrict__ y,
+                                                    const float *__restrict__ stats, int64_t R, int d,
+                                                    const float *__restrict__ g, void *dy, bool dy_bf16,
+                                                    float *part) {
+  // block: kLnBwdRows rows, one wave per row at a time; per-lane column
+  // partials of dg, db kept in LDS [4 waves][d] and folded in wave order
+  extern __shared__ float sm[];
+  float *pg = sm, *pb = sm + 4 * d;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int f = lane; f < d; f += 64) {
+    pg[w * d + f] = 0.f;
+    pb[w * d + f] = 0.f;
+  }
+  const int64_t rb = (int64_t)blockIdx.x * kLnBwdRows;
+  for (int i = w; i < kLnBwdRows; i += 4) {
+    const int64_t r = rb + i;
+    if (r >= R) break;
+    const float mu = stats[2 * r], rstd = stats[2 * r + 1];
+    const float *dr = dout + r * d, *yr = y + r * d;
+    float s1 = 0.f, s2 = 0.f;
+    for (int f = lane; f < d; f += 64) {
+      const float xh = (yr[f] - mu) * rstd, gy = dr[f] * g[f];
+      s1 += gy;
+      s2 += gy * xh;
+      pg[w * d + f] += dr[f] * xh;
+      pb[w * d + f] += dr[f];
+    }
+    s1 = wave_sum(s1) / d;
+    s2 = wave_sum(s2) / d;
+    for (int f = lane; f < d; f += 64) {
+      const float xh = (yr[f] - mu) * rstd, gy = dr[f] * g[f];
+      const float v = rstd * (gy - s1 - xh * s2);
+      if (dy_bf16) store<bf16_t>(dy, r * d + f, v);
+      else store<float>(dy, r * d + f, v);
+    }
+  }
+  __syncthreads();
+  for (int f = threadIdx.x; f < d; f += kT) {
+    float a = 0.f, c = 0.f;
+    for (int k = 0; k < 4; ++k) {
+      a += pg[k * d + f];
+      c += pb[k * d + f];
+    }
+    part[(int64_t)blockIdx.x * 2 * d + f] = a;
+    part[(int64_t)blockIdx.x * 2 * d + d + f] = c;
+  }
+}
+
+__global__ __launch_bounds__(kT) void ln_fold_kernel(const float *__restrict__ part, int64_t nblk, int d, float *dg,
+                                                     float *db) {
+  const int f = blockIdx.x * kT + threadIdx.x;
+  if (f >= 2 * d) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nblk; ++b) s += part[b * 2 * d + f];
+  if (f < d) dg[f] += s;
+  else db[f - d] += s;
+}
+
+__global__ __launch_bounds__(kT) void add_rows_kernel(const float *__restrict__ src, int64_t lds, float *dst,
+                                                      int64_t ldd, int64_t R, int d, bool accumulate) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= R * d) return;
+  const int64_t r = e / d;
+  const int f = (int)(e % d);
+  const float v = src[r * lds + f];
+  dst[r * ldd + f] = accumulate ? dst[r * ldd + f] + v : v;
+}
+
+__global__ __launch_bounds__(kT) void concat_kernel(const float *__restrict__ src, int S, int64_t R, int d,
+                                                    float *dst) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= (int64_t)S * R * d) return;
+  const int64_t sidx = e / (R * d), rem = e % (R * d);
+  const int64_t r = rem / d;
+  const int f = (int)(rem % d);
+  dst[r * S * d + sidx * d + f] = src[e];
+}
+
+__global__ __launch_bounds__(kT) void scatter_kernel(const float *__restrict__ rows, const int *__restrict__ ids,
+                                                     int64_t R, int d, float *table, int64_t table_rows) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= R * d) return;
+  const int64_t r = e / d;
+  const int id = ids[r];
+  if (id < 0 || (int64_t)id >= table_rows) return;
+  atomicAdd(table + (int64_t)id * d + (e % d), rows[e]);
+}
+
+unsigned blocks(int64_t n) { return (unsigned)((n + kT - 1) / kT); }
+
+}  // namespace
+
+hipError_t launch_gather_rows(const bf16_t *table, int64_t table_rows, const int *ids, int64_t R, int d, void *out,
+                              bool out_bf16, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, table, table_rows, ids, R, d, out, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const float *h13, int64_t R, int h, void *g, bool g_bf16, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, h13, R, h, g, g_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const float *dg, const float *h13, int64_t R, int h, void *dh13, bool out_bf16,
+                             hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, dg, h13, R, h, dh13, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_fwd(const float *y, int64_t R, int d, const float *g, const float *b, void *out, bool out_bf16,
+                         float *stats, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (!g) {
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, y, R * d, out, out_bf16);
+  } else {
+    const unsigned nb = (unsigned)((R + kLnRowsPerBlock - 1) / kLnRowsPerBlock);
+    hipLaunchKernelGGL(ln_fwd_kernel, dim3(nb), dim3(kT), 0, s, y, R, d, g, b, out, out_bf16, stats);
+  }
+  return hipGetLastError();
+}
+
+int64_t ln_part_rows(int64_t R) { return (R + kLnBwdRows - 1) / kLnBwdRows; }
+
+hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, int64_t R, int d, const float *g,
+                         void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (!g) {
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, dout, R * d, dy, dy_bf16);
+    return hipGetLastError();
+  }
+  const int64_t nblk = ln_part_rows(R);
+  hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)nblk), dim3(kT), 8 * d * sizeof(float), s, dout, y, stats, R, d, g,
+                     dy, dy_bf16, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ln_fold_kernel, dim3(blocks(2 * d)), dim3(kT), 0, s, part, nblk, d, dg, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rows(const float *src, int64_t lds, float *dst, int64_t ldd, int64_t R, int d, bool accumulate,
+                           hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(add_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, src, lds, dst, ldd, R, d, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float *dst, hipStream_t s) {
+  if (R <= 0 || S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(concat_kernel, dim3(blocks((int64_t)S * R * d)), dim3(kT), 0, s, src, S, R, d, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
+                              hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, ids, R, d, table, table_rows);
+  return hipGetLastError();
+}
+
+}  // namespace stca

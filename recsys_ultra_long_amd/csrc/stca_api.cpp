@@ -46,6 +46,21 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(STCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+}  // namespace
+
+namespace stca {
+int api_error(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+void api_clear_error() { g_err[0] = 0; }
+}  // namespace stca
+
+namespace {
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr size_t kAlign = 256;
@@ -344,7 +359,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   if (!out->z && batch->n_tgt > 0) return fail(STCA_ERR_INVALID_ARG, "outputs->z is required");
   {
     const void *ptrs[] = {out->z, out->o_layers, out->attn, out->active, out->q_dump, out->kv_dump,
-                          out->x_dump, out->dev_status};
+                          out->x_dump, out->dev_status, out->lse};
     for (const void *p : ptrs)
       if (p && (reinterpret_cast<uintptr_t>(p) & 3u)) return fail(STCA_ERR_INVALID_ARG, "output pointer %p misaligned", p);
     const void *p16[] = {out->z, out->o_layers, out->attn, out->q_dump, out->x_dump};
@@ -516,6 +531,7 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     at_.attn = out->attn ? out->attn + (size_t)i * T * d : at<float>(ws, L.attn32);
     at_.attn_lo = at<void>(ws, L.attnlo);
     at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
+    at_.lse = (out->lse && cfg->score == STCA_SCORE_SOFTMAX) ? out->lse + (size_t)i * T * H : nullptr;
     at_.B = B;
     if (batch->n_hist == 0) at_.max_units = 0;
     return at_;

@@ -9,6 +9,10 @@
 
 namespace stca {
 
+// Thread-local error message of the C ABI (stca_last_error); returns `code`.
+int api_error(int code, const char *fmt, ...);
+void api_clear_error();
+
 // Device-side batch plan written by the planner kernel (all int32):
 //   hoff[B+1]  sanitised history offsets (all zero when the CSR is bad)
 //   toff[B+1]  sanitised target offsets
@@ -162,6 +166,7 @@ struct AttnArgs {
   float *attn;              // [n_tgt, d] fp32 (required)
   void *attn_lo;            // [n_tgt, d] config dtype copy (optional)
   int *active;              // [n_tgt, H] (optional)
+  float *lse;               // [n_tgt, H] (optional, softmax): max + ln(sum of weights)
   int B;
 };
 

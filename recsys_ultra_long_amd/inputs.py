@@ -20,8 +20,11 @@ Distributions (readings of the workload descriptions, restated in the design doc):
   LayerNorm gain 1 and bias 0 unless ``ln_random`` is set (tests use random
   gain/bias so that a dropped affine term is caught);
 * ids: uniform on [0, N) or bounded Zipf, P(k) proportional to (k+1)^-s;
-* ragged lengths: L_u = max(16, ceil(L_max * beta)), beta ~ Beta(2, 1),
-  sampled as sqrt(U);
+* ragged lengths: L_u = max(16, ceil(L_max * beta)), beta ~ Beta(alpha, 1),
+  sampled as U^(1/alpha) (alpha = 2 for the ragged inference workload;
+  alpha = 1/4 for the training workload, whose mean length L_max / 5 = 2K is
+  the training length the reading notes give for 10K inference);
+* the upstream gradient of z for the backward: i.i.d. N(0, 1);
 * bf16 storage is produced by round-to-nearest-even from float32.
 
 Storage convention: a bf16 array is a ``numpy.uint16`` array of raw bf16
@@ -93,8 +96,9 @@ class Spec:
     kv_ln: bool = True                  # LN after the history FFN
     z_ln: bool = False                  # LN on the final z
     L: Optional[int] = None             # fixed history length
-    L_max: Optional[int] = None         # ragged: max(16, ceil(L_max * Beta(2,1)))
+    L_max: Optional[int] = None         # ragged: max(L_min, ceil(L_max * Beta(beta_a, 1)))
     L_min: int = 16
+    beta_a: float = 2.0
     m: int = 1                          # targets (or queries) per user
     ids: str = "zipf"                   # "zipf" | "uniform"
     zipf_s: float = 1.1
@@ -127,9 +131,19 @@ def spec(k: int, **over) -> Spec | dict:
                     seed=51)
         search = replace(feed, name="hyformer-search", L=1024, seed=52)
         return {"feed": replace(feed, **over), "search": replace(search, **over)}
+    elif k == 6:
+        # training: the RLB long model on Beta(1/4, 1) lengths (mean 2K of 10K)
+        s = Spec("rlb-train-bf16", B=128, d=256, H=8, hidden=512, M=4,
+                 table_rows=4_000_000, L_max=10_240, beta_a=0.25, m=16, seed=6)
     else:
         raise ValueError(f"unknown workload {k}")
     return replace(s, **over)
+
+
+def upstream_grad(sp: Spec, n_tgt: int, seed: int = 0) -> np.ndarray:
+    """Seeded upstream gradient dL/dz [n_tgt, d] (float32) for the backward."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 7919, seed])))
+    return g.standard_normal((n_tgt, sp.d), dtype=np.float32)
 
 
 # --------------------------------------------------------------------------
@@ -163,7 +177,8 @@ def sample_ids(rng: np.random.Generator, n: int, rows: int, law: str, s: float) 
 def sample_lengths(rng: np.random.Generator, sp: Spec) -> np.ndarray:
     if sp.L is not None:
         return np.full(sp.B, sp.L, dtype=np.int64)
-    beta = np.sqrt(rng.random(sp.B))                  # Beta(2, 1)
+    u = rng.random(sp.B)
+    beta = np.sqrt(u) if sp.beta_a == 2.0 else u ** (1.0 / sp.beta_a)   # Beta(a, 1)
     return np.maximum(sp.L_min, np.ceil(sp.L_max * beta)).astype(np.int64)
 
 

@@ -26,7 +26,8 @@ FLAG_KV_LN, FLAG_Z_LN, FLAG_DEDUP = 1, 2, 4
 DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
-           "stca_attention", "stca_status_string", "stca_last_error", "stca_version")
+           "stca_attention", "stca_backward_workspace_size", "stca_backward",
+           "stca_status_string", "stca_last_error", "stca_version")
 
 _vp = C.c_void_p
 
@@ -60,7 +61,22 @@ class Weights(C.Structure):
 class Outputs(C.Structure):
     _fields_ = [("z", _vp), ("o_layers", _vp), ("attn", _vp), ("active", _vp), ("q_dump", _vp),
                 ("kv_dump", _vp), ("x_dump", _vp), ("dev_status", _vp),
-                ("stage_events", C.POINTER(_vp)), ("n_stage_events", C.c_int32)]
+                ("stage_events", C.POINTER(_vp)), ("n_stage_events", C.c_int32), ("lse", _vp)]
+
+
+class FfnGrad(C.Structure):
+    _fields_ = [("w1", _vp), ("w3", _vp), ("w2", _vp), ("ln_g", _vp), ("ln_b", _vp)]
+
+
+class LayerGrad(C.Structure):
+    _fields_ = [("kv", FfnGrad), ("q", FfnGrad), ("wk", _vp), ("wv", _vp), ("wq", _vp), ("wo", _vp),
+                ("wc", _vp)]
+
+
+class Grads(C.Structure):
+    _fields_ = [("layers", C.POINTER(LayerGrad)), ("z", FfnGrad), ("wz", _vp), ("table", _vp),
+                ("d_hist", _vp), ("d_tgt", _vp), ("z_out", _vp), ("dq_dump", _vp), ("da_dump", _vp),
+                ("dkv_dump", _vp), ("dev_status", _vp)]
 
 
 class AttnArgs(C.Structure):
@@ -95,12 +111,16 @@ def load() -> C.CDLL:
                                      C.POINTER(Outputs), _vp, C.c_size_t, _vp]
         lib.stca_attention_workspace_size.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
         lib.stca_attention.argtypes = [C.POINTER(AttnArgs), _vp, C.c_size_t, _vp]
+        lib.stca_backward_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(Batch),
+                                                     C.POINTER(C.c_size_t)]
+        lib.stca_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
+                                      C.POINTER(Grads), _vp, C.c_size_t, _vp]
         lib.stca_status_string.restype = C.c_char_p
         lib.stca_status_string.argtypes = [C.c_int]
         lib.stca_last_error.restype = C.c_char_p
         lib.stca_version.restype = C.c_int
         for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
-                  "stca_attention"):
+                  "stca_attention", "stca_backward_workspace_size", "stca_backward"):
             getattr(lib, f).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -261,11 +281,13 @@ class Forward:
         self.kv_dump = (torch.empty((M, 2, dp.n_hist, d), dtype=lo, device=dev)
                         if "kv" in dumps else None)
         self.x_dump = torch.empty((dp.n_hist, d), dtype=lo, device=dev) if "x" in dumps else None
+        self.lse = torch.empty((M, T, H), dtype=torch.float32, device=dev) if "lse" in want else None
         self.status = torch.zeros(4, dtype=torch.int32, device=dev)
         self.b, self.w, self._layers = _structs(dp)
         self.out = Outputs(_ptr(self.z), _ptr(self.o), _ptr(self.attn), _ptr(self.active),
                            _ptr(self.q_dump), _ptr(self.kv_dump), _ptr(self.x_dump),
                            _ptr(self.status))
+        self.out.lse = _ptr(self.lse)
         if events is not None:
             self.out.stage_events = events.ptr
             self.out.n_stage_events = events.n
@@ -285,8 +307,91 @@ class Forward:
 
     def results(self) -> dict:
         r = {"z": self.z, "o": self.o, "attn": self.attn, "active": self.active,
-             "q": self.q_dump, "kv": self.kv_dump, "x": self.x_dump, "status": self.status}
+             "q": self.q_dump, "kv": self.kv_dump, "x": self.x_dump, "lse": self.lse,
+             "status": self.status}
         return {k: v for k, v in r.items() if v is not None}
+
+
+class Backward:
+    """Reusable backward call (``stca_backward``): gradient buffers, upstream
+    gradient and workspace are allocated once.  ``grads`` mirrors the weight
+    nesting (layers[i]["kv"|"q"][w1|w3|w2|ln_g|ln_b], wk, wv, wq, wo, wc;
+    z[...]; wz) with fp32 tensors; the library accumulates into them, so
+    ``zero()`` them before a fresh step."""
+
+    def __init__(self, dp: DeviceProblem, dz, outputs=("table", "d_hist", "d_tgt", "z"), dumps=(),
+                 stream=None):
+        import torch
+        self.dp = dp
+        self.lib = load()
+        cfg = dp.cfg
+        dev = dp.table.device
+        T, d, M = dp.n_tgt, cfg.d, cfg.M
+        f32 = dict(dtype=torch.float32, device=dev)
+
+        def like(w):
+            if w is None:
+                return None
+            if isinstance(w, dict):
+                return {k: like(v) for k, v in w.items()}
+            return torch.zeros(tuple(w.shape), **f32)
+        self.grads = {"layers": [like({k: v for k, v in l.items() if k != "r"}) for l in dp.layers],
+                      "z": like(dp.z), "wz": like(dp.wz)}
+        self.dz = dz
+        self.table = torch.zeros((cfg.table_rows, d), **f32) if "table" in outputs else None
+        self.d_hist = torch.empty((dp.n_hist, d), **f32) if "d_hist" in outputs else None
+        self.d_tgt = torch.empty((T, d), **f32) if "d_tgt" in outputs else None
+        self.z_out = torch.empty((T, d), **f32) if "z" in outputs else None
+        self.dq_dump = torch.empty((M, T, d), **f32) if "dq" in dumps else None
+        self.da_dump = torch.empty((M, T, d), **f32) if "da" in dumps else None
+        self.dkv_dump = (torch.empty((M, dp.n_hist, 2 * d), dtype=torch.int16, device=dev)
+                         if "dkv" in dumps else None)
+        self.status = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.b, self.w, self._layers = _structs(dp)
+
+        def fg(g):
+            if g is None:
+                return FfnGrad()
+            return FfnGrad(_ptr(g["w1"]), _ptr(g["w3"]), _ptr(g["w2"]), _ptr(g.get("ln_g")),
+                           _ptr(g.get("ln_b")))
+        lg = (LayerGrad * M)()
+        for i, g in enumerate(self.grads["layers"]):
+            lg[i] = LayerGrad(fg(g["kv"]), fg(g["q"]), _ptr(g["wk"]), _ptr(g["wv"]), _ptr(g["wq"]),
+                              _ptr(g["wo"]), _ptr(g.get("wc")))
+        self._lg = lg
+        self.g = Grads(lg, fg(self.grads["z"]), _ptr(self.grads["wz"]), _ptr(self.table),
+                       _ptr(self.d_hist), _ptr(self.d_tgt), _ptr(self.z_out), _ptr(self.dq_dump),
+                       _ptr(self.da_dump), _ptr(self.dkv_dump), _ptr(self.status))
+        n = C.c_size_t(0)
+        _check(self.lib.stca_backward_workspace_size(C.byref(cfg), C.byref(self.b), C.byref(n)))
+        self.ws_bytes = n.value
+        self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
+        self.stream = stream
+
+    def zero(self):
+        def z(g):
+            if g is None:
+                return
+            if isinstance(g, dict):
+                for v in g.values():
+                    z(v)
+            elif isinstance(g, list):
+                for v in g:
+                    z(v)
+            else:
+                g.zero_()
+        z(self.grads)
+        if self.table is not None:
+            self.table.zero_()
+        return self
+
+    def __call__(self):
+        import torch
+        s = self.stream if self.stream is not None else torch.cuda.current_stream()
+        _check(self.lib.stca_backward(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
+                                      _ptr(self.dz), C.byref(self.g), self.ws.data_ptr(), self.ws_bytes,
+                                      s.cuda_stream))
+        return self
 
 
 def forward(dp: DeviceProblem, want=("o", "attn", "active"), dumps=()) -> dict:
