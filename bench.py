@@ -44,6 +44,8 @@ def workload(name):
         return I.spec(2)
     if name == "ragged":
         return I.spec(4)
+    if name == "rlb-train":
+        return I.spec(6)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -80,12 +82,115 @@ def cpu_baseline(p, seconds):
             "target_scores_per_s": tgts / dt}
 
 
+def cpu_baseline_backward(p, dz, seconds):
+    """Float64 backward oracle on whole users of the training workload until
+    `seconds` pass."""
+    from oracle import stca_grad as OG
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = 1
+    sp = p.spec
+    t0 = time.perf_counter()
+    users, toks = 0, 0
+    while users < sp.B:
+        OG.backward_problem(p, dz, users=[users])
+        toks += int(p.hist_offsets[users + 1] - p.hist_offsets[users])
+        users += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": toks * sp.M / dt, "unit": "history tokens/s per STCA layer (backward)",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{users} of {sp.B} users ({toks} history tokens, {sp.M} layers) in {dt:.1f} s, "
+                      "float64 numpy backward (forward recompute included)"}
+
+
+def bench_backward(args):
+    """One training step = stca_forward (fused path: z for the loss head) +
+    stca_backward (gradients of every weight and table row for a seeded dz)."""
+    import numpy as np
+    import torch
+    from recsys_ultra_long_amd import inputs as I
+    from recsys_ultra_long_amd import stca
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stca.load()
+    sp = workload(args.workload)
+    t = time.time()
+    p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
+    log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} n_tgt={p.n_tgt}")
+    dz_np = I.upstream_grad(sp, p.n_tgt)
+    dz = torch.from_numpy(dz_np).cuda()
+    dp_f = stca.upload(p, path="fused")
+    dp_b = stca.upload(p, table=dp_f.table)
+    f = stca.Forward(dp_f, want=(), dumps=())
+    bw = stca.Backward(dp_b, dz, outputs=("table",))
+    log(f"backward workspace {bw.ws_bytes / 2**30:.2f} GiB")
+    for _ in range(args.warmup):
+        bw.zero()
+        f()
+        bw()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        bw.zero()
+        ev[k][0].record()
+        f()
+        ev[k][1].record()
+        bw()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ms_b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    if int(bw.status[0].item()) != 0 or int(f.status[0].item()) != 0:
+        raise SystemExit("device status flagged")
+    d, h, M = sp.d, sp.hidden, sp.M
+    n_hist, T = p.n_hist, p.n_tgt
+    pairs = int(np.sum(np.diff(p.hist_offsets).astype(np.int64) * np.diff(p.tgt_offsets)))
+    # backward proper, per layer: history 18 d h + 8 d^2 per item (recomputed
+    # FFN, dXt, dG, dX, weight gradients), attention 10 d per (item, target)
+    # pair; the forward recompute inside the call adds one forward
+    flops_b = M * (n_hist * (18 * d * h + 8 * d * d) + 10 * d * pairs)
+    flops_f = M * (n_hist * (6 * d * h + 4 * d * d) + 4 * d * pairs)
+    ms = ms_f + ms_b
+    res = {
+        "metric": "training step (forward + backward) history tokens/s per STCA layer",
+        "value": round(n_hist * M / (ms * 1e-3), 1),
+        "unit": "history tokens/s per STCA layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "ms_forward": round(ms_f, 4), "ms_backward": round(ms_b, 4),
+        "ms_wall_per_step": round(wall, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{sp.name}: B={sp.B} users, L ~ max(16, ceil(10240 Beta({sp.beta_a},1))) "
+                               f"(sum {n_hist}), m={sp.m} targets/user, table {sp.table_rows}x{d} bf16 "
+                               f"Zipf({sp.zipf_s}) ids, d={d}, H={sp.H}, hidden={h}, M={M}, softmax; "
+                               "forward on the fused path, backward recomputes on the staged path",
+                   "global_batch": sp.B, "targets": T, "parallelism": "single GPU"},
+        "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
+        "backward_flops": {"proper": flops_b, "recompute": flops_f},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the float64 backward oracle for ~{args.cpu_seconds:.0f}s")
+        res["cpu_baseline"] = cpu_baseline_backward(p, dz_np, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="rlb-long")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step (forward + stca_backward) on the training "
+                         "workload (rlb-train unless --workload names another)")
     ap.add_argument("--path", default="fused", choices=["staged", "fused"],
                     help="fused (default, the faster complete path here) or staged")
     ap.add_argument("--dedup", action="store_true",
@@ -99,6 +204,10 @@ def main():
                     help="run only a plain device copy of 1 GiB (x5), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.backward:
+        if args.workload == "rlb-long":
+            args.workload = "rlb-train"
+        return bench_backward(args)
     if args.copy_calibration:
         import torch
         n = 1 << 30

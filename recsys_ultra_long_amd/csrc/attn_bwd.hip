@@ -115,10 +115,21 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
     const int key = kb + l32;
     const bool kval = key < k_end;
     bf16x8 kf[KS], vf[KS];
+    if (a.tok2u) {  // the item's unique row: blocked K, row-major V
+      const int ui = kval ? a.tok2u[h0 + key] : 0;
+      const bf16_t *kr = a.k + ((((int64_t)(ui >> 5)) * a.H + eta) * 32 + (ui & 31)) * DH;
+      const bf16_t *vr = a.v + (int64_t)ui * d + col0;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = kval ? ld8(a.k + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
-      vf[s] = kval ? ld8(a.v + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
+      for (int s = 0; s < KS; ++s) {
+        kf[s] = kval ? ld8(kr + 16 * s + 8 * g) : zero8;
+        vf[s] = kval ? ld8(vr + 16 * s + 8 * g) : zero8;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        kf[s] = kval ? ld8(a.k + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
+        vf[s] = kval ? ld8(a.v + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
+      }
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s)

@@ -157,6 +157,31 @@ __global__ __launch_bounds__(kT) void pad_kernel(DedupArgs d, int64_t rows) {
   if (r < rows && r >= *d.n_unique) d.uniq_rows[r] = -1;
 }
 
+// Sort keys of the unique rows: id + 1 (the out-of-range entry, id -1, sorts
+// first), padding rows after every id.
+__global__ __launch_bounds__(kT) void sortkey_kernel(DedupArgs d, int64_t rows, int pad_key) {
+  const int64_t r = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (r < rows) d.sort_in[r] = r < *d.n_unique ? d.uniq_rows[r] + 1 : pad_key;
+}
+
+// Row r of the id order was row perm^-1(r) of the slot order.
+__global__ __launch_bounds__(kT) void renumber_kernel(DedupArgs d, int64_t rows, const int *skeys,
+                                                      const int *svals) {
+  const int64_t r = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (r >= rows) return;
+  if (r < *d.n_unique) {
+    d.perm[svals[r]] = (int)r;
+    d.uniq_rows[r] = skeys[r] - 1;
+  } else {
+    d.uniq_rows[r] = -1;
+  }
+}
+
+__global__ __launch_bounds__(kT) void slot_renumber_kernel(DedupArgs d) {
+  const int64_t s = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (d.keys[s] != kEmpty) d.slot_uid[s] = d.perm[d.slot_uid[s]];
+}
+
 __global__ __launch_bounds__(kT) void map_kernel(DedupArgs d) {
   const int64_t t = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (t >= d.n_hist) return;
@@ -246,6 +271,18 @@ hipError_t launch_dedup(DedupArgs &d, hipStream_t s) {
   hipLaunchKernelGGL(assign_kernel, dim3(gs), dim3(kT), 0, s, d);
   const int64_t rows = dedup_rows(d.n_hist);
   hipLaunchKernelGGL(pad_kernel, dim3((unsigned)((rows + kT - 1) / kT)), dim3(kT), 0, s, d, rows);
+  // number the unique rows in increasing id order
+  const int bits = radix_bits(d.table_rows + 1);  // keys 0 .. table_rows, and the padding key
+  const int pad_key = (int)((1ll << bits) - 1);
+  const unsigned gr = (unsigned)((rows + kT - 1) / kT);
+  hipLaunchKernelGGL(sortkey_kernel, dim3(gr), dim3(kT), 0, s, d, rows, pad_key);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  RadixResult rr;
+  if ((e = launch_radix_sort(d.sort_in, nullptr, rows, bits, d.sort_keys, d.sort_vals, d.sort_hist, &rr, s)))
+    return e;
+  hipLaunchKernelGGL(renumber_kernel, dim3(gr), dim3(kT), 0, s, d, rows, rr.keys, rr.vals);
+  hipLaunchKernelGGL(slot_renumber_kernel, dim3(gs), dim3(kT), 0, s, d);
   hipLaunchKernelGGL(map_kernel, dim3(g), dim3(kT), 0, s, d);
   return hipGetLastError();
 }

@@ -34,58 +34,83 @@ template <> DEV void load8<float>(const float *p, float (&v)[8]) {
   }
 }
 
-// Stage a [128 rows x 32 k] tile of an operand into S[row * LDK + k] (bf16).
-// Rows r0 .. r0+127 of R, k0 .. k0+31 of [k0, ke).  KC: the k stride is 1
-// (else the row stride is 1).  vec: 8-element runs along the contiguous
-// dimension may be loaded as vectors (aligned, and the other stride a
-// multiple of 8).
+// A [128 rows x 32 k] tile of an operand, as each thread holds it between
+// its global load and its LDS store: two runs of 8 elements along the
+// contiguous dimension (KC: along k; else along rows).  Rows r0 .. r0+127 of
+// R, k in [k0, k0 + 32) within [.., ke).  vec: an 8-element run may be loaded
+// as vectors (aligned, and the other stride a multiple of 8).
+struct Frag {
+  float v[2][8];
+};
+
 template <typename T, bool KC>
-DEV void stage(const T *__restrict__ p, int64_t sr, int64_t sk, int64_t r0, int64_t R, int64_t k0, int64_t ke,
-               bool vec, bf16_t *S, int tid) {
+DEV void tile_load(const T *__restrict__ p, int64_t sr, int64_t sk, int64_t r0, int64_t R, int64_t k0, int64_t ke,
+                   bool vec, Frag &f, int tid) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int c = tid + 256 * j;
     if (KC) {
-      const int r = c >> 2, kc = (c & 3) * 8;
-      const int64_t gr = r0 + r, gk = k0 + kc;
-      float v[8];
+      const int64_t gr = r0 + (c >> 2), gk = k0 + (c & 3) * 8;
       if (gr < R && vec && gk + 8 <= ke) {
-        load8<T>(p + gr * sr + gk, v);
+        load8<T>(p + gr * sr + gk, f.v[j]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (gr < R && gk + e < ke) ? to_f<T>(p[gr * sr + gk + e]) : 0.f;
+        for (int e = 0; e < 8; ++e) f.v[j][e] = (gr < R && gk + e < ke) ? to_f<T>(p[gr * sr + gk + e]) : 0.f;
       }
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf2(v[2 * e], v[2 * e + 1]);
-      *reinterpret_cast<u32x4 *>(S + r * LDK + kc) = w;
     } else {
-      const int k = c >> 4, rc = (c & 15) * 8;
-      const int64_t gk = k0 + k, gr = r0 + rc;
-      float v[8];
+      const int64_t gk = k0 + (c >> 4), gr = r0 + (c & 15) * 8;
       if (gk < ke && vec && gr + 8 <= R) {
-        load8<T>(p + gk * sk + gr, v);
+        load8<T>(p + gk * sk + gr, f.v[j]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (gk < ke && gr + e < R) ? to_f<T>(p[gk * sk + gr + e]) : 0.f;
+        for (int e = 0; e < 8; ++e) f.v[j][e] = (gk < ke && gr + e < R) ? to_f<T>(p[gk * sk + gr + e]) : 0.f;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) S[(rc + e) * LDK + k] = f2bf(v[e]);
     }
   }
 }
 
+// ... into S[row * LDK + k] (bf16, rounded to nearest even)
+template <bool KC>
+DEV void tile_store(const Frag &f, bf16_t *S, int tid) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + 256 * j;
+    if (KC) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf2(f.v[j][2 * e], f.v[j][2 * e + 1]);
+      *reinterpret_cast<u32x4 *>(S + (c >> 2) * LDK + (c & 3) * 8) = w;
+    } else {
+      const int k = c >> 4, rc = (c & 15) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S[(rc + e) * LDK + k] = f2bf(f.v[j][e]);
+    }
+  }
+}
+
+// Double-buffered: tile k+1 is loaded into registers while tile k is
+// multiplied out of LDS, then stored into the other buffer; one barrier per
+// k-tile.
 template <typename TA, typename TB, bool AKC, bool BKC, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, bool va, bool vb) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDK];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
-  int64_t kb = 0, ke = g.K;
+  int64_t kb = 0, ke = g.K, Meff = g.M;
   if (SPLIT) {
     kb = (int64_t)blockIdx.z * kchunk;
     ke = kb + kchunk < g.K ? kb + kchunk : g.K;
+  }
+  if (g.dev_rows) {
+    const int64_t lim = *g.dev_rows;
+    if (g.dev_dim == 1) {
+      Meff = lim < g.M ? lim : g.M;
+      if (m0 >= Meff) return;  // the whole workgroup: before any barrier
+    } else if (g.dev_dim == 2 && lim < ke) {
+      ke = lim;
+    }
   }
   const TA *A = (const TA *)g.A;
   const TB *B = (const TB *)g.B;
@@ -96,23 +121,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  Frag fa, fb;
+  if (kb < ke) {
+    tile_load<TA, AKC>(A, g.sam, g.sak, m0, Meff, kb, ke, va, fa, tid);
+    tile_load<TB, BKC>(B, g.sbn, g.sbk, n0, g.N, kb, ke, vb, fb, tid);
+    tile_store<AKC>(fa, As[0], tid);
+    tile_store<BKC>(fb, Bs[0], tid);
+  }
+  __syncthreads();
+  int cur = 0;
   for (int64_t k0 = kb; k0 < ke; k0 += BK) {
-    stage<TA, AKC>(A, g.sam, g.sak, m0, g.M, k0, ke, va, As, tid);
-    stage<TB, BKC>(B, g.sbn, g.sbk, n0, g.N, k0, ke, vb, Bs, tid);
-    __syncthreads();
+    const bool more = k0 + BK < ke;
+    if (more) {
+      tile_load<TA, AKC>(A, g.sam, g.sak, m0, Meff, k0 + BK, ke, va, fa, tid);
+      tile_load<TB, BKC>(B, g.sbn, g.sbk, n0, g.N, k0 + BK, ke, vb, fb, tid);
+    }
+    const bf16_t *as = As[cur], *bs = Bs[cur];
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = ld8(As + (wm * 64 + i * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5));
+      for (int i = 0; i < 2; ++i) af[i] = ld8(as + (wm * 64 + i * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = ld8(Bs + (wn * 64 + j * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5));
+      for (int j = 0; j < 2; ++j) bfr[j] = ld8(bs + (wn * 64 + j * 32 + (lane & 31)) * LDK + kk + 8 * (lane >> 5));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
+    if (more) {
+      tile_store<AKC>(fa, As[cur ^ 1], tid);
+      tile_store<BKC>(fb, Bs[cur ^ 1], tid);
+    }
     __syncthreads();
+    cur ^= 1;
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -123,7 +165,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + wm * 64 + i * 32 + c32_row(lane, r);
-        if (m >= g.M) continue;
+        if (m >= Meff) continue;
         if (SPLIT) {
           g.part[((int64_t)blockIdx.z * g.M + m) * g.N + n] = acc[i][j][r];
         } else {
@@ -148,10 +190,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split
 
 template <typename TA, typename TB, bool AKC, bool BKC>
 hipError_t run(const GemmArgs &g, hipStream_t s) {
-  const int64_t es_a = g.a_bf16 ? 2 : 4, es_b = g.b_bf16 ? 2 : 4;
   // vector loads: 16-byte aligned base, and the non-unit stride a multiple of 8
-  const bool va = (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) && ((AKC ? g.sam : g.sak) % 8 == 0) && es_a > 0;
-  const bool vb = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && ((BKC ? g.sbn : g.sbk) % 8 == 0) && es_b > 0;
+  const bool va = (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) && ((AKC ? g.sam : g.sak) % 8 == 0);
+  const bool vb = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && ((BKC ? g.sbn : g.sbk) % 8 == 0);
   const unsigned gx = (unsigned)((g.M + BM - 1) / BM), gy = (unsigned)((g.N + BN - 1) / BN);
   if (g.split > 1) {
     int64_t kchunk = (g.K + g.split - 1) / g.split;

@@ -2,9 +2,30 @@
 // Not part of the public ABI.
 #pragma once
 
+#include "stca.h"
 #include "stca_internal.h"
 
 namespace stca {
+
+// ------------------------------------------------------------ forward internals
+// stca_forward with, when STCA_FLAG_DEDUP is set, the location of its
+// unique-row buffers (valid until the workspace is reused):
+//   tok2u[n_hist]       unique index of every history item
+//   uniq_rows[drows]    table id of every unique row (-1: padding / out of range)
+//   n_unique            device int: the number of unique rows
+//   ukv                 layer i: K of the unique rows at ukv + 2 i ukv_layer_elems,
+//                       blocked [row / 32][H][32][d_h]
+//   vrows               layer i: V of the unique rows at vrows + i drows d, [row][d]
+struct ForwardInternals {
+  bool dedup;
+  const int *tok2u, *uniq_rows, *n_unique;
+  int64_t drows;
+  const bf16_t *ukv;
+  size_t ukv_layer_elems;
+  const bf16_t *vrows;
+};
+int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                           const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi);
 
 // ------------------------------------------------------------ generic GEMM
 // C(m, n) = alpha * sum_k A(m, k) B(k, n) + beta * C(m, n)
@@ -13,6 +34,9 @@ namespace stca {
 // Operands are fp32 or bf16 (converted to bf16 for the MFMA), accumulation
 // fp32, C fp32.  split > 1 cuts K into that many ranges, each writing a
 // partial [M, N] into `part` (split * M * N floats), folded in range order.
+// dev_rows (optional): a device count that caps M (dev_dim 1: row tiles past
+// it exit, their C rows are left as they are) or K (dev_dim 2: the sum stops
+// there), for products over rows whose number is only known on the device.
 struct GemmArgs {
   int64_t M, N, K;
   const void *A;
@@ -26,6 +50,8 @@ struct GemmArgs {
   float alpha, beta;
   int split;
   float *part;
+  const int *dev_rows;
+  int dev_dim;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 // Split factor for a long-K product (weight gradients), and the partial
@@ -36,23 +62,26 @@ inline int64_t gemm_part_floats(int64_t M, int64_t N, int split) { return split 
 // ------------------------------------------------------------ row kernels
 // out[r, :] = table[ids[r], :] for valid ids, zero rows otherwise (bf16 in;
 // bf16 or fp32 out).
+// Every row kernel takes an optional device count `dev_rows` that caps R.
 hipError_t launch_gather_rows(const bf16_t *table, int64_t table_rows, const int *ids, int64_t R, int d,
-                              void *out, bool out_bf16, hipStream_t s);
+                              void *out, bool out_bf16, hipStream_t s, const int *dev_rows = nullptr);
 // G = SiLU(H1) * H3 with H13 = [H1 | H3] ([R, 2h] fp32); G bf16 or fp32.
-hipError_t launch_swiglu_fwd(const float *h13, int64_t R, int h, void *g, bool g_bf16, hipStream_t s);
+hipError_t launch_swiglu_fwd(const float *h13, int64_t R, int h, void *g, bool g_bf16, hipStream_t s,
+                             const int *dev_rows = nullptr);
 // dH1 = dG * H3 * SiLU'(H1), dH3 = dG * SiLU(H1) into [R, 2h] (bf16 or fp32).
 hipError_t launch_swiglu_bwd(const float *dg, const float *h13, int64_t R, int h, void *dh13, bool out_bf16,
-                             hipStream_t s);
+                             hipStream_t s, const int *dev_rows = nullptr);
 // LayerNorm over rows of Y [R, d] (fp32): out = xhat * g + b (bf16 or fp32);
 // per-row (mean, rstd) into stats [R, 2].  g == nullptr: out = Y, no stats.
 hipError_t launch_ln_fwd(const float *y, int64_t R, int d, const float *g, const float *b, void *out, bool out_bf16,
-                         float *stats, hipStream_t s);
+                         float *stats, hipStream_t s, const int *dev_rows = nullptr);
 // Backward of the LN above: dY (bf16 or fp32) from dOut [R, d] fp32; dg, db
 // accumulated (+=) over the rows through per-block partials `part`
 // (2 * ln_part_rows(R) * d floats).  g == nullptr: dY = dOut.
 int64_t ln_part_rows(int64_t R);
 hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, int64_t R, int d, const float *g,
-                         void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s);
+                         void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s,
+                         const int *dev_rows = nullptr);
 // dst[r, :] (+)= src[r, :] over a [R, d] block with row strides.
 hipError_t launch_add_rows(const float *src, int64_t lds, float *dst, int64_t ldd, int64_t R, int d, bool accumulate,
                            hipStream_t s);
@@ -60,7 +89,7 @@ hipError_t launch_add_rows(const float *src, int64_t lds, float *dst, int64_t ld
 hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float *dst, hipStream_t s);
 // table[ids[r], :] += rows[r, :] (atomic), ids outside the table skipped.
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
-                              hipStream_t s);
+                              hipStream_t s, const int *dev_rows = nullptr);
 
 // ------------------------------------------------------------ attention backward
 // Inputs per layer, all token-indexed: Q (scaled, bf16 [T, d]), K and V rows
@@ -82,8 +111,35 @@ struct AttnBwdArgs {
   float *part_dq;   // [max_chunks * H * 4 * 64 * dh] scratch
   float *dq;
   bf16_t *dkv;
+  // optional: K and V through the unique rows (STCA_FLAG_DEDUP): k is the
+  // unique rows' blocked K [row / 32][H][32][d_h], v their V rows [row][d],
+  // tok2u[n_hist] the unique row of every history item
+  const int *tok2u;
 };
 int64_t attn_bwd_part_floats(int64_t max_chunks, int H, int dh);
 hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
+
+// ------------------------------------------------------------ per-unique sums
+// out[u] = sum over the items j with tok2u[j] = u, in item order, of dkv[j]
+// (fp32 accumulation, bf16 out), u < *n_unique.
+struct UniqueSumArgs {
+  int64_t n;              // history items
+  int64_t max_u;          // host bound on the unique rows
+  const int *tok2u;       // [n]
+  const int *n_unique;    // device count
+  int *keys[2], *vals[2]; // [n] ints each (scratch)
+  int *hist;              // sort_hist_ints(n) ints (scratch)
+  int *seg, *poff, *moff; // [max_u + 1] ints each (scratch)
+  const bf16_t *dkv;      // [n, d2]
+  int d2;
+  float *ppart;           // [agg_max_partials(n), d2] (scratch)
+  bf16_t *out;            // [max_u, d2]
+  const int *sorted_items;  // set by launch_unique_sort (points into vals)
+};
+int64_t agg_max_partials(int64_t n);
+// Once per batch: the items sorted by (unique row, item) and the run / piece
+// offsets; then per layer: the sums of that layer's dkv.
+hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s);
+hipError_t launch_unique_sums(const UniqueSumArgs &a, hipStream_t s);
 
 }  // namespace stca

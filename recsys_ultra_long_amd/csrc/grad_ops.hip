@@ -25,7 +25,8 @@ template <typename T> DEV void store(void *p, int64_t i, float v) { ((T *)p)[i] 
 
 __global__ __launch_bounds__(kT) void gather_kernel(const bf16_t *__restrict__ table, int64_t table_rows,
                                                     const int *__restrict__ ids, int64_t R, int d, void *out,
-                                                    bool out_bf16) {
+                                                    bool out_bf16, const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= R * d) return;
   const int64_t r = e / d;
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(kT) void gather_kernel(const bf16_t *__restrict__ t
 }
 
 __global__ __launch_bounds__(kT) void swiglu_fwd_kernel(const float *__restrict__ h13, int64_t R, int h, void *g,
-                                                        bool g_bf16) {
+                                                        bool g_bf16, const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= R * h) return;
   const int64_t r = e / h;
@@ -49,7 +51,9 @@ __global__ __launch_bounds__(kT) void swiglu_fwd_kernel(const float *__restrict_
 }
 
 __global__ __launch_bounds__(kT) void swiglu_bwd_kernel(const float *__restrict__ dg, const float *__restrict__ h13,
-                                                        int64_t R, int h, void *dh13, bool out_bf16) {
+                                                        int64_t R, int h, void *dh13, bool out_bf16,
+                                                        const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= R * h) return;
   const int64_t r = e / h;
@@ -74,7 +78,8 @@ constexpr int kLnRowsPerBlock = 4;
 
 __global__ __launch_bounds__(kT) void ln_fwd_kernel(const float *__restrict__ y, int64_t R, int d,
                                                     const float *__restrict__ g, const float *__restrict__ b, void *out,
-                                                    bool out_bf16, float *stats) {
+                                                    bool out_bf16, float *stats, const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
   if (r >= R) return;
@@ -100,7 +105,8 @@ __global__ __launch_bounds__(kT) void ln_fwd_kernel(const float *__restrict__ y,
 }
 
 __global__ __launch_bounds__(kT) void copy_rows_kernel(const float *__restrict__ y, int64_t n, void *out,
-                                                       bool out_bf16) {
+                                                       bool out_bf16, const int *dev_rows, int d) {
+  if (dev_rows) n = min(n, (int64_t)*dev_rows * d);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= n) return;
   if (out_bf16) store<bf16_t>(out, e, y[e]);
@@ -109,11 +115,13 @@ __global__ __launch_bounds__(kT) void copy_rows_kernel(const float *__restrict__
 
 // rows per LN-backward block, and its partial sums of dg, db
 constexpr int kLnBwdRows = 64;
+constexpr int kFoldSlices = 64;  // first fold stage: partial rows cut into this many slices
 
 __global__ __launch_bounds__(kT) void ln_bwd_kernel(const float *__restrict__ dout, const float *__restrict__ y,
                                                     const float *__restrict__ stats, int64_t R, int d,
                                                     const float *__restrict__ g, void *dy, bool dy_bf16,
-                                                    float *part) {
+                                                    float *part, const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   // block: kLnBwdRows rows, one wave per row at a time; per-lane column
   // partials of dg, db kept in LDS [4 waves][d] and folded in wave order
   extern __shared__ float sm[];
@@ -158,12 +166,30 @@ __global__ __launch_bounds__(kT) void ln_bwd_kernel(const float *__restrict__ do
   }
 }
 
-__global__ __launch_bounds__(kT) void ln_fold_kernel(const float *__restrict__ part, int64_t nblk, int d, float *dg,
-                                                     float *db) {
+// Two-stage fold of the per-block partials [nblk][2d], fixed order: stage 1,
+// block (column group of 64, slice) sums its slice of partial rows (4 waves
+// interleaved, then in wave order) into part2[slice][2d]; stage 2 sums the
+// slices in order.  Columns are read 64 at a time by a wave: coalesced.
+__global__ __launch_bounds__(kT) void ln_fold1_kernel(const float *__restrict__ part, int64_t nblk, int d,
+                                                      float *part2) {
+  __shared__ float sm[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int f = blockIdx.x * 64 + lane;
+  const int64_t per = (nblk + kFoldSlices - 1) / kFoldSlices;
+  const int64_t b0 = (int64_t)blockIdx.y * per, b1 = b0 + per < nblk ? b0 + per : nblk;
+  float s = 0.f;
+  if (f < 2 * d)
+    for (int64_t b = b0 + w; b < b1; b += 4) s += part[b * 2 * d + f];
+  sm[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && f < 2 * d) part2[(int64_t)blockIdx.y * 2 * d + f] = ((sm[0][lane] + sm[1][lane]) + sm[2][lane]) + sm[3][lane];
+}
+
+__global__ __launch_bounds__(kT) void ln_fold2_kernel(const float *__restrict__ part2, int d, float *dg, float *db) {
   const int f = blockIdx.x * kT + threadIdx.x;
   if (f >= 2 * d) return;
   float s = 0.f;
-  for (int64_t b = 0; b < nblk; ++b) s += part[b * 2 * d + f];
+  for (int i = 0; i < kFoldSlices; ++i) s += part2[(int64_t)i * 2 * d + f];
   if (f < d) dg[f] += s;
   else db[f - d] += s;
 }
@@ -189,7 +215,9 @@ __global__ __launch_bounds__(kT) void concat_kernel(const float *__restrict__ sr
 }
 
 __global__ __launch_bounds__(kT) void scatter_kernel(const float *__restrict__ rows, const int *__restrict__ ids,
-                                                     int64_t R, int d, float *table, int64_t table_rows) {
+                                                     int64_t R, int d, float *table, int64_t table_rows,
+                                                     const int *dev_rows) {
+  if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= R * d) return;
   const int64_t r = e / d;
@@ -203,52 +231,60 @@ unsigned blocks(int64_t n) { return (unsigned)((n + kT - 1) / kT); }
 }  // namespace
 
 hipError_t launch_gather_rows(const bf16_t *table, int64_t table_rows, const int *ids, int64_t R, int d, void *out,
-                              bool out_bf16, hipStream_t s) {
+                              bool out_bf16, hipStream_t s, const int *dev_rows) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, table, table_rows, ids, R, d, out, out_bf16);
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, table, table_rows, ids, R, d, out, out_bf16,
+                     dev_rows);
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_fwd(const float *h13, int64_t R, int h, void *g, bool g_bf16, hipStream_t s) {
+hipError_t launch_swiglu_fwd(const float *h13, int64_t R, int h, void *g, bool g_bf16, hipStream_t s,
+                             const int *dev_rows) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, h13, R, h, g, g_bf16);
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, h13, R, h, g, g_bf16, dev_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_swiglu_bwd(const float *dg, const float *h13, int64_t R, int h, void *dh13, bool out_bf16,
-                             hipStream_t s) {
+                             hipStream_t s, const int *dev_rows) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, dg, h13, R, h, dh13, out_bf16);
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(blocks(R * h)), dim3(kT), 0, s, dg, h13, R, h, dh13, out_bf16, dev_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_ln_fwd(const float *y, int64_t R, int d, const float *g, const float *b, void *out, bool out_bf16,
-                         float *stats, hipStream_t s) {
+                         float *stats, hipStream_t s, const int *dev_rows) {
   if (R <= 0) return hipSuccess;
   if (!g) {
-    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, y, R * d, out, out_bf16);
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, y, R * d, out, out_bf16, dev_rows, d);
   } else {
     const unsigned nb = (unsigned)((R + kLnRowsPerBlock - 1) / kLnRowsPerBlock);
-    hipLaunchKernelGGL(ln_fwd_kernel, dim3(nb), dim3(kT), 0, s, y, R, d, g, b, out, out_bf16, stats);
+    hipLaunchKernelGGL(ln_fwd_kernel, dim3(nb), dim3(kT), 0, s, y, R, d, g, b, out, out_bf16, stats, dev_rows);
   }
   return hipGetLastError();
 }
 
-int64_t ln_part_rows(int64_t R) { return (R + kLnBwdRows - 1) / kLnBwdRows; }
+int64_t ln_part_rows(int64_t R) { return (R + kLnBwdRows - 1) / kLnBwdRows + kFoldSlices; }
 
 hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, int64_t R, int d, const float *g,
-                         void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s) {
+                         void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s,
+                         const int *dev_rows) {
   if (R <= 0) return hipSuccess;
   if (!g) {
-    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, dout, R * d, dy, dy_bf16);
+    hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, dout, R * d, dy, dy_bf16, dev_rows, d);
     return hipGetLastError();
   }
-  const int64_t nblk = ln_part_rows(R);
+  const int64_t nblk = (R + kLnBwdRows - 1) / kLnBwdRows;
   hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)nblk), dim3(kT), 8 * d * sizeof(float), s, dout, y, stats, R, d, g,
-                     dy, dy_bf16, part);
+                     dy, dy_bf16, part, dev_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ln_fold_kernel, dim3(blocks(2 * d)), dim3(kT), 0, s, part, nblk, d, dg, db);
+  float *part2 = part + nblk * 2 * d;  // ln_part_rows() leaves room for the slices
+  hipLaunchKernelGGL(ln_fold1_kernel, dim3((unsigned)((2 * d + 63) / 64), kFoldSlices), dim3(kT), 0, s, part, nblk,
+                     d, part2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ln_fold2_kernel, dim3(blocks(2 * d)), dim3(kT), 0, s, part2, d, dg, db);
   return hipGetLastError();
 }
 
@@ -266,9 +302,10 @@ hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float
 }
 
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
-                              hipStream_t s) {
+                              hipStream_t s, const int *dev_rows) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, ids, R, d, table, table_rows);
+  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, ids, R, d, table, table_rows,
+                     dev_rows);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@
 #include <cstring>
 #include <vector>
 
+#include "grad_internal.h"
 #include "stca.h"
 #include "stca_internal.h"
 
@@ -92,7 +93,7 @@ struct Layout {
   size_t prow = 0;         // staged bf16: padded-row id map (0 = none)
   bool dedup = false;      // STCA_FLAG_DEDUP: encoder over the unique ids
   int64_t drows = 0, dslots = 0;
-  size_t d_keys = 0, d_slot = 0, d_bcnt = 0, d_boff = 0, d_uniq = 0, d_tok2u = 0, d_small = 0;
+  size_t d_keys = 0, d_slot = 0, d_bcnt = 0, d_boff = 0, d_uniq = 0, d_tok2u = 0, d_small = 0, d_sort = 0;
   size_t ukv = 0, ukv_layer = 0, vrows = 0;
   size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0, fstate = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
@@ -264,6 +265,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
     L.d_uniq = cv.take(sizeof(int) * (size_t)L.drows);
     L.d_tok2u = cv.take(sizeof(int) * (size_t)b->n_hist);
     L.d_small = cv.take(sizeof(int) * 8);
+    L.d_sort = cv.take(sizeof(int) * (size_t)L.drows * 6 + sizeof(int) * (size_t)radix_hist_ints(L.drows));
     L.ukv_layer = (size_t)L.drows * d * 2;  // K or V of the unique rows, one layer
     L.ukv = cv.take(2 * L.ukv_layer * c->M);
     L.vrows = cv.take(L.ukv_layer * c->M);  // each layer's unique V, row-major
@@ -348,9 +350,14 @@ int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t 
   return STCA_OK;
 }
 
-int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
-                 const stca_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace stca {
+
+int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                           const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi) {
   g_err[0] = 0;
+  if (fi) std::memset(fi, 0, sizeof(*fi));
   int r = validate_cfg(cfg);
   if (r) return r;
   if ((r = validate_batch(cfg, batch))) return r;
@@ -583,6 +590,17 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     da.uplan_toff = small + 3;
     da.uplan_pblk = small + 5;
     da.status = out->dev_status;
+    {
+      int *sb = at<int>(ws, L.d_sort);
+      const size_t nr = (size_t)L.drows;
+      da.sort_in = sb;
+      da.sort_keys[0] = sb + nr;
+      da.sort_keys[1] = sb + 2 * nr;
+      da.sort_vals[0] = sb + 3 * nr;
+      da.sort_vals[1] = sb + 4 * nr;
+      da.perm = sb + 5 * nr;
+      da.sort_hist = sb + 6 * nr;
+    }
     if ((e = launch_dedup(da, s))) return hip_fail(e, "id dedup");
     uplan.hoff = da.uplan_hoff;
     uplan.toff = da.uplan_toff;
@@ -591,6 +609,16 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
     uplan.prow = da.uniq_rows;
     n_unique = da.n_unique;
     tok2u = da.tok2u;
+    if (fi) {
+      fi->dedup = true;
+      fi->tok2u = tok2u;
+      fi->uniq_rows = da.uniq_rows;
+      fi->n_unique = n_unique;
+      fi->drows = L.drows;
+      fi->ukv = (const bf16_t *)ukvbase;
+      fi->ukv_layer_elems = L.ukv_layer / 2;
+      fi->vrows = at<bf16_t>(ws, L.vrows);
+    }
   }
   // the encoder's view of the rows: the batch, or the unique ids
   auto enc_args = [&](int i) {
@@ -797,6 +825,15 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
   }
   if ((e = rec(2 + 5 * M))) return hip_fail(e, "stage event");
   return STCA_OK;
+}
+
+}  // namespace stca
+
+extern "C" {
+
+int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                 const stca_outputs *out, void *ws, size_t ws_bytes, void *stream) {
+  return forward_with_internals(cfg, batch, w, out, ws, ws_bytes, stream, nullptr);
 }
 
 // ---------------------------------------------------------------- attention only

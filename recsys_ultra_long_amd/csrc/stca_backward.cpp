@@ -57,13 +57,16 @@ struct BwdLayout {
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
   size_t ln_part = 0, gemm_part = 0;
   int64_t max_chunks = 0;
+  // STCA_FLAG_DEDUP: the history backward runs over Rh = drows unique rows
+  bool dedup = false;
+  int64_t Rh = 0;
+  size_t keys0 = 0, keys1 = 0, vals0 = 0, vals1 = 0, hist = 0, seg = 0, poff = 0, moff = 0, ppart = 0, dKVu = 0;
   size_t total = 0;
 };
 
 stca_config forward_cfg(const stca_config *c) {
   stca_config f = *c;
-  f.path = STCA_PATH_STAGED;
-  f.flags &= ~STCA_FLAG_DEDUP;
+  f.path = STCA_PATH_STAGED;  // STCA_FLAG_DEDUP is kept: the recompute then encodes unique rows
   return f;
 }
 
@@ -90,6 +93,9 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   if (r) return r;
   const int64_t d = cfg->d, h = cfg->hidden, M = cfg->M, H = cfg->H, dh = d / H;
   const int64_t T = b->n_tgt, R = b->n_hist;
+  L.dedup = (cfg->flags & STCA_FLAG_DEDUP) && R > 0;
+  const int64_t Rh = L.dedup ? dedup_rows(R) : R;  // rows of the history backward
+  L.Rh = Rh;
   Carver cv;
   L.fws_bytes = fws;
   L.fws = cv.take(fws);
@@ -97,7 +103,7 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.o = cv.take(M * T * d * 4);
   L.attn = cv.take(M * T * d * 4);
   L.q = cv.take(M * T * d * 2);
-  L.kv = cv.take(M * 2 * R * d * 2);
+  L.kv = cv.take(L.dedup ? 0 : M * 2 * R * d * 2);  // dedup: K/V read through the unique rows
   L.lse = cv.take(M * T * H * 4);
   L.plan = cv.take(4 * sizeof(int) * (size_t)(cfg->B + 1));
   L.xt = cv.take(T * d * 4);
@@ -120,20 +126,32 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.dsum = cv.take(T * H * 4);
   L.max_chunks = max_chunks(R, cfg->B, kBwdChunkBlocks);
   L.part_dq = cv.take((size_t)attn_bwd_part_floats(L.max_chunks, (int)H, (int)dh) * 4);
-  L.X = cv.take(R * d * 2);
-  L.H13 = cv.take(R * 2 * h * 4);
-  L.G = cv.take(R * h * 2);
-  L.Y = cv.take(R * d * 4);
-  L.ST = cv.take(R * 2 * 4);
-  L.XT = cv.take(R * d * 2);
   L.dKV = cv.take(R * 2 * d * 2);
-  L.dXT = cv.take(R * d * 4);
-  L.dY = cv.take(R * d * 2);
-  L.dG = cv.take(R * h * 4);
-  L.dH13 = cv.take(R * 2 * h * 2);
-  L.dX = cv.take(R * d * 4);
-  L.ln_part = cv.take((size_t)2 * ln_part_rows(std::max(R, T)) * d * 4);
-  L.gemm_part = cv.take((size_t)part_floats_needed(d, h, M, R, T) * 4);
+  L.X = cv.take(Rh * d * 2);
+  L.H13 = cv.take(Rh * 2 * h * 4);
+  L.G = cv.take(Rh * h * 2);
+  L.Y = cv.take(Rh * d * 4);
+  L.ST = cv.take(Rh * 2 * 4);
+  L.XT = cv.take(Rh * d * 2);
+  L.dXT = cv.take(Rh * d * 4);
+  L.dY = cv.take(Rh * d * 2);
+  L.dG = cv.take(Rh * h * 4);
+  L.dH13 = cv.take(Rh * 2 * h * 2);
+  L.dX = cv.take(Rh * d * 4);
+  if (L.dedup) {
+    L.keys0 = cv.take(R * 4);
+    L.keys1 = cv.take(R * 4);
+    L.vals0 = cv.take(R * 4);
+    L.vals1 = cv.take(R * 4);
+    L.hist = cv.take((size_t)radix_hist_ints(R) * 4);
+    L.seg = cv.take((size_t)(Rh + 1) * 4);
+    L.poff = cv.take((size_t)(Rh + 1) * 4);
+    L.moff = cv.take((size_t)(Rh + 1) * 4);
+    L.ppart = cv.take((size_t)agg_max_partials(R) * 2 * d * 4);
+    L.dKVu = cv.take(Rh * 2 * d * 2);
+  }
+  L.ln_part = cv.take((size_t)2 * ln_part_rows(std::max(Rh, T)) * d * 4);
+  L.gemm_part = cv.take((size_t)part_floats_needed(d, h, M, Rh, T) * 4);
   L.total = cv.off;
   return STCA_OK;
 }
@@ -164,6 +182,9 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
       return api_error(STCA_ERR_INVALID_ARG, "gradient buffer NULL (layer %d)", i);
   }
   if (!ffn_ok(g->z, zln) || !g->wz) return api_error(STCA_ERR_INVALID_ARG, "z gradient buffer NULL");
+  if ((c->flags & STCA_FLAG_DEDUP) && g->d_hist)
+    return api_error(STCA_ERR_UNSUPPORTED,
+                     "d_hist is not available with STCA_FLAG_DEDUP (the history backward runs per unique row)");
   const void *p16[] = {g->table, g->d_hist, g->d_tgt, g->z_out, g->dq_dump, g->da_dump, g->dkv_dump};
   for (const void *p : p16)
     if (p && !aligned16(p)) return api_error(STCA_ERR_INVALID_ARG, "gradient output %p not 16-byte aligned", p);
@@ -217,10 +238,13 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   fo.o_layers = o_all;
   fo.attn = a_all;
   fo.q_dump = q_all;
-  fo.kv_dump = kv_all;
+  fo.kv_dump = L.dedup ? nullptr : kv_all;
   fo.lse = cfg->score == STCA_SCORE_SOFTMAX ? lse_all : nullptr;
   fo.dev_status = gr->dev_status;
-  if ((r = stca_forward(&fc, batch, w, &fo, at<void>(ws, L.fws), L.fws_bytes, stream))) return r;
+  ForwardInternals fi;
+  if ((r = forward_with_internals(&fc, batch, w, &fo, at<void>(ws, L.fws), L.fws_bytes, stream, &fi))) return r;
+  const int64_t Rh = L.Rh;
+  const int *hdev = L.dedup ? fi.n_unique : nullptr;  // device cap on the history backward's rows
 
   float *dX = gr->d_hist ? gr->d_hist : at<float>(ws, L.dX);
   float *dxt = gr->d_tgt ? gr->d_tgt : at<float>(ws, L.dxt);
@@ -246,6 +270,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   }
 
   // ---- GEMM helper: C = alpha * A B + beta * C with explicit strides
+  const int *gdev = nullptr;  // device cap applied by gemm(): rows (M) or, for split products, K
   auto gemm = [&](int64_t Mm, int64_t Nn, int64_t Kk, const void *A, bool abf, int64_t sam, int64_t sak,
                   const void *Bp, bool bbf, int64_t sbk, int64_t sbn, float *C, int64_t scm, int64_t scn, float alpha,
                   float beta, bool split) -> hipError_t {
@@ -268,6 +293,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     g.beta = beta;
     g.split = split ? gemm_split_for(Mm, Nn, Kk) : 1;
     g.part = gpart;
+    g.dev_rows = gdev;
+    g.dev_dim = gdev ? (split ? 2 : 1) : 0;
     return launch_gemm(g, s);
   };
   // ---- 2. planner for the attention backward (its own chunking)
@@ -344,8 +371,29 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   float *dG = at<float>(ws, L.dG);
   bf16_t *G = at<bf16_t>(ws, L.G), *XT = at<bf16_t>(ws, L.XT), *dY = at<bf16_t>(ws, L.dY);
   bf16_t *dH13 = at<bf16_t>(ws, L.dH13);
-  if (R > 0 && (e = launch_gather_rows(table, cfg->table_rows, batch->hist_ids, R, d, X, true, s)))
+  const int *hids = L.dedup ? fi.uniq_rows : batch->hist_ids;
+  if (R > 0 && (e = launch_gather_rows(table, cfg->table_rows, hids, Rh, d, X, true, s, hdev)))
     return hip_err("history gather");
+  UniqueSumArgs ua;
+  std::memset(&ua, 0, sizeof(ua));
+  if (L.dedup) {  // items in (unique row, item) order, once for every layer
+    ua.n = R;
+    ua.max_u = Rh;
+    ua.tok2u = fi.tok2u;
+    ua.n_unique = fi.n_unique;
+    ua.keys[0] = at<int>(ws, L.keys0);
+    ua.keys[1] = at<int>(ws, L.keys1);
+    ua.vals[0] = at<int>(ws, L.vals0);
+    ua.vals[1] = at<int>(ws, L.vals1);
+    ua.hist = at<int>(ws, L.hist);
+    ua.seg = at<int>(ws, L.seg);
+    ua.poff = at<int>(ws, L.poff);
+    ua.moff = at<int>(ws, L.moff);
+    ua.d2 = 2 * d;
+    ua.ppart = at<float>(ws, L.ppart);
+    ua.out = at<bf16_t>(ws, L.dKVu);
+    if ((e = launch_unique_sort(ua, s))) return hip_err("unique sort");
+  }
 
   // ---- 4. layers, last to first
   for (int i = M - 1; i >= 0; --i) {
@@ -374,8 +422,14 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       ab.plan = plan;
       ab.max_chunks = L.max_chunks;
       ab.q = q_all + (size_t)i * T * d;
-      ab.k = kv_all + (size_t)i * 2 * R * d;
-      ab.v = ab.k + (size_t)R * d;
+      if (L.dedup) {
+        ab.k = fi.ukv + (size_t)2 * i * fi.ukv_layer_elems;
+        ab.v = fi.vrows + (size_t)i * fi.drows * d;
+        ab.tok2u = fi.tok2u;
+      } else {
+        ab.k = kv_all + (size_t)i * 2 * R * d;
+        ab.v = ab.k + (size_t)R * d;
+      }
       ab.a = a_i;
       ab.da = da;
       ab.lse = lse_all + (size_t)i * T * H;
@@ -413,42 +467,52 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     } else {
       if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
     }
-    // history side of layer i over the R history items
+    // history side of layer i, over the history items or (dedup) the unique
+    // rows with each row's dK | dV summed over its items
     if (R > 0) {
+      const bf16_t *dkvh = dkv;
+      if (L.dedup) {
+        ua.dkv = dkv;
+        if ((e = launch_unique_sums(ua, s))) return hip_err("unique sums");
+        dkvh = ua.out;
+      }
       const stca_ffn &f = lw.kv;
       const stca_ffn_grad &fg = lg.kv;
-      if ((e = gemm(R, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h1");
-      if ((e = gemm(R, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h3");
-      if ((e = launch_swiglu_fwd(H13, R, h, G, true, s))) return hip_err("swiglu");
-      if ((e = gemm(R, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, false))) return hip_err("y");
-      if ((e = launch_ln_fwd(Y, R, d, kvln ? f.ln_g : nullptr, f.ln_b, XT, true, ST, s))) return hip_err("ln");
+      gdev = hdev;
+      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h1");
+      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h3");
+      if ((e = launch_swiglu_fwd(H13, Rh, h, G, true, s, hdev))) return hip_err("swiglu");
+      if ((e = gemm(Rh, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, false))) return hip_err("y");
+      if ((e = launch_ln_fwd(Y, Rh, d, kvln ? f.ln_g : nullptr, f.ln_b, XT, true, ST, s, hdev))) return hip_err("ln");
       // dXt = dK W_K^T + dV W_V^T; dW_K += Xt^T dK, dW_V += Xt^T dV
-      if ((e = gemm(R, d, d, dkv, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, false))) return hip_err("dxt");
-      if ((e = gemm(R, d, d, dkv + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, false))) return hip_err("dxt");
+      if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, false)))
         return hip_err("dxt");
-      if ((e = gemm(d, d, R, XT, true, 1, d, dkv, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, true))) return hip_err("dWk");
-      if ((e = gemm(d, d, R, XT, true, 1, d, dkv + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, true)))
+      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, true))) return hip_err("dWk");
+      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, true)))
         return hip_err("dWv");
-      if ((e = launch_ln_bwd(dXT, Y, ST, R, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart, s)))
+      if ((e = launch_ln_bwd(dXT, Y, ST, Rh, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart, s, hdev)))
         return hip_err("ln backward");
       // dG = dY W2^T, dW2 += G^T dY
-      if ((e = gemm(R, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, false))) return hip_err("dg");
-      if ((e = gemm(h, d, R, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, true))) return hip_err("dW2");
-      if ((e = launch_swiglu_bwd(dG, H13, R, h, dH13, true, s))) return hip_err("swiglu backward");
-      if ((e = gemm(d, h, R, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, true))) return hip_err("dW1");
-      if ((e = gemm(d, h, R, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, true)))
+      if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, false))) return hip_err("dg");
+      if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, true))) return hip_err("dW2");
+      if ((e = launch_swiglu_bwd(dG, H13, Rh, h, dH13, true, s, hdev))) return hip_err("swiglu backward");
+      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, true))) return hip_err("dW1");
+      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, true)))
         return hip_err("dW3");
       const float beta0 = i == M - 1 ? 0.f : 1.f;
-      if ((e = gemm(R, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, false)))
+      if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, false)))
         return hip_err("dx");
-      if ((e = gemm(R, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(Rh, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, false)))
         return hip_err("dx");
+      gdev = nullptr;
     }
   }
 
   // ---- 5. row gradients into the table
   if (gr->table) {
-    if ((e = launch_scatter_add(dX, batch->hist_ids, R, d, gr->table, cfg->table_rows, s))) return hip_err("scatter");
+    if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev)))
+      return hip_err("scatter");
     if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s))) return hip_err("scatter");
   }
   return STCA_OK;

@@ -215,6 +215,20 @@ hipError_t launch_fused256(const ChainArgs &a, AttnArgs &at, int64_t max_tiles, 
 // then runs on a one-user plan over the unique ids (uplan_*, prow =
 // uniq_rows, padded with -1 to whole 128-row tiles), and each layer's K/V of
 // the tokens is expanded from the unique rows.
+// ------------------------------------------------------------ radix sort
+// Stable LSD radix sort (8-bit digits) of n (key, value) pairs by the low
+// `bits` bits of the keys (keys >= 0).  vin == nullptr: the values are the
+// item indices.  keys[2], vals[2]: [n] ints each, hist: radix_hist_ints(n)
+// ints (scratch).  The sorted pairs are at res->keys / res->vals (inside
+// the scratch, or the inputs when bits == 0).
+struct RadixResult {
+  const int *keys, *vals;
+};
+int64_t radix_hist_ints(int64_t n);
+int radix_bits(int64_t max_key);  // bits that cover keys 0 .. max_key
+hipError_t launch_radix_sort(const int *kin, const int *vin, int64_t n, int bits, int *keys[2], int *vals[2],
+                             int *hist, RadixResult *res, hipStream_t s);
+
 struct DedupArgs {
   const int *ids;
   int64_t n_hist, table_rows;
@@ -226,6 +240,10 @@ struct DedupArgs {
   int *n_unique;             // [1]
   int *uplan_hoff, *uplan_toff, *uplan_pblk;  // [2] each
   int *status;
+  // renumbering of the unique rows in increasing id order (the slot order a
+  // concurrent insert leaves is not reproducible), dedup_rows(n_hist) ints
+  // each, and radix_hist_ints(dedup_rows(n_hist)) for the histogram
+  int *sort_in, *sort_keys[2], *sort_vals[2], *sort_hist, *perm;
 };
 inline int64_t dedup_rows(int64_t n_hist) { return ((n_hist + 127) / 128 + 1) * 128; }
 inline int64_t dedup_slots(int64_t n_hist) {

@@ -13,7 +13,11 @@ Checks:
   exactly the same weight gradients again; users without history or targets;
 * full size (training workload, every user present): dz nonzero for a few
   sampled users only, so the weight gradients equal those users' own
-  contributions, which the oracle computes.
+  contributions, which the oracle computes;
+* unique-id dedup (STCA_FLAG_DEDUP): the history backward once per distinct
+  id on the summed dK | dV of its items -- against the oracle on every
+  workload above, bitwise repeatable, with out-of-range ids, and at full
+  size.
 """
 import numpy as np
 import pytest
@@ -38,9 +42,11 @@ def rel_fro(g, o):
     return float(np.linalg.norm(g - o) / den) if den > 0 else float(np.linalg.norm(g))
 
 
-def gpu_backward(p, dz, outputs=("table", "d_hist", "d_tgt", "z"), dumps=(), calls=1, zero=True):
+def gpu_backward(p, dz, outputs=("table", "d_hist", "d_tgt", "z"), dumps=(), calls=1, zero=True, dedup=False):
     from recsys_ultra_long_amd import stca
-    dp = stca.upload(p)
+    dp = stca.upload(p, dedup=dedup)
+    if dedup:
+        outputs = tuple(o for o in outputs if o != "d_hist")
     dzt = torch.from_numpy(np.ascontiguousarray(dz, dtype=np.float32)).cuda()
     bw = stca.Backward(dp, dzt, outputs=outputs, dumps=dumps)
     if zero:
@@ -79,7 +85,8 @@ def compare_all(p, g, ref, tol=TOL, table=True):
     errs = {}
     for path, o in leaves(ref["grads"]):
         errs["/".join(map(str, path))] = rel_fro(get(g["grads"], path), o)
-    errs["d_hist"] = rel_fro(g["d_hist"], ref["d_hist"])
+    if g["d_hist"] is not None:
+        errs["d_hist"] = rel_fro(g["d_hist"], ref["d_hist"])
     errs["d_tgt"] = rel_fro(g["d_tgt"], ref["d_tgt"])
     if table:
         sp = p.spec
@@ -210,4 +217,68 @@ def test_backward_fullsize_training_sampled():
     g = gpu_backward(p, dz, outputs=("d_hist", "d_tgt"))
     ref = OG.backward_problem(p, dz, users=users)
     assert g["status"] == 0
+    compare_all(p, g, ref, table=False)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 6])
+def test_backward_dedup_matches_oracle(k):
+    p = I.make_problem(_small(k))
+    dz = I.upstream_grad(p.spec, p.n_tgt)
+    print(f"[bwd-dedup] workload {k}: n_hist={p.n_hist} unique={len(np.unique(p.hist_ids))}", flush=True)
+    g = gpu_backward(p, dz, dedup=True)
+    ref = OG.backward_problem(p, dz)
+    assert g["status"] == 0
+    compare_all(p, g, ref)
+
+
+def test_backward_dedup_repeatable_and_close_to_plain():
+    """Fixed-order sums: two dedup runs are bitwise equal; against the plain
+    path the gradients differ only by where bf16 rounding happens."""
+    p = I.make_problem(_small(6, B=6))
+    dz = I.upstream_grad(p.spec, p.n_tgt)
+    g1 = gpu_backward(p, dz, outputs=(), dedup=True)
+    g2 = gpu_backward(p, dz, outputs=(), dedup=True)
+    g0 = gpu_backward(p, dz, outputs=())
+    worst = 0.0
+    for path, v in leaves(g1["grads"]):
+        assert np.array_equal(get(g2["grads"], path), v), path
+        worst = max(worst, rel_fro(v, get(g0["grads"], path)))
+    print(f"[bwd-dedup] dedup vs plain: worst {worst:.2e}", flush=True)
+    assert worst < 1e-2
+
+
+def test_backward_dedup_out_of_range_ids():
+    p = I.make_problem(_small(3, B=2, L=300, m=8))
+    p.hist_ids[[5, 77, 78]] = p.spec.table_rows + 11      # one bad id, three items
+    dz = I.upstream_grad(p.spec, p.n_tgt)
+    from recsys_ultra_long_amd import stca
+    g = gpu_backward(p, dz, dedup=True)
+    assert g["status"] & stca.DEV_BAD_ID
+    ref = OG.backward_problem(p, dz)
+    compare_all(p, g, ref)
+
+
+def test_backward_dedup_fullsize_training_sampled():
+    sp = I.spec(6)
+    p = I.make_problem(sp, threads=16)
+    L = np.diff(p.hist_offsets)
+    users = sorted({0, int(np.argmax(L)), int(np.argmin(L))})
+    dz = np.zeros((p.n_tgt, sp.d), np.float32)
+    full = I.upstream_grad(sp, p.n_tgt)
+    for u in users:
+        dz[p.tgt_offsets[u]:p.tgt_offsets[u + 1]] = full[p.tgt_offsets[u]:p.tgt_offsets[u + 1]]
+    g = gpu_backward(p, dz, outputs=("d_tgt", "table"), dedup=True)
+    ref = OG.backward_problem(p, dz, users=users)
+    assert g["status"] == 0
+    # the table gradient of the sampled users' rows (other rows get nothing)
+    tg = np.zeros((sp.table_rows, sp.d))
+    for u in users:
+        ids = p.hist_ids[p.hist_offsets[u]:p.hist_offsets[u + 1]]
+        np.add.at(tg, ids, ref["d_hist"][p.hist_offsets[u]:p.hist_offsets[u + 1]])
+        tids = p.tgt_ids[p.tgt_offsets[u]:p.tgt_offsets[u + 1]]
+        np.add.at(tg, tids, ref["d_tgt"][p.tgt_offsets[u]:p.tgt_offsets[u + 1]])
+    rows = np.unique(np.concatenate([p.hist_ids, p.tgt_ids]))
+    err_t = rel_fro(g["table"][rows], tg[rows])
+    print(f"[bwd-dedup] full size table rows err {err_t:.2e}", flush=True)
+    assert err_t <= TOL
     compare_all(p, g, ref, table=False)
