@@ -123,7 +123,7 @@ def bench_backward(args):
     dz_np = I.upstream_grad(sp, p.n_tgt)
     dz = torch.from_numpy(dz_np).cuda()
     dp_f = stca.upload(p, path="fused")
-    dp_b = stca.upload(p, table=dp_f.table)
+    dp_b = stca.upload(p, table=dp_f.table, dedup=args.dedup)
     f = stca.Forward(dp_f, want=(), dumps=())
     bw = stca.Backward(dp_b, dz, outputs=("table",))
     log(f"backward workspace {bw.ws_bytes / 2**30:.2f} GiB")
@@ -169,7 +169,9 @@ def bench_backward(args):
         "config": {"workload": f"{sp.name}: B={sp.B} users, L ~ max(16, ceil(10240 Beta({sp.beta_a},1))) "
                                f"(sum {n_hist}), m={sp.m} targets/user, table {sp.table_rows}x{d} bf16 "
                                f"Zipf({sp.zipf_s}) ids, d={d}, H={sp.H}, hidden={h}, M={M}, softmax; "
-                               "forward on the fused path, backward recomputes on the staged path",
+                               "forward on the fused path, backward recomputes on the staged path"
+                               + (f", unique-id dedup of the history side ({len(np.unique(p.hist_ids))} unique "
+                                  f"of {n_hist})" if args.dedup else ""),
                    "global_batch": sp.B, "targets": T, "parallelism": "single GPU"},
         "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
         "backward_flops": {"proper": flops_b, "recompute": flops_f},

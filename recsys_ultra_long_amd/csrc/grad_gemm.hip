@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
       if (m0 >= Meff) return;  // the whole workgroup: before any barrier
     } else if (g.dev_dim == 2 && lim < ke) {
       ke = lim;
+      if (SPLIT && kb >= ke) return;  // a range past the device count: the fold skips it
     }
   }
   const TA *A = (const TA *)g.A;
@@ -177,9 +178,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
     }
 }
 
-__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split) {
+// Folds the K ranges in order; with a device cap on K only the ranges that
+// start below it were written.
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split, int64_t kchunk) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= g.M * g.N) return;
+  if (g.dev_rows && g.dev_dim == 2 && kchunk > 0) {
+    const int64_t lim = *g.dev_rows;
+    const int64_t live = (lim + kchunk - 1) / kchunk;
+    if (live < split) split = (int)live;
+  }
   const int64_t m = e / g.N, n = e % g.N;
   float s = 0.f;
   for (int z = 0; z < split; ++z) s += g.part[(int64_t)z * g.M * g.N + e];
@@ -198,12 +206,13 @@ hipError_t run(const GemmArgs &g, hipStream_t s) {
     int64_t kchunk = (g.K + g.split - 1) / g.split;
     kchunk = (kchunk + BK - 1) / BK * BK;
     const int split = (int)((g.K + kchunk - 1) / kchunk);
+    if (!g.part || (int64_t)split * g.M * g.N > g.part_cap) return hipErrorInvalidValue;
     hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, true>), dim3(gx, gy, split), dim3(256), 0, s, g, kchunk, va,
                        vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = g.M * g.N;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, split);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, split, kchunk);
   } else {
     hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, false>), dim3(gx, gy, 1), dim3(256), 0, s, g, g.K, va, vb);
   }
@@ -221,11 +230,11 @@ hipError_t run_layout(const GemmArgs &g, hipStream_t s) {
 
 }  // namespace
 
-int gemm_split_for(int64_t M, int64_t N, int64_t K) {
+int gemm_split_for(int64_t M, int64_t N, int64_t K, int64_t target, int64_t min_chunk) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   int64_t split = 1;
-  // aim at ~1024 workgroups, each with at least 512 of K
-  while (tiles * split < 1024 && K / (split * 2) >= 512) split *= 2;
+  // aim at `target` workgroups, each with at least min_chunk of K
+  while (tiles * split < target && K / (split * 2) >= min_chunk) split *= 2;
   return (int)split;
 }
 
@@ -240,7 +249,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
     if (g.beta == 1.f) return hipSuccess;
     // reuse the reduce kernel with zero partials: write alpha * 0 + beta * C
     z.part = nullptr;
-    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, z, 0);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, z, 0, (int64_t)0);
     return hipGetLastError();
   }
   if (g.a_bf16 && g.b_bf16) return run_layout<bf16_t, bf16_t>(g, s);

@@ -50,13 +50,14 @@ struct GemmArgs {
   float alpha, beta;
   int split;
   float *part;
+  int64_t part_cap;  // floats in `part`: a split needing more is refused
   const int *dev_rows;
   int dev_dim;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 // Split factor for a long-K product (weight gradients), and the partial
 // buffer it needs (floats).
-int gemm_split_for(int64_t M, int64_t N, int64_t K);
+int gemm_split_for(int64_t M, int64_t N, int64_t K, int64_t target = 1024, int64_t min_chunk = 128);
 inline int64_t gemm_part_floats(int64_t M, int64_t N, int split) { return split > 1 ? (int64_t)split * M * N : 0; }
 
 // ------------------------------------------------------------ row kernels

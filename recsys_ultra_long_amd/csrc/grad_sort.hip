@@ -42,29 +42,31 @@ __global__ __launch_bounds__(kT) void sort_hist_kernel(const int *__restrict__ k
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = c[threadIdx.x];
 }
 
-// exclusive scan of n ints in place (one workgroup)
+// exclusive scan of n ints in place (one workgroup): thread t sums its
+// contiguous chunk, the 1024 chunk sums are scanned in LDS, then every
+// thread writes its chunk's prefixes
 __global__ __launch_bounds__(1024) void scan_kernel(int *v, int64_t n, int *total) {
   __shared__ int sh[1024];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
+  const int t = threadIdx.x;
+  const int64_t C = (n + 1023) / 1024;
+  const int64_t i0 = (int64_t)t * C, i1 = i0 + C < n ? i0 + C : n;
+  int sum = 0;
+  for (int64_t i = i0; i < i1; ++i) sum += v[i];
+  sh[t] = sum;
   __syncthreads();
-  for (int64_t base = 0; base < n; base += 1024) {
-    const int64_t i = base + threadIdx.x;
-    const int x = i < n ? v[i] : 0;
-    sh[threadIdx.x] = x;
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int y = t >= o ? sh[t - o] : 0;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-      const int y = threadIdx.x >= o ? sh[threadIdx.x - o] : 0;
-      __syncthreads();
-      sh[threadIdx.x] += y;
-      __syncthreads();
-    }
-    if (i < n) v[i] = carry + sh[threadIdx.x] - x;
-    __syncthreads();
-    if (threadIdx.x == 0) carry += sh[1023];
+    sh[t] += y;
     __syncthreads();
   }
-  if (threadIdx.x == 0 && total) *total = carry;
+  int run = sh[t] - sum;
+  for (int64_t i = i0; i < i1; ++i) {
+    const int x = v[i];
+    v[i] = run;
+    run += x;
+  }
+  if (t == 1023 && total) *total = sh[1023];
 }
 
 __global__ __launch_bounds__(kT) void sort_scatter_kernel(const int *__restrict__ kin, const int *__restrict__ vin,

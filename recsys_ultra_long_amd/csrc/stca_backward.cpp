@@ -70,19 +70,34 @@ stca_config forward_cfg(const stca_config *c) {
   return f;
 }
 
+// Split-K choice: weight gradients (K = rows) aim at 2048 workgroups (the
+// rows may be capped on the device, leaving only part of them live); a
+// product over rows with few output tiles is split too (K = the width).
+int split_weight_grad(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 2048, 256); }
+int split_rows(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 512, 64); }
+
+// Largest split-K partial buffer any product of the backward asks for (its
+// GEMM refuses a split that would need more).
 int64_t part_floats_needed(int64_t d, int64_t h, int64_t M, int64_t R, int64_t T) {
   int64_t best = 0;
-  auto need = [&](int64_t m, int64_t n, int64_t k) {
-    const int sp = gemm_split_for(m, n, k);
+  auto need = [&](int64_t m, int64_t n, int64_t k, bool wg) {
+    const int sp = wg ? split_weight_grad(m, n, k) : split_rows(m, n, k);
     best = std::max(best, gemm_part_floats(m, n, sp));
   };
-  need(d, h, R);
-  need(h, d, R);
-  need(d, d, R);
-  need(d, h, T);
-  need(h, d, T);
-  need(d, d, T);
-  need(M * d, d, T);
+  for (int64_t rows : {R, T}) {  // weight gradients over the history items / targets
+    need(d, h, rows, true);
+    need(h, d, rows, true);
+    need(d, d, rows, true);
+  }
+  for (int64_t k = 1; k <= M; ++k) {  // fusion and z maps: [o_1..o_k] blocks of width k d
+    need(k * d, d, T, true);
+    need(T, d, k * d, false);
+    need(T, k * d, d, false);
+  }
+  // the query side's FFN and projections over the T target rows
+  need(T, h, d, false);
+  need(T, d, h, false);
+  need(T, d, d, false);
   return best;
 }
 
@@ -249,6 +264,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   float *dX = gr->d_hist ? gr->d_hist : at<float>(ws, L.dX);
   float *dxt = gr->d_tgt ? gr->d_tgt : at<float>(ws, L.dxt);
   float *gpart = at<float>(ws, L.gemm_part);
+  const int64_t gpart_cap = part_floats_needed(d, h, M, L.Rh, T);
   float *lnpart = at<float>(ws, L.ln_part);
   if (T == 0 || B == 0) {  // nothing reads the history: every gradient is zero
     if (gr->d_hist && R > 0) {  // K = 0 product: writes beta * C = 0
@@ -271,9 +287,14 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
 
   // ---- GEMM helper: C = alpha * A B + beta * C with explicit strides
   const int *gdev = nullptr;  // device cap applied by gemm(): rows (M) or, for split products, K
+  // kind: kWgrad = a weight gradient (K = rows, split along K); kTgt = a
+  // product over the target rows (split along the width when it has few
+  // output tiles); kHist = a product over the history rows (never split:
+  // thousands of tiles, and a device row cap under dedup)
+  enum { kHist = 0, kWgrad = 1, kTgt = 2 };
   auto gemm = [&](int64_t Mm, int64_t Nn, int64_t Kk, const void *A, bool abf, int64_t sam, int64_t sak,
                   const void *Bp, bool bbf, int64_t sbk, int64_t sbn, float *C, int64_t scm, int64_t scn, float alpha,
-                  float beta, bool split) -> hipError_t {
+                  float beta, int kind) -> hipError_t {
     GemmArgs g;
     g.M = Mm;
     g.N = Nn;
@@ -291,10 +312,11 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     g.scn = scn;
     g.alpha = alpha;
     g.beta = beta;
-    g.split = split ? gemm_split_for(Mm, Nn, Kk) : 1;
+    g.split = kind == kWgrad ? split_weight_grad(Mm, Nn, Kk) : kind == kTgt ? split_rows(Mm, Nn, Kk) : 1;
     g.part = gpart;
+    g.part_cap = gpart_cap;
     g.dev_rows = gdev;
-    g.dev_dim = gdev ? (split ? 2 : 1) : 0;
+    g.dev_dim = gdev ? (kind == kWgrad ? 2 : 1) : 0;
     return launch_gemm(g, s);
   };
   // ---- 2. planner for the attention backward (its own chunking)
@@ -321,10 +343,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   // h13 = x [W1 | W3], g = SiLU(h1) h3, y = g W2, out = LN(y) (or y).
   auto ffn_fwd = [&](int64_t n, const float *x, const stca_ffn &f, bool ln, float *out) -> hipError_t {
     hipError_t er;
-    if ((er = gemm(n, h, d, x, false, d, 1, f.w1, true, h, 1, h13, 2 * h, 1, 1.f, 0.f, false))) return er;
-    if ((er = gemm(n, h, d, x, false, d, 1, f.w3, true, h, 1, h13 + h, 2 * h, 1, 1.f, 0.f, false))) return er;
+    if ((er = gemm(n, h, d, x, false, d, 1, f.w1, true, h, 1, h13, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
+    if ((er = gemm(n, h, d, x, false, d, 1, f.w3, true, h, 1, h13 + h, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
     if ((er = launch_swiglu_fwd(h13, n, h, g, false, s))) return er;
-    if ((er = gemm(n, d, h, g, false, h, 1, f.w2, true, d, 1, y, d, 1, 1.f, 0.f, false))) return er;
+    if ((er = gemm(n, d, h, g, false, h, 1, f.w2, true, d, 1, y, d, 1, 1.f, 0.f, kTgt))) return er;
     if (ln) return launch_ln_fwd(y, n, d, f.ln_g, f.ln_b, out, false, st, s);
     return hipSuccess;
   };
@@ -338,30 +360,30 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       dyv = dy;
     }
     // dG = dY W2^T; dW2 += G^T dY
-    if ((er = gemm(n, h, d, dyv, false, d, 1, f.w2, true, 1, d, dg, h, 1, 1.f, 0.f, false))) return er;
-    if ((er = gemm(h, d, n, g, false, 1, h, dyv, false, d, 1, fg.w2, d, 1, 1.f, 1.f, true))) return er;
+    if ((er = gemm(n, h, d, dyv, false, d, 1, f.w2, true, 1, d, dg, h, 1, 1.f, 0.f, kTgt))) return er;
+    if ((er = gemm(h, d, n, g, false, 1, h, dyv, false, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return er;
     if ((er = launch_swiglu_bwd(dg, h13, n, h, dh13, false, s))) return er;
     // dW1 += x^T dH1, dW3 += x^T dH3
-    if ((er = gemm(d, h, n, x, false, 1, d, dh13, false, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, true))) return er;
-    if ((er = gemm(d, h, n, x, false, 1, d, dh13 + h, false, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, true))) return er;
+    if ((er = gemm(d, h, n, x, false, 1, d, dh13, false, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return er;
+    if ((er = gemm(d, h, n, x, false, 1, d, dh13 + h, false, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad))) return er;
     // dx = dH1 W1^T + dH3 W3^T
-    if ((er = gemm(n, d, h, dh13, false, 2 * h, 1, f.w1, true, 1, h, dx, d, 1, 1.f, 0.f, false))) return er;
-    return gemm(n, d, h, dh13 + h, false, 2 * h, 1, f.w3, true, 1, h, dx, d, 1, 1.f, 1.f, false);
+    if ((er = gemm(n, d, h, dh13, false, 2 * h, 1, f.w1, true, 1, h, dx, d, 1, 1.f, 0.f, kTgt))) return er;
+    return gemm(n, d, h, dh13 + h, false, 2 * h, 1, f.w3, true, 1, h, dx, d, 1, 1.f, 1.f, kTgt);
   };
 
   // ---- 3. z head: cz = [o_1..o_M | x_t] W_Z, z = SwiGLU_Z(cz) (+LN)
   {
-    if ((e = gemm(T, d, MD, ocat, false, MD, 1, w->wz, true, d, 1, c, d, 1, 1.f, 0.f, false))) return hip_err("z");
-    if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, false)))
+    if ((e = gemm(T, d, MD, ocat, false, MD, 1, w->wz, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("z");
+    if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
       return hip_err("z");
     if ((e = ffn_fwd(T, c, w->z, zln, qln))) return hip_err("z ffn");
     if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc))) return hip_err("z backward");
     // dW_Z += [o | x_t]^T dcz; d[o | x_t] = dcz W_Z^T
-    if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, true))) return hip_err("dWz");
-    if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, true)))
+    if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWz");
+    if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
       return hip_err("dWz");
-    if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, false))) return hip_err("do");
-    if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, false)))
+    if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
+    if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, kTgt)))
       return hip_err("dx_t");
   }
 
@@ -402,8 +424,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     const float *a_i = a_all + (size_t)i * T * d;
     float *do_i = docat + (size_t)i * d;
     // W_O: da = do W_O^T, dW_O += a^T do
-    if ((e = gemm(T, d, d, do_i, false, MD, 1, lw.wo, true, 1, d, da, d, 1, 1.f, 0.f, false))) return hip_err("da");
-    if ((e = gemm(d, d, T, a_i, false, 1, d, do_i, false, MD, 1, lg.wo, d, 1, 1.f, 1.f, true))) return hip_err("dWo");
+    if ((e = gemm(T, d, d, do_i, false, MD, 1, lw.wo, true, 1, d, da, d, 1, 1.f, 0.f, kTgt))) return hip_err("da");
+    if ((e = gemm(d, d, T, a_i, false, 1, d, do_i, false, MD, 1, lg.wo, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWo");
     if (gr->da_dump && (e = launch_add_rows(da, d, gr->da_dump + (size_t)i * T * d, d, T, d, false, s)))
       return hip_err("da dump");
     // attention backward
@@ -446,23 +468,23 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     const float *cin = xt;
     if (i > 0) {
       const int64_t K1 = (int64_t)i * d;
-      if ((e = gemm(T, d, K1, ocat, false, MD, 1, lw.wc, true, d, 1, c, d, 1, 1.f, 0.f, false))) return hip_err("wc");
-      if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, d, 1, c, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(T, d, K1, ocat, false, MD, 1, lw.wc, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("wc");
+      if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
         return hip_err("wc");
       cin = c;
     }
     if ((e = ffn_fwd(T, cin, lw.q, true, qln))) return hip_err("query ffn");
     // Q = q W_Q / sqrt(d_h): dW_Q += q^T dQ / sqrt(d_h), dq = dQ W_Q^T / sqrt(d_h)
-    if ((e = gemm(d, d, T, qln, false, 1, d, dq, false, d, 1, lg.wq, d, 1, qscale, 1.f, true))) return hip_err("dWq");
-    if ((e = gemm(T, d, d, dq, false, d, 1, lw.wq, true, 1, d, qln, d, 1, qscale, 0.f, false))) return hip_err("dq");
+    if ((e = gemm(d, d, T, qln, false, 1, d, dq, false, d, 1, lg.wq, d, 1, qscale, 1.f, kWgrad))) return hip_err("dWq");
+    if ((e = gemm(T, d, d, dq, false, d, 1, lw.wq, true, 1, d, qln, d, 1, qscale, 0.f, kTgt))) return hip_err("dq");
     if ((e = ffn_bwd(T, cin, lw.q, lg.q, true, qln, dc))) return hip_err("query backward");
     if (i > 0) {
       const int64_t K1 = (int64_t)i * d;
-      if ((e = gemm(K1, d, T, ocat, false, 1, MD, dc, false, d, 1, lg.wc, d, 1, 1.f, 1.f, true))) return hip_err("dWc");
-      if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, lg.wc + K1 * d, d, 1, 1.f, 1.f, true)))
+      if ((e = gemm(K1, d, T, ocat, false, 1, MD, dc, false, d, 1, lg.wc, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWc");
+      if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, lg.wc + K1 * d, d, 1, 1.f, 1.f, kWgrad)))
         return hip_err("dWc");
-      if ((e = gemm(T, K1, d, dc, false, d, 1, lw.wc, true, 1, d, docat, MD, 1, 1.f, 1.f, false))) return hip_err("do");
-      if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, 1, d, dxt, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(T, K1, d, dc, false, d, 1, lw.wc, true, 1, d, docat, MD, 1, 1.f, 1.f, kTgt))) return hip_err("do");
+      if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, 1, d, dxt, d, 1, 1.f, 1.f, kTgt)))
         return hip_err("dx_t");
     } else {
       if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
@@ -479,31 +501,31 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       const stca_ffn &f = lw.kv;
       const stca_ffn_grad &fg = lg.kv;
       gdev = hdev;
-      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h1");
-      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, false))) return hip_err("h3");
+      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
+      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h3");
       if ((e = launch_swiglu_fwd(H13, Rh, h, G, true, s, hdev))) return hip_err("swiglu");
-      if ((e = gemm(Rh, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, false))) return hip_err("y");
+      if ((e = gemm(Rh, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, kHist))) return hip_err("y");
       if ((e = launch_ln_fwd(Y, Rh, d, kvln ? f.ln_g : nullptr, f.ln_b, XT, true, ST, s, hdev))) return hip_err("ln");
       // dXt = dK W_K^T + dV W_V^T; dW_K += Xt^T dK, dW_V += Xt^T dV
-      if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, false))) return hip_err("dxt");
-      if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, kHist))) return hip_err("dxt");
+      if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, kHist)))
         return hip_err("dxt");
-      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, true))) return hip_err("dWk");
-      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, true)))
+      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWk");
+      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
         return hip_err("dWv");
       if ((e = launch_ln_bwd(dXT, Y, ST, Rh, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart, s, hdev)))
         return hip_err("ln backward");
       // dG = dY W2^T, dW2 += G^T dY
-      if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, false))) return hip_err("dg");
-      if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, true))) return hip_err("dW2");
+      if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, kHist))) return hip_err("dg");
+      if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
       if ((e = launch_swiglu_bwd(dG, H13, Rh, h, dH13, true, s, hdev))) return hip_err("swiglu backward");
-      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, true))) return hip_err("dW1");
-      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, true)))
+      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return hip_err("dW1");
+      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
         return hip_err("dW3");
       const float beta0 = i == M - 1 ? 0.f : 1.f;
-      if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, false)))
+      if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, kHist)))
         return hip_err("dx");
-      if ((e = gemm(Rh, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, false)))
+      if ((e = gemm(Rh, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, kHist)))
         return hip_err("dx");
       gdev = nullptr;
     }
