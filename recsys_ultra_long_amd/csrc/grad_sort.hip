@@ -42,10 +42,63 @@ __global__ __launch_bounds__(kT) void sort_hist_kernel(const int *__restrict__ k
   hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = c[threadIdx.x];
 }
 
-// exclusive scan of n ints in place (one workgroup): thread t sums its
-// contiguous chunk, the 1024 chunk sums are scanned in LDS, then every
-// thread writes its chunk's prefixes
-__global__ __launch_bounds__(1024) void scan_kernel(int *v, int64_t n, int *total) {
+// Exclusive scan of n ints in place, in three coalesced steps: each block
+// scans 1024 consecutive values (4 per thread) and leaves its total; one
+// workgroup scans the totals; each block adds its offset.
+constexpr int kScanB = 1024;
+
+DEV int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// exclusive scan of the 256 threads' values of a block; returns the block total
+DEV int block_excl_scan(int x, int &excl, int *sh) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int inc = wave_incl_scan(x, lane);
+  if (lane == 63) sh[w] = inc;
+  __syncthreads();
+  int off = 0;
+  for (int k = 0; k < w; ++k) off += sh[k];
+  const int total = sh[0] + sh[1] + sh[2] + sh[3];
+  excl = off + inc - x;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kT) void scan_local_kernel(int *v, int64_t n, int *totals) {
+  __shared__ int sh[4];
+  const int64_t i0 = (int64_t)blockIdx.x * kScanB + 4 * threadIdx.x;
+  int x[4], s = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = i0 + e < n ? v[i0 + e] : 0;
+    s += x[e];
+  }
+  int excl;
+  const int total = block_excl_scan(s, excl, sh);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (i0 + e < n) v[i0 + e] = excl;
+    excl += x[e];
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kT) void scan_add_kernel(int *v, int64_t n, const int *offs) {
+  const int64_t i0 = (int64_t)blockIdx.x * kScanB + 4 * threadIdx.x;
+  const int o = offs[blockIdx.x];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (i0 + e < n) v[i0 + e] += o;
+}
+
+// exclusive scan of a short array (one workgroup, chunk per thread)
+__global__ __launch_bounds__(1024) void scan_small_kernel(int *v, int64_t n) {
   __shared__ int sh[1024];
   const int t = threadIdx.x;
   const int64_t C = (n + 1023) / 1024;
@@ -66,7 +119,6 @@ __global__ __launch_bounds__(1024) void scan_kernel(int *v, int64_t n, int *tota
     v[i] = run;
     run += x;
   }
-  if (t == 1023 && total) *total = sh[1023];
 }
 
 __global__ __launch_bounds__(kT) void sort_scatter_kernel(const int *__restrict__ kin, const int *__restrict__ vin,
@@ -211,7 +263,23 @@ int bits_for(int64_t n) {
 int64_t agg_max_pieces(int64_t n, int64_t max_u) { return max_u + n / kPiece + 1; }
 int64_t agg_max_partials(int64_t n) { return 2 * (n / kPiece) + 2; }
 
-int64_t radix_hist_ints(int64_t n) { return 256 * ((n + kIPB - 1) / kIPB); }
+// scratch of excl_scan over n values: one total per block (the block totals
+// of any scan of up to 256 * n / kIPB + n values fit after the histogram)
+hipError_t excl_scan(int *v, int64_t n, int *tmp, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t nb = (n + kScanB - 1) / kScanB;
+  hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nb), dim3(kT), 0, s, v, n, tmp);
+  hipLaunchKernelGGL(scan_small_kernel, dim3(1), dim3(1024), 0, s, tmp, nb);
+  hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)nb), dim3(kT), 0, s, v, n, (const int *)tmp);
+  return hipGetLastError();
+}
+
+// histogram (256 per sort block) followed by room for the block totals of
+// the scans that use it as scratch
+int64_t radix_hist_ints(int64_t n) {
+  const int64_t h = 256 * ((n + kIPB - 1) / kIPB);
+  return h + (h + n + 2) / kScanB + 2;
+}
 int radix_bits(int64_t max_key) { return bits_for(max_key + 1); }
 
 hipError_t launch_radix_sort(const int *kin, const int *vin, int64_t n, int bits, int *keys[2], int *vals[2],
@@ -220,6 +288,7 @@ hipError_t launch_radix_sort(const int *kin, const int *vin, int64_t n, int bits
   res->vals = vin;
   if (n <= 0) return hipSuccess;
   const int nblk = (int)((n + kIPB - 1) / kIPB);
+  int *scan_tmp = hist + (int64_t)256 * nblk;  // block totals of the histogram scan
   hipError_t e = hipSuccess;
   if (!vin) {  // values: the item indices
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)((n + kT - 1) / kT)), dim3(kT), 0, s, vals[0], n);
@@ -233,7 +302,7 @@ hipError_t launch_radix_sort(const int *kin, const int *vin, int64_t n, int bits
     int *kout = keys[cur];
     int *vout = (vin == vals[0]) ? vals[1] : vals[0];
     hipLaunchKernelGGL(sort_hist_kernel, dim3(nblk), dim3(kT), 0, s, kin, n, shift, hist, nblk);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist, (int64_t)256 * nblk, (int *)nullptr);
+    if ((e = excl_scan(hist, (int64_t)256 * nblk, scan_tmp, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(sort_scatter_kernel, dim3(nblk), dim3(kT), 0, s, kin, vin, kout, vout, n, shift, hist, nblk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     kin = kout;
@@ -256,8 +325,8 @@ hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(seg_kernel, dim3(g), dim3(kT), 0, s, rr.keys, n, a.n_unique, a.seg);
   const unsigned gu = (unsigned)((a.max_u + 1 + kT - 1) / kT);
   hipLaunchKernelGGL(pieces_kernel, dim3(gu), dim3(kT), 0, s, a.seg, a.n_unique, a.max_u, a.poff, a.moff);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.poff, a.max_u + 1, (int *)nullptr);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.moff, a.max_u + 1, (int *)nullptr);
+  if ((e = excl_scan(a.poff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
+  if ((e = excl_scan(a.moff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
