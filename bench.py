@@ -125,6 +125,9 @@ def bench_backward(args):
     dp_f = stca.upload(p, path="fused")
     dp_b = stca.upload(p, table=dp_f.table, dedup=args.dedup)
     f = stca.Forward(dp_f, want=(), dumps=())
+    M = sp.M
+    nev = stca.n_backward_stage_events(M)
+    evs = [stca.StageEvents(nev) for _ in range(args.steps)]
     bw = stca.Backward(dp_b, dz, outputs=("table",))
     log(f"backward workspace {bw.ws_bytes / 2**30:.2f} GiB")
     for _ in range(args.warmup):
@@ -137,6 +140,8 @@ def bench_backward(args):
     t0 = time.perf_counter()
     for k in range(args.steps):
         bw.zero()
+        bw.g.stage_events = evs[k].ptr
+        bw.g.n_stage_events = nev
         ev[k][0].record()
         f()
         ev[k][1].record()
@@ -148,14 +153,48 @@ def bench_backward(args):
     ms_b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     if int(bw.status[0].item()) != 0 or int(f.status[0].item()) != 0:
         raise SystemExit("device status flagged")
-    d, h, M = sp.d, sp.hidden, sp.M
+
+    def stage(i, j):
+        return float(np.mean([e.elapsed(i, j) for e in evs]))
+    recompute, zhead = stage(0, 1), stage(1, 2)
+    attn_b, qside, hist_b = [], [], []
+    for j in range(M):  # j-th layer processed: layer M-1-j
+        prev = 2 if j == 0 else 5 + 3 * (j - 1)
+        attn_b.append(stage(prev, 3 + 3 * j))
+        qside.append(stage(3 + 3 * j, 4 + 3 * j))
+        hist_b.append(stage(4 + 3 * j, 5 + 3 * j))
+    table_t = stage(5 + 3 * (M - 1), 3 + 3 * M)
+    for e in evs:
+        e.close()
+    d, h = sp.d, sp.hidden
     n_hist, T = p.n_hist, p.n_tgt
+    n_unique = int(len(np.unique(p.hist_ids)))
+    rows_h = n_unique if args.dedup else n_hist
     pairs = int(np.sum(np.diff(p.hist_offsets).astype(np.int64) * np.diff(p.tgt_offsets)))
-    # backward proper, per layer: history 18 d h + 8 d^2 per item (recomputed
-    # FFN, dXt, dG, dX, weight gradients), attention 10 d per (item, target)
-    # pair; the forward recompute inside the call adds one forward
-    flops_b = M * (n_hist * (18 * d * h + 8 * d * d) + 10 * d * pairs)
-    flops_f = M * (n_hist * (6 * d * h + 4 * d * d) + 4 * d * pairs)
+    # backward proper, per layer: history 18 d h + 8 d^2 per row (recomputed
+    # FFN 6dh, dXt 4d^2, dG 2dh, dX 4dh, weight gradients 6dh + 4d^2), over
+    # the unique rows with dedup; attention 10 d per (item, target) pair
+    flops_hist_layer = rows_h * (18 * d * h + 8 * d * d)
+    flops_b = M * (flops_hist_layer + 10 * d * pairs)
+    flops_f = M * (rows_h * (6 * d * h + 4 * d * d) + 4 * d * pairs)
+    t_hist = float(np.mean(hist_b)) * 1e-3
+    hist_tf = flops_hist_layer / t_hist / 1e12
+    # attention backward: K, V rows read, dK | dV rows written (bf16), Q, dA read
+    bytes_attn = n_hist * 8 * d + T * 4 * d
+    t_attn = float(np.mean(attn_b)) * 1e-3
+    attn_gbs = bytes_attn / t_attn / 1e9
+    roof_hist = {"kernel": "history backward stage of one layer (recomputed FFN+LN, dX, weight gradients: "
+                           "14 strided MFMA GEMMs + row kernels)", "bound": "mfma",
+                 "achieved": round(hist_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(hist_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                 "launch_ms": round(t_hist * 1e3, 4),
+                 "per_launch": f"{rows_h} {'unique rows' if args.dedup else 'history items'} x "
+                               f"{18 * d * h + 8 * d * d} flop"}
+    roof_attn = {"kernel": "attention backward of one layer (incl. W_O and the dQ fold)", "bound": "hbm",
+                 "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                 "launch_ms": round(t_attn * 1e3, 4),
+                 "per_launch": f"{n_hist} items x {8 * d} B + {T} targets x {4 * d} B"}
     ms = ms_f + ms_b
     res = {
         "metric": "training step (forward + backward) history tokens/s per STCA layer",
@@ -170,9 +209,17 @@ def bench_backward(args):
                                f"(sum {n_hist}), m={sp.m} targets/user, table {sp.table_rows}x{d} bf16 "
                                f"Zipf({sp.zipf_s}) ids, d={d}, H={sp.H}, hidden={h}, M={M}, softmax; "
                                "forward on the fused path, backward recomputes on the staged path"
-                               + (f", unique-id dedup of the history side ({len(np.unique(p.hist_ids))} unique "
+                               + (f", unique-id dedup of the history side ({n_unique} unique "
                                   f"of {n_hist})" if args.dedup else ""),
                    "global_batch": sp.B, "targets": T, "parallelism": "single GPU"},
+        "roofline": roof_hist if sum(hist_b) >= sum(attn_b) else roof_attn,
+        "roofline_history_backward": roof_hist,
+        "roofline_attention_backward": roof_attn,
+        "backward_stages_ms": {"forward_recompute": round(recompute, 4), "z_head": round(zhead, 4),
+                               "attention_backward": [round(x, 4) for x in attn_b],
+                               "query_side": [round(x, 4) for x in qside],
+                               "history_backward": [round(x, 4) for x in hist_b],
+                               "table_scatter": round(table_t, 4)},
         "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
         "backward_flops": {"proper": flops_b, "recompute": flops_f},
     }

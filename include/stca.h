@@ -262,6 +262,16 @@ typedef struct {
                           output (heads concatenated, before W_O) */
   void *dkv_dump;      /* [M, n_hist, 2d] optional, bf16: each layer's dK | dV rows */
   int32_t *dev_status; /* optional: STCA_DEV_* bits, as for stca_forward */
+  /* Optional stage timing, as for stca_forward: up to n_stage_events of
+   *   0            start of the call
+   *   1            forward recompute done
+   *   2            z head, history-row gather and (dedup) unique-row sort done
+   *   3 + 3j       layer i = M-1-j: output projection and attention backward done
+   *   4 + 3j       layer i: query side done
+   *   5 + 3j       layer i: history side done
+   *   3 + 3M       row gradients added to the table     (3M + 4 events in all) */
+  void *const *stage_events;
+  int32_t n_stage_events;
 } stca_grads;
 
 int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t *bytes);

@@ -24,6 +24,8 @@ struct ForwardInternals {
   size_t ukv_layer_elems;
   const bf16_t *vrows;
 };
+// The forward's synchronous argument checks (config, batch, weights).
+int forward_check(const stca_config *cfg, const stca_batch *batch, const stca_weights *w);
 int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
                            const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi);
 

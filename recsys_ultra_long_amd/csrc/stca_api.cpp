@@ -354,6 +354,13 @@ int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t 
 
 namespace stca {
 
+int forward_check(const stca_config *cfg, const stca_batch *batch, const stca_weights *w) {
+  int r = validate_cfg(cfg);
+  if (r) return r;
+  if ((r = validate_batch(cfg, batch))) return r;
+  return validate_weights(cfg, w);
+}
+
 int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
                            const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi) {
   g_err[0] = 0;

@@ -241,8 +241,15 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   const bool kvln = cfg->flags & STCA_FLAG_KV_LN, zln = cfg->flags & STCA_FLAG_Z_LN;
   hipError_t e = hipSuccess;
   auto hip_err = [&](const char *what) { return api_error(STCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e)); };
+  if (gr->n_stage_events < 0 || (gr->n_stage_events > 0 && !gr->stage_events))
+    return api_error(STCA_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+  auto rec = [&](int k) -> hipError_t {
+    if (k < gr->n_stage_events && gr->stage_events[k])
+      return hipEventRecord(reinterpret_cast<hipEvent_t>(gr->stage_events[k]), s);
+    return hipSuccess;
+  };
 
-  // ---- 1. forward recompute (validates the weights before anything is enqueued)
+  // ---- 1. forward recompute (arguments checked before anything is enqueued)
   const stca_config fc = forward_cfg(cfg);
   stca_outputs fo;
   std::memset(&fo, 0, sizeof(fo));
@@ -257,7 +264,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   fo.lse = cfg->score == STCA_SCORE_SOFTMAX ? lse_all : nullptr;
   fo.dev_status = gr->dev_status;
   ForwardInternals fi;
+  if ((r = forward_check(&fc, batch, w))) return r;
+  if ((e = rec(0))) return hip_err("stage event");
   if ((r = forward_with_internals(&fc, batch, w, &fo, at<void>(ws, L.fws), L.fws_bytes, stream, &fi))) return r;
+  if ((e = rec(1))) return hip_err("stage event");
   const int64_t Rh = L.Rh;
   const int *hdev = L.dedup ? fi.n_unique : nullptr;  // device cap on the history backward's rows
 
@@ -416,6 +426,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     ua.out = at<bf16_t>(ws, L.dKVu);
     if ((e = launch_unique_sort(ua, s))) return hip_err("unique sort");
   }
+  if ((e = rec(2))) return hip_err("stage event");
 
   // ---- 4. layers, last to first
   for (int i = M - 1; i >= 0; --i) {
@@ -464,6 +475,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     }
     if (gr->dq_dump && (e = launch_add_rows(dq, d, gr->dq_dump + (size_t)i * T * d, d, T, d, false, s)))
       return hip_err("dq dump");
+    const int ev = 3 + 3 * (M - 1 - i);
+    if ((e = rec(ev))) return hip_err("stage event");
     // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C
     const float *cin = xt;
     if (i > 0) {
@@ -489,6 +502,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     } else {
       if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
     }
+    if ((e = rec(ev + 1))) return hip_err("stage event");
     // history side of layer i, over the history items or (dedup) the unique
     // rows with each row's dK | dV summed over its items
     if (R > 0) {
@@ -529,6 +543,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         return hip_err("dx");
       gdev = nullptr;
     }
+    if ((e = rec(ev + 2))) return hip_err("stage event");
   }
 
   // ---- 5. row gradients into the table
@@ -537,6 +552,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       return hip_err("scatter");
     if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s))) return hip_err("scatter");
   }
+  if ((e = rec(3 + 3 * M))) return hip_err("stage event");
   return STCA_OK;
 }
 

@@ -76,7 +76,8 @@ class LayerGrad(C.Structure):
 class Grads(C.Structure):
     _fields_ = [("layers", C.POINTER(LayerGrad)), ("z", FfnGrad), ("wz", _vp), ("table", _vp),
                 ("d_hist", _vp), ("d_tgt", _vp), ("z_out", _vp), ("dq_dump", _vp), ("da_dump", _vp),
-                ("dkv_dump", _vp), ("dev_status", _vp)]
+                ("dkv_dump", _vp), ("dev_status", _vp), ("stage_events", C.POINTER(_vp)),
+                ("n_stage_events", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -260,6 +261,10 @@ def n_stage_events(M: int) -> int:
     return 5 * M + 3
 
 
+def n_backward_stage_events(M: int) -> int:
+    return 3 * M + 4
+
+
 class Forward:
     """Reusable forward call: outputs and workspace are allocated once."""
 
@@ -320,7 +325,7 @@ class Backward:
     ``zero()`` them before a fresh step."""
 
     def __init__(self, dp: DeviceProblem, dz, outputs=("table", "d_hist", "d_tgt", "z"), dumps=(),
-                 stream=None):
+                 stream=None, events: Optional[StageEvents] = None):
         import torch
         self.dp = dp
         self.lib = load()
@@ -362,6 +367,9 @@ class Backward:
         self.g = Grads(lg, fg(self.grads["z"]), _ptr(self.grads["wz"]), _ptr(self.table),
                        _ptr(self.d_hist), _ptr(self.d_tgt), _ptr(self.z_out), _ptr(self.dq_dump),
                        _ptr(self.da_dump), _ptr(self.dkv_dump), _ptr(self.status))
+        if events is not None:
+            self.g.stage_events = events.ptr
+            self.g.n_stage_events = events.n
         n = C.c_size_t(0)
         _check(self.lib.stca_backward_workspace_size(C.byref(cfg), C.byref(self.b), C.byref(n)))
         self.ws_bytes = n.value
