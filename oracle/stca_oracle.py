@@ -42,6 +42,15 @@ Readings taken where the pages are silent (each one is listed in the design doc):
 * Empty history: attention output 0, active count 0.
 * HyFormer linear mode: Q_{l+1} = O_l R_l, output O_M ([HyFormer] eq. (9),
   (16), with the boosting block replaced by a fixed linear map).
+* HyFormer query mode ([HyFormer] §3.3.2 eq. (3)-(4), §3.5 eq. (10)-(15),
+  §3.6 eq. (16)-(17)): every "FFN" is the SwiGLU block above without LN; the
+  N queries of a user are FFN_n(Concat(F_1, ..., F_M, MeanPool(Seq))) with
+  Seq the user's raw history rows (zero for an empty history); each layer
+  decodes them with the multi-head cross attention and W_O, then boosts
+  [decoded queries | F_1 .. F_M] (T = N + M tokens) by the subspace token
+  mixing, one FFN per mixed token and the residual; the first N boosted
+  tokens are the next layer's queries (the non-sequence tokens re-enter from
+  F at every layer) and, after the last layer, the output z.
 
 Parity pins: every function below is pinned by a closed form, an invariant,
 a brute-force enumeration or an independent library routine in
@@ -151,6 +160,42 @@ def attention_core(Qs: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: 
     return attn, cnt, amb
 
 
+# ---------------------------------------------------------------- HyFormer queries
+def mean_pool(X: np.ndarray) -> np.ndarray:
+    """MeanPool(Seq) over the rows of a user's history (zero when empty)."""
+    return X.mean(axis=0) if len(X) else np.zeros(X.shape[1])
+
+
+def ffn_n(x: np.ndarray, w: dict, n: int) -> np.ndarray:
+    """The n-th of a stack of SwiGLU FFNs (w1, w3 [n, in, h], w2 [n, h, d])."""
+    return (silu(x @ w["w1"][n]) * (x @ w["w3"][n])) @ w["w2"][n]
+
+
+def query_generation(F: np.ndarray, X: np.ndarray, qgen: dict) -> np.ndarray:
+    """eq. (3)-(4): Q = [FFN_1(g), ..., FFN_N(g)], g = Concat(F_1..F_M, MeanPool(X))."""
+    g = np.concatenate([F.reshape(-1), mean_pool(X)])
+    return np.stack([ffn_n(g, qgen, n) for n in range(qgen["w1"].shape[0])])
+
+
+def token_mix(Q: np.ndarray) -> np.ndarray:
+    """eq. (11)-(13): token t is cut into T subspaces of width D / T; mixed
+    token h is the concatenation over t of every token's h-th subspace."""
+    T, D = Q.shape
+    w = D // T
+    out = np.empty_like(Q)
+    for h in range(T):
+        for t in range(T):
+            out[h, t * w:(t + 1) * w] = Q[t, h * w:(h + 1) * w]
+    return out
+
+
+def query_boost(Qdec: np.ndarray, F: np.ndarray, boost: dict) -> np.ndarray:
+    """eq. (10), (14), (15): Q = [Qdec | F], Q_boost = Q + PerToken-FFN(mix(Q))."""
+    Q = np.concatenate([Qdec, F], axis=0)
+    Qm = token_mix(Q)
+    return Q + np.stack([ffn_n(Qm[h], boost, h) for h in range(Q.shape[0])])
+
+
 # ---------------------------------------------------------------- weights
 def weights_f64(layers, z=None, wz=None):
     """Upcast stored weights (bf16 bits or fp32) to float64 dictionaries."""
@@ -172,7 +217,7 @@ def encode_history(X: np.ndarray, lw: dict, kv_ln: bool):
 
 
 def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=None, wz=None,
-            tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q")):
+            tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q"), hy=None):
     """The STCA forward for the users in ``users`` (default: all).
 
     cfg: dict with d, H, M, score ("softmax"|"relu"), qmode ("fusion"|"linear"),
@@ -201,6 +246,25 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
         # Request Level Batching: the user's K/V of every layer is computed
         # once and serves all of the user's targets ([Notes] §RLB).
         KV = [encode_history(X, layers[i], cfg["kv_ln"]) for i in range(M)]
+        if qmode == "hyformer":
+            t0, t1 = int(to[u]), int(to[u + 1])
+            F = hy["ns"][u]
+            q = query_generation(F, X, hy["qgen"])        # [N, d]
+            for i in range(M):
+                K, V = KV[i]
+                dec = np.zeros((t1 - t0, d))
+                for n in range(t1 - t0):
+                    Q = q[n] @ layers[i]["wq"]
+                    a, c, amb = attention_target(Q, K, V, H, score)
+                    dec[n] = a @ layers[i]["wo"]
+                    out["qs"][i, t0 + n] = Q
+                    out["attn"][i, t0 + n] = a
+                    out["active"][i, t0 + n] = c
+                    out["amb"][i, t0 + n] = amb
+                    out["o"][i, t0 + n] = dec[n]
+                q = query_boost(dec, F, layers[i]["boost"])[:t1 - t0]
+            out["z"][t0:t1] = q
+            continue
         for t in range(int(to[u]), int(to[u + 1])):
             if qmode == "fusion":
                 x_t = rows_f64(np.asarray([tgt_ids[t]]))[0]
@@ -240,6 +304,10 @@ def forward_problem(p, users=None):
     layers, z, wz = weights_f64(p.layers, p.z, p.wz)
     cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode,
                kv_ln=sp.kv_ln, z_ln=sp.z_ln)
+    hy = None
+    if sp.qmode == "hyformer":
+        hy = {"ns": stored_to_f64(p.extra["ns"]),
+              "qgen": {k: stored_to_f64(v) for k, v in p.extra["qgen"].items()}}
     return forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets,
                    lambda ids: stored_to_f64(p.rows(ids)), layers, z, wz,
-                   tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users)
+                   tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users, hy=hy)

@@ -25,6 +25,10 @@ Distributions (readings of the workload descriptions, restated in the design doc):
   alpha = 1/4 for the training workload, whose mean length L_max / 5 = 2K is
   the training length the reading notes give for 10K inference);
 * the upstream gradient of z for the backward: i.i.d. N(0, 1);
+* HyFormer query mode: n_ns non-sequence feature tokens per user i.i.d.
+  N(0, 0.02^2) like table rows; the query-generation FFNs (input
+  (n_ns + 1) d) and the per-token boosting FFNs i.i.d. N(0, 1/fan_in), drawn
+  from a stream of their own so the other arrays are unchanged;
 * bf16 storage is produced by round-to-nearest-even from float32.
 
 Storage convention: a bf16 array is a ``numpy.uint16`` array of raw bf16
@@ -93,12 +97,15 @@ class Spec:
     dtype: str = "bf16"                 # "bf16" | "f32"
     score: str = "softmax"              # "softmax" | "relu"
     qmode: str = "fusion"               # "fusion" (STCA W_C chain) | "linear" (Q' = O R)
+                                        # | "hyformer" (generated queries + boosting)
     kv_ln: bool = True                  # LN after the history FFN
     z_ln: bool = False                  # LN on the final z
     L: Optional[int] = None             # fixed history length
     L_max: Optional[int] = None         # ragged: max(L_min, ceil(L_max * Beta(beta_a, 1)))
     L_min: int = 16
     beta_a: float = 2.0
+    n_ns: int = 0                       # hyformer: non-sequence feature tokens per user
+    hy_hidden: Optional[int] = None     # hyformer: hidden width of the query FFNs (default d)
     m: int = 1                          # targets (or queries) per user
     ids: str = "zipf"                   # "zipf" | "uniform"
     zipf_s: float = 1.1
@@ -310,16 +317,40 @@ def make_problem(sp: Spec, *, with_table: bool = True, threads: int = 8) -> Prob
     tgt_offsets = (np.arange(sp.B + 1, dtype=np.int64) * sp.m)
     n_tgt = int(tgt_offsets[-1])
     tgt_ids, q0 = None, None
+    extra = {}
     if sp.qmode == "fusion":
         tgt_ids = sample_ids(np.random.Generator(np.random.PCG64(s_tgt)), n_tgt,
                              sp.table_rows, sp.ids, sp.zipf_s)
+    elif sp.qmode == "hyformer":
+        extra = _make_hyformer(sp)
     else:
         gq = np.random.Generator(np.random.PCG64(s_q))
         q0 = _store(gq.standard_normal((n_tgt, sp.d), dtype=np.float32), sp.dtype)
     layers, z, wz = _make_weights(np.random.Generator(np.random.PCG64(s_w)), sp)
+    if sp.qmode == "hyformer":
+        for i, l in enumerate(layers):
+            l["boost"] = extra["boost"][i]
     table = make_table(sp, threads) if with_table else None
     return Problem(sp, hist_offsets.astype(np.int32), hist_ids, tgt_offsets.astype(np.int32),
-                   tgt_ids, q0, table, layers, z, wz)
+                   tgt_ids, q0, table, layers, z, wz,
+                   {k: v for k, v in extra.items() if k != "boost"})
+
+
+def _make_hyformer(sp: Spec) -> dict:
+    """Non-sequence tokens [B, n_ns, d], the m query-generation FFNs
+    (w1, w3 [m, (n_ns+1) d, hh], w2 [m, hh, d]) and, per layer, the m + n_ns
+    per-token boosting FFNs (w1, w3 [T, d, hh], w2 [T, hh, d])."""
+    d, hh, N, F = sp.d, sp.hy_hidden or sp.d, sp.m, sp.n_ns
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 0x4859])))
+    ns = _store(g.standard_normal((sp.B, F, d), dtype=np.float32) * np.float32(TABLE_STD), sp.dtype)
+
+    def ffn(n, din):
+        return {"w1": _store(g.standard_normal((n, din, hh), dtype=np.float32) / np.float32(math.sqrt(din)), sp.dtype),
+                "w3": _store(g.standard_normal((n, din, hh), dtype=np.float32) / np.float32(math.sqrt(din)), sp.dtype),
+                "w2": _store(g.standard_normal((n, hh, d), dtype=np.float32) / np.float32(math.sqrt(hh)), sp.dtype)}
+    qgen = ffn(N, (F + 1) * d)
+    boost = [ffn(N + F, d) for _ in range(sp.M)]
+    return {"ns": ns, "qgen": qgen, "boost": boost}
 
 
 def subset_users(p: Problem, users) -> Problem:
@@ -342,4 +373,5 @@ def subset_users(p: Problem, users) -> Problem:
                    np.asarray(toff, np.int32),
                    cat(tid, np.int32) if p.tgt_ids is not None else None,
                    (np.concatenate(q0) if q0 else None) if p.q0 is not None else None,
-                   p.table, p.layers, p.z, p.wz, dict(p.extra))
+                   p.table, p.layers, p.z, p.wz,
+                   {**p.extra, **({"ns": p.extra["ns"][users]} if "ns" in p.extra else {})})
