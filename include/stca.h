@@ -63,7 +63,21 @@ typedef enum {
 
 enum { STCA_F32 = 0, STCA_BF16 = 1 };                  /* stca_config.dtype  */
 enum { STCA_SCORE_SOFTMAX = 0, STCA_SCORE_RELU = 1 };  /* stca_config.score  */
-enum { STCA_Q_FUSION = 0, STCA_Q_LINEAR = 1 };         /* stca_config.qmode  */
+enum { STCA_Q_FUSION = 0, STCA_Q_LINEAR = 1,          /* stca_config.qmode  */
+       STCA_Q_HYFORMER = 2 };
+/* STCA_Q_HYFORMER ([HyFormer] §3.3.2 eq. (3)-(4), §3.5 eq. (10)-(15), §3.6
+ * eq. (16)-(17)): every user has exactly m = max_tgt_per_user queries
+ * (tgt_offsets[u] = u m), generated from the user's non-sequence tokens F
+ * (batch->ns_feats) and the mean of its raw history rows:
+ *   g_u = [F_u,1 | .. | F_u,n_ns | MeanPool(rows)],  q_u,n = FFN_n(g_u);
+ * each layer decodes them (multi-head cross attention, W_O) into o and boosts
+ * Q = [o_u,1..m | F_u,1..n_ns] (T = m + n_ns tokens, T divides d): every token
+ * is cut into T subspaces of width d / T, mixed token h concatenates every
+ * token's h-th subspace, Q_boost = Q + [FFN'_1(mixed 1) | .. | FFN'_T(mixed T)]
+ * position by position; the first m boosted tokens are the next queries and,
+ * after the last layer, z.  Every FFN is SwiGLU without LN, hidden width
+ * cfg->q_hidden.  bf16, staged path; the history side is HyFormer's
+ * eq. (7)-(8) encoding as in STCA_Q_LINEAR. */
 enum { STCA_PATH_STAGED = 0, STCA_PATH_FUSED = 1 };    /* stca_config.path   */
 enum {                                                 /* stca_config.flags  */
   STCA_FLAG_KV_LN = 1,  /* LN after the history FFN (STCA); clear for HyFormer eq. (7) */
@@ -97,6 +111,8 @@ typedef struct {
                            64 targets per user; otherwise STCA_ERR_UNSUPPORTED     */
   int32_t flags;        /* STCA_FLAG_*                                            */
   int32_t chunk_keys;   /* keys per split-L chunk (multiple of 32); 0 = automatic  */
+  int32_t n_ns;         /* STCA_Q_HYFORMER: non-sequence feature tokens per user   */
+  int32_t q_hidden;     /* STCA_Q_HYFORMER: hidden width of the query FFNs (x32)   */
 } stca_config;
 
 /* One batch of requests: ragged histories and targets in CSR form.
@@ -113,6 +129,7 @@ typedef struct {
   int64_t n_hist;               /* host: total history tokens, < 2^31               */
   int64_t n_tgt;                /* host: total targets, < 2^31                      */
   int32_t max_tgt_per_user;     /* host: upper bound on any m_u, 1..4096            */
+  const void *ns_feats;         /* [B, n_ns, d] non-sequence tokens (STCA_Q_HYFORMER) */
 } stca_batch;
 
 /* SwiGLU FFN d -> h -> d, optionally followed by LayerNorm (eps 1e-5):
@@ -136,12 +153,17 @@ typedef struct {
   const void *wc;     /* [(i+1) d, d] fusion matrix (STCA_Q_FUSION, i > 0; else NULL) */
   const void *r;      /* [d, d] next-query map Q_{i+1} = O_i R_i (STCA_Q_LINEAR,
                          i < M-1; else ignored)                                      */
+  const void *boost_w1, *boost_w3;  /* [T, d, q_hidden] per-token boosting FFNs      */
+  const void *boost_w2;             /* [T, q_hidden, d]   (STCA_Q_HYFORMER)           */
 } stca_layer;
 
 typedef struct {
   const stca_layer *layers;  /* host array [M]                                      */
   stca_ffn z;                /* final SwiGLU (+LN with STCA_FLAG_Z_LN), STCA_Q_FUSION */
   const void *wz;            /* [(M+1) d, d] final concat map, STCA_Q_FUSION          */
+  /* STCA_Q_HYFORMER query generation: FFN_n for n < m */
+  const void *qgen_w1, *qgen_w3;  /* [m, (n_ns+1) d, q_hidden]                         */
+  const void *qgen_w2;            /* [m, q_hidden, d]                                  */
 } stca_weights;
 
 typedef struct {

@@ -115,6 +115,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
   }
   const TA *A = (const TA *)g.A;
   const TB *B = (const TB *)g.B;
+  float *Cb = g.C;
+  if (!SPLIT && g.batch > 1) {
+    A += (int64_t)blockIdx.z * g.bsa;
+    B += (int64_t)blockIdx.z * g.bsb;
+    Cb += (int64_t)blockIdx.z * g.bsc;
+  }
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
         if (SPLIT) {
           g.part[((int64_t)blockIdx.z * g.M + m) * g.N + n] = acc[i][j][r];
         } else {
-          float *c = g.C + m * g.scm + n * g.scn;
+          float *c = Cb + m * g.scm + n * g.scn;
           const float v = g.alpha * acc[i][j][r];
           *c = g.beta != 0.f ? v + g.beta * *c : v;
         }
@@ -199,8 +205,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split
 template <typename TA, typename TB, bool AKC, bool BKC>
 hipError_t run(const GemmArgs &g, hipStream_t s) {
   // vector loads: 16-byte aligned base, and the non-unit stride a multiple of 8
-  const bool va = (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) && ((AKC ? g.sam : g.sak) % 8 == 0);
-  const bool vb = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && ((BKC ? g.sbn : g.sbk) % 8 == 0);
+  const bool bat = g.batch > 1;
+  const bool va = (reinterpret_cast<uintptr_t>(g.A) % 16 == 0) && ((AKC ? g.sam : g.sak) % 8 == 0) &&
+                  (!bat || g.bsa % 8 == 0);
+  const bool vb = (reinterpret_cast<uintptr_t>(g.B) % 16 == 0) && ((BKC ? g.sbn : g.sbk) % 8 == 0) &&
+                  (!bat || g.bsb % 8 == 0);
   const unsigned gx = (unsigned)((g.M + BM - 1) / BM), gy = (unsigned)((g.N + BN - 1) / BN);
   if (g.split > 1) {
     int64_t kchunk = (g.K + g.split - 1) / g.split;
@@ -214,7 +223,8 @@ hipError_t run(const GemmArgs &g, hipStream_t s) {
     const int64_t n = g.M * g.N;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, split, kchunk);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, false>), dim3(gx, gy, 1), dim3(256), 0, s, g, g.K, va, vb);
+    const unsigned gz = g.batch > 1 ? (unsigned)g.batch : 1u;
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, false>), dim3(gx, gy, gz), dim3(256), 0, s, g, g.K, va, vb);
   }
   return hipGetLastError();
 }
@@ -241,6 +251,7 @@ int gemm_split_for(int64_t M, int64_t N, int64_t K, int64_t target, int64_t min_
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (!((g.sak == 1 || g.sam == 1) && (g.sbk == 1 || g.sbn == 1))) return hipErrorInvalidValue;
+  if (g.batch > 1 && g.split > 1) return hipErrorInvalidValue;
   if (g.K <= 0) {  // empty sum: C = beta * C
     GemmArgs z = g;
     z.split = 1;

@@ -55,6 +55,10 @@ struct GemmArgs {
   int64_t part_cap;  // floats in `part`: a split needing more is refused
   const int *dev_rows;
   int dev_dim;
+  // batch > 1 (no split): blockIdx.z picks problem z, whose A, B, C start
+  // z * bsa, z * bsb, z * bsc elements further
+  int batch;
+  int64_t bsa, bsb, bsc;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 // Split factor for a long-K product (weight gradients), and the partial
@@ -121,6 +125,23 @@ struct AttnBwdArgs {
 };
 int64_t attn_bwd_part_floats(int64_t max_chunks, int H, int dh);
 hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
+
+// ------------------------------------------------------------ HyFormer queries
+// mp[u, :] = mean of the table rows of user u's history (zero when empty)
+hipError_t launch_mean_pool(const bf16_t *table, int64_t table_rows, const int *hist_ids, const Plan &plan, int B,
+                            int d, float *mp, hipStream_t s);
+// g[u] = [F_u,1 .. F_u,n_ns | mp[u]] (fp32, [B, (n_ns + 1) d]) from bf16 F
+hipError_t launch_global_info(const bf16_t *ns, const float *mp, int B, int n_ns, int d, float *g, hipStream_t s);
+// qcur[u m + n] = bf16(src[n][u]) for src [m][B][d] fp32
+hipError_t launch_queries_from_stack(const float *src, int m, int B, int d, bf16_t *qcur, hipStream_t s);
+// qcat[u][t] = o[u m + t] (t < m), F_u,t-m (t >= m); qmix[h][u] = mixed token h
+// of user u (T = m + n_ns tokens, subspaces of width d / T)
+hipError_t launch_boost_input(const float *o, const bf16_t *ns, int B, int m, int n_ns, int d, float *qcat,
+                              float *qmix, hipStream_t s);
+// Q_boost[u][t] = qcat[u][t] + ffn[t][u]; its first m tokens -> qcur (bf16)
+// and, when z is given, -> z (fp32)
+hipError_t launch_boost_output(const float *qcat, const float *ffn, int B, int m, int n_ns, int d, bf16_t *qcur,
+                               float *z, hipStream_t s);
 
 // ------------------------------------------------------------ per-unique sums
 // out[u] = sum over the items j with tok2u[j] = u, in item order, of dkv[j]

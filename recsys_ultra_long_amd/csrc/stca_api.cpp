@@ -97,6 +97,7 @@ struct Layout {
   size_t ukv = 0, ukv_layer = 0, vrows = 0;
   size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0, fstate = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
+  size_t hy_mp = 0, hy_g = 0, hy_h13 = 0, hy_gg = 0, hy_out = 0, hy_qcat = 0, hy_qmix = 0, hy_o32 = 0;
   std::vector<PrepLayer> pl;
   size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
 };
@@ -126,8 +127,15 @@ int validate_cfg(const stca_config *c) {
     return fail(STCA_ERR_INVALID_ARG, "dtype %d unknown", c->dtype);
   if (c->score != STCA_SCORE_SOFTMAX && c->score != STCA_SCORE_RELU)
     return fail(STCA_ERR_INVALID_ARG, "score %d unknown", c->score);
-  if (c->qmode != STCA_Q_FUSION && c->qmode != STCA_Q_LINEAR)
+  if (c->qmode != STCA_Q_FUSION && c->qmode != STCA_Q_LINEAR && c->qmode != STCA_Q_HYFORMER)
     return fail(STCA_ERR_INVALID_ARG, "qmode %d unknown", c->qmode);
+  if (c->qmode == STCA_Q_HYFORMER) {
+    if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "STCA_Q_HYFORMER is bf16 only");
+    if (c->path != STCA_PATH_STAGED) return fail(STCA_ERR_UNSUPPORTED, "STCA_Q_HYFORMER needs the staged path");
+    if (c->n_ns < 0) return fail(STCA_ERR_INVALID_ARG, "n_ns %d < 0", c->n_ns);
+    if (c->q_hidden <= 0 || c->q_hidden % 32)
+      return fail(STCA_ERR_UNSUPPORTED, "q_hidden %d must be a positive multiple of 32", c->q_hidden);
+  }
   if (c->path != STCA_PATH_STAGED && c->path != STCA_PATH_FUSED)
     return fail(STCA_ERR_INVALID_ARG, "path %d unknown", c->path);
   if (c->flags & ~(STCA_FLAG_KV_LN | STCA_FLAG_Z_LN | STCA_FLAG_DEDUP))
@@ -191,6 +199,15 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
     return fail(STCA_ERR_INVALID_ARG, "tgt_ids is NULL (fusion mode)");
   if (c->qmode == STCA_Q_LINEAR && b->n_tgt > 0 && !b->q0)
     return fail(STCA_ERR_INVALID_ARG, "q0 is NULL (linear mode)");
+  if (c->qmode == STCA_Q_HYFORMER) {
+    const int m = b->max_tgt_per_user, T = m + c->n_ns;
+    if (b->n_tgt != (int64_t)c->B * m)
+      return fail(STCA_ERR_INVALID_ARG, "STCA_Q_HYFORMER: n_tgt %lld != B * max_tgt_per_user (%d * %d)",
+                  (long long)b->n_tgt, c->B, m);
+    if (c->d % T) return fail(STCA_ERR_UNSUPPORTED, "STCA_Q_HYFORMER: m + n_ns = %d must divide d = %d", T, c->d);
+    if (c->n_ns > 0 && b->n_tgt > 0 && !b->ns_feats) return fail(STCA_ERR_INVALID_ARG, "ns_feats is NULL");
+    if (b->ns_feats && !aligned16(b->ns_feats)) return fail(STCA_ERR_INVALID_ARG, "ns_feats not 16-byte aligned");
+  }
   const void *ptrs[] = {b->hist_offsets, b->hist_ids, b->tgt_offsets, b->tgt_ids, b->q0, b->table};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
@@ -224,9 +241,20 @@ int validate_weights(const stca_config *c, const stca_weights *w) {
       if ((r = check_ffn(l.q, true, "q", i))) return r;
       if (i > 0 && !l.wc) return fail(STCA_ERR_INVALID_ARG, "W_C NULL (layer %d)", i);
       if (l.wc && !aligned16(l.wc)) return fail(STCA_ERR_INVALID_ARG, "W_C not aligned (layer %d)", i);
-    } else if (i + 1 < c->M) {
+    } else if (c->qmode == STCA_Q_LINEAR && i + 1 < c->M) {
       if (!l.r) return fail(STCA_ERR_INVALID_ARG, "R NULL (layer %d, linear mode)", i);
       if (!aligned16(l.r)) return fail(STCA_ERR_INVALID_ARG, "R not aligned (layer %d)", i);
+    }
+  }
+  if (c->qmode == STCA_Q_HYFORMER) {
+    const void *qm[] = {w->qgen_w1, w->qgen_w3, w->qgen_w2};
+    for (const void *p : qm)
+      if (!p || !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "query-generation weight NULL or misaligned");
+    for (int i = 0; i < c->M; ++i) {
+      const stca_layer &l = w->layers[i];
+      const void *bm[] = {l.boost_w1, l.boost_w3, l.boost_w2};
+      for (const void *p : bm)
+        if (!p || !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "boosting weight NULL or misaligned (layer %d)", i);
     }
   }
   if (c->qmode == STCA_Q_FUSION) {
@@ -286,7 +314,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
         p.q_w3 = e; e += h * d;
         p.q_w2 = e; e += h * d;
         if (i > 0) { p.wc = e; e += d * (i + 1) * d; }
-      } else {
+      } else if (c->qmode == STCA_Q_LINEAR) {
         p.r = e; e += d * d;
       }
     }
@@ -315,6 +343,18 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   L.attn32 = cv.take(T * d * sizeof(float));
   L.attnlo = cv.take(T * d * L.esize);
   L.qcur = cv.take(T * d * L.esize);
+  if (c->qmode == STCA_Q_HYFORMER) {  // query generation and boosting (fp32)
+    const int64_t m = b->max_tgt_per_user, Tk = m + c->n_ns, hq = c->q_hidden, Bu = c->B;
+    const int64_t stack = std::max(m, Tk) * Bu;
+    L.hy_mp = cv.take(Bu * d * 4);
+    L.hy_g = cv.take(Bu * (c->n_ns + 1) * d * 4);
+    L.hy_h13 = cv.take(stack * 2 * hq * 4);
+    L.hy_gg = cv.take(stack * hq * 4);
+    L.hy_out = cv.take(stack * d * 4);
+    L.hy_qcat = cv.take(Bu * Tk * d * 4);
+    L.hy_qmix = cv.take(Bu * Tk * d * 4);
+    L.hy_o32 = cv.take(T * d * 4);
+  }
   L.total = cv.off;
   return L;
 }
@@ -447,7 +487,7 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
         if ((e = add(l.q.w3, d, hd, p.q_w3, 0))) break;
         if ((e = add(l.q.w2, hd, d, p.q_w2, 0))) break;
         if (i > 0 && (e = add(l.wc, (i + 1) * d, d, p.wc, 0))) break;
-      } else if (i + 1 < M) {
+      } else if (cfg->qmode == STCA_Q_LINEAR && i + 1 < M) {
         if ((e = add(l.r, d, d, p.r, 0))) break;
       }
     }
@@ -696,6 +736,65 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
   void *qs = at<void>(ws, L.qs);
   void *qcur = at<void>(ws, L.qcur);
   void *attnlo = at<void>(ws, L.attnlo);
+  // HyFormer queries: one strided GEMM per step, batched over the m query
+  // FFNs (or the T boosting FFNs), with the SwiGLU row kernel between
+  const bool hyf = cfg->qmode == STCA_Q_HYFORMER;
+  const int hm = batch->max_tgt_per_user, hT = hm + cfg->n_ns, hq = cfg->q_hidden;
+  float *hy_h13 = hyf ? at<float>(ws, L.hy_h13) : nullptr, *hy_gg = hyf ? at<float>(ws, L.hy_gg) : nullptr;
+  float *hy_out = hyf ? at<float>(ws, L.hy_out) : nullptr;
+  // n FFNs (w1, w3 [n, din, hq], w2 [n, hq, d]) on n stacked [B, din] inputs
+  // (a_batch_stride 0: one shared input) -> hy_out [n][B][d]
+  auto ffn_stack = [&](int n, const float *a, int64_t din, int64_t a_bs, const void *w1, const void *w3,
+                       const void *w2) -> hipError_t {
+    GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
+    g.M = B;
+    g.N = hq;
+    g.K = din;
+    g.A = a;
+    g.sam = din;
+    g.sak = 1;
+    g.B = w1;
+    g.sbk = hq;
+    g.sbn = 1;
+    g.b_bf16 = true;
+    g.C = hy_h13;
+    g.scm = 2 * hq;
+    g.scn = 1;
+    g.alpha = 1.f;
+    g.split = 1;
+    g.batch = n;
+    g.bsa = a_bs;
+    g.bsb = din * hq;
+    g.bsc = (int64_t)B * 2 * hq;
+    hipError_t er = launch_gemm(g, s);
+    if (er) return er;
+    g.B = w3;
+    g.C = hy_h13 + hq;
+    if ((er = launch_gemm(g, s))) return er;
+    if ((er = launch_swiglu_fwd(hy_h13, (int64_t)n * B, hq, hy_gg, false, s))) return er;
+    g.A = hy_gg;
+    g.sam = hq;
+    g.K = hq;
+    g.bsa = (int64_t)B * hq;
+    g.B = w2;
+    g.sbk = d;
+    g.N = d;
+    g.bsb = (int64_t)hq * d;
+    g.C = hy_out;
+    g.scm = d;
+    g.bsc = (int64_t)B * d;
+    return launch_gemm(g, s);
+  };
+  if (hyf) {  // q_u,n = FFN_n([F_u | MeanPool(rows of u)])
+    float *mp = at<float>(ws, L.hy_mp), *gi = at<float>(ws, L.hy_g);
+    e = launch_mean_pool((const bf16_t *)batch->table, cfg->table_rows, batch->hist_ids, plan, B, d, mp, s);
+    if (!e) e = launch_global_info((const bf16_t *)batch->ns_feats, mp, B, cfg->n_ns, d, gi, s);
+    const int64_t din = (int64_t)(cfg->n_ns + 1) * d;
+    if (!e) e = ffn_stack(hm, gi, din, 0, w->qgen_w1, w->qgen_w3, w->qgen_w2);
+    if (!e) e = launch_queries_from_stack(hy_out, hm, B, d, (bf16_t *)qcur, s);
+    if (e) return hip_fail(e, "query generation");
+  }
   for (int i = 0; i < M; ++i) {
     const stca_layer &l = w->layers[i];
     const PrepLayer *p = bf ? &L.pl[i] : nullptr;
@@ -734,7 +833,7 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
         }
       } else {
         a.in_mode = IN_DENSE;
-        a.a = i == 0 ? batch->q0 : qcur;
+        a.a = (i == 0 && !hyf) ? batch->q0 : qcur;
         a.lda = d;
       }
       if ((e = chain(a))) return hip_fail(e, "query");
@@ -777,18 +876,28 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
       if (out->o_layers) {
         a.out32 = out->o_layers + (size_t)i * T * d;
         a.ldo32 = d;
+      } else if (hyf) {  // the boosting reads o in fp32
+        a.out32 = at<float>(ws, L.hy_o32);
+        a.ldo32 = d;
       } else if (!fusion && last) {
         a.out32 = out->z;
         a.ldo32 = d;
       }
       if ((e = chain(a))) return hip_fail(e, "output projection");
-      if (!fusion && last && out->o_layers) {  // z = O_M
+      if (!fusion && !hyf && last && out->o_layers) {  // z = O_M
         e = hipMemcpy2DAsync(out->z, d * sizeof(float), out->o_layers + (size_t)i * T * d,
                              d * sizeof(float), d * sizeof(float), T, hipMemcpyDeviceToDevice, s);
         if (e) return hip_fail(e, "z copy");
       }
     }
-    if (!fusion && !last) {  // Q_{i+1} = O_i R_i
+    if (hyf) {  // Q_boost = [o | F] + FFN'(mix([o | F])); first m tokens -> next queries (or z)
+      const float *o32 = out->o_layers ? out->o_layers + (size_t)i * T * d : at<float>(ws, L.hy_o32);
+      float *qcat = at<float>(ws, L.hy_qcat), *qmix = at<float>(ws, L.hy_qmix);
+      e = launch_boost_input(o32, (const bf16_t *)batch->ns_feats, B, hm, cfg->n_ns, d, qcat, qmix, s);
+      if (!e) e = ffn_stack(hT, qmix, d, (int64_t)B * d, l.boost_w1, l.boost_w3, l.boost_w2);
+      if (!e) e = launch_boost_output(qcat, hy_out, B, hm, cfg->n_ns, d, (bf16_t *)qcur, last ? out->z : nullptr, s);
+      if (e) return hip_fail(e, "query boosting");
+    } else if (!fusion && !last) {  // Q_{i+1} = O_i R_i
       ChainArgs a = base_args();
       a.in_mode = IN_DENSE;
       a.out_mode = OUT_ROWS;

@@ -306,6 +306,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
                   const void *Bp, bool bbf, int64_t sbk, int64_t sbn, float *C, int64_t scm, int64_t scn, float alpha,
                   float beta, int kind) -> hipError_t {
     GemmArgs g;
+    std::memset(&g, 0, sizeof(g));
     g.M = Mm;
     g.N = Nn;
     g.K = Kk;

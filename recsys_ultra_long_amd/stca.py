@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libstca.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 SCORE = {"softmax": 0, "relu": 1}
-QMODE = {"fusion": 0, "linear": 1}
+QMODE = {"fusion": 0, "linear": 1, "hyformer": 2}
 PATH = {"staged": 0, "fused": 1}
 FLAG_KV_LN, FLAG_Z_LN, FLAG_DEDUP = 1, 2, 4
 DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
@@ -36,13 +36,14 @@ class Config(C.Structure):
     _fields_ = [("B", C.c_int32), ("d", C.c_int32), ("H", C.c_int32), ("hidden", C.c_int32),
                 ("M", C.c_int32), ("table_rows", C.c_int64), ("dtype", C.c_int32),
                 ("score", C.c_int32), ("qmode", C.c_int32), ("path", C.c_int32),
-                ("flags", C.c_int32), ("chunk_keys", C.c_int32)]
+                ("flags", C.c_int32), ("chunk_keys", C.c_int32), ("n_ns", C.c_int32),
+                ("q_hidden", C.c_int32)]
 
 
 class Batch(C.Structure):
     _fields_ = [("hist_offsets", _vp), ("hist_ids", _vp), ("tgt_offsets", _vp), ("tgt_ids", _vp),
                 ("q0", _vp), ("table", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
-                ("max_tgt_per_user", C.c_int32)]
+                ("max_tgt_per_user", C.c_int32), ("ns_feats", _vp)]
 
 
 class Ffn(C.Structure):
@@ -51,11 +52,12 @@ class Ffn(C.Structure):
 
 class Layer(C.Structure):
     _fields_ = [("kv", Ffn), ("q", Ffn), ("wk", _vp), ("wv", _vp), ("wq", _vp), ("wo", _vp),
-                ("wc", _vp), ("r", _vp)]
+                ("wc", _vp), ("r", _vp), ("boost_w1", _vp), ("boost_w3", _vp), ("boost_w2", _vp)]
 
 
 class Weights(C.Structure):
-    _fields_ = [("layers", C.POINTER(Layer)), ("z", Ffn), ("wz", _vp)]
+    _fields_ = [("layers", C.POINTER(Layer)), ("z", Ffn), ("wz", _vp), ("qgen_w1", _vp), ("qgen_w3", _vp),
+                ("qgen_w2", _vp)]
 
 
 class Outputs(C.Structure):
@@ -161,6 +163,8 @@ class DeviceProblem:
     n_hist: int
     n_tgt: int
     max_tgt: int
+    ns: object = None     # HyFormer: non-sequence tokens [B, n_ns, d]
+    qgen: Optional[dict] = None
 
 
 def _dev(a, device):
@@ -181,7 +185,8 @@ def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=Fals
     flags = (FLAG_KV_LN if sp.kv_ln else 0) | (FLAG_Z_LN if sp.z_ln else 0) | (FLAG_DEDUP if dedup else 0)
     cfg = Config(B=sp.B, d=sp.d, H=sp.H, hidden=sp.hidden, M=sp.M, table_rows=sp.table_rows,
                  dtype=BF16 if sp.dtype == "bf16" else F32, score=SCORE[sp.score],
-                 qmode=QMODE[sp.qmode], path=PATH[path], flags=flags, chunk_keys=chunk_keys)
+                 qmode=QMODE[sp.qmode], path=PATH[path], flags=flags, chunk_keys=chunk_keys,
+                 n_ns=sp.n_ns, q_hidden=(sp.hy_hidden or sp.d) if sp.qmode == "hyformer" else 0)
 
     def conv(w):
         if w is None:
@@ -195,7 +200,8 @@ def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=Fals
     return DeviceProblem(cfg, _dev(p.hist_offsets, device), _dev(p.hist_ids, device),
                          _dev(p.tgt_offsets, device), _dev(p.tgt_ids, device), _dev(p.q0, device),
                          table, [conv(l) for l in p.layers], conv(p.z), _dev(p.wz, device),
-                         p.n_hist, p.n_tgt, max(1, int(m.max()) if len(m) else 1))
+                         p.n_hist, p.n_tgt, max(1, int(m.max()) if len(m) else 1),
+                         _dev(p.extra.get("ns"), device), conv(p.extra.get("qgen")))
 
 
 def _ffn(f) -> Ffn:
@@ -207,11 +213,14 @@ def _ffn(f) -> Ffn:
 def _structs(dp: DeviceProblem):
     layers = (Layer * len(dp.layers))()
     for i, l in enumerate(dp.layers):
+        bo = l.get("boost") or {}
         layers[i] = Layer(_ffn(l["kv"]), _ffn(l.get("q")), _ptr(l["wk"]), _ptr(l["wv"]),
-                          _ptr(l["wq"]), _ptr(l["wo"]), _ptr(l.get("wc")), _ptr(l.get("r")))
-    w = Weights(layers, _ffn(dp.z), _ptr(dp.wz))
+                          _ptr(l["wq"]), _ptr(l["wo"]), _ptr(l.get("wc")), _ptr(l.get("r")),
+                          _ptr(bo.get("w1")), _ptr(bo.get("w3")), _ptr(bo.get("w2")))
+    qg = dp.qgen or {}
+    w = Weights(layers, _ffn(dp.z), _ptr(dp.wz), _ptr(qg.get("w1")), _ptr(qg.get("w3")), _ptr(qg.get("w2")))
     b = Batch(_ptr(dp.hist_offsets), _ptr(dp.hist_ids), _ptr(dp.tgt_offsets), _ptr(dp.tgt_ids),
-              _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt)
+              _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt, _ptr(dp.ns))
     return b, w, layers
 
 

@@ -62,7 +62,7 @@ def ws_size(c, b):
     (dict(M=17), stca.ERR_INVALID_ARG),
     (dict(dtype=7), stca.ERR_INVALID_ARG),
     (dict(score=3), stca.ERR_INVALID_ARG),
-    (dict(qmode=2), stca.ERR_INVALID_ARG),
+    (dict(qmode=3), stca.ERR_INVALID_ARG),
     (dict(flags=64), stca.ERR_INVALID_ARG),
     (dict(chunk_keys=33), stca.ERR_INVALID_ARG),
     (dict(table_rows=0), stca.ERR_INVALID_ARG),
@@ -216,3 +216,54 @@ def test_dedup_workspace_and_x_dump():
     w, keep = _weights()
     out = stca.Outputs(z=FAKE, x_dump=FAKE)
     assert _forward(c, b, w, out, dd) == stca.ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------- HyFormer query mode
+def _hy_cfg(**over):
+    c = dict(B=2, d=512, H=8, hidden=1024, M=3, table_rows=1000, dtype=stca.BF16, score=0,
+             qmode=stca.QMODE["hyformer"], path=0, flags=0, chunk_keys=0, n_ns=8, q_hidden=512)
+    c.update(over)
+    return stca.Config(**c)
+
+
+def _hy_batch(**over):
+    b = dict(hist_offsets=FAKE, hist_ids=FAKE, tgt_offsets=FAKE, tgt_ids=None, q0=None,
+             table=FAKE, n_hist=1000, n_tgt=16, max_tgt_per_user=8, ns_feats=FAKE)
+    b.update(over)
+    return stca.Batch(**b)
+
+
+@pytest.mark.parametrize("cover,bover,code", [
+    ({}, {}, stca.OK),
+    (dict(dtype=stca.F32), {}, stca.ERR_UNSUPPORTED),
+    (dict(path=1), {}, stca.ERR_UNSUPPORTED),
+    (dict(q_hidden=0), {}, stca.ERR_UNSUPPORTED),
+    (dict(q_hidden=100), {}, stca.ERR_UNSUPPORTED),
+    (dict(n_ns=-1), {}, stca.ERR_INVALID_ARG),
+    ({}, dict(n_tgt=15), stca.ERR_INVALID_ARG),           # not B * m
+    (dict(n_ns=5), {}, stca.ERR_UNSUPPORTED),             # m + n_ns = 13 does not divide d
+    ({}, dict(ns_feats=None), stca.ERR_INVALID_ARG),
+    (dict(n_ns=0), dict(ns_feats=None), stca.OK),          # no non-sequence tokens: none needed
+])
+def test_hyformer_validation(cover, bover, code):
+    r, n = ws_size(_hy_cfg(**cover), _hy_batch(**bover))
+    assert r == code, stca.last_error()
+    if code == stca.OK:
+        assert n > 0
+
+
+def test_hyformer_forward_needs_query_weights():
+    c, b = _hy_cfg(), _hy_batch()
+    M = c.M
+    layers = (stca.Layer * M)()
+    ffn = stca.Ffn(FAKE, FAKE, FAKE, FAKE, FAKE)
+    for i in range(M):
+        layers[i] = stca.Layer(ffn, ffn, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE)
+    out = stca.Outputs(z=FAKE)
+    w = stca.Weights(layers, stca.Ffn(), None, None, FAKE, FAKE)      # qgen_w1 missing
+    assert _forward(c, b, w, out, 1 << 40) == stca.ERR_INVALID_ARG
+    assert "query-generation" in stca.last_error()
+    w = stca.Weights(layers, stca.Ffn(), None, FAKE, FAKE, FAKE)
+    layers[1].boost_w2 = None
+    assert _forward(c, b, w, out, 1 << 40) == stca.ERR_INVALID_ARG
+    assert "boosting" in stca.last_error()
