@@ -46,6 +46,10 @@ def workload(name):
         return I.spec(4)
     if name == "rlb-train":
         return I.spec(6)
+    if name in ("hyformer-feed", "hyformer-search"):
+        # the HyFormer workload's sequence with generated, boosted queries
+        from dataclasses import replace
+        return replace(I.spec(5)[name.split("-")[1]], qmode="hyformer", n_ns=8)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -66,9 +70,13 @@ def cpu_baseline(p, seconds):
     t0 = time.perf_counter()
     users, toks, tgts = 0, 0, 0
     q0 = O.stored_to_f64(p.q0) if p.q0 is not None else None
+    hy = None
+    if sp.qmode == "hyformer":
+        hy = {"ns": O.stored_to_f64(p.extra["ns"]),
+              "qgen": {k: O.stored_to_f64(v) for k, v in p.extra["qgen"].items()}}
     while users < sp.B:
         O.forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets, rows, layers, z, wz,
-                  tgt_ids=p.tgt_ids, q0=q0, users=[users])
+                  tgt_ids=p.tgt_ids, q0=q0, users=[users], hy=hy)
         toks += int(p.hist_offsets[users + 1] - p.hist_offsets[users])
         tgts += int(p.tgt_offsets[users + 1] - p.tgt_offsets[users])
         users += 1
@@ -281,9 +289,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     stca.load()
-    if args.dedup:
-        args.path = "staged"
     sp = workload(args.workload)
+    if args.dedup or sp.d == 512 or sp.qmode == "hyformer":  # the fused path serves d <= 256, STCA queries
+        args.path = "staged"
     t = time.time()
     p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
     log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} "
@@ -399,6 +407,8 @@ def main():
         "config": {"workload": f"{sp.name}: B={sp.B} users, L={sp.L}, m={sp.m} targets/user (RLB), "
                                f"table {sp.table_rows}x{d} bf16 Zipf({sp.zipf_s}) ids, d={d}, H={H}, "
                                f"hidden={h}, M={M} layers, softmax, path={args.path}"
+                               + (f", HyFormer queries: {sp.n_ns} non-sequence tokens, query FFN hidden "
+                                  f"{sp.hy_hidden or d}, no history LN" if sp.qmode == "hyformer" else "")
                                + (f", unique-id dedup ({n_unique} unique of {n_hist})" if args.dedup else ""),
                    "global_batch": sp.B, "seq_len": sp.L, "targets": T, "parallelism": "single GPU"},
         "target_scores_per_s_per_layer": round(T * M / (ms * 1e-3), 1),
@@ -411,7 +421,7 @@ def main():
                       **({"history": [round(x, 4) for x in hist]} if args.path == "staged" else {}),
                       "query": [round(x, 4) for x in query],
                       ("attn_partial" if args.path == "staged" else "fused"): [round(x, 4) for x in part],
-                      "attn_merge": [round(x, 4) for x in merge], "w_o": [round(x, 4) for x in wo],
+                      "attn_merge": [round(x, 4) for x in merge], ("w_o+boost" if sp.qmode == "hyformer" else "w_o"): [round(x, 4) for x in wo],
                       "z": round(zt, 4)},
     }
     for e in evs:
@@ -422,6 +432,8 @@ def main():
         # row here depends on its id alone)
         del f
         others = [("staged" if args.path == "fused" else "fused", False), ("staged", True)]
+        if sp.d == 512 or sp.qmode == "hyformer":
+            others = [("staged", True)]
         res["other_paths"] = []
         for other, dd in others:
             dpo = stca.upload(p, path=other, table=dp.table, dedup=dd)

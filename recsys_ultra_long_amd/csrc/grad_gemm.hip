@@ -99,8 +99,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
   const int wm = w >> 1, wn = w & 1;
   const int64_t m0 = (int64_t)blockIdx.x * BM, n0 = (int64_t)blockIdx.y * BN;
   int64_t kb = 0, ke = g.K, Meff = g.M;
+  int bz = blockIdx.z;  // batch index (and, split, K range: z = batch * ranges + range)
   if (SPLIT) {
-    kb = (int64_t)blockIdx.z * kchunk;
+    const int ranges = (int)((g.K + kchunk - 1) / kchunk);
+    bz = (int)blockIdx.z / ranges;
+    kb = (int64_t)(blockIdx.z % ranges) * kchunk;
     ke = kb + kchunk < g.K ? kb + kchunk : g.K;
   }
   if (g.dev_rows) {
@@ -116,10 +119,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
   const TA *A = (const TA *)g.A;
   const TB *B = (const TB *)g.B;
   float *Cb = g.C;
-  if (!SPLIT && g.batch > 1) {
-    A += (int64_t)blockIdx.z * g.bsa;
-    B += (int64_t)blockIdx.z * g.bsb;
-    Cb += (int64_t)blockIdx.z * g.bsc;
+  if (g.batch > 1) {
+    A += (int64_t)bz * g.bsa;
+    B += (int64_t)bz * g.bsb;
+    Cb += (int64_t)bz * g.bsc;
   }
   f32x16 acc[2][2];
 #pragma unroll
@@ -185,10 +188,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
 }
 
 // Folds the K ranges in order; with a device cap on K only the ranges that
-// start below it were written.
+// start below it were written.  Partials: [batch][split][M][N].
 __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split, int64_t kchunk) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= g.M * g.N) return;
+  const int64_t MN = g.M * g.N;
+  const int nb = g.batch > 1 ? g.batch : 1;
+  const int64_t ei = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (ei >= MN * nb) return;
+  const int64_t b = ei / MN, e = ei % MN;
+  const int stride = split;
   if (g.dev_rows && g.dev_dim == 2 && kchunk > 0) {
     const int64_t lim = *g.dev_rows;
     const int64_t live = (lim + kchunk - 1) / kchunk;
@@ -196,8 +203,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split
   }
   const int64_t m = e / g.N, n = e % g.N;
   float s = 0.f;
-  for (int z = 0; z < split; ++z) s += g.part[(int64_t)z * g.M * g.N + e];
-  float *c = g.C + m * g.scm + n * g.scn;
+  for (int z = 0; z < split; ++z) s += g.part[((int64_t)b * stride + z) * MN + e];
+  float *c = g.C + b * g.bsc + m * g.scm + n * g.scn;
   const float v = g.alpha * s;
   *c = g.beta != 0.f ? v + g.beta * *c : v;
 }
@@ -215,12 +222,13 @@ hipError_t run(const GemmArgs &g, hipStream_t s) {
     int64_t kchunk = (g.K + g.split - 1) / g.split;
     kchunk = (kchunk + BK - 1) / BK * BK;
     const int split = (int)((g.K + kchunk - 1) / kchunk);
-    if (!g.part || (int64_t)split * g.M * g.N > g.part_cap) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, true>), dim3(gx, gy, split), dim3(256), 0, s, g, kchunk, va,
-                       vb);
+    const int nb = g.batch > 1 ? g.batch : 1;
+    if (!g.part || (int64_t)nb * split * g.M * g.N > g.part_cap) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, AKC, BKC, true>), dim3(gx, gy, (unsigned)(split * nb)), dim3(256), 0, s,
+                       g, kchunk, va, vb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = g.M * g.N;
+    const int64_t n = g.M * g.N * nb;
     hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, split, kchunk);
   } else {
     const unsigned gz = g.batch > 1 ? (unsigned)g.batch : 1u;
@@ -251,7 +259,6 @@ int gemm_split_for(int64_t M, int64_t N, int64_t K, int64_t target, int64_t min_
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (!((g.sak == 1 || g.sam == 1) && (g.sbk == 1 || g.sbn == 1))) return hipErrorInvalidValue;
-  if (g.batch > 1 && g.split > 1) return hipErrorInvalidValue;
   if (g.K <= 0) {  // empty sum: C = beta * C
     GemmArgs z = g;
     z.split = 1;

@@ -55,8 +55,8 @@ struct GemmArgs {
   int64_t part_cap;  // floats in `part`: a split needing more is refused
   const int *dev_rows;
   int dev_dim;
-  // batch > 1 (no split): blockIdx.z picks problem z, whose A, B, C start
-  // z * bsa, z * bsb, z * bsc elements further
+  // batch > 1: `batch` problems whose A, B, C start z * bsa, z * bsb, z * bsc
+  // elements further (with split > 1 the partials are [batch][split][M][N])
   int batch;
   int64_t bsa, bsb, bsc;
 };
@@ -127,9 +127,11 @@ int64_t attn_bwd_part_floats(int64_t max_chunks, int H, int dh);
 hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s);
 
 // ------------------------------------------------------------ HyFormer queries
-// mp[u, :] = mean of the table rows of user u's history (zero when empty)
+// mp[u, :] = mean of the table rows of user u's history (zero when empty);
+// part: mean_pool_part_floats(B, d) floats of scratch
+int64_t mean_pool_part_floats(int B, int d);
 hipError_t launch_mean_pool(const bf16_t *table, int64_t table_rows, const int *hist_ids, const Plan &plan, int B,
-                            int d, float *mp, hipStream_t s);
+                            int d, float *mp, float *part, hipStream_t s);
 // g[u] = [F_u,1 .. F_u,n_ns | mp[u]] (fp32, [B, (n_ns + 1) d]) from bf16 F
 hipError_t launch_global_info(const bf16_t *ns, const float *mp, int B, int n_ns, int d, float *g, hipStream_t s);
 // qcur[u m + n] = bf16(src[n][u]) for src [m][B][d] fp32

@@ -4,8 +4,8 @@
 // kernel (grad_ops.hip).
 //
 //   MeanPool(Seq): per user, the mean of the raw history rows (one pass over
-//     the history, four waves per (user, 64-feature slice) taking every
-//     fourth row, folded in wave order);
+//     the history: 16 interleaved row chunks per user, partial sums folded
+//     in a fixed order);
 //   GlobalInfo = Concat(F_1..F_M, MeanPool(Seq)) per user;
 //   boosting input: Q = [decoded queries | F] per user (T = m + n_ns tokens),
 //     and its mixed form, grouped by mixed token so that each token's FFN is
@@ -20,23 +20,56 @@ namespace {
 
 constexpr int kT = 256;
 
-__global__ __launch_bounds__(kT) void mean_pool_kernel(const bf16_t *__restrict__ table, int64_t table_rows,
-                                                       const int *__restrict__ ids, Plan P, int B, int d,
-                                                       float *mp) {
+// Partial sums of user u's rows in chunk c (rows c, c + kPoolChunks, ..):
+// four waves x four rows in flight, folded in wave order; then the chunks
+// are folded in order.  The order depends on the lengths alone.
+constexpr int kPoolChunks = 16;
+
+__global__ __launch_bounds__(kT) void mean_pool_part_kernel(const bf16_t *__restrict__ table, int64_t table_rows,
+                                                            const int *__restrict__ ids, Plan P, int B, int d,
+                                                            float *part) {
   __shared__ float sm[4][64];
-  const int u = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int u = blockIdx.x / kPoolChunks, c = blockIdx.x % kPoolChunks;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int f = blockIdx.y * 64 + lane;
   if (u >= B) return;
   const int h0 = P.hoff[u], L = P.hoff[u + 1] - h0;
+  // this wave's rows: j = c + kPoolChunks * (w + 4 k), k = 0, 1, ..
+  constexpr int S = 4 * kPoolChunks;
   float s = 0.f;
-  if (f < d)
-    for (int j = w; j < L; j += 4) {
+  if (f < d) {
+    int j = c + kPoolChunks * w;
+    for (; j + 3 * S < L; j += 4 * S) {
+      int id[4];
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) id[q] = ids[h0 + j + q * S];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = (id[q] >= 0 && (int64_t)id[q] < table_rows) ? bf2f(table[(int64_t)id[q] * d + f]) : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += v[q];
+    }
+    for (; j < L; j += S) {
       const int id = ids[h0 + j];
       if (id >= 0 && (int64_t)id < table_rows) s += bf2f(table[(int64_t)id * d + f]);
     }
+  }
   sm[w][lane] = s;
   __syncthreads();
-  if (w == 0 && f < d) mp[(int64_t)u * d + f] = L > 0 ? (((sm[0][lane] + sm[1][lane]) + sm[2][lane]) + sm[3][lane]) / L : 0.f;
+  if (w == 0 && f < d)
+    part[((int64_t)u * kPoolChunks + c) * d + f] = ((sm[0][lane] + sm[1][lane]) + sm[2][lane]) + sm[3][lane];
+}
+
+__global__ __launch_bounds__(kT) void mean_pool_fold_kernel(const float *__restrict__ part, Plan P, int B, int d,
+                                                            float *mp) {
+  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (e >= (int64_t)B * d) return;
+  const int64_t u = e / d, f = e % d;
+  const int L = P.hoff[u + 1] - P.hoff[u];
+  float s = 0.f;
+  for (int c = 0; c < kPoolChunks; ++c) s += part[(u * kPoolChunks + c) * d + f];
+  mp[e] = L > 0 ? s / L : 0.f;
 }
 
 __global__ __launch_bounds__(kT) void global_info_kernel(const bf16_t *__restrict__ ns, const float *__restrict__ mp,
@@ -89,11 +122,16 @@ unsigned blocks(int64_t n) { return (unsigned)((n + kT - 1) / kT); }
 
 }  // namespace
 
+int64_t mean_pool_part_floats(int B, int d) { return (int64_t)B * kPoolChunks * d; }
+
 hipError_t launch_mean_pool(const bf16_t *table, int64_t table_rows, const int *hist_ids, const Plan &plan, int B,
-                            int d, float *mp, hipStream_t s) {
+                            int d, float *mp, float *part, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mean_pool_kernel, dim3((unsigned)B, (unsigned)((d + 63) / 64)), dim3(kT), 0, s, table,
-                     table_rows, hist_ids, plan, B, d, mp);
+  hipLaunchKernelGGL(mean_pool_part_kernel, dim3((unsigned)(B * kPoolChunks), (unsigned)((d + 63) / 64)), dim3(kT),
+                     0, s, table, table_rows, hist_ids, plan, B, d, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mean_pool_fold_kernel, dim3(blocks((int64_t)B * d)), dim3(kT), 0, s, part, plan, B, d, mp);
   return hipGetLastError();
 }
 

@@ -98,6 +98,8 @@ struct Layout {
   size_t plan = 0, prep = 0, kv = 0, kv_layer = 0, part_ml = 0, part_acc = 0, part_cnt = 0, fstate = 0;
   size_t xt = 0, ocat = 0, qs = 0, attn32 = 0, attnlo = 0, qcur = 0, total = 0;
   size_t hy_mp = 0, hy_g = 0, hy_h13 = 0, hy_gg = 0, hy_out = 0, hy_qcat = 0, hy_qmix = 0, hy_o32 = 0;
+  size_t hy_pool = 0, hy_part = 0;
+  int64_t hy_part_floats = 0;
   std::vector<PrepLayer> pl;
   size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
 };
@@ -266,6 +268,16 @@ int validate_weights(const stca_config *c, const stca_weights *w) {
   return STCA_OK;
 }
 
+// Split-K of the HyFormer query FFN products: n problems of [M x N] over K,
+// aiming at ~512 workgroups in all.
+int hy_split(int64_t n, int64_t M, int64_t N, int64_t K) {
+  return gemm_split_for(M, N, K, std::max<int64_t>(1, 512 / std::max<int64_t>(n, 1)), 128);
+}
+int64_t hy_part_floats(int64_t n, int64_t M, int64_t N, int64_t K) {
+  const int sp = hy_split(n, M, N, K);
+  return sp > 1 ? n * sp * M * N : 0;
+}
+
 Layout make_layout(const stca_config *c, const stca_batch *b) {
   Layout L;
   const int64_t d = c->d, h = c->hidden, T = b->n_tgt;
@@ -354,6 +366,12 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
     L.hy_qcat = cv.take(Bu * Tk * d * 4);
     L.hy_qmix = cv.take(Bu * Tk * d * 4);
     L.hy_o32 = cv.take(T * d * 4);
+    L.hy_pool = cv.take((size_t)mean_pool_part_floats(c->B, (int)d) * 4);
+    const int64_t din = (int64_t)(c->n_ns + 1) * d;
+    int64_t pf = std::max({hy_part_floats(m, Bu, hq, din), hy_part_floats(Tk, Bu, hq, d),
+                           hy_part_floats(m, Bu, d, hq), hy_part_floats(Tk, Bu, d, hq)});
+    L.hy_part_floats = pf;
+    L.hy_part = cv.take((size_t)pf * 4);
   }
   L.total = cv.off;
   return L;
@@ -767,6 +785,9 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     g.bsa = a_bs;
     g.bsb = din * hq;
     g.bsc = (int64_t)B * 2 * hq;
+    g.part = at<float>(ws, L.hy_part);
+    g.part_cap = L.hy_part_floats;
+    g.split = hy_split(n, B, hq, din);
     hipError_t er = launch_gemm(g, s);
     if (er) return er;
     g.B = w3;
@@ -784,11 +805,13 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     g.C = hy_out;
     g.scm = d;
     g.bsc = (int64_t)B * d;
+    g.split = hy_split(n, B, d, hq);
     return launch_gemm(g, s);
   };
   if (hyf) {  // q_u,n = FFN_n([F_u | MeanPool(rows of u)])
     float *mp = at<float>(ws, L.hy_mp), *gi = at<float>(ws, L.hy_g);
-    e = launch_mean_pool((const bf16_t *)batch->table, cfg->table_rows, batch->hist_ids, plan, B, d, mp, s);
+    e = launch_mean_pool((const bf16_t *)batch->table, cfg->table_rows, batch->hist_ids, plan, B, d, mp,
+                         at<float>(ws, L.hy_pool), s);
     if (!e) e = launch_global_info((const bf16_t *)batch->ns_feats, mp, B, cfg->n_ns, d, gi, s);
     const int64_t din = (int64_t)(cfg->n_ns + 1) * d;
     if (!e) e = ffn_stack(hm, gi, din, 0, w->qgen_w1, w->qgen_w3, w->qgen_w2);
