@@ -42,6 +42,12 @@ Readings taken where the pages are silent (each one is listed in the design doc):
 * Empty history: attention output 0, active count 0.
 * HyFormer linear mode: Q_{l+1} = O_l R_l, output O_M ([HyFormer] eq. (9),
   (16), with the boosting block replaced by a fixed linear map).
+* Cross-Mask ([WeChat] §3.2-3.3): a vertical mask keeps, per head (one
+  feature domain's column slice, its horizontal mask), only the history items
+  its condition selects: softmax / ReLU over those items, 0 when none; heads
+  sharing an attention map score with the same Q / K columns (a head map)
+  under their own masks and V columns.  The context-similarity score bias the
+  page mentions has no formula there and is not modelled.
 * HyFormer query mode ([HyFormer] §3.3.2 eq. (3)-(4), §3.5 eq. (10)-(15),
   §3.6 eq. (16)-(17)): every "FFN" is the SwiGLU block above without LN; the
   N queries of a user are FFN_n(Concat(F_1, ..., F_M, MeanPool(Seq))) with
@@ -104,7 +110,7 @@ def ffn_ln(x: np.ndarray, w: dict, ln: bool) -> np.ndarray:
 
 # ---------------------------------------------------------------- attention
 def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
-                     scale: Optional[float] = None):
+                     scale: Optional[float] = None, key_mask=None, head_map=None):
     """One target (query row ``Q`` of width d, already multiplied by W_Q)
     against one user's keys K and values V ([L, d] each).
 
@@ -115,6 +121,11 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
     ([Review] formula for alpha and o; [WeChat] §1.2 for the ReLU form.)
 
     ``scale`` defaults to 1/sqrt(d_h); pass 1.0 when ``Q`` already carries it.
+
+    Cross-Mask ([WeChat] §3.2-3.3): ``key_mask`` [L] (ints) keeps, for head
+    eta, only the keys whose bit eta is set (a head with none gives 0);
+    ``head_map[eta]`` names the head whose Q / K columns give head eta's
+    scores (V and the output stay head eta's columns).
 
     Returns (a [d], cnt [H], amb [H]) where ``amb`` counts the scores whose
     sign an fp32 evaluation of the same operands could flip:
@@ -132,16 +143,25 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
         return a, cnt, amb
     for eta in range(H):
         cols = slice(eta * dh, (eta + 1) * dh)
-        q = Q[cols]
-        s = (K[:, cols] @ q) * scale
+        qk = eta if head_map is None else int(head_map[eta])
+        qcols = slice(qk * dh, (qk + 1) * dh)
+        if key_mask is None:
+            Ke, Ve = K, V
+        else:
+            sel = ((np.asarray(key_mask, dtype=np.int64) >> eta) & 1).astype(bool)
+            if not sel.any():
+                continue                      # no visible key: output 0
+            Ke, Ve = K[sel], V[sel]
+        q = Q[qcols]
+        s = (Ke[:, qcols] @ q) * scale
         if score == "softmax":
             p = np.exp(s - s.max())
-            a[cols] = (p @ V[:, cols]) / p.sum()
+            a[cols] = (p @ Ve[:, cols]) / p.sum()
         elif score == "relu":
             w = np.maximum(s, 0.0)
-            a[cols] = w @ V[:, cols]
+            a[cols] = w @ Ve[:, cols]
             cnt[eta] = int(np.count_nonzero(s > 0.0))
-            bound = dh * 2.0 ** -23 * (np.abs(K[:, cols]) @ np.abs(q)) * scale
+            bound = dh * 2.0 ** -23 * (np.abs(Ke[:, qcols]) @ np.abs(q)) * scale
             amb[eta] = int(np.count_nonzero(np.abs(s) <= bound))
         else:
             raise ValueError(score)
@@ -149,14 +169,14 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
 
 
 def attention_core(Qs: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
-                   scale: Optional[float] = None):
+                   scale: Optional[float] = None, key_mask=None, head_map=None):
     """Every target of one user: rows of ``Qs`` handled one at a time."""
     m, d = Qs.shape
     attn = np.zeros((m, d))
     cnt = np.zeros((m, H), dtype=np.int64)
     amb = np.zeros((m, H), dtype=np.int64)
     for t in range(m):
-        attn[t], cnt[t], amb[t] = attention_target(Qs[t], K, V, H, score, scale)
+        attn[t], cnt[t], amb[t] = attention_target(Qs[t], K, V, H, score, scale, key_mask, head_map)
     return attn, cnt, amb
 
 
@@ -217,7 +237,8 @@ def encode_history(X: np.ndarray, lw: dict, kv_ln: bool):
 
 
 def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=None, wz=None,
-            tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q"), hy=None):
+            tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q"), hy=None,
+            key_mask=None, head_map=None):
     """The STCA forward for the users in ``users`` (default: all).
 
     cfg: dict with d, H, M, score ("softmax"|"relu"), qmode ("fusion"|"linear"),
@@ -246,6 +267,8 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
         # Request Level Batching: the user's K/V of every layer is computed
         # once and serves all of the user's targets ([Notes] §RLB).
         KV = [encode_history(X, layers[i], cfg["kv_ln"]) for i in range(M)]
+        km = None if key_mask is None else np.asarray(key_mask)[ho[u]:ho[u + 1]]
+        cm = dict(key_mask=km, head_map=head_map)
         if qmode == "hyformer":
             t0, t1 = int(to[u]), int(to[u + 1])
             F = hy["ns"][u]
@@ -255,7 +278,7 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
                 dec = np.zeros((t1 - t0, d))
                 for n in range(t1 - t0):
                     Q = q[n] @ layers[i]["wq"]
-                    a, c, amb = attention_target(Q, K, V, H, score)
+                    a, c, amb = attention_target(Q, K, V, H, score, **cm)
                     dec[n] = a @ layers[i]["wo"]
                     out["qs"][i, t0 + n] = Q
                     out["attn"][i, t0 + n] = a
@@ -275,7 +298,7 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
             for i in range(M):
                 Q = q @ layers[i]["wq"]
                 K, V = KV[i]
-                a, c, amb = attention_target(Q, K, V, H, score)
+                a, c, amb = attention_target(Q, K, V, H, score, **cm)
                 o = a @ layers[i]["wo"]
                 outs.append(o)
                 out["qs"][i, t] = Q
@@ -310,4 +333,5 @@ def forward_problem(p, users=None):
               "qgen": {k: stored_to_f64(v) for k, v in p.extra["qgen"].items()}}
     return forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets,
                    lambda ids: stored_to_f64(p.rows(ids)), layers, z, wz,
-                   tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users, hy=hy)
+                   tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users, hy=hy,
+                   key_mask=p.extra.get("key_mask"), head_map=p.extra.get("head_map"))

@@ -147,6 +147,19 @@ def spec(k: int, **over) -> Spec | dict:
     return replace(s, **over)
 
 
+def cross_mask(sp: Spec, n_hist: int, masked_heads, keep: float = 0.5, seed: int = 0) -> np.ndarray:
+    """Seeded Cross-Mask vertical masks [n_hist] (uint32): every head sees
+    every item except the heads in ``masked_heads``, which see an item with
+    probability ``keep`` (a stand-in for a per-item feature condition such as
+    "action = complete")."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 0x4D41, seed])))
+    m = np.full(n_hist, (1 << sp.H) - 1, dtype=np.uint64)
+    for h in masked_heads:
+        off = g.random(n_hist) >= keep
+        m[off] &= ~np.uint64(1 << h)
+    return m.astype(np.uint32)
+
+
 def upstream_grad(sp: Spec, n_tgt: int, seed: int = 0) -> np.ndarray:
     """Seeded upstream gradient dL/dz [n_tgt, d] (float32) for the backward."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 7919, seed])))
@@ -374,4 +387,6 @@ def subset_users(p: Problem, users) -> Problem:
                    cat(tid, np.int32) if p.tgt_ids is not None else None,
                    (np.concatenate(q0) if q0 else None) if p.q0 is not None else None,
                    p.table, p.layers, p.z, p.wz,
-                   {**p.extra, **({"ns": p.extra["ns"][users]} if "ns" in p.extra else {})})
+                   {**p.extra, **({"ns": p.extra["ns"][users]} if "ns" in p.extra else {}),
+                    **({"key_mask": np.concatenate([p.extra["key_mask"][ho[u]:ho[u + 1]] for u in users])
+                        .astype(np.uint32)} if "key_mask" in p.extra else {})})
