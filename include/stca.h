@@ -113,6 +113,11 @@ typedef struct {
   int32_t chunk_keys;   /* keys per split-L chunk (multiple of 32); 0 = automatic  */
   int32_t n_ns;         /* STCA_Q_HYFORMER: non-sequence feature tokens per user   */
   int32_t q_hidden;     /* STCA_Q_HYFORMER: hidden width of the query FFNs (x32)   */
+  const int32_t *head_map; /* host [H] or NULL: Cross-Mask shared attention maps
+                           ([WeChat] §3.3.1, several heads share one attention map
+                           under different masks): head h scores with the Q / K
+                           columns of head head_map[h] (values in [0, H)); its V
+                           columns and output slice stay its own.  Staged bf16 only */
 } stca_config;
 
 /* One batch of requests: ragged histories and targets in CSR form.
@@ -130,6 +135,11 @@ typedef struct {
   int64_t n_tgt;                /* host: total targets, < 2^31                      */
   int32_t max_tgt_per_user;     /* host: upper bound on any m_u, 1..4096            */
   const void *ns_feats;         /* [B, n_ns, d] non-sequence tokens (STCA_Q_HYFORMER) */
+  const uint32_t *key_mask;     /* [n_hist] or NULL: Cross-Mask vertical masks ([WeChat]
+                                   §3.2): bit h set = history item j is visible to head h
+                                   (its feature-domain condition holds, e.g. "action =
+                                   complete"); softmax and ReLU then run over the visible
+                                   items only, a head with none gives 0.  Staged bf16 only */
 } stca_batch;
 
 /* SwiGLU FFN d -> h -> d, optionally followed by LayerNorm (eps 1e-5):
@@ -233,6 +243,8 @@ typedef struct {
   float *attn;              /* [n_tgt, d] output */
   int32_t *active;          /* [n_tgt, H] output, ReLU only (optional) */
   int32_t *dev_status;      /* optional */
+  const uint32_t *key_mask; /* [n_hist] or NULL, as stca_batch.key_mask (bf16 only) */
+  const int32_t *head_map;  /* host [H] or NULL, as stca_config.head_map (bf16 only) */
 } stca_attn_args;
 
 int stca_attention_workspace_size(const stca_attn_args *a, size_t *bytes);

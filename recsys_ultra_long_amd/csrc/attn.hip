@@ -69,7 +69,14 @@ DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
 // rows' blocked K (16 bytes per lane, as above); the V rows of a block are
 // read row-major (a.vrows) and written transposed into a wave-private LDS
 // tile, from which the V^T fragments are read.
-template <int DH, int NT, int SCORE, bool IND>
+//
+// MASK (Cross-Mask vertical masks, [WeChat] §3.2): each lane also loads the
+// mask word of key lane % 32 of a block (in the same pipeline stage as K/V),
+// and one ballot turns the head's bit of the 32 words into the block's
+// visibility word.  A head map (a.has_map) takes head h's scores from the
+// Q / K columns of head a.head_map[h] ([WeChat] §3.3.1: heads sharing one
+// attention map under different masks); V and the output stay head h's.
+template <int DH, int NT, int SCORE, bool IND, bool MASK>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
   constexpr int DT = DH / 16;  // feature tiles of the output
@@ -97,6 +104,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const UnitPos pos = decode_unit(P, a.B, HG, unit);
     const int seg_end = min(unit_end, pos.first + pos.nc);
     const int u = pos.u, grp = pos.pair / H, h = pos.pair % H;
+    const int hq = a.has_map ? a.head_map[h] : h;  // the head whose Q / K give the scores
     const int tbase = P.toff[u];
     const int m_u = P.toff[u + 1] - tbase;
     const int t0 = grp * TG;
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
       AttnState<DH, NT> st;
       attn_reset(st);
-      attn_load_q(st, Q, a.d, h, tbase, t0, m_u, lane);
+      attn_load_q(st, Q, a.d, hq, tbase, t0, m_u, lane);
       bf16x8 kf[2][KS], vf[DT];
       // IND: the V rows of a block come as DT 16-byte chunks per lane: chunk
       // lane + 64 i = (key, part) with DH / 8 parts of 8 features per key
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             for (int k = 0; k < KS; ++k) {
               bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
               kk[kt][k] = ui < 0 ? z
-                                 : ld8(Kb + ((((int64_t)(ui >> 5)) * H + h) * 32 + (ui & 31)) * DH + k * 32 + g16 * 8);
+                                 : ld8(Kb + ((((int64_t)(ui >> 5)) * H + hq) * 32 + (ui & 31)) * DH + k * 32 + g16 * 8);
             }
           }
 #pragma unroll
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             vv[i] = ui < 0 ? z : ld8(Vr + (int64_t)ui * a.d + h * DH + part * 8);
           }
         } else {
-          const bf16_t *kb = Kb + ((int64_t)b * H + h) * 32 * DH;
+          const bf16_t *kb = Kb + ((int64_t)b * H + hq) * 32 * DH;
           const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
@@ -185,24 +193,44 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int t = 0; t < DT; ++t) out[t] = raw[t];
         }
       };
+      // MASK: the mask word of key lane % 32 of block b (0 past the history)
+      auto load_mask = [&](int b) -> uint32_t {
+        const int key = lane & 31, j = (b - P.pblk[u]) * 32 + key;
+        return j < L ? a.key_mask[tok0 + (int64_t)b * 32 + key] : 0u;
+      };
+      uint32_t mk = 0, mk1 = 0;
       // two blocks of this wave in flight ahead of the one being used: the
       // loads, not the arithmetic, set the pace once the block step is lean
       bf16x8 k1[2][KS], v1[DT];
-      if (b0 + w < b1) load_kv(b0 + w, kf, vf);
-      if (b0 + w + 4 < b1) load_kv(b0 + w + 4, k1, v1);
+      if (b0 + w < b1) {
+        load_kv(b0 + w, kf, vf);
+        if (MASK) mk = load_mask(b0 + w);
+      }
+      if (b0 + w + 4 < b1) {
+        load_kv(b0 + w + 4, k1, v1);
+        if (MASK) mk1 = load_mask(b0 + w + 4);
+      }
       if (IND && b0 + w + 8 < b1) load_uids(b0 + w + 8, U8);
       for (int b = b0 + w; b < b1; b += 4) {
         bf16x8 k2[2][KS], v2[DT];
         Uids U12;
         // uids first: waiting for them later does not wait for the rows below
         if (IND && b + 12 < b1) load_uids(b + 12, U12);
-        if (b + 8 < b1) load_kv(b + 8, k2, v2);
+        uint32_t mk2 = 0;
+        if (b + 8 < b1) {
+          load_kv(b + 8, k2, v2);
+          if (MASK) mk2 = load_mask(b + 8);
+        }
         if (IND) U8 = U12;
         __builtin_amdgcn_sched_barrier(0);
         // keys of this lane: 8g + 4kt + r; valid while below the user's length
         bf16x8 vuse[DT];
         v_fragments(vf, vuse);
-        attn_block<DH, NT, SCORE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, lane);
+        uint32_t kvis = 0xffffffffu;
+        if (MASK) kvis = (uint32_t)__ballot((mk >> h) & 1u);  // lanes 0..31: keys 0..31
+        attn_block<DH, NT, SCORE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
+        mk = mk1;
+        mk1 = mk2;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -470,13 +498,13 @@ int persistent_grid(K kernel, int threads, int64_t units) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * per_cu));
 }
 
-template <int DH, int SCORE, bool IND>
+template <int DH, int SCORE, bool IND, bool MASK>
 hipError_t launch_bf16(AttnArgs &a, hipStream_t s) {
   const int nt = a.groups > 1 ? 4 : (a.max_tgt + 15) / 16;
   const dim3 block(256);
 #define GO(NT)                                                                         \
   {                                                                                    \
-    auto k = attn_bf16_kernel<DH, NT, SCORE, IND>;                                     \
+    auto k = attn_bf16_kernel<DH, NT, SCORE, IND, MASK>;                               \
     a.grid = persistent_grid(k, 256, a.max_units);                                     \
     hipLaunchKernelGGL(k, dim3(a.grid), block, 0, s, a);                               \
   }
@@ -491,15 +519,19 @@ hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
   a.grid = 0;
   if (a.max_units <= 0 || a.n_tgt <= 0) return hipSuccess;
   if (a.dtype == 1) {
-    if (a.tok2u) {
-      if (a.dh == 32) return a.score ? launch_bf16<32, 1, true>(a, s) : launch_bf16<32, 0, true>(a, s);
-      if (a.dh == 64) return a.score ? launch_bf16<64, 1, true>(a, s) : launch_bf16<64, 0, true>(a, s);
-      return hipErrorInvalidValue;
-    }
-    if (a.dh == 32) return a.score ? launch_bf16<32, 1, false>(a, s) : launch_bf16<32, 0, false>(a, s);
-    if (a.dh == 64) return a.score ? launch_bf16<64, 1, false>(a, s) : launch_bf16<64, 0, false>(a, s);
-    return hipErrorInvalidValue;
+#define SEL(IND, MASK)                                                                                      \
+  {                                                                                                         \
+    if (a.dh == 32) return a.score ? launch_bf16<32, 1, IND, MASK>(a, s) : launch_bf16<32, 0, IND, MASK>(a, s); \
+    if (a.dh == 64) return a.score ? launch_bf16<64, 1, IND, MASK>(a, s) : launch_bf16<64, 0, IND, MASK>(a, s); \
+    return hipErrorInvalidValue;                                                                            \
   }
+    if (a.tok2u) {
+      if (a.key_mask) SEL(true, true) else SEL(true, false)
+    }
+    if (a.key_mask) SEL(false, true) else SEL(false, false)
+#undef SEL
+  }
+  if (a.key_mask || a.has_map) return hipErrorInvalidValue;  // fp32: no Cross-Mask
 #define GO(DH, SC)                                                   \
   {                                                                  \
     auto k = attn_f32_kernel<DH, SC>;                                \

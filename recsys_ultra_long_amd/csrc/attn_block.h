@@ -81,13 +81,18 @@ DEV void attn_load_q(AttnState<DH, NT> &s, const bf16_t *Q, int d, int h, int64_
 constexpr float kAttnLazy = 8.0f / kAttnLog2e;
 
 // One block: kf = K fragments (score tiles 0/1, k-steps), vf = V^T fragments
-// (feature tiles); keys at or beyond nvalid (block-local) are masked.
+// (feature tiles); keys at or beyond nvalid (block-local) are masked, and so
+// is every key j whose bit j of kvis is clear (a Cross-Mask vertical mask,
+// [WeChat] §3.2: the head attends only to the rows its feature-domain
+// condition selects).  Masked keys take weight 0 and no part in the max.
 template <int DH, int NT, int SCORE>
 DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const bf16x8 (&vf)[DH / 16],
-                    int nvalid, int lane) {
+                    int nvalid, uint32_t kvis, int lane) {
   constexpr int KS = DH / 32, DT = DH / 16;
   const int g = lane >> 4;
-  const bool full = nvalid >= 32;  // uniform: only a user's last block is partial
+  // uniform: only a user's last block is partial, and masks are per block
+  const bool full = nvalid >= 32 && kvis == 0xffffffffu;
+  auto visible = [&](int j) { return j < nvalid && ((kvis >> j) & 1u); };
   f32x4 st[2][NT];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -106,7 +111,7 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
         for (int n = 0; n < NT; ++n)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (8 * g + 4 * kt + r >= nvalid) st[kt][n][r] = kAttnNegBig;
+            if (!visible(8 * g + 4 * kt + r)) st[kt][n][r] = kAttnNegBig;
     }
     float mx[NT];
     bool raise = false;
@@ -138,6 +143,13 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) pv[4 * kt + r] = attn_ex2(fmaf(st[kt][n][r], kAttnLog2e, -mb));
+      if (!full) {  // exactly 0, also while no visible key has raised the max yet
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!visible(8 * g + 4 * kt + r)) pv[4 * kt + r] = 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t pr = pack_bf2(pv[e], pv[e + 1]);
@@ -154,7 +166,7 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sc = st[kt][n][r];
-          const bool on = (full || 8 * g + 4 * kt + r < nvalid) && sc > 0.f;
+          const bool on = (full || visible(8 * g + 4 * kt + r)) && sc > 0.f;
           s.cnt[n] += on ? 1 : 0;
           pv[4 * kt + r] = on ? sc : 0.f;
         }

@@ -779,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArg
             kf[kt][k] = ld8(kst + (hh * 64 + blk * 32 + kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
 #pragma unroll
         for (int t = 0; t < DT; ++t) vf[t] = ld8(vst + (hh * DH + t * 16 + c16) * 64 + blk * 32 + g16 * 8);
-        attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, lane);
+        attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, 0xffffffffu, lane);
       }
       if (!last) {
 #pragma unroll

@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs a
         const int f = head * DH + t * 16 + c16;
         vf[t] = ld8(vst + f * kR + (((blk * 4 + g16) ^ (f & 15)) * 8));
       }
-      attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, lane);
+      attn_block<DH, NT, SCORE>(st, kf, vf, nvalid, 0xffffffffu, lane);
     }
     if (!last) {
 #pragma unroll

@@ -168,6 +168,25 @@ int validate_dedup(const stca_config *c) {
   return STCA_OK;
 }
 
+int validate_map(const int32_t *map, int H) {
+  if (!map) return STCA_OK;
+  if (H > 16) return fail(STCA_ERR_UNSUPPORTED, "head_map supports at most 16 heads (got %d)", H);
+  for (int h = 0; h < H; ++h)
+    if (map[h] < 0 || map[h] >= H) return fail(STCA_ERR_INVALID_ARG, "head_map[%d] = %d outside [0, %d)", h, map[h], H);
+  return STCA_OK;
+}
+
+// Cross-Mask masks and maps: the staged bf16 attention implements them
+int validate_cross_mask(const stca_config *c, const stca_batch *b) {
+  const bool any = c->head_map || (b && b->key_mask);
+  if (!any) return STCA_OK;
+  if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need bf16");
+  if (c->path != STCA_PATH_STAGED) return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need the staged path");
+  if (b && b->key_mask && ((reinterpret_cast<uintptr_t>(b->key_mask) & 15u)))
+    return fail(STCA_ERR_INVALID_ARG, "key_mask not 16-byte aligned");
+  return validate_map(c->head_map, c->H);
+}
+
 int validate_fused(const stca_config *c, const stca_batch *b) {
   if (c->path != STCA_PATH_FUSED) return STCA_OK;
   const int dh = c->d / c->H;
@@ -215,6 +234,7 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
   int r = validate_dedup(c);
   if (r) return r;
+  if ((r = validate_cross_mask(c, b))) return r;
   return validate_fused(c, b);
 }
 
@@ -604,6 +624,11 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     at_.attn_lo = at<void>(ws, L.attnlo);
     at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
     at_.lse = (out->lse && cfg->score == STCA_SCORE_SOFTMAX) ? out->lse + (size_t)i * T * H : nullptr;
+    at_.key_mask = batch->key_mask;
+    if (cfg->head_map) {
+      at_.has_map = 1;
+      for (int hh = 0; hh < H; ++hh) at_.head_map[hh] = cfg->head_map[hh];
+    }
     at_.B = B;
     if (batch->n_hist == 0) at_.max_units = 0;
     return at_;
@@ -993,10 +1018,12 @@ static int attn_validate(const stca_attn_args *a) {
   if (a->B > 0 && (!a->hist_offsets || !a->tgt_offsets)) return fail(STCA_ERR_INVALID_ARG, "offsets NULL");
   if (a->n_tgt > 0 && (!a->q || !a->attn)) return fail(STCA_ERR_INVALID_ARG, "q / attn NULL");
   if (a->n_hist > 0 && (!a->k || !a->v)) return fail(STCA_ERR_INVALID_ARG, "k / v NULL");
-  const void *ptrs[] = {a->hist_offsets, a->tgt_offsets, a->q, a->k, a->v, a->attn, a->active};
+  const void *ptrs[] = {a->hist_offsets, a->tgt_offsets, a->q, a->k, a->v, a->attn, a->active, a->key_mask};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "pointer %p not 16-byte aligned", p);
-  return STCA_OK;
+  if ((a->key_mask || a->head_map) && a->dtype != STCA_BF16)
+    return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need bf16");
+  return validate_map(a->head_map, a->H);
 }
 
 struct AttnLayout {
@@ -1078,6 +1105,11 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   at_.attn = a->attn;
   at_.active = a->active;
   at_.B = a->B;
+  at_.key_mask = a->key_mask;
+  if (a->head_map) {
+    at_.has_map = 1;
+    for (int hh = 0; hh < a->H; ++hh) at_.head_map[hh] = a->head_map[hh];
+  }
   if ((e = launch_attention(at_, s))) return hip_fail(e, "attention");
   return STCA_OK;
 }

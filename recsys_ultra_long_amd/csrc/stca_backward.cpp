@@ -176,6 +176,8 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
   if (!b) return api_error(STCA_ERR_INVALID_ARG, "batch is NULL");
   if (c->dtype != STCA_BF16) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward is bf16 only");
   if (c->qmode != STCA_Q_FUSION) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs STCA_Q_FUSION");
+  if (c->head_map || b->key_mask)
+    return api_error(STCA_ERR_UNSUPPORTED, "stca_backward does not take Cross-Mask key_mask / head_map");
   if (c->H <= 0 || c->d % c->H) return api_error(STCA_ERR_INVALID_ARG, "d %% H != 0");
   const int dh = c->d / c->H;
   if (dh != 32 && dh != 64) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs d_h 32 or 64 (got %d)", dh);

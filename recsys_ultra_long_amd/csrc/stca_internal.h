@@ -168,6 +168,12 @@ struct AttnArgs {
   int *active;              // [n_tgt, H] (optional)
   float *lse;               // [n_tgt, H] (optional, softmax): max + ln(sum of weights)
   int B;
+  // Cross-Mask ([WeChat] §3.2-3.3): key_mask[token] bit h = the key is visible
+  // to head h (NULL: all visible); head_map[h] = the head whose Q/K columns
+  // give head h's scores (has_map; V and the output stay head h's own)
+  const uint32_t *key_mask;
+  int has_map;
+  int head_map[16];
 };
 
 // Partials + merge.  launch_attn_partial fills a.grid, which the merge reads.

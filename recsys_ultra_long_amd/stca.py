@@ -37,13 +37,13 @@ class Config(C.Structure):
                 ("M", C.c_int32), ("table_rows", C.c_int64), ("dtype", C.c_int32),
                 ("score", C.c_int32), ("qmode", C.c_int32), ("path", C.c_int32),
                 ("flags", C.c_int32), ("chunk_keys", C.c_int32), ("n_ns", C.c_int32),
-                ("q_hidden", C.c_int32)]
+                ("q_hidden", C.c_int32), ("head_map", C.POINTER(C.c_int32))]
 
 
 class Batch(C.Structure):
     _fields_ = [("hist_offsets", _vp), ("hist_ids", _vp), ("tgt_offsets", _vp), ("tgt_ids", _vp),
                 ("q0", _vp), ("table", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
-                ("max_tgt_per_user", C.c_int32), ("ns_feats", _vp)]
+                ("max_tgt_per_user", C.c_int32), ("ns_feats", _vp), ("key_mask", _vp)]
 
 
 class Ffn(C.Structure):
@@ -87,7 +87,8 @@ class AttnArgs(C.Structure):
                 ("score", C.c_int32), ("chunk_keys", C.c_int32), ("hist_offsets", _vp),
                 ("tgt_offsets", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
                 ("max_tgt_per_user", C.c_int32), ("q", _vp), ("k", _vp), ("v", _vp),
-                ("attn", _vp), ("active", _vp), ("dev_status", _vp)]
+                ("attn", _vp), ("active", _vp), ("dev_status", _vp), ("key_mask", _vp),
+                ("head_map", C.POINTER(C.c_int32))]
 
 
 _LIB = None
@@ -165,6 +166,8 @@ class DeviceProblem:
     max_tgt: int
     ns: object = None     # HyFormer: non-sequence tokens [B, n_ns, d]
     qgen: Optional[dict] = None
+    key_mask: object = None   # Cross-Mask: [n_hist] visibility bits (int32 view of uint32)
+    head_map: object = None   # Cross-Mask: ctypes int32 array [H] (kept alive here)
 
 
 def _dev(a, device):
@@ -197,11 +200,18 @@ def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=Fals
     if table is None:
         table = _dev(p.table, device)
     m = np.diff(p.tgt_offsets)
+    km = p.extra.get("key_mask")
+    hm = p.extra.get("head_map")
+    hmap = None
+    if hm is not None:
+        hmap = (C.c_int32 * len(hm))(*[int(x) for x in hm])
+        cfg.head_map = C.cast(hmap, C.POINTER(C.c_int32))
     return DeviceProblem(cfg, _dev(p.hist_offsets, device), _dev(p.hist_ids, device),
                          _dev(p.tgt_offsets, device), _dev(p.tgt_ids, device), _dev(p.q0, device),
                          table, [conv(l) for l in p.layers], conv(p.z), _dev(p.wz, device),
                          p.n_hist, p.n_tgt, max(1, int(m.max()) if len(m) else 1),
-                         _dev(p.extra.get("ns"), device), conv(p.extra.get("qgen")))
+                         _dev(p.extra.get("ns"), device), conv(p.extra.get("qgen")),
+                         _dev(None if km is None else np.asarray(km, np.uint32).view(np.int32), device), hmap)
 
 
 def _ffn(f) -> Ffn:
@@ -220,7 +230,8 @@ def _structs(dp: DeviceProblem):
     qg = dp.qgen or {}
     w = Weights(layers, _ffn(dp.z), _ptr(dp.wz), _ptr(qg.get("w1")), _ptr(qg.get("w3")), _ptr(qg.get("w2")))
     b = Batch(_ptr(dp.hist_offsets), _ptr(dp.hist_ids), _ptr(dp.tgt_offsets), _ptr(dp.tgt_ids),
-              _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt, _ptr(dp.ns))
+              _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt, _ptr(dp.ns),
+              _ptr(dp.key_mask))
     return b, w, layers
 
 
@@ -416,7 +427,7 @@ def forward(dp: DeviceProblem, want=("o", "attn", "active"), dumps=()) -> dict:
 
 
 def attention(q, k, v, hist_offsets, tgt_offsets, H: int, score: str = "softmax",
-              max_tgt: Optional[int] = None, chunk_keys: int = 0):
+              max_tgt: Optional[int] = None, chunk_keys: int = 0, key_mask=None, head_map=None):
     """The attention core alone (``stca_attention``) on device tensors.
     q: [T, d] (already scaled by 1/sqrt(d_h)), k/v: [n_hist, d]; fp32, or
     bf16 bits as int16.  Returns (attn fp32 [T, d], active int32 [T, H] or None,
@@ -434,7 +445,12 @@ def attention(q, k, v, hist_offsets, tgt_offsets, H: int, score: str = "softmax"
     a = AttnArgs(B=B, d=d, H=H, dtype=dtype, score=SCORE[score], chunk_keys=chunk_keys,
                  hist_offsets=_ptr(hist_offsets), tgt_offsets=_ptr(tgt_offsets),
                  n_hist=k.shape[0], n_tgt=T, max_tgt_per_user=max_tgt, q=_ptr(q), k=_ptr(k),
-                 v=_ptr(v), attn=_ptr(attn), active=_ptr(active), dev_status=_ptr(status))
+                 v=_ptr(v), attn=_ptr(attn), active=_ptr(active), dev_status=_ptr(status),
+                 key_mask=_ptr(key_mask))
+    hmap = None
+    if head_map is not None:
+        hmap = (C.c_int32 * len(head_map))(*[int(x) for x in head_map])
+        a.head_map = C.cast(hmap, C.POINTER(C.c_int32))
     n = C.c_size_t(0)
     _check(lib.stca_attention_workspace_size(C.byref(a), C.byref(n)))
     ws = torch.empty(max(1, n.value), dtype=torch.uint8, device=q.device)

@@ -1,0 +1,125 @@
+"""GPU parity of the Cross-Mask attention ([WeChat] §3.2-3.3): per-head
+vertical masks over the history items and heads sharing an attention map,
+in the staged bf16 attention kernel.
+
+Cases: the attention core on shared operands (softmax and ReLU, d_h 32 and
+64, ragged users including empty ones and users whose masked heads see no
+item, exact active counts where no score is within rounding of 0); the
+whole forward on the RLB workload reduced with two masked heads and a head
+map; dedup bitwise equal to the plain path under masks; an all-visible mask
+bitwise equal to no mask; the full-size RLB workload with masks, sampled.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from oracle import stca_oracle as O
+from recsys_ultra_long_amd import inputs as I
+
+from parity_util import TOL, compare_forward, gpu_run, oracle_run, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU visible")]
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).cuda()
+
+
+@pytest.mark.parametrize("score", ["softmax", "relu"])
+@pytest.mark.parametrize("dh,H,hmap", [(32, 8, [0, 0, 2, 3, 3, 5, 6, 0]), (64, 4, None)])
+def test_cross_mask_attention_core(score, dh, H, hmap):
+    from recsys_ultra_long_amd import stca
+    g = np.random.default_rng(dh + H)
+    lens = [0, 1, 31, 32, 33, 200, 1000, 5, 40]
+    ms = [3, 1, 17, 64, 70, 2, 33, 0, 5]
+    d = dh * H
+    ho = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    to = np.concatenate([[0], np.cumsum(ms)]).astype(np.int32)
+    n, T = int(ho[-1]), int(to[-1])
+    q = I.f32_to_bf16_bits((g.standard_normal((T, d)) / np.sqrt(dh)).astype(np.float32))
+    k = I.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
+    v = I.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
+    # heads 1 and 3 see ~30% of the items; head 2 sees none of user 8's items
+    mask = np.full(n, (1 << H) - 1, dtype=np.uint32)
+    for h in (1, 3):
+        mask[g.random(n) > 0.3] &= np.uint32(~(1 << h) & 0xffffffff)
+    mask[ho[8]:ho[9]] &= np.uint32(~(1 << 2) & 0xffffffff)
+    attn, active, st = stca.attention(_dev(q), _dev(k), _dev(v), _dev(ho), _dev(to), H, score,
+                                      chunk_keys=64, key_mask=_dev(mask), head_map=hmap)
+    torch.cuda.synchronize()
+    attn = attn.cpu().numpy()
+    assert int(st.cpu()[0]) == 0
+    Q, K, V = O.stored_to_f64(q), O.stored_to_f64(k), O.stored_to_f64(v)
+    worst = 0.0
+    for u in range(len(lens)):
+        a, b, t0, t1 = ho[u], ho[u + 1], to[u], to[u + 1]
+        if t1 == t0:
+            continue
+        ref, cnt, amb = O.attention_core(Q[t0:t1], K[a:b], V[a:b], H, score, scale=1.0,
+                                         key_mask=mask[a:b], head_map=hmap)
+        err = row_rel_err(attn[t0:t1], ref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (u, err)
+        if score == "relu":
+            gc = active.cpu().numpy()[t0:t1]
+            exact = amb == 0
+            assert np.array_equal(gc[exact], cnt[exact]), u
+            assert np.all(np.abs(gc - cnt) <= amb), u
+    # user 8: head 2 sees nothing -> exact zeros
+    assert np.all(attn[to[8]:to[9], 2 * dh:3 * dh] == 0)
+    print(f"[cross-mask] core {score} d_h {dh}: worst {worst:.2e}", flush=True)
+
+
+def _masked(sp, masked=(1, 5), keep=0.4, head_map=None, seed=0):
+    p = I.make_problem(sp)
+    p.extra["key_mask"] = I.cross_mask(sp, p.n_hist, masked, keep, seed)
+    if head_map is not None:
+        p.extra["head_map"] = list(head_map)
+    return p
+
+
+def test_cross_mask_forward_matches_oracle():
+    sp = I.spec(3, B=3, L=700, m=24, M=3, table_rows=20000, ln_random=True)
+    p = _masked(sp, head_map=[0, 1, 1, 3, 4, 4, 6, 7])
+    g = gpu_run(p, path="staged")
+    o = oracle_run(p)
+    errs = compare_forward(g, o, "bf16")
+    print(f"[cross-mask] forward errors {errs}", flush=True)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+def test_cross_mask_dedup_bitwise_and_all_visible_is_no_mask():
+    sp = I.spec(4, B=5, L_max=500, m=8, table_rows=20000)
+    p = _masked(sp, masked=(0, 2), head_map=[0, 0, 2, 2])
+    a = gpu_run(p, path="staged")
+    b = gpu_run(p, path="staged", dedup=True)
+    for k in ("z", "o", "attn"):
+        assert np.array_equal(a[k], b[k]), k
+    q = I.make_problem(sp)
+    c = gpu_run(q, path="staged")
+    q.extra["key_mask"] = np.full(q.n_hist, (1 << sp.H) - 1, dtype=np.uint32)
+    d = gpu_run(q, path="staged")
+    for k in ("z", "o", "attn"):
+        assert np.array_equal(c[k], d[k]), k
+
+
+def test_cross_mask_fullsize_rlb_sampled():
+    sp = I.spec(3)
+    p = _masked(sp, masked=(2, 6), keep=0.25, head_map=[0, 1, 1, 3, 4, 5, 5, 7])
+    users = [0, 15, 31]
+    g = gpu_run(p, path="staged")
+    o = oracle_run(p, users)
+    ut = np.concatenate([np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users])
+    errs = compare_forward(g, o, "bf16", users_t=ut)
+    print(f"[cross-mask] full size errors {errs}", flush=True)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
