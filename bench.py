@@ -245,6 +245,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="rlb-long")
+    ap.add_argument("--cross-mask", action="store_true",
+                    help="Cross-Mask attention: heads 2 and 6 see a quarter of the items (seeded "
+                         "per-item masks) and pairs of heads share one attention map (staged path)")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + stca_backward) on the training "
                          "workload (rlb-train unless --workload names another)")
@@ -290,12 +293,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     stca.load()
     sp = workload(args.workload)
-    if args.dedup or sp.d == 512 or sp.qmode == "hyformer":  # the fused path serves d <= 256, STCA queries
+    if args.dedup or args.cross_mask or sp.d == 512 or sp.qmode == "hyformer":  # the fused path serves d <= 256, STCA queries
         args.path = "staged"
     t = time.time()
     p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
     log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} "
         f"n_tgt={p.n_tgt} table={sp.table_rows}x{sp.d} {sp.dtype}")
+    if args.cross_mask:
+        p.extra["key_mask"] = I.cross_mask(sp, p.n_hist, (2, 6), keep=0.25)
+        p.extra["head_map"] = [h - (h % 2) for h in range(sp.H)]
     dp = stca.upload(p, path=args.path, dedup=args.dedup)
     n_unique = int(len(np.unique(p.hist_ids))) if args.dedup else None
     torch.cuda.synchronize()
@@ -407,6 +413,8 @@ def main():
         "config": {"workload": f"{sp.name}: B={sp.B} users, L={sp.L}, m={sp.m} targets/user (RLB), "
                                f"table {sp.table_rows}x{d} bf16 Zipf({sp.zipf_s}) ids, d={d}, H={H}, "
                                f"hidden={h}, M={M} layers, softmax, path={args.path}"
+                               + (", Cross-Mask: heads 2 and 6 see 25% of the items, heads 2k and 2k+1 "
+                                  "share the map of head 2k" if args.cross_mask else "")
                                + (f", HyFormer queries: {sp.n_ns} non-sequence tokens, query FFN hidden "
                                   f"{sp.hy_hidden or d}, no history LN" if sp.qmode == "hyformer" else "")
                                + (f", unique-id dedup ({n_unique} unique of {n_hist})" if args.dedup else ""),
@@ -432,7 +440,7 @@ def main():
         # row here depends on its id alone)
         del f
         others = [("staged" if args.path == "fused" else "fused", False), ("staged", True)]
-        if sp.d == 512 or sp.qmode == "hyformer":
+        if sp.d == 512 or sp.qmode == "hyformer" or args.cross_mask:
             others = [("staged", True)]
         res["other_paths"] = []
         for other, dd in others:
