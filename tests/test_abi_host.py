@@ -267,3 +267,51 @@ def test_hyformer_forward_needs_query_weights():
     layers[1].boost_w2 = None
     assert _forward(c, b, w, out, 1 << 40) == stca.ERR_INVALID_ARG
     assert "boosting" in stca.last_error()
+
+
+# ----------------------------------------------------------------- Cross-Mask
+def _map(vals):
+    arr = (C.c_int32 * len(vals))(*vals)
+    return arr, C.cast(arr, C.POINTER(C.c_int32))
+
+
+@pytest.mark.parametrize("cover,bover,hmap,code", [
+    ({}, dict(key_mask=FAKE), None, stca.OK),
+    ({}, {}, [0, 0, 2, 2, 4, 4, 6, 6], stca.OK),
+    (dict(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP), dict(key_mask=FAKE), [0, 1, 1, 3, 4, 5, 5, 7], stca.OK),
+    (dict(path=1), dict(key_mask=FAKE), None, stca.ERR_UNSUPPORTED),          # fused path
+    (dict(path=1), {}, [0] * 8, stca.ERR_UNSUPPORTED),
+    (dict(dtype=stca.F32, d=64, H=2, hidden=64), dict(key_mask=FAKE), None, stca.ERR_UNSUPPORTED),
+    ({}, dict(key_mask=FAKE + 4), None, stca.ERR_INVALID_ARG),                # misaligned
+    ({}, {}, [0, 1, 2, 3, 4, 5, 6, 8], stca.ERR_INVALID_ARG),                 # outside [0, H)
+    ({}, {}, [0, 1, 2, -1, 4, 5, 6, 7], stca.ERR_INVALID_ARG),
+])
+def test_cross_mask_validation(cover, bover, hmap, code):
+    c = cfg(**cover)
+    keep = None
+    if hmap is not None:
+        keep, c.head_map = _map(hmap)
+    r, _ = ws_size(c, batch(**bover))
+    assert r == code, stca.last_error()
+    if code != stca.OK:
+        assert "mask" in stca.last_error() or "head_map" in stca.last_error()
+
+
+def test_cross_mask_attention_and_backward_validation():
+    lib = stca.load()
+    a = stca.AttnArgs(B=2, d=256, H=8, dtype=stca.BF16, score=0, chunk_keys=0,
+                      hist_offsets=FAKE, tgt_offsets=FAKE, n_hist=100, n_tgt=4,
+                      max_tgt_per_user=2, q=FAKE, k=FAKE, v=FAKE, attn=FAKE, key_mask=FAKE)
+    n = C.c_size_t(0)
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.OK
+    keep, a.head_map = _map([0, 0, 1, 1, 2, 2, 3, 9])
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.ERR_INVALID_ARG
+    a.head_map = None
+    a.dtype, a.d, a.H = stca.F32, 64, 2
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.ERR_UNSUPPORTED
+    # the backward takes no masks: rejected before anything is enqueued
+    c, b = cfg(), batch(key_mask=FAKE)
+    w, keepw = _weights()
+    g = stca.Grads()
+    r = lib.stca_backward(C.byref(c), C.byref(b), C.byref(w), FAKE, C.byref(g), FAKE, 1 << 30, None)
+    assert r == stca.ERR_UNSUPPORTED and "Cross-Mask" in stca.last_error()
