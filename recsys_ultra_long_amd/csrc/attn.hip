@@ -167,9 +167,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kk[kt][k] = ld8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+            for (int k = 0; k < KS; ++k) kk[kt][k] = ldnt8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
 #pragma unroll
-          for (int t = 0; t < DT; ++t) vv[t] = ld8(vb + (t * 16 + c16) * 32 + g16 * 8);
+          for (int t = 0; t < DT; ++t) vv[t] = ldnt8(vb + (t * 16 + c16) * 32 + g16 * 8);
         }
       };
       // IND: V row chunks -> transposed wave-private tile -> V^T fragments

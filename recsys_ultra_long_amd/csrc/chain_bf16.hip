@@ -497,7 +497,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         vst = fused_v_stage(sm, w);
       }
 #pragma unroll
-      for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T: 4 consecutive features / token
+      for (int sp = 0; sp < NSP; ++sp) {  // K^T = W_K^T Xt^T
         f32x16 acc[YT][TT];
         zero(acc);
         const bf16_t *gp[YT], *nx[2];
@@ -510,24 +510,29 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
           const int blk = (int)(row0 >> 5) + t;
           if (OUT == OUT_KV && blk >= total_blocks) continue;
 #pragma unroll
-          for (int i = 0; i < YT; ++i)
+          for (int i = 0; i < YT; ++i) {
+            if constexpr (OUT == OUT_FUSED) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              u32x2 v = {pack_bf2(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
-                         pack_bf2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
-              if constexpr (OUT == OUT_FUSED) {
+              for (int q = 0; q < 4; ++q) {
+                u32x2 v = {pack_bf2(acc[i][t][4 * q], acc[i][t][4 * q + 1]),
+                           pack_bf2(acc[i][t][4 * q + 2], acc[i][t][4 * q + 3])};
                 const int fl = (sp * YT + i) * 32 + 8 * q + 4 * hi;  // wave-local feature
                 *reinterpret_cast<u32x2 *>(kst + ((fl / FDH) * 64 + t * 32 + l32) * FDH + fl % FDH) = v;
-              } else {
-                const int f = w * (D / 4) + (sp * YT + i) * 32 + 8 * q + 4 * hi;
-                const int h = f / DH, dh = f % DH;
-                *reinterpret_cast<u32x2 *>(kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh) = v;
               }
+            } else {  // 16 consecutive features of key l32 per lane, streamed out
+              u32x4 o0, o1;
+              halves16(acc[i][t], hi, o0, o1);
+              const int f = w * (D / 4) + (sp * YT + i) * 32 + 16 * hi;
+              const int h = f / DH, dh = f % DH;
+              bf16_t *dst = kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh;
+              stnt16(dst, o0);
+              stnt16(dst + 8, o1);
             }
+          }
         }
       }
 #pragma unroll
-      for (int sp = 0; sp < NSP; ++sp) {  // V = Xt W_V: 4 consecutive tokens / feature -> V^T
+      for (int sp = 0; sp < NSP; ++sp) {  // V = Xt W_V -> V^T
         f32x16 acc[TT][YT];
         zero(acc);
         const bf16_t *gp[YT], *nx[2];
@@ -545,19 +550,23 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
           if (OUT == OUT_KV && blk >= total_blocks) continue;
 #pragma unroll
           for (int j = 0; j < YT; ++j) {
+            if constexpr (OUT == OUT_FUSED) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int key = 8 * q + 4 * hi;
-              u32x2 v = {pack_bf2(acc[t][j][4 * q], acc[t][j][4 * q + 1]),
-                         pack_bf2(acc[t][j][4 * q + 2], acc[t][j][4 * q + 3])};
-              if constexpr (OUT == OUT_FUSED) {
+              for (int q = 0; q < 4; ++q) {
+                const int key = 8 * q + 4 * hi;
+                u32x2 v = {pack_bf2(acc[t][j][4 * q], acc[t][j][4 * q + 1]),
+                           pack_bf2(acc[t][j][4 * q + 2], acc[t][j][4 * q + 3])};
                 const int fl = (sp * YT + j) * 32 + l32;
                 *reinterpret_cast<u32x2 *>(vst + fl * 64 + t * 32 + key) = v;
-              } else {
-                const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
-                const int h = f / DH, dh = f % DH;
-                *reinterpret_cast<u32x2 *>(vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
               }
+            } else {  // 16 consecutive keys of feature f per lane, streamed out
+              u32x4 o0, o1;
+              halves16(acc[t][j], hi, o0, o1);
+              const int f = w * (D / 4) + (sp * YT + j) * 32 + l32;
+              const int h = f / DH, dh = f % DH;
+              bf16_t *dst = vb + (((int64_t)blk * H + h) * DH + dh) * 32 + 16 * hi;
+              stnt16(dst, o0);
+              stnt16(dst + 8, o1);
             }
           }
         }

@@ -55,6 +55,28 @@ DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 DEV int c32_row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
+// A 32x32 accumulator holds, in lane (c, hi), rows 8q + 4hi + r (q, r < 4)
+// of column c.  Exchanged with lane c + 32(1 - 2hi), each lane ends up with
+// 16 consecutive rows as bf16: rows 0..15 for hi = 0, 16..31 for hi = 1.
+DEV void halves16(const f32x16 &acc, int hi, u32x4 &o0, u32x4 &o1) {
+  u32x2 p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] = u32x2{pack_bf2(acc[4 * q], acc[4 * q + 1]), pack_bf2(acc[4 * q + 2], acc[4 * q + 3])};
+  const u32x2 s0 = hi ? p[0] : p[2], s1 = hi ? p[1] : p[3];
+  u32x2 r0, r1;
+  r0[0] = __shfl_xor((int)s0[0], 32);
+  r0[1] = __shfl_xor((int)s0[1], 32);
+  r1[0] = __shfl_xor((int)s1[0], 32);
+  r1[1] = __shfl_xor((int)s1[1], 32);
+  if (hi) {
+    o0 = u32x4{r0[0], r0[1], p[2][0], p[2][1]};
+    o1 = u32x4{r1[0], r1[1], p[3][0], p[3][1]};
+  } else {
+    o0 = u32x4{p[0][0], p[0][1], r0[0], r0[1]};
+    o1 = u32x4{p[1][0], p[1][1], r1[0], r1[1]};
+  }
+}
+
 DEV bf16x8 ld8(const bf16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
 
 // Loads through pointers known to address global memory.  A pointer whose
@@ -66,6 +88,13 @@ typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;
 typedef __attribute__((address_space(1))) const f32x4 gf32x4;
 DEV bf16x8 ldg8(const bf16_t *p) { return *(gbf16x8 *)p; }
 DEV f32x4 ldg4(const float *p) { return *(gf32x4 *)p; }
+
+// Streaming (non-temporal) access for data touched once: K/V written by the
+// history encoder and read once per layer by the attention.  Neither side
+// then leaves K/V lines in the memory-side cache, where dirty ones would
+// otherwise be written back during the next kernels' reads.
+DEV bf16x8 ldnt8(const bf16_t *p) { return __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(p)); }
+DEV void stnt16(bf16_t *p, const u32x4 &v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p)); }
 
 // ---------------------------------------------------------------- misc
 DEV float wave_max(float v) {

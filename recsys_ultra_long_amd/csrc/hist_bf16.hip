@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     ffn_ln<LN>(ring, L, sm, xt, w, lane, nkh, nchunk);
 
     // ------------------------------------------------------------ W_K | W_V
-    {  // K^T = W_K^T X~^T: 4 consecutive features of one key per lane
+    {  // K^T = W_K^T X~^T: 16 consecutive features of one key per lane (after the exchange)
       f32x16 acc[4];
       zero16(acc);
       const Src cur = src_proj(L, w, lane), nxt = src_proj(L, kD / 32 + w, lane);
@@ -337,16 +337,16 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
       for (int j = 0; j < 4; ++j) {
         const int blk = (int)(row0 >> 5) + j;
         if (blk >= total_blocks) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int f = w * 32 + 8 * q + 4 * hi;
-          const int h = f / DH, dh = f % DH;
-          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
-          *reinterpret_cast<u32x2 *>(L.kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh) = v;
-        }
+        u32x4 o0, o1;
+        halves16(acc[j], hi, o0, o1);
+        const int f = w * 32 + 16 * hi;
+        const int h = f / DH, dh = f % DH;
+        bf16_t *dst = L.kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh;
+        stnt16(dst, o0);
+        stnt16(dst + 8, o1);
       }
     }
-    {  // V = X~ W_V with keys as MFMA rows: 4 consecutive keys of one feature per lane
+    {  // V = X~ W_V with keys as MFMA rows: 16 consecutive keys of one feature per lane
       f32x16 acc[4];
       zero16(acc);
       const bool more = li + 1 < hl.M;
@@ -370,14 +370,13 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
       for (int j = 0; j < 4; ++j) {
         const int blk = (int)(row0 >> 5) + j;
         if (blk >= total_blocks) continue;
+        u32x4 o0, o1;
+        halves16(acc[j], hi, o0, o1);
         const int f = w * 32 + l32;
         const int h = f / DH, dh = f % DH;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int key = 8 * q + 4 * hi;
-          u32x2 v = {pack_bf2(acc[j][4 * q], acc[j][4 * q + 1]), pack_bf2(acc[j][4 * q + 2], acc[j][4 * q + 3])};
-          *reinterpret_cast<u32x2 *>(L.vb + (((int64_t)blk * H + h) * DH + dh) * 32 + key) = v;
-        }
+        bf16_t *dst = L.vb + (((int64_t)blk * H + h) * DH + dh) * 32 + 16 * hi;
+        stnt16(dst, o0);
+        stnt16(dst + 8, o1);
       }
     }
   }
