@@ -251,8 +251,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + stca_backward) on the training "
                          "workload (rlb-train unless --workload names another)")
-    ap.add_argument("--path", default="fused", choices=["staged", "fused"],
-                    help="fused (default, the faster complete path here) or staged")
+    ap.add_argument("--path", default="staged", choices=["staged", "fused"],
+                    help="staged (default: K/V streamed through HBM, so the projection (MFMA) and "
+                         "attention (HBM) stages are timed apart) or fused (no K/V in HBM)")
     ap.add_argument("--dedup", action="store_true",
                     help="staged path with unique-id dedup of the history encoding "
                          "(bit-identical results; valid because a row's encoding depends on its id alone)")
@@ -389,7 +390,7 @@ def main():
     picks = {"history": lambda k: (k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
                                    (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
              "attention": lambda k: k.startswith("attn_bf16_kernel<"),
-             "fused": lambda k: k.startswith(f"fused_kernel<{d},")}
+             "fused": lambda k: k.startswith("fused256_kernel<") or k.startswith(f"fused_kernel<{d},")}
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{args.path}.md"))
     if tr is not None:
         for name, roof in roofs.items():
