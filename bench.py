@@ -36,6 +36,45 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_peaks():
+    """Attainable rates on this GPU, quoted beside the nominal peaks the
+    rooflines are priced against: dense bf16 MFMA from registers (the
+    library's MFMA-only kernel, best of three launches) and a 1 GiB device
+    copy (read + write bytes / time, best of five)."""
+    import torch
+    from recsys_ultra_long_amd import stca
+    mfma = stca.peak_mfma_bf16()
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b.copy_(a)
+    best = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        best = max(best, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_copy_gbs": round(best, 1)}
+
+
+def attach_measured_peaks(res):
+    """Beside each roofline's nominal peak: the attainable rate measured in
+    this run and the achieved fraction of it (context; `frac` stays the
+    fraction of the nominal peak)."""
+    mp = measured_peaks()
+    res["measured_peaks"] = mp
+    log(f"measured peaks: {mp}")
+    for k, roof in res.items():
+        if k.startswith("roofline") and isinstance(roof, dict):
+            pm = mp["mfma_bf16_tflops"] if roof["unit"] == "TFLOP/s" else mp["hbm_copy_gbs"]
+            roof["peak_measured"] = pm
+            roof["frac_measured"] = round(roof["achieved"] / pm, 4)
+
+
 def workload(name):
     from recsys_ultra_long_amd import inputs as I
     if name == "rlb-long":
@@ -231,6 +270,7 @@ def bench_backward(args):
         "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
         "backward_flops": {"proper": flops_b, "recompute": flops_f},
     }
+    attach_measured_peaks(res)
     if not args.no_cpu_baseline:
         log(f"timing the float64 backward oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline_backward(p, dz_np, args.cpu_seconds)
@@ -462,6 +502,7 @@ def main():
                                        "value": round(n_hist * M / (mso * 1e-3), 1)})
             log(f"other path ({other}{'+dedup' if dd else ''}): {mso:.3f} ms/step")
             del fo, dpo
+    attach_measured_peaks(res)
     if not args.no_cpu_baseline:
         log(f"timing the float64 oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)

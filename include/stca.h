@@ -314,6 +314,15 @@ int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch
 int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const float *dz,
                   const stca_grads *grads, void *workspace, size_t ws_bytes, void *hip_stream);
 
+/* Measurement aid, not a step of the method: `blocks` workgroups of 256
+ * threads, every wave doing `iters` rounds of 8 independent dense bf16
+ * 32x32x16 MFMA products from registers (blocks * 4 * iters * 8 * 32768
+ * flop), writing one checksum per wave to out[blocks * 4] (device, fp32).
+ * Timed by the caller on `hip_stream`, it gives the matrix cores' attainable
+ * rate at the clock the chip holds under that load.  Enqueued only; returns
+ * STCA_ERR_INVALID_ARG for non-positive sizes or a NULL out. */
+int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, void *hip_stream);
+
 const char *stca_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char *stca_last_error(void);

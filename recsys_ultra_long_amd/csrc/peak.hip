@@ -1,0 +1,49 @@
+// peak.hip -- a measurement aid, not a step of the method: a kernel that
+// does nothing but dense bf16 MFMA from registers, so the matrix cores'
+// attainable rate at the clock the chip holds under that load can be quoted
+// beside the nominal figure the rooflines are priced against.
+#include "stca.h"
+#include "stca_internal.h"
+
+namespace stca {
+namespace {
+
+// Each wave: `iters` rounds of 8 independent 32x32x16 bf16 products
+// (8 x 32,768 flop per round); one checksum per wave keeps the work live.
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (short)(0x3c00 + ((lane + e) & 7));  // small positive bf16 values
+    b[e] = (short)(0x3c00 + ((lane * 3 + e) & 7));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mfma32(a, b, acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+}  // namespace stca
+
+extern "C" int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, void *hip_stream) {
+  using namespace stca;
+  api_clear_error();
+  if (blocks <= 0 || iters <= 0 || !out) return api_error(STCA_ERR_INVALID_ARG, "blocks, iters must be > 0, out non-NULL");
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, (int)iters, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return api_error(STCA_ERR_HIP, "mfma peak launch: %s", hipGetErrorString(e));
+  return STCA_OK;
+}

@@ -27,7 +27,7 @@ DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
            "stca_attention", "stca_backward_workspace_size", "stca_backward",
-           "stca_status_string", "stca_last_error", "stca_version")
+           "stca_peak_mfma_bf16", "stca_status_string", "stca_last_error", "stca_version")
 
 _vp = C.c_void_p
 
@@ -119,12 +119,13 @@ def load() -> C.CDLL:
                                                      C.POINTER(C.c_size_t)]
         lib.stca_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
                                       C.POINTER(Grads), _vp, C.c_size_t, _vp]
+        lib.stca_peak_mfma_bf16.argtypes = [C.c_int32, C.c_int32, _vp, _vp]
         lib.stca_status_string.restype = C.c_char_p
         lib.stca_status_string.argtypes = [C.c_int]
         lib.stca_last_error.restype = C.c_char_p
         lib.stca_version.restype = C.c_int
         for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
-                  "stca_attention", "stca_backward_workspace_size", "stca_backward"):
+                  "stca_attention", "stca_backward_workspace_size", "stca_backward", "stca_peak_mfma_bf16"):
             getattr(lib, f).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -465,3 +466,23 @@ def to_numpy_stored(t) -> np.ndarray:
     if a.dtype == np.int16:
         a = a.view(np.uint16)
     return a
+
+
+def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3) -> float:
+    """Attainable dense bf16 MFMA rate (TFLOP/s): the best of `repeats` timed
+    launches of the library's MFMA-only measurement kernel."""
+    import torch
+    lib = load()
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    flops = blocks * 4 * iters * 8 * 32768
+    best = 0.0
+    _check(lib.stca_peak_mfma_bf16(blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(s.cuda_stream)))
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        _check(lib.stca_peak_mfma_bf16(blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(s.cuda_stream)))
+        b.record(s)
+        b.synchronize()
+        best = max(best, flops / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best

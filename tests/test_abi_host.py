@@ -315,3 +315,10 @@ def test_cross_mask_attention_and_backward_validation():
     g = stca.Grads()
     r = lib.stca_backward(C.byref(c), C.byref(b), C.byref(w), FAKE, C.byref(g), FAKE, 1 << 30, None)
     assert r == stca.ERR_UNSUPPORTED and "Cross-Mask" in stca.last_error()
+
+
+def test_peak_mfma_validation():
+    lib = stca.load()
+    assert lib.stca_peak_mfma_bf16(0, 10, C.c_void_p(FAKE), None) == stca.ERR_INVALID_ARG
+    assert lib.stca_peak_mfma_bf16(4, 0, C.c_void_p(FAKE), None) == stca.ERR_INVALID_ARG
+    assert lib.stca_peak_mfma_bf16(4, 10, None, None) == stca.ERR_INVALID_ARG
