@@ -250,8 +250,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int n = 0; n < NT; ++n) {
         const float l = st.l[n][0];  // already the whole block range's sum
         int cn = st.cnt[n];
-        cn += __shfl_xor(cn, 16);
-        cn += __shfl_xor(cn, 32);
+        cn = isum_x16(cn);
+        cn = isum_x32(cn);
         if (g16 == 0) {
           sm_m[w][n * 16 + c16] = st.mrun[n];
           sm_l[w][n * 16 + c16] = l;

@@ -429,7 +429,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
                 const float x = y[sp][t][j][e];
                 v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
               }
-          v += __shfl_xor(v, 32);
+          v = sum_x32(v);
           if (hi == 0) red[pass][w][j * 32 + l32] = v;
         }
         __syncthreads();
@@ -813,8 +813,8 @@ __global__ __launch_bounds__(kThreads, 2) void fused_kernel(ChainArgs a, AttnArg
       for (int n = 0; n < NT; ++n) {
         const float l = st.l[n][0];
         int cn = st.cnt[n];
-        cn += __shfl_xor(cn, 16);
-        cn += __shfl_xor(cn, 32);
+        cn = isum_x16(cn);
+        cn = isum_x32(cn);
         const int tl = n * 16 + c16;
         if (tl < m_u) {
           const int64_t idx = partial_index(slot, H, h, at.tgs, tl);

@@ -55,26 +55,71 @@ DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 DEV int c32_row(int lane, int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
+// Cross-lane exchanges through the VALU (gfx950 v_permlane32_swap /
+// v_permlane16_swap) rather than an LDS permute.  swap32: a <- [a lanes 0-31,
+// b lanes 0-31], b <- [a lanes 32-63, b lanes 32-63].  swap16, per row of 16
+// lanes r0..r3: a <- [a.r0, b.r0, a.r2, b.r2], b <- [a.r1, b.r1, a.r3, b.r3].
+DEV void swap32(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+DEV void swap16(uint32_t &a, uint32_t &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+// v(lane) op v(lane ^ 32) and v(lane) op v(lane ^ 16), for commutative ops.
+DEV float sum_x32(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap32(a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+DEV float max_x32(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap32(a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+DEV float max_x16(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap16(a, b);
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+DEV float sum_x16(float v) {
+  uint32_t a = __float_as_uint(v), b = a;
+  swap16(a, b);
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+DEV int isum_x32(int v) {
+  uint32_t a = (uint32_t)v, b = a;
+  swap32(a, b);
+  return (int)(a + b);
+}
+DEV int isum_x16(int v) {
+  uint32_t a = (uint32_t)v, b = a;
+  swap16(a, b);
+  return (int)(a + b);
+}
+
 // A 32x32 accumulator holds, in lane (c, hi), rows 8q + 4hi + r (q, r < 4)
 // of column c.  Exchanged with lane c + 32(1 - 2hi), each lane ends up with
-// 16 consecutive rows as bf16: rows 0..15 for hi = 0, 16..31 for hi = 1.
+// 16 consecutive rows as bf16: rows 0..15 for hi = 0, 16..31 for hi = 1
+// (lanes of the lower half keep their rows 8q + r of q = 0, 1 and take the
+// partner's 8q + 4 + r; the upper half the same for q = 2, 3).
 DEV void halves16(const f32x16 &acc, int hi, u32x4 &o0, u32x4 &o1) {
-  u32x2 p[4];
+  uint32_t p[4][2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) p[q] = u32x2{pack_bf2(acc[4 * q], acc[4 * q + 1]), pack_bf2(acc[4 * q + 2], acc[4 * q + 3])};
-  const u32x2 s0 = hi ? p[0] : p[2], s1 = hi ? p[1] : p[3];
-  u32x2 r0, r1;
-  r0[0] = __shfl_xor((int)s0[0], 32);
-  r0[1] = __shfl_xor((int)s0[1], 32);
-  r1[0] = __shfl_xor((int)s1[0], 32);
-  r1[1] = __shfl_xor((int)s1[1], 32);
-  if (hi) {
-    o0 = u32x4{r0[0], r0[1], p[2][0], p[2][1]};
-    o1 = u32x4{r1[0], r1[1], p[3][0], p[3][1]};
-  } else {
-    o0 = u32x4{p[0][0], p[0][1], r0[0], r0[1]};
-    o1 = u32x4{p[1][0], p[1][1], r1[0], r1[1]};
+  for (int q = 0; q < 4; ++q) {
+    p[q][0] = pack_bf2(acc[4 * q], acc[4 * q + 1]);
+    p[q][1] = pack_bf2(acc[4 * q + 2], acc[4 * q + 3]);
   }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    swap32(p[0][e], p[2][e]);
+    swap32(p[1][e], p[3][e]);
+  }
+  o0 = u32x4{p[0][0], p[0][1], p[2][0], p[2][1]};
+  o1 = u32x4{p[1][0], p[1][1], p[3][0], p[3][1]};
 }
 
 DEV bf16x8 ld8(const bf16_t *p) { return *reinterpret_cast<const bf16x8 *>(p); }
@@ -98,13 +143,16 @@ DEV void stnt16(bf16_t *p, const u32x4 &v) { __builtin_nontemporal_store(v, rein
 
 // ---------------------------------------------------------------- misc
 DEV float wave_max(float v) {
+  v = max_x16(max_x32(v));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 DEV float wave_sum(float v) {
+  v = sum_x32(v);
+  v = sum_x16(v);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 

@@ -29,11 +29,15 @@ constexpr int kD = 256;
 constexpr int kT = 512;          // threads: 8 waves
 constexpr int kR = 128;          // rows per tile
 constexpr int kHC = 128;         // hidden units per chunk (16 per wave)
-constexpr int kXLD = kD + 8;     // LDS row stride of X / X~ (elements)
+constexpr int kXLD = kD + 8;     // LDS row stride of X~ (elements)
+// Row strides are chosen per read pattern: on gfx950 16-byte LDS reads of
+// 16 rows x 4 column groups (the 16x16x32 B operand) are conflict-free at a
+// 544-byte stride but not at 528; 32 rows x 2 groups (32x32x16) the reverse.
+constexpr int kXRLD = kD + 16;   // LDS row stride of the raw rows X (G phase)
 constexpr int kGLD = kHC + 8;    // LDS row stride of a G chunk
 
 struct Smem {
-  __attribute__((aligned(16))) bf16_t xs[kR * kXLD];
+  __attribute__((aligned(16))) bf16_t xs[kR * kXRLD];
   __attribute__((aligned(16))) bf16_t gs[2][kR * kGLD];
   float red[2][8][kR];
   int s_id[kR], s_tok[kR];
@@ -87,7 +91,8 @@ DEV void run_phase(Ring &ring, const Src &cur, const Src &nxt, bool more, F mma)
     else if (more) ring_load(ring, nb % 4, nxt, nb - NK);
     __builtin_amdgcn_sched_barrier(0);
     mma(kb, kb % 4);
-    __builtin_amdgcn_sched_barrier(0);
+    // the last block's products may overlap the epilogue that follows
+    if (kb + 1 < NK) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -138,7 +143,7 @@ DEV void gather_tile(const ChainArgs &a, Smem &sm, int64_t row0, int total_block
     const int id = sm.s_id[r];
     u32x4 v = {0u, 0u, 0u, 0u};
     if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * kD + c);
-    *reinterpret_cast<u32x4 *>(sm.xs + r * kXLD + c) = v;
+    *reinterpret_cast<u32x4 *>(sm.xs + r * kXRLD + c) = v;
     if (a.in_dump && sm.s_tok[r] >= 0)
       *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)sm.s_tok[r] * kD + c) = v;
   }
@@ -154,7 +159,7 @@ template <bool LN>
 DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lane, int nkh, int nchunk) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int c16 = lane & 15, g16 = lane >> 4;
-  const bf16_t *const xrow = sm.xs + c16 * kXLD + g16 * 8;  // G-phase operand base
+  const bf16_t *const xrow = sm.xs + c16 * kXRLD + g16 * 8;  // G-phase operand base
   // ------------------------------------------------------------ SwiGLU FFN
   f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
   zero16(y);
@@ -171,7 +176,7 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
         for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
           bf16x8 bx[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXLD + kb * 32);
+          for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXRLD + kb * 32);
 #pragma unroll
           for (int f = 0; f < 2; ++f)
 #pragma unroll
@@ -227,7 +232,7 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
           const float x = y[j][i];
           v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
         }
-        v += __shfl_xor(v, 32);
+        v = sum_x32(v);
         if (hi == 0) sm.red[pass][w][j * 32 + l32] = v;
       }
       __syncthreads();
@@ -562,8 +567,8 @@ __global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs a
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       int cn = st.cnt[n];
-      cn += __shfl_xor(cn, 16);
-      cn += __shfl_xor(cn, 32);
+      cn = isum_x16(cn);
+      cn = isum_x32(cn);
       const int tl = t0 + n * 16 + c16;
       if (tl < m_u) {
         const int64_t idx = partial_index(slot, H, head, at.tgs, tl);
