@@ -933,6 +933,10 @@ __global__ __launch_bounds__(256) void pack_batch_kernel(PackBatch pb) {
   if (t.fmt == 1) {  // 16x16x32 A operand
     const int lane = 16 * (kk / 8) + ng % 16;
     d = t.dst + (((int64_t)(ng / 16) * (t.K / 32) + k0 / 32) * 64 + lane) * 8;
+  } else if (t.fmt >= 4) {  // W_K (4) / W_V (5), k blocks interleaved
+    const int lane = 32 * (kk / 16) + ng % 32;
+    d = t.dst + (((((int64_t)(ng / 32) * (t.K / 32) + k0 / 32) * 2 + (t.fmt - 4)) * 2 + (kk % 16) / 8) * 512 +
+                 lane * 8);
   } else {
     const int lane = 32 * (kk / 16) + ng % 32;
     d = t.dst + frag_off(ng / 32, k0 / 32, t.K / 32, (kk % 16) / 8, lane);

@@ -73,9 +73,19 @@ DEV Src src_y(const Layer &L, int hc, int w, int lane, int nkh) {
   const bf16_t *p = L.w2 + frag_off(w, hc * (kHC / 32), nkh, 0, lane);
   return Src{p, p + 512, 1024};
 }
-DEV Src src_proj(const Layer &L, int tile, int lane) {
-  const bf16_t *p = L.wp + frag_off(tile, 0, kD / 32, 0, lane);
+// W_K and W_V are packed with their k blocks interleaved (K0, V0, K1, V1, ..
+// for each 32-feature tile): one stream for both, or every other block.
+DEV Src src_kv(const Layer &L, int w, int lane) {
+  const bf16_t *p = L.wp + (int64_t)w * (kD / 32) * 2048 + lane * 8;
   return Src{p, p + 512, 1024};
+}
+DEV Src src_k(const Layer &L, int w, int lane) {
+  const bf16_t *p = L.wp + (int64_t)w * (kD / 32) * 2048 + lane * 8;
+  return Src{p, p + 512, 2048};
+}
+DEV Src src_v(const Layer &L, int w, int lane) {
+  const bf16_t *p = L.wp + (int64_t)w * (kD / 32) * 2048 + 1024 + lane * 8;
+  return Src{p, p + 512, 2048};
 }
 
 // The NK blocks of one phase; `mma(kb, slot)` does the block's matrix work.
@@ -153,65 +163,77 @@ DEV void gather_tile(const ChainArgs &a, Smem &sm, int64_t row0, int total_block
 // SwiGLU FFN [+ LN] of one layer over the 128 rows in sm.xs; X~ goes to
 // `xt` (row stride kXLD: over the rows themselves, or into the G buffers when
 // the rows must survive for another layer).  The ring enters holding the
-// first blocks of G chunk 0 and leaves holding those of the W_K phase; X~ is
-// visible to every thread on return.
+// first blocks of G chunk 0 and leaves holding those of `after` (the
+// projection's weight stream); X~ is visible to every thread on return.
 template <bool LN>
-DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lane, int nkh, int nchunk) {
+DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lane, int nkh, int nchunk,
+                const Src &after) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int c16 = lane & 15, g16 = lane >> 4;
   const bf16_t *const xrow = sm.xs + c16 * kXRLD + g16 * 8;  // G-phase operand base
   // ------------------------------------------------------------ SwiGLU FFN
+  // Software-pipelined over hidden chunks: the products of chunk hc's G
+  // tiles, then chunk hc - 1's Y products with chunk hc's SiLU epilogue
+  // (VALU) interleaved among them, then one barrier.  Order of weight
+  // phases: G0 | G1, Y0 | G2, Y1 | ... | Y(last).
   f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
   zero16(y);
-#pragma unroll 1
-  for (int hc = 0; hc < nchunk; ++hc) {
-    bf16_t *g = sm.gs[hc & 1];
-    {  // G^T tiles: W1 and W3 rows of this wave's 16 hidden units x 128 tokens
-      f32x4 acc[2][8];
-      zero4(acc[0]);
-      zero4(acc[1]);
-      const Src cur = src_g(L, hc, w, lane), nxt = src_y(L, hc, w, lane, nkh);
-      run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+  f32x4 acc[2][8];  // G^T of one chunk: W1 and W3 rows of this wave's 16 units x 128 tokens
+  auto g_mma = [&](int hc, const Src &nxt) {
+    zero4(acc[0]);
+    zero4(acc[1]);
+    run_phase<kD / 32>(ring, src_g(L, hc, w, lane), nxt, true, [&](int kb, int slot) {
 #pragma unroll
-        for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
-          bf16x8 bx[4];
+      for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
+        bf16x8 bx[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXRLD + kb * 32);
+        for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXRLD + kb * 32);
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
-        }
-      });
-      // lane: hidden rows 4 g16 + i of token 16 t + c16
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float gv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gv[i] = silu_fast(acc[0][t][i]) * acc[1][t][i];
-        u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
-        *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
+          for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
       }
-    }
+    });
+  };
+  // lane: hidden rows 4 g16 + i of token 16 t + c16
+  auto silu_store = [&](bf16_t *g, int t) {
+    float gv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = silu_fast(acc[0][t][i]) * acc[1][t][i];
+    u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
+    *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
+  };
+  // Y^T += W2^T[features 32w.., chunk hc] G^T[chunk, tokens]; with `gnext`,
+  // also the SiLU epilogue of the chunk in acc (two row tiles per block)
+  auto y_mma = [&](int hc, const Src &nxt, bf16_t *gnext) {
+    const bf16_t *g = sm.gs[hc & 1];
+    run_phase<kHC / 32>(ring, src_y(L, hc, w, lane, nkh), nxt, true, [&](int kb, int slot) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 bg[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
+      }
+      if (gnext) {
+        silu_store(gnext, 2 * kb);
+        silu_store(gnext, 2 * kb + 1);
+      }
+    });
+  };
+  static_assert(kHC / 32 * 2 == 8, "two row tiles of the SiLU epilogue per Y block");
+  g_mma(0, nchunk > 1 ? src_g(L, 1, w, lane) : src_y(L, 0, w, lane, nkh));
+#pragma unroll
+  for (int t = 0; t < 8; ++t) silu_store(sm.gs[0], t);
+  __syncthreads();
+#pragma unroll 1
+  for (int hc = 1; hc < nchunk; ++hc) {
+    g_mma(hc, src_y(L, hc - 1, w, lane, nkh));
+    y_mma(hc - 1, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : src_y(L, hc, w, lane, nkh), sm.gs[hc & 1]);
     __syncthreads();
-    {  // Y^T += W2^T[features 32w.., chunk] G^T[chunk, tokens]
-      Src nxt;
-      bool more = true;
-      if (hc + 1 < nchunk) nxt = src_g(L, hc + 1, w, lane);
-      else nxt = src_proj(L, w, lane);
-      const Src cur = src_y(L, hc, w, lane, nkh);
-      run_phase<kHC / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 bg[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
-        }
-      });
-    }
   }
+  y_mma(nchunk - 1, after, nullptr);
 
   // ------------------------------------------------------------ LayerNorm
   // lane: features 32w + c32_row(lane, i) of tokens 32j + l32
@@ -222,29 +244,44 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
     rstd[j] = 1.f;
   }
   if (LN) {
+    // Row statistics in one exchange: each lane's 16 values give a partial
+    // (mean, sum of squared deviations), merged with the other half-wave and
+    // then across the 8 waves by the pairwise formula
+    //   M2 = M2_a + M2_b + (mean_a - mean_b)^2 n_a n_b / (n_a + n_b).
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int j = 0; j < 4; ++j) {
+      float s1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v = 0.f;
+      for (int i = 0; i < 16; ++i) s1 += y[j][i];
+      const float m16 = s1 * (1.0f / 16);
+      float m2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float x = y[j][i];
-          v += pass == 0 ? x : (x - mean[j]) * (x - mean[j]);
-        }
-        v = sum_x32(v);
-        if (hi == 0) sm.red[pass][w][j * 32 + l32] = v;
+      for (int i = 0; i < 16; ++i) m2 += (y[j][i] - m16) * (y[j][i] - m16);
+      uint32_t ma = __float_as_uint(m16), mb = ma, qa = __float_as_uint(m2), qb = qa;
+      swap32(ma, mb);  // ma: lower half-wave's partial, mb: upper's
+      swap32(qa, qb);
+      const float dm = __uint_as_float(ma) - __uint_as_float(mb);
+      if (hi == 0) {
+        sm.red[0][w][j * 32 + l32] = 0.5f * (__uint_as_float(ma) + __uint_as_float(mb));
+        sm.red[1][w][j * 32 + l32] = __uint_as_float(qa) + __uint_as_float(qb) + 8.0f * dm * dm;
       }
-      __syncthreads();
+    }
+    __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = j * 32 + l32;
-        float tot = 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const int t = j * 32 + l32;
+      float mq[8], tot = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tot += sm.red[pass][q][t];
-        if (pass == 0) mean[j] = tot * (1.0f / kD);
-        else rstd[j] = rsqrtf(tot * (1.0f / kD) + 1e-5f);
+      for (int q = 0; q < 8; ++q) {
+        mq[q] = sm.red[0][q][t];
+        tot += mq[q];
       }
+      const float mu = tot * (1.0f / 8);
+      float m2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m2 += sm.red[1][q][t] + 32.0f * (mq[q] - mu) * (mq[q] - mu);
+      mean[j] = mu;
+      rstd[j] = rsqrtf(m2 * (1.0f / kD) + 1e-5f);
     }
   } else {
     __syncthreads();  // every wave is done reading the last G chunk
@@ -321,21 +358,40 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
     if (li > 0) __syncthreads();  // the previous layer's projection is done with X~
 
-    ffn_ln<LN>(ring, L, sm, xt, w, lane, nkh, nchunk);
+    ffn_ln<LN>(ring, L, sm, xt, w, lane, nkh, nchunk, src_kv(L, w, lane));
 
     // ------------------------------------------------------------ W_K | W_V
-    {  // K^T = W_K^T X~^T: 16 consecutive features of one key per lane (after the exchange)
-      f32x16 acc[4];
-      zero16(acc);
-      const Src cur = src_proj(L, w, lane), nxt = src_proj(L, kD / 32 + w, lane);
-      run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
+    // K^T = W_K^T X~^T and V = X~ W_V in one pass over the interleaved weight
+    // stream (K0, V0, K1, V1, ..): the X~ operand of a k block is read once,
+    // for both products.  After the exchange each lane holds 16 consecutive
+    // features of one key (K) or 16 consecutive keys of one feature (V).
+    {
+      f32x16 ka[4], va[4];
+      zero16(ka);
+      zero16(va);
+      bf16x8 bx[2][4];
+      const bool more = li + 1 < hl.M;
+      Src nxt = src_kv(L, w, lane);  // any valid address when nothing follows
+      if (more) {
+        const Layer Ln = layer(li + 1);
+        nxt = src_g(Ln, 0, w, lane);
+      }
+      run_phase<2 * kD / 32>(ring, src_kv(L, w, lane), nxt, more, [&](int b, int slot) {
+        const int kb = b >> 1;
+        if ((b & 1) == 0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 bx[4];
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) bx[j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
+            for (int j = 0; j < 4; ++j) bx[h][j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = mfma32(ring.v[slot][h], bx[j], acc[j]);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ka[j] = mfma32(ring.v[slot][h], bx[h][j], ka[j]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) va[j] = mfma32(bx[h][j], ring.v[slot][h], va[j]);
         }
       });
 #pragma unroll
@@ -343,40 +399,19 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
         const int blk = (int)(row0 >> 5) + j;
         if (blk >= total_blocks) continue;
         u32x4 o0, o1;
-        halves16(acc[j], hi, o0, o1);
+        halves16(ka[j], hi, o0, o1);
         const int f = w * 32 + 16 * hi;
         const int h = f / DH, dh = f % DH;
         bf16_t *dst = L.kb + (((int64_t)blk * H + h) * 32 + l32) * DH + dh;
         stnt16(dst, o0);
         stnt16(dst + 8, o1);
       }
-    }
-    {  // V = X~ W_V with keys as MFMA rows: 16 consecutive keys of one feature per lane
-      f32x16 acc[4];
-      zero16(acc);
-      const bool more = li + 1 < hl.M;
-      Src nxt = src_proj(L, w, lane);  // any valid address when nothing follows
-      if (more) {
-        const Layer Ln = layer(li + 1);
-        nxt = src_g(Ln, 0, w, lane);
-      }
-      const Src cur = src_proj(L, kD / 32 + w, lane);
-      run_phase<kD / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          bf16x8 bx[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bx[j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] = mfma32(bx[j], ring.v[slot][h], acc[j]);
-        }
-      });
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int blk = (int)(row0 >> 5) + j;
         if (blk >= total_blocks) continue;
         u32x4 o0, o1;
-        halves16(acc[j], hi, o0, o1);
+        halves16(va[j], hi, o0, o1);
         const int f = w * 32 + l32;
         const int h = f / DH, dh = f % DH;
         bf16_t *dst = L.vb + (((int64_t)blk * H + h) * DH + dh) * 32 + 16 * hi;
@@ -451,14 +486,14 @@ __global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs a
     __syncthreads();  // the previous tile's attention is done with the staging
     const int64_t row0 = (int64_t)tile * kR;
     gather_tile(a, sm, row0, P.pblk[at.B], ltid, false);
-    ffn_ln<LN>(ring, L, sm, sm.xs, w, lane, nkh, nchunk);
+    ffn_ln<LN>(ring, L, sm, sm.xs, w, lane, nkh, nchunk, src_k(L, w, lane));
 
     bf16_t *const kst = &sm.gs[0][0];  // K: [key][feature], row stride kXLD
     bf16_t *const vst = sm.xs;         // V^T: [feature][128 keys], swizzled chunks
     {  // K^T = W_K^T X~^T
       f32x16 acc[4];
       zero16(acc);
-      const Src cur = src_proj(L, w, lane), nxt = src_proj(L, kD / 32 + w, lane);
+      const Src cur = src_k(L, w, lane), nxt = src_v(L, w, lane);
       run_phase<kD / 32>(ring, cur, nxt, true, [&](int kb, int slot) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -482,7 +517,7 @@ __global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs a
       f32x16 acc[4];
       zero16(acc);
       const bool more = tile + 1 < tend;  // then the next tile's first G blocks follow
-      const Src cur = src_proj(L, kD / 32 + w, lane), nxt = src_g(L, 0, w, lane);
+      const Src cur = src_v(L, w, lane), nxt = src_g(L, 0, w, lane);
       run_phase<kD / 32>(ring, cur, nxt, more, [&](int kb, int slot) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

@@ -516,8 +516,13 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
       if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
       if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
       if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
-      if ((e = add(l.wk, d, d, p.wkv, 0))) break;
-      if ((e = add(l.wv, d, d, p.wkv, d / 32))) break;
+      if (d == 256) {  // the d = 256 encoders read W_K and W_V block-interleaved
+        if ((e = add(l.wk, d, d, p.wkv, 0, 4))) break;
+        if ((e = add(l.wv, d, d, p.wkv, 0, 5))) break;
+      } else {
+        if ((e = add(l.wk, d, d, p.wkv, 0))) break;
+        if ((e = add(l.wv, d, d, p.wkv, d / 32))) break;
+      }
       if ((e = add(l.wq, d, d, p.wq, 0))) break;
       if ((e = add(l.wo, d, d, p.wo, 0))) break;
       if (fusion) {

@@ -119,6 +119,11 @@ hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 //   h = (k % 16) / 8, e = k % 8, NK = K / 32.
 // so one fragment load is a single contiguous 1 KB read.  row_tile0 places
 // the matrix at a tile offset of the destination (W_K and W_V share one).
+// fmt 4 / 5 pack W_K / W_V of one layer (d = 256) into one array whose k
+// blocks alternate between the two matrices, so that one wave's K and V
+// fragments of a k block are adjacent:
+//   element (n, k) -> (((rt * NK + kb) * 2 + m) * 2 + h) * 512 + lane * 8 + e,
+//   m = 0 for W_K (fmt 4), 1 for W_V (fmt 5), the rest as fmt 0.
 // fmt 1 packs for the 16x16x32 A operand instead (16-row tiles):
 //   element (n, k) -> ((n / 16 * NK + kb) * 64 + lane) * 8 + e,
 //   lane = 16 * ((k % 32) / 8) + n % 16,  e = k % 8.
