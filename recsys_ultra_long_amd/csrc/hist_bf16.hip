@@ -165,17 +165,18 @@ DEV void gather_tile(const ChainArgs &a, Smem &sm, int64_t row0, int total_block
 // the rows must survive for another layer).  The ring enters holding the
 // first blocks of G chunk 0 and leaves holding those of `after` (the
 // projection's weight stream); X~ is visible to every thread on return.
-template <bool LN>
+template <bool LN, bool PIPE>
 DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lane, int nkh, int nchunk,
                 const Src &after) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int c16 = lane & 15, g16 = lane >> 4;
   const bf16_t *const xrow = sm.xs + c16 * kXRLD + g16 * 8;  // G-phase operand base
   // ------------------------------------------------------------ SwiGLU FFN
-  // Software-pipelined over hidden chunks: the products of chunk hc's G
-  // tiles, then chunk hc - 1's Y products with chunk hc's SiLU epilogue
+  // PIPE: software-pipelined over hidden chunks: the products of chunk hc's
+  // G tiles, then chunk hc - 1's Y products with chunk hc's SiLU epilogue
   // (VALU) interleaved among them, then one barrier.  Order of weight
-  // phases: G0 | G1, Y0 | G2, Y1 | ... | Y(last).
+  // phases: G0 | G1, Y0 | G2, Y1 | ... | Y(last).  Otherwise (fewer live
+  // registers, for the fused kernel): G(hc), its SiLU, a barrier, Y(hc).
   f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
   zero16(y);
   f32x4 acc[2][8];  // G^T of one chunk: W1 and W3 rows of this wave's 16 units x 128 tokens
@@ -223,17 +224,28 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
     });
   };
   static_assert(kHC / 32 * 2 == 8, "two row tiles of the SiLU epilogue per Y block");
-  g_mma(0, nchunk > 1 ? src_g(L, 1, w, lane) : src_y(L, 0, w, lane, nkh));
+  if (PIPE) {
+    g_mma(0, nchunk > 1 ? src_g(L, 1, w, lane) : src_y(L, 0, w, lane, nkh));
 #pragma unroll
-  for (int t = 0; t < 8; ++t) silu_store(sm.gs[0], t);
-  __syncthreads();
-#pragma unroll 1
-  for (int hc = 1; hc < nchunk; ++hc) {
-    g_mma(hc, src_y(L, hc - 1, w, lane, nkh));
-    y_mma(hc - 1, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : src_y(L, hc, w, lane, nkh), sm.gs[hc & 1]);
+    for (int t = 0; t < 8; ++t) silu_store(sm.gs[0], t);
     __syncthreads();
+#pragma unroll 1
+    for (int hc = 1; hc < nchunk; ++hc) {
+      g_mma(hc, src_y(L, hc - 1, w, lane, nkh));
+      y_mma(hc - 1, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : src_y(L, hc, w, lane, nkh), sm.gs[hc & 1]);
+      __syncthreads();
+    }
+    y_mma(nchunk - 1, after, nullptr);
+  } else {
+#pragma unroll 1
+    for (int hc = 0; hc < nchunk; ++hc) {
+      g_mma(hc, src_y(L, hc, w, lane, nkh));
+#pragma unroll
+      for (int t = 0; t < 8; ++t) silu_store(sm.gs[hc & 1], t);
+      __syncthreads();
+      y_mma(hc, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : after, nullptr);
+    }
   }
-  y_mma(nchunk - 1, after, nullptr);
 
   // ------------------------------------------------------------ LayerNorm
   // lane: features 32w + c32_row(lane, i) of tokens 32j + l32
@@ -358,7 +370,7 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
     if (li > 0) __syncthreads();  // the previous layer's projection is done with X~
 
-    ffn_ln<LN>(ring, L, sm, xt, w, lane, nkh, nchunk, src_kv(L, w, lane));
+    ffn_ln<LN, true>(ring, L, sm, xt, w, lane, nkh, nchunk, src_kv(L, w, lane));
 
     // ------------------------------------------------------------ W_K | W_V
     // K^T = W_K^T X~^T and V = X~ W_V in one pass over the interleaved weight
@@ -486,7 +498,7 @@ __global__ __launch_bounds__(kT, 1) void fused256_kernel(ChainArgs a, AttnArgs a
     __syncthreads();  // the previous tile's attention is done with the staging
     const int64_t row0 = (int64_t)tile * kR;
     gather_tile(a, sm, row0, P.pblk[at.B], ltid, false);
-    ffn_ln<LN>(ring, L, sm, sm.xs, w, lane, nkh, nchunk, src_k(L, w, lane));
+    ffn_ln<LN, false>(ring, L, sm, sm.xs, w, lane, nkh, nchunk, src_k(L, w, lane));
 
     bf16_t *const kst = &sm.gs[0][0];  // K: [key][feature], row stride kXLD
     bf16_t *const vst = sm.xs;         // V^T: [feature][128 keys], swizzled chunks
