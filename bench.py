@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+NOMINAL_CLOCK_GHZ = 2.4        # the clock the bf16 peak is quoted at (256 CUs x 4 SIMDs x 1024 flop/clk)
 
 
 def log(msg):
@@ -43,7 +44,7 @@ def measured_peaks():
     copy (read + write bytes / time, best of five)."""
     import torch
     from recsys_ultra_long_amd import stca
-    mfma = stca.peak_mfma_bf16()
+    mfma, mfma_clk = stca.peak_mfma_bf16()
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -58,7 +59,8 @@ def measured_peaks():
         e1.synchronize()
         best = max(best, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del a, b
-    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_copy_gbs": round(best, 1)}
+    return {"mfma_bf16_tflops": round(mfma, 1), "mfma_bf16_clock_ghz": round(mfma_clk, 3),
+            "hbm_copy_gbs": round(best, 1)}
 
 
 def attach_measured_peaks(res):
@@ -356,6 +358,9 @@ def main():
     torch.cuda.synchronize()
     log(f"warm-up done ({args.warmup} steps)")
 
+    # shader clock during the history launch (staged bf16 path at d = 256)
+    clk = torch.zeros(8, 4, dtype=torch.int64, device="cuda")
+    f.out.clock_probe = clk.data_ptr()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -427,6 +432,13 @@ def main():
                            "launch_ms": round(t_attn * 1e3, 4),
                            "per_launch": f"{n_hist} tokens x {6 * d * h + 4 * d * d} flop + "
                                          f"{pairs} (token, target) pairs x {4 * d} flop"}}
+    ghz = stca.clock_ghz(clk.cpu().numpy())
+    if args.path == "staged" and d == 256 and sp.dtype == "bf16" and ghz == ghz:
+        at_clk = PEAK_BF16_TFLOPS * ghz / NOMINAL_CLOCK_GHZ
+        roof_hist.update({"shader_clock_ghz": round(ghz, 3), "peak_at_clock": round(at_clk, 1),
+                          "frac_at_clock": round(hist_tf / at_clk, 4)})
+        log(f"history launch: shader clock {ghz:.3f} GHz -> bf16 MFMA peak at that clock "
+            f"{at_clk:.0f} TFLOP/s, achieved {hist_tf / at_clk:.1%}")
     picks = {"history": lambda k: (k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
                                    (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
              "attention": lambda k: k.startswith("attn_bf16_kernel<"),

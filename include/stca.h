@@ -209,6 +209,14 @@ typedef struct {
                           head)'s softmax denominator, ln sum_j exp(s_j) (the max plus the
                           log of the rescaled sum; 0 for an empty history).  The backward
                           recomputes the weights exp(s_j - lse) from it. */
+  uint64_t *clock_probe; /* [8][4] optional measurement aid, bf16 staged path at
+                          d = 256: workgroups 0..7 of the history-encoding launch (one
+                          per XCD under round-robin dispatch) write, from their first
+                          wave, {shader-clock counter (s_memtime), 100 MHz counter
+                          (s_memrealtime)} at their start and at their end.  The
+                          ratio of the differences x 0.1 GHz is the shader clock the
+                          chip held during the launch.  Rows of workgroups that do not
+                          exist are left untouched.                                */
 } stca_outputs;
 
 /* Workspace bytes stca_forward needs for this configuration and batch.
@@ -319,9 +327,11 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
  * 32x32x16 MFMA products from registers (blocks * 4 * iters * 8 * 32768
  * flop), writing one checksum per wave to out[blocks * 4] (device, fp32).
  * Timed by the caller on `hip_stream`, it gives the matrix cores' attainable
- * rate at the clock the chip holds under that load.  Enqueued only; returns
+ * rate at the clock the chip holds under that load.  clock (device,
+ * optional, [4]): workgroup 0's {s_memtime, s_memrealtime} at its start and
+ * end, as for stca_outputs.clock_probe.  Enqueued only; returns
  * STCA_ERR_INVALID_ARG for non-positive sizes or a NULL out. */
-int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, void *hip_stream);
+int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, uint64_t *clock, void *hip_stream);
 
 const char *stca_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -333,6 +333,14 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
   if (row0 >= (int64_t)total_blocks * 32) return;
   const int nkh = a.hidden / 32, nchunk = a.hidden / kHC;
   const int H = a.H, DH = kD / a.H;
+  // optional clock probe: shader-clock and 100 MHz counters at start and end
+  // (written at once, so that nothing is held across the layers)
+  const bool probe = hl.clock && blockIdx.x < 8 && tid == 0;
+  if (probe) {
+    const unsigned long long clk0 = __builtin_amdgcn_s_memtime(), rt0 = __builtin_amdgcn_s_memrealtime();
+    hl.clock[blockIdx.x * 4] = clk0;
+    hl.clock[blockIdx.x * 4 + 1] = rt0;
+  }
   auto layer = [&](int i) {
     Layer L;
     L.w1 = (const bf16_t *)hl.w1[i];
@@ -431,6 +439,11 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
         stnt16(dst + 8, o1);
       }
     }
+  }
+  if (hl.clock && blockIdx.x < 8 && tid == 0) {
+    const unsigned long long clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    hl.clock[blockIdx.x * 4 + 2] = clk1;
+    hl.clock[blockIdx.x * 4 + 3] = rt1;
   }
 }
 

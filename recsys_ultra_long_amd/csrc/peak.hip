@@ -10,8 +10,12 @@ namespace {
 
 // Each wave: `iters` rounds of 8 independent 32x32x16 bf16 products
 // (8 x 32,768 flop per round); one checksum per wave keeps the work live.
-__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out) {
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out, unsigned long long *clock) {
   const int lane = threadIdx.x & 63;
+  if (clock && blockIdx.x == 0 && threadIdx.x == 0) {
+    clock[0] = __builtin_amdgcn_s_memtime();
+    clock[1] = __builtin_amdgcn_s_memrealtime();
+  }
   bf16x8 a, b;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -33,16 +37,21 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += acc[j][r];
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+  if (clock && blockIdx.x == 0 && threadIdx.x == 0) {
+    clock[2] = __builtin_amdgcn_s_memtime();
+    clock[3] = __builtin_amdgcn_s_memrealtime();
+  }
 }
 
 }  // namespace
 }  // namespace stca
 
-extern "C" int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, void *hip_stream) {
+extern "C" int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, uint64_t *clock, void *hip_stream) {
   using namespace stca;
   api_clear_error();
   if (blocks <= 0 || iters <= 0 || !out) return api_error(STCA_ERR_INVALID_ARG, "blocks, iters must be > 0, out non-NULL");
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, (int)iters, out);
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, (int)iters, out,
+                     reinterpret_cast<unsigned long long *>(clock));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return api_error(STCA_ERR_HIP, "mfma peak launch: %s", hipGetErrorString(e));
   return STCA_OK;

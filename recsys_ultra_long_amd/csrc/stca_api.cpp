@@ -753,6 +753,7 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     HistLayers hl;
     std::memset(&hl, 0, sizeof(hl));
     hl.M = M;
+    hl.clock = reinterpret_cast<unsigned long long *>(out->clock_probe);
     for (int i = 0; i < M; ++i) {
       const PrepLayer &p = L.pl[i];
       hl.w1[i] = prep + p.kv_w1;

@@ -104,6 +104,7 @@ struct HistLayers {
   const float *ln_g[kMaxLayers], *ln_b[kMaxLayers];
   void *kbuf[kMaxLayers], *vbuf[kMaxLayers];
   int M;
+  unsigned long long *clock;  // optional [8][4]: start / end clock counters of workgroups 0..7
 };
 hipError_t launch_hist_layers(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
 // d = 256: 128-row tiles on 8 waves (W1, W3 packed with fmt 1).

@@ -63,7 +63,8 @@ class Weights(C.Structure):
 class Outputs(C.Structure):
     _fields_ = [("z", _vp), ("o_layers", _vp), ("attn", _vp), ("active", _vp), ("q_dump", _vp),
                 ("kv_dump", _vp), ("x_dump", _vp), ("dev_status", _vp),
-                ("stage_events", C.POINTER(_vp)), ("n_stage_events", C.c_int32), ("lse", _vp)]
+                ("stage_events", C.POINTER(_vp)), ("n_stage_events", C.c_int32), ("lse", _vp),
+                ("clock_probe", _vp)]
 
 
 class FfnGrad(C.Structure):
@@ -119,7 +120,7 @@ def load() -> C.CDLL:
                                                      C.POINTER(C.c_size_t)]
         lib.stca_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
                                       C.POINTER(Grads), _vp, C.c_size_t, _vp]
-        lib.stca_peak_mfma_bf16.argtypes = [C.c_int32, C.c_int32, _vp, _vp]
+        lib.stca_peak_mfma_bf16.argtypes = [C.c_int32, C.c_int32, _vp, _vp, _vp]
         lib.stca_status_string.restype = C.c_char_p
         lib.stca_status_string.argtypes = [C.c_int]
         lib.stca_last_error.restype = C.c_char_p
@@ -468,21 +469,38 @@ def to_numpy_stored(t) -> np.ndarray:
     return a
 
 
-def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3) -> float:
-    """Attainable dense bf16 MFMA rate (TFLOP/s): the best of `repeats` timed
-    launches of the library's MFMA-only measurement kernel."""
+def clock_ghz(c) -> float:
+    """Shader clock (GHz) from {s_memtime, s_memrealtime} pairs at start and
+    end (rows of 4 counters, as the library writes them; rows with no elapsed
+    100 MHz ticks are ignored)."""
+    c = np.asarray(c, dtype=np.int64).reshape(-1, 4)
+    ticks = c[:, 3] - c[:, 1]
+    ok = ticks > 0
+    if not ok.any():
+        return float("nan")
+    return float(np.mean((c[ok, 2] - c[ok, 0]) / ticks[ok]) * 0.1)
+
+
+def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3):
+    """Attainable dense bf16 MFMA rate (TFLOP/s), the best of `repeats` timed
+    launches of the library's MFMA-only measurement kernel, and the shader
+    clock (GHz) during that launch."""
     import torch
     lib = load()
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(4, dtype=torch.int64, device="cuda")
     s = torch.cuda.current_stream()
     flops = blocks * 4 * iters * 8 * 32768
-    best = 0.0
-    _check(lib.stca_peak_mfma_bf16(blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(s.cuda_stream)))
+    best, best_clk = 0.0, float("nan")
+    args = (blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(clk.data_ptr()), C.c_void_p(s.cuda_stream))
+    _check(lib.stca_peak_mfma_bf16(*args))
     for _ in range(repeats):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(s)
-        _check(lib.stca_peak_mfma_bf16(blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(s.cuda_stream)))
+        _check(lib.stca_peak_mfma_bf16(*args))
         b.record(s)
         b.synchronize()
-        best = max(best, flops / (a.elapsed_time(b) * 1e-3) / 1e12)
-    return best
+        rate = flops / (a.elapsed_time(b) * 1e-3) / 1e12
+        if rate > best:
+            best, best_clk = rate, clock_ghz(clk.cpu().numpy())
+    return best, best_clk

@@ -319,6 +319,13 @@ def test_cross_mask_attention_and_backward_validation():
 
 def test_peak_mfma_validation():
     lib = stca.load()
-    assert lib.stca_peak_mfma_bf16(0, 10, C.c_void_p(FAKE), None) == stca.ERR_INVALID_ARG
-    assert lib.stca_peak_mfma_bf16(4, 0, C.c_void_p(FAKE), None) == stca.ERR_INVALID_ARG
-    assert lib.stca_peak_mfma_bf16(4, 10, None, None) == stca.ERR_INVALID_ARG
+    assert lib.stca_peak_mfma_bf16(0, 10, C.c_void_p(FAKE), None, None) == stca.ERR_INVALID_ARG
+    assert lib.stca_peak_mfma_bf16(4, 0, C.c_void_p(FAKE), None, None) == stca.ERR_INVALID_ARG
+    assert lib.stca_peak_mfma_bf16(4, 10, None, None, None) == stca.ERR_INVALID_ARG
+
+
+def test_clock_ghz():
+    # 2.3e6 shader cycles over 1e5 ticks of the 100 MHz counter = 2.3 GHz; a
+    # row with no elapsed ticks (workgroup that did not exist) is ignored
+    c = [[10, 1000, 10 + 2_300_000, 1000 + 100_000], [0, 0, 0, 0]]
+    assert abs(stca.clock_ghz(c) - 2.3) < 1e-12
