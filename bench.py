@@ -63,10 +63,13 @@ def measured_peaks():
             "hbm_copy_gbs": round(best, 1)}
 
 
-def attach_measured_peaks(res):
+def attach_measured_peaks(res, skip=False):
     """Beside each roofline's nominal peak: the attainable rate measured in
     this run and the achieved fraction of it (context; `frac` stays the
     fraction of the nominal peak)."""
+    if skip:
+        res["measured_peaks"] = None
+        return
     mp = measured_peaks()
     res["measured_peaks"] = mp
     log(f"measured peaks: {mp}")
@@ -272,7 +275,7 @@ def bench_backward(args):
         "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
         "backward_flops": {"proper": flops_b, "recompute": flops_f},
     }
-    attach_measured_peaks(res)
+    attach_measured_peaks(res, args.no_measured_peaks)
     if not args.no_cpu_baseline:
         log(f"timing the float64 backward oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline_backward(p, dz_np, args.cpu_seconds)
@@ -303,6 +306,8 @@ def main():
                     help="skip timing the other path for comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the MFMA-only and device-copy measurements (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (x5), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -514,7 +519,7 @@ def main():
                                        "value": round(n_hist * M / (mso * 1e-3), 1)})
             log(f"other path ({other}{'+dedup' if dd else ''}): {mso:.3f} ms/step")
             del fo, dpo
-    attach_measured_peaks(res)
+    attach_measured_peaks(res, args.no_measured_peaks)
     if not args.no_cpu_baseline:
         log(f"timing the float64 oracle for ~{args.cpu_seconds:.0f}s")
         res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
