@@ -333,6 +333,16 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
  * STCA_ERR_INVALID_ARG for non-positive sizes or a NULL out. */
 int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, uint64_t *clock, void *hip_stream);
 
+/* Measurement aid, not a step of the method: `blocks` workgroups of 256
+ * threads stream `bytes` (a multiple of 16) of device memory at buf once with
+ * 16-byte non-temporal loads, the access the attention uses for K/V, and
+ * write one word to out[0] (device) only if the data XOR to a sentinel (so
+ * the loads are live).  Timed by the caller over a buffer larger than the
+ * memory-side cache, it gives the attainable HBM read rate.  Enqueued only;
+ * STCA_ERR_INVALID_ARG for non-positive sizes, a size not a multiple of 16,
+ * or NULL pointers. */
+int stca_peak_hbm_read(const void *buf, int64_t bytes, int32_t blocks, uint32_t *out, void *hip_stream);
+
 const char *stca_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char *stca_last_error(void);

@@ -28,6 +28,11 @@ COMMON = [
 ]
 
 
+# Per-source flags.  attn.hip: no NaN reaches the attention (masked keys get
+# a large finite negative score), so max() needs no NaN-quieting moves.
+FILE_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
+
+
 def sources(src_dir: str = CSRC):
     return sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir)
                   if f.endswith((".hip", ".cpp")))
@@ -42,7 +47,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, extra, obj_dir: str) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *extra, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stderr or "").splitlines()
                      if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)

@@ -27,7 +27,8 @@ DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
            "stca_attention", "stca_backward_workspace_size", "stca_backward",
-           "stca_peak_mfma_bf16", "stca_status_string", "stca_last_error", "stca_version")
+           "stca_peak_mfma_bf16", "stca_peak_hbm_read", "stca_status_string", "stca_last_error",
+           "stca_version")
 
 _vp = C.c_void_p
 
@@ -121,12 +122,14 @@ def load() -> C.CDLL:
         lib.stca_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
                                       C.POINTER(Grads), _vp, C.c_size_t, _vp]
         lib.stca_peak_mfma_bf16.argtypes = [C.c_int32, C.c_int32, _vp, _vp, _vp]
+        lib.stca_peak_hbm_read.argtypes = [_vp, C.c_int64, C.c_int32, _vp, _vp]
         lib.stca_status_string.restype = C.c_char_p
         lib.stca_status_string.argtypes = [C.c_int]
         lib.stca_last_error.restype = C.c_char_p
         lib.stca_version.restype = C.c_int
         for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
-                  "stca_attention", "stca_backward_workspace_size", "stca_backward", "stca_peak_mfma_bf16"):
+                  "stca_attention", "stca_backward_workspace_size", "stca_backward", "stca_peak_mfma_bf16",
+                  "stca_peak_hbm_read"):
             getattr(lib, f).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -479,6 +482,29 @@ def clock_ghz(c) -> float:
     if not ok.any():
         return float("nan")
     return float(np.mean((c[ok, 2] - c[ok, 0]) / ticks[ok]) * 0.1)
+
+
+def peak_hbm_read(nbytes: int = 2 << 30, blocks: int = 1024, repeats: int = 4) -> float:
+    """Attainable HBM read rate (GB/s): the best of `repeats` timed launches
+    of the library's streaming-read kernel over a fresh buffer of `nbytes`
+    (larger than the 256 MB memory-side cache by default)."""
+    import torch
+    lib = load()
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream()
+    args = (C.c_void_p(buf.data_ptr()), nbytes, blocks, C.c_void_p(out.data_ptr()), C.c_void_p(s.cuda_stream))
+    _check(lib.stca_peak_hbm_read(*args))
+    best = 0.0
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        _check(lib.stca_peak_hbm_read(*args))
+        b.record(s)
+        b.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return best
 
 
 def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3):

@@ -324,6 +324,15 @@ def test_peak_mfma_validation():
     assert lib.stca_peak_mfma_bf16(4, 10, None, None, None) == stca.ERR_INVALID_ARG
 
 
+def test_peak_hbm_read_validation():
+    lib = stca.load()
+    for args in [(None, 1024, 4, FAKE), (FAKE, 0, 4, FAKE), (FAKE, 1000, 4, FAKE), (FAKE, 1024, 0, FAKE),
+                 (FAKE, 1024, 4, None)]:
+        buf, n, blocks, out = args
+        assert lib.stca_peak_hbm_read(C.c_void_p(buf) if buf else None, n, blocks,
+                                      C.c_void_p(out) if out else None, None) == stca.ERR_INVALID_ARG
+
+
 def test_clock_ghz():
     # 2.3e6 shader cycles over 1e5 ticks of the 100 MHz counter = 2.3 GHz; a
     # row with no elapsed ticks (workgroup that did not exist) is ignored

@@ -23,6 +23,12 @@ def test_peak_kernel_clock():
     assert 0.3 < ghz < 3.0
 
 
+def test_hbm_read_stream():
+    # 256 MB: the rate is only sanity-checked here (the bench streams 2 GiB)
+    rate = stca.peak_hbm_read(nbytes=256 << 20, blocks=512, repeats=2)
+    assert 500.0 < rate < 20000.0
+
+
 def test_history_launch_clock_probe():
     # 3 users of 300 items: 1,024 padded rows = 8 workgroups of 128 rows; a
     # sentinel row past them must stay untouched
