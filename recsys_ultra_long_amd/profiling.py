@@ -3,9 +3,12 @@
     python -m recsys_ultra_long_amd.profiling kernels  <stats.csv> <out.md> <command...>
     python -m recsys_ultra_long_amd.profiling traffic  <fetch.csv> <write.csv> \
         <copy_fetch.csv> <copy_write.csv> <copy_bytes> <out.md> <command...>
+    python -m recsys_ultra_long_amd.profiling mfma  <counters.csv> <kernel_trace.csv> <out.md> <command...>
 
 ``kernels`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
-average duration).  ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+average duration).  ``mfma`` turns a ``--pmc MfmaUtil MfmaFlopsBF16
+--kernel-trace`` run into per-kernel MFMA busy percentage and bf16 MFMA
+TFLOP/s (counted operations over the dispatch's own duration).  ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of the profiled
 kernels, each scaled by what the same counter reads for a plain device copy
 of known size (``bench.py --copy-calibration``).  The traffic summary carries
@@ -27,7 +30,10 @@ CSRC = os.path.join(HERE, "csrc")
 
 
 def source_hash() -> str:
+    """Hash of the kernel sources and of the flags they are compiled with."""
+    from recsys_ultra_long_amd import build
     h = hashlib.sha256()
+    h.update(json.dumps([build.COMMON[1:], build.FILE_FLAGS], sort_keys=True).encode())
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".cpp", ".h")):
             h.update(f.encode())
@@ -96,6 +102,34 @@ def write_traffic(fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, out,
     open(out, "w").write("\n".join(lines))
 
 
+def write_mfma(counters_csv: str, trace_csv: str, out: str, command: str):
+    """Per kernel: dispatches, mean MfmaUtil (%), mean bf16 MFMA flops per
+    dispatch and the rate over the dispatch's own duration."""
+    dur = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name = short_name(r.get("Kernel_Name") or r.get("KernelName"))
+        dur[name].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    util = pmc_per_kernel(counters_csv, "MfmaUtil")
+    flops = pmc_per_kernel(counters_csv, "MfmaFlopsBF16")
+    lines = ["# MFMA counters per dispatch (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --kernel-trace)", "",
+             f"Command: `{command}`", "",
+             "MfmaUtil = busy cycles of the matrix cores over GPU-active cycles, all SIMDs; "
+             "MfmaFlopsBF16 = bf16 MFMA operations counted by the hardware; rate = those over "
+             "the dispatch's mean duration in the same run.", "",
+             "| kernel | dispatches | MfmaUtil % | bf16 MFMA GFLOP / dispatch | mean us | bf16 TFLOP/s |",
+             "|---|---|---|---|---|---|"]
+    rows = []
+    for k, f in flops.items():
+        if f <= 0:
+            continue
+        d = sum(dur.get(k, [0.0])) / max(len(dur.get(k, [])), 1)
+        rows.append((k, len(dur.get(k, [])), util.get(k, float("nan")), f / 1e9, d / 1e3,
+                     f / (d * 1e-9) / 1e12 if d > 0 else float("nan")))
+    for k, n, u, g, us, tf in sorted(rows, key=lambda r: -r[3] * r[1]):
+        lines.append(f"| `{k}` | {n} | {u:.1f} | {g:.1f} | {us:.1f} | {tf:.0f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def read_traffic(path: str):
     """The JSON block of a traffic summary, or None if missing or stale."""
     if not os.path.exists(path):
@@ -113,6 +147,8 @@ if __name__ == "__main__":
         write_kernels(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif cmd == "traffic":
         write_traffic(*sys.argv[2:8], " ".join(sys.argv[8:]))
+    elif cmd == "mfma":
+        write_mfma(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
     elif cmd == "hash":
         print(source_hash())
     else:
