@@ -57,6 +57,15 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   mixing, one FFN per mixed token and the residual; the first N boosted
   tokens are the next layer's queries (the non-sequence tokens re-enter from
   F at every layer) and, after the last layer, the output z.
+* LONGER-style sequence encoding ([HyFormer] §3.4.1 (ii), eq. (6), then (8)):
+  per layer, H_l = CrossAttn(S_short, S, S) is the standard multi-head
+  softmax cross attention (its own W_Q, W_K, W_V, W_O per layer, heads as
+  d_h-wide column slices, scale 1/sqrt(d_h), no residual, no LN) from the
+  compact short sequence to the whole sequence, and K_l = H_l W_K,
+  V_l = H_l W_V; the queries then decode these L_H rows.  S_short is the
+  last min(L, L_H) rows of the user's history (the page does not say how the
+  short sequence is formed; the most recent items are the plainest reading).
+  The history FFN and its LN are not applied in this mode.
 
 Parity pins: every function below is pinned by a closed form, an invariant,
 a brute-force enumeration or an independent library routine in
@@ -229,10 +238,31 @@ def weights_f64(layers, z=None, wz=None):
 
 
 # ---------------------------------------------------------------- forward
-def encode_history(X: np.ndarray, lw: dict, kv_ln: bool):
+def longer_encode(X: np.ndarray, enc: dict, l_short: int, H: int) -> np.ndarray:
+    """[HyFormer] eq. (6): H_l = CrossAttn(S_short, S, S) over one user's
+    raw rows X [L, d]: each of the last min(L, l_short) rows, projected by
+    enc["wq"], attends (multi-head softmax) over all of X projected by
+    enc["wk"], enc["wv"]; the head outputs, concatenated, go through
+    enc["wo"].  Returns [min(L, l_short), d]."""
+    L, d = X.shape
+    ls = min(L, l_short)
+    Ke, Ve = X @ enc["wk"], X @ enc["wv"]
+    out = np.zeros((ls, d))
+    for r in range(ls):
+        a, _, _ = attention_target(X[L - ls + r] @ enc["wq"], Ke, Ve, H, "softmax")
+        out[r] = a @ enc["wo"]
+    return out
+
+
+def encode_history(X: np.ndarray, lw: dict, kv_ln: bool, encoder: str = "swiglu", l_short: int = 0,
+                   H: int = 0):
     """History side of one layer: K = Xt W_K, V = Xt W_V with
-    Xt = LN(SwiGLU(X)) ([Notes] §STCA; [HyFormer] eq. (7)-(8) without LN)."""
-    xt = ffn_ln(X, lw["kv"], kv_ln)
+    Xt = LN(SwiGLU(X)) ([Notes] §STCA; [HyFormer] eq. (7)-(8) without LN), or,
+    for the LONGER-style encoder, Xt = H_l of eq. (6) (``longer_encode``)."""
+    if encoder == "longer":
+        xt = longer_encode(X, lw["enc"], l_short, H)
+    else:
+        xt = ffn_ln(X, lw["kv"], kv_ln)
     return xt @ lw["wk"], xt @ lw["wv"]
 
 
@@ -242,7 +272,7 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
     """The STCA forward for the users in ``users`` (default: all).
 
     cfg: dict with d, H, M, score ("softmax"|"relu"), qmode ("fusion"|"linear"),
-         kv_ln, z_ln.
+         kv_ln, z_ln; optionally encoder ("swiglu"|"longer") and l_short.
     rows_f64: callable ids -> float64 table rows [len(ids), d].
     layers/z/wz: float64 weights (see ``weights_f64``).
     Returns a dict of float64 arrays indexed by global target index:
@@ -266,7 +296,8 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
         X = rows_f64(ids) if len(ids) else np.zeros((0, d))
         # Request Level Batching: the user's K/V of every layer is computed
         # once and serves all of the user's targets ([Notes] §RLB).
-        KV = [encode_history(X, layers[i], cfg["kv_ln"]) for i in range(M)]
+        KV = [encode_history(X, layers[i], cfg["kv_ln"], cfg.get("encoder", "swiglu"), cfg.get("l_short", 0), H)
+              for i in range(M)]
         km = None if key_mask is None else np.asarray(key_mask)[ho[u]:ho[u + 1]]
         cm = dict(key_mask=km, head_map=head_map)
         if qmode == "hyformer":
@@ -326,7 +357,8 @@ def forward_problem(p, users=None):
     sp = p.spec
     layers, z, wz = weights_f64(p.layers, p.z, p.wz)
     cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode,
-               kv_ln=sp.kv_ln, z_ln=sp.z_ln)
+               kv_ln=sp.kv_ln, z_ln=sp.z_ln, encoder=getattr(sp, "encoder", "swiglu"),
+               l_short=getattr(sp, "l_short", 0))
     hy = None
     if sp.qmode == "hyformer":
         hy = {"ns": stored_to_f64(p.extra["ns"]),

@@ -106,6 +106,8 @@ class Spec:
     beta_a: float = 2.0
     n_ns: int = 0                       # hyformer: non-sequence feature tokens per user
     hy_hidden: Optional[int] = None     # hyformer: hidden width of the query FFNs (default d)
+    encoder: str = "swiglu"             # history encoding: "swiglu" (FFN [+LN]) | "longer"
+    l_short: int = 0                    # longer: length L_H of the short query sequence
     m: int = 1                          # targets (or queries) per user
     ids: str = "zipf"                   # "zipf" | "uniform"
     zipf_s: float = 1.1
@@ -343,6 +345,10 @@ def make_problem(sp: Spec, *, with_table: bool = True, threads: int = 8) -> Prob
     if sp.qmode == "hyformer":
         for i, l in enumerate(layers):
             l["boost"] = extra["boost"][i]
+    if sp.encoder == "longer":  # the encoder's own projections, from a stream of their own
+        ge = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 0x4C4E])))
+        for l in layers:
+            l["enc"] = {k: _mat(ge, sp, sp.d, sp.d) for k in ("wq", "wk", "wv", "wo")}
     table = make_table(sp, threads) if with_table else None
     return Problem(sp, hist_offsets.astype(np.int32), hist_ids, tgt_offsets.astype(np.int32),
                    tgt_ids, q0, table, layers, z, wz,
