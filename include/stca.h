@@ -79,6 +79,18 @@ enum { STCA_Q_FUSION = 0, STCA_Q_LINEAR = 1,          /* stca_config.qmode  */
  * cfg->q_hidden.  bf16, staged path; the history side is HyFormer's
  * eq. (7)-(8) encoding as in STCA_Q_LINEAR. */
 enum { STCA_PATH_STAGED = 0, STCA_PATH_FUSED = 1 };    /* stca_config.path   */
+enum { STCA_ENC_SWIGLU = 0, STCA_ENC_LONGER = 1 };     /* stca_config.encoder */
+/* History (sequence) encoding of every layer:
+ *  STCA_ENC_SWIGLU: Xt = [LN](SwiGLU(X)) of the raw rows X ([Notes] §STCA;
+ *    [HyFormer] eq. (7)), K = Xt W_K, V = Xt W_V.
+ *  STCA_ENC_LONGER ([HyFormer] §3.4.1 (ii), eq. (6) then (8)): per layer
+ *    H_l = CrossAttn(S_short, S, S), the multi-head softmax cross attention
+ *    (scale 1/sqrt(d_h), the layer's own enc_wq / enc_wk / enc_wv / enc_wo,
+ *    no residual, no LN) from the user's last min(L_u, l_short) history rows
+ *    (S_short) to all of its rows (S); then K = H_l W_K, V = H_l W_V, and the
+ *    targets attend over these min(L_u, l_short) rows.  bf16, staged path,
+ *    softmax scores; not with STCA_FLAG_DEDUP, Cross-Mask, x_dump, kv_dump or
+ *    stca_backward.  The history FFN weights (layer.kv) are not read. */
 enum {                                                 /* stca_config.flags  */
   STCA_FLAG_KV_LN = 1,  /* LN after the history FFN (STCA); clear for HyFormer eq. (7) */
   STCA_FLAG_Z_LN = 2,   /* LN on the final z ([Notes] wording); default is [Review]'s z */
@@ -118,6 +130,8 @@ typedef struct {
                            under different masks): head h scores with the Q / K
                            columns of head head_map[h] (values in [0, H)); its V
                            columns and output slice stay its own.  Staged bf16 only */
+  int32_t encoder;      /* STCA_ENC_* (0: the SwiGLU encoding)                    */
+  int32_t l_short;      /* STCA_ENC_LONGER: short-sequence length L_H, 1..4096     */
 } stca_config;
 
 /* One batch of requests: ragged histories and targets in CSR form.
@@ -165,6 +179,8 @@ typedef struct {
                          i < M-1; else ignored)                                      */
   const void *boost_w1, *boost_w3;  /* [T, d, q_hidden] per-token boosting FFNs      */
   const void *boost_w2;             /* [T, q_hidden, d]   (STCA_Q_HYFORMER)           */
+  const void *enc_wq, *enc_wk, *enc_wv, *enc_wo;  /* [d, d] each: the cross attention of
+                                                     STCA_ENC_LONGER (NULL otherwise) */
 } stca_layer;
 
 typedef struct {

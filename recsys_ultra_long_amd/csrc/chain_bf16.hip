@@ -879,8 +879,9 @@ hipError_t dispatch_d(const ChainArgs &a, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    auto k = a.ln ? chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>
-                  : chain_kernel<D, TTH, IN_GATHER_CSR, true, false, true, OUT_KV>;
+    auto k = !a.ffn ? chain_kernel<D, TTH, IN_GATHER_CSR, false, false, true, OUT_KV>
+             : a.ln ? chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>
+                    : chain_kernel<D, TTH, IN_GATHER_CSR, true, false, true, OUT_KV>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
     ah.pf_stride = cus * per_cu;
@@ -889,14 +890,16 @@ hipError_t dispatch_d(const ChainArgs &a, hipStream_t s) {
 #define CH(TT, IN, FFN, LN, PROJ, OUT) \
   hipLaunchKernelGGL((chain_kernel<D, TT, IN, FFN, LN, PROJ, OUT>), grid(TT), block, 0, s, a)
   switch (a.in_mode) {
-    case IN_GATHER_CSR:  // history: FFN (+LN) then K/V
-      if (!(f && p && a.out_mode == OUT_KV)) return hipErrorInvalidValue;
-      if (l) hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>), grid(TTH), block, 0, s, ah);
+    case IN_GATHER_CSR:  // history: FFN (+LN) then K/V; or K/V of the raw rows alone
+      if (!(p && a.out_mode == OUT_KV) || (!f && l)) return hipErrorInvalidValue;
+      if (!f) hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, false, false, true, OUT_KV>), grid(TTH), block, 0, s, ah);
+      else if (l) hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, true, true, true, OUT_KV>), grid(TTH), block, 0, s, ah);
       else hipLaunchKernelGGL((chain_kernel<D, TTH, IN_GATHER_CSR, true, false, true, OUT_KV>), grid(TTH), block, 0, s, ah);
       break;
-    case IN_GATHER_IDS:  // first query: FFN + LN + W_Q
-      if (!(f && l && p)) return hipErrorInvalidValue;
-      CH(TTQ, IN_GATHER_IDS, true, true, true, OUT_ROWS);
+    case IN_GATHER_IDS:  // first query: FFN + LN + W_Q; or a projection of the gathered rows alone
+      if (f && l && p) CH(TTQ, IN_GATHER_IDS, true, true, true, OUT_ROWS);
+      else if (!f && !l && p) CH(TTQ, IN_GATHER_IDS, false, false, true, OUT_ROWS);
+      else return hipErrorInvalidValue;
       break;
     case IN_DENSE:  // projections only (W_Q, W_O, R)
       if (f || l || !p) return hipErrorInvalidValue;

@@ -37,8 +37,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ int bad_h, bad_t;
   const int t = threadIdx.x;
   if (t == 0) {
-    bad_h = (hist_off[0] != 0) || ((long long)hist_off[B] != n_hist);
-    bad_t = (tgt_off[0] != 0) || ((long long)tgt_off[B] != n_tgt);
+    // a negative total means the offsets were built on the device and the
+    // host holds only an upper bound (the LONGER short sequences)
+    bad_h = (hist_off[0] != 0) || (n_hist >= 0 ? (long long)hist_off[B] != n_hist : false);
+    bad_t = (tgt_off[0] != 0) || (n_tgt >= 0 ? (long long)tgt_off[B] != n_tgt : false);
   }
   __syncthreads();
   for (int u = t; u < B; u += kPlanThreads) {
@@ -98,7 +100,64 @@ __global__ __launch_bounds__(256) void padded_ids_kernel(Plan plan, int B, const
   plan.prow[r] = id;
 }
 
+// Short sequences of the LONGER-style encoding ([HyFormer] eq. (6)): user u
+// keeps its last ls_u = min(L_u, l_short) items.  One block: ls_u and its
+// exclusive scan into short_off (all users empty when hist_off is
+// inconsistent, as in the planner).
+__global__ __launch_bounds__(kPlanThreads) void short_off_kernel(const int *__restrict__ hist_off, int B,
+                                                                 long long n_hist, int l_short, int *short_off) {
+  __shared__ int sh[kPlanThreads];
+  __shared__ int bad;
+  const int t = threadIdx.x;
+  if (t == 0) bad = (hist_off[0] != 0) || ((long long)hist_off[B] != n_hist);
+  __syncthreads();
+  for (int u = t; u < B; u += kPlanThreads)
+    if (hist_off[u + 1] - hist_off[u] < 0) atomicOr(&bad, 1);
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base <= B; base += kPlanThreads) {
+    const int u = base + t;
+    int ls = 0;
+    if (u < B && !bad) ls = min(hist_off[u + 1] - hist_off[u], l_short);
+    int tot;
+    const int ex = block_exclusive_scan(ls, sh, tot);
+    if (u <= B) short_off[u] = carry + ex;
+    carry += tot;
+  }
+}
+
+// One block per user: the table ids of its short items (in history order),
+// then every block fills its share of the identity map and pads short_ids up
+// to the host bound with id 0 (rows past the device count are computed by
+// bound-sized launches and discarded; they must still gather a valid row).
+__global__ __launch_bounds__(256) void short_ids_kernel(const int *__restrict__ hist_off,
+                                                        const int *__restrict__ hist_ids, int B,
+                                                        const int *__restrict__ short_off, long long bound,
+                                                        int *short_ids, int *iota) {
+  const int u = blockIdx.x;
+  const int s0 = short_off[u], ls = short_off[u + 1] - s0;
+  const int end = hist_off[u + 1];
+  for (int r = threadIdx.x; r < ls; r += 256) short_ids[s0 + r] = hist_ids[end - ls + r];
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < bound; i += stride) {
+    iota[i] = (int)i;
+    if (i >= short_off[B]) short_ids[i] = 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_short_seq(const int *hist_off, const int *hist_ids, int B, int64_t n_hist, int l_short,
+                            int64_t bound, int *short_off, int *short_ids, int *iota, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(short_off_kernel, dim3(1), dim3(kPlanThreads), 0, s, hist_off, B, (long long)n_hist, l_short,
+                     short_off);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || bound <= 0) return e;
+  hipLaunchKernelGGL(short_ids_kernel, dim3((unsigned)B), dim3(256), 0, s, hist_off, hist_ids, B, short_off,
+                     (long long)bound, short_ids, iota);
+  return hipGetLastError();
+}
 
 hipError_t launch_padded_ids(const Plan &plan, int B, const int *hist_ids, int64_t table_rows,
                              int64_t max_blocks, int *status, hipStream_t s) {

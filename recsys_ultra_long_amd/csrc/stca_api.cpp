@@ -157,6 +157,17 @@ int validate_cfg(const stca_config *c) {
     if (c->hidden <= 0 || c->hidden % 32)
       return fail(STCA_ERR_UNSUPPORTED, "fp32 needs hidden a positive multiple of 32 (got %d)", c->hidden);
   }
+  if (c->encoder != STCA_ENC_SWIGLU && c->encoder != STCA_ENC_LONGER)
+    return fail(STCA_ERR_INVALID_ARG, "encoder %d unknown", c->encoder);
+  if (c->encoder == STCA_ENC_LONGER) {
+    if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is bf16 only");
+    if (c->path != STCA_PATH_STAGED) return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER needs the staged path");
+    if (c->score != STCA_SCORE_SOFTMAX) return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER uses softmax scores");
+    if (c->flags & STCA_FLAG_DEDUP) return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is not available with STCA_FLAG_DEDUP");
+    if (c->head_map) return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is not available with Cross-Mask maps");
+    if (c->l_short < 1 || c->l_short > 4096)
+      return fail(STCA_ERR_INVALID_ARG, "l_short %d outside 1..4096", c->l_short);
+  }
   return STCA_OK;
 }
 
@@ -232,6 +243,8 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
   const void *ptrs[] = {b->hist_offsets, b->hist_ids, b->tgt_offsets, b->tgt_ids, b->q0, b->table};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
+  if (c->encoder == STCA_ENC_LONGER && b->key_mask)
+    return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is not available with Cross-Mask masks");
   int r = validate_dedup(c);
   if (r) return r;
   if ((r = validate_cross_mask(c, b))) return r;
@@ -252,8 +265,14 @@ int validate_weights(const stca_config *c, const stca_weights *w) {
   const bool kvln = c->flags & STCA_FLAG_KV_LN;
   for (int i = 0; i < c->M; ++i) {
     const stca_layer &l = w->layers[i];
-    int r = check_ffn(l.kv, kvln, "kv", i);
-    if (r) return r;
+    int r = STCA_OK;
+    if (c->encoder == STCA_ENC_LONGER) {  // the history FFN is not used
+      const void *em[] = {l.enc_wq, l.enc_wk, l.enc_wv, l.enc_wo};
+      for (const void *p : em)
+        if (!p || !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "encoder weight NULL or misaligned (layer %d)", i);
+    } else if ((r = check_ffn(l.kv, kvln, "kv", i))) {
+      return r;
+    }
     const void *mats[] = {l.wk, l.wv, l.wq, l.wo};
     for (const void *p : mats) {
       if (!p) return fail(STCA_ERR_INVALID_ARG, "W_K/W_V/W_Q/W_O NULL (layer %d)", i);
@@ -399,6 +418,70 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
 
 template <typename T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>((char *)ws + off); }
 
+// LONGER-style encoding ([HyFormer] eq. (6), (8)): workspace of the pre-pass
+// that turns every layer's raw history into its short rows H_l.  The forward
+// proper then runs over the short rows (a batch whose history is the short
+// sequences and whose "table" is the stack of H_l), after this area.
+struct LongerLayout {
+  int64_t nS = 0;             // host bound on the short rows: min(n_hist, B * l_short)
+  int64_t mb = 0, mc = 0;     // raw history: max 32-key blocks, chunks
+  int nb = 4;
+  size_t plan = 0, soff = 0, sids = 0, iota = 0, prep = 0, kv = 0, kvl = 0;
+  size_t ml = 0, acc = 0, cnt = 0, qe = 0, a32 = 0, alo = 0, htab = 0, total = 0;
+};
+
+LongerLayout make_longer_layout(const stca_config *c, const stca_batch *b) {
+  LongerLayout LL;
+  const int64_t d = c->d;
+  LL.nS = std::min<int64_t>(b->n_hist, (int64_t)c->B * c->l_short);
+  LL.nb = choose_nb(c->chunk_keys);
+  LL.mb = max_blocks(b->n_hist, c->B, 1);
+  LL.mc = max_chunks(b->n_hist, c->B, LL.nb);
+  const size_t rows = (size_t)std::max<int64_t>(LL.nS, 1);
+  Carver cv;
+  LL.plan = cv.take(4 * sizeof(int) * (size_t)(c->B + 1));
+  LL.soff = cv.take(sizeof(int) * (size_t)(c->B + 1));
+  LL.sids = cv.take(sizeof(int) * rows);
+  LL.iota = cv.take(sizeof(int) * rows);
+  LL.prep = cv.take((size_t)c->M * 4 * d * d * 2);  // per layer: W'_Q, W'_K | W'_V, W'_O (packed bf16)
+  LL.kvl = (size_t)LL.mb * 32 * d * 2;
+  LL.kv = cv.take(2 * LL.kvl);
+  const size_t np = partial_slots(LL.mc, c->H, c->l_short);
+  LL.ml = cv.take(np * 2 * sizeof(float));
+  LL.acc = cv.take(np * (d / c->H) * sizeof(float));
+  LL.cnt = cv.take(np * sizeof(int));
+  LL.qe = cv.take(rows * d * 2);
+  LL.a32 = cv.take(rows * d * 4);
+  LL.alo = cv.take(rows * d * 2);
+  LL.htab = cv.take((size_t)c->M * rows * d * 2);
+  LL.total = cv.off;
+  return LL;
+}
+
+// What the forward over the short rows needs of the caller's batch.
+struct LongerInner {
+  const stca_batch *raw;   // the caller's batch (raw history, targets, table)
+  Plan raw_plan;           // offsets of the raw history (HyFormer mean pool)
+  int64_t raw_table_rows;  // rows of the caller's table
+  int64_t layer_rows;      // short rows per layer in the stacked table
+};
+
+// The configuration and batch of the forward over the short rows.  Pointers
+// into `ws` (which may be NULL when only sizes are wanted).
+void longer_inner(const stca_config *c, const stca_batch *b, const LongerLayout &LL, void *ws,
+                  stca_config &c2, stca_batch &b2) {
+  c2 = *c;
+  c2.encoder = STCA_ENC_SWIGLU;
+  c2.flags &= ~STCA_FLAG_KV_LN;
+  c2.table_rows = std::max<int64_t>(LL.nS, 1);
+  b2 = *b;
+  b2.hist_offsets = at<int>(ws, LL.soff);
+  b2.hist_ids = at<int>(ws, LL.iota);
+  b2.n_hist = LL.nS;
+  b2.table = at<void>(ws, LL.htab);
+  b2.key_mask = nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,6 +507,14 @@ int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t 
   int r = validate_cfg(cfg);
   if (r) return r;
   if ((r = validate_batch(cfg, batch))) return r;
+  if (cfg->encoder == STCA_ENC_LONGER) {
+    const LongerLayout LL = make_longer_layout(cfg, batch);
+    stca_config c2;
+    stca_batch b2;
+    longer_inner(cfg, batch, LL, nullptr, c2, b2);
+    *bytes = LL.total + make_layout(&c2, &b2).total;
+    return STCA_OK;
+  }
   *bytes = make_layout(cfg, batch).total;
   return STCA_OK;
 }
@@ -431,6 +522,11 @@ int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t 
 }  // extern "C"
 
 namespace stca {
+
+int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const stca_outputs *out,
+                 void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi, const LongerInner *li);
+int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const stca_outputs *out,
+                   void *ws, size_t ws_bytes, void *stream);
 
 int forward_check(const stca_config *cfg, const stca_batch *batch, const stca_weights *w) {
   int r = validate_cfg(cfg);
@@ -462,6 +558,21 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     return fail(STCA_ERR_UNSUPPORTED, "x_dump is not available with STCA_FLAG_DEDUP (the encoder gathers unique rows)");
   if (cfg->path == STCA_PATH_FUSED && out->kv_dump)
     return fail(STCA_ERR_UNSUPPORTED, "kv_dump needs the staged path (the fused path keeps no K/V)");
+  if (cfg->encoder == STCA_ENC_LONGER) {
+    if (fi) return fail(STCA_ERR_UNSUPPORTED, "the backward of STCA_ENC_LONGER is not available");
+    if (out->x_dump || out->kv_dump)
+      return fail(STCA_ERR_UNSUPPORTED, "x_dump / kv_dump are not available with STCA_ENC_LONGER");
+    return longer_forward(cfg, batch, w, out, ws, ws_bytes, stream);
+  }
+  return forward_body(cfg, batch, w, out, ws, ws_bytes, stream, fi, nullptr);
+}
+
+// The forward after validation.  li != NULL: the history of `batch` is the
+// short rows of a LONGER-style encoding (its table the stacked H_l, one block
+// of rows per layer, already encoded); target-side gathers and the HyFormer
+// mean pool read the caller's raw table and history through li.
+int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const stca_outputs *out,
+                 void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi, const LongerInner *li) {
   const Layout L = make_layout(cfg, batch);
   if (!ws && L.total > 0) return fail(STCA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
   if (ws_bytes < L.total)
@@ -491,7 +602,7 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
   plan.coff = plan.pblk + (B + 1);
   plan.prow = L.prow ? at<int>(ws, L.prow) : nullptr;
 
-  if ((e = rec(0))) return hip_fail(e, "stage event");
+  if (!li && (e = rec(0))) return hip_fail(e, "stage event");
   // ---- 1. weight preparation (bf16): fragment-packed W^T into the workspace
   bf16_t *prep = bf ? at<bf16_t>(ws, L.prep) : nullptr;
   if (bf) {
@@ -513,10 +624,12 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
       const PrepLayer &p = L.pl[i];
       // the d = 256 history encoders (staged and fused) read W1 / W3 as 16-row tiles
       const int f13 = d == 256 ? 1 : 0;
-      if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
-      if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
-      if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
-      if (d == 256) {  // the d = 256 encoders read W_K and W_V block-interleaved
+      if (!li) {  // short rows are encoded already: no history FFN
+        if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
+        if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
+        if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
+      }
+      if (d == 256 && !li) {  // the d = 256 encoders read W_K and W_V block-interleaved
         if ((e = add(l.wk, d, d, p.wkv, 0, 4))) break;
         if ((e = add(l.wv, d, d, p.wkv, 0, 5))) break;
       } else {
@@ -546,7 +659,8 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
 
   // ---- 2. planner
   if (B > 0) {
-    e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, batch->n_hist, T,
+    // short rows: n_hist is only a bound on the device-side total
+    e = launch_plan(batch->hist_offsets, batch->tgt_offsets, B, li ? -1 : batch->n_hist, T,
                     batch->max_tgt_per_user, L.nb, L.tile_blocks, plan, out->dev_status, s);
     if (e) return hip_fail(e, "planner");
     if (plan.prow) {
@@ -563,8 +677,8 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     std::memset(&a, 0, sizeof(a));
     a.d = d;
     a.hidden = cfg->hidden;
-    a.table = batch->table;
-    a.table_rows = cfg->table_rows;
+    a.table = li ? li->raw->table : batch->table;
+    a.table_rows = li ? li->raw_table_rows : cfg->table_rows;
     a.plan = plan;
     a.B = B;
     a.H = H;
@@ -580,9 +694,13 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
     ChainArgs a = base_args();
     a.in_mode = IN_GATHER_CSR;
     a.out_mode = L.fused ? OUT_FUSED : OUT_KV;
-    a.ffn = true;
-    a.ln = kvln;
+    a.ffn = !li;
+    a.ln = kvln && !li;
     a.proj = true;
+    if (li) {  // layer i's block of short rows
+      a.table = (const char *)batch->table + (size_t)i * li->layer_rows * d * L.esize;
+      a.table_rows = li->layer_rows;
+    }
     a.n_rows = L.max_blocks * 32;
     a.ids = batch->hist_ids;
     a.in_dump = i == 0 ? out->x_dump : nullptr;
@@ -747,7 +865,7 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
   };
 
   // bf16, d <= 256: all layers in one launch that gathers each tile once
-  const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers;
+  const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers && !li;
   if (multi) {
     ChainArgs a = enc_args(0);
     HistLayers hl;
@@ -841,8 +959,12 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
   };
   if (hyf) {  // q_u,n = FFN_n([F_u | MeanPool(rows of u)])
     float *mp = at<float>(ws, L.hy_mp), *gi = at<float>(ws, L.hy_g);
-    e = launch_mean_pool((const bf16_t *)batch->table, cfg->table_rows, batch->hist_ids, plan, B, d, mp,
-                         at<float>(ws, L.hy_pool), s);
+    if (li)  // MeanPool over the raw history, not the short rows
+      e = launch_mean_pool((const bf16_t *)li->raw->table, li->raw_table_rows, li->raw->hist_ids, li->raw_plan, B, d,
+                           mp, at<float>(ws, L.hy_pool), s);
+    else
+      e = launch_mean_pool((const bf16_t *)batch->table, cfg->table_rows, batch->hist_ids, plan, B, d, mp,
+                           at<float>(ws, L.hy_pool), s);
     if (!e) e = launch_global_info((const bf16_t *)batch->ns_feats, mp, B, cfg->n_ns, d, gi, s);
     const int64_t din = (int64_t)(cfg->n_ns + 1) * d;
     if (!e) e = ffn_stack(hm, gi, din, 0, w->qgen_w1, w->qgen_w3, w->qgen_w2);
@@ -995,6 +1117,169 @@ int forward_with_internals(const stca_config *cfg, const stca_batch *batch, cons
   }
   if ((e = rec(2 + 5 * M))) return hip_fail(e, "stage event");
   return STCA_OK;
+}
+
+// LONGER-style encoding ([HyFormer] §3.4.1, eq. (6) then (8)).  Per layer l:
+//   H_l = CrossAttn(S_short, S, S) = softmax_h((S_short W'_Q)(S W'_K)^T / sqrt(d_h)) (S W'_V) W'_O,
+// S the user's raw rows, S_short the last min(L_u, l_short) of them; the
+// layer's K/V are then H_l W_K, H_l W_V.  The pre-pass reuses the row chain
+// (projections without FFN) and the split-L attention with the short rows as
+// its targets, and writes every layer's H_l into a stacked table; the forward
+// then runs over the short rows as its history.
+int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const stca_outputs *out,
+                   void *ws, size_t ws_bytes, void *stream) {
+  const LongerLayout LL = make_longer_layout(cfg, batch);
+  stca_config c2;
+  stca_batch b2;
+  longer_inner(cfg, batch, LL, ws, c2, b2);
+  const size_t inner = make_layout(&c2, &b2).total;
+  if (!ws) return fail(STCA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", LL.total + inner);
+  if (ws_bytes < LL.total + inner)
+    return fail(STCA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, LL.total + inner);
+  if (!aligned16(ws)) return fail(STCA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  if (out->n_stage_events < 0 || (out->n_stage_events > 0 && !out->stage_events))
+    return fail(STCA_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int B = cfg->B, d = cfg->d, H = cfg->H, M = cfg->M;
+  hipError_t e = hipSuccess;
+  if (out->n_stage_events > 0 && out->stage_events[0] &&
+      (e = hipEventRecord(reinterpret_cast<hipEvent_t>(out->stage_events[0]), s)))
+    return hip_fail(e, "stage event");
+
+  // encoder weights, packed as the row chain reads them: W'_Q, W'_K | W'_V, W'_O
+  bf16_t *prep = at<bf16_t>(ws, LL.prep);
+  const size_t dd = (size_t)d * d;
+  {
+    PackBatch pb;
+    int n = 0;
+    for (int i = 0; i < M && !e; ++i) {
+      const stca_layer &l = w->layers[i];
+      bf16_t *base = prep + (size_t)i * 4 * dd;
+      const PackDesc ds[4] = {{(const bf16_t *)l.enc_wq, base, d, d, 0, 0},
+                              {(const bf16_t *)l.enc_wk, base + dd, d, d, 0, 0},
+                              {(const bf16_t *)l.enc_wv, base + dd, d, d, d / 32, 0},
+                              {(const bf16_t *)l.enc_wo, base + 3 * dd, d, d, 0, 0}};
+      for (const PackDesc &pd : ds) {
+        pb.m[n++] = pd;
+        if (n == kMaxPacks) {
+          e = launch_pack_batch(pb, n, s);
+          n = 0;
+          if (e) break;
+        }
+      }
+    }
+    if (!e && n) e = launch_pack_batch(pb, n, s);
+    if (e) return hip_fail(e, "encoder weight preparation");
+  }
+
+  // short sequences and the raw plan (the short rows are the raw history's targets)
+  Plan P;
+  P.hoff = at<int>(ws, LL.plan);
+  P.toff = P.hoff + (B + 1);
+  P.pblk = P.toff + (B + 1);
+  P.coff = P.pblk + (B + 1);
+  P.prow = nullptr;
+  int *soff = at<int>(ws, LL.soff), *sids = at<int>(ws, LL.sids);
+  const int64_t rows = std::max<int64_t>(LL.nS, 1);
+  if (B > 0) {
+    e = launch_short_seq(batch->hist_offsets, batch->hist_ids, B, batch->n_hist, cfg->l_short, rows, soff, sids,
+                         at<int>(ws, LL.iota), s);
+    if (!e) e = launch_plan(batch->hist_offsets, soff, B, batch->n_hist, -1, cfg->l_short, LL.nb, 1, P,
+                            out->dev_status, s);
+    if (e) return hip_fail(e, "short sequences");
+  }
+
+  if (B > 0 && batch->n_hist > 0) {
+    const int dh = d / H;
+    void *kb = at<void>(ws, LL.kv), *vb = at<char>(ws, LL.kv) + LL.kvl;
+    for (int i = 0; i < M; ++i) {
+      const bf16_t *base = prep + (size_t)i * 4 * dd;
+      ChainArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.d = d;
+      a.hidden = cfg->hidden;
+      a.table = batch->table;
+      a.table_rows = cfg->table_rows;
+      a.plan = P;
+      a.B = B;
+      a.H = H;
+      a.scale = 1.0f;
+      a.status = out->dev_status;
+      a.proj = true;
+      {  // S W'_K, S W'_V over the raw rows -> blocked K/V
+        ChainArgs k = a;
+        k.in_mode = IN_GATHER_CSR;
+        k.out_mode = OUT_KV;
+        k.n_rows = LL.mb * 32;
+        k.ids = batch->hist_ids;
+        k.wp = base + dd;
+        k.pn = 2 * d;
+        k.kbuf = kb;
+        k.vbuf = vb;
+        if ((e = launch_chain_bf16(k, s))) return hip_fail(e, "encoder K/V");
+      }
+      bf16_t *qe = at<bf16_t>(ws, LL.qe);
+      {  // S_short W'_Q / sqrt(d_h)
+        ChainArgs q = a;
+        q.in_mode = IN_GATHER_IDS;
+        q.out_mode = OUT_ROWS;
+        q.n_rows = rows;
+        q.ids = sids;
+        q.wp = base;
+        q.pn = d;
+        q.scale = 1.0f / std::sqrt((float)dh);
+        q.out = qe;
+        q.ldo = d;
+        if ((e = launch_chain_bf16(q, s))) return hip_fail(e, "encoder queries");
+      }
+      {  // per-head softmax attention of each short row over the user's raw rows
+        AttnArgs at_;
+        std::memset(&at_, 0, sizeof(at_));
+        at_.dtype = STCA_BF16;
+        at_.score = STCA_SCORE_SOFTMAX;
+        at_.d = d;
+        at_.H = H;
+        at_.dh = dh;
+        at_.nb = LL.nb;
+        at_.max_tgt = cfg->l_short;
+        attn_shape(at_, LL.mc);
+        at_.tile_blocks = 1;
+        at_.plan = P;
+        at_.q = qe;
+        at_.n_tgt = rows;
+        at_.kbuf = kb;
+        at_.vbuf = vb;
+        at_.part_ml = at<float>(ws, LL.ml);
+        at_.part_acc = at<float>(ws, LL.acc);
+        at_.part_cnt = at<int>(ws, LL.cnt);
+        at_.attn = at<float>(ws, LL.a32);
+        at_.attn_lo = at<void>(ws, LL.alo);
+        at_.B = B;
+        if ((e = launch_attention(at_, s))) return hip_fail(e, "encoder attention");
+      }
+      {  // H_l = attn W'_O -> layer i's block of the stacked table
+        ChainArgs o = a;
+        o.in_mode = IN_DENSE;
+        o.out_mode = OUT_ROWS;
+        o.n_rows = rows;
+        o.a = at<void>(ws, LL.alo);
+        o.lda = d;
+        o.wp = base + 3 * dd;
+        o.pn = d;
+        o.out = at<bf16_t>(ws, LL.htab) + (size_t)i * rows * d;
+        o.ldo = d;
+        if ((e = launch_chain_bf16(o, s))) return hip_fail(e, "encoder output projection");
+      }
+    }
+  }
+
+  LongerInner li;
+  li.raw = batch;
+  li.raw_plan = P;
+  li.raw_table_rows = cfg->table_rows;
+  li.layer_rows = rows;
+  return forward_body(&c2, &b2, w, out, (char *)ws + LL.total, ws_bytes - LL.total, stream, nullptr, &li);
 }
 
 }  // namespace stca

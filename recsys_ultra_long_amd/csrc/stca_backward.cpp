@@ -176,6 +176,8 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
   if (!b) return api_error(STCA_ERR_INVALID_ARG, "batch is NULL");
   if (c->dtype != STCA_BF16) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward is bf16 only");
   if (c->qmode != STCA_Q_FUSION) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs STCA_Q_FUSION");
+  if (c->encoder != STCA_ENC_SWIGLU)
+    return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs the SwiGLU history encoder");
   if (c->head_map || b->key_mask)
     return api_error(STCA_ERR_UNSUPPORTED, "stca_backward does not take Cross-Mask key_mask / head_map");
   if (c->H <= 0 || c->d % c->H) return api_error(STCA_ERR_INVALID_ARG, "d %% H != 0");
@@ -218,6 +220,8 @@ int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch
   api_clear_error();
   if (!bytes) return api_error(STCA_ERR_INVALID_ARG, "bytes is NULL");
   if (!cfg || !batch) return api_error(STCA_ERR_INVALID_ARG, "config or batch is NULL");
+  if (cfg->encoder != STCA_ENC_SWIGLU)
+    return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs the SwiGLU history encoder");
   BwdLayout L;
   int r = make_layout(cfg, batch, L);
   if (r) return r;

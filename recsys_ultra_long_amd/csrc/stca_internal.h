@@ -41,8 +41,15 @@ inline int64_t prow_rows(int64_t max_blocks) { return (max_blocks + 4) * 32; }
 hipError_t launch_padded_ids(const Plan &plan, int B, const int *hist_ids, int64_t table_rows,
                              int64_t max_blocks, int *status, hipStream_t s);
 
+// LONGER-style encoding: short_off [B+1] of the users' last min(L_u, l_short)
+// items, their table ids (short_ids, padded with 0 up to `bound`) and the
+// identity map iota [bound].  bound >= the device total.
+hipError_t launch_short_seq(const int *hist_off, const int *hist_ids, int B, int64_t n_hist, int l_short,
+                            int64_t bound, int *short_off, int *short_ids, int *iota, hipStream_t s);
+
 // align: every user is padded to a multiple of `align` 32-key blocks (2 on
-// the fused path, whose tiles hold 64 keys).
+// the fused path, whose tiles hold 64 keys).  n_hist / n_tgt < 0: the host
+// holds only a bound, and the offsets' totals are not checked against it.
 hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n_hist,
                        int64_t n_tgt, int max_tgt, int nb, int align, Plan plan, int *status,
                        hipStream_t s);

@@ -22,6 +22,7 @@ F32, BF16 = 0, 1
 SCORE = {"softmax": 0, "relu": 1}
 QMODE = {"fusion": 0, "linear": 1, "hyformer": 2}
 PATH = {"staged": 0, "fused": 1}
+ENCODER = {"swiglu": 0, "longer": 1}
 FLAG_KV_LN, FLAG_Z_LN, FLAG_DEDUP = 1, 2, 4
 DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 
@@ -38,7 +39,8 @@ class Config(C.Structure):
                 ("M", C.c_int32), ("table_rows", C.c_int64), ("dtype", C.c_int32),
                 ("score", C.c_int32), ("qmode", C.c_int32), ("path", C.c_int32),
                 ("flags", C.c_int32), ("chunk_keys", C.c_int32), ("n_ns", C.c_int32),
-                ("q_hidden", C.c_int32), ("head_map", C.POINTER(C.c_int32))]
+                ("q_hidden", C.c_int32), ("head_map", C.POINTER(C.c_int32)), ("encoder", C.c_int32),
+                ("l_short", C.c_int32)]
 
 
 class Batch(C.Structure):
@@ -53,7 +55,8 @@ class Ffn(C.Structure):
 
 class Layer(C.Structure):
     _fields_ = [("kv", Ffn), ("q", Ffn), ("wk", _vp), ("wv", _vp), ("wq", _vp), ("wo", _vp),
-                ("wc", _vp), ("r", _vp), ("boost_w1", _vp), ("boost_w3", _vp), ("boost_w2", _vp)]
+                ("wc", _vp), ("r", _vp), ("boost_w1", _vp), ("boost_w3", _vp), ("boost_w2", _vp),
+                ("enc_wq", _vp), ("enc_wk", _vp), ("enc_wv", _vp), ("enc_wo", _vp)]
 
 
 class Weights(C.Structure):
@@ -194,7 +197,8 @@ def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=Fals
     cfg = Config(B=sp.B, d=sp.d, H=sp.H, hidden=sp.hidden, M=sp.M, table_rows=sp.table_rows,
                  dtype=BF16 if sp.dtype == "bf16" else F32, score=SCORE[sp.score],
                  qmode=QMODE[sp.qmode], path=PATH[path], flags=flags, chunk_keys=chunk_keys,
-                 n_ns=sp.n_ns, q_hidden=(sp.hy_hidden or sp.d) if sp.qmode == "hyformer" else 0)
+                 n_ns=sp.n_ns, q_hidden=(sp.hy_hidden or sp.d) if sp.qmode == "hyformer" else 0,
+                 encoder=ENCODER[getattr(sp, "encoder", "swiglu")], l_short=getattr(sp, "l_short", 0))
 
     def conv(w):
         if w is None:
@@ -229,9 +233,11 @@ def _structs(dp: DeviceProblem):
     layers = (Layer * len(dp.layers))()
     for i, l in enumerate(dp.layers):
         bo = l.get("boost") or {}
+        en = l.get("enc") or {}
         layers[i] = Layer(_ffn(l["kv"]), _ffn(l.get("q")), _ptr(l["wk"]), _ptr(l["wv"]),
                           _ptr(l["wq"]), _ptr(l["wo"]), _ptr(l.get("wc")), _ptr(l.get("r")),
-                          _ptr(bo.get("w1")), _ptr(bo.get("w3")), _ptr(bo.get("w2")))
+                          _ptr(bo.get("w1")), _ptr(bo.get("w3")), _ptr(bo.get("w2")),
+                          _ptr(en.get("wq")), _ptr(en.get("wk")), _ptr(en.get("wv")), _ptr(en.get("wo")))
     qg = dp.qgen or {}
     w = Weights(layers, _ffn(dp.z), _ptr(dp.wz), _ptr(qg.get("w1")), _ptr(qg.get("w3")), _ptr(qg.get("w2")))
     b = Batch(_ptr(dp.hist_offsets), _ptr(dp.hist_ids), _ptr(dp.tgt_offsets), _ptr(dp.tgt_ids),

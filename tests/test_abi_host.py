@@ -338,3 +338,46 @@ def test_clock_ghz():
     # row with no elapsed ticks (workgroup that did not exist) is ignored
     c = [[10, 1000, 10 + 2_300_000, 1000 + 100_000], [0, 0, 0, 0]]
     assert abs(stca.clock_ghz(c) - 2.3) < 1e-12
+
+
+# ------------------------------------------------------- LONGER-style encoding
+@pytest.mark.parametrize("over,bover,code", [
+    (dict(encoder=1, l_short=256), {}, stca.OK),
+    (dict(encoder=1, l_short=256, flags=0), {}, stca.OK),
+    (dict(encoder=2), {}, stca.ERR_INVALID_ARG),
+    (dict(encoder=1, l_short=0), {}, stca.ERR_INVALID_ARG),
+    (dict(encoder=1, l_short=4097), {}, stca.ERR_INVALID_ARG),
+    (dict(encoder=1, l_short=64, path=1), {}, stca.ERR_UNSUPPORTED),
+    (dict(encoder=1, l_short=64, dtype=stca.F32), {}, stca.ERR_UNSUPPORTED),
+    (dict(encoder=1, l_short=64, score=1), {}, stca.ERR_UNSUPPORTED),
+    (dict(encoder=1, l_short=64, flags=stca.FLAG_DEDUP), {}, stca.ERR_UNSUPPORTED),
+    (dict(encoder=1, l_short=64), dict(key_mask=FAKE), stca.ERR_UNSUPPORTED),
+])
+def test_longer_validation(over, bover, code):
+    r, n = ws_size(cfg(**over), batch(**bover))
+    assert r == code, stca.last_error()
+    if code == stca.OK:
+        assert n > 0
+
+
+def test_longer_workspace_and_rejections():
+    lib = stca.load()
+    b = batch(n_hist=100_000, n_tgt=64, max_tgt_per_user=32)
+    _, plain = ws_size(cfg(), b)
+    _, lo = ws_size(cfg(encoder=1, l_short=256), b)
+    # the raw K/V of one layer at a time, and every layer's B x l_short short rows
+    assert lo > 2 * 100_000 * 256 * 2 + 4 * 2 * 256 * 256 * 2
+    _, lo_small = ws_size(cfg(encoder=1, l_short=16), b)
+    assert lo_small < lo
+    c = cfg(encoder=1, l_short=256)
+    w, keep = _weights()
+    assert _forward(c, b, w, stca.Outputs(z=FAKE), lo) == stca.ERR_INVALID_ARG  # no encoder weights
+    assert "encoder weight" in stca.last_error()
+    for i in range(c.M):
+        keep[i].enc_wq = keep[i].enc_wk = keep[i].enc_wv = keep[i].enc_wo = FAKE
+    for f in ("x_dump", "kv_dump"):
+        assert _forward(c, b, w, stca.Outputs(z=FAKE, **{f: FAKE}), lo) == stca.ERR_UNSUPPORTED
+    assert _forward(c, b, w, stca.Outputs(z=FAKE), lo - 1) == stca.ERR_WORKSPACE
+    n = C.c_size_t(0)
+    assert lib.stca_backward_workspace_size(C.byref(c), C.byref(b), C.byref(n)) == stca.ERR_UNSUPPORTED
+    assert "SwiGLU" in stca.last_error()
