@@ -85,6 +85,12 @@ def attach_measured_peaks(res, skip=False):
 
 def workload(name):
     from recsys_ultra_long_amd import inputs as I
+    if name.endswith("-longer"):
+        # the same workload with the LONGER-style sequence encoding: each
+        # layer's history is the cross attention of the last 256 items over
+        # all of them (the pages fix no short length; 256 << 8192)
+        from dataclasses import replace
+        return replace(workload(name[:-len("-longer")]), encoder="longer", l_short=256)
     if name == "rlb-long":
         return I.spec(3)
     if name == "single-target":
@@ -112,7 +118,7 @@ def cpu_baseline(p, seconds):
     sp = p.spec
     layers, z, wz = O.weights_f64(p.layers, p.z, p.wz)
     cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode, kv_ln=sp.kv_ln,
-               z_ln=sp.z_ln)
+               z_ln=sp.z_ln, encoder=sp.encoder, l_short=sp.l_short)
     rows = lambda ids: O.stored_to_f64(p.rows(ids))
     t0 = time.perf_counter()
     users, toks, tgts = 0, 0, 0
@@ -358,7 +364,8 @@ def main():
     torch.cuda.synchronize()
     log("uploaded")
     M = sp.M
-    nev = stca.n_stage_events(M)
+    longer = sp.encoder == "longer"
+    nev = stca.n_stage_events(M, longer)
     evs = [stca.StageEvents(nev) for _ in range(args.steps)]
     f = stca.Forward(dp, want=(), dumps=())
     for _ in range(args.warmup):
@@ -400,12 +407,17 @@ def main():
 
     d, h, H = sp.d, sp.hidden, sp.H
     n_hist, T = p.n_hist, p.n_tgt
-    enc_rows = n_unique if args.dedup else n_hist              # rows the encoder processes
-    flops_hist = enc_rows * (6 * d * h + 4 * d * d)           # per layer
+    lens = np.diff(p.hist_offsets).astype(np.int64)
+    # LONGER: the layers decode over each user's min(L_u, l_short) encoded rows
+    dec_lens = np.minimum(lens, sp.l_short) if longer else lens
+    n_dec = int(dec_lens.sum())
+    enc_rows = n_unique if args.dedup else n_dec              # rows the history chain processes
+    row_flops = 4 * d * d if longer else 6 * d * h + 4 * d * d
+    flops_hist = enc_rows * row_flops                         # per layer
     # attention flops: 4 d per (history token, target of the same user) pair
-    pairs = int(np.sum(np.diff(p.hist_offsets).astype(np.int64) * np.diff(p.tgt_offsets)))
+    pairs = int(np.sum(dec_lens * np.diff(p.tgt_offsets)))
     flops_attn = 4 * d * pairs
-    bytes_attn = n_hist * 4 * d + T * 2 * d                  # K,V bf16 read once + Q
+    bytes_attn = n_dec * 4 * d + T * 2 * d                   # K,V bf16 read once + Q
     # bf16 at d <= 256 encodes every layer's history in one launch (its
     # duration lands in the first history stage): per-layer figures use
     # the total over layers
@@ -415,21 +427,52 @@ def main():
     t_attn = float(np.mean(part)) * 1e-3
     hist_tf = flops_hist / t_hist / 1e12
     attn_gbs = bytes_attn / t_attn / 1e9
-    roof_hist = {"kernel": "history chain (gather+SwiGLU+LN+W_K|W_V)", "bound": "mfma",
+    roof_hist = {"kernel": "history chain (gather+W_K|W_V of the encoded short rows)" if longer
+                 else "history chain (gather+SwiGLU+LN+W_K|W_V)", "bound": "mfma",
                  "achieved": round(hist_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(hist_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                  "launch_ms": round(t_hist * hist_layers_per_launch * 1e3, 4),
                  "per_launch": f"{enc_rows} {'unique rows' if args.dedup else 'tokens'} x "
-                               f"{hist_layers_per_launch} layer(s) x {6 * d * h + 4 * d * d} flop"}
+                               f"{hist_layers_per_launch} layer(s) x {row_flops} flop"}
     roof_attn = {"kernel": "m-target cross attention (split-L partials)", "bound": "hbm",
                  "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                  "launch_ms": round(t_attn * 1e3, 4),
-                 "per_launch": f"{n_hist} tokens x {4 * d} B + {T} targets x {2 * d} B"}
+                 "per_launch": f"{n_dec} tokens x {4 * d} B + {T} targets x {2 * d} B"}
     # HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     # was taken on the current kernel sources
     from recsys_ultra_long_amd import profiling
     roofs = {"history": roof_hist, "attention": roof_attn}
+    times = {"history": float(np.sum(hist)), "attention": float(np.sum(part))}
+    enc_stages = {}
+    if longer:
+        # the encoding pre-pass, per layer: S W'_K | S W'_V over the raw rows,
+        # S_short W'_Q, the short rows' attention over the raw rows, W'_O
+        e0 = 3 + 5 * M
+        enc_kv = [stage(e0 + 4 * i, e0 + 1 + 4 * i) for i in range(M)]
+        enc_q = [stage(e0 + 1 + 4 * i, e0 + 2 + 4 * i) for i in range(M)]
+        enc_at = [stage(e0 + 2 + 4 * i, e0 + 3 + 4 * i) for i in range(M)]
+        enc_wo = [stage(e0 + 3 + 4 * i, e0 + 4 + 4 * i) for i in range(M)]
+        enc_stages = {"enc_setup": round(stage(0, e0), 4), "enc_kv": [round(x, 4) for x in enc_kv],
+                      "enc_q": [round(x, 4) for x in enc_q], "enc_attention": [round(x, 4) for x in enc_at],
+                      "enc_wo": [round(x, 4) for x in enc_wo], "prep_plan": round(stage(e0 + 4 * M, 1), 4)}
+        t_ekv = float(np.mean(enc_kv)) * 1e-3
+        ekv_tf = n_hist * 4 * d * d / t_ekv / 1e12
+        roofs["encoder_kv"] = {"kernel": "encoder chain (gather+W'_K|W'_V, raw rows)", "bound": "mfma",
+                               "achieved": round(ekv_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(ekv_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                               "launch_ms": round(t_ekv * 1e3, 4),
+                               "per_launch": f"{n_hist} tokens x {4 * d * d} flop"}
+        pairs_enc = int(np.sum(dec_lens * lens))
+        t_eat = float(np.mean(enc_at)) * 1e-3
+        eat_tf = 4 * d * pairs_enc / t_eat / 1e12
+        roofs["encoder_attention"] = {
+            "kernel": "encoder attention (short rows over raw rows, partials + merge)", "bound": "mfma",
+            "achieved": round(eat_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(eat_tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "launch_ms": round(t_eat * 1e3, 4),
+            "per_launch": f"{pairs_enc} (short row, raw row) pairs x {4 * d} flop"}
+        times["encoder_kv"] = float(np.sum(enc_kv))
+        times["encoder_attention"] = float(np.sum(enc_at))
     if args.path == "fused":
         # one kernel per layer: gather, history FFN + LN, W_K | W_V and the
         # attention; K/V never leave the chip, so it is bound by the MFMA
@@ -460,7 +503,7 @@ def main():
     if args.path == "fused":
         dominant = roofs["fused"]
     else:
-        dominant = roof_hist if sum(hist) >= sum(part) else roof_attn
+        dominant = roofs[max(times, key=times.get)]
 
     value = n_hist * M / (ms * 1e-3)
     res = {
@@ -478,7 +521,9 @@ def main():
                                   "share the map of head 2k" if args.cross_mask else "")
                                + (f", HyFormer queries: {sp.n_ns} non-sequence tokens, query FFN hidden "
                                   f"{sp.hy_hidden or d}, no history LN" if sp.qmode == "hyformer" else "")
-                               + (f", unique-id dedup ({n_unique} unique of {n_hist})" if args.dedup else ""),
+                               + (f", unique-id dedup ({n_unique} unique of {n_hist})" if args.dedup else "")
+                               + (f", LONGER-style encoding: each layer's history is the cross attention of the "
+                                  f"last {sp.l_short} items over all items" if longer else ""),
                    "global_batch": sp.B, "seq_len": sp.L, "targets": T, "parallelism": "single GPU"},
         "target_scores_per_s_per_layer": round(T * M / (ms * 1e-3), 1),
         "target_scores_per_s": round(T / (ms * 1e-3), 1),
@@ -486,6 +531,8 @@ def main():
         "roofline": dominant,
         **({"roofline_attention": roof_attn, "roofline_history": roof_hist}
            if args.path == "staged" else {}),
+        **({"roofline_encoder_kv": roofs["encoder_kv"], "roofline_encoder_attention": roofs["encoder_attention"],
+            "encoder_stages_ms": enc_stages} if longer else {}),
         "stages_ms": {"prep_plan": round(prep, 4),
                       **({"history": [round(x, 4) for x in hist]} if args.path == "staged" else {}),
                       "query": [round(x, 4) for x in query],
@@ -495,7 +542,7 @@ def main():
     }
     for e in evs:
         e.close()
-    if not args.no_other_path and not args.dedup:
+    if not args.no_other_path and not args.dedup and not longer:
         # the same inputs through the other path, and through the staged path
         # with unique-id dedup (bit-identical outputs, valid because a history
         # row here depends on its id alone)

@@ -218,7 +218,14 @@ typedef struct {
    *   3 + M + 4i   attention partials of layer i done
    *   4 + M + 4i   partial merge of layer i done
    *   5 + M + 4i   output projection (and next-query map) of layer i done
-   *   2 + 5M       final z done                     (5M + 3 events in all) */
+   *   2 + 5M       final z done                     (5M + 3 events in all)
+   * With STCA_ENC_LONGER the span 0..1 also holds the encoding pre-pass, whose
+   * boundaries follow (9M + 4 events in all):
+   *   3 + 5M       encoder weights packed, short sequences and raw plan built
+   *   4 + 5M + 4i  encoder K/V (S W'_K | S W'_V, raw rows) of layer i done
+   *   5 + 5M + 4i  encoder queries (S_short W'_Q) of layer i done
+   *   6 + 5M + 4i  encoder attention (partials and merge) of layer i done
+   *   7 + 5M + 4i  H_l = attention W'_O of layer i done */
   void *const *stage_events;
   int32_t n_stage_events;
   float *lse;          /* [M, n_tgt, H] optional, STCA_SCORE_SOFTMAX: log of each (target,

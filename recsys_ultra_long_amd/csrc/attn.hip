@@ -27,6 +27,7 @@
 //   V[b][h][d_h][key 0..31]   (transposed: a feature's 32 keys contiguous)
 // so every MFMA operand fragment is one 16-byte load.
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_block.h"
 #include "stca_internal.h"
@@ -56,6 +57,13 @@ DEV UnitPos decode_unit(const Plan &P, int B, int HG, int unit) {
 // Units per workgroup of the persistent grid.
 DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
 
+// Logical workgroup of hardware workgroup b.  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2); this order gives every
+// XCD a contiguous share of the logical ranges, so neighbouring ranges (the
+// target groups of one user and head, when a user has more than 64 targets)
+// read the same K/V through one L2.  Identity when n is not a multiple of 8.
+DEV int xcd_order(int b, int n) { return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3); }
+
 // ------------------------------------------------------------------ bf16 / MFMA
 // S^T = K Q^T (16 keys x 16 targets per MFMA), online softmax in registers,
 // O^T += V^T P^T (16 features x 16 targets per MFMA).  The key order inside a
@@ -76,7 +84,11 @@ DEV int units_per_wg(int total, int grid) { return (total + grid - 1) / grid; }
 // visibility word.  A head map (a.has_map) takes head h's scores from the
 // Q / K columns of head a.head_map[h] ([WeChat] §3.3.1: heads sharing one
 // attention map under different masks); V and the output stay head h's.
-template <int DH, int NT, int SCORE, bool IND, bool MASK>
+//
+// SHARE (more than one target group): K/V are read with the default cache
+// policy instead of the streaming one, so that the other groups' workgroups
+// find the lines in L2.
+template <int DH, int NT, int SCORE, bool IND, bool MASK, bool SHARE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
   constexpr int DT = DH / 16;  // feature tiles of the output
@@ -88,10 +100,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t sm_vt[IND ? 4 : 1][IND ? DH * LDT : 8];
 
   const Plan P = a.plan;
-  const int H = a.H, G = a.groups, HG = H * G;
+  const int H = a.H, G = a.groups, HG = SHARE ? H : H * G;  // pairs per user: heads, or (group, head)
   const int total = P.coff[a.B] * HG;
   const int per = units_per_wg(total, gridDim.x);
-  int unit = blockIdx.x * per;
+  int unit = xcd_order(blockIdx.x, gridDim.x) * per;
   const int unit_end = min(total, unit + per);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -103,10 +115,15 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   while (unit < unit_end) {
     const UnitPos pos = decode_unit(P, a.B, HG, unit);
     const int seg_end = min(unit_end, pos.first + pos.nc);
-    const int u = pos.u, grp = pos.pair / H, h = pos.pair % H;
+    // SHARE (at most 4 groups): wave w serves target group w over every
+    // block of the segment (waves past the user's groups have no targets);
+    // otherwise the four waves split the blocks of the workgroup's group
+    const int u = pos.u, grp = SHARE ? w : pos.pair / H, h = SHARE ? pos.pair : pos.pair % H;
     const int hq = a.has_map ? a.head_map[h] : h;  // the head whose Q / K give the scores
     const int tbase = P.toff[u];
     const int m_u = P.toff[u + 1] - tbase;
+    constexpr int BS = SHARE ? 1 : 4;  // block stride of a wave
+    const int bw = SHARE ? 0 : w;      // first block of a wave
     const int t0 = grp * TG;
     if (t0 < m_u) {
       const int L = P.hoff[u + 1] - P.hoff[u];
@@ -142,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if constexpr (IND) {
           const bf16_t *Vr = (const bf16_t *)a.vrows;
           Uids U;
-          if (b < b0 + w + 8) load_uids(b, U);  // pipeline start
+          if (b < b0 + bw + 2 * BS) load_uids(b, U);  // pipeline start
           else U = U8;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
@@ -164,12 +181,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         } else {
           const bf16_t *kb = Kb + ((int64_t)b * H + hq) * 32 * DH;
           const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
+          auto ldkv = [](const bf16_t *q) {
+            if constexpr (SHARE) return ld8(q);
+            else return ldnt8(q);
+          };
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kk[kt][k] = ldnt8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+            for (int k = 0; k < KS; ++k) kk[kt][k] = ldkv(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
 #pragma unroll
-          for (int t = 0; t < DT; ++t) vv[t] = ldnt8(vb + (t * 16 + c16) * 32 + g16 * 8);
+          for (int t = 0; t < DT; ++t) vv[t] = ldkv(vb + (t * 16 + c16) * 32 + g16 * 8);
         }
       };
       // IND: V row chunks -> transposed wave-private tile -> V^T fragments
@@ -202,24 +223,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       // two blocks of this wave in flight ahead of the one being used: the
       // loads, not the arithmetic, set the pace once the block step is lean
       bf16x8 k1[2][KS], v1[DT];
-      if (b0 + w < b1) {
-        load_kv(b0 + w, kf, vf);
-        if (MASK) mk = load_mask(b0 + w);
+      if (b0 + bw < b1) {
+        load_kv(b0 + bw, kf, vf);
+        if (MASK) mk = load_mask(b0 + bw);
       }
-      if (b0 + w + 4 < b1) {
-        load_kv(b0 + w + 4, k1, v1);
-        if (MASK) mk1 = load_mask(b0 + w + 4);
+      if (b0 + bw + BS < b1) {
+        load_kv(b0 + bw + BS, k1, v1);
+        if (MASK) mk1 = load_mask(b0 + bw + BS);
       }
-      if (IND && b0 + w + 8 < b1) load_uids(b0 + w + 8, U8);
-      for (int b = b0 + w; b < b1; b += 4) {
+      if (IND && b0 + bw + 2 * BS < b1) load_uids(b0 + bw + 2 * BS, U8);
+      // one block of this wave; FULL: every key of the block is visible
+      auto step = [&](const int b, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
         bf16x8 k2[2][KS], v2[DT];
         Uids U12;
         // uids first: waiting for them later does not wait for the rows below
-        if (IND && b + 12 < b1) load_uids(b + 12, U12);
+        if (IND && b + 3 * BS < b1) load_uids(b + 3 * BS, U12);
         uint32_t mk2 = 0;
-        if (b + 8 < b1) {
-          load_kv(b + 8, k2, v2);
-          if (MASK) mk2 = load_mask(b + 8);
+        if (b + 2 * BS < b1) {
+          load_kv(b + 2 * BS, k2, v2);
+          if (MASK) mk2 = load_mask(b + 2 * BS);
         }
         if (IND) U8 = U12;
         __builtin_amdgcn_sched_barrier(0);
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         v_fragments(vf, vuse);
         uint32_t kvis = 0xffffffffu;
         if (MASK) kvis = (uint32_t)__ballot((mk >> h) & 1u);  // lanes 0..31: keys 0..31
-        attn_block<DH, NT, SCORE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
+        attn_block<DH, NT, SCORE, FULL>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
         mk = mk1;
         mk1 = mk2;
 #pragma unroll
@@ -243,9 +266,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
           vf[t] = v1[t];
           v1[t] = v2[t];
         }
-      }
+      };
+      // the user's full blocks first, then its partial last block (and any
+      // padding); with Cross-Mask masks every block takes the masked step.
+      // Two loops over one pipeline: a branch per block would keep both
+      // bodies' registers live at once.
+      const int bfull = MASK ? b0 : min(b1, P.pblk[u] + L / 32);
+      int b = b0 + bw;
+      for (; b < bfull; b += BS) step(b, std::true_type{});
+      for (; b < b1; b += BS) step(b, std::false_type{});
 
-      // ---- merge the four waves in LDS, write this segment's partial
+      // ---- merge the four waves in LDS (SHARE: each wave alone), write
+      // this segment's partial
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const float l = st.l[n][0];  // already the whole block range's sum
@@ -262,32 +294,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = st.o[t][n][r];
       }
-      __syncthreads();
-      const int64_t pbase = (int64_t)unit * a.tgs;
-      for (int e = tid; e < TG * DH; e += 256) {
-        const int tl = e / DH, dh = e % DH;
-        if (t0 + tl >= m_u) continue;
-        if (SCORE == 0) {
-          const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
-          float acc = 0.f, l = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float f = ex2((sm_m[q][tl] - M) * kLog2e);
-            acc += sm_o[q][tl][dh] * f;
-            l += sm_l[q][tl] * f;
-          }
-          a.part_acc[(pbase + tl) * DH + dh] = acc;
+      if constexpr (SHARE) {  // one wave's partial: no other wave's LDS is read
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int64_t pw = ((int64_t)unit * G + grp) * a.tgs;
+        for (int e = lane; e < TG * DH; e += 64) {
+          const int tl = e / DH, dh = e % DH;
+          if (t0 + tl >= m_u) continue;
+          a.part_acc[(pw + tl) * DH + dh] = sm_o[w][tl][dh];
           if (dh == 0) {
-            a.part_ml[(pbase + tl) * 2] = M;
-            a.part_ml[(pbase + tl) * 2 + 1] = l;
+            if (SCORE == 0) {
+              a.part_ml[(pw + tl) * 2] = sm_m[w][tl];
+              a.part_ml[(pw + tl) * 2 + 1] = sm_l[w][tl];
+            } else {
+              a.part_cnt[pw + tl] = sm_c[w][tl];
+            }
           }
-        } else {
-          a.part_acc[(pbase + tl) * DH + dh] =
-              sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
-          if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
         }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the wave's LDS is reused by its next segment
+      } else {
+        __syncthreads();
+        const int64_t pbase = (int64_t)unit * a.tgs;
+        for (int e = tid; e < TG * DH; e += 256) {
+          const int tl = e / DH, dh = e % DH;
+          if (t0 + tl >= m_u) continue;
+          if (SCORE == 0) {
+            const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
+            float acc = 0.f, l = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float f = ex2((sm_m[q][tl] - M) * kLog2e);
+              acc += sm_o[q][tl][dh] * f;
+              l += sm_l[q][tl] * f;
+            }
+            a.part_acc[(pbase + tl) * DH + dh] = acc;
+            if (dh == 0) {
+              a.part_ml[(pbase + tl) * 2] = M;
+              a.part_ml[(pbase + tl) * 2 + 1] = l;
+            }
+          } else {
+            a.part_acc[(pbase + tl) * DH + dh] =
+                sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
+            if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
+          }
+        }
+        __syncthreads();  // LDS reused by the next segment
       }
-      __syncthreads();  // LDS reused by the next segment
     }
     unit = seg_end;
   }
@@ -406,12 +459,14 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       per = units_per_wg(P.pblk[a.B] / tb, a.grid);
     } else {
       nu = P.coff[u + 1] - P.coff[u];
-      first = P.coff[u] * HG + (grp * H + h) * nu;
-      per = units_per_wg(P.coff[a.B] * HG, a.grid);
+      const int hg = a.share ? H : HG;  // pairs per user of the partial kernel's units
+      first = P.coff[u] * hg + (a.share ? h : grp * H + h) * nu;
+      per = units_per_wg(P.coff[a.B] * hg, a.grid);
     }
     auto pidx = [&](int wg) -> int64_t {
       if (a.fused) return partial_index(wg + u, H, h, a.tgs, tg);
-      return (int64_t)max(first, wg * per) * a.tgs + tg;
+      const int64_t seg = max(first, wg * per);
+      return (a.share ? seg * G + grp : seg) * a.tgs + tg;
     };
     if (nu > 0) {
       const int w0 = first / per, w1 = (first + nu - 1) / per;
@@ -502,13 +557,22 @@ template <int DH, int SCORE, bool IND, bool MASK>
 hipError_t launch_bf16(AttnArgs &a, hipStream_t s) {
   const int nt = a.groups > 1 ? 4 : (a.max_tgt + 15) / 16;
   const dim3 block(256);
-#define GO(NT)                                                                         \
+#define GO(NT, SH)                                                                     \
   {                                                                                    \
-    auto k = attn_bf16_kernel<DH, NT, SCORE, IND, MASK>;                               \
+    auto k = attn_bf16_kernel<DH, NT, SCORE, IND, MASK, SH>;                           \
     a.grid = persistent_grid(k, 256, a.max_units);                                     \
     hipLaunchKernelGGL(k, dim3(a.grid), block, 0, s, a);                               \
   }
-  if (nt >= 4) GO(4) else if (nt == 3) GO(3) else if (nt == 2) GO(2) else GO(1)
+  if constexpr (!IND && !MASK) {
+    if (a.groups > 1 && a.groups <= 4) {  // units are (user, head) x 128 keys; each wave one group
+      a.share = 1;
+      auto k = attn_bf16_kernel<DH, 4, SCORE, IND, MASK, true>;
+      a.grid = persistent_grid(k, 256, a.max_units / a.groups);
+      hipLaunchKernelGGL(k, dim3(a.grid), block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (nt >= 4) GO(4, false) else if (nt == 3) GO(3, false) else if (nt == 2) GO(2, false) else GO(1, false)
 #undef GO
   return hipGetLastError();
 }
@@ -517,6 +581,7 @@ hipError_t launch_bf16(AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
   a.grid = 0;
+  a.share = 0;
   if (a.max_units <= 0 || a.n_tgt <= 0) return hipSuccess;
   if (a.dtype == 1) {
 #define SEL(IND, MASK)                                                                                      \

@@ -85,13 +85,16 @@ constexpr float kAttnLazy = 8.0f / kAttnLog2e;
 // is every key j whose bit j of kvis is clear (a Cross-Mask vertical mask,
 // [WeChat] §3.2: the head attends only to the rows its feature-domain
 // condition selects).  Masked keys take weight 0 and no part in the max.
-template <int DH, int NT, int SCORE>
+// FULL: the caller has checked that every key is visible (the code for
+// masking is then left out; left in, the compiler turns it into selects on
+// every score of every block).
+template <int DH, int NT, int SCORE, bool FULL = false>
 DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const bf16x8 (&vf)[DH / 16],
                     int nvalid, uint32_t kvis, int lane) {
   constexpr int KS = DH / 32, DT = DH / 16;
   const int g = lane >> 4;
   // uniform: only a user's last block is partial, and masks are per block
-  const bool full = nvalid >= 32 && kvis == 0xffffffffu;
+  const bool full = FULL || (nvalid >= 32 && kvis == 0xffffffffu);
   auto visible = [&](int j) { return j < nvalid && ((kvis >> j) & 1u); };
   f32x4 st[2][NT];
 #pragma unroll

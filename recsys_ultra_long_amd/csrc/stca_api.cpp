@@ -1143,9 +1143,13 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int B = cfg->B, d = cfg->d, H = cfg->H, M = cfg->M;
   hipError_t e = hipSuccess;
-  if (out->n_stage_events > 0 && out->stage_events[0] &&
-      (e = hipEventRecord(reinterpret_cast<hipEvent_t>(out->stage_events[0]), s)))
-    return hip_fail(e, "stage event");
+  auto rec = [&](int k) -> hipError_t {
+    if (k < out->n_stage_events && out->stage_events[k])
+      return hipEventRecord(reinterpret_cast<hipEvent_t>(out->stage_events[k]), s);
+    return hipSuccess;
+  };
+  const int ev0 = 3 + 5 * M;  // the pre-pass events follow the forward's own
+  if ((e = rec(0))) return hip_fail(e, "stage event");
 
   // encoder weights, packed as the row chain reads them: W'_Q, W'_K | W'_V, W'_O
   bf16_t *prep = at<bf16_t>(ws, LL.prep);
@@ -1189,6 +1193,7 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
                             out->dev_status, s);
     if (e) return hip_fail(e, "short sequences");
   }
+  if ((e = rec(ev0))) return hip_fail(e, "stage event");
 
   if (B > 0 && batch->n_hist > 0) {
     const int dh = d / H;
@@ -1218,6 +1223,7 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
         k.kbuf = kb;
         k.vbuf = vb;
         if ((e = launch_chain_bf16(k, s))) return hip_fail(e, "encoder K/V");
+        if ((e = rec(ev0 + 1 + 4 * i))) return hip_fail(e, "stage event");
       }
       bf16_t *qe = at<bf16_t>(ws, LL.qe);
       {  // S_short W'_Q / sqrt(d_h)
@@ -1232,6 +1238,7 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
         q.out = qe;
         q.ldo = d;
         if ((e = launch_chain_bf16(q, s))) return hip_fail(e, "encoder queries");
+        if ((e = rec(ev0 + 2 + 4 * i))) return hip_fail(e, "stage event");
       }
       {  // per-head softmax attention of each short row over the user's raw rows
         AttnArgs at_;
@@ -1257,6 +1264,7 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
         at_.attn_lo = at<void>(ws, LL.alo);
         at_.B = B;
         if ((e = launch_attention(at_, s))) return hip_fail(e, "encoder attention");
+        if ((e = rec(ev0 + 3 + 4 * i))) return hip_fail(e, "stage event");
       }
       {  // H_l = attn W'_O -> layer i's block of the stacked table
         ChainArgs o = a;
@@ -1270,6 +1278,7 @@ int longer_forward(const stca_config *cfg, const stca_batch *batch, const stca_w
         o.out = at<bf16_t>(ws, LL.htab) + (size_t)i * rows * d;
         o.ldo = d;
         if ((e = launch_chain_bf16(o, s))) return hip_fail(e, "encoder output projection");
+        if ((e = rec(ev0 + 4 + 4 * i))) return hip_fail(e, "stage event");
       }
     }
   }

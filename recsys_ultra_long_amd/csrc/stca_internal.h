@@ -163,6 +163,8 @@ struct AttnArgs {
   int tgs;                  // target slots per partial (max_tgt if one group, else 64)
   int64_t max_units;        // host bound on units (chunks x H x groups); 0: nothing to do
   int grid;                 // persistent workgroups (set by the partial launch)
+  int share;                // set by the partial launch: units are (user, head) x keys and
+                            // the partials are per (segment, group); 0: (user, group, head)
   int max_grid;             // fused: bound on the grid the partial buffers hold
   int fused;                // partials come from the fused kernel (slot = workgroup + user)
   int tile_blocks;          // fused: 32-key blocks per tile (2: d = 128, 4: d = 256)

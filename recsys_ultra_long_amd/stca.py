@@ -288,8 +288,9 @@ class StageEvents:
                 self.arr[i] = None
 
 
-def n_stage_events(M: int) -> int:
-    return 5 * M + 3
+def n_stage_events(M: int, longer: bool = False) -> int:
+    """Stage events of stca_forward (with the LONGER pre-pass's after them)."""
+    return 9 * M + 4 if longer else 5 * M + 3
 
 
 def n_backward_stage_events(M: int) -> int:

@@ -7,7 +7,8 @@ against the float64 oracle at the bf16 tolerance.
 Cases: the three query modes (HyFormer, fusion, linear) at reduced sizes with
 ragged histories, so that some users have fewer than l_short items and their
 short sequence is the whole history; d = 128 / 256 / 512 (d_h 32 and 64);
-l_short = 1; users with an empty history; and the HyFormer feed workload at
+l_short = 1; 65..256 short rows (one wave per target group in the
+encoder attention); users with an empty history; and the HyFormer feed workload at
 full size (64 users x 8192 items, l_short = 256) in the bench's launch
 configuration, checked on sampled users.
 """
@@ -58,6 +59,11 @@ CASES = {
                                    qmode="linear", encoder="longer", l_short=40, seed=41),
     "fusion-lshort1": lambda: replace(I.spec(2), B=4, L=300, M=2, table_rows=20000, m=3,
                                       encoder="longer", l_short=1, seed=21),
+    # 65..256 short rows: one wave per group of 64 in the encoder attention
+    "fusion-3groups-dh32": lambda: replace(I.spec(3), B=3, L=None, L_max=1500, L_min=20, m=8, M=2,
+                                           table_rows=20000, encoder="longer", l_short=130, seed=32),
+    "hyformer-4groups-ragged": lambda: _hy(B=5, L=None, L_max=900, L_min=60, beta_a=0.7, table_rows=20000,
+                                           M=2, l_short=250, seed=53),
 }
 
 

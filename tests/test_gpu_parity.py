@@ -46,10 +46,23 @@ def _attn_case(dtype, score, dh, H, lens, ms, seed=0, scale_q=1.0):
 @pytest.mark.parametrize("score", ["softmax", "relu"])
 @pytest.mark.parametrize("dh,H", [(32, 8), (64, 4)])
 def test_attention_core_shared_operands(dtype, score, dh, H):
+    # 70 targets for one user: two target groups (bf16: one wave per group)
+    _check_core(dtype, score, dh, H, [0, 1, 31, 32, 33, 200, 1000, 5], [3, 1, 17, 64, 70, 2, 33, 0], dh + H)
+
+
+@pytest.mark.parametrize("score", ["softmax", "relu"])
+@pytest.mark.parametrize("dh,H", [(32, 8), (64, 8)])
+@pytest.mark.parametrize("ms", [[256, 3, 130, 0, 200, 64], [300, 3, 130, 0, 200, 64]])
+def test_attention_core_many_targets(score, dh, H, ms):
+    # up to 256 targets per user (four groups, one per wave, K/V read once
+    # per workgroup), and 300 (five groups, the waves split the keys)
+    _check_core("bf16", score, dh, H, [700, 40, 1, 300, 0, 2049], ms, 7 + dh)
+
+
+def _check_core(dtype, score, dh, H, lens, ms, seed):
     stca = _stca()
-    lens = [0, 1, 31, 32, 33, 200, 1000, 5]
-    ms = [3, 1, 17, 64, 70, 2, 33, 0]
-    ho, to, q, k, v = _attn_case(dtype, score, dh, H, lens, ms, seed=dh + H)
+    print(f"[core] {dtype} {score} dh={dh} H={H} lens={lens} ms={ms}", flush=True)
+    ho, to, q, k, v = _attn_case(dtype, score, dh, H, lens, ms, seed=seed)
     dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
     attn, active, st = stca.attention(dev(q), dev(k), dev(v), dev(ho), dev(to), H, score,
                                       chunk_keys=64)
@@ -82,6 +95,19 @@ def test_attention_split_invariance():
     ho, to, q, k, v = _attn_case("bf16", "softmax", 32, 8, [5000, 77, 1], [64, 9, 1], seed=5)
     dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
     args = (dev(q), dev(k), dev(v), dev(ho), dev(to), 8, "softmax")
+    outs = [stca.attention(*args, chunk_keys=ck)[0].cpu().numpy() for ck in (32, 128, 1024, 0)]
+    again = stca.attention(*args, chunk_keys=128)[0].cpu().numpy()
+    assert np.array_equal(outs[1], again)
+    for o in outs[1:]:
+        assert row_rel_err(o, outs[0]) < 1e-2
+
+
+def test_attention_split_invariance_four_groups():
+    """The same with 256 targets for the long user (one wave per target group)."""
+    stca = _stca()
+    ho, to, q, k, v = _attn_case("bf16", "softmax", 64, 4, [5000, 77, 1], [256, 9, 1], seed=6)
+    dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+    args = (dev(q), dev(k), dev(v), dev(ho), dev(to), 4, "softmax")
     outs = [stca.attention(*args, chunk_keys=ck)[0].cpu().numpy() for ck in (32, 128, 1024, 0)]
     again = stca.attention(*args, chunk_keys=128)[0].cpu().numpy()
     assert np.array_equal(outs[1], again)
