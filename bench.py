@@ -490,9 +490,16 @@ def main():
                           "frac_at_clock": round(hist_tf / at_clk, 4)})
         log(f"history launch: shader clock {ghz:.3f} GHz -> bf16 MFMA peak at that clock "
             f"{at_clk:.0f} TFLOP/s, achieved {hist_tf / at_clk:.1%}")
-    picks = {"history": lambda k: (k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
-                                   (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
-             "attention": lambda k: k.startswith("attn_bf16_kernel<"),
+    # kernel names in the traffic summary (template arguments: <D, rows, input mode, FFN, LN, projection,
+    # output> for the chain; the attention's last argument is its one-wave-per-group mode).  With the
+    # LONGER encoding the short-row history chain and the encoder K/V chain are one kernel instance,
+    # so a per-name average would mix them: neither gets a traffic figure.
+    picks = {"history": lambda k: not longer and (
+                 k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
+                 (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
+             "attention": lambda k: k.startswith("attn_bf16_kernel<") and k.endswith("false>"),
+             "encoder_attention": lambda k: k.startswith("attn_bf16_kernel<") and k.endswith("true>"),
+             "encoder_kv": lambda k: False,
              "fused": lambda k: k.startswith("fused256_kernel<") or k.startswith(f"fused_kernel<{d},")}
     tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{args.path}.md"))
     if tr is not None:

@@ -430,8 +430,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// One thread per (target, feature): fold the partials of the target's
-// (user, group, head) in workgroup order.
+// One thread per (target, 4 consecutive features of one head): fold the
+// partials of the target's (user, group, head) in workgroup order.
 //   softmax: attn = sum_w acc_w e^{m_w - M} / sum_w l_w e^{m_w - M};  ReLU: sums.
 // Streaming partials: a workgroup's segment of a pair is stored at the
 // segment's first unit.  Fused partials (one per workgroup and user, all
@@ -439,12 +439,24 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 template <int SCORE>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int d = a.d, DH = a.dh, H = a.H, G = a.groups, HG = H * G;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= a.n_tgt * d) return;
-  const int t = (int)(e / d), f = (int)(e % d);
-  const int h = f / DH, dh = f % DH;
+  const int d4 = d >> 2;  // d = H d_h, d_h 32 or 64
+  const int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n4 = a.n_tgt * d4;
+  if (e4 >= n4) return;
+  int t, f;
+  if (n4 <= 0x7fffffff) {
+    const unsigned q = (unsigned)e4 / (unsigned)d4;
+    t = (int)q;
+    f = ((int)e4 - (int)q * d4) * 4;
+  } else {
+    t = (int)(e4 / d4);
+    f = (int)(e4 % d4) * 4;
+  }
+  const int hs = DH == 64 ? 6 : 5;
+  const int h = f >> hs, dh = f & (DH - 1);
   const Plan P = a.plan;
-  float out = 0.f, lse_v = 0.f;
+  f32x4 out = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = 0.f;
   int cnt = 0;
   if (t < P.toff[a.B] && a.grid > 0) {
     const int u = upper_index(P.toff, a.B, t);
@@ -473,43 +485,58 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       if (SCORE == 0 && a.dtype) {
         float M = kNegBig;
         for (int wg = w0; wg <= w1; ++wg) M = fmaxf(M, a.part_ml[pidx(wg) * 2]);
-        float acc = 0.f, l = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float l = 0.f;
         for (int wg = w0; wg <= w1; ++wg) {
           const int64_t pi = pidx(wg);
           const float fct = ex2((a.part_ml[pi * 2] - M) * kLog2e);
-          acc += a.part_acc[pi * DH + dh] * fct;
+          const f32x4 pa = ldg4(a.part_acc + pi * DH + dh);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] += pa[c] * fct;
           l += a.part_ml[pi * 2 + 1] * fct;
         }
-        out = l > 0.f ? acc / l : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = l > 0.f ? acc[c] / l : 0.f;
         lse_v = l > 0.f ? M + logf(l) : 0.f;
       } else if (SCORE == 0) {  // fp32 path: normalised partials, fp64 fold
         double M = -1.0e300;
         for (int wg = w0; wg <= w1; ++wg) M = fmax(M, (double)a.part_ml[pidx(wg) * 2]);
-        double acc = 0.0, l = 0.0;
+        double acc[4] = {0.0, 0.0, 0.0, 0.0}, l = 0.0;
         for (int wg = w0; wg <= w1; ++wg) {
           const int64_t pi = pidx(wg);
           const double wgt = (double)a.part_ml[pi * 2 + 1] * exp((double)a.part_ml[pi * 2] - M);
-          acc += (double)a.part_acc[pi * DH + dh] * wgt;
+          const f32x4 pa = ldg4(a.part_acc + pi * DH + dh);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] += (double)pa[c] * wgt;
           l += wgt;
         }
-        out = l > 0.0 ? (float)(acc / l) : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = l > 0.0 ? (float)(acc[c] / l) : 0.f;
         lse_v = l > 0.0 ? (float)(M + log(l)) : 0.f;
       } else {
-        double acc = 0.0;
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
         for (int wg = w0; wg <= w1; ++wg) {
           const int64_t pi = pidx(wg);
-          acc += (double)a.part_acc[pi * DH + dh];
+          const f32x4 pa = ldg4(a.part_acc + pi * DH + dh);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] += (double)pa[c];
           if (dh == 0) cnt += a.part_cnt[pi];
         }
-        out = (float)acc;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) out[c] = (float)acc[c];
       }
     }
   }
   if (SCORE == 0 && a.lse && dh == 0) a.lse[(int64_t)t * H + h] = lse_v;
-  a.attn[e] = out;
+  const int64_t e = e4 * 4;
+  *reinterpret_cast<f32x4 *>(a.attn + e) = out;
   if (a.attn_lo) {
-    if (a.dtype) ((bf16_t *)a.attn_lo)[e] = f2bf(out);
-    else ((float *)a.attn_lo)[e] = out;
+    if (a.dtype) {
+      const uint32_t lo = pack_bf2(out[0], out[1]), hi = pack_bf2(out[2], out[3]);
+      *reinterpret_cast<uint2 *>((bf16_t *)a.attn_lo + e) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<f32x4 *>((float *)a.attn_lo + e) = out;
+    }
   }
   if (SCORE == 1 && a.active && dh == 0) a.active[(int64_t)t * H + h] = cnt;
 }
@@ -616,7 +643,8 @@ hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s) {
   if (a.n_tgt <= 0) return hipSuccess;
-  const int64_t n = a.n_tgt * a.d;
+  if ((a.dh != 32 && a.dh != 64) || a.d % 4) return hipErrorInvalidValue;
+  const int64_t n = a.n_tgt * (a.d / 4);  // threads: 4 features each
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (a.score) hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(merge_kernel<0>, grid, block, 0, s, a);
