@@ -89,3 +89,39 @@ def test_longer_fullsize_feed_sampled():
     sp = _hy()
     p = I.make_problem(sp, threads=16)
     _check(p, users=sorted({0, sp.B // 2, sp.B - 1}))
+
+
+def _fusion(**over):
+    sp = replace(I.spec(3), B=3, L=300, m=4, M=2, table_rows=20000, encoder="longer", l_short=64, seed=33)
+    return replace(sp, **over)
+
+
+@pytest.mark.parametrize("mode", ["hyformer", "fusion"])
+def test_longer_all_histories_empty(mode):
+    sp = _hy(B=3, L=100, table_rows=20000, M=2, l_short=16) if mode == "hyformer" else _fusion(L=100)
+    p = I.make_problem(sp)
+    p.hist_offsets = np.zeros(sp.B + 1, np.int32)
+    p.hist_ids = p.hist_ids[:0].copy()
+    g, _ = _check(p)
+    assert np.all(g["attn"] == 0)
+
+
+def test_longer_no_targets():
+    p = I.make_problem(_fusion())
+    p.tgt_offsets = np.zeros(p.spec.B + 1, np.int32)
+    p.tgt_ids = p.tgt_ids[:0].copy()
+    print(f"[longer] no targets: n_hist={p.n_hist}", flush=True)
+    g = gpu_run(p)
+    assert int(g["status"][0]) == 0
+    assert g["z"].shape[0] == 0
+
+
+def test_longer_bad_offsets_flagged_not_faulting():
+    from recsys_ultra_long_amd import stca
+    p = I.make_problem(_fusion(L=200))
+    p.hist_offsets = p.hist_offsets.copy()
+    p.hist_offsets[1] = p.hist_offsets[2] + 5        # not monotone
+    print("[longer] bad offsets", flush=True)
+    g = gpu_run(p)
+    assert int(g["status"][0]) & stca.DEV_BAD_HIST_OFFSETS
+    assert np.all(g["attn"] == 0)                      # every user treated as empty
