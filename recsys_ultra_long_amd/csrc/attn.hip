@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         v_fragments(vf, vuse);
         uint32_t kvis = 0xffffffffu;
         if (MASK) kvis = (uint32_t)__ballot((mk >> h) & 1u);  // lanes 0..31: keys 0..31
-        attn_block<DH, NT, SCORE, FULL>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
+        attn_block<DH, NT, SCORE, FULL, SHARE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
         mk = mk1;
         mk1 = mk2;
 #pragma unroll

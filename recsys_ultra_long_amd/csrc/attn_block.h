@@ -87,8 +87,10 @@ constexpr float kAttnLazy = 8.0f / kAttnLog2e;
 // condition selects).  Masked keys take weight 0 and no part in the max.
 // FULL: the caller has checked that every key is visible (the code for
 // masking is then left out; left in, the compiler turns it into selects on
-// every score of every block).
-template <int DH, int NT, int SCORE, bool FULL = false>
+// every score of every block).  SWAP: the block max crosses lanes with lane
+// swaps (VALU) instead of LDS permutes, for launches bound by the block
+// step's latency rather than by memory.
+template <int DH, int NT, int SCORE, bool FULL = false, bool SWAP = false>
 DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const bf16x8 (&vf)[DH / 16],
                     int nvalid, uint32_t kvis, int lane) {
   constexpr int KS = DH / 32, DT = DH / 16;
@@ -122,8 +124,12 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
     for (int n = 0; n < NT; ++n) {
       float m = fmaxf(fmaxf(fmaxf(st[0][n][0], st[0][n][1]), fmaxf(st[0][n][2], st[0][n][3])),
                       fmaxf(fmaxf(st[1][n][0], st[1][n][1]), fmaxf(st[1][n][2], st[1][n][3])));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+      if constexpr (SWAP) {
+        m = max_x32(max_x16(m));
+      } else {
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+      }
       mx[n] = m;
       raise |= m > s.mrun[n] + kAttnLazy;
     }
