@@ -85,9 +85,9 @@ DEV int xcd_order(int b, int n) { return (n & 7) ? b : (b & 7) * (n >> 3) + (b >
 // Q / K columns of head a.head_map[h] ([WeChat] §3.3.1: heads sharing one
 // attention map under different masks); V and the output stay head h's.
 //
-// SHARE (more than one target group): K/V are read with the default cache
-// policy instead of the streaming one, so that the other groups' workgroups
-// find the lines in L2.
+// SHARE (two to four target groups): the units are (user, head) x 128 keys,
+// each wave serves one group over every block, and a block's K/V go from HBM
+// through a workgroup-wide LDS ring (see below) instead of to every wave.
 template <int DH, int NT, int SCORE, bool IND, bool MASK, bool SHARE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = DH / 32;  // k-steps of the score MFMA
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int LDT = 32 + 8;  // row stride of the transposed V tile
   __shared__ float sm_m[4][TG], sm_l[4][TG];
   __shared__ int sm_c[4][TG];
-  __shared__ float sm_o[4][TG][DH + 1];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][TG][DH + 1];
   __shared__ __attribute__((aligned(16))) bf16_t sm_vt[IND ? 4 : 1][IND ? DH * LDT : 8];
 
   const Plan P = a.plan;
@@ -122,10 +122,129 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int hq = a.has_map ? a.head_map[h] : h;  // the head whose Q / K give the scores
     const int tbase = P.toff[u];
     const int m_u = P.toff[u + 1] - tbase;
-    constexpr int BS = SHARE ? 1 : 4;  // block stride of a wave
-    const int bw = SHARE ? 0 : w;      // first block of a wave
     const int t0 = grp * TG;
-    if (t0 < m_u) {
+    if constexpr (SHARE) {
+      // Each block of the segment is read from HBM once per workgroup: the
+      // 256 threads load it cooperatively (16 bytes x DH / 32 each, two
+      // blocks ahead in registers), write it one block ahead into a 3-slot LDS
+      // ring over sm_o (used only after the loop), and every wave reads its
+      // MFMA fragments from there.  The 16-byte pieces of a row are permuted
+      // by row bits so that the 16 lanes of a fragment read hit 16 distinct
+      // bank groups.  Waves without targets still load and synchronise.
+      const bool act = t0 < m_u;
+      const int L = P.hoff[u + 1] - P.hoff[u];
+      const int cl = unit - pos.first;
+      const int b0 = P.pblk[u] + cl * a.nb;
+      const int b1 = min(P.pblk[u + 1], P.pblk[u] + (cl + seg_end - unit) * a.nb);
+      AttnState<DH, NT> st;
+      attn_reset(st);
+      if (act) attn_load_q(st, Q, a.d, hq, tbase, t0, m_u, lane);
+      constexpr int NP = DH / 32;      // 16-byte pieces per thread per block
+      constexpr int BLK = 64 * DH;     // bf16 of one head's K and V in a block
+      constexpr int KP = DH / 8;       // 16-byte pieces per K row (one key)
+      bf16_t *ring = reinterpret_cast<bf16_t *>(&sm_o[0][0][0]);
+      static_assert(sizeof(sm_o) >= 3 * BLK * sizeof(bf16_t), "K/V ring exceeds sm_o");
+      auto kswz = [](int r) {  // K row r: piece permutation
+        return DH == 64 ? (((r >> 1) & 1) | (((r >> 3) & 3) << 1)) : ((r >> 3) & 3);
+      };
+      auto vswz = [](int r) { return (r >> 2) & 3; };  // V row r (one feature, 32 keys)
+      auto gload = [&](int b, bf16x8 (&g)[NP]) {
+        const bf16_t *kb = Kb + ((int64_t)b * H + hq) * 32 * DH;
+        const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          const int pc = tid + 256 * j;
+          const bf16_t *src = pc < 4 * DH ? kb + pc * 8 : vb + (pc - 4 * DH) * 8;
+          g[j] = ldnt8(src);
+        }
+      };
+      auto swrite = [&](int b, const bf16x8 (&g)[NP]) {
+        bf16_t *dst = ring + (b % 3) * BLK;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+          const int pc = tid + 256 * j;
+          int off;
+          if (pc < 4 * DH) {
+            const int r = pc / KP, c = pc % KP;
+            off = r * DH + ((c ^ kswz(r)) << 3);
+          } else {
+            const int q = pc - 4 * DH, r = q >> 2, c = q & 3;
+            off = 32 * DH + r * 32 + ((c ^ vswz(r)) << 3);
+          }
+          *reinterpret_cast<bf16x8 *>(dst + off) = g[j];
+        }
+      };
+      bf16x8 ga[NP], gb[NP];
+      if (b0 < b1) {
+        gload(b0, ga);
+        swrite(b0, ga);
+      }
+      if (b0 + 1 < b1) gload(b0 + 1, gb);
+      __syncthreads();
+      auto step = [&](const int b, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        if (b + 2 < b1) gload(b + 2, ga);
+        if (b + 1 < b1) swrite(b + 1, gb);
+        __syncthreads();  // block b + 1 written; every wave is past block b - 2 (its slot)
+        if (act) {
+          const bf16_t *kl = ring + (b % 3) * BLK, *vl = kl + 32 * DH;
+          bf16x8 kf[2][KS], vf[DT];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const int r = kr0 + 4 * kt;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) kf[kt][k] = ld8(kl + r * DH + (((4 * k + g16) ^ kswz(r)) << 3));
+          }
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            const int r = t * 16 + c16;
+            vf[t] = ld8(vl + r * 32 + ((g16 ^ vswz(r)) << 3));
+          }
+          attn_block<DH, NT, SCORE, FULL, true>(st, kf, vf, L - (b - P.pblk[u]) * 32, 0xffffffffu, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < NP; ++j) gb[j] = ga[j];
+      };
+      const int bfull = min(b1, P.pblk[u] + L / 32);
+      int b = b0;
+      for (; b < bfull; ++b) step(b, std::true_type{});
+      for (; b < b1; ++b) step(b, std::false_type{});
+      __syncthreads();  // the ring (over sm_o) is read no more
+      if (act) {  // this wave's partial, through its own LDS rows
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          int cn = st.cnt[n];
+          cn = isum_x16(cn);
+          cn = isum_x32(cn);
+          if (g16 == 0) {
+            sm_m[w][n * 16 + c16] = st.mrun[n];
+            sm_l[w][n * 16 + c16] = st.l[n][0];
+            sm_c[w][n * 16 + c16] = cn;
+          }
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = st.o[t][n][r];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int64_t pw = ((int64_t)unit * G + grp) * a.tgs;
+        for (int e = lane; e < TG * DH; e += 64) {
+          const int tl = e / DH, dh = e % DH;
+          if (t0 + tl >= m_u) continue;
+          a.part_acc[(pw + tl) * DH + dh] = sm_o[w][tl][dh];
+          if (dh == 0) {
+            if (SCORE == 0) {
+              a.part_ml[(pw + tl) * 2] = sm_m[w][tl];
+              a.part_ml[(pw + tl) * 2 + 1] = sm_l[w][tl];
+            } else {
+              a.part_cnt[pw + tl] = sm_c[w][tl];
+            }
+          }
+        }
+      }
+      __syncthreads();  // sm_o is the next segment's ring
+    } else if (t0 < m_u) {
       const int L = P.hoff[u + 1] - P.hoff[u];
       const int cl = unit - (pos.first);  // first unit of this segment within the pair
       const int b0 = P.pblk[u] + cl * a.nb;
@@ -159,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         if constexpr (IND) {
           const bf16_t *Vr = (const bf16_t *)a.vrows;
           Uids U;
-          if (b < b0 + bw + 2 * BS) load_uids(b, U);  // pipeline start
+          if (b < b0 + w + 8) load_uids(b, U);  // pipeline start
           else U = U8;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
@@ -181,16 +300,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         } else {
           const bf16_t *kb = Kb + ((int64_t)b * H + hq) * 32 * DH;
           const bf16_t *vb = Vb + ((int64_t)b * H + h) * DH * 32;
-          auto ldkv = [](const bf16_t *q) {
-            if constexpr (SHARE) return ld8(q);
-            else return ldnt8(q);
-          };
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kk[kt][k] = ldkv(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
+            for (int k = 0; k < KS; ++k) kk[kt][k] = ldnt8(kb + (kr0 + 4 * kt) * DH + k * 32 + g16 * 8);
 #pragma unroll
-          for (int t = 0; t < DT; ++t) vv[t] = ldkv(vb + (t * 16 + c16) * 32 + g16 * 8);
+          for (int t = 0; t < DT; ++t) vv[t] = ldnt8(vb + (t * 16 + c16) * 32 + g16 * 8);
         }
       };
       // IND: V row chunks -> transposed wave-private tile -> V^T fragments
@@ -223,26 +338,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       // two blocks of this wave in flight ahead of the one being used: the
       // loads, not the arithmetic, set the pace once the block step is lean
       bf16x8 k1[2][KS], v1[DT];
-      if (b0 + bw < b1) {
-        load_kv(b0 + bw, kf, vf);
-        if (MASK) mk = load_mask(b0 + bw);
+      if (b0 + w < b1) {
+        load_kv(b0 + w, kf, vf);
+        if (MASK) mk = load_mask(b0 + w);
       }
-      if (b0 + bw + BS < b1) {
-        load_kv(b0 + bw + BS, k1, v1);
-        if (MASK) mk1 = load_mask(b0 + bw + BS);
+      if (b0 + w + 4 < b1) {
+        load_kv(b0 + w + 4, k1, v1);
+        if (MASK) mk1 = load_mask(b0 + w + 4);
       }
-      if (IND && b0 + bw + 2 * BS < b1) load_uids(b0 + bw + 2 * BS, U8);
+      if (IND && b0 + w + 8 < b1) load_uids(b0 + w + 8, U8);
       // one block of this wave; FULL: every key of the block is visible
       auto step = [&](const int b, auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
         bf16x8 k2[2][KS], v2[DT];
         Uids U12;
         // uids first: waiting for them later does not wait for the rows below
-        if (IND && b + 3 * BS < b1) load_uids(b + 3 * BS, U12);
+        if (IND && b + 12 < b1) load_uids(b + 12, U12);
         uint32_t mk2 = 0;
-        if (b + 2 * BS < b1) {
-          load_kv(b + 2 * BS, k2, v2);
-          if (MASK) mk2 = load_mask(b + 2 * BS);
+        if (b + 8 < b1) {
+          load_kv(b + 8, k2, v2);
+          if (MASK) mk2 = load_mask(b + 8);
         }
         if (IND) U8 = U12;
         __builtin_amdgcn_sched_barrier(0);
@@ -251,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         v_fragments(vf, vuse);
         uint32_t kvis = 0xffffffffu;
         if (MASK) kvis = (uint32_t)__ballot((mk >> h) & 1u);  // lanes 0..31: keys 0..31
-        attn_block<DH, NT, SCORE, FULL, SHARE>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
+        attn_block<DH, NT, SCORE, FULL>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
         mk = mk1;
         mk1 = mk2;
 #pragma unroll
@@ -272,12 +387,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       // Two loops over one pipeline: a branch per block would keep both
       // bodies' registers live at once.
       const int bfull = MASK ? b0 : min(b1, P.pblk[u] + L / 32);
-      int b = b0 + bw;
-      for (; b < bfull; b += BS) step(b, std::true_type{});
-      for (; b < b1; b += BS) step(b, std::false_type{});
+      int b = b0 + w;
+      for (; b < bfull; b += 4) step(b, std::true_type{});
+      for (; b < b1; b += 4) step(b, std::false_type{});
 
-      // ---- merge the four waves in LDS (SHARE: each wave alone), write
-      // this segment's partial
+      // ---- merge the four waves in LDS, write this segment's partial
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const float l = st.l[n][0];  // already the whole block range's sum
@@ -294,53 +408,32 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = st.o[t][n][r];
       }
-      if constexpr (SHARE) {  // one wave's partial: no other wave's LDS is read
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        const int64_t pw = ((int64_t)unit * G + grp) * a.tgs;
-        for (int e = lane; e < TG * DH; e += 64) {
-          const int tl = e / DH, dh = e % DH;
-          if (t0 + tl >= m_u) continue;
-          a.part_acc[(pw + tl) * DH + dh] = sm_o[w][tl][dh];
-          if (dh == 0) {
-            if (SCORE == 0) {
-              a.part_ml[(pw + tl) * 2] = sm_m[w][tl];
-              a.part_ml[(pw + tl) * 2 + 1] = sm_l[w][tl];
-            } else {
-              a.part_cnt[pw + tl] = sm_c[w][tl];
-            }
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();  // the wave's LDS is reused by its next segment
-      } else {
-        __syncthreads();
-        const int64_t pbase = (int64_t)unit * a.tgs;
-        for (int e = tid; e < TG * DH; e += 256) {
-          const int tl = e / DH, dh = e % DH;
-          if (t0 + tl >= m_u) continue;
-          if (SCORE == 0) {
-            const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
-            float acc = 0.f, l = 0.f;
+      __syncthreads();
+      const int64_t pbase = (int64_t)unit * a.tgs;
+      for (int e = tid; e < TG * DH; e += 256) {
+        const int tl = e / DH, dh = e % DH;
+        if (t0 + tl >= m_u) continue;
+        if (SCORE == 0) {
+          const float M = fmaxf(fmaxf(sm_m[0][tl], sm_m[1][tl]), fmaxf(sm_m[2][tl], sm_m[3][tl]));
+          float acc = 0.f, l = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float f = ex2((sm_m[q][tl] - M) * kLog2e);
-              acc += sm_o[q][tl][dh] * f;
-              l += sm_l[q][tl] * f;
-            }
-            a.part_acc[(pbase + tl) * DH + dh] = acc;
-            if (dh == 0) {
-              a.part_ml[(pbase + tl) * 2] = M;
-              a.part_ml[(pbase + tl) * 2 + 1] = l;
-            }
-          } else {
-            a.part_acc[(pbase + tl) * DH + dh] =
-                sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
-            if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
+          for (int q = 0; q < 4; ++q) {
+            const float f = ex2((sm_m[q][tl] - M) * kLog2e);
+            acc += sm_o[q][tl][dh] * f;
+            l += sm_l[q][tl] * f;
           }
+          a.part_acc[(pbase + tl) * DH + dh] = acc;
+          if (dh == 0) {
+            a.part_ml[(pbase + tl) * 2] = M;
+            a.part_ml[(pbase + tl) * 2 + 1] = l;
+          }
+        } else {
+          a.part_acc[(pbase + tl) * DH + dh] =
+              sm_o[0][tl][dh] + sm_o[1][tl][dh] + sm_o[2][tl][dh] + sm_o[3][tl][dh];
+          if (dh == 0) a.part_cnt[pbase + tl] = sm_c[0][tl] + sm_c[1][tl] + sm_c[2][tl] + sm_c[3][tl];
         }
-        __syncthreads();  // LDS reused by the next segment
       }
+      __syncthreads();  // LDS reused by the next segment
     }
     unit = seg_end;
   }
