@@ -89,12 +89,24 @@ DEV void ring_prime(Ring &r, const bf16_t *const (&p)[NG]) {
 // operand, else B is.  `lp` are the LDS operand's tile pointers.  While the
 // last three blocks are consumed, blocks 0..2 of the next phase (pointers
 // `np`, two tiles; NGN = 0 when nothing follows) are loaded into the ring.
-template <int RT, int CT, int NK, bool GA, int NGN>
+// LDB: the LDS operand of block kb + 1 is read before block kb's matrix
+// work (for one-wave-per-SIMD launches, where no other wave covers the LDS
+// latency; it costs 4 NL more registers).
+template <int RT, int CT, int NK, bool GA, int NGN, bool LDB = false>
 DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ? RT : CT],
                const bf16_t *const (&lp)[GA ? CT : RT], const bf16_t *const (&np)[2]) {
   static_assert(NK % 4 == 0 && NK >= 4, "phase length must be a multiple of 4 blocks");
   constexpr int NG = GA ? RT : CT;
   constexpr int NL = GA ? CT : RT;
+  bf16x8 lo[LDB ? 2 : 1][NL][2];  // LDS operand (LDB: of this block and the next)
+  auto lds_load = [&](int kb, bf16x8 (&o)[NL][2]) {
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      o[t][0] = ld8(lp[t] + kb * 32);
+      o[t][1] = ld8(lp[t] + kb * 32 + 8);
+    }
+  };
+  if (LDB) lds_load(0, lo[0]);
 #pragma unroll
   for (int kb = 0; kb < NK; ++kb) {
     const int nb = kb + 3;
@@ -103,12 +115,9 @@ DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ?
     } else if (NGN > 0) {
       ring_load<2>(ring, nb % 4, np, nb - NK);
     }
-    bf16x8 lo[NL][2];  // LDS operand of this block
-#pragma unroll
-    for (int t = 0; t < NL; ++t) {
-      lo[t][0] = ld8(lp[t] + kb * 32);
-      lo[t][1] = ld8(lp[t] + kb * 32 + 8);
-    }
+    const int cur = LDB ? kb & 1 : 0;
+    if (!LDB) lds_load(kb, lo[0]);
+    else if (kb + 1 < NK) lds_load(kb + 1, lo[cur ^ 1]);
     // keep the prefetches issued ahead of this block's matrix work
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -117,8 +126,8 @@ DEV void phase(f32x16 (&acc)[RT][CT], Ring &ring, const bf16_t *const (&gp)[GA ?
       for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int j = 0; j < CT; ++j) {
-          const bf16x8 av = GA ? ring.v[kb % 4][i][h] : lo[i][h];
-          const bf16x8 bv = GA ? lo[j][h] : ring.v[kb % 4][j][h];
+          const bf16x8 av = GA ? ring.v[kb % 4][i][h] : lo[cur][i][h];
+          const bf16x8 bv = GA ? lo[cur][j][h] : ring.v[kb % 4][j][h];
           acc[i][j] = mfma32(av, bv, acc[i][j]);
         }
     __builtin_amdgcn_sched_barrier(0);
@@ -191,6 +200,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
   constexpr int XLD = D + kPad;
   constexpr int GLD = kHC + kPad;
   constexpr int FT = D / 128;  // 32-feature tiles per wave for d-wide outputs
+  constexpr bool LDB = D >= 512;  // one wave per SIMD at d = 512: prefetch LDS operands
   bf16_t *const xs = sm.xs;
   auto &gs = sm.gs;
   auto &red = sm.red;
@@ -376,7 +386,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         const bf16_t *gp[2], *nx[2];
         g_ptrs(hc, gp);
         y_ptrs(hc, 0, nx);
-        phase<2, TT, D / 32, true, 2>(acc, ring, gp, bx, nx);
+        phase<2, TT, D / 32, true, 2, LDB>(acc, ring, gp, bx, nx);
 #pragma unroll
         for (int j = 0; j < TT; ++j)
 #pragma unroll
@@ -401,7 +411,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
           if (sp + 1 < NSP) y_ptrs(hc, sp + 1, nx);
           else if (hc + 1 < nchunk) g_ptrs(hc + 1, nx);
           else first_proj_ptrs(nx);
-          phase<YT, TT, kHC / 32, true, 2>(y[sp], ring, gp, bg, nx);
+          phase<YT, TT, kHC / 32, true, 2, LDB>(y[sp], ring, gp, bg, nx);
         }
       }
     }
@@ -504,7 +514,7 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) proj_ptrs2(sp + 1, 0, nx);
         else proj_ptrs2(0, nkD, nx);
-        phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bp, nx);
+        phase<YT, TT, D / 32, true, 2, LDB>(acc, ring, gp, bp, nx);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
           const int blk = (int)(row0 >> 5) + t;
@@ -539,9 +549,9 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, nkD, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, nkD, nx);
-          phase<TT, YT, D / 32, false, 2>(acc, ring, gp, bp, nx);
+          phase<TT, YT, D / 32, false, 2, LDB>(acc, ring, gp, bp, nx);
         } else {
-          phase<TT, YT, D / 32, false, 0>(acc, ring, gp, bp, nx);
+          phase<TT, YT, D / 32, false, 0, LDB>(acc, ring, gp, bp, nx);
         }
         if constexpr (OUT == OUT_FUSED) __syncthreads();  // V^T goes over rows other waves read
 #pragma unroll
@@ -580,9 +590,9 @@ DEV void chain_tile(const ChainArgs &a, const int64_t row0, ChainSmem<D, TT, FFN
         proj_ptrs(sp, 0, gp);
         if (sp + 1 < NSP) {
           proj_ptrs2(sp + 1, 0, nx);
-          phase<YT, TT, D / 32, true, 2>(acc, ring, gp, bp, nx);
+          phase<YT, TT, D / 32, true, 2, LDB>(acc, ring, gp, bp, nx);
         } else {
-          phase<YT, TT, D / 32, true, 0>(acc, ring, gp, bp, nx);
+          phase<YT, TT, D / 32, true, 0, LDB>(acc, ring, gp, bp, nx);
         }
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
