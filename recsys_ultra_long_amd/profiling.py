@@ -32,8 +32,10 @@ CSRC = os.path.join(HERE, "csrc")
 def source_hash() -> str:
     """Hash of the kernel sources and of the flags they are compiled with."""
     from recsys_ultra_long_amd import build
+    root = os.path.dirname(HERE)  # paths in flags relative to the checkout, which moves between machines
+    flags = [os.path.relpath(f, root) if os.path.isabs(f) else f for f in build.COMMON[1:]]
     h = hashlib.sha256()
-    h.update(json.dumps([build.COMMON[1:], build.FILE_FLAGS], sort_keys=True).encode())
+    h.update(json.dumps([flags, build.FILE_FLAGS], sort_keys=True).encode())
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".hip", ".cpp", ".h")):
             h.update(f.encode())
