@@ -30,29 +30,52 @@ constexpr int kPad = 8;       // bf16 elements of row padding in LDS (16 bytes)
 // acc[i][j] += A(tile i) * B(tile j)^T over k in [0, K) with A a packed
 // weight (ar[i]: the lane's fragment of tile i at the first k block) and B
 // plain rows (br[j]: the lane's row, already offset by its 16-element k group).
+// The loads of the next two 32-wide k blocks are in flight while a block is
+// multiplied (three register stages; the rows are few, so the launch is
+// bound by load latency, not by bandwidth).
 template <int RT, int CT>
 DEV void mma_packed_a(f32x16 (&acc)[RT][CT], const bf16_t *const (&ar)[RT],
                       const bf16_t *const (&br)[CT], int K) {
-#pragma unroll 1
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    bf16x8 a[RT][2], b[CT][2];
+  constexpr int S = 3;
+  const int nk = K / 32;
+  bf16x8 a[S][RT][2], b[S][CT][2];
+  auto load = [&](int kb, bf16x8 (&sa)[RT][2], bf16x8 (&sb)[CT][2]) {
+    const int k0 = kb * 32;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      a[i][0] = ld8(ar[i] + k0 * 32);
-      a[i][1] = ld8(ar[i] + k0 * 32 + 512);
+      sa[i][0] = ld8(ar[i] + k0 * 32);
+      sa[i][1] = ld8(ar[i] + k0 * 32 + 512);
     }
 #pragma unroll
     for (int j = 0; j < CT; ++j) {
-      b[j][0] = ld8(br[j] + k0);
-      b[j][1] = ld8(br[j] + k0 + 8);
+      sb[j][0] = ld8(br[j] + k0);
+      sb[j][1] = ld8(br[j] + k0 + 8);
     }
+  };
+  auto mma = [&](const bf16x8 (&sa)[RT][2], const bf16x8 (&sb)[CT][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < CT; ++j) acc[i][j] = mfma32(a[i][h], b[j][h], acc[i][j]);
+        for (int j = 0; j < CT; ++j) acc[i][j] = mfma32(sa[i][h], sb[j][h], acc[i][j]);
+  };
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) load(st, a[st], b[st]);
+  int kb = 0;
+#pragma unroll 1
+  for (; kb + S <= nk; kb += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) {  // stage st holds block kb + st
+      const int nx = kb + st + S - 1;
+      if (nx < nk) load(nx, a[(st + S - 1) % S], b[(st + S - 1) % S]);
+      mma(a[st], b[st]);
+    }
   }
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)  // fewer than S blocks remain, already loaded
+    if (kb + st < nk) mma(a[st], b[st]);
 }
 
 // ---------------------------------------------------------------- weight ring
