@@ -28,37 +28,51 @@ constexpr int kPoolChunks = 16;
 __global__ __launch_bounds__(kT) void mean_pool_part_kernel(const bf16_t *__restrict__ table, int64_t table_rows,
                                                             const int *__restrict__ ids, Plan P, int B, int d,
                                                             float *part) {
-  __shared__ float sm[4][64];
+  // 8 consecutive features per lane (one 16-byte load per row), 512 per wave
+  __shared__ float sm[4][512];
   const int u = blockIdx.x / kPoolChunks, c = blockIdx.x % kPoolChunks;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int f = blockIdx.y * 64 + lane;
+  const int f0 = blockIdx.y * 512 + lane * 8;
   if (u >= B) return;
   const int h0 = P.hoff[u], L = P.hoff[u + 1] - h0;
   // this wave's rows: j = c + kPoolChunks * (w + 4 k), k = 0, 1, ..
   constexpr int S = 4 * kPoolChunks;
-  float s = 0.f;
-  if (f < d) {
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto row = [&](int id) -> bf16x8 {
+    bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    return (id >= 0 && (int64_t)id < table_rows) ? ld8(table + (int64_t)id * d + f0) : z;
+  };
+  if (f0 < d) {
     int j = c + kPoolChunks * w;
     for (; j + 3 * S < L; j += 4 * S) {
       int id[4];
-      float v[4];
+      bf16x8 v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) id[q] = ids[h0 + j + q * S];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[q] = (id[q] >= 0 && (int64_t)id[q] < table_rows) ? bf2f(table[(int64_t)id[q] * d + f]) : 0.f;
+      for (int q = 0; q < 4; ++q) v[q] = row(id[q]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s += v[q];
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += bf2f((bf16_t)v[q][e]);
     }
     for (; j < L; j += S) {
-      const int id = ids[h0 + j];
-      if (id >= 0 && (int64_t)id < table_rows) s += bf2f(table[(int64_t)id * d + f]);
+      const bf16x8 v = row(ids[h0 + j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += bf2f((bf16_t)v[e]);
     }
   }
-  sm[w][lane] = s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[w][lane * 8 + e] = s[e];
   __syncthreads();
-  if (w == 0 && f < d)
-    part[((int64_t)u * kPoolChunks + c) * d + f] = ((sm[0][lane] + sm[1][lane]) + sm[2][lane]) + sm[3][lane];
+  if (w == 0 && f0 < d) {
+    const int64_t o = ((int64_t)u * kPoolChunks + c) * d + f0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int x = lane * 8 + e;
+      part[o + e] = ((sm[0][x] + sm[1][x]) + sm[2][x]) + sm[3][x];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kT) void mean_pool_fold_kernel(const float *__restrict__ part, Plan P, int B, int d,
@@ -127,7 +141,8 @@ int64_t mean_pool_part_floats(int B, int d) { return (int64_t)B * kPoolChunks * 
 hipError_t launch_mean_pool(const bf16_t *table, int64_t table_rows, const int *hist_ids, const Plan &plan, int B,
                             int d, float *mp, float *part, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mean_pool_part_kernel, dim3((unsigned)(B * kPoolChunks), (unsigned)((d + 63) / 64)), dim3(kT),
+  if (d % 8) return hipErrorInvalidValue;  // 16-byte row pieces
+  hipLaunchKernelGGL(mean_pool_part_kernel, dim3((unsigned)(B * kPoolChunks), (unsigned)((d + 511) / 512)), dim3(kT),
                      0, s, table, table_rows, hist_ids, plan, B, d, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
