@@ -103,7 +103,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int H = a.H, G = a.groups, HG = SHARE ? H : H * G;  // pairs per user: heads, or (group, head)
   const int total = P.coff[a.B] * HG;
   const int per = units_per_wg(total, gridDim.x);
-  int unit = xcd_order(blockIdx.x, gridDim.x) * per;
+  const int wgl = xcd_order(blockIdx.x, gridDim.x);  // logical workgroup
+  int unit = wgl * per;
   const int unit_end = min(total, unit + per);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        const int64_t pw = ((int64_t)unit * G + grp) * a.tgs;
+        const int64_t pw = ((int64_t)(wgl + u * H + h) * G + grp) * a.tgs;  // slot (workgroup + pair), group
         for (int e = lane; e < TG * DH; e += 64) {
           const int tl = e / DH, dh = e % DH;
           if (t0 + tl >= m_u) continue;
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int r = 0; r < 4; ++r) sm_o[w][n * 16 + c16][t * 16 + 4 * g16 + r] = st.o[t][n][r];
       }
       __syncthreads();
-      const int64_t pbase = (int64_t)unit * a.tgs;
+      const int64_t pbase = (int64_t)(wgl + u * HG + pos.pair) * a.tgs;  // slot: workgroup + pair
       for (int e = tid; e < TG * DH; e += 256) {
         const int tl = e / DH, dh = e % DH;
         if (t0 + tl >= m_u) continue;
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         }
       }
       if (act) {
-        const int64_t pi = (int64_t)unit * a.tgs + (tl - grp * 64);
+        const int64_t pi = (int64_t)(blockIdx.x + u * HG + pos.pair) * a.tgs + (tl - grp * 64);
         // softmax partials are stored normalised by their own running sum
         // (a convex combination, no cancellation), the sum separately
         if (SCORE == 0) {
@@ -568,10 +569,11 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       first = P.coff[u] * hg + (a.share ? h : grp * H + h) * nu;
       per = units_per_wg(P.coff[a.B] * hg, a.grid);
     }
+    // slot of the segment of workgroup wg: wg + the pair's global index
+    const int64_t gp = a.share ? (int64_t)u * H + h : (int64_t)u * HG + grp * H + h;
     auto pidx = [&](int wg) -> int64_t {
       if (a.fused) return partial_index(wg + u, H, h, a.tgs, tg);
-      const int64_t seg = max(first, wg * per);
-      return (a.share ? seg * G + grp : seg) * a.tgs + tg;
+      return (a.share ? (wg + gp) * G + grp : wg + gp) * a.tgs + tg;
     };
     if (nu > 0) {
       const int w0 = first / per, w1 = (first + nu - 1) / per;
@@ -670,7 +672,7 @@ int persistent_grid(K kernel, int threads, int64_t units) {
     cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(units, (int64_t)cus * per_cu));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({units, (int64_t)cus * per_cu, (int64_t)kAttnMaxGrid}));
 }
 
 template <int DH, int SCORE, bool IND, bool MASK>

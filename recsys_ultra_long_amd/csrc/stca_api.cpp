@@ -109,12 +109,14 @@ struct Layout {
 // grid, not by the unit), so they are small: 128 keys.
 int choose_nb(int chunk_keys) { return chunk_keys > 0 ? chunk_keys / 32 : 4; }
 
-// Partial slots of the attention: one per unit, each with room for the
-// targets of one group.
-size_t partial_slots(int64_t max_chunks, int H, int max_tgt) {
+// Partial slots of the streaming attention: (grid cap + B H) x groups slots
+// (one per segment of a workgroup and a (user, group, head) pair, or of a
+// (user, head) pair and each of its groups), each with room for the targets of
+// one group.
+size_t partial_slots(int64_t B, int H, int max_tgt) {
   const int groups = (max_tgt + 63) / 64;
   const int tgs = groups > 1 ? 64 : max_tgt;
-  return (size_t)max_chunks * H * groups * tgs;
+  return (size_t)(kAttnMaxGrid + B * H) * groups * tgs;
 }
 
 int validate_cfg(const stca_config *c) {
@@ -381,7 +383,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   // staged: blocked K/V of every layer; fused: none (the point of that path)
   L.kv_layer = L.fused ? 0 : (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
   L.kv = cv.take(2 * L.kv_layer * c->M);
-  size_t np = partial_slots(L.max_chunks, c->H, b->max_tgt_per_user);
+  size_t np = partial_slots(c->B, c->H, b->max_tgt_per_user);
   if (L.fused)  // one slot per (workgroup, user): independent of the history length
     np = (size_t)(L.fused_grid + c->B) * c->H * b->max_tgt_per_user;
   L.part_ml = cv.take(np * 2 * sizeof(float));
@@ -446,7 +448,7 @@ LongerLayout make_longer_layout(const stca_config *c, const stca_batch *b) {
   LL.prep = cv.take((size_t)c->M * 4 * d * d * 2);  // per layer: W'_Q, W'_K | W'_V, W'_O (packed bf16)
   LL.kvl = (size_t)LL.mb * 32 * d * 2;
   LL.kv = cv.take(2 * LL.kvl);
-  const size_t np = partial_slots(LL.mc, c->H, c->l_short);
+  const size_t np = partial_slots(c->B, c->H, c->l_short);
   LL.ml = cv.take(np * 2 * sizeof(float));
   LL.acc = cv.take(np * (d / c->H) * sizeof(float));
   LL.cnt = cv.take(np * sizeof(int));
@@ -1342,7 +1344,7 @@ static AttnLayout attn_layout(const stca_attn_args *a) {
   L.plan = cv.take(4 * sizeof(int) * (size_t)(a->B + 1));
   L.kvl = (size_t)L.mb * 32 * a->d * es;
   L.kv = cv.take(2 * L.kvl);
-  const size_t np = partial_slots(L.mc, a->H, a->max_tgt_per_user);
+  const size_t np = partial_slots(a->B, a->H, a->max_tgt_per_user);
   L.ml = cv.take(np * 2 * sizeof(float));
   L.acc = cv.take(np * (a->d / a->H) * sizeof(float));
   L.cnt = cv.take(np * sizeof(int));

@@ -211,6 +211,12 @@ inline void attn_shape(AttnArgs &a, int64_t max_chunks) {
 // workgroup keeps its heads' state in fused_state_bytes / grid bytes of
 // at.fstate.  Sets at.grid.
 constexpr int kFusedMaxGrid = 512;
+// Streaming attention: cap on its persistent grid (MI355X launches 256 CUs x 2
+// workgroups).  Its partials live in slots (logical workgroup + global pair):
+// each workgroup's range of units covers an ordered run of pairs, so the slots
+// of different (workgroup, pair) segments are distinct, and their number is
+// bounded by the cap plus the pairs, whatever the history length.
+constexpr int kAttnMaxGrid = 1024;
 // d = 256 runs 128-key tiles on 8 waves (launch_fused256), d = 128 64-key
 // tiles on 4 waves (launch_fused); users are padded to whole tiles.
 inline int fused_tile_blocks(int d) { return d == 256 ? 4 : 2; }
