@@ -90,7 +90,8 @@ enum { STCA_ENC_SWIGLU = 0, STCA_ENC_LONGER = 1 };     /* stca_config.encoder */
  *    (S_short) to all of its rows (S); then K = H_l W_K, V = H_l W_V, and the
  *    targets attend over these min(L_u, l_short) rows.  bf16, staged path,
  *    softmax scores; not with STCA_FLAG_DEDUP, Cross-Mask, x_dump, kv_dump or
- *    stca_backward.  The history FFN weights (layer.kv) are not read. */
+ *    stca_backward.  The history FFN weights (layer.kv) are not read, and
+ *    STCA_FLAG_KV_LN is ignored. */
 enum {                                                 /* stca_config.flags  */
   STCA_FLAG_KV_LN = 1,  /* LN after the history FFN (STCA); clear for HyFormer eq. (7) */
   STCA_FLAG_Z_LN = 2,   /* LN on the final z ([Notes] wording); default is [Review]'s z */
