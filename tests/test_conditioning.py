@@ -1,0 +1,146 @@
+"""Conditioning of the ReLU-scored chain, on the CPU.
+
+The ReLU-scored attention ([WeChat] §1.2: a key is active when its score is
+above zero, and the output is the unnormalised weighted sum) uses the score
+itself as the weight.  A score is a d_h-term dot product whose absolute error
+under rounding is about eps |q| |k| while its size is about |q| |k| / sqrt(d_h)
+times a cosine, so the weights carry a relative error of roughly
+eps sqrt(d_h) (unbounded for scores near zero); softmax turns the same
+absolute score error into a relative weight error of the same absolute size
+(exp(s + delta) = exp(s) (1 + delta + ...)).  Across M stacked layers the
+query chain carries these errors on.
+
+These tests measure, with the oracle's own steps (``conditioning.py``), how
+far the end-to-end outputs move when intermediates are stored at a lower
+precision, on the inputs of the GPU parity tests.  The GPU end-to-end bar of
+the ReLU chain is derived from exactly this measurement (2x the deviation of
+a model with the GPU's storage and accumulation precision), and the last test
+shows that bar still fails the mistakes it must catch.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from oracle import stca_oracle as O
+from recsys_ultra_long_amd import inputs as I
+
+import conditioning as C
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def _relu_bf16():
+    # the reduced ragged workload of the GPU parity tests (d 128, H 4, M 3, m 16)
+    return I.make_problem(I.spec(4, B=6, L_max=1200, table_rows=20000, score="relu"))
+
+
+def _relu_f32():
+    # the fp32 ragged multi-layer ReLU case of the GPU parity tests
+    return I.make_problem(I.spec(1, L=None, L_max=300, L_min=1, B=5, M=3, m=5, score="relu",
+                                 ln_random=True))
+
+
+def test_round_helpers():
+    import torch
+    x = np.random.default_rng(0).standard_normal(4096) * 10.0 ** np.random.default_rng(1).integers(-8, 8, 4096)
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(C.round_bf16(x), ref)
+    assert np.array_equal(C.round_bf16(x), I.bf16_bits_to_f32(I.f32_to_bf16_bits(x.astype(np.float32))))
+    assert np.array_equal(C.round_f32(x), x.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("make", [_relu_bf16, _relu_f32])
+def test_no_rounding_reproduces_the_oracle(make):
+    """The composition re-walks the oracle's forward: without any rounding,
+    in float64, it must give the oracle's outputs."""
+    p = make()
+    ex = O.forward_problem(p)
+    dev = C.deviation(p, "bf16", points=(), exact=ex)
+    assert all(v < 1e-12 for v in dev.values()), dev
+
+
+def test_no_rounding_reproduces_the_oracle_linear_mode():
+    sp = I.spec(5)["feed"]
+    p = I.make_problem(replace(sp, B=2, L=120, table_rows=3000, score="relu"))
+    dev = C.deviation(p, "bf16", points=())
+    assert all(v < 1e-12 for v in dev.values()), dev
+
+
+def test_relu_chain_bf16_exceeds_the_tolerance_from_kv_rounding_alone():
+    """Rounding only K and V to bf16, everything else exact, already moves the
+    ReLU chain's z and attention beyond 2e-2; the softmax chain on the same
+    inputs stays well inside it even with every storage point rounded."""
+    p = _relu_bf16()
+    ex = O.forward_problem(p)
+    kv = C.deviation(p, "bf16", points=("kv",), exact=ex)
+    assert kv["z"] > TOL["bf16"], kv
+    full = C.deviation(p, "bf16", exact=ex, arith="f32")
+    assert min(full.values()) > TOL["bf16"], full
+    ps = replace(p, spec=replace(p.spec, score="softmax"))
+    soft = C.deviation(ps, "bf16", arith="f32")
+    assert max(soft.values()) < TOL["bf16"] / 2, soft
+
+
+def test_relu_chain_f32_exceeds_the_tolerance():
+    """The fp32 ReLU chain: storing at fp32 (exact arithmetic otherwise) moves
+    the attention beyond 1e-5, and fp32 row arithmetic (the fp32 path's
+    accumulation) by more than 1e-4; the softmax chain stays below 1e-6.  The
+    worst row is a target whose heads see at most two barely positive
+    scores: its output is tiny, so its relative error is large."""
+    p = _relu_f32()
+    ex = O.forward_problem(p)
+    st = C.deviation(p, "f32", exact=ex)
+    assert st["attn"] > TOL["f32"], st
+    ar = C.deviation(p, "f32", exact=ex, arith="f32", attn_arith="f64")
+    assert ar["attn"] > 10 * TOL["f32"], ar
+    pert = C.perturbed_forward(p, "f32", arith="f32", attn_arith="f64")
+    M, T, _ = ex["attn"].shape
+    errs = np.zeros((M, T))
+    for i in range(M):
+        for t in range(T):
+            den = np.abs(ex["attn"][i, t]).max()
+            errs[i, t] = np.abs(pert["attn"][i, t] - ex["attn"][i, t]).max() / den if den > 0 else 0.0
+    i, t = np.unravel_index(errs.argmax(), errs.shape)
+    assert ex["active"][i, t].max() <= 2, ex["active"][i, t]
+    assert np.abs(ex["attn"][i, t]).max() < 1e-2 * np.median(np.abs(ex["attn"][i]).max(axis=1))
+    ps = replace(p, spec=replace(p.spec, score="softmax"))
+    soft = C.deviation(ps, "f32", arith="f32", attn_arith="f64")
+    assert max(soft.values()) < TOL["f32"] / 10, soft
+
+
+def _mistakes(p):
+    """Copies of ``p`` with one planted mistake each (what an implementation
+    could get wrong in the chain)."""
+    out = {}
+    q = replace(p, layers=[dict(l) for l in p.layers])
+    wc = q.layers[1]["wc"].copy()
+    wc[-p.spec.d:] = 0                    # x_t block of the fusion concat dropped
+    q.layers[1]["wc"] = wc
+    out["xt_dropped"] = q
+    q = replace(p, layers=[dict(l) for l in p.layers])
+    dh = p.spec.d_h
+    wq = q.layers[0]["wq"].copy()
+    wq[:, :dh], wq[:, dh:2 * dh] = p.layers[0]["wq"][:, dh:2 * dh], p.layers[0]["wq"][:, :dh]
+    q.layers[0]["wq"] = wq                # heads 0 and 1 of W_Q swapped
+    out["heads_swapped"] = q
+    q = replace(p, layers=[dict(l) for l in p.layers])
+    q.layers[2]["wk"] = p.layers[1]["wk"]  # a layer reads another layer's W_K
+    out["wrong_layer_wk"] = q
+    q = replace(p, layers=[dict(l) for l in p.layers])
+    q.layers[1]["wo"] = np.ascontiguousarray(p.layers[1]["wo"].T)  # W_O transposed
+    out["wo_transposed"] = q
+    return out
+
+
+def test_relu_end_to_end_bar_still_catches_mistakes():
+    """The GPU bar for the ReLU chain is max(tol, 2 D) with D the deviation of
+    the storage-precision model.  Each planted mistake, evaluated exactly,
+    deviates from the oracle by far more than that bar."""
+    p = _relu_bf16()
+    ex = O.forward_problem(p)
+    D = C.deviation(p, "bf16", exact=ex, arith="f32")
+    bar = max(TOL["bf16"], 2 * max(D.values()))
+    for name, q in _mistakes(p).items():
+        dev = C.deviation(q, "bf16", points=(), exact=ex)
+        assert max(dev["z"], dev["o"]) > 3 * bar, (name, dev, bar)

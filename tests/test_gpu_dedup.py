@@ -2,7 +2,9 @@
 history id of the batch is encoded once and its K/V copied to every token
 carrying it.  A row's K/V depends on its id alone and the encoder's per-row
 arithmetic does not depend on which rows share its tile, so the whole forward
-must equal the plain staged path bit for bit -- every output and dump."""
+must equal the plain staged path bit for bit -- every output and dump -- and,
+like it, the float64 oracle within the parity bar (every user of the reduced
+workloads; sampled users at full size)."""
 from dataclasses import replace
 
 import numpy as np
@@ -10,7 +12,7 @@ import pytest
 
 from recsys_ultra_long_amd import inputs as I
 
-from parity_util import gpu_run
+from parity_util import end_to_end_bar, gpu_run, oracle_run, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +31,23 @@ def _small(k, **over):
     return I.spec(k, **base)
 
 
-def _same(p, dumps=("q", "kv")):
+def _vs_oracle(p, g, users=None):
+    """The dedup forward against the oracle: z, o and attn within the bar
+    (the bf16 tolerance; for ReLU-scored chains the conditioning bar)."""
+    o = oracle_run(p, users)
+    rows = (np.arange(p.n_tgt) if users is None else
+            np.concatenate([np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users]))
+    errs = {k: row_rel_err(g[k][..., rows, :], o[k][..., rows, :]) for k in ("z", "o", "attn")}
+    bar = end_to_end_bar(p, users=users, exact=o)
+    print(f"[dedup] vs oracle {errs} bar {bar}", flush=True)
+    assert all(errs[k] <= bar[k] for k in errs), (errs, bar)
+    if p.spec.score == "relu" and users is None:
+        # counts on the first layer, where both sides start from the same rows
+        diff = np.abs(g["active"][0].astype(np.int64) - o["active"][0])
+        assert diff.mean() < 0.02 * max(1.0, o["active"][0].mean())
+
+
+def _same(p, dumps=("q", "kv"), oracle_users="all"):
     g0 = gpu_run(p, dumps=dumps)
     g1 = gpu_run(p, dumps=dumps, dedup=True)
     n_u = len(np.unique(p.hist_ids))
@@ -41,6 +59,8 @@ def _same(p, dumps=("q", "kv")):
             continue
         assert a.shape == b.shape, key
         assert np.array_equal(a, b), key
+    if oracle_users is not None:
+        _vs_oracle(p, g1, None if oracle_users == "all" else oracle_users)
     return g0, g1
 
 
@@ -77,4 +97,5 @@ def test_dedup_all_ids_equal():
 
 def test_dedup_fullsize_rlb_long():
     p = I.make_problem(I.spec(3), threads=16)
-    _same(p, dumps=())
+    users = sorted({int(u) for u in np.linspace(0, p.spec.B - 1, 8).round()})
+    _same(p, dumps=(), oracle_users=users)

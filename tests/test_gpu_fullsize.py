@@ -1,8 +1,9 @@
 """Full-size parity: the workloads at their real sizes, run through the C ABI in
-the launch configuration bench.py times, checked against the float64 oracle on
-sampled users (the first, the last, a middle one, and for ragged batches the
-shortest and the longest history).  The oracle computes those users' targets
-one by one; the GPU computes the whole batch.
+the launch configuration bench.py times, checked against the float64 oracle:
+every user of the single-target workload (64 users x 2,048 items), and on the
+others eight users spread over the batch plus the shortest and the longest
+history.  The oracle computes those users' targets one by one; the GPU
+computes the whole batch.
 """
 from dataclasses import replace
 
@@ -11,7 +12,7 @@ import pytest
 
 from recsys_ultra_long_amd import inputs as I
 
-from parity_util import TOL, gpu_run, oracle_run, row_rel_err, stepwise_errors
+from parity_util import TOL, end_to_end_bar, gpu_run, oracle_run, row_rel_err, stepwise_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -20,11 +21,16 @@ if not torch.cuda.is_available():
     pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU visible")]
 
 
-def _sample_users(p, k=3):
+def _sample_users(p, k=8):
+    """Every user when the batch has at most 64; else k users evenly spread
+    (the first and the last among them) plus the shortest and the longest."""
     B = p.spec.B
+    if B <= 64 and p.spec.name.startswith("single-target"):
+        return list(range(B))
     lens = np.diff(p.hist_offsets)
-    users = {0, B // 2, B - 1, int(lens.argmin()), int(lens.argmax())}
-    return sorted(users)[: max(k, 5)]
+    users = {int(u) for u in np.linspace(0, B - 1, k).round()}
+    users |= {int(lens.argmin()), int(lens.argmax())}
+    return sorted(users)
 
 
 def _target_rows(p, users):
@@ -58,10 +64,13 @@ def test_fullsize_ragged_softmax():
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
 
 
-def test_fullsize_ragged_relu_stepwise():
+def test_fullsize_ragged_relu():
     """ReLU-scored ragged batch at full size: each step of the sampled users is
-    checked at the operands the GPU fed it (see parity_util.stepwise_errors)."""
+    checked at the operands the GPU fed it (see parity_util.stepwise_errors),
+    and the end-to-end outputs against the bar the chain's conditioning on
+    those users sets (parity_util.end_to_end_bar)."""
     p = I.make_problem(I.spec(4, score="relu"), threads=16)
+    print(f"[fullsize] {p.spec.name} relu B={p.spec.B} n_hist={p.n_hist}", flush=True)
     g = gpu_run(p, dumps=("q", "kv"))
     users = _sample_users(p)
     sub = I.subset_users(p, users)
@@ -74,6 +83,11 @@ def test_fullsize_ragged_relu_stepwise():
     print(f"[fullsize] relu users {users} stepwise {errs}", flush=True)
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
     assert cnt_exact and cnt_band
+    o = oracle_run(sub)
+    e2e = {k: row_rel_err(gs[k], o[k]) for k in ("z", "o", "attn")}
+    bar = end_to_end_bar(sub, exact=o)
+    print(f"[fullsize] relu end-to-end {e2e} bar {bar}", flush=True)
+    assert all(e2e[k] <= bar[k] for k in e2e), (e2e, bar)
 
 
 @pytest.mark.parametrize("seq", ["feed", "search"])
