@@ -40,14 +40,21 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   count is #{j : s_j > 0} ([WeChat] §1.2: a key is active when its score is
   above zero).
 * Empty history: attention output 0, active count 0.
+* An id outside [0, table rows) reads a zero row (no page covers invalid ids;
+  this is the boundary's convention, which the library also flags).
 * HyFormer linear mode: Q_{l+1} = O_l R_l, output O_M ([HyFormer] eq. (9),
   (16), with the boosting block replaced by a fixed linear map).
 * Cross-Mask ([WeChat] §3.2-3.3): a vertical mask keeps, per head (one
   feature domain's column slice, its horizontal mask), only the history items
   its condition selects: softmax / ReLU over those items, 0 when none; heads
   sharing an attention map score with the same Q / K columns (a head map)
-  under their own masks and V columns.  The context-similarity score bias the
-  page mentions has no formula there and is not modelled.
+  under their own masks and V columns.
+* Context-similarity score bias ([WeChat] §2.2.3, 上下文利用: the context
+  similarity of two videos fine-tunes the target-attention score; the page
+  gives no formula): an additive bias b[j, eta] per history item and head,
+  added to the scaled score of every target of the user in every layer
+  (all targets of one request share the user's current context), before the
+  softmax or the ReLU.  Its values are the caller's.
 * HyFormer query mode ([HyFormer] §3.3.2 eq. (3)-(4), §3.5 eq. (10)-(15),
   §3.6 eq. (16)-(17)): every "FFN" is the SwiGLU block above without LN; the
   N queries of a user are FFN_n(Concat(F_1, ..., F_M, MeanPool(Seq))) with
@@ -119,7 +126,7 @@ def ffn_ln(x: np.ndarray, w: dict, ln: bool) -> np.ndarray:
 
 # ---------------------------------------------------------------- attention
 def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
-                     scale: Optional[float] = None, key_mask=None, head_map=None):
+                     scale: Optional[float] = None, key_mask=None, head_map=None, score_bias=None):
     """One target (query row ``Q`` of width d, already multiplied by W_Q)
     against one user's keys K and values V ([L, d] each).
 
@@ -136,9 +143,14 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
     ``head_map[eta]`` names the head whose Q / K columns give head eta's
     scores (V and the output stay head eta's columns).
 
+    Context-similarity bias ([WeChat] §2.2.3): ``score_bias`` [L, H] is added
+    to the scaled scores, s_j = Q_eta . K_{j,eta} * scale + b[j, eta], before
+    the softmax or the ReLU.
+
     Returns (a [d], cnt [H], amb [H]) where ``amb`` counts the scores whose
     sign an fp32 evaluation of the same operands could flip:
-    |s_j| <= d_h * 2^-23 * scale * sum_k |Q_k K_jk|.
+    |s_j| <= d_h * 2^-23 * scale * sum_k |Q_k K_jk|  (plus 2^-23 (|s| + |b|)
+    for the bias addition when a bias is given).
     """
     d = Q.shape[0]
     dh = d // H
@@ -154,6 +166,7 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
         cols = slice(eta * dh, (eta + 1) * dh)
         qk = eta if head_map is None else int(head_map[eta])
         qcols = slice(qk * dh, (qk + 1) * dh)
+        be = None if score_bias is None else np.asarray(score_bias, dtype=np.float64)[:, eta]
         if key_mask is None:
             Ke, Ve = K, V
         else:
@@ -161,8 +174,11 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
             if not sel.any():
                 continue                      # no visible key: output 0
             Ke, Ve = K[sel], V[sel]
+            be = None if be is None else be[sel]
         q = Q[qcols]
         s = (Ke[:, qcols] @ q) * scale
+        if be is not None:
+            s = s + be
         if score == "softmax":
             p = np.exp(s - s.max())
             a[cols] = (p @ Ve[:, cols]) / p.sum()
@@ -171,6 +187,8 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
             a[cols] = w @ Ve[:, cols]
             cnt[eta] = int(np.count_nonzero(s > 0.0))
             bound = dh * 2.0 ** -23 * (np.abs(Ke[:, qcols]) @ np.abs(q)) * scale
+            if be is not None:
+                bound = bound + 2.0 ** -23 * (np.abs(s - be) + np.abs(be))
             amb[eta] = int(np.count_nonzero(np.abs(s) <= bound))
         else:
             raise ValueError(score)
@@ -178,14 +196,15 @@ def attention_target(Q: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score:
 
 
 def attention_core(Qs: np.ndarray, K: np.ndarray, V: np.ndarray, H: int, score: str,
-                   scale: Optional[float] = None, key_mask=None, head_map=None):
+                   scale: Optional[float] = None, key_mask=None, head_map=None, score_bias=None):
     """Every target of one user: rows of ``Qs`` handled one at a time."""
     m, d = Qs.shape
     attn = np.zeros((m, d))
     cnt = np.zeros((m, H), dtype=np.int64)
     amb = np.zeros((m, H), dtype=np.int64)
     for t in range(m):
-        attn[t], cnt[t], amb[t] = attention_target(Qs[t], K, V, H, score, scale, key_mask, head_map)
+        attn[t], cnt[t], amb[t] = attention_target(Qs[t], K, V, H, score, scale, key_mask, head_map,
+                                                   score_bias)
     return attn, cnt, amb
 
 
@@ -268,7 +287,7 @@ def encode_history(X: np.ndarray, lw: dict, kv_ln: bool, encoder: str = "swiglu"
 
 def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=None, wz=None,
             tgt_ids=None, q0=None, users=None, want=("z", "o", "attn", "active", "q"), hy=None,
-            key_mask=None, head_map=None):
+            key_mask=None, head_map=None, score_bias=None):
     """The STCA forward for the users in ``users`` (default: all).
 
     cfg: dict with d, H, M, score ("softmax"|"relu"), qmode ("fusion"|"linear"),
@@ -299,7 +318,8 @@ def forward(cfg: dict, hist_offsets, hist_ids, tgt_offsets, rows_f64, layers, z=
         KV = [encode_history(X, layers[i], cfg["kv_ln"], cfg.get("encoder", "swiglu"), cfg.get("l_short", 0), H)
               for i in range(M)]
         km = None if key_mask is None else np.asarray(key_mask)[ho[u]:ho[u + 1]]
-        cm = dict(key_mask=km, head_map=head_map)
+        sb = None if score_bias is None else np.asarray(score_bias, dtype=np.float64)[ho[u]:ho[u + 1]]
+        cm = dict(key_mask=km, head_map=head_map, score_bias=sb)
         if qmode == "hyformer":
             t0, t1 = int(to[u]), int(to[u + 1])
             F = hy["ns"][u]
@@ -363,7 +383,17 @@ def forward_problem(p, users=None):
     if sp.qmode == "hyformer":
         hy = {"ns": stored_to_f64(p.extra["ns"]),
               "qgen": {k: stored_to_f64(v) for k, v in p.extra["qgen"].items()}}
+    def rows(ids):
+        # an id outside [0, table_rows) reads a zero row (the boundary's
+        # convention for invalid ids; the backward oracle's too)
+        ids = np.asarray(ids, dtype=np.int64)
+        out = np.zeros((len(ids), sp.d))
+        ok = (ids >= 0) & (ids < sp.table_rows)
+        if ok.any():
+            out[ok] = stored_to_f64(p.rows(ids[ok]))
+        return out
     return forward(cfg, p.hist_offsets, p.hist_ids, p.tgt_offsets,
-                   lambda ids: stored_to_f64(p.rows(ids)), layers, z, wz,
+                   rows, layers, z, wz,
                    tgt_ids=p.tgt_ids, q0=stored_to_f64(p.q0), users=users, hy=hy,
-                   key_mask=p.extra.get("key_mask"), head_map=p.extra.get("head_map"))
+                   key_mask=p.extra.get("key_mask"), head_map=p.extra.get("head_map"),
+                   score_bias=p.extra.get("score_bias"))

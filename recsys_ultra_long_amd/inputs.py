@@ -25,6 +25,8 @@ Distributions (readings of the workload descriptions, restated in the design doc):
   alpha = 1/4 for the training workload, whose mean length L_max / 5 = 2K is
   the training length the reading notes give for 10K inference);
 * the upstream gradient of z for the backward: i.i.d. N(0, 1);
+* context-similarity score bias (Cross-Mask page): i.i.d. N(0, 0.5^2) per
+  history item and head;
 * HyFormer query mode: n_ns non-sequence feature tokens per user i.i.d.
   N(0, 0.02^2) like table rows; the query-generation FFNs (input
   (n_ns + 1) d) and the per-token boosting FFNs i.i.d. N(0, 1/fan_in), drawn
@@ -160,6 +162,14 @@ def cross_mask(sp: Spec, n_hist: int, masked_heads, keep: float = 0.5, seed: int
         off = g.random(n_hist) >= keep
         m[off] &= ~np.uint64(1 << h)
     return m.astype(np.uint32)
+
+
+def score_bias(sp: Spec, n_hist: int, std: float = 0.5, seed: int = 0) -> np.ndarray:
+    """Seeded context-similarity score bias [n_hist, H] (float32), i.i.d.
+    N(0, std^2): a stand-in for the per-item, per-head similarity between an
+    item's context and the request's, which the pages name but do not define."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([sp.seed, 0x4249, seed])))
+    return (g.standard_normal((n_hist, sp.H), dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
 def upstream_grad(sp: Spec, n_tgt: int, seed: int = 0) -> np.ndarray:
@@ -395,4 +405,6 @@ def subset_users(p: Problem, users) -> Problem:
                    p.table, p.layers, p.z, p.wz,
                    {**p.extra, **({"ns": p.extra["ns"][users]} if "ns" in p.extra else {}),
                     **({"key_mask": np.concatenate([p.extra["key_mask"][ho[u]:ho[u + 1]] for u in users])
-                        .astype(np.uint32)} if "key_mask" in p.extra else {})})
+                        .astype(np.uint32)} if "key_mask" in p.extra else {}),
+                    **({"score_bias": np.concatenate([p.extra["score_bias"][ho[u]:ho[u + 1]] for u in users])
+                        .astype(np.float32)} if "score_bias" in p.extra else {})})

@@ -141,6 +141,118 @@ def test_relu_constructed_keys():                                 # P7
     assert cnt0[0] == 0
 
 
+# ----------------------------------------------------------------- ambiguity band
+# The bit-exact active-count contract is stated on shared operands: where a
+# score lies so close to zero that an fp32 evaluation of the same d_h-term
+# dot product could give it the other sign, the count may differ.  The
+# oracle reports those keys (``amb``) with the bound
+#     |s| <= d_h 2^-23 scale sum_k |Q_k K_k|,
+# twice the classical forward-error bound of a recursively summed dot
+# product, gamma_n sum |x_k y_k| with gamma_n = n u / (1 - n u) and
+# u = 2^-24 for fp32 round to nearest (Higham, "Accuracy and Stability of
+# Numerical Algorithms", section 3.1); the factor two covers any summation
+# order and fused or unfused products.
+
+
+def _fp32_scores(q, k):
+    """q.k in float32 arithmetic: sequential, reversed, pairwise, blocked by 8."""
+    q32, k32 = q.astype(np.float32), k.astype(np.float32)
+    p = q32 * k32
+    out = []
+    for order in (p, p[::-1]):
+        acc = np.float32(0)
+        for x in order:
+            acc = np.float32(acc + x)
+        out.append(float(acc))
+    v = p.copy()
+    while len(v) > 1:
+        if len(v) % 2:
+            v = np.append(v, np.float32(0))
+        v = (v[0::2] + v[1::2]).astype(np.float32)
+    out.append(float(v[0]))
+    out.append(float(np.float32(sum(np.float32(p[i:i + 8].sum(dtype=np.float32)) for i in range(0, len(p), 8)))))
+    return out
+
+
+def _amb_case(dh, s_over_bound, seed):
+    """One head of width dh, one key whose exact score is s_over_bound times
+    the oracle's ambiguity bound."""
+    g = rng(seed)
+    q = g.normal(size=dh)
+    k = g.normal(size=dh)
+    k -= (k @ q) / (q @ q) * q          # exactly orthogonal up to float64 rounding
+    scale = 1.0 / math.sqrt(dh)
+    # add t q so that s = t |q|^2 scale; the bound grows with |k| only slowly
+    for _ in range(50):
+        bound = dh * 2.0 ** -23 * scale * (np.abs(q) @ np.abs(k))
+        t = s_over_bound * bound / ((q @ q) * scale) - (k @ q) / (q @ q)
+        k = k + t * q
+    return q, k
+
+
+@pytest.mark.parametrize("dh", [32, 64])
+def test_amb_constant(dh):
+    """A key just inside the bound is ambiguous, one just outside is not, for
+    either sign: this fixes the constant (a doubled or halved bound fails)."""
+    for i, (r, want) in enumerate([(0.9, 1), (1.1, 0), (-0.9, 1), (-1.1, 0), (0.55, 1), (1.9, 0)]):
+        q, k = _amb_case(dh, r, seed=31 * dh + i)
+        _, cnt, amb = O.attention_target(q, k[None, :], np.ones((1, dh)), 1, "relu")
+        assert amb[0] == want, (r, amb)
+        assert cnt[0] == (1 if r > 0 else 0)
+
+
+def test_amb_exact_zero_score():
+    q = np.zeros(32)
+    q[0] = 1.0
+    k = np.zeros(32)
+    k[1] = 3.0                                   # s = 0 exactly, bound = 0
+    _, cnt, amb = O.attention_target(q, k[None, :], np.ones((1, 32)), 1, "relu")
+    assert cnt[0] == 0 and amb[0] == 1
+
+
+def test_amb_far_scores_are_exact():
+    g = rng(5)
+    d, H, L = 64, 2, 200
+    Q = g.normal(size=d)
+    K = g.normal(size=(L, d))
+    _, cnt, amb = O.attention_target(Q, K, np.ones((L, d)), H, "relu")
+    dh = d // H
+    s = np.stack([K[:, h * dh:(h + 1) * dh] @ Q[h * dh:(h + 1) * dh] for h in range(H)], 1) / math.sqrt(dh)
+    bound = np.stack([np.abs(K[:, h * dh:(h + 1) * dh]) @ np.abs(Q[h * dh:(h + 1) * dh]) for h in range(H)], 1) \
+        * dh * 2.0 ** -23 / math.sqrt(dh)
+    assert np.all(np.abs(s) > 10 * bound)        # random scores sit far from the band
+    assert np.all(amb == 0) and np.array_equal(cnt, (s > 0).sum(0))
+
+
+def test_amb_bounds_every_fp32_evaluation():
+    """For near-cancelling dot products (exact scores within a few bounds of
+    zero) every fp32 evaluation order stays within the bound of the exact
+    score, so a key outside the band keeps its sign under any of them."""
+    worst = 0.0
+    for seed in range(400):
+        dh = (32, 64)[seed % 2]
+        q, k = _amb_case(dh, rng(1000 + seed).uniform(-3, 3), seed=2000 + seed)
+        s = q @ k                                  # scale 1: the bound's own units
+        b = dh * 2.0 ** -23 * (np.abs(q) @ np.abs(k))
+        for s32 in _fp32_scores(q, k):
+            worst = max(worst, abs(s32 - s) / b)
+    assert worst <= 1.0, worst
+    assert worst > 1e-3                          # the cases do exercise rounding
+
+
+def test_amb_flags_a_key_fp32_gets_wrong():
+    """A key whose exact score is positive but which a sequential fp32
+    evaluation rounds to zero is counted active by the oracle and marked
+    ambiguous, so the GPU's count may differ by it."""
+    q = np.zeros(32)
+    q[:3] = 1.0
+    k = np.zeros(32)
+    k[:3] = [1.0, 2.0 ** -25, -1.0]
+    assert min(abs(s) for s in _fp32_scores(q, k)[:1]) == 0.0   # 1 + 2^-25 rounds to 1
+    _, cnt, amb = O.attention_target(q, k[None, :], np.ones((1, 32)), 1, "relu")
+    assert cnt[0] == 1 and amb[0] == 1
+
+
 def test_empty_history():
     a, cnt, amb = O.attention_target(np.ones(8), np.zeros((0, 8)), np.zeros((0, 8)), 2, "softmax")
     assert np.all(a == 0) and np.all(cnt == 0)
