@@ -18,7 +18,9 @@
  *   [WeChat]   "视频号推荐超长序列技术演进：从端到端到 Cross-Mask Transformer":
  *              §1.1 显存优化 (lookup fused with target attention, no [B,L,D]
  *              KV tensor), §1.2 (ReLU-activated target attention, active keys
- *              are those with score > 0).
+ *              are those with score > 0), §2.2.3 (context similarity added
+ *              to the target-attention score), §3.2-3.3 (Cross-Mask masks and
+ *              shared attention maps).
  *   [HyFormer] "HyFormer：重新审视序列建模和特征交互在 CTR 预测中的作用":
  *              eq. (7)-(9) and (16) (per-layer SwiGLU encoding without LN,
  *              multi-query cross attention), §3.7 (one query set per sequence).
@@ -155,6 +157,17 @@ typedef struct {
                                    (its feature-domain condition holds, e.g. "action =
                                    complete"); softmax and ReLU then run over the visible
                                    items only, a head with none gives 0.  Staged bf16 only */
+  const float *score_bias;      /* [n_hist, H] fp32 or NULL: context-similarity score bias
+                                   ([WeChat] §2.2.3, 上下文利用: the context similarity of two
+                                   videos fine-tunes the target-attention score; the page
+                                   gives no formula, the values are the caller's).  Every
+                                   layer's score of item j and head h becomes
+                                   s_j = q . k_j / sqrt(d_h) + score_bias[j, h] for every
+                                   target of the user, before the softmax or the ReLU (the
+                                   active count is then #{j : s_j > 0}).  With a head map,
+                                   head h adds its own bias column.  Staged bf16 only, not
+                                   with STCA_ENC_LONGER; read once per call (a blocked copy
+                                   in the workspace) */
 } stca_batch;
 
 /* SwiGLU FFN d -> h -> d, optionally followed by LayerNorm (eps 1e-5):
@@ -260,7 +273,8 @@ int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_wei
  *   s_j = q_t[eta] . k_j[eta]                (q rows already carry 1/sqrt(d_h))
  *   softmax: attn_t[eta] = sum_j exp(s_j - max) v_j[eta] / sum_j exp(s_j - max)
  *   relu:    attn_t[eta] = sum_j max(0, s_j) v_j[eta], active = #{j : s_j > 0}
- * over the user's history rows j.  An empty history gives zeros. */
+ * over the user's history rows j (plus score_bias[j, eta] when given).  An
+ * empty history gives zeros. */
 typedef struct {
   int32_t B, d, H;          /* host                                                  */
   int32_t dtype;            /* STCA_F32 / STCA_BF16 for q, k, v                       */
@@ -277,6 +291,8 @@ typedef struct {
   int32_t *dev_status;      /* optional */
   const uint32_t *key_mask; /* [n_hist] or NULL, as stca_batch.key_mask (bf16 only) */
   const int32_t *head_map;  /* host [H] or NULL, as stca_config.head_map (bf16 only) */
+  const float *score_bias;  /* [n_hist, H] or NULL, as stca_batch.score_bias: added to
+                               s_j (bf16 only) */
 } stca_attn_args;
 
 int stca_attention_workspace_size(const stca_attn_args *a, size_t *bytes);
@@ -293,8 +309,12 @@ int stca_attention(const stca_attn_args *a, void *workspace, size_t ws_bytes, vo
  * of stca_forward (recomputed inside the call from the same inputs: nothing is
  * kept between calls).  Supported: bf16, STCA_Q_FUSION, d_h 32 or 64,
  * max_tgt_per_user <= 64, softmax or ReLU scores, with or without the history
- * and z LayerNorms (cfg->path and STCA_FLAG_DEDUP are ignored: the recompute
- * runs the staged path).
+ * and z LayerNorms.  cfg->path is ignored (the recompute runs the staged path).
+ * STCA_FLAG_DEDUP is honoured: the recompute encodes each distinct history id
+ * once, and the history side's backward runs once per distinct id on the sum
+ * of its items' dK | dV (fixed item order); grads->d_hist (a per-item output)
+ * is then rejected with STCA_ERR_UNSUPPORTED.  Cross-Mask masks and maps and
+ * the score bias are rejected (STCA_ERR_UNSUPPORTED).
  *
  * Weight gradients are fp32, shaped like the weights ([in, out] row-major), and
  * ACCUMULATED (+=) into the caller's buffers: zero them for a fresh step.  The

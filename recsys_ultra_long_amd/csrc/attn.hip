@@ -78,12 +78,16 @@ DEV int xcd_order(int b, int n) { return (n & 7) ? b : (b & 7) * (n >> 3) + (b >
 // read row-major (a.vrows) and written transposed into a wave-private LDS
 // tile, from which the V^T fragments are read.
 //
-// MASK (Cross-Mask vertical masks, [WeChat] §3.2): each lane also loads the
-// mask word of key lane % 32 of a block (in the same pipeline stage as K/V),
-// and one ballot turns the head's bit of the 32 words into the block's
-// visibility word.  A head map (a.has_map) takes head h's scores from the
+// MASK (Cross-Mask vertical masks, [WeChat] §3.2, and the context-similarity
+// score bias, [WeChat] §2.2.3): each lane also loads the mask word of key
+// lane % 32 of a block (in the same pipeline stage as K/V; all ones without
+// a mask), and one ballot turns the head's bit of the 32 words into the
+// block's visibility word; with a bias it loads the bias of its eight keys of
+// the block (two 16-byte loads from the blocked copy) and the block step adds
+// them to the scores.  A head map (a.has_map) takes head h's scores from the
 // Q / K columns of head a.head_map[h] ([WeChat] §3.3.1: heads sharing one
-// attention map under different masks); V and the output stay head h's.
+// attention map under different masks); V, the bias and the output stay
+// head h's.
 //
 // SHARE (two to four target groups): the units are (user, head) x 128 keys,
 // each wave serves one group over every block, and a block's K/V go from HBM
@@ -330,22 +334,42 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int t = 0; t < DT; ++t) out[t] = raw[t];
         }
       };
-      // MASK: the mask word of key lane % 32 of block b (0 past the history)
+      // MASK: the mask word of key lane % 32 of block b (0 past the history,
+      // all ones without a mask)
       auto load_mask = [&](int b) -> uint32_t {
         const int key = lane & 31, j = (b - P.pblk[u]) * 32 + key;
-        return j < L ? a.key_mask[tok0 + (int64_t)b * 32 + key] : 0u;
+        if (j >= L) return 0u;
+        return a.key_mask ? a.key_mask[tok0 + (int64_t)b * 32 + key] : 0xffffffffu;
+      };
+      // MASK: this lane's eight keys' bias of block b for head h (0 without a bias)
+      auto load_bias = [&](int b, f32x4 (&bb)[2]) {
+        if (a.bias_blk) {
+          const float *src = a.bias_blk + ((int64_t)b * H + h) * 32 + 8 * g16;
+          bb[0] = ldg4(src);
+          bb[1] = ldg4(src + 4);
+        } else {
+          bb[0] = bb[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       };
       uint32_t mk = 0, mk1 = 0;
+      f32x4 bz[2], bz1[2];
+      bz[0] = bz[1] = bz1[0] = bz1[1] = f32x4{0.f, 0.f, 0.f, 0.f};
       // two blocks of this wave in flight ahead of the one being used: the
       // loads, not the arithmetic, set the pace once the block step is lean
       bf16x8 k1[2][KS], v1[DT];
       if (b0 + w < b1) {
         load_kv(b0 + w, kf, vf);
-        if (MASK) mk = load_mask(b0 + w);
+        if (MASK) {
+          mk = load_mask(b0 + w);
+          load_bias(b0 + w, bz);
+        }
       }
       if (b0 + w + 4 < b1) {
         load_kv(b0 + w + 4, k1, v1);
-        if (MASK) mk1 = load_mask(b0 + w + 4);
+        if (MASK) {
+          mk1 = load_mask(b0 + w + 4);
+          load_bias(b0 + w + 4, bz1);
+        }
       }
       if (IND && b0 + w + 8 < b1) load_uids(b0 + w + 8, U8);
       // one block of this wave; FULL: every key of the block is visible
@@ -356,9 +380,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         // uids first: waiting for them later does not wait for the rows below
         if (IND && b + 12 < b1) load_uids(b + 12, U12);
         uint32_t mk2 = 0;
+        f32x4 bz2[2];
+        bz2[0] = bz2[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (b + 8 < b1) {
           load_kv(b + 8, k2, v2);
-          if (MASK) mk2 = load_mask(b + 8);
+          if (MASK) {
+            mk2 = load_mask(b + 8);
+            load_bias(b + 8, bz2);
+          }
         }
         if (IND) U8 = U12;
         __builtin_amdgcn_sched_barrier(0);
@@ -367,9 +396,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         v_fragments(vf, vuse);
         uint32_t kvis = 0xffffffffu;
         if (MASK) kvis = (uint32_t)__ballot((mk >> h) & 1u);  // lanes 0..31: keys 0..31
-        attn_block<DH, NT, SCORE, FULL>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane);
+        attn_block<DH, NT, SCORE, FULL, false, MASK>(st, kf, vuse, L - (b - P.pblk[u]) * 32, kvis, lane, bz);
         mk = mk1;
         mk1 = mk2;
+        if constexpr (MASK) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            bz[i] = bz1[i];
+            bz1[i] = bz2[i];
+          }
+        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -663,6 +699,20 @@ __global__ void relayout_kernel(const T *k, const T *v, T *kb, T *vb, Plan P, in
   }
 }
 
+// One workgroup per padded block: out[(b * H + h) * 32 + key] = the caller's
+// bias[token, h] of the block's key, 0 on padding rows.
+__global__ __launch_bounds__(256) void bias_relayout_kernel(const float *bias, float *out, Plan P, int B, int H) {
+  const int b = blockIdx.x;
+  if (b >= P.pblk[B]) return;
+  const int u = upper_index(P.pblk, B, b);
+  const int L = P.hoff[u + 1] - P.hoff[u];
+  const int j0 = (b - P.pblk[u]) * 32;
+  for (int e = threadIdx.x; e < 32 * H; e += blockDim.x) {
+    const int h = e >> 5, key = e & 31;
+    const int64_t row = (int64_t)P.hoff[u] + j0 + key;
+    out[((int64_t)b * H + h) * 32 + key] = j0 + key < L ? bias[row * H + h] : 0.f;
+  }
+}
 
 template <typename K>
 int persistent_grid(K kernel, int threads, int64_t units) {
@@ -712,13 +762,14 @@ hipError_t launch_attn_partial(AttnArgs &a, hipStream_t s) {
     if (a.dh == 64) return a.score ? launch_bf16<64, 1, IND, MASK>(a, s) : launch_bf16<64, 0, IND, MASK>(a, s); \
     return hipErrorInvalidValue;                                                                            \
   }
+    const bool mod = a.key_mask || a.bias_blk;  // masks and / or a score bias
     if (a.tok2u) {
-      if (a.key_mask) SEL(true, true) else SEL(true, false)
+      if (mod) SEL(true, true) else SEL(true, false)
     }
-    if (a.key_mask) SEL(false, true) else SEL(false, false)
+    if (mod) SEL(false, true) else SEL(false, false)
 #undef SEL
   }
-  if (a.key_mask || a.has_map) return hipErrorInvalidValue;  // fp32: no Cross-Mask
+  if (a.key_mask || a.has_map || a.bias_blk) return hipErrorInvalidValue;  // fp32: no Cross-Mask, no bias
 #define GO(DH, SC)                                                   \
   {                                                                  \
     auto k = attn_f32_kernel<DH, SC>;                                \
@@ -743,6 +794,13 @@ hipError_t launch_attn_merge(const AttnArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   if (a.score) hipLaunchKernelGGL(merge_kernel<1>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(merge_kernel<0>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_relayout(const float *bias, float *out, const Plan &plan, int B, int64_t max_blocks, int H,
+                                hipStream_t s) {
+  if (max_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bias_relayout_kernel, dim3((unsigned)max_blocks), dim3(256), 0, s, bias, out, plan, B, H);
   return hipGetLastError();
 }
 

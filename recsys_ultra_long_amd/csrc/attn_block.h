@@ -89,10 +89,12 @@ constexpr float kAttnLazy = 8.0f / kAttnLog2e;
 // masking is then left out; left in, the compiler turns it into selects on
 // every score of every block).  SWAP: the block max crosses lanes with lane
 // swaps (VALU) instead of LDS permutes, for launches bound by the block
-// step's latency rather than by memory.
-template <int DH, int NT, int SCORE, bool FULL = false, bool SWAP = false>
+// step's latency rather than by memory.  BIAS: bias[kt][r] is added to the
+// score of key 8g + 4kt + r (this lane's keys) for every target before the
+// softmax or the ReLU (the context-similarity bias of [WeChat] §2.2.3).
+template <int DH, int NT, int SCORE, bool FULL = false, bool SWAP = false, bool BIAS = false>
 DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const bf16x8 (&vf)[DH / 16],
-                    int nvalid, uint32_t kvis, int lane) {
+                    int nvalid, uint32_t kvis, int lane, const f32x4 *bias = nullptr) {
   constexpr int KS = DH / 32, DT = DH / 16;
   const int g = lane >> 4;
   // uniform: only a user's last block is partial, and masks are per block
@@ -106,6 +108,7 @@ DEV void attn_block(AttnState<DH, NT> &s, const bf16x8 (&kf)[2][DH / 32], const 
       st[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) st[kt][n] = mfma16(kf[kt][k], s.qf[n][k], st[kt][n]);
+      if constexpr (BIAS) st[kt][n] += bias[kt];
     }
   bf16x8 pk[NT];
   if (SCORE == 0) {

@@ -100,6 +100,7 @@ struct Layout {
   size_t hy_mp = 0, hy_g = 0, hy_h13 = 0, hy_gg = 0, hy_out = 0, hy_qcat = 0, hy_qmix = 0, hy_o32 = 0;
   size_t hy_pool = 0, hy_part = 0;
   int64_t hy_part_floats = 0;
+  size_t bias = 0;         // score bias, blocked like K (0 = none)
   std::vector<PrepLayer> pl;
   size_t z_w1 = 0, z_w3 = 0, z_w2 = 0, wz = 0, prep_elems = 0;
 };
@@ -189,14 +190,19 @@ int validate_map(const int32_t *map, int H) {
   return STCA_OK;
 }
 
-// Cross-Mask masks and maps: the staged bf16 attention implements them
+// Cross-Mask masks and maps, and the score bias: the staged bf16 attention
+// implements them
 int validate_cross_mask(const stca_config *c, const stca_batch *b) {
-  const bool any = c->head_map || (b && b->key_mask);
+  const bool any = c->head_map || (b && (b->key_mask || b->score_bias));
   if (!any) return STCA_OK;
-  if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need bf16");
-  if (c->path != STCA_PATH_STAGED) return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need the staged path");
+  if (c->dtype != STCA_BF16) return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map / score_bias need bf16");
+  if (c->path != STCA_PATH_STAGED)
+    return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map / score_bias need the staged path");
   if (b && b->key_mask && ((reinterpret_cast<uintptr_t>(b->key_mask) & 15u)))
     return fail(STCA_ERR_INVALID_ARG, "key_mask not 16-byte aligned");
+  if (b && b->score_bias && ((reinterpret_cast<uintptr_t>(b->score_bias) & 15u)))
+    return fail(STCA_ERR_INVALID_ARG, "score_bias not 16-byte aligned");
+  if (b && b->score_bias && c->H > 16) return fail(STCA_ERR_UNSUPPORTED, "score_bias supports at most 16 heads");
   return validate_map(c->head_map, c->H);
 }
 
@@ -247,6 +253,8 @@ int validate_batch(const stca_config *c, const stca_batch *b) {
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "batch pointer %p not 16-byte aligned", p);
   if (c->encoder == STCA_ENC_LONGER && b->key_mask)
     return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is not available with Cross-Mask masks");
+  if (c->encoder == STCA_ENC_LONGER && b->score_bias)
+    return fail(STCA_ERR_UNSUPPORTED, "STCA_ENC_LONGER is not available with a score bias");
   int r = validate_dedup(c);
   if (r) return r;
   if ((r = validate_cross_mask(c, b))) return r;
@@ -383,6 +391,7 @@ Layout make_layout(const stca_config *c, const stca_batch *b) {
   // staged: blocked K/V of every layer; fused: none (the point of that path)
   L.kv_layer = L.fused ? 0 : (size_t)L.max_blocks * 32 * d * L.esize;  // K or V of one layer
   L.kv = cv.take(2 * L.kv_layer * c->M);
+  if (b->score_bias && b->n_hist > 0) L.bias = cv.take((size_t)L.max_blocks * c->H * 32 * sizeof(float));
   size_t np = partial_slots(c->B, c->H, b->max_tgt_per_user);
   if (L.fused)  // one slot per (workgroup, user): independent of the history length
     np = (size_t)(L.fused_grid + c->B) * c->H * b->max_tgt_per_user;
@@ -482,6 +491,7 @@ void longer_inner(const stca_config *c, const stca_batch *b, const LongerLayout 
   b2.n_hist = LL.nS;
   b2.table = at<void>(ws, LL.htab);
   b2.key_mask = nullptr;
+  b2.score_bias = nullptr;
 }
 
 }  // namespace
@@ -669,6 +679,10 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
       e = launch_padded_ids(plan, B, batch->hist_ids, cfg->table_rows, L.max_blocks, out->dev_status, s);
       if (e) return hip_fail(e, "padded ids");
     }
+    if (L.bias) {  // the score bias in the blocked layout the attention reads
+      e = launch_bias_relayout(batch->score_bias, at<float>(ws, L.bias), plan, B, L.max_blocks, H, s);
+      if (e) return hip_fail(e, "score bias relayout");
+    }
   }
   if ((e = rec(1))) return hip_fail(e, "stage event");
   if (B == 0 || (batch->n_hist == 0 && T == 0)) return STCA_OK;
@@ -750,6 +764,7 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
     at_.active = out->active ? out->active + (size_t)i * T * H : nullptr;
     at_.lse = (out->lse && cfg->score == STCA_SCORE_SOFTMAX) ? out->lse + (size_t)i * T * H : nullptr;
     at_.key_mask = batch->key_mask;
+    at_.bias_blk = L.bias ? at<float>(ws, L.bias) : nullptr;
     if (cfg->head_map) {
       at_.has_map = 1;
       for (int hh = 0; hh < H; ++hh) at_.head_map[hh] = cfg->head_map[hh];
@@ -1320,18 +1335,20 @@ static int attn_validate(const stca_attn_args *a) {
   if (a->B > 0 && (!a->hist_offsets || !a->tgt_offsets)) return fail(STCA_ERR_INVALID_ARG, "offsets NULL");
   if (a->n_tgt > 0 && (!a->q || !a->attn)) return fail(STCA_ERR_INVALID_ARG, "q / attn NULL");
   if (a->n_hist > 0 && (!a->k || !a->v)) return fail(STCA_ERR_INVALID_ARG, "k / v NULL");
-  const void *ptrs[] = {a->hist_offsets, a->tgt_offsets, a->q, a->k, a->v, a->attn, a->active, a->key_mask};
+  const void *ptrs[] = {a->hist_offsets, a->tgt_offsets, a->q, a->k, a->v, a->attn, a->active, a->key_mask,
+                        a->score_bias};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return fail(STCA_ERR_INVALID_ARG, "pointer %p not 16-byte aligned", p);
-  if ((a->key_mask || a->head_map) && a->dtype != STCA_BF16)
-    return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map need bf16");
+  if ((a->key_mask || a->head_map || a->score_bias) && a->dtype != STCA_BF16)
+    return fail(STCA_ERR_UNSUPPORTED, "key_mask / head_map / score_bias need bf16");
+  if (a->score_bias && a->H > 16) return fail(STCA_ERR_UNSUPPORTED, "score_bias supports at most 16 heads");
   return validate_map(a->head_map, a->H);
 }
 
 struct AttnLayout {
   int nb;
   int64_t mb, mc;
-  size_t plan, kv, kvl, ml, acc, cnt, total;
+  size_t plan, kv, kvl, ml, acc, cnt, bias, total;
 };
 
 static AttnLayout attn_layout(const stca_attn_args *a) {
@@ -1348,6 +1365,7 @@ static AttnLayout attn_layout(const stca_attn_args *a) {
   L.ml = cv.take(np * 2 * sizeof(float));
   L.acc = cv.take(np * (a->d / a->H) * sizeof(float));
   L.cnt = cv.take(np * sizeof(int));
+  L.bias = (a->score_bias && a->n_hist > 0) ? cv.take((size_t)L.mb * a->H * 32 * sizeof(float)) : 0;
   L.total = cv.off;
   return L;
 }
@@ -1384,6 +1402,10 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   if (a->n_hist > 0) {
     e = launch_kv_relayout(a->dtype, a->k, a->v, kv, kv + L.kvl, plan, a->B, L.mb, a->d, a->H, true, s);
     if (e) return hip_fail(e, "relayout");
+    if (L.bias) {
+      e = launch_bias_relayout(a->score_bias, at<float>(ws, L.bias), plan, a->B, L.mb, a->H, s);
+      if (e) return hip_fail(e, "score bias relayout");
+    }
   }
   AttnArgs at_;
   std::memset(&at_, 0, sizeof(at_));
@@ -1408,6 +1430,7 @@ int stca_attention(const stca_attn_args *a, void *ws, size_t ws_bytes, void *str
   at_.active = a->active;
   at_.B = a->B;
   at_.key_mask = a->key_mask;
+  at_.bias_blk = L.bias ? at<float>(ws, L.bias) : nullptr;
   if (a->head_map) {
     at_.has_map = 1;
     for (int hh = 0; hh < a->H; ++hh) at_.head_map[hh] = a->head_map[hh];

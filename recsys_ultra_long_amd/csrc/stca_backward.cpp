@@ -180,6 +180,7 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
     return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs the SwiGLU history encoder");
   if (c->head_map || b->key_mask)
     return api_error(STCA_ERR_UNSUPPORTED, "stca_backward does not take Cross-Mask key_mask / head_map");
+  if (b->score_bias) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward does not take a score bias");
   if (c->H <= 0 || c->d % c->H) return api_error(STCA_ERR_INVALID_ARG, "d %% H != 0");
   const int dh = c->d / c->H;
   if (dh != 32 && dh != 64) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward needs d_h 32 or 64 (got %d)", dh);

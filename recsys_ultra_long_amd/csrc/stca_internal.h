@@ -189,6 +189,10 @@ struct AttnArgs {
   const uint32_t *key_mask;
   int has_map;
   int head_map[16];
+  // Context-similarity score bias ([WeChat] §2.2.3), blocked like K:
+  // bias_blk[(b * H + h) * 32 + key] is added to the score of key `key` of
+  // padded block b for head h (0 on padding rows).  NULL: no bias.
+  const float *bias_blk;
 };
 
 // Partials + merge.  launch_attn_partial fills a.grid, which the merge reads.
@@ -291,6 +295,11 @@ hipError_t launch_expand_kv(const bf16_t *uk, const bf16_t *vrows, bf16_t *k, bf
 hipError_t launch_kv_relayout(int dtype, const void *k, const void *v, void *kbuf, void *vbuf,
                               Plan plan, int B, int64_t max_blocks, int d, int H, bool to_blocked,
                               hipStream_t s);
+
+// Caller's score bias [n_hist, H] -> the blocked layout of AttnArgs.bias_blk
+// (max_blocks * H * 32 floats).
+hipError_t launch_bias_relayout(const float *bias, float *out, const Plan &plan, int B, int64_t max_blocks, int H,
+                                hipStream_t s);
 
 hipError_t launch_copy_rows(int dtype, const void *src, int lds, void *dst, int ldd,
                             int64_t rows, int cols, hipStream_t s);

@@ -46,7 +46,8 @@ class Config(C.Structure):
 class Batch(C.Structure):
     _fields_ = [("hist_offsets", _vp), ("hist_ids", _vp), ("tgt_offsets", _vp), ("tgt_ids", _vp),
                 ("q0", _vp), ("table", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
-                ("max_tgt_per_user", C.c_int32), ("ns_feats", _vp), ("key_mask", _vp)]
+                ("max_tgt_per_user", C.c_int32), ("ns_feats", _vp), ("key_mask", _vp),
+                ("score_bias", _vp)]
 
 
 class Ffn(C.Structure):
@@ -93,7 +94,7 @@ class AttnArgs(C.Structure):
                 ("tgt_offsets", _vp), ("n_hist", C.c_int64), ("n_tgt", C.c_int64),
                 ("max_tgt_per_user", C.c_int32), ("q", _vp), ("k", _vp), ("v", _vp),
                 ("attn", _vp), ("active", _vp), ("dev_status", _vp), ("key_mask", _vp),
-                ("head_map", C.POINTER(C.c_int32))]
+                ("head_map", C.POINTER(C.c_int32)), ("score_bias", _vp)]
 
 
 _LIB = None
@@ -176,6 +177,7 @@ class DeviceProblem:
     qgen: Optional[dict] = None
     key_mask: object = None   # Cross-Mask: [n_hist] visibility bits (int32 view of uint32)
     head_map: object = None   # Cross-Mask: ctypes int32 array [H] (kept alive here)
+    score_bias: object = None  # context-similarity score bias [n_hist, H] fp32
 
 
 def _dev(a, device):
@@ -220,7 +222,9 @@ def upload(p, device="cuda", table=None, path="staged", chunk_keys=0, dedup=Fals
                          table, [conv(l) for l in p.layers], conv(p.z), _dev(p.wz, device),
                          p.n_hist, p.n_tgt, max(1, int(m.max()) if len(m) else 1),
                          _dev(p.extra.get("ns"), device), conv(p.extra.get("qgen")),
-                         _dev(None if km is None else np.asarray(km, np.uint32).view(np.int32), device), hmap)
+                         _dev(None if km is None else np.asarray(km, np.uint32).view(np.int32), device), hmap,
+                         _dev(None if p.extra.get("score_bias") is None
+                              else np.asarray(p.extra["score_bias"], np.float32), device))
 
 
 def _ffn(f) -> Ffn:
@@ -242,7 +246,7 @@ def _structs(dp: DeviceProblem):
     w = Weights(layers, _ffn(dp.z), _ptr(dp.wz), _ptr(qg.get("w1")), _ptr(qg.get("w3")), _ptr(qg.get("w2")))
     b = Batch(_ptr(dp.hist_offsets), _ptr(dp.hist_ids), _ptr(dp.tgt_offsets), _ptr(dp.tgt_ids),
               _ptr(dp.q0), _ptr(dp.table), dp.n_hist, dp.n_tgt, dp.max_tgt, _ptr(dp.ns),
-              _ptr(dp.key_mask))
+              _ptr(dp.key_mask), _ptr(dp.score_bias))
     return b, w, layers
 
 
@@ -439,7 +443,8 @@ def forward(dp: DeviceProblem, want=("o", "attn", "active"), dumps=()) -> dict:
 
 
 def attention(q, k, v, hist_offsets, tgt_offsets, H: int, score: str = "softmax",
-              max_tgt: Optional[int] = None, chunk_keys: int = 0, key_mask=None, head_map=None):
+              max_tgt: Optional[int] = None, chunk_keys: int = 0, key_mask=None, head_map=None,
+              score_bias=None):
     """The attention core alone (``stca_attention``) on device tensors.
     q: [T, d] (already scaled by 1/sqrt(d_h)), k/v: [n_hist, d]; fp32, or
     bf16 bits as int16.  Returns (attn fp32 [T, d], active int32 [T, H] or None,
@@ -458,7 +463,7 @@ def attention(q, k, v, hist_offsets, tgt_offsets, H: int, score: str = "softmax"
                  hist_offsets=_ptr(hist_offsets), tgt_offsets=_ptr(tgt_offsets),
                  n_hist=k.shape[0], n_tgt=T, max_tgt_per_user=max_tgt, q=_ptr(q), k=_ptr(k),
                  v=_ptr(v), attn=_ptr(attn), active=_ptr(active), dev_status=_ptr(status),
-                 key_mask=_ptr(key_mask))
+                 key_mask=_ptr(key_mask), score_bias=_ptr(score_bias))
     hmap = None
     if head_map is not None:
         hmap = (C.c_int32 * len(head_map))(*[int(x) for x in head_map])

@@ -60,9 +60,10 @@ def _ffn(x, w, ln, rp):
     return O.layer_norm(y, w["ln_g"], w["ln_b"]) if ln else y
 
 
-def _attention(Q, K, V, H, score, rp, at):
+def _attention(Q, K, V, H, score, rp, at, key_mask=None, head_map=None, bias=None):
     """One target, every head: the oracle's two-pass formulas, evaluated in
-    the float type ``at``, with the value product's weights rounded at ``w``."""
+    the float type ``at``, with the value product's weights rounded at ``w``
+    (Cross-Mask masks and maps and the score bias as in the oracle)."""
     Q, K, V = Q.astype(at), K.astype(at), V.astype(at)
     d = Q.shape[0]
     dh = d // H
@@ -71,12 +72,24 @@ def _attention(Q, K, V, H, score, rp, at):
         return a
     for h in range(H):
         c = slice(h * dh, (h + 1) * dh)
-        s = K[:, c] @ Q[c]
+        hq = h if head_map is None else int(head_map[h])
+        cq = slice(hq * dh, (hq + 1) * dh)
+        Kh, Vh = K, V
+        bh = None if bias is None else bias[:, h].astype(at)
+        if key_mask is not None:
+            sel = ((np.asarray(key_mask, dtype=np.int64) >> h) & 1).astype(bool)
+            if not sel.any():
+                continue
+            Kh, Vh = K[sel], V[sel]
+            bh = None if bh is None else bh[sel]
+        s = Kh[:, cq] @ Q[cq]
+        if bh is not None:
+            s = s + bh
         if score == "softmax":
             p = rp("w", np.exp(s - s.max())).astype(at)
-            a[c] = (p @ V[:, c]) / p.sum()
+            a[c] = (p @ Vh[:, c]) / p.sum()
         else:
-            a[c] = rp("w", np.maximum(s, 0.0)).astype(at) @ V[:, c]
+            a[c] = rp("w", np.maximum(s, 0.0)).astype(at) @ Vh[:, c]
     return a
 
 
@@ -112,8 +125,11 @@ def perturbed_forward(p, precision: str = "bf16", points=ALL_POINTS, users=None,
     ho, to = p.hist_offsets.astype(np.int64), p.tgt_offsets.astype(np.int64)
     T = int(to[-1])
     out = {"z": np.zeros((T, d)), "o": np.zeros((M, T, d)), "attn": np.zeros((M, T, d))}
+    km_all, hmap, sb_all = p.extra.get("key_mask"), p.extra.get("head_map"), p.extra.get("score_bias")
     for u in (range(sp.B) if users is None else users):
         ids = p.hist_ids[ho[u]:ho[u + 1]]
+        km = None if km_all is None else np.asarray(km_all)[ho[u]:ho[u + 1]]
+        sb = None if sb_all is None else np.asarray(sb_all, np.float64)[ho[u]:ho[u + 1]]
         X = (O.stored_to_f64(p.rows(ids)) if len(ids) else np.zeros((0, d))).astype(ft)
         KV = []
         for i in range(M):
@@ -128,7 +144,7 @@ def perturbed_forward(p, precision: str = "bf16", points=ALL_POINTS, users=None,
             cat = []
             for i in range(M):
                 Q = rp("q", (q @ layers[i]["wq"]) * scale)
-                a = _attention(Q, KV[i][0], KV[i][1], H, sp.score, rp, at)
+                a = _attention(Q, KV[i][0], KV[i][1], H, sp.score, rp, at, km, hmap, sb)
                 o = rp("attn", a).astype(ft) @ layers[i]["wo"]
                 out["attn"][i, t], out["o"][i, t] = a, o
                 cat.append(rp("o", o))

@@ -317,6 +317,43 @@ def test_cross_mask_attention_and_backward_validation():
     assert r == stca.ERR_UNSUPPORTED and "Cross-Mask" in stca.last_error()
 
 
+@pytest.mark.parametrize("cover,bover,code", [
+    ({}, dict(score_bias=FAKE), stca.OK),
+    (dict(flags=stca.FLAG_KV_LN | stca.FLAG_DEDUP), dict(score_bias=FAKE, key_mask=FAKE), stca.OK),
+    (dict(path=1), dict(score_bias=FAKE), stca.ERR_UNSUPPORTED),                # fused path
+    (dict(dtype=stca.F32, d=64, H=2, hidden=64), dict(score_bias=FAKE), stca.ERR_UNSUPPORTED),
+    ({}, dict(score_bias=FAKE + 4), stca.ERR_INVALID_ARG),                      # misaligned
+    (dict(encoder=1, l_short=64), dict(score_bias=FAKE), stca.ERR_UNSUPPORTED),
+])
+def test_score_bias_validation(cover, bover, code):
+    r, n = ws_size(cfg(**cover), batch(**bover))
+    assert r == code, stca.last_error()
+    if code == stca.OK:
+        r0, n0 = ws_size(cfg(**cover), batch(**{k: v for k, v in bover.items() if k != "score_bias"}))
+        assert n > n0            # the blocked copy of the bias lives in the workspace
+    else:
+        assert "bias" in stca.last_error() or "LONGER" in stca.last_error()
+
+
+def test_score_bias_attention_and_backward_validation():
+    lib = stca.load()
+    a = stca.AttnArgs(B=2, d=256, H=8, dtype=stca.BF16, score=1, chunk_keys=0,
+                      hist_offsets=FAKE, tgt_offsets=FAKE, n_hist=100, n_tgt=4,
+                      max_tgt_per_user=2, q=FAKE, k=FAKE, v=FAKE, attn=FAKE, score_bias=FAKE)
+    n = C.c_size_t(0)
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.OK
+    a.score_bias = FAKE + 8
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.ERR_INVALID_ARG
+    a.score_bias = FAKE
+    a.dtype, a.d, a.H = stca.F32, 64, 2
+    assert lib.stca_attention_workspace_size(C.byref(a), C.byref(n)) == stca.ERR_UNSUPPORTED
+    c, b = cfg(), batch(score_bias=FAKE)
+    w, keepw = _weights()
+    g = stca.Grads()
+    r = lib.stca_backward(C.byref(c), C.byref(b), C.byref(w), FAKE, C.byref(g), FAKE, 1 << 30, None)
+    assert r == stca.ERR_UNSUPPORTED and "bias" in stca.last_error()
+
+
 def test_peak_mfma_validation():
     lib = stca.load()
     assert lib.stca_peak_mfma_bf16(0, 10, C.c_void_p(FAKE), None, None) == stca.ERR_INVALID_ARG

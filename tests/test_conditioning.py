@@ -60,6 +60,17 @@ def test_no_rounding_reproduces_the_oracle(make):
     assert all(v < 1e-12 for v in dev.values()), dev
 
 
+@pytest.mark.parametrize("score", ["softmax", "relu"])
+def test_no_rounding_reproduces_the_oracle_with_masks_maps_and_bias(score):
+    sp = I.spec(3, B=2, L=150, m=6, M=2, table_rows=3000, ln_random=True, score=score)
+    p = I.make_problem(sp)
+    p.extra["key_mask"] = I.cross_mask(sp, p.n_hist, (1, 5), 0.4, 0)
+    p.extra["head_map"] = [0, 1, 1, 3, 4, 4, 6, 7]
+    p.extra["score_bias"] = I.score_bias(sp, p.n_hist)
+    dev = C.deviation(p, "bf16", points=())
+    assert all(v < 1e-12 for v in dev.values()), dev
+
+
 def test_no_rounding_reproduces_the_oracle_linear_mode():
     sp = I.spec(5)["feed"]
     p = I.make_problem(replace(sp, B=2, L=120, table_rows=3000, score="relu"))

@@ -8,6 +8,13 @@ item, exact active counts where no score is within rounding of 0); the
 whole forward on the RLB workload reduced with two masked heads and a head
 map; dedup bitwise equal to the plain path under masks; an all-visible mask
 bitwise equal to no mask; the full-size RLB workload with masks, sampled.
+
+The context-similarity score bias ([WeChat] §2.2.3, additive per item and
+head): the attention core with a bias, alone and with masks and a head map
+(softmax and ReLU, d_h 32 and 64); a zero bias bitwise equal to no bias; a
+-1e4 bias bitwise equal to the mask it encodes; the whole forward (softmax
+and ReLU) against the oracle; dedup bitwise equal under a bias; the
+full-size RLB workload with a bias, sampled.
 """
 from dataclasses import replace
 
@@ -17,7 +24,7 @@ import pytest
 from oracle import stca_oracle as O
 from recsys_ultra_long_amd import inputs as I
 
-from parity_util import TOL, compare_forward, gpu_run, oracle_run, row_rel_err
+from parity_util import TOL, compare_forward, end_to_end_bar, gpu_run, oracle_run, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -122,4 +129,125 @@ def test_cross_mask_fullsize_rlb_sampled():
     ut = np.concatenate([np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users])
     errs = compare_forward(g, o, "bf16", users_t=ut)
     print(f"[cross-mask] full size errors {errs}", flush=True)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+# ----------------------------------------------------------------- score bias
+def _core_case(dh, H, seed, max_m=70):
+    g = np.random.default_rng(seed)
+    lens = [0, 1, 31, 32, 33, 200, 1000, 5, 40]
+    ms = [min(m, max_m) for m in [3, 1, 17, 64, 70, 2, 33, 0, 5]]
+    d = dh * H
+    ho = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    to = np.concatenate([[0], np.cumsum(ms)]).astype(np.int32)
+    n, T = int(ho[-1]), int(to[-1])
+    q = I.f32_to_bf16_bits((g.standard_normal((T, d)) / np.sqrt(dh)).astype(np.float32))
+    k = I.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
+    v = I.f32_to_bf16_bits(g.standard_normal((n, d)).astype(np.float32))
+    bias = (g.standard_normal((n, H)) * 1.5).astype(np.float32)
+    return lens, ho, to, q, k, v, bias, g
+
+
+@pytest.mark.parametrize("score", ["softmax", "relu"])
+@pytest.mark.parametrize("dh,H,hmap,masked", [(32, 8, None, False), (32, 8, [0, 0, 2, 3, 3, 5, 6, 0], True),
+                                              (64, 4, None, True)])
+def test_score_bias_attention_core(score, dh, H, hmap, masked):
+    from recsys_ultra_long_amd import stca
+    lens, ho, to, q, k, v, bias, g = _core_case(dh, H, 100 + dh + H)
+    n = int(ho[-1])
+    mask = None
+    if masked:
+        mask = np.full(n, (1 << H) - 1, dtype=np.uint32)
+        for h in (1, 3):
+            mask[g.random(n) > 0.3] &= np.uint32(~(1 << h) & 0xffffffff)
+    print(f"[bias] core {score} d_h {dh} map {hmap} masked {masked}", flush=True)
+    attn, active, st = stca.attention(_dev(q), _dev(k), _dev(v), _dev(ho), _dev(to), H, score,
+                                      chunk_keys=64, key_mask=None if mask is None else _dev(mask),
+                                      head_map=hmap, score_bias=_dev(bias))
+    torch.cuda.synchronize()
+    attn = attn.cpu().numpy()
+    assert int(st.cpu()[0]) == 0
+    Q, K, V = O.stored_to_f64(q), O.stored_to_f64(k), O.stored_to_f64(v)
+    worst = 0.0
+    for u in range(len(lens)):
+        a, b, t0, t1 = ho[u], ho[u + 1], to[u], to[u + 1]
+        if t1 == t0:
+            continue
+        ref, cnt, amb = O.attention_core(Q[t0:t1], K[a:b], V[a:b], H, score, scale=1.0,
+                                         key_mask=None if mask is None else mask[a:b], head_map=hmap,
+                                         score_bias=bias[a:b])
+        err = row_rel_err(attn[t0:t1], ref)
+        worst = max(worst, err)
+        assert err <= TOL["bf16"], (u, err)
+        if score == "relu":
+            gc = active.cpu().numpy()[t0:t1]
+            exact = amb == 0
+            assert np.array_equal(gc[exact], cnt[exact]), u
+            assert np.all(np.abs(gc - cnt) <= amb), u
+    print(f"[bias] core worst {worst:.2e}", flush=True)
+
+
+def test_score_bias_zero_is_no_bias_and_large_negative_is_a_mask():
+    """Bitwise: with at most 64 targets per user the kernel with a bias runs
+    the same schedule (the same split of each history into partials) as the
+    one without, so adding zeros changes nothing.  (With more targets the
+    one without a bias serves each target group from one wave and splits the
+    keys differently, which moves results at the bf16 rounding of the
+    weights; the core test above holds that case to the oracle.)"""
+    from recsys_ultra_long_amd import stca
+    dh, H = 32, 8
+    lens, ho, to, q, k, v, bias, g = _core_case(dh, H, 7, max_m=64)
+    n = int(ho[-1])
+    args = (_dev(q), _dev(k), _dev(v), _dev(ho), _dev(to), H, "softmax")
+    a0 = stca.attention(*args, chunk_keys=64)[0].cpu().numpy()
+    a1 = stca.attention(*args, chunk_keys=64, score_bias=_dev(np.zeros((n, H), np.float32)))[0].cpu().numpy()
+    assert np.array_equal(a0, a1)
+    mask = np.full(n, (1 << H) - 1, dtype=np.uint32)
+    for h in (2, 5):
+        mask[g.random(n) > 0.5] &= np.uint32(~(1 << h) & 0xffffffff)
+    nb = np.where(((mask[:, None] >> np.arange(H)) & 1) == 1, 0.0, -1e4).astype(np.float32)
+    am = stca.attention(*args, chunk_keys=64, key_mask=_dev(mask))[0].cpu().numpy()
+    ab = stca.attention(*args, chunk_keys=64, score_bias=_dev(nb))[0].cpu().numpy()
+    # exp(-1e4 - max) is exactly 0 in fp32, as a masked key's weight; a head
+    # whose every item is masked differs (0 vs the mean of nothing), so
+    # compare only rows whose users see at least one item in every head
+    ok = np.ones(len(to) - 1, bool)
+    for u in range(len(to) - 1):
+        seg = mask[ho[u]:ho[u + 1]]
+        ok[u] = len(seg) > 0 and all(((seg >> h) & 1).any() for h in range(H))
+    rows = np.concatenate([np.arange(to[u], to[u + 1]) for u in range(len(to) - 1) if ok[u]])
+    assert np.array_equal(am[rows], ab[rows])
+
+
+@pytest.mark.parametrize("score", ["softmax", "relu"])
+def test_score_bias_forward_matches_oracle(score):
+    sp = I.spec(3, B=3, L=700, m=24, M=3, table_rows=20000, ln_random=True, score=score)
+    p = _masked(sp, head_map=[0, 1, 1, 3, 4, 4, 6, 7])
+    p.extra["score_bias"] = I.score_bias(sp, p.n_hist)
+    g = gpu_run(p, path="staged")
+    o = oracle_run(p)
+    errs = compare_forward(g, o, "bf16")
+    bar = end_to_end_bar(p, exact=o)
+    print(f"[bias] forward {score} errors {errs} bar {bar}", flush=True)
+    assert all(errs[k] <= bar[k] for k in errs), (errs, bar)
+
+
+def test_score_bias_dedup_bitwise_and_fullsize_sampled():
+    sp = I.spec(4, B=5, L_max=500, m=8, table_rows=20000)
+    p = I.make_problem(sp)
+    p.extra["score_bias"] = I.score_bias(sp, p.n_hist)
+    a = gpu_run(p, path="staged")
+    b = gpu_run(p, path="staged", dedup=True)
+    for k in ("z", "o", "attn"):
+        assert np.array_equal(a[k], b[k]), k
+    sp = I.spec(3)
+    p = I.make_problem(sp, threads=16)
+    p.extra["score_bias"] = I.score_bias(sp, p.n_hist)
+    print(f"[bias] full size n_hist={p.n_hist}", flush=True)
+    users = [0, 11, 21, 31]
+    g = gpu_run(p, path="staged")
+    o = oracle_run(p, users)
+    ut = np.concatenate([np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users])
+    errs = compare_forward(g, o, "bf16", users_t=ut)
+    print(f"[bias] full size errors {errs}", flush=True)
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
