@@ -3,9 +3,20 @@ for every weight and embedding row against the float64 backward oracle.
 
 Checks:
 * end to end on reduced workloads (d 256 with d_h 64 / 32, d 128 ragged, the
-  training workload's Beta(1/4, 1) lengths, random LN affine and z-LN): every
-  weight gradient, the per-item and per-target row gradients and the table
-  gradient, relative Frobenius error within the bf16 bar;
+  training workload's Beta(1/4, 1) lengths, random LN affine and z-LN): the
+  per-item and per-target row gradients and the table gradient on every row a
+  history item or target touched, row by row (each row's largest error over
+  its largest magnitude) within the bf16 bar 2e-2; every weight gradient
+  within 2e-2 relative Frobenius and, row by row (each input feature's row of
+  an [in, out] gradient), within WEIGHT_ROW_TOL of max(its own largest
+  magnitude, the median row's).  Row r of a weight gradient is
+  sum_t x_t[r] g_t over tokens or targets: a feature r that is small for
+  every token makes a row far below the others, and its error comes from the
+  forward's error in x_t[r], which is relative to the whole row x_t, not to
+  x_t[r] -- hence the median floor.  The largest row error of bf16 rounding
+  noise sits 2-4x above its Frobenius level (measured on these workloads:
+  Frobenius <= 1.2e-2, floored rows <= 3.7e-2), hence 5e-2; a wrong, swapped
+  or missing row is off by the order of the row scale itself;
 * the attention backward stepwise, softmax and ReLU: dQ, dK, dV against the
   oracle evaluated at the operands the GPU actually used (its Q, K, V rows
   and its upstream gradient of the attention output);
@@ -33,6 +44,26 @@ if not torch.cuda.is_available():
     pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU visible")]
 
 TOL = 2e-2
+WEIGHT_ROW_TOL = 5e-2
+
+
+def row_err(g, o, floor=0.0, info=False):
+    """max over rows of max_k |g - o| / max(max_k |o|, floor * median row max)
+    (rows along the last axis; a 1-D array is one row); an all-zero reference
+    row is compared absolutely.  ``info``: also return (row, its max, the
+    median row max) of the worst row."""
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    if o.size == 0:
+        return (0.0, None) if info else 0.0
+    g = g.reshape(-1, o.shape[-1])
+    o = o.reshape(-1, o.shape[-1])
+    rm = np.abs(o).max(axis=1)
+    med = float(np.median(rm))
+    den = np.maximum(rm, floor * med)
+    r = np.abs(g - o).max(axis=1) / np.where(den > 0, den, 1.0)
+    w = int(r.argmax())
+    return (float(r[w]), (w, float(rm[w]), med)) if info else float(r[w])
 
 
 def rel_fro(g, o):
@@ -81,21 +112,50 @@ def get(tree, path):
     return tree
 
 
-def compare_all(p, g, ref, tol=TOL, table=True):
-    errs = {}
-    for path, o in leaves(ref["grads"]):
-        errs["/".join(map(str, path))] = rel_fro(get(g["grads"], path), o)
+def touched_rows(p, users=None):
+    """Valid table rows read by the history items or targets (of ``users``)."""
+    ho, to = p.hist_offsets, p.tgt_offsets
+    us = range(p.spec.B) if users is None else users
+    ids = np.concatenate([p.hist_ids[ho[u]:ho[u + 1]] for u in us] + [p.tgt_ids[to[u]:to[u + 1]] for u in us])
+    ids = ids.astype(np.int64)
+    return np.unique(ids[(ids >= 0) & (ids < p.spec.table_rows)])
+
+
+def compare_all(p, g, ref, tol=TOL, table=True, users=None):
+    """Row gradients (items, targets, table rows) row by row within ``tol``;
+    weight gradients within ``tol`` relative Frobenius and, row by row with
+    the median floor, within WEIGHT_ROW_TOL (see the module docstring)."""
+    errs, fro = {}, {}
+    pairs = [("/".join(map(str, path)), get(g["grads"], path), o) for path, o in leaves(ref["grads"])]
+    n_weights = len(pairs)
+    rows_t = None if users is None else np.concatenate(
+        [np.arange(p.tgt_offsets[u], p.tgt_offsets[u + 1]) for u in users])
+    rows_h = None if users is None else np.concatenate(
+        [np.arange(p.hist_offsets[u], p.hist_offsets[u + 1]) for u in users])
     if g["d_hist"] is not None:
-        errs["d_hist"] = rel_fro(g["d_hist"], ref["d_hist"])
-    errs["d_tgt"] = rel_fro(g["d_tgt"], ref["d_tgt"])
+        pairs.append(("d_hist", g["d_hist"] if rows_h is None else g["d_hist"][rows_h],
+                      ref["d_hist"] if rows_h is None else ref["d_hist"][rows_h]))
+    pairs.append(("d_tgt", g["d_tgt"] if rows_t is None else g["d_tgt"][rows_t],
+                  ref["d_tgt"] if rows_t is None else ref["d_tgt"][rows_t]))
     if table:
         sp = p.spec
         tg = OG.table_grad(sp.table_rows, sp.d, p.hist_ids, p.tgt_ids, ref["d_hist"], ref["d_tgt"])
-        errs["table"] = rel_fro(g["table"], tg)
+        rows = touched_rows(p)
+        pairs.append(("table", g["table"][rows], tg[rows]))
+    bad = {}
+    for i, (name, a, b) in enumerate(pairs):
+        fro[name] = rel_fro(a, b)
+        if i < n_weights:
+            errs[name] = row_err(a, b, floor=1.0)
+            if not (errs[name] <= WEIGHT_ROW_TOL and fro[name] <= tol):
+                bad[name] = (errs[name], fro[name])
+        else:
+            errs[name] = row_err(a, b)
+            if not errs[name] <= tol:
+                bad[name] = errs[name]
     worst = max(errs, key=errs.get)
-    print(f"[bwd] {p.spec.name}: worst {worst} {errs[worst]:.3e}; "
-          + " ".join(f"{k}={v:.1e}" for k, v in sorted(errs.items())), flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= tol}
+    print(f"[bwd] {p.spec.name}: worst row error {worst} {errs[worst]:.3e}; "
+          + " ".join(f"{k}={v:.1e}/{fro[k]:.1e}" for k, v in sorted(errs.items())), flush=True)
     assert not bad, bad
     return errs
 
@@ -122,7 +182,7 @@ def test_backward_matches_oracle(k):
     compare_all(p, g, ref)
     # the recomputed forward's z is the forward's
     zo = O.forward_problem(p)["z"]
-    assert rel_fro(g["z"], zo) < TOL
+    assert row_err(g["z"], zo) < TOL
 
 
 @pytest.mark.parametrize("score", ["softmax", "relu"])
@@ -152,11 +212,11 @@ def test_attention_backward_stepwise(score):
             dQ, dK, dV = OG.attention_backward(qd[i, t0:t1], kvd[i, 0, a:b], kvd[i, 1, a:b],
                                                g["da"][i, t0:t1].astype(np.float64), sp.H, score, scale=1.0)
             dq_ref[t0:t1], dk_ref[a:b], dv_ref[a:b] = dQ, dK, dV
-        worst["dq"] = max(worst["dq"], rel_fro(g["dq"][i], dq_ref))
-        worst["dk"] = max(worst["dk"], rel_fro(dkv[i, :, :sp.d], dk_ref))
-        worst["dv"] = max(worst["dv"], rel_fro(dkv[i, :, sp.d:], dv_ref))
+        worst["dq"] = max(worst["dq"], row_err(g["dq"][i], dq_ref))
+        worst["dk"] = max(worst["dk"], row_err(dkv[i, :, :sp.d], dk_ref))
+        worst["dv"] = max(worst["dv"], row_err(dkv[i, :, sp.d:], dv_ref))
     print(f"[bwd] attention stepwise {score}: {worst}", flush=True)
-    assert all(v <= 1e-2 for v in worst.values()), worst
+    assert all(v <= TOL for v in worst.values()), worst  # row by row, at the GPU's own operands
 
 
 def test_backward_zero_upstream_gives_zero():
@@ -217,7 +277,7 @@ def test_backward_fullsize_training_sampled():
     g = gpu_backward(p, dz, outputs=("d_hist", "d_tgt"))
     ref = OG.backward_problem(p, dz, users=users)
     assert g["status"] == 0
-    compare_all(p, g, ref, table=False)
+    compare_all(p, g, ref, table=False, users=users)
 
 
 @pytest.mark.parametrize("k", [2, 3, 4, 6])
@@ -277,8 +337,8 @@ def test_backward_dedup_fullsize_training_sampled():
         np.add.at(tg, ids, ref["d_hist"][p.hist_offsets[u]:p.hist_offsets[u + 1]])
         tids = p.tgt_ids[p.tgt_offsets[u]:p.tgt_offsets[u + 1]]
         np.add.at(tg, tids, ref["d_tgt"][p.tgt_offsets[u]:p.tgt_offsets[u + 1]])
-    rows = np.unique(np.concatenate([p.hist_ids, p.tgt_ids]))
-    err_t = rel_fro(g["table"][rows], tg[rows])
+    rows = touched_rows(p, users)
+    err_t = row_err(g["table"][rows], tg[rows])
     print(f"[bwd-dedup] full size table rows err {err_t:.2e}", flush=True)
     assert err_t <= TOL
-    compare_all(p, g, ref, table=False)
+    compare_all(p, g, ref, table=False, users=users)
