@@ -267,6 +267,21 @@ int stca_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t 
 int stca_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
                  const stca_outputs *out, void *workspace, size_t ws_bytes, void *hip_stream);
 
+/* stca_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same forward, its workspace taken from a static device array of
+ * STCA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends.  The caller still passes every input and output.
+ * A batch whose stca_workspace_size exceeds the array is rejected with
+ * STCA_ERR_WORKSPACE before anything is enqueued.  The device is the one
+ * current on the calling thread (hip_stream must belong to it).  Every call
+ * on a device shares that device's array: calls that overlap on one device
+ * (other streams, other threads) race and must be serialised by the caller.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library routine. */
+#define STCA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int stca_forward_noalloc(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
+                         const stca_outputs *out, void *hip_stream);
+
 /* The attention core alone on caller-provided operands ([Review] formula for
  * alpha and o; [WeChat] §1.2 for the ReLU form): for every user u, target t of
  * u and head eta,

@@ -29,7 +29,9 @@ DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
            "stca_attention", "stca_backward_workspace_size", "stca_backward",
            "stca_peak_mfma_bf16", "stca_peak_hbm_read", "stca_status_string", "stca_last_error",
-           "stca_version")
+           "stca_version", "stca_forward_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # STCA_NOALLOC_SCRATCH_BYTES
 
 _vp = C.c_void_p
 
@@ -119,6 +121,8 @@ def load() -> C.CDLL:
         lib.stca_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(C.c_size_t)]
         lib.stca_forward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights),
                                      C.POINTER(Outputs), _vp, C.c_size_t, _vp]
+        lib.stca_forward_noalloc.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights),
+                                             C.POINTER(Outputs), _vp]
         lib.stca_attention_workspace_size.argtypes = [C.POINTER(AttnArgs), C.POINTER(C.c_size_t)]
         lib.stca_attention.argtypes = [C.POINTER(AttnArgs), _vp, C.c_size_t, _vp]
         lib.stca_backward_workspace_size.argtypes = [C.POINTER(Config), C.POINTER(Batch),
@@ -133,7 +137,7 @@ def load() -> C.CDLL:
         lib.stca_version.restype = C.c_int
         for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
                   "stca_attention", "stca_backward_workspace_size", "stca_backward", "stca_peak_mfma_bf16",
-                  "stca_peak_hbm_read"):
+                  "stca_peak_hbm_read", "stca_forward_noalloc"):
             getattr(lib, f).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -302,10 +306,12 @@ def n_backward_stage_events(M: int) -> int:
 
 
 class Forward:
-    """Reusable forward call: outputs and workspace are allocated once."""
+    """Reusable forward call: outputs and workspace are allocated once.
+    ``noalloc``: call ``stca_forward_noalloc`` (no workspace; the library's
+    static scratch) instead of ``stca_forward``."""
 
     def __init__(self, dp: DeviceProblem, want=("o", "attn", "active"), dumps=(), stream=None,
-                 events: Optional[StageEvents] = None):
+                 events: Optional[StageEvents] = None, noalloc: bool = False):
         import torch
         self.dp = dp
         self.lib = load()
@@ -332,15 +338,23 @@ class Forward:
         if events is not None:
             self.out.stage_events = events.ptr
             self.out.n_stage_events = events.n
+        self.noalloc = noalloc
+        self.stream = stream
+        if noalloc:
+            self.ws, self.ws_bytes = None, 0
+            return
         n = C.c_size_t(0)
         _check(self.lib.stca_workspace_size(C.byref(cfg), C.byref(self.b), C.byref(n)))
         self.ws_bytes = n.value
         self.ws = torch.empty(max(1, self.ws_bytes), dtype=torch.uint8, device=dev)
-        self.stream = stream
 
     def __call__(self):
         import torch
         s = self.stream if self.stream is not None else torch.cuda.current_stream()
+        if self.noalloc:
+            _check(self.lib.stca_forward_noalloc(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
+                                                 C.byref(self.out), s.cuda_stream))
+            return self
         _check(self.lib.stca_forward(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
                                      C.byref(self.out), self.ws.data_ptr(), self.ws_bytes,
                                      s.cuda_stream))

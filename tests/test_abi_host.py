@@ -354,6 +354,25 @@ def test_score_bias_attention_and_backward_validation():
     assert r == stca.ERR_UNSUPPORTED and "bias" in stca.last_error()
 
 
+def test_noalloc_rejects_on_the_host_before_any_device_call():
+    """stca_forward_noalloc validates and sizes the batch on the host first:
+    invalid arguments and a workspace beyond the static scratch return at once
+    (no GPU is touched, so this runs without one)."""
+    lib = stca.load()
+    w, keepw = _weights()
+    out = stca.Outputs(z=FAKE)
+    c = cfg()
+    big = batch(n_hist=20_000_000, n_tgt=64, max_tgt_per_user=64)
+    n = C.c_size_t(0)
+    assert lib.stca_workspace_size(C.byref(c), C.byref(big), C.byref(n)) == stca.OK
+    assert n.value > stca.NOALLOC_SCRATCH_BYTES
+    r = lib.stca_forward_noalloc(C.byref(c), C.byref(big), C.byref(w), C.byref(out), None)
+    assert r == stca.ERR_WORKSPACE and "static scratch" in stca.last_error()
+    bad = cfg(H=7)
+    r = lib.stca_forward_noalloc(C.byref(bad), C.byref(batch()), C.byref(w), C.byref(out), None)
+    assert r == stca.ERR_INVALID_ARG
+
+
 def test_peak_mfma_validation():
     lib = stca.load()
     assert lib.stca_peak_mfma_bf16(0, 10, C.c_void_p(FAKE), None, None) == stca.ERR_INVALID_ARG
