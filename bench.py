@@ -85,6 +85,10 @@ def attach_measured_peaks(res, skip=False):
 
 def workload(name):
     from recsys_ultra_long_amd import inputs as I
+    from dataclasses import replace
+    if name.endswith("-relu"):
+        # the same workload with ReLU-scored attention (and active counts)
+        return replace(workload(name[:-len("-relu")]), score="relu")
     if name.endswith("-longer"):
         # the same workload with the LONGER-style sequence encoding: each
         # layer's history is the cross attention of the last 256 items over
@@ -101,20 +105,52 @@ def workload(name):
         return I.spec(6)
     if name in ("hyformer-feed", "hyformer-search"):
         # the HyFormer workload's sequence with generated, boosted queries
-        from dataclasses import replace
         return replace(I.spec(5)[name.split("-")[1]], qmode="hyformer", n_ns=8)
+    if name in ("hyformer-feed-linear", "hyformer-search-linear", "hyformer-linear"):
+        # the HyFormer-style workload as configured: N_q = 8 given queries per
+        # sequence, the next layer's queries a fixed random linear map of the
+        # cross output; "hyformer-linear" is both sequences (feed, then search)
+        return I.spec(5)["search" if "search" in name else "feed"]
     raise SystemExit(f"unknown workload {name}")
 
 
+def host_info():
+    """What the CPU baseline ran on: CPU model, the cores this process may
+    use, and the BLAS library numpy calls (with its thread count)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = (f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')}, "
+                        f"{i.get('threading_layer')}; {os.path.basename(i.get('filepath', ''))})")
+                threads = i.get("num_threads")
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "blas": blas,
+            "blas_threads": threads}
+
+
 def cpu_baseline(p, seconds):
-    """Float64 oracle on whole users of the same workload until `seconds` pass."""
+    """Float64 oracle on whole users of the same workload until `seconds`
+    pass.  Its products run in the BLAS library on every core of the process's
+    affinity set; its per-target and per-head loops are single-threaded
+    Python, so `cores` is the affinity count (the threads it may use), with
+    the host's CPU model and BLAS named beside it."""
     import numpy as np
     from oracle import stca_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        cores = 1
+    hi = host_info()
+    cores = hi["affinity_cores"]
     sp = p.spec
     layers, z, wz = O.weights_f64(p.layers, p.z, p.wz)
     cfg = dict(d=sp.d, H=sp.H, M=sp.M, score=sp.score, qmode=sp.qmode, kv_ln=sp.kv_ln,
@@ -139,19 +175,17 @@ def cpu_baseline(p, seconds):
     return {"value": toks * sp.M / dt, "unit": "history tokens/s per STCA layer",
             "cores": int(cores), "kind": "oracle",
             "sample": f"{users} of {sp.B} users ({toks} history tokens, {tgts} targets, "
-                      f"{sp.M} layers) in {dt:.1f} s, float64 numpy",
-            "target_scores_per_s": tgts / dt}
+                      f"{sp.M} layers) in {dt:.1f} s, float64 numpy (BLAS products on "
+                      f"{hi['blas_threads']} threads, per-target loops single-threaded)",
+            "target_scores_per_s": tgts / dt, **hi}
 
 
 def cpu_baseline_backward(p, dz, seconds):
     """Float64 backward oracle on whole users of the training workload until
     `seconds` pass."""
     from oracle import stca_grad as OG
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        cores = 1
+    hi = host_info()
+    cores = hi["affinity_cores"]
     sp = p.spec
     t0 = time.perf_counter()
     users, toks = 0, 0
@@ -165,7 +199,7 @@ def cpu_baseline_backward(p, dz, seconds):
     return {"value": toks * sp.M / dt, "unit": "history tokens/s per STCA layer (backward)",
             "cores": int(cores), "kind": "oracle",
             "sample": f"{users} of {sp.B} users ({toks} history tokens, {sp.M} layers) in {dt:.1f} s, "
-                      "float64 numpy backward (forward recompute included)"}
+                      "float64 numpy backward (forward recompute included)", **hi}
 
 
 def bench_backward(args):
@@ -293,6 +327,77 @@ def bench_backward(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_lsweep(args):
+    """History length sweep at a fixed total: the RLB long model (d 256, H 8,
+    M 4, m 64 targets per user) over sum(L) = 327,680 history tokens cut into
+    B = sum(L) / L users of length L, for L = 1,024 .. 10,240.  The review's
+    complexity table gives STCA O(L d_h) time per layer, so the history
+    encoding and the attention -- the stages whose work is per history token
+    (the attention's per (token, target) pair, with m fixed) -- should run at a
+    flat rate in history tokens per second; the query side grows with the
+    number of users (targets = B m) and is reported apart."""
+    from dataclasses import replace
+    import numpy as np
+    import torch
+    from recsys_ultra_long_amd import inputs as I
+    from recsys_ultra_long_amd import stca
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    stca.load()
+    total = 327_680
+    base = I.spec(3)
+    table = None
+    rows = []
+    for L in (1024, 2048, 4096, 8192, 10240):
+        sp = replace(base, L=L, B=total // L)
+        p = I.make_problem(sp, with_table=table is None, threads=min(16, os.cpu_count() or 8))
+        dp = stca.upload(p, path="staged", table=table)
+        table = dp.table
+        M = sp.M
+        nev = stca.n_stage_events(M)
+        evs = [stca.StageEvents(nev) for _ in range(args.steps)]
+        f = stca.Forward(dp, want=(), dumps=())
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for k in range(args.steps):
+            f.out.stage_events = evs[k].ptr
+            f.out.n_stage_events = nev
+            f()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        if int(f.status[0].item()) != 0:
+            raise SystemExit("device status flagged")
+        stage = lambda a, b: float(np.mean([e.elapsed(a, b) for e in evs]))
+        hist = sum(stage(1 + i, 2 + i) for i in range(M))
+        attn = [stage(2 + M + 4 * i, 3 + M + 4 * i) + stage(3 + M + 4 * i, 4 + M + 4 * i) for i in range(M)]
+        rest = ms - hist - sum(attn)
+        rows.append({"L": L, "B": sp.B, "targets": p.n_tgt, "ms_per_step": round(ms, 4),
+                     "tokens_per_s_per_layer": round(total * M / (ms * 1e-3), 1),
+                     "history_ms": round(hist, 4), "history_tokens_per_s_per_layer": round(total * M / (hist * 1e-3), 1),
+                     "attention_ms_per_layer": round(float(np.mean(attn)), 4),
+                     "attention_tokens_per_s": round(total / (float(np.mean(attn)) * 1e-3), 1),
+                     "query_side_and_rest_ms": round(rest, 4)})
+        log(f"L={L} B={sp.B}: {ms:.3f} ms/step, history {hist:.3f} ms, attention {np.mean(attn):.4f} ms/layer")
+        for e in evs:
+            e.close()
+        del f, dp
+        torch.cuda.synchronize()
+    flat = lambda key: round(max(r[key] for r in rows) / min(r[key] for r in rows), 4)
+    res = {"metric": "history tokens/s per STCA layer across L at fixed sum(L) (O(L) check)",
+           "unit": "history tokens/s per STCA layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"rlb-long model (d 256, H 8, hidden 512, M 4, m 64), sum(L) = {total} "
+                                  "history tokens in B = sum(L) / L users, staged path"},
+           "sweep": rows,
+           "max_over_min": {"history": flat("history_tokens_per_s_per_layer"),
+                            "attention": flat("attention_tokens_per_s"),
+                            "whole_forward": flat("tokens_per_s_per_layer")}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +422,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the MFMA-only and device-copy measurements (for profiler runs)")
+    ap.add_argument("--lsweep", action="store_true",
+                    help="history-length sweep at fixed sum(L) (one JSON line of its own)")
+    ap.add_argument("--replicas", type=int, default=1,
+                    help="the workload with this many times its users (same per-user shape): K/V "
+                         "beyond the 256 MB Infinity Cache for the attention's HBM figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB (x5), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -325,6 +435,8 @@ def main():
         if args.workload == "rlb-long":
             args.workload = "rlb-train"
         return bench_backward(args)
+    if args.lsweep:
+        return bench_lsweep(args)
     if args.copy_calibration:
         import torch
         n = 1 << 30
@@ -350,8 +462,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     stca.load()
     sp = workload(args.workload)
-    if args.dedup or args.cross_mask or sp.d == 512 or sp.qmode == "hyformer":  # the fused path serves d <= 256, STCA queries
-        args.path = "staged"
+    if args.replicas > 1:
+        from dataclasses import replace
+        sp = replace(sp, B=sp.B * args.replicas)
+    if args.dedup or args.cross_mask or sp.d == 512 or sp.qmode in ("hyformer", "linear"):
+        args.path = "staged"  # the fused path serves d <= 256 and STCA (fusion) queries
     t = time.time()
     p = I.make_problem(sp, with_table=True, threads=min(16, os.cpu_count() or 8))
     log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} "
@@ -361,6 +476,15 @@ def main():
         p.extra["head_map"] = [h - (h % 2) for h in range(sp.H)]
     dp = stca.upload(p, path=args.path, dedup=args.dedup)
     n_unique = int(len(np.unique(p.hist_ids))) if args.dedup else None
+    # both sequences of the HyFormer-style workload: the search sequence's
+    # forward follows the feed's in every step (each has its own table and
+    # weights); stage figures are the feed's
+    companion = None
+    if args.workload == "hyformer-linear":
+        sp2 = workload("hyformer-search-linear")
+        p2 = I.make_problem(sp2, with_table=True, threads=min(16, os.cpu_count() or 8))
+        companion = stca.Forward(stca.upload(p2, path="staged"), want=(), dumps=())
+        log(f"search sequence: B={sp2.B} n_hist={p2.n_hist} n_tgt={p2.n_tgt}")
     torch.cuda.synchronize()
     log("uploaded")
     M = sp.M
@@ -370,6 +494,8 @@ def main():
     f = stca.Forward(dp, want=(), dumps=())
     for _ in range(args.warmup):
         f()
+        if companion is not None:
+            companion()
     torch.cuda.synchronize()
     log(f"warm-up done ({args.warmup} steps)")
 
@@ -383,10 +509,12 @@ def main():
         f.out.stage_events = evs[k].ptr
         f.out.n_stage_events = nev
         f()
+        if companion is not None:
+            companion()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    st = int(f.status[0].item())
+    st = int(f.status[0].item()) | (int(companion.status[0].item()) if companion is not None else 0)
     if st != 0:
         raise SystemExit(f"device status flagged: {st}")
     log(f"timed {args.steps} steps: {ms:.3f} ms/step")
@@ -512,7 +640,11 @@ def main():
     else:
         dominant = roofs[max(times, key=times.get)]
 
-    value = n_hist * M / (ms * 1e-3)
+    n_hist_all, T_all = n_hist, T
+    if companion is not None:
+        n_hist_all += companion.dp.n_hist
+        T_all += companion.dp.n_tgt
+    value = n_hist_all * M / (ms * 1e-3)
     res = {
         "metric": "history tokens/s + target scores/s per STCA layer at L=10K; % of HBM/MFMA peak",
         "value": round(value, 1),
@@ -521,9 +653,18 @@ def main():
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{sp.name}: B={sp.B} users, L={sp.L}, m={sp.m} targets/user (RLB), "
+        "config": {"workload": f"{sp.name}: B={sp.B} users, "
+                               + (f"L={sp.L}" if sp.L else f"L = max({sp.L_min}, ceil({sp.L_max} Beta({sp.beta_a}, 1))) "
+                                  f"(sum {n_hist})")
+                               + f", m={sp.m} {'queries' if sp.qmode != 'fusion' else 'targets'}/user (RLB), "
                                f"table {sp.table_rows}x{d} bf16 Zipf({sp.zipf_s}) ids, d={d}, H={H}, "
-                               f"hidden={h}, M={M} layers, softmax, path={args.path}"
+                               f"hidden={h}, M={M} layers, {sp.score}, path={args.path}"
+                               + (", queries N(0,1), next queries a fixed random linear map of the cross "
+                                  "output, no history LN" if sp.qmode == "linear" else "")
+                               + (f"; with the search sequence (B={companion.dp.cfg.B}, L=1024, its own "
+                                  "2,000,000x512 table and weights) in the same step" if companion is not None else "")
+                               + (f"; {args.replicas}x the workload's users (K/V beyond the 256 MB Infinity "
+                                  "Cache)" if args.replicas > 1 else "")
                                + (", Cross-Mask: heads 2 and 6 see 25% of the items, heads 2k and 2k+1 "
                                   "share the map of head 2k" if args.cross_mask else "")
                                + (f", HyFormer queries: {sp.n_ns} non-sequence tokens, query FFN hidden "
@@ -532,9 +673,9 @@ def main():
                                + (f", LONGER-style encoding: each layer's history is the cross attention of the "
                                   f"last {sp.l_short} items over all items" if longer else ""),
                    "global_batch": sp.B, "seq_len": sp.L, "targets": T, "parallelism": "single GPU"},
-        "target_scores_per_s_per_layer": round(T * M / (ms * 1e-3), 1),
-        "target_scores_per_s": round(T / (ms * 1e-3), 1),
-        "history_tokens_per_s": round(n_hist / (ms * 1e-3), 1),
+        "target_scores_per_s_per_layer": round(T_all * M / (ms * 1e-3), 1),
+        "target_scores_per_s": round(T_all / (ms * 1e-3), 1),
+        "history_tokens_per_s": round(n_hist_all / (ms * 1e-3), 1),
         "roofline": dominant,
         **({"roofline_attention": roof_attn, "roofline_history": roof_hist}
            if args.path == "staged" else {}),
@@ -549,13 +690,13 @@ def main():
     }
     for e in evs:
         e.close()
-    if not args.no_other_path and not args.dedup and not longer:
+    if not args.no_other_path and not args.dedup and not longer and companion is None:
         # the same inputs through the other path, and through the staged path
         # with unique-id dedup (bit-identical outputs, valid because a history
         # row here depends on its id alone)
         del f
         others = [("staged" if args.path == "fused" else "fused", False), ("staged", True)]
-        if sp.d == 512 or sp.qmode == "hyformer" or args.cross_mask:
+        if sp.d == 512 or sp.qmode in ("hyformer", "linear") or args.cross_mask:
             others = [("staged", True)]
         res["other_paths"] = []
         for other, dd in others:
