@@ -20,10 +20,18 @@
 #include <algorithm>
 
 #include "attn_block.h"
+#include "hist_common.h"
 #include "stca_internal.h"
 
 namespace stca {
 namespace {
+
+using enc::Ring;
+using enc::Src;
+using enc::ring_load;
+using enc::run_phase;
+using enc::zero16;
+using enc::zero4;
 
 constexpr int kD = 256;
 constexpr int kT = 512;          // threads: 8 waves
@@ -43,20 +51,6 @@ struct Smem {
   int s_id[kR], s_tok[kR];
 };
 static_assert(sizeof(Smem::gs) >= sizeof(bf16_t) * kR * kXLD, "LN output must fit the G buffers");
-
-// Two 16-byte fragments per k block: (W1, W3) of a 16-row tile in the G
-// phase, the two k halves of a 32-row tile elsewhere.
-struct Src {
-  const bf16_t *p0, *p1;
-  int stride;  // elements per k block
-};
-struct Ring {
-  bf16x8 v[4][2];
-};
-DEV void ring_load(Ring &r, int slot, const Src &s, int kb) {
-  r.v[slot][0] = ldg8(s.p0 + kb * s.stride);
-  r.v[slot][1] = ldg8(s.p1 + kb * s.stride);
-}
 
 // Per-wave weight sources of each phase.  W1/W3 are packed for the 16x16x32
 // A operand (frag16), W2 and W_K|W_V for the 32x32x16 A operand (frag_off).
@@ -88,76 +82,9 @@ DEV Src src_v(const Layer &L, int w, int lane) {
   return Src{p, p + 512, 2048};
 }
 
-// The NK blocks of one phase; `mma(kb, slot)` does the block's matrix work.
-// Block kb + 3 is loaded while block kb is used (from the next phase once this
-// one runs out; `more` = whether there is a next phase).
-template <int NK, class F>
-DEV void run_phase(Ring &ring, const Src &cur, const Src &nxt, bool more, F mma) {
-  static_assert(NK % 4 == 0, "phase length must be a multiple of 4 blocks");
-#pragma unroll
-  for (int kb = 0; kb < NK; ++kb) {
-    const int nb = kb + 3;
-    if (nb < NK) ring_load(ring, nb % 4, cur, nb);
-    else if (more) ring_load(ring, nb % 4, nxt, nb - NK);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(kb, kb % 4);
-    // the last block's products may overlap the epilogue that follows
-    if (kb + 1 < NK) __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-template <int N>
-DEV void zero4(f32x4 (&a)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-template <int N>
-DEV void zero16(f32x16 (&a)[N]) {
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) a[i][e] = 0.f;
-}
-
-// Gather the 128 table rows of a tile into sm.xs (zeros for padding rows and
-// for ids outside the table), with the optional copy by history token.
-// `use_prow`: take the planner's padded-row ids when present.  Ends synchronised.
+// Gather the 128 table rows of a tile into sm.xs (see enc::gather_tile).
 DEV void gather_tile(const ChainArgs &a, Smem &sm, int64_t row0, int total_blocks, int tid, bool use_prow) {
-  if (tid < kR) {
-    const int64_t p = row0 + tid;
-    int id = -1, tok = -1;
-    const int blk = (int)(p >> 5);
-    if (use_prow && a.plan.prow && !a.in_dump) {
-      id = a.plan.prow[p];  // planner-validated id of this padded row
-    } else if (blk < total_blocks) {
-      const int u = upper_index(a.plan.pblk, a.B, blk);
-      const int j = (int)(p - (int64_t)a.plan.pblk[u] * 32);
-      if (j < a.plan.hoff[u + 1] - a.plan.hoff[u]) {
-        tok = a.plan.hoff[u] + j;
-        id = a.ids[tok];
-        if (id < 0 || (int64_t)id >= a.table_rows) {
-          set_status(a.status, 4);
-          id = -1;
-        }
-      }
-    }
-    sm.s_id[tid] = id;
-    sm.s_tok[tid] = tok;
-  }
-  __syncthreads();
-  const bf16_t *table = (const bf16_t *)a.table;
-  constexpr int C8 = kD / 8;
-#pragma unroll
-  for (int k = 0; k < kR * C8 / kT; ++k) {
-    const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
-    const int id = sm.s_id[r];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * kD + c);
-    *reinterpret_cast<u32x4 *>(sm.xs + r * kXRLD + c) = v;
-    if (a.in_dump && sm.s_tok[r] >= 0)
-      *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)sm.s_tok[r] * kD + c) = v;
-  }
-  __syncthreads();
+  enc::gather_tile<kD, kR, kXRLD, kT>(a, sm.xs, sm.s_id, sm.s_tok, row0, total_blocks, tid, use_prow);
 }
 
 // SwiGLU FFN [+ LN] of one layer over the 128 rows in sm.xs; X~ goes to

@@ -615,6 +615,9 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
   plan.prow = L.prow ? at<int>(ws, L.prow) : nullptr;
 
   if (!li && (e = rec(0))) return hip_fail(e, "stage event");
+  // bf16, d <= 256: all layers' history encoding in one launch that gathers
+  // each tile once (the 128-row encoders, hist_bf16.hip / hist128_bf16.hip)
+  const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers && !li;
   // ---- 1. weight preparation (bf16): fragment-packed W^T into the workspace
   bf16_t *prep = bf ? at<bf16_t>(ws, L.prep) : nullptr;
   if (bf) {
@@ -634,14 +637,16 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
     for (int i = 0; i < M; ++i) {
       const stca_layer &l = w->layers[i];
       const PrepLayer &p = L.pl[i];
-      // the d = 256 history encoders (staged and fused) read W1 / W3 as 16-row tiles
-      const int f13 = d == 256 ? 1 : 0;
+      // the 128-row history encoders (d = 256 staged and fused, d = 128 staged)
+      // read W1 / W3 as 16-row tiles and W_K, W_V block-interleaved
+      const bool enc128 = d == 256 || (d == 128 && multi);
+      const int f13 = enc128 ? 1 : 0;
       if (!li) {  // short rows are encoded already: no history FFN
         if ((e = add(l.kv.w1, d, hd, p.kv_w1, 0, f13))) break;
         if ((e = add(l.kv.w3, d, hd, p.kv_w3, 0, f13))) break;
         if ((e = add(l.kv.w2, hd, d, p.kv_w2, 0))) break;
       }
-      if (d == 256 && !li) {  // the d = 256 encoders read W_K and W_V block-interleaved
+      if (enc128 && !li) {
         if ((e = add(l.wk, d, d, p.wkv, 0, 4))) break;
         if ((e = add(l.wv, d, d, p.wkv, 0, 5))) break;
       } else {
@@ -881,8 +886,6 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
     return er;
   };
 
-  // bf16, d <= 256: all layers in one launch that gathers each tile once
-  const bool multi = bf && d <= 256 && !L.fused && batch->n_hist > 0 && M <= kMaxLayers && !li;
   if (multi) {
     ChainArgs a = enc_args(0);
     HistLayers hl;
@@ -900,7 +903,7 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
       hl.kbuf[i] = enc_k(i);
       hl.vbuf[i] = enc_v(i);
     }
-    e = d == 256 ? launch_hist256(a, hl, s) : launch_hist_layers(a, hl, s);
+    e = d == 256 ? launch_hist256(a, hl, s) : launch_hist128(a, hl, s);
     if (e) return hip_fail(e, "history encoding");
     for (int i = 0; i < M; ++i)
       if ((e = finish_layer(i))) return hip_fail(e, "history K/V");

@@ -58,7 +58,7 @@ hipError_t launch_plan(const int *hist_off, const int *tgt_off, int B, int64_t n
 // One launch computes, for a set of rows,
 //   input -> [SwiGLU FFN] -> [LN] -> [projection (scaled)] -> output
 // Input modes:
-enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3, IN_STAGED = 4 };
+enum InMode { IN_GATHER_CSR = 0, IN_GATHER_IDS = 1, IN_DENSE = 2, IN_PREGEMM = 3 };
 // Output modes:
 enum OutMode { OUT_KV = 0, OUT_ROWS = 1, OUT_FUSED = 2 };
 
@@ -102,8 +102,8 @@ struct ChainArgs {
 
 hipError_t launch_chain_bf16(const ChainArgs &a, hipStream_t s);
 
-// All M layers' history encodings in one launch (bf16, d 128 or 256): the
-// gathered rows of a tile are reused by every layer.  `a` carries the batch,
+// All M layers' history encodings in one launch (bf16, d 128 or 256,
+// 128-row tiles): the gathered rows of a tile are reused by every layer.  `a` carries the batch,
 // plan, flags and in_dump; the per-layer weights and K/V buffers come from hl.
 constexpr int kMaxLayers = 16;
 struct HistLayers {
@@ -113,9 +113,10 @@ struct HistLayers {
   int M;
   unsigned long long *clock;  // optional [8][4]: start / end clock counters of workgroups 0..7
 };
-hipError_t launch_hist_layers(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
 // d = 256: 128-row tiles on 8 waves (W1, W3 packed with fmt 1).
 hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
+// The same 128-row encoder at d = 128 (hist128_bf16.hip).
+hipError_t launch_hist128(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
 hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 
 // Weight preparation (bf16): a matrix W [K, N] (row-major, y = x W) is stored

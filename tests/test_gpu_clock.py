@@ -29,10 +29,11 @@ def test_hbm_read_stream():
     assert 500.0 < rate < 20000.0
 
 
-def test_history_launch_clock_probe():
-    # 3 users of 300 items: 1,024 padded rows = 8 workgroups of 128 rows; a
-    # sentinel row past them must stay untouched
-    sp = I.spec(3, B=3, L=300, m=8, table_rows=20000)
+@pytest.mark.parametrize("k", [3, 4])
+def test_history_launch_clock_probe(k):
+    # d = 256 and d = 128: 3 users of 300 items: 1,024 padded rows = 8
+    # workgroups of 128 rows; a sentinel row past them must stay untouched
+    sp = I.spec(k, B=3, L=300, L_max=None, m=8, table_rows=20000)
     p = I.make_problem(sp)
     dp = stca.upload(p, path="staged")
     f = stca.Forward(dp, want=(), dumps=())
