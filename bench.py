@@ -40,12 +40,14 @@ def log(msg):
 def measured_peaks():
     """Attainable rates on this GPU, quoted beside the nominal peaks the
     rooflines are priced against: dense bf16 MFMA from registers (the
-    library's MFMA-only kernel, best of three launches), an HBM read stream
+    library's MFMA-only kernel, best of three launches, on fixed low-entropy
+    operands and on operands that vary like real data), an HBM read stream
     (the library's streaming-read kernel over 2 GiB, best of four) and a
     1 GiB device copy (read + write bytes / time, best of five)."""
     import torch
     from recsys_ultra_long_amd import stca
     mfma, mfma_clk = stca.peak_mfma_bf16()
+    mfma_mx, mfma_mx_clk = stca.peak_mfma_bf16(mixed=True)
     hbm_read = stca.peak_hbm_read()
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -62,6 +64,7 @@ def measured_peaks():
         best = max(best, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del a, b
     return {"mfma_bf16_tflops": round(mfma, 1), "mfma_bf16_clock_ghz": round(mfma_clk, 3),
+            "mfma_bf16_mixed_tflops": round(mfma_mx, 1), "mfma_bf16_mixed_clock_ghz": round(mfma_mx_clk, 3),
             "hbm_read_gbs": round(hbm_read, 1), "hbm_copy_gbs": round(best, 1)}
 
 
@@ -81,6 +84,9 @@ def attach_measured_peaks(res, skip=False):
             pm = mp["mfma_bf16_tflops"] if roof["unit"] == "TFLOP/s" else mp["hbm_read_gbs"]
             roof["peak_measured"] = pm
             roof["frac_measured"] = round(roof["achieved"] / pm, 4)
+            if roof["unit"] == "TFLOP/s":  # the same, for operands that switch like real data
+                roof["peak_measured_mixed"] = mp["mfma_bf16_mixed_tflops"]
+                roof["frac_measured_mixed"] = round(roof["achieved"] / mp["mfma_bf16_mixed_tflops"], 4)
 
 
 def workload(name):
@@ -499,7 +505,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warm-up done ({args.warmup} steps)")
 
-    # shader clock during the history launch (staged bf16 path at d = 256)
+    # shader clock during the history launch (staged bf16 path at d = 128, 256)
     clk = torch.zeros(8, 4, dtype=torch.int64, device="cuda")
     f.out.clock_probe = clk.data_ptr()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -612,7 +618,7 @@ def main():
                            "per_launch": f"{n_hist} tokens x {6 * d * h + 4 * d * d} flop + "
                                          f"{pairs} (token, target) pairs x {4 * d} flop"}}
     ghz = stca.clock_ghz(clk.cpu().numpy())
-    if args.path == "staged" and d == 256 and sp.dtype == "bf16" and ghz == ghz:
+    if args.path == "staged" and d in (128, 256) and sp.dtype == "bf16" and ghz == ghz:
         at_clk = PEAK_BF16_TFLOPS * ghz / NOMINAL_CLOCK_GHZ
         roof_hist.update({"shader_clock_ghz": round(ghz, 3), "peak_at_clock": round(at_clk, 1),
                           "frac_at_clock": round(hist_tf / at_clk, 4)})
@@ -623,7 +629,7 @@ def main():
     # LONGER encoding the short-row history chain and the encoder K/V chain are one kernel instance,
     # so a per-name average would mix them: neither gets a traffic figure.
     picks = {"history": lambda k: not longer and (
-                 k.startswith("hist256_kernel<") or k.startswith(f"hist_layers_kernel<{d},") or
+                 k.startswith("hist256_kernel<") or k.startswith("hist128_kernel<") or
                  (k.startswith(f"chain_kernel<{d},") and ", 0, true, " in k)),
              "attention": lambda k: k.startswith("attn_bf16_kernel<") and k.endswith("false>"),
              "encoder_attention": lambda k: k.startswith("attn_bf16_kernel<") and k.endswith("true>"),

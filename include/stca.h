@@ -247,7 +247,7 @@ typedef struct {
                           log of the rescaled sum; 0 for an empty history).  The backward
                           recomputes the weights exp(s_j - lse) from it. */
   uint64_t *clock_probe; /* [8][4] optional measurement aid, bf16 staged path at
-                          d = 256: workgroups 0..7 of the history-encoding launch (one
+                          d = 128 or 256: workgroups 0..7 of the history-encoding launch (one
                           per XCD under round-robin dispatch) write, from their first
                           wave, {shader-clock counter (s_memtime), 100 MHz counter
                           (s_memrealtime)} at their start and at their end.  The
@@ -386,10 +386,15 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
  * 32x32x16 MFMA products from registers (blocks * 4 * iters * 8 * 32768
  * flop), writing one checksum per wave to out[blocks * 4] (device, fp32).
  * Timed by the caller on `hip_stream`, it gives the matrix cores' attainable
- * rate at the clock the chip holds under that load.  clock (device,
- * optional, [4]): workgroup 0's {s_memtime, s_memrealtime} at its start and
- * end, as for stca_outputs.clock_probe.  Enqueued only; returns
- * STCA_ERR_INVALID_ARG for non-positive sizes or a NULL out. */
+ * rate at the clock the chip holds under that load.  The operands are fixed
+ * low-entropy values; with iters < 0 the kernel runs |iters| rounds on
+ * operands whose signs, exponents and mantissas vary like real data (four
+ * random A and B fragments per lane, a different pair for consecutive
+ * products): the chip's clock under MFMA load depends on how many operand
+ * bits switch, so this is the attainable rate for realistic operands.  clock
+ * (device, optional, [4]): workgroup 0's {s_memtime, s_memrealtime} at its
+ * start and end, as for stca_outputs.clock_probe.  Enqueued only; returns
+ * STCA_ERR_INVALID_ARG for blocks <= 0, iters = 0 or a NULL out. */
 int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, uint64_t *clock, void *hip_stream);
 
 /* Measurement aid, not a step of the method: `blocks` workgroups of 256

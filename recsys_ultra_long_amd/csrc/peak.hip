@@ -43,6 +43,58 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *out, u
   }
 }
 
+// The same product stream with operands whose bits vary like real data:
+// every lane holds four A and four B fragments of random signs, exponents
+// (magnitudes 2^-7 .. 2^-3) and mantissas, and consecutive products take
+// different ones, so the matrix cores switch as many operand bits as they do
+// on activations and weights (the chip's clock under MFMA load depends on it).
+// Random bits from the lowbias32 integer hash (C. Wellons) of
+// (block, lane, element).
+DEV uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+__global__ __launch_bounds__(256) void mfma_peak_mixed_kernel(int iters, float *out, unsigned long long *clock) {
+  const int lane = threadIdx.x & 63;
+  if (clock && blockIdx.x == 0 && threadIdx.x == 0) {
+    clock[0] = __builtin_amdgcn_s_memtime();
+    clock[1] = __builtin_amdgcn_s_memrealtime();
+  }
+  bf16x8 a[4], b[4];
+  const uint32_t seed = ((uint32_t)blockIdx.x * 256u + threadIdx.x) * 64u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ha = hash32(seed + 16u * i + e), hb = hash32(seed + 16u * i + 8u + e);
+      a[i][e] = (short)((ha & 0x807fu) | (0x3c00u + ((ha >> 16) & 3u) * 0x80u));
+      b[i][e] = (short)((hb & 0x807fu) | (0x3c00u + ((hb >> 16) & 3u) * 0x80u));
+    }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = mfma32(a[j & 3], b[(j + (j >> 2)) & 3], acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+  if (clock && blockIdx.x == 0 && threadIdx.x == 0) {
+    clock[2] = __builtin_amdgcn_s_memtime();
+    clock[3] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
 // Each thread reads four 16-byte words per round, one grid stride apart.
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *p, int64_t n, uint32_t *out) {
   uint32_t x = 0;
@@ -79,9 +131,14 @@ extern "C" int stca_peak_hbm_read(const void *buf, int64_t bytes, int32_t blocks
 extern "C" int stca_peak_mfma_bf16(int32_t blocks, int32_t iters, float *out, uint64_t *clock, void *hip_stream) {
   using namespace stca;
   api_clear_error();
-  if (blocks <= 0 || iters <= 0 || !out) return api_error(STCA_ERR_INVALID_ARG, "blocks, iters must be > 0, out non-NULL");
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, (int)iters, out,
-                     reinterpret_cast<unsigned long long *>(clock));
+  // iters < 0: the mixed-operand variant, |iters| rounds
+  if (blocks <= 0 || iters == 0 || !out) return api_error(STCA_ERR_INVALID_ARG, "blocks > 0, iters != 0, out non-NULL");
+  if (iters > 0)
+    hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, (int)iters,
+                       out, reinterpret_cast<unsigned long long *>(clock));
+  else
+    hipLaunchKernelGGL(mfma_peak_mixed_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
+                       (int)-iters, out, reinterpret_cast<unsigned long long *>(clock));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return api_error(STCA_ERR_HIP, "mfma peak launch: %s", hipGetErrorString(e));
   return STCA_OK;

@@ -533,10 +533,11 @@ def peak_hbm_read(nbytes: int = 2 << 30, blocks: int = 1024, repeats: int = 4) -
     return best
 
 
-def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3):
+def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3, mixed: bool = False):
     """Attainable dense bf16 MFMA rate (TFLOP/s), the best of `repeats` timed
     launches of the library's MFMA-only measurement kernel, and the shader
-    clock (GHz) during that launch."""
+    clock (GHz) during that launch.  ``mixed``: operands that vary like real
+    data (the kernel's iters < 0 mode)."""
     import torch
     lib = load()
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
@@ -544,7 +545,8 @@ def peak_mfma_bf16(blocks: int = 1024, iters: int = 20000, repeats: int = 3):
     s = torch.cuda.current_stream()
     flops = blocks * 4 * iters * 8 * 32768
     best, best_clk = 0.0, float("nan")
-    args = (blocks, iters, C.c_void_p(out.data_ptr()), C.c_void_p(clk.data_ptr()), C.c_void_p(s.cuda_stream))
+    args = (blocks, -iters if mixed else iters, C.c_void_p(out.data_ptr()), C.c_void_p(clk.data_ptr()),
+            C.c_void_p(s.cuda_stream))
     _check(lib.stca_peak_mfma_bf16(*args))
     for _ in range(repeats):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
