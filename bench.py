@@ -635,7 +635,9 @@ def main():
              "encoder_attention": lambda k: k.startswith("attn_bf16_kernel<") and k.endswith("true>"),
              "encoder_kv": lambda k: False,
              "fused": lambda k: k.startswith("fused256_kernel<") or k.startswith(f"fused_kernel<{d},")}
-    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}_{args.path}.md"))
+    rep = f"-x{args.replicas}" if args.replicas > 1 else ""
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{args.workload}{rep}_{args.path}"
+                                                                 f"{'_dedup' if args.dedup else ''}.md"))
     if tr is not None:
         for name, roof in roofs.items():
             hits = [v["hbm_bytes"] for k, v in tr["kernels"].items() if picks[name](k)]
