@@ -918,7 +918,7 @@ __global__ __launch_bounds__(256) void pack_batch_kernel(PackBatch pb) {
   const int kk = k0 % 32;
   uint32_t v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = t.src[(int64_t)(k0 + e) * t.N + n];
+  for (int e = 0; e < 8; ++e) v[e] = t.src_t ? t.src[(int64_t)n * t.K + k0 + e] : t.src[(int64_t)(k0 + e) * t.N + n];
   const u32x4 pk = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
   bf16_t *d;
   if (t.fmt == 1) {  // 16x16x32 A operand

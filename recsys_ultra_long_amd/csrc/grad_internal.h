@@ -86,6 +86,10 @@ hipError_t launch_ln_fwd(const float *y, int64_t R, int d, const float *g, const
 // accumulated (+=) over the rows through per-block partials `part`
 // (2 * ln_part_rows(R) * d floats).  g == nullptr: dY = dOut.
 int64_t ln_part_rows(int64_t R);
+// dg, db += the sums over nblk per-block partials [nblk, 2, d] (gain, then
+// bias) in `part`, folded in a fixed order; `part` holds 2 * (nblk + 64) * d
+// floats (the fold's slices follow the partials).
+hipError_t launch_ln_fold(float *part, int64_t nblk, int d, float *dg, float *db, hipStream_t s);
 hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, int64_t R, int d, const float *g,
                          void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s,
                          const int *dev_rows = nullptr);
@@ -97,6 +101,42 @@ hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float
 // table[ids[r], :] += rows[r, :] (atomic), ids outside the table skipped.
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
                               hipStream_t s, const int *dev_rows = nullptr);
+
+// ------------------------------------------------------------ history backward (d = 256)
+// One layer of the history encoder's backward on 128-row tiles in one launch
+// (hist_bwd_bf16.hip): the forward recomputed from the rows X, then
+// dX~ = dK W_K^T + dV W_V^T, the LN backward, dG = dY W2^T, the SwiGLU
+// backward and dX (+)= dH1 W1^T + dH3 W3^T.  It writes the operands of the
+// weight-gradient products (X~, G, dY, dH1 | dH3, bf16, row-major) and, with
+// LN, per-tile partial sums of the LN gain and bias gradients.
+struct HistBwdArgs {
+  int64_t R;              // rows (host bound)
+  const int *dev_rows;    // optional device count capping R
+  int hidden;             // multiple of 128
+  bool ln;
+  const bf16_t *x;        // [R, 256] the rows X
+  const bf16_t *dkv;      // [R, 512] dK | dV
+  // packed operands (launch_pack_batch): W1, W3 fmt 1 (K 256, N hidden);
+  // W2 fmt 0 (K hidden, N 256); W_K^T | W_V^T fmt 4 / 5 from transposed
+  // sources (K = N = 256); W2^T fmt 1 from a transposed source (K 256,
+  // N hidden); W1^T | W3^T fmt 4 / 5 from transposed sources (K hidden, N 256)
+  const bf16_t *w1p, *w3p, *w2p, *wkvt, *w2t, *w13t;
+  const float *ln_g, *ln_b;
+  bf16_t *xt;             // [R, 256] X~ = LN(Y)
+  bf16_t *g;              // [R, hidden] G
+  bf16_t *dy;             // [R, 256] dY
+  bf16_t *dh13;           // [R, 2 hidden] dH1 | dH3
+  bf16_t *hs;             // scratch: hist_bwd_scratch_elems(R, hidden)
+  float *dx;              // [R, 256] fp32
+  bool dx_acc;            // dX += (else dX =)
+  float *ln_part;         // [hist_bwd_tiles(R), 2, 256] (with LN)
+};
+inline bool hist_bwd256_ok(int d, int hidden) { return d == 256 && hidden >= 128 && hidden % 128 == 0; }
+inline int64_t hist_bwd_tiles(int64_t R) { return (R + 127) / 128; }
+inline int64_t hist_bwd_scratch_elems(int64_t R, int hidden) { return hist_bwd_tiles(R) * 128 * 2 * (int64_t)hidden; }
+// Elements of one layer's packed operands.
+inline int64_t hist_bwd_pack_elems(int d, int hidden) { return 6 * (int64_t)d * hidden + 2 * (int64_t)d * d; }
+hipError_t launch_hist_bwd256(const HistBwdArgs &a, hipStream_t s);
 
 // ------------------------------------------------------------ attention backward
 // Inputs per layer, all token-indexed: Q (scaled, bf16 [T, d]), K and V rows

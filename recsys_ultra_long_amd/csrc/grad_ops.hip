@@ -288,6 +288,17 @@ hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, 
   return hipGetLastError();
 }
 
+hipError_t launch_ln_fold(float *part, int64_t nblk, int d, float *dg, float *db, hipStream_t s) {
+  if (nblk <= 0) return hipSuccess;
+  float *part2 = part + nblk * 2 * d;
+  hipLaunchKernelGGL(ln_fold1_kernel, dim3((unsigned)((2 * d + 63) / 64), kFoldSlices), dim3(kT), 0, s, part, nblk,
+                     d, part2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ln_fold2_kernel, dim3(blocks(2 * d)), dim3(kT), 0, s, part2, d, dg, db);
+  return hipGetLastError();
+}
+
 hipError_t launch_add_rows(const float *src, int64_t lds, float *dst, int64_t ldd, int64_t R, int d, bool accumulate,
                            hipStream_t s) {
   if (R <= 0) return hipSuccess;

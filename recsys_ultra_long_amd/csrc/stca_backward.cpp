@@ -56,6 +56,10 @@ struct BwdLayout {
   size_t da_lo = 0, dsum = 0, part_dq = 0;
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
   size_t ln_part = 0, gemm_part = 0;
+  // d = 256 with hidden % 128 == 0: one fused launch per layer for the
+  // history side (its H1 / H3 scratch and per-layer packed operands)
+  bool fused_hist = false;
+  size_t HS = 0, bwpack = 0;
   int64_t max_chunks = 0;
   // STCA_FLAG_DEDUP: the history backward runs over Rh = drows unique rows
   bool dedup = false;
@@ -142,15 +146,21 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.max_chunks = max_chunks(R, cfg->B, kBwdChunkBlocks);
   L.part_dq = cv.take((size_t)attn_bwd_part_floats(L.max_chunks, (int)H, (int)dh) * 4);
   L.dKV = cv.take(R * 2 * d * 2);
+  L.fused_hist = hist_bwd256_ok((int)d, (int)h);
+  const bool fh = L.fused_hist;  // the fp32 row buffers are the unfused sequence's only
   L.X = cv.take(Rh * d * 2);
-  L.H13 = cv.take(Rh * 2 * h * 4);
+  L.H13 = cv.take(fh ? 0 : Rh * 2 * h * 4);
   L.G = cv.take(Rh * h * 2);
-  L.Y = cv.take(Rh * d * 4);
-  L.ST = cv.take(Rh * 2 * 4);
+  L.Y = cv.take(fh ? 0 : Rh * d * 4);
+  L.ST = cv.take(fh ? 0 : Rh * 2 * 4);
   L.XT = cv.take(Rh * d * 2);
-  L.dXT = cv.take(Rh * d * 4);
+  L.dXT = cv.take(fh ? 0 : Rh * d * 4);
   L.dY = cv.take(Rh * d * 2);
-  L.dG = cv.take(Rh * h * 4);
+  L.dG = cv.take(fh ? 0 : Rh * h * 4);
+  if (fh) {
+    L.HS = cv.take((size_t)hist_bwd_scratch_elems(Rh, (int)h) * 2);
+    L.bwpack = cv.take((size_t)M * hist_bwd_pack_elems((int)d, (int)h) * 2);
+  }
   L.dH13 = cv.take(Rh * 2 * h * 2);
   L.dX = cv.take(Rh * d * 4);
   if (L.dedup) {
@@ -434,6 +444,37 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     ua.out = at<bf16_t>(ws, L.dKVu);
     if ((e = launch_unique_sort(ua, s))) return hip_err("unique sort");
   }
+  // operands of the fused history backward, packed for its MFMA fragments
+  bf16_t *const bwpack = L.fused_hist ? at<bf16_t>(ws, L.bwpack) : nullptr;
+  const int64_t pk_layer = L.fused_hist ? hist_bwd_pack_elems(d, h) : 0;
+  const int64_t pk_dh = (int64_t)d * h, pk_dd = (int64_t)d * d;
+  auto pk = [&](int i, int which) -> bf16_t * {  // W1 W3 W2 W_KV^T W2^T W13^T
+    const int64_t off[6] = {0, pk_dh, 2 * pk_dh, 3 * pk_dh, 3 * pk_dh + 2 * pk_dd, 4 * pk_dh + 2 * pk_dd};
+    return bwpack + i * pk_layer + off[which];
+  };
+  if (L.fused_hist && R > 0) {
+    PackBatch pb;
+    int n = 0;
+    for (int i = 0; i < M && !e; ++i) {
+      const stca_layer &lw = w->layers[i];
+      const stca_ffn &f = lw.kv;
+      const PackDesc ds[8] = {
+          {(const bf16_t *)f.w1, pk(i, 0), d, h, 0, 1, 0},  {(const bf16_t *)f.w3, pk(i, 1), d, h, 0, 1, 0},
+          {(const bf16_t *)f.w2, pk(i, 2), h, d, 0, 0, 0},  {(const bf16_t *)lw.wk, pk(i, 3), d, d, 0, 4, 1},
+          {(const bf16_t *)lw.wv, pk(i, 3), d, d, 0, 5, 1}, {(const bf16_t *)f.w2, pk(i, 4), d, h, 0, 1, 1},
+          {(const bf16_t *)f.w1, pk(i, 5), h, d, 0, 4, 1},  {(const bf16_t *)f.w3, pk(i, 5), h, d, 0, 5, 1}};
+      for (const PackDesc &pd : ds) {
+        pb.m[n++] = pd;
+        if (n == kMaxPacks) {
+          e = launch_pack_batch(pb, n, s);
+          n = 0;
+          if (e) break;
+        }
+      }
+    }
+    if (!e && n) e = launch_pack_batch(pb, n, s);
+    if (e) return hip_err("pack");
+  }
   if ((e = rec(2))) return hip_err("stage event");
 
   // ---- 4. layers, last to first
@@ -523,6 +564,48 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       const stca_ffn &f = lw.kv;
       const stca_ffn_grad &fg = lg.kv;
       gdev = hdev;
+      if (L.fused_hist) {
+        // one launch for the row side, then the weight-gradient products
+        HistBwdArgs hb;
+        std::memset(&hb, 0, sizeof(hb));
+        hb.R = Rh;
+        hb.dev_rows = hdev;
+        hb.hidden = h;
+        hb.ln = kvln;
+        hb.x = X;
+        hb.dkv = dkvh;
+        hb.w1p = pk(i, 0);
+        hb.w3p = pk(i, 1);
+        hb.w2p = pk(i, 2);
+        hb.wkvt = pk(i, 3);
+        hb.w2t = pk(i, 4);
+        hb.w13t = pk(i, 5);
+        hb.ln_g = kvln ? f.ln_g : nullptr;
+        hb.ln_b = kvln ? f.ln_b : nullptr;
+        hb.xt = XT;
+        hb.g = G;
+        hb.dy = dY;
+        hb.dh13 = dH13;
+        hb.hs = at<bf16_t>(ws, L.HS);
+        hb.dx = dX;
+        hb.dx_acc = i != M - 1;
+        hb.ln_part = lnpart;
+        if ((e = launch_hist_bwd256(hb, s))) return hip_err("history backward");
+        if (kvln && (e = launch_ln_fold(lnpart, hist_bwd_tiles(Rh), d, fg.ln_g, fg.ln_b, s)))
+          return hip_err("ln fold");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dWk");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dWv");
+        if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dW1");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dW3");
+        gdev = nullptr;
+        if ((e = rec(ev + 2))) return hip_err("stage event");
+        continue;
+      }
       if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
       if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h3");
       if ((e = launch_swiglu_fwd(H13, Rh, h, G, true, s, hdev))) return hip_err("swiglu");

@@ -136,11 +136,14 @@ hipError_t launch_chain_f32(const ChainArgs &a, hipStream_t s);
 // fmt 1 packs for the 16x16x32 A operand instead (16-row tiles):
 //   element (n, k) -> ((n / 16 * NK + kb) * 64 + lane) * 8 + e,
 //   lane = 16 * ((k % 32) / 8) + n % 16,  e = k % 8.
+// src_t = 1: the source holds W^T instead ([N, K] row-major: element (n, k)
+// at src[n K + k]), for operands that are the transpose of a stored weight.
 struct PackDesc {
   const bf16_t *src;
   bf16_t *dst;
   int K, N, row_tile0;
   int fmt;
+  int src_t;
 };
 constexpr int kMaxPacks = 48;
 struct PackBatch {

@@ -185,6 +185,23 @@ def test_backward_matches_oracle(k):
     assert row_err(g["z"], zo) < TOL
 
 
+@pytest.mark.parametrize("over", [dict(kv_ln=False), dict(hidden=128), dict(hidden=256, M=2),
+                                  dict(hidden=384, B=2, L=650)])
+@pytest.mark.parametrize("dedup", [False, True])
+def test_backward_history_shapes(over, dedup):
+    """The d = 256 history backward runs as one launch per layer over hidden
+    chunks of 128: without the LN after the encoder, one to three chunks, and
+    row counts that leave a ragged last tile."""
+    sp = _small(3, **over)  # m = 24: enough targets for the query side's weight-gradient rows
+    p = I.make_problem(sp)
+    dz = I.upstream_grad(sp, p.n_tgt)
+    print(f"[bwd] history shapes {over} dedup={dedup}: n_hist={p.n_hist}", flush=True)
+    g = gpu_backward(p, dz, outputs=("table", "d_tgt") if dedup else ("table", "d_hist", "d_tgt"), dedup=dedup)
+    ref = OG.backward_problem(p, dz)
+    assert g["status"] == 0
+    compare_all(p, g, ref)
+
+
 @pytest.mark.parametrize("score", ["softmax", "relu"])
 def test_attention_backward_stepwise(score):
     """dQ, dK, dV of every layer at the operands the GPU used: its scaled Q,
