@@ -85,16 +85,28 @@ DEV void gather_tile(const ChainArgs &a, bf16_t *xs, int *s_id, int *s_tok, int6
   __syncthreads();
   const bf16_t *table = (const bf16_t *)a.table;
   constexpr int C8 = D / 8;
-  static_assert((R * C8) % NT == 0, "whole 16-byte pieces per thread");
+  constexpr int NL = R * C8 / NT;
+  static_assert(NL * NT == R * C8, "whole 16-byte pieces per thread");
+  // Every row load is issued before any is used (rows without a valid id
+  // read table row 0 and are replaced by zeros), so that all of them are in
+  // flight together rather than one round trip each.
+  u32x4 v[NL];
+  if (a.table_rows > 0) {
 #pragma unroll
-  for (int k = 0; k < R * C8 / NT; ++k) {
+    for (int k = 0; k < NL; ++k) {
+      const int e = tid + k * NT, r = e / C8, c = (e % C8) * 8;
+      const int id = s_id[r];
+      v[k] = *reinterpret_cast<const u32x4 *>(table + (int64_t)(id >= 0 ? id : 0) * D + c);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
     const int e = tid + k * NT, r = e / C8, c = (e % C8) * 8;
-    const int id = s_id[r];
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (id >= 0) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)id * D + c);
-    *reinterpret_cast<u32x4 *>(xs + r * XRLD + c) = v;
+    const uint32_t keep = s_id[r] >= 0 ? 0xffffffffu : 0u;  // (all ids invalid when the table is empty)
+    const u32x4 val = v[k] & keep;
+    *reinterpret_cast<u32x4 *>(xs + r * XRLD + c) = val;
     if (a.in_dump && s_tok[r] >= 0)
-      *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)s_tok[r] * D + c) = v;
+      *reinterpret_cast<u32x4 *>((bf16_t *)a.in_dump + (int64_t)s_tok[r] * D + c) = val;
   }
   __syncthreads();
 }
