@@ -208,9 +208,24 @@ def cpu_baseline_backward(p, dz, seconds):
                       "float64 numpy backward (forward recompute included)", **hi}
 
 
+def traffic_for(kernel_prefix, name):
+    """Calibrated HBM bytes per launch of the kernel whose name starts with
+    kernel_prefix, from profiles/traffic_<name>.md, or None when that summary
+    is missing or was taken on other kernel sources."""
+    from recsys_ultra_long_amd import profiling
+    tr = profiling.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{name}.md"))
+    if tr is None:
+        return None
+    hits = [v["hbm_bytes"] for k, v in tr["kernels"].items() if k.startswith(kernel_prefix)]
+    return round(max(hits)) if hits else None
+
+
 def bench_backward(args):
-    """One training step = stca_forward (fused path: z for the loss head) +
-    stca_backward (gradients of every weight and table row for a seeded dz)."""
+    """One training step = a forward (z for the loss head) + stca_backward
+    (gradients of every weight and table row for a seeded dz).  The forward is
+    stca_forward_for_backward, which leaves its activations in the backward's
+    workspace so that the backward skips its recompute; with --recompute it is
+    stca_forward on the fused path and the backward recomputes."""
     import numpy as np
     import torch
     from recsys_ultra_long_amd import inputs as I
@@ -223,18 +238,33 @@ def bench_backward(args):
     log(f"workload generated in {time.time() - t:.1f}s: B={sp.B} n_hist={p.n_hist} n_tgt={p.n_tgt}")
     dz_np = I.upstream_grad(sp, p.n_tgt)
     dz = torch.from_numpy(dz_np).cuda()
-    dp_f = stca.upload(p, path="fused")
-    dp_b = stca.upload(p, table=dp_f.table, dedup=args.dedup)
-    f = stca.Forward(dp_f, want=(), dumps=())
+    dp_b = stca.upload(p, dedup=args.dedup)
     M = sp.M
     nev = stca.n_backward_stage_events(M)
     evs = [stca.StageEvents(nev) for _ in range(args.steps)]
     bw = stca.Backward(dp_b, dz, outputs=("table",))
     log(f"backward workspace {bw.ws_bytes / 2**30:.2f} GiB")
+    if args.recompute:  # forward on the fused path, the backward recomputes its activations
+        dp_f = stca.upload(p, path="fused", table=dp_b.table)
+        fwd = stca.Forward(dp_f, want=(), dumps=())
+
+        def f():
+            fwd()
+
+        def b():
+            bw()
+    else:  # the forward keeps its activations in the backward's workspace
+        z = torch.empty((p.n_tgt, sp.d), dtype=torch.float32, device="cuda")
+
+        def f():
+            bw.forward_for_backward(z)
+
+        def b():
+            bw(saved_forward=True)
     for _ in range(args.warmup):
         bw.zero()
         f()
-        bw()
+        b()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -246,25 +276,29 @@ def bench_backward(args):
         ev[k][0].record()
         f()
         ev[k][1].record()
-        bw()
+        b()
         ev[k][2].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_f = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     ms_b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    if int(bw.status[0].item()) != 0 or int(f.status[0].item()) != 0:
+    if int(bw.status[0].item()) != 0 or (args.recompute and int(fwd.status[0].item()) != 0):
         raise SystemExit("device status flagged")
 
     def stage(i, j):
         return float(np.mean([e.elapsed(i, j) for e in evs]))
     recompute, zhead = stage(0, 1), stage(1, 2)
-    attn_b, qside, hist_b = [], [], []
-    for j in range(M):  # j-th layer processed: layer M-1-j
-        prev = 2 if j == 0 else 5 + 3 * (j - 1)
-        attn_b.append(stage(prev, 3 + 3 * j))
-        qside.append(stage(3 + 3 * j, 4 + 3 * j))
-        hist_b.append(stage(4 + 3 * j, 5 + 3 * j))
-    table_t = stage(5 + 3 * (M - 1), 3 + 3 * M)
+    attn_b, qside, hist_b, usum, hrows, hwgrad = [], [], [], [], [], []
+    for j in range(M):  # j-th layer processed: layer M-1-j (five events per layer)
+        b = 3 + 5 * j
+        prev = 2 if j == 0 else b - 1
+        attn_b.append(stage(prev, b))
+        qside.append(stage(b, b + 1))
+        hist_b.append(stage(b + 1, b + 4))
+        usum.append(stage(b + 1, b + 2))
+        hrows.append(stage(b + 2, b + 3))
+        hwgrad.append(stage(b + 3, b + 4))
+    table_t = stage(2 + 5 * M, 3 + 5 * M)
     for e in evs:
         e.close()
     d, h = sp.d, sp.hidden
@@ -284,13 +318,27 @@ def bench_backward(args):
     bytes_attn = n_hist * 8 * d + T * 4 * d
     t_attn = float(np.mean(attn_b)) * 1e-3
     attn_gbs = bytes_attn / t_attn / 1e9
-    roof_hist = {"kernel": "history backward stage of one layer (recomputed FFN+LN, dX, weight gradients: "
-                           "14 strided MFMA GEMMs + row kernels)", "bound": "mfma",
+    roof_hist = {"kernel": "history backward stage of one layer (per-unique-row dK | dV sums with dedup, "
+                           "the row pass, five split-K weight-gradient GEMMs)", "bound": "mfma",
                  "achieved": round(hist_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(hist_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                  "launch_ms": round(t_hist * 1e3, 4),
                  "per_launch": f"{rows_h} {'unique rows' if args.dedup else 'history items'} x "
                                f"{18 * d * h + 8 * d * d} flop"}
+    # the row pass alone: at d = 256 one launch (hist_bwd256_kernel): recomputed
+    # FFN 6dh, dX~ 4d^2, dG 2dh, dX 4dh per row
+    t_rows = float(np.mean(hrows)) * 1e-3
+    row_flops = 12 * d * h + 4 * d * d
+    rows_tf = rows_h * row_flops / t_rows / 1e12
+    roof_rows = {"kernel": "hist_bwd256_kernel (history backward row pass of one layer: recomputed FFN + LN, "
+                           "dX~, LN backward, dG, SwiGLU backward, dX)" if d == 256 and h % 128 == 0 else
+                           "history backward row pass of one layer (strided GEMMs + row kernels)",
+                 "bound": "mfma", "achieved": round(rows_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(rows_tf / PEAK_BF16_TFLOPS, 4),
+                 "traffic": traffic_for("hist_bwd256_kernel<true>", "rlb-train_backward"
+                                        + ("_dedup" if args.dedup else "")),
+                 "launch_ms": round(t_rows * 1e3, 4),
+                 "per_launch": f"{rows_h} {'unique rows' if args.dedup else 'history items'} x {row_flops} flop"}
     roof_attn = {"kernel": "attention backward of one layer (incl. W_O and the dQ fold)", "bound": "hbm",
                  "achieved": round(attn_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": round(attn_gbs / PEAK_HBM_GBS, 4), "traffic": None,
@@ -309,17 +357,23 @@ def bench_backward(args):
         "config": {"workload": f"{sp.name}: B={sp.B} users, L ~ max(16, ceil(10240 Beta({sp.beta_a},1))) "
                                f"(sum {n_hist}), m={sp.m} targets/user, table {sp.table_rows}x{d} bf16 "
                                f"Zipf({sp.zipf_s}) ids, d={d}, H={sp.H}, hidden={h}, M={M}, softmax; "
-                               "forward on the fused path, backward recomputes on the staged path"
+                               + ("forward on the fused path, backward recomputes on the staged path"
+                                  if args.recompute else "forward on the staged path keeping its activations "
+                                  "for the backward (stca_forward_for_backward)")
                                + (f", unique-id dedup of the history side ({n_unique} unique "
                                   f"of {n_hist})" if args.dedup else ""),
                    "global_batch": sp.B, "targets": T, "parallelism": "single GPU"},
-        "roofline": roof_hist if sum(hist_b) >= sum(attn_b) else roof_attn,
+        "roofline": roof_rows if sum(hrows) >= sum(attn_b) else roof_attn,
         "roofline_history_backward": roof_hist,
+        "roofline_history_row_pass": roof_rows,
         "roofline_attention_backward": roof_attn,
         "backward_stages_ms": {"forward_recompute": round(recompute, 4), "z_head": round(zhead, 4),
                                "attention_backward": [round(x, 4) for x in attn_b],
                                "query_side": [round(x, 4) for x in qside],
                                "history_backward": [round(x, 4) for x in hist_b],
+                               "history_unique_sums": [round(x, 4) for x in usum],
+                               "history_row_pass": [round(x, 4) for x in hrows],
+                               "history_weight_gradients": [round(x, 4) for x in hwgrad],
                                "table_scatter": round(table_t, 4)},
         "backward_tflops": round((flops_b + flops_f) / (ms_b * 1e-3) / 1e12, 2),
         "backward_flops": {"proper": flops_b, "recompute": flops_f},
@@ -416,6 +470,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward + stca_backward) on the training "
                          "workload (rlb-train unless --workload names another)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --backward: the step's forward on the fused path and the backward "
+                         "recomputing its activations (default: the forward keeps them)")
     ap.add_argument("--path", default="staged", choices=["staged", "fused"],
                     help="staged (default: K/V streamed through HBM, so the projection (MFMA) and "
                          "attention (HBM) stages are timed apart) or fused (no K/V in HBM)")

@@ -367,12 +367,21 @@ typedef struct {
    *   0            start of the call
    *   1            forward recompute done
    *   2            z head, history-row gather and (dedup) unique-row sort done
-   *   3 + 3j       layer i = M-1-j: output projection and attention backward done
-   *   4 + 3j       layer i: query side done
-   *   5 + 3j       layer i: history side done
-   *   3 + 3M       row gradients added to the table     (3M + 4 events in all) */
+   *   3 + 5j       layer i = M-1-j: output projection and attention backward done
+   *   4 + 5j       layer i: query side done
+   *   5 + 5j       layer i: (dedup) dK | dV summed per unique row
+   *   6 + 5j       layer i: history side's row pass done (recompute, dX; at d = 256
+   *                one fused launch, otherwise recorded with the next event)
+   *   7 + 5j       layer i: history side done (weight gradients)
+   *   3 + 5M       row gradients added to the table     (5M + 4 events in all) */
   void *const *stage_events;
   int32_t n_stage_events;
+  /* Nonzero: skip the forward recompute.  The caller has run
+   * stca_forward_for_backward with the same config, batch and weights on this
+   * workspace, and nothing has written the workspace since; its activations
+   * are used as they are (events 0 and 1 are recorded back to back).  z_out
+   * must then be NULL (z is that call's output). */
+  int32_t saved_forward;
 } stca_grads;
 
 int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch, size_t *bytes);
@@ -380,6 +389,19 @@ int stca_backward_workspace_size(const stca_config *cfg, const stca_batch *batch
 /* dz: [n_tgt, d] fp32 device array, the upstream gradient of z. */
 int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const float *dz,
                   const stca_grads *grads, void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* The forward of a training step, keeping its activations for the backward
+ * instead of having stca_backward recompute them: the same computation as
+ * stca_backward's recompute (the staged path, STCA_FLAG_DEDUP honoured, the
+ * same checks and the same results bit for bit), writing z [n_tgt, d] (fp32,
+ * required when n_tgt > 0) and leaving each layer's o, attention output,
+ * scaled Q, K/V rows and softmax lse in `workspace` (stca_backward's, of
+ * stca_backward_workspace_size bytes).  Then stca_backward with
+ * grads->saved_forward = 1 on the same workspace skips its recompute.  A
+ * training step saves the recompute this way at the cost of keeping the
+ * workspace between the two calls.  dev_status (optional): STCA_DEV_* bits. */
+int stca_forward_for_backward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, float *z,
+                              int32_t *dev_status, void *workspace, size_t ws_bytes, void *hip_stream);
 
 /* Measurement aid, not a step of the method: `blocks` workgroups of 256
  * threads, every wave doing `iters` rounds of 8 independent dense bf16

@@ -28,6 +28,8 @@ struct ForwardInternals {
 int forward_check(const stca_config *cfg, const stca_batch *batch, const stca_weights *w);
 int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
                            const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi);
+// The internals a forward of (cfg, batch) leaves in ws, without running it.
+void forward_internals(const stca_config *cfg, const stca_batch *batch, void *ws, ForwardInternals *fi);
 
 // ------------------------------------------------------------ generic GEMM
 // C(m, n) = alpha * sum_k A(m, k) B(k, n) + beta * C(m, n)

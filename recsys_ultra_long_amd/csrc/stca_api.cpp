@@ -547,6 +547,24 @@ int forward_check(const stca_config *cfg, const stca_batch *batch, const stca_we
   return validate_weights(cfg, w);
 }
 
+// Where the forward leaves its unique-row buffers in `ws` (STCA_FLAG_DEDUP).
+void set_internals(const Layout &L, void *ws, ForwardInternals *fi) {
+  std::memset(fi, 0, sizeof(*fi));
+  if (!L.dedup) return;
+  fi->dedup = true;
+  fi->tok2u = at<int>(ws, L.d_tok2u);
+  fi->uniq_rows = at<int>(ws, L.d_uniq);
+  fi->n_unique = at<int>(ws, L.d_small);
+  fi->drows = L.drows;
+  fi->ukv = at<bf16_t>(ws, L.ukv);
+  fi->ukv_layer_elems = L.ukv_layer / 2;
+  fi->vrows = at<bf16_t>(ws, L.vrows);
+}
+
+void forward_internals(const stca_config *cfg, const stca_batch *batch, void *ws, ForwardInternals *fi) {
+  set_internals(make_layout(cfg, batch), ws, fi);
+}
+
 int forward_with_internals(const stca_config *cfg, const stca_batch *batch, const stca_weights *w,
                            const stca_outputs *out, void *ws, size_t ws_bytes, void *stream, ForwardInternals *fi) {
   g_err[0] = 0;
@@ -844,16 +862,7 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
     uplan.prow = da.uniq_rows;
     n_unique = da.n_unique;
     tok2u = da.tok2u;
-    if (fi) {
-      fi->dedup = true;
-      fi->tok2u = tok2u;
-      fi->uniq_rows = da.uniq_rows;
-      fi->n_unique = n_unique;
-      fi->drows = L.drows;
-      fi->ukv = (const bf16_t *)ukvbase;
-      fi->ukv_layer_elems = L.ukv_layer / 2;
-      fi->vrows = at<bf16_t>(ws, L.vrows);
-    }
+    if (fi) set_internals(L, ws, fi);
   }
   // the encoder's view of the rows: the batch, or the unique ids
   auto enc_args = [&](int i) {

@@ -181,7 +181,8 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   return STCA_OK;
 }
 
-int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, const float *dz, const stca_grads *g) {
+// What the backward supports (also checked by stca_forward_for_backward).
+int validate_model(const stca_config *c, const stca_batch *b, const stca_weights *w) {
   if (!c) return api_error(STCA_ERR_INVALID_ARG, "config is NULL");
   if (!b) return api_error(STCA_ERR_INVALID_ARG, "batch is NULL");
   if (c->dtype != STCA_BF16) return api_error(STCA_ERR_UNSUPPORTED, "stca_backward is bf16 only");
@@ -197,10 +198,16 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
   if (b->max_tgt_per_user > 64)
     return api_error(STCA_ERR_UNSUPPORTED, "stca_backward serves at most 64 targets per user (got %d)",
                      b->max_tgt_per_user);
+  if (!w || !w->layers) return api_error(STCA_ERR_INVALID_ARG, "weights NULL");
+  return STCA_OK;
+}
+
+int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, const float *dz, const stca_grads *g) {
+  int r = validate_model(c, b, w);
+  if (r) return r;
   if (!g) return api_error(STCA_ERR_INVALID_ARG, "grads is NULL");
   if (b->n_tgt > 0 && !dz) return api_error(STCA_ERR_INVALID_ARG, "dz is NULL");
   if (dz && !aligned16(dz)) return api_error(STCA_ERR_INVALID_ARG, "dz not 16-byte aligned");
-  if (!w || !w->layers) return api_error(STCA_ERR_INVALID_ARG, "weights NULL");
   if (!g->layers) return api_error(STCA_ERR_INVALID_ARG, "grads->layers is NULL");
   const bool kvln = c->flags & STCA_FLAG_KV_LN, zln = c->flags & STCA_FLAG_Z_LN;
   auto ffn_ok = [&](const stca_ffn_grad &f, bool ln) {
@@ -222,6 +229,24 @@ int validate(const stca_config *c, const stca_batch *b, const stca_weights *w, c
 }
 
 template <typename T> T *at(void *ws, size_t off) { return reinterpret_cast<T *>((char *)ws + off); }
+
+// Step 1: the forward on the staged path into the backward's workspace,
+// keeping each layer's o, attention output, scaled Q, K/V rows (without
+// dedup) and softmax lse where the backward reads them; z into `z`.
+int recompute_forward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, const BwdLayout &L,
+                      void *ws, float *z, int32_t *dev_status, void *stream, ForwardInternals *fi) {
+  const stca_config fc = forward_cfg(cfg);
+  stca_outputs fo;
+  std::memset(&fo, 0, sizeof(fo));
+  fo.z = z;
+  fo.o_layers = at<float>(ws, L.o);
+  fo.attn = at<float>(ws, L.attn);
+  fo.q_dump = at<bf16_t>(ws, L.q);
+  fo.kv_dump = L.dedup ? nullptr : at<bf16_t>(ws, L.kv);
+  fo.lse = cfg->score == STCA_SCORE_SOFTMAX ? at<float>(ws, L.lse) : nullptr;
+  fo.dev_status = dev_status;
+  return forward_with_internals(&fc, batch, w, &fo, at<void>(ws, L.fws), L.fws_bytes, stream, fi);
+}
 
 }  // namespace
 
@@ -266,24 +291,22 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     return hipSuccess;
   };
 
-  // ---- 1. forward recompute (arguments checked before anything is enqueued)
+  // ---- 1. forward recompute (arguments checked before anything is enqueued),
+  // or the activations stca_forward_for_backward left in the workspace
   const stca_config fc = forward_cfg(cfg);
-  stca_outputs fo;
-  std::memset(&fo, 0, sizeof(fo));
-  float *z = gr->z_out ? gr->z_out : at<float>(ws, L.z);
   float *o_all = at<float>(ws, L.o), *a_all = at<float>(ws, L.attn), *lse_all = at<float>(ws, L.lse);
   bf16_t *q_all = at<bf16_t>(ws, L.q), *kv_all = at<bf16_t>(ws, L.kv);
-  fo.z = z;
-  fo.o_layers = o_all;
-  fo.attn = a_all;
-  fo.q_dump = q_all;
-  fo.kv_dump = L.dedup ? nullptr : kv_all;
-  fo.lse = cfg->score == STCA_SCORE_SOFTMAX ? lse_all : nullptr;
-  fo.dev_status = gr->dev_status;
   ForwardInternals fi;
   if ((r = forward_check(&fc, batch, w))) return r;
+  if (gr->saved_forward && gr->z_out)
+    return api_error(STCA_ERR_INVALID_ARG, "z_out must be NULL with saved_forward (z came from the saving forward)");
   if ((e = rec(0))) return hip_err("stage event");
-  if ((r = forward_with_internals(&fc, batch, w, &fo, at<void>(ws, L.fws), L.fws_bytes, stream, &fi))) return r;
+  if (gr->saved_forward) {
+    forward_internals(&fc, batch, at<void>(ws, L.fws), &fi);
+  } else {
+    float *z = gr->z_out ? gr->z_out : at<float>(ws, L.z);
+    if ((r = recompute_forward(cfg, batch, w, L, ws, z, gr->dev_status, stream, &fi))) return r;
+  }
   if ((e = rec(1))) return hip_err("stage event");
   const int64_t Rh = L.Rh;
   const int *hdev = L.dedup ? fi.n_unique : nullptr;  // device cap on the history backward's rows
@@ -524,7 +547,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     }
     if (gr->dq_dump && (e = launch_add_rows(dq, d, gr->dq_dump + (size_t)i * T * d, d, T, d, false, s)))
       return hip_err("dq dump");
-    const int ev = 3 + 3 * (M - 1 - i);
+    const int ev = 3 + 5 * (M - 1 - i);
     if ((e = rec(ev))) return hip_err("stage event");
     // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C
     const float *cin = xt;
@@ -561,6 +584,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         if ((e = launch_unique_sums(ua, s))) return hip_err("unique sums");
         dkvh = ua.out;
       }
+      if ((e = rec(ev + 2))) return hip_err("stage event");
       const stca_ffn &f = lw.kv;
       const stca_ffn_grad &fg = lg.kv;
       gdev = hdev;
@@ -591,6 +615,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         hb.dx_acc = i != M - 1;
         hb.ln_part = lnpart;
         if ((e = launch_hist_bwd256(hb, s))) return hip_err("history backward");
+        if ((e = rec(ev + 3))) return hip_err("stage event");
         if (kvln && (e = launch_ln_fold(lnpart, hist_bwd_tiles(Rh), d, fg.ln_g, fg.ln_b, s)))
           return hip_err("ln fold");
         if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad)))
@@ -603,7 +628,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
           return hip_err("dW3");
         gdev = nullptr;
-        if ((e = rec(ev + 2))) return hip_err("stage event");
+        if ((e = rec(ev + 4))) return hip_err("stage event");
         continue;
       }
       if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
@@ -634,7 +659,9 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         return hip_err("dx");
       gdev = nullptr;
     }
-    if ((e = rec(ev + 2))) return hip_err("stage event");
+    if (R == 0 && (e = rec(ev + 2))) return hip_err("stage event");
+    if ((e = rec(ev + 3))) return hip_err("stage event");
+    if ((e = rec(ev + 4))) return hip_err("stage event");
   }
 
   // ---- 5. row gradients into the table
@@ -643,8 +670,24 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       return hip_err("scatter");
     if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s))) return hip_err("scatter");
   }
-  if ((e = rec(3 + 3 * M))) return hip_err("stage event");
+  if ((e = rec(3 + 5 * M))) return hip_err("stage event");
   return STCA_OK;
+}
+
+int stca_forward_for_backward(const stca_config *cfg, const stca_batch *batch, const stca_weights *w, float *z,
+                              int32_t *dev_status, void *ws, size_t ws_bytes, void *stream) {
+  api_clear_error();
+  int r = validate_model(cfg, batch, w);
+  if (r) return r;
+  if (batch->n_tgt > 0 && !z) return api_error(STCA_ERR_INVALID_ARG, "z is NULL");
+  if (z && !aligned16(z)) return api_error(STCA_ERR_INVALID_ARG, "z not 16-byte aligned");
+  BwdLayout L;
+  if ((r = make_layout(cfg, batch, L))) return r;
+  if (!ws && L.total > 0) return api_error(STCA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total) return api_error(STCA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, L.total);
+  if (ws && !aligned16(ws)) return api_error(STCA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  ForwardInternals fi;
+  return recompute_forward(cfg, batch, w, L, ws, z ? z : at<float>(ws, L.z), dev_status, stream, &fi);
 }
 
 }  // extern "C"

@@ -29,7 +29,7 @@ DEV_BAD_HIST_OFFSETS, DEV_BAD_TGT_OFFSETS, DEV_BAD_ID = 1, 2, 4
 EXPORTS = ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
            "stca_attention", "stca_backward_workspace_size", "stca_backward",
            "stca_peak_mfma_bf16", "stca_peak_hbm_read", "stca_status_string", "stca_last_error",
-           "stca_version", "stca_forward_noalloc")
+           "stca_version", "stca_forward_noalloc", "stca_forward_for_backward")
 
 NOALLOC_SCRATCH_BYTES = 128 << 20   # STCA_NOALLOC_SCRATCH_BYTES
 
@@ -87,7 +87,7 @@ class Grads(C.Structure):
     _fields_ = [("layers", C.POINTER(LayerGrad)), ("z", FfnGrad), ("wz", _vp), ("table", _vp),
                 ("d_hist", _vp), ("d_tgt", _vp), ("z_out", _vp), ("dq_dump", _vp), ("da_dump", _vp),
                 ("dkv_dump", _vp), ("dev_status", _vp), ("stage_events", C.POINTER(_vp)),
-                ("n_stage_events", C.c_int32)]
+                ("n_stage_events", C.c_int32), ("saved_forward", C.c_int32)]
 
 
 class AttnArgs(C.Structure):
@@ -129,6 +129,8 @@ def load() -> C.CDLL:
                                                      C.POINTER(C.c_size_t)]
         lib.stca_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
                                       C.POINTER(Grads), _vp, C.c_size_t, _vp]
+        lib.stca_forward_for_backward.argtypes = [C.POINTER(Config), C.POINTER(Batch), C.POINTER(Weights), _vp,
+                                                  _vp, _vp, C.c_size_t, _vp]
         lib.stca_peak_mfma_bf16.argtypes = [C.c_int32, C.c_int32, _vp, _vp, _vp]
         lib.stca_peak_hbm_read.argtypes = [_vp, C.c_int64, C.c_int32, _vp, _vp]
         lib.stca_status_string.restype = C.c_char_p
@@ -137,7 +139,7 @@ def load() -> C.CDLL:
         lib.stca_version.restype = C.c_int
         for f in ("stca_workspace_size", "stca_forward", "stca_attention_workspace_size",
                   "stca_attention", "stca_backward_workspace_size", "stca_backward", "stca_peak_mfma_bf16",
-                  "stca_peak_hbm_read", "stca_forward_noalloc"):
+                  "stca_peak_hbm_read", "stca_forward_noalloc", "stca_forward_for_backward"):
             getattr(lib, f).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -302,7 +304,7 @@ def n_stage_events(M: int, longer: bool = False) -> int:
 
 
 def n_backward_stage_events(M: int) -> int:
-    return 3 * M + 4
+    return 5 * M + 4
 
 
 class Forward:
@@ -443,13 +445,27 @@ class Backward:
             self.table.zero_()
         return self
 
-    def __call__(self):
+    def __call__(self, saved_forward: bool = False):
+        """stca_backward; saved_forward: skip its recompute, using the
+        activations forward_for_backward() left in the workspace."""
         import torch
         s = self.stream if self.stream is not None else torch.cuda.current_stream()
+        self.g.saved_forward = 1 if saved_forward else 0
         _check(self.lib.stca_backward(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
                                       _ptr(self.dz), C.byref(self.g), self.ws.data_ptr(), self.ws_bytes,
                                       s.cuda_stream))
         return self
+
+    def forward_for_backward(self, z):
+        """stca_forward_for_backward into this call's workspace: z (fp32
+        [n_tgt, d] device tensor) is written, the activations stay for a
+        following ``self(saved_forward=True)``."""
+        import torch
+        s = self.stream if self.stream is not None else torch.cuda.current_stream()
+        _check(self.lib.stca_forward_for_backward(C.byref(self.dp.cfg), C.byref(self.b), C.byref(self.w),
+                                                  _ptr(z), _ptr(self.status), self.ws.data_ptr(), self.ws_bytes,
+                                                  s.cuda_stream))
+        return z
 
 
 def forward(dp: DeviceProblem, want=("o", "attn", "active"), dumps=()) -> dict:

@@ -437,3 +437,33 @@ def test_longer_workspace_and_rejections():
     n = C.c_size_t(0)
     assert lib.stca_backward_workspace_size(C.byref(c), C.byref(b), C.byref(n)) == stca.ERR_UNSUPPORTED
     assert "SwiGLU" in stca.last_error()
+
+
+def test_forward_for_backward_rejects_on_the_host():
+    """stca_forward_for_backward checks what the backward supports, z and the
+    workspace before anything is enqueued; stca_backward with saved_forward
+    refuses a z_out (z is the saving forward's output)."""
+    lib = stca.load()
+    w, keepw = _weights()
+    b = batch()
+    n = C.c_size_t(0)
+    assert lib.stca_backward_workspace_size(C.byref(cfg()), C.byref(b), C.byref(n)) == stca.OK
+
+    def ffb(c, z=FAKE, ws=FAKE, ws_bytes=None):
+        return lib.stca_forward_for_backward(C.byref(c), C.byref(b), C.byref(w), z, None, ws,
+                                             n.value if ws_bytes is None else ws_bytes, None)
+    assert ffb(cfg(dtype=stca.F32, d=64, H=2, hidden=64)) == stca.ERR_UNSUPPORTED
+    assert ffb(cfg(qmode=1)) == stca.ERR_UNSUPPORTED
+    assert ffb(cfg(), z=None) == stca.ERR_INVALID_ARG and "z" in stca.last_error()
+    assert ffb(cfg(), z=FAKE + 4) == stca.ERR_INVALID_ARG
+    assert ffb(cfg(), ws_bytes=n.value - 1) == stca.ERR_WORKSPACE
+    assert ffb(cfg(), ws=None) == stca.ERR_WORKSPACE
+    lg = (stca.LayerGrad * 4)()
+    fg = stca.FfnGrad(FAKE, FAKE, FAKE, FAKE, FAKE)
+    for i in range(4):
+        lg[i] = stca.LayerGrad(fg, fg, FAKE, FAKE, FAKE, FAKE, FAKE)
+    g = stca.Grads(lg, fg, FAKE)
+    g.z_out = FAKE
+    g.saved_forward = 1
+    r = lib.stca_backward(C.byref(cfg()), C.byref(b), C.byref(w), FAKE, C.byref(g), FAKE, n.value, None)
+    assert r == stca.ERR_INVALID_ARG and "saved_forward" in stca.last_error()

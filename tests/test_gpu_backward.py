@@ -202,6 +202,36 @@ def test_backward_history_shapes(over, dedup):
     compare_all(p, g, ref)
 
 
+@pytest.mark.parametrize("dedup", [False, True])
+def test_backward_with_saved_forward_equals_the_recompute(dedup):
+    """stca_forward_for_backward + stca_backward(saved_forward) is the same
+    computation as stca_backward's own recompute: z, every weight gradient and
+    the target rows bit for bit, a second saved step the same again; the table
+    gradient up to the order of its fp32 atomic adds (rows read more than once)."""
+    from recsys_ultra_long_amd import stca
+    p = I.make_problem(_small(6, B=6, score="relu") if dedup else _small(3, B=3))
+    dz = I.upstream_grad(p.spec, p.n_tgt)
+    ref = gpu_backward(p, dz, outputs=("table", "d_tgt", "z"), dedup=dedup)
+    dp = stca.upload(p, dedup=dedup)
+    dzt = torch.from_numpy(np.ascontiguousarray(dz, dtype=np.float32)).cuda()
+    bw = stca.Backward(dp, dzt, outputs=("table", "d_tgt"))
+    z = torch.empty((p.n_tgt, p.spec.d), dtype=torch.float32, device="cuda")
+    for step in range(2):
+        bw.zero()
+        z.fill_(float("nan"))
+        bw.forward_for_backward(z)
+        bw(saved_forward=True)
+        torch.cuda.synchronize()
+        assert int(bw.status[0].item()) == 0
+        assert np.array_equal(z.cpu().numpy(), ref["z"]), step
+        for path, v in leaves(ref["grads"]):
+            assert np.array_equal(get(bw.grads, path).cpu().numpy(), v), (step, path)
+        assert np.array_equal(bw.d_tgt.cpu().numpy(), ref["d_tgt"])
+        tab = bw.table.cpu().numpy()
+        scale = np.abs(ref["table"]).max(axis=1, keepdims=True)
+        assert np.all(np.abs(tab - ref["table"]) <= 1e-5 * np.maximum(scale, 1e-30))
+
+
 @pytest.mark.parametrize("score", ["softmax", "relu"])
 def test_attention_backward_stepwise(score):
     """dQ, dK, dV of every layer at the operands the GPU used: its scaled Q,
