@@ -289,13 +289,16 @@ def bench_backward(args):
         return float(np.mean([e.elapsed(i, j) for e in evs]))
     recompute, zhead = stage(0, 1), stage(1, 2)
     attn_b, qside, hist_b, usum, hrows, hwgrad = [], [], [], [], [], []
-    for j in range(M):  # j-th layer processed: layer M-1-j (five events per layer)
+    # j-th layer processed: layer M-1-j (five events per layer).  The history
+    # side runs on the library's second stream from the attention backward's
+    # end (event b) on, alongside the query side: its stages are timed from b.
+    for j in range(M):
         b = 3 + 5 * j
-        prev = 2 if j == 0 else b - 1
+        prev = 2 if j == 0 else b - 4  # the previous layer's query side
         attn_b.append(stage(prev, b))
         qside.append(stage(b, b + 1))
-        hist_b.append(stage(b + 1, b + 4))
-        usum.append(stage(b + 1, b + 2))
+        hist_b.append(stage(b, b + 4))
+        usum.append(stage(b, b + 2))
         hrows.append(stage(b + 2, b + 3))
         hwgrad.append(stage(b + 3, b + 4))
     table_t = stage(2 + 5 * M, 3 + 5 * M)

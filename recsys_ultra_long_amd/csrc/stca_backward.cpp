@@ -17,12 +17,18 @@
 //   4. per-item row gradients scattered into the table gradient.
 // Every product is one call of the strided GEMM (grad_gemm.hip); the
 // element-wise and row-wise derivatives are in grad_ops.hip; the attention
-// backward in attn_bwd.hip.  ([Review] 核心公式 for the layer and the fusion,
+// backward in attn_bwd.hip; at d = 256 the history side's row pass is one
+// launch (hist_bwd_bf16.hip).  The history side of each layer reads only that
+// layer's dK | dV and writes only dX and weight gradients, so it runs on a
+// second stream, forked after the layer's attention backward and joined
+// before the table scatter, overlapping the next layers' latency-bound
+// attention and query-side launches.  ([Review] 核心公式 for the layer and the fusion,
 // [Notes] §STCA for the history side reading the raw rows at every layer.)
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "grad_internal.h"
@@ -55,7 +61,7 @@ struct BwdLayout {
   size_t c = 0, h13 = 0, g = 0, y = 0, st = 0, qln = 0, dy = 0, dg = 0, dh13 = 0, dc = 0, da = 0, dq = 0;
   size_t da_lo = 0, dsum = 0, part_dq = 0;
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
-  size_t ln_part = 0, gemm_part = 0;
+  size_t ln_part = 0, gemm_part = 0, ln_part_h = 0, gemm_part_h = 0;
   // d = 256 with hidden % 128 == 0: one fused launch per layer for the
   // history side (its H1 / H3 scratch and per-layer packed operands)
   bool fused_hist = false;
@@ -105,6 +111,44 @@ int64_t part_floats_needed(int64_t d, int64_t h, int64_t M, int64_t R, int64_t T
   return best;
 }
 
+// ... and by the history side's weight-gradient products (K = its rows).
+int64_t part_floats_hist(int64_t d, int64_t h, int64_t R) {
+  int64_t best = 0;
+  for (auto mn : {std::make_pair(d, h), std::make_pair(h, d), std::make_pair(d, d)})
+    best = std::max(best, gemm_part_floats(mn.first, mn.second, split_weight_grad(mn.first, mn.second, R)));
+  return best;
+}
+
+// The history side's stream (one per device, default priority, created on
+// first use) and the events that fork it from the caller's stream per layer
+// and join it back.  Calls on one device are enqueued under a lock, so that
+// the events are not recorded by two calls at once.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork[16] = {}, join = nullptr;
+};
+constexpr int kSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kSideDevices];
+
+hipError_t side_stream(SideStream **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
+  SideStream &ss = g_side[dev];
+  if (!ss.s) {
+    hipStream_t st = nullptr;
+    if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    for (hipEvent_t &x : ss.fork)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    ss.s = st;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   const stca_config fc = forward_cfg(cfg);
   size_t fws = 0;
@@ -145,7 +189,7 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.dsum = cv.take(T * H * 4);
   L.max_chunks = max_chunks(R, cfg->B, kBwdChunkBlocks);
   L.part_dq = cv.take((size_t)attn_bwd_part_floats(L.max_chunks, (int)H, (int)dh) * 4);
-  L.dKV = cv.take(R * 2 * d * 2);
+  L.dKV = cv.take(M * R * 2 * d * 2);  // one per layer: the history side of a layer runs concurrently
   L.fused_hist = hist_bwd256_ok((int)d, (int)h);
   const bool fh = L.fused_hist;  // the fp32 row buffers are the unfused sequence's only
   L.X = cv.take(Rh * d * 2);
@@ -175,8 +219,10 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
     L.ppart = cv.take((size_t)agg_max_partials(R) * 2 * d * 4);
     L.dKVu = cv.take(Rh * 2 * d * 2);
   }
-  L.ln_part = cv.take((size_t)2 * ln_part_rows(std::max(Rh, T)) * d * 4);
-  L.gemm_part = cv.take((size_t)part_floats_needed(d, h, M, Rh, T) * 4);
+  L.ln_part = cv.take((size_t)2 * ln_part_rows(T) * d * 4);
+  L.gemm_part = cv.take((size_t)part_floats_needed(d, h, M, 0, T) * 4);
+  L.ln_part_h = cv.take((size_t)2 * ln_part_rows(Rh) * d * 4);  // the history side's own partials
+  L.gemm_part_h = cv.take((size_t)part_floats_hist(d, h, Rh) * 4);
   L.total = cv.off;
   return STCA_OK;
 }
@@ -285,11 +331,12 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   auto hip_err = [&](const char *what) { return api_error(STCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e)); };
   if (gr->n_stage_events < 0 || (gr->n_stage_events > 0 && !gr->stage_events))
     return api_error(STCA_ERR_INVALID_ARG, "stage_events inconsistent with n_stage_events");
-  auto rec = [&](int k) -> hipError_t {
+  auto rec_on = [&](int k, hipStream_t st) -> hipError_t {
     if (k < gr->n_stage_events && gr->stage_events[k])
-      return hipEventRecord(reinterpret_cast<hipEvent_t>(gr->stage_events[k]), s);
+      return hipEventRecord(reinterpret_cast<hipEvent_t>(gr->stage_events[k]), st);
     return hipSuccess;
   };
+  auto rec = [&](int k) { return rec_on(k, s); };
 
   // ---- 1. forward recompute (arguments checked before anything is enqueued),
   // or the activations stca_forward_for_backward left in the workspace
@@ -300,6 +347,11 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   if ((r = forward_check(&fc, batch, w))) return r;
   if (gr->saved_forward && gr->z_out)
     return api_error(STCA_ERR_INVALID_ARG, "z_out must be NULL with saved_forward (z came from the saving forward)");
+  // every argument is checked: from here on work is enqueued
+  std::lock_guard<std::mutex> side_lock(g_side_mu);
+  SideStream *side = nullptr;
+  if ((e = side_stream(&side))) return hip_err("history stream");
+  bool forked = false;
   if ((e = rec(0))) return hip_err("stage event");
   if (gr->saved_forward) {
     forward_internals(&fc, batch, at<void>(ws, L.fws), &fi);
@@ -314,8 +366,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   float *dX = gr->d_hist ? gr->d_hist : at<float>(ws, L.dX);
   float *dxt = gr->d_tgt ? gr->d_tgt : at<float>(ws, L.dxt);
   float *gpart = at<float>(ws, L.gemm_part);
-  const int64_t gpart_cap = part_floats_needed(d, h, M, L.Rh, T);
+  const int64_t gpart_cap = part_floats_needed(d, h, M, 0, T);
   float *lnpart = at<float>(ws, L.ln_part);
+  float *gpart_h = at<float>(ws, L.gemm_part_h), *lnpart_h = at<float>(ws, L.ln_part_h);
+  const int64_t gpart_h_cap = part_floats_hist(d, h, L.Rh);
   if (T == 0 || B == 0) {  // nothing reads the history: every gradient is zero
     if (gr->d_hist && R > 0) {  // K = 0 product: writes beta * C = 0
       GemmArgs z0;
@@ -337,6 +391,9 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
 
   // ---- GEMM helper: C = alpha * A B + beta * C with explicit strides
   const int *gdev = nullptr;  // device cap applied by gemm(): rows (M) or, for split products, K
+  hipStream_t gs = s;         // stream and split-K partials of gemm(): the caller's, or the history side's
+  float *gp = gpart;
+  int64_t gcap = gpart_cap;
   // kind: kWgrad = a weight gradient (K = rows, split along K); kTgt = a
   // product over the target rows (split along the width when it has few
   // output tiles); kHist = a product over the history rows (never split:
@@ -364,11 +421,11 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     g.alpha = alpha;
     g.beta = beta;
     g.split = kind == kWgrad ? split_weight_grad(Mm, Nn, Kk) : kind == kTgt ? split_rows(Mm, Nn, Kk) : 1;
-    g.part = gpart;
-    g.part_cap = gpart_cap;
+    g.part = gp;
+    g.part_cap = gcap;
     g.dev_rows = gdev;
     g.dev_dim = gdev ? (kind == kWgrad ? 2 : 1) : 0;
-    return launch_gemm(g, s);
+    return launch_gemm(g, gs);
   };
   // ---- 2. planner for the attention backward (its own chunking)
   Plan plan;
@@ -512,7 +569,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     if (gr->da_dump && (e = launch_add_rows(da, d, gr->da_dump + (size_t)i * T * d, d, T, d, false, s)))
       return hip_err("da dump");
     // attention backward
-    bf16_t *dkv = gr->dkv_dump ? (bf16_t *)gr->dkv_dump + (size_t)i * R * 2 * d : at<bf16_t>(ws, L.dKV);
+    bf16_t *dkv = (gr->dkv_dump ? (bf16_t *)gr->dkv_dump : at<bf16_t>(ws, L.dKV)) + (size_t)i * R * 2 * d;
     {
       AttnBwdArgs ab;
       std::memset(&ab, 0, sizeof(ab));
@@ -549,6 +606,105 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       return hip_err("dq dump");
     const int ev = 3 + 5 * (M - 1 - i);
     if ((e = rec(ev))) return hip_err("stage event");
+    // history side of layer i, over the history items or (dedup) the unique
+    // rows with each row's dK | dV summed over its items: on the side stream,
+    // forked here (the layer's dK | dV are written)
+    if (R > 0) {
+      hipStream_t hs = side->s;
+      if ((e = hipEventRecord(side->fork[i], s)) || (e = hipStreamWaitEvent(hs, side->fork[i], 0)))
+        return hip_err("history stream fork");
+      forked = true;
+      const bf16_t *dkvh = dkv;
+      if (L.dedup) {
+        ua.dkv = dkv;
+        if ((e = launch_unique_sums(ua, hs))) return hip_err("unique sums");
+        dkvh = ua.out;
+      }
+      if ((e = rec_on(ev + 2, hs))) return hip_err("stage event");
+      const stca_ffn &f = lw.kv;
+      const stca_ffn_grad &fg = lg.kv;
+      gdev = hdev;
+      gs = hs;
+      gp = gpart_h;
+      gcap = gpart_h_cap;
+      if (L.fused_hist) {
+        // one launch for the row side, then the weight-gradient products
+        HistBwdArgs hb;
+        std::memset(&hb, 0, sizeof(hb));
+        hb.R = Rh;
+        hb.dev_rows = hdev;
+        hb.hidden = h;
+        hb.ln = kvln;
+        hb.x = X;
+        hb.dkv = dkvh;
+        hb.w1p = pk(i, 0);
+        hb.w3p = pk(i, 1);
+        hb.w2p = pk(i, 2);
+        hb.wkvt = pk(i, 3);
+        hb.w2t = pk(i, 4);
+        hb.w13t = pk(i, 5);
+        hb.ln_g = kvln ? f.ln_g : nullptr;
+        hb.ln_b = kvln ? f.ln_b : nullptr;
+        hb.xt = XT;
+        hb.g = G;
+        hb.dy = dY;
+        hb.dh13 = dH13;
+        hb.hs = at<bf16_t>(ws, L.HS);
+        hb.dx = dX;
+        hb.dx_acc = i != M - 1;
+        hb.ln_part = lnpart_h;
+        if ((e = launch_hist_bwd256(hb, hs))) return hip_err("history backward");
+        if ((e = rec_on(ev + 3, hs))) return hip_err("stage event");
+        if (kvln && (e = launch_ln_fold(lnpart_h, hist_bwd_tiles(Rh), d, fg.ln_g, fg.ln_b, hs)))
+          return hip_err("ln fold");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dWk");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dWv");
+        if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dW1");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dW3");
+      } else {
+        if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
+        if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h3");
+        if ((e = launch_swiglu_fwd(H13, Rh, h, G, true, hs, hdev))) return hip_err("swiglu");
+        if ((e = gemm(Rh, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, kHist))) return hip_err("y");
+        if ((e = launch_ln_fwd(Y, Rh, d, kvln ? f.ln_g : nullptr, f.ln_b, XT, true, ST, hs, hdev))) return hip_err("ln");
+        // dXt = dK W_K^T + dV W_V^T; dW_K += Xt^T dK, dW_V += Xt^T dV
+        if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, kHist))) return hip_err("dxt");
+        if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, kHist)))
+          return hip_err("dxt");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWk");
+        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dWv");
+        if ((e = launch_ln_bwd(dXT, Y, ST, Rh, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart_h, hs,
+                               hdev)))
+          return hip_err("ln backward");
+        // dG = dY W2^T, dW2 += G^T dY
+        if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, kHist))) return hip_err("dg");
+        if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
+        if ((e = launch_swiglu_bwd(dG, H13, Rh, h, dH13, true, hs, hdev))) return hip_err("swiglu backward");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return hip_err("dW1");
+        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
+          return hip_err("dW3");
+        const float beta0 = i == M - 1 ? 0.f : 1.f;
+        if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, kHist)))
+          return hip_err("dx");
+        if ((e = gemm(Rh, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, kHist)))
+          return hip_err("dx");
+        if ((e = rec_on(ev + 3, hs))) return hip_err("stage event");
+      }
+      if ((e = rec_on(ev + 4, hs))) return hip_err("stage event");
+      gdev = nullptr;
+      gs = s;
+      gp = gpart;
+      gcap = gpart_cap;
+    } else {
+      for (int k = 2; k <= 4; ++k)
+        if ((e = rec(ev + k))) return hip_err("stage event");
+    }
     // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C
     const float *cin = xt;
     if (i > 0) {
@@ -575,96 +731,12 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
     }
     if ((e = rec(ev + 1))) return hip_err("stage event");
-    // history side of layer i, over the history items or (dedup) the unique
-    // rows with each row's dK | dV summed over its items
-    if (R > 0) {
-      const bf16_t *dkvh = dkv;
-      if (L.dedup) {
-        ua.dkv = dkv;
-        if ((e = launch_unique_sums(ua, s))) return hip_err("unique sums");
-        dkvh = ua.out;
-      }
-      if ((e = rec(ev + 2))) return hip_err("stage event");
-      const stca_ffn &f = lw.kv;
-      const stca_ffn_grad &fg = lg.kv;
-      gdev = hdev;
-      if (L.fused_hist) {
-        // one launch for the row side, then the weight-gradient products
-        HistBwdArgs hb;
-        std::memset(&hb, 0, sizeof(hb));
-        hb.R = Rh;
-        hb.dev_rows = hdev;
-        hb.hidden = h;
-        hb.ln = kvln;
-        hb.x = X;
-        hb.dkv = dkvh;
-        hb.w1p = pk(i, 0);
-        hb.w3p = pk(i, 1);
-        hb.w2p = pk(i, 2);
-        hb.wkvt = pk(i, 3);
-        hb.w2t = pk(i, 4);
-        hb.w13t = pk(i, 5);
-        hb.ln_g = kvln ? f.ln_g : nullptr;
-        hb.ln_b = kvln ? f.ln_b : nullptr;
-        hb.xt = XT;
-        hb.g = G;
-        hb.dy = dY;
-        hb.dh13 = dH13;
-        hb.hs = at<bf16_t>(ws, L.HS);
-        hb.dx = dX;
-        hb.dx_acc = i != M - 1;
-        hb.ln_part = lnpart;
-        if ((e = launch_hist_bwd256(hb, s))) return hip_err("history backward");
-        if ((e = rec(ev + 3))) return hip_err("stage event");
-        if (kvln && (e = launch_ln_fold(lnpart, hist_bwd_tiles(Rh), d, fg.ln_g, fg.ln_b, s)))
-          return hip_err("ln fold");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dWk");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dWv");
-        if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dW1");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dW3");
-        gdev = nullptr;
-        if ((e = rec(ev + 4))) return hip_err("stage event");
-        continue;
-      }
-      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
-      if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h3");
-      if ((e = launch_swiglu_fwd(H13, Rh, h, G, true, s, hdev))) return hip_err("swiglu");
-      if ((e = gemm(Rh, d, h, G, true, h, 1, f.w2, true, d, 1, Y, d, 1, 1.f, 0.f, kHist))) return hip_err("y");
-      if ((e = launch_ln_fwd(Y, Rh, d, kvln ? f.ln_g : nullptr, f.ln_b, XT, true, ST, s, hdev))) return hip_err("ln");
-      // dXt = dK W_K^T + dV W_V^T; dW_K += Xt^T dK, dW_V += Xt^T dV
-      if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, kHist))) return hip_err("dxt");
-      if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, kHist)))
-        return hip_err("dxt");
-      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWk");
-      if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
-        return hip_err("dWv");
-      if ((e = launch_ln_bwd(dXT, Y, ST, Rh, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart, s, hdev)))
-        return hip_err("ln backward");
-      // dG = dY W2^T, dW2 += G^T dY
-      if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, kHist))) return hip_err("dg");
-      if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
-      if ((e = launch_swiglu_bwd(dG, H13, Rh, h, dH13, true, s, hdev))) return hip_err("swiglu backward");
-      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return hip_err("dW1");
-      if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
-        return hip_err("dW3");
-      const float beta0 = i == M - 1 ? 0.f : 1.f;
-      if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, kHist)))
-        return hip_err("dx");
-      if ((e = gemm(Rh, d, h, dH13 + h, true, 2 * h, 1, f.w3, true, 1, h, dX, d, 1, 1.f, 1.f, kHist)))
-        return hip_err("dx");
-      gdev = nullptr;
-    }
-    if (R == 0 && (e = rec(ev + 2))) return hip_err("stage event");
-    if ((e = rec(ev + 3))) return hip_err("stage event");
     if ((e = rec(ev + 4))) return hip_err("stage event");
   }
 
-  // ---- 5. row gradients into the table
+  // ---- 5. row gradients into the table, once the history side is done
+  if (forked && ((e = hipEventRecord(side->join, side->s)) || (e = hipStreamWaitEvent(s, side->join, 0))))
+    return hip_err("history stream join");
   if (gr->table) {
     if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev)))
       return hip_err("scatter");
