@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, int64_t kchunk, b
         if (SPLIT) {
           g.part[((int64_t)blockIdx.z * g.M + m) * g.N + n] = acc[i][j][r];
         } else {
-          float *c = Cb + m * g.scm + n * g.scn;
+          float *c = g.C2 && n >= g.n_split ? g.C2 + m * g.scm + (n - g.n_split) * g.scn : Cb + m * g.scm + n * g.scn;
           const float v = g.alpha * acc[i][j][r];
           *c = g.beta != 0.f ? v + g.beta * *c : v;
         }
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g, int split
   const int64_t m = e / g.N, n = e % g.N;
   float s = 0.f;
   for (int z = 0; z < split; ++z) s += g.part[((int64_t)b * stride + z) * MN + e];
-  float *c = g.C + b * g.bsc + m * g.scm + n * g.scn;
+  float *c = g.C2 && n >= g.n_split ? g.C2 + m * g.scm + (n - g.n_split) * g.scn : g.C + b * g.bsc + m * g.scm + n * g.scn;
   const float v = g.alpha * s;
   *c = g.beta != 0.f ? v + g.beta * *c : v;
 }
@@ -293,6 +293,7 @@ int gemm_split_for(int64_t M, int64_t N, int64_t K, int64_t target, int64_t min_
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (!((g.sak == 1 || g.sam == 1) && (g.sbk == 1 || g.sbn == 1))) return hipErrorInvalidValue;
+  if (g.C2 && (g.batch > 1 || g.n_split <= 0 || g.n_split >= g.N)) return hipErrorInvalidValue;
   if (g.K <= 0) {  // empty sum: C = beta * C
     GemmArgs z = g;
     z.split = 1;

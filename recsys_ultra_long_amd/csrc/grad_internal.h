@@ -61,6 +61,11 @@ struct GemmArgs {
   // elements further (with split > 1 the partials are [batch][split][M][N])
   int batch;
   int64_t bsa, bsb, bsc;
+  // optional second output: columns n >= n_split go to C2 (column n - n_split,
+  // same strides), e.g. two weight gradients with one shared operand as one
+  // product (no batching with it)
+  float *C2;
+  int64_t n_split;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 // Split factor for a long-K product (weight gradients), and the partial

@@ -114,7 +114,7 @@ int64_t part_floats_needed(int64_t d, int64_t h, int64_t M, int64_t R, int64_t T
 // ... and by the history side's weight-gradient products (K = its rows).
 int64_t part_floats_hist(int64_t d, int64_t h, int64_t R) {
   int64_t best = 0;
-  for (auto mn : {std::make_pair(d, h), std::make_pair(h, d), std::make_pair(d, d)})
+  for (auto mn : {std::make_pair(d, 2 * h), std::make_pair(h, d), std::make_pair(d, 2 * d)})
     best = std::max(best, gemm_part_floats(mn.first, mn.second, split_weight_grad(mn.first, mn.second, R)));
   return best;
 }
@@ -401,7 +401,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   enum { kHist = 0, kWgrad = 1, kTgt = 2 };
   auto gemm = [&](int64_t Mm, int64_t Nn, int64_t Kk, const void *A, bool abf, int64_t sam, int64_t sak,
                   const void *Bp, bool bbf, int64_t sbk, int64_t sbn, float *C, int64_t scm, int64_t scn, float alpha,
-                  float beta, int kind) -> hipError_t {
+                  float beta, int kind, float *C2 = nullptr, int64_t n_split = 0) -> hipError_t {
     GemmArgs g;
     std::memset(&g, 0, sizeof(g));
     g.M = Mm;
@@ -425,6 +425,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     g.part_cap = gcap;
     g.dev_rows = gdev;
     g.dev_dim = gdev ? (kind == kWgrad ? 2 : 1) : 0;
+    g.C2 = C2;
+    g.n_split = n_split;
     return launch_gemm(g, gs);
   };
   // ---- 2. planner for the attention backward (its own chunking)
@@ -657,15 +659,12 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         if ((e = rec_on(ev + 3, hs))) return hip_err("stage event");
         if (kvln && (e = launch_ln_fold(lnpart_h, hist_bwd_tiles(Rh), d, fg.ln_g, fg.ln_b, hs)))
           return hip_err("ln fold");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dWk");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dWv");
+        // [dW_K | dW_V] += X~^T [dK | dV], dW2 += G^T dY, [dW1 | dW3] += X^T [dH1 | dH3]
+        if ((e = gemm(d, 2 * d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad, lg.wv, d)))
+          return hip_err("dWk | dWv");
         if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dW1");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dW3");
+        if ((e = gemm(d, 2 * h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad, fg.w3, h)))
+          return hip_err("dW1 | dW3");
       } else {
         if ((e = gemm(Rh, h, d, X, true, d, 1, f.w1, true, h, 1, H13, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h1");
         if ((e = gemm(Rh, h, d, X, true, d, 1, f.w3, true, h, 1, H13 + h, 2 * h, 1, 1.f, 0.f, kHist))) return hip_err("h3");
@@ -676,9 +675,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         if ((e = gemm(Rh, d, d, dkvh, true, 2 * d, 1, lw.wk, true, 1, d, dXT, d, 1, 1.f, 0.f, kHist))) return hip_err("dxt");
         if ((e = gemm(Rh, d, d, dkvh + d, true, 2 * d, 1, lw.wv, true, 1, d, dXT, d, 1, 1.f, 1.f, kHist)))
           return hip_err("dxt");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWk");
-        if ((e = gemm(d, d, Rh, XT, true, 1, d, dkvh + d, true, 2 * d, 1, lg.wv, d, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dWv");
+        if ((e = gemm(d, 2 * d, Rh, XT, true, 1, d, dkvh, true, 2 * d, 1, lg.wk, d, 1, 1.f, 1.f, kWgrad, lg.wv, d)))
+          return hip_err("dWk | dWv");
         if ((e = launch_ln_bwd(dXT, Y, ST, Rh, d, kvln ? f.ln_g : nullptr, dY, true, fg.ln_g, fg.ln_b, lnpart_h, hs,
                                hdev)))
           return hip_err("ln backward");
@@ -686,9 +684,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
         if ((e = gemm(Rh, h, d, dY, true, d, 1, f.w2, true, 1, d, dG, h, 1, 1.f, 0.f, kHist))) return hip_err("dg");
         if ((e = gemm(h, d, Rh, G, true, 1, h, dY, true, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dW2");
         if ((e = launch_swiglu_bwd(dG, H13, Rh, h, dH13, true, hs, hdev))) return hip_err("swiglu backward");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return hip_err("dW1");
-        if ((e = gemm(d, h, Rh, X, true, 1, d, dH13 + h, true, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad)))
-          return hip_err("dW3");
+        if ((e = gemm(d, 2 * h, Rh, X, true, 1, d, dH13, true, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad, fg.w3, h)))
+          return hip_err("dW1 | dW3");
         const float beta0 = i == M - 1 ? 0.f : 1.f;
         if ((e = gemm(Rh, d, h, dH13, true, 2 * h, 1, f.w1, true, 1, h, dX, d, 1, 1.f, beta0, kHist)))
           return hip_err("dx");
