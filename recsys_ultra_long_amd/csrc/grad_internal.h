@@ -206,10 +206,13 @@ struct UniqueSumArgs {
   const bf16_t *dkv;      // [n, d2]
   int d2;
   float *ppart;           // [agg_max_partials(n), d2] (scratch)
+  int *p2u;               // [agg_max_pieces(n, max_u)] (scratch): the unique row of every piece
+  int *cnt;               // [max_u] (scratch): pieces of a row done (zero between calls)
   bf16_t *out;            // [max_u, d2]
   const int *sorted_items;  // set by launch_unique_sort (points into vals)
 };
 int64_t agg_max_partials(int64_t n);
+int64_t agg_max_pieces(int64_t n, int64_t max_u);
 // Once per batch: the items sorted by (unique row, item) and the run / piece
 // offsets; then per layer: the sums of that layer's dkv.
 hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s);

@@ -184,17 +184,31 @@ __global__ __launch_bounds__(kT) void pieces_kernel(const int *__restrict__ seg,
   mp[u] = b;
 }
 
+// The unique row of every piece, and a zero count of finished pieces per row.
+__global__ __launch_bounds__(kT) void p2u_kernel(const int *__restrict__ poff, const int *n_unique, int64_t max_u,
+                                                 int *p2u, int *cnt) {
+  const int64_t u = (int64_t)blockIdx.x * kT + threadIdx.x;
+  if (u >= max_u) return;
+  cnt[u] = 0;
+  if (u >= *n_unique) return;
+  for (int p = poff[u]; p < poff[u + 1]; ++p) p2u[p] = (int)u;
+}
+
 // One wave per piece: the fp32 sum of its items' dK | dV rows (2d bf16
-// values per row, 8 per lane per 512-value chunk), in item order.
+// values per row, 8 per lane per 512-value chunk), in item order.  A row of
+// one piece is written at once; a row of several leaves one partial per
+// piece, and the wave that finishes the row's last piece (a per-row count,
+// after a device-scope fence) folds them in piece order and clears the count.
 __global__ __launch_bounds__(kT) void agg_kernel(const bf16_t *__restrict__ dkv, const int *__restrict__ stok,
                                                  const int *__restrict__ seg, const int *__restrict__ poff,
-                                                 const int *__restrict__ moff, const int *n_unique, int d2,
-                                                 int64_t max_pieces, bf16_t *out, float *ppart) {
+                                                 const int *__restrict__ moff, const int *__restrict__ p2u,
+                                                 const int *n_unique, int d2, int64_t max_pieces, bf16_t *out,
+                                                 float *ppart, int *cnt) {
   const int lane = threadIdx.x & 63;
   const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int U = *n_unique;
   if (p >= max_pieces || p >= poff[U]) return;
-  const int u = upper_index(poff, U, (int)p);
+  const int u = p2u[p];
   const int k = (int)(p - poff[u]);
   const int npu = poff[u + 1] - poff[u];
   const int i0 = seg[u] + k * kPiece;
@@ -227,29 +241,28 @@ __global__ __launch_bounds__(kT) void agg_kernel(const bf16_t *__restrict__ dkv,
       for (int e = 0; e < 8; ++e) pp[e] = acc[e];
     }
   }
-}
-
-// rows with several pieces: their partials folded in piece order
-__global__ __launch_bounds__(kT) void agg_fold_kernel(const int *__restrict__ poff, const int *__restrict__ moff,
-                                                      const int *n_unique, int d2, int64_t max_u,
-                                                      const float *__restrict__ ppart, bf16_t *out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (u >= max_u || u >= *n_unique) return;
-  const int npu = poff[u + 1] - poff[u];
-  if (npu <= 1) return;
+  if (npu == 1) return;
+  __threadfence();  // this piece's partial is visible device-wide
+  int done = 0;
+  if (lane == 0) done = atomicAdd(&cnt[u], 1);
+  done = __shfl(done, 0);
+  if (done != npu - 1) return;
+  __threadfence();
+  // the row's last piece: fold all of its partials in piece order (loads
+  // that bypass this CU's cache: other workgroups wrote them)
   for (int f0 = lane * 8; f0 < d2; f0 += 512) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < npu; ++k) {
-      const float *pp = ppart + (int64_t)(moff[u] + k) * d2 + f0;
+    for (int q = 0; q < npu; ++q) {
+      const float *pp = ppart + (int64_t)(moff[u] + q) * d2 + f0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += pp[e];
+      for (int e = 0; e < 8; ++e) acc[e] += __hip_atomic_load(pp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     u32x4 wv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) wv[e] = pack_bf2(acc[2 * e], acc[2 * e + 1]);
-    *reinterpret_cast<u32x4 *>(out + u * d2 + f0) = wv;
+    *reinterpret_cast<u32x4 *>(out + (int64_t)u * d2 + f0) = wv;
   }
+  if (lane == 0) cnt[u] = 0;  // ready for the next layer's sums
 }
 
 int bits_for(int64_t n) {
@@ -327,6 +340,8 @@ hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(pieces_kernel, dim3(gu), dim3(kT), 0, s, a.seg, a.n_unique, a.max_u, a.poff, a.moff);
   if ((e = excl_scan(a.poff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
   if ((e = excl_scan(a.moff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(p2u_kernel, dim3((unsigned)((a.max_u + kT - 1) / kT)), dim3(kT), 0, s, a.poff, a.n_unique,
+                     a.max_u, a.p2u, a.cnt);
   return hipGetLastError();
 }
 
@@ -334,9 +349,7 @@ hipError_t launch_unique_sums(const UniqueSumArgs &a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   const int64_t maxp = agg_max_pieces(a.n, a.max_u);
   hipLaunchKernelGGL(agg_kernel, dim3((unsigned)((maxp + 3) / 4)), dim3(kT), 0, s, a.dkv, a.sorted_items, a.seg,
-                     a.poff, a.moff, a.n_unique, a.d2, maxp, a.out, a.ppart);
-  hipLaunchKernelGGL(agg_fold_kernel, dim3((unsigned)((a.max_u + 3) / 4)), dim3(kT), 0, s, a.poff, a.moff,
-                     a.n_unique, a.d2, a.max_u, a.ppart, a.out);
+                     a.poff, a.moff, a.p2u, a.n_unique, a.d2, maxp, a.out, a.ppart, a.cnt);
   return hipGetLastError();
 }
 
