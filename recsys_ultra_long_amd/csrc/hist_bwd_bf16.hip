@@ -103,27 +103,56 @@ DEV Src src_dx(const Ops &L, int hc, int w, int lane, int nkh) {
 // zeros past nrows (row0 < nrows).  Every load is issued unconditionally
 // (rows past the end read row0 and are replaced by zeros afterwards), so that
 // all of them are in flight together.  All threads; the caller synchronises.
-template <int W, int LD>
-DEV void load_rows(const bf16_t *src, bf16_t *dst, int64_t row0, int64_t nrows, int tid) {
-  constexpr int C8 = W / 8;
-  constexpr int N = kR * C8 / kT;
+template <int W>
+struct Rows {
+  static constexpr int C8 = W / 8, N = kR * C8 / kT;
   static_assert(N * kT == kR * C8, "whole 16-byte pieces per thread");
   u32x4 v[N];
+  DEV void load(const bf16_t *src, int64_t row0, int64_t nrows, int tid) {
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
-    const int64_t row = row0 + r < nrows ? row0 + r : row0;
-    v[k] = *(gu32x4 *)(src + row * W + c);
+    for (int k = 0; k < N; ++k) {
+      const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
+      const int64_t row = row0 + r < nrows ? row0 + r : row0;
+      v[k] = *(gu32x4 *)(src + row * W + c);
+    }
   }
+  template <int LD>
+  DEV void store(bf16_t *dst, int64_t row0, int64_t nrows, int tid) const {
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
-    const uint32_t keep = row0 + r < nrows ? 0xffffffffu : 0u;
-    *reinterpret_cast<u32x4 *>(dst + r * LD + c) = v[k] & keep;
+    for (int k = 0; k < N; ++k) {
+      const int e = tid + k * kT, r = e / C8, c = (e % C8) * 8;
+      const uint32_t keep = row0 + r < nrows ? 0xffffffffu : 0u;
+      *reinterpret_cast<u32x4 *>(dst + r * LD + c) = v[k] & keep;
+    }
   }
+};
+template <int W, int LD>
+DEV void load_rows(const bf16_t *src, bf16_t *dst, int64_t row0, int64_t nrows, int tid) {
+  Rows<W> rw;
+  rw.load(src, row0, nrows, tid);
+  rw.template store<LD>(dst, row0, nrows, tid);
 }
 
 DEV float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Sum over the 32 lanes of each half-wave, in every lane: four DPP steps
+// within rows of 16 (pairs, quads, half-row and row mirrors) and one swap
+// between the rows -- VALU only, no LDS round trips.
+DEV float dpp_add(float v, int ctrl) {
+  switch (ctrl) {  // the control must be a constant of the builtin
+    case 0xB1: return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    case 0x4E: return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    case 0x141: return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    default: return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  }
+}
+DEV float sum32_lanes(float v) {
+  v = dpp_add(v, 0xB1);   // quad_perm [1,0,3,2]: pairs
+  v = dpp_add(v, 0x4E);   // quad_perm [2,3,0,1]: quads
+  v = dpp_add(v, 0x141);  // row_half_mirror: 8 lanes
+  v = dpp_add(v, 0x140);  // row_mirror: 16 lanes
+  return sum_x16(v);      // with the other row of the half-wave
+}
 
 template <bool LN>
 __global__ __launch_bounds__(kT, 1) void hist_bwd256_kernel(HistBwdArgs a) {
@@ -259,6 +288,10 @@ __global__ __launch_bounds__(kT, 1) void hist_bwd256_kernel(HistBwdArgs a) {
     }
     y_mma(nchunk - 1, src_b(L, w, lane), -1);
   }
+  // the tile's dK | dV rows: loads issued now (after the weight stream's last
+  // loads of phase A), stored to LDS once every wave is done with X and G
+  Rows<2 * kD> kvrows;
+  kvrows.load(a.dkv, row0, nrows, tid);
 
   roles();
   // LN statistics (the encoder's single exchange: per-lane partial mean and
@@ -290,8 +323,7 @@ __global__ __launch_bounds__(kT, 1) void hist_bwd256_kernel(HistBwdArgs a) {
     }
   }
   __syncthreads();  // (also: every wave is done with X and the G chunks)
-  // the dK | dV rows over P and Q, loaded while the statistics are folded
-  load_rows<2 * kD, kKVLD>(a.dkv, kvs, row0, nrows, tid);
+  kvrows.store<kKVLD>(kvs, row0, nrows, tid);  // over P and Q
   if (LN) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -386,13 +418,8 @@ __global__ __launch_bounds__(kT, 1) void hist_bwd256_kernel(HistBwdArgs a) {
         pg += dxt[j][i] * y[j][i];
         pb += dxt[j][i];
       }
-      pg = sum_x16(pg);
-      pb = sum_x16(pb);
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        pg += __shfl_xor(pg, o);
-        pb += __shfl_xor(pb, o);
-      }
+      pg = sum32_lanes(pg);
+      pb = sum32_lanes(pb);
       if (l32 == 0) {
         const int f = w * 32 + c32_row(lane, i);
         part[f] = pg;
