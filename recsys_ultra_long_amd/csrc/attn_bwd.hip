@@ -83,17 +83,29 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
   const int d = a.d;
   const int64_t col0 = (int64_t)eta * DH;
 
-  for (int e = tid; e < kMaxTgt * DH; e += 256) {
-    const int t = e / DH, n = e % DH;
-    bf16_t q = 0, gq = 0;
-    if (t < m) {
-      q = a.q[(t0 + t) * d + col0 + n];
-      gq = a.da_lo[(t0 + t) * d + col0 + n];
+  // the user's Q and dA rows of this head, in 16-byte pieces (all loads in
+  // flight together; rows past m read target 0 and are zeroed)
+  constexpr int PER = DH / 8;
+  static_assert((kMaxTgt * PER) % 256 == 0, "whole pieces per thread");
+#pragma unroll
+  for (int e0 = 0; e0 < kMaxTgt * PER; e0 += 256) {
+    const int e = e0 + tid, t = e / PER, n0 = (e % PER) * 8;
+    u32x4 q = {0u, 0u, 0u, 0u}, gq = q;
+    if (m > 0) {  // (uniform)
+      const int64_t row = (t0 + (t < m ? t : 0)) * d + col0 + n0;
+      q = *reinterpret_cast<const u32x4 *>(a.q + row);
+      gq = *reinterpret_cast<const u32x4 *>(a.da_lo + row);
+      const uint32_t keep = t < m ? 0xffffffffu : 0u;
+      q &= keep;
+      gq &= keep;
     }
-    sQ[t * (DH + 8) + n] = q;
-    sdA[t * (DH + 8) + n] = gq;
-    sQT[n * LT + t] = q;
-    sdAT[n * LT + t] = gq;
+    *reinterpret_cast<u32x4 *>(sQ + t * (DH + 8) + n0) = q;
+    *reinterpret_cast<u32x4 *>(sdA + t * (DH + 8) + n0) = gq;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sQT[(n0 + k) * LT + t] = (bf16_t)(q[k >> 1] >> (16 * (k & 1)));
+      sdAT[(n0 + k) * LT + t] = (bf16_t)(gq[k >> 1] >> (16 * (k & 1)));
+    }
   }
   if (tid < kMaxTgt) {
     slse[tid] = (SCORE == 0 && tid < m) ? a.lse[(t0 + tid) * a.H + eta] : 0.f;
@@ -188,7 +200,9 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
       }
     }
     wave_sync();
-    // dK = dS^T Q, dV = P^T dA over this user's targets (16 per k-step)
+    // dK^T = Q^T dS, dV^T = dA^T P over this user's targets (16 per k-step):
+    // features as accumulator rows, keys as columns, so that each lane ends
+    // up with 16 consecutive features of one key for 16-byte stores
     f32x16 dk[NN], dv[NN];
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn)
@@ -204,22 +218,24 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
       const bf16x8 pa = ld8(p_w + l32 * LT + 16 * kt + 8 * g);
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
-        dk[nn] = mfma32(dsa, ld8(sQT + (nn * 32 + l32) * LT + 16 * kt + 8 * g), dk[nn]);
-        dv[nn] = mfma32(pa, ld8(sdAT + (nn * 32 + l32) * LT + 16 * kt + 8 * g), dv[nn]);
+        dk[nn] = mfma32(ld8(sQT + (nn * 32 + l32) * LT + 16 * kt + 8 * g), dsa, dk[nn]);
+        dv[nn] = mfma32(ld8(sdAT + (nn * 32 + l32) * LT + 16 * kt + 8 * g), pa, dv[nn]);
       }
     }
     wave_sync();
 #pragma unroll
-    for (int nn = 0; nn < NN; ++nn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = kb + c32_row(lane, r);
-        if (kk < k_end) {
-          bf16_t *row = a.dkv + (h0 + kk) * 2 * d + col0 + nn * 32 + l32;
-          row[0] = f2bf(dk[nn][r]);
-          row[d] = f2bf(dv[nn][r]);
-        }
+    for (int nn = 0; nn < NN; ++nn) {
+      u32x4 k0, k1, v0, v1;
+      halves16(dk[nn], g, k0, k1);  // lane (key l32, g): features 16 g .. 16 g + 15 of the tile
+      halves16(dv[nn], g, v0, v1);
+      if (key < k_end) {
+        bf16_t *row = a.dkv + (h0 + key) * 2 * d + col0 + nn * 32 + 16 * g;
+        *reinterpret_cast<u32x4 *>(row) = k0;
+        *reinterpret_cast<u32x4 *>(row + 8) = k1;
+        *reinterpret_cast<u32x4 *>(row + d) = v0;
+        *reinterpret_cast<u32x4 *>(row + d + 8) = v1;
       }
+    }
   }
   // this wave's dQ partial: [64 targets][d_h]
   float *pd = a.part_dq + (((int64_t)c * a.H + eta) * 4 + w) * kMaxTgt * DH;
