@@ -113,17 +113,20 @@ __global__ __launch_bounds__(kT) void copy_rows_kernel(const float *__restrict__
   else store<float>(out, e, y[e]);
 }
 
-// rows per LN-backward block, and its partial sums of dg, db
-constexpr int kLnBwdRows = 64;
+// Rows per LN-backward block (each block leaves one partial row of dg, db):
+// a few thousand rows (the targets) in blocks of 8, so that the launch fills
+// the chip, more in blocks of 64.
 constexpr int kFoldSlices = 64;  // first fold stage: partial rows cut into this many slices
+int ln_bwd_rows(int64_t R) { return R <= 16384 ? 8 : 64; }
 
 __global__ __launch_bounds__(kT) void ln_bwd_kernel(const float *__restrict__ dout, const float *__restrict__ y,
-                                                    const float *__restrict__ stats, int64_t R, int d,
+                                                    const float *__restrict__ stats, int64_t R, int d, int rows,
                                                     const float *__restrict__ g, void *dy, bool dy_bf16,
                                                     float *part, const int *dev_rows) {
   if (dev_rows) R = min(R, (int64_t)*dev_rows);
-  // block: kLnBwdRows rows, one wave per row at a time; per-lane column
-  // partials of dg, db kept in LDS [4 waves][d] and folded in wave order
+  // block: `rows` rows, one wave per row at a time; per-lane column
+  // partials of dg, db kept in LDS [4 waves][d] and folded in wave order.
+  // A row's values (d <= 512: up to 8 per lane) are loaded before any is used.
   extern __shared__ float sm[];
   float *pg = sm, *pb = sm + 4 * d;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -131,27 +134,45 @@ __global__ __launch_bounds__(kT) void ln_bwd_kernel(const float *__restrict__ do
     pg[w * d + f] = 0.f;
     pb[w * d + f] = 0.f;
   }
-  const int64_t rb = (int64_t)blockIdx.x * kLnBwdRows;
-  for (int i = w; i < kLnBwdRows; i += 4) {
+  const int64_t rb = (int64_t)blockIdx.x * rows;
+  for (int i = w; i < rows; i += 4) {
     const int64_t r = rb + i;
     if (r >= R) break;
     const float mu = stats[2 * r], rstd = stats[2 * r + 1];
     const float *dr = dout + r * d, *yr = y + r * d;
+    float dv[8], yv[8], gv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = k * 64 + lane;
+      if (f < d) {
+        dv[k] = dr[f];
+        yv[k] = yr[f];
+        gv[k] = g[f];
+      }
+    }
     float s1 = 0.f, s2 = 0.f;
-    for (int f = lane; f < d; f += 64) {
-      const float xh = (yr[f] - mu) * rstd, gy = dr[f] * g[f];
-      s1 += gy;
-      s2 += gy * xh;
-      pg[w * d + f] += dr[f] * xh;
-      pb[w * d + f] += dr[f];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = k * 64 + lane;
+      if (f < d) {
+        const float xh = (yv[k] - mu) * rstd, gy = dv[k] * gv[k];
+        s1 += gy;
+        s2 += gy * xh;
+        pg[w * d + f] += dv[k] * xh;
+        pb[w * d + f] += dv[k];
+      }
     }
     s1 = wave_sum(s1) / d;
     s2 = wave_sum(s2) / d;
-    for (int f = lane; f < d; f += 64) {
-      const float xh = (yr[f] - mu) * rstd, gy = dr[f] * g[f];
-      const float v = rstd * (gy - s1 - xh * s2);
-      if (dy_bf16) store<bf16_t>(dy, r * d + f, v);
-      else store<float>(dy, r * d + f, v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int f = k * 64 + lane;
+      if (f < d) {
+        const float xh = (yv[k] - mu) * rstd, gy = dv[k] * gv[k];
+        const float v = rstd * (gy - s1 - xh * s2);
+        if (dy_bf16) store<bf16_t>(dy, r * d + f, v);
+        else store<float>(dy, r * d + f, v);
+      }
     }
   }
   __syncthreads();
@@ -264,7 +285,7 @@ hipError_t launch_ln_fwd(const float *y, int64_t R, int d, const float *g, const
   return hipGetLastError();
 }
 
-int64_t ln_part_rows(int64_t R) { return (R + kLnBwdRows - 1) / kLnBwdRows + kFoldSlices; }
+int64_t ln_part_rows(int64_t R) { return (R + ln_bwd_rows(R) - 1) / ln_bwd_rows(R) + kFoldSlices; }
 
 hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, int64_t R, int d, const float *g,
                          void *dy, bool dy_bf16, float *dg, float *db, float *part, hipStream_t s,
@@ -274,9 +295,11 @@ hipError_t launch_ln_bwd(const float *dout, const float *y, const float *stats, 
     hipLaunchKernelGGL(copy_rows_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, dout, R * d, dy, dy_bf16, dev_rows, d);
     return hipGetLastError();
   }
-  const int64_t nblk = (R + kLnBwdRows - 1) / kLnBwdRows;
-  hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)nblk), dim3(kT), 8 * d * sizeof(float), s, dout, y, stats, R, d, g,
-                     dy, dy_bf16, part, dev_rows);
+  if (d > 512) return hipErrorInvalidValue;  // up to 8 values per lane
+  const int rows = ln_bwd_rows(R);
+  const int64_t nblk = (R + rows - 1) / rows;
+  hipLaunchKernelGGL(ln_bwd_kernel, dim3((unsigned)nblk), dim3(kT), 8 * d * sizeof(float), s, dout, y, stats, R, d,
+                     rows, g, dy, dy_bf16, part, dev_rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   float *part2 = part + nblk * 2 * d;  // ln_part_rows() leaves room for the slices

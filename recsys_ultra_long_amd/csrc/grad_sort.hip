@@ -22,6 +22,7 @@ constexpr int kT = 256;
 constexpr int kIPT = 8;                // items per thread per sort block
 constexpr int kIPB = kT * kIPT;        // items per sort block
 constexpr int kPiece = 256;            // items per aggregation piece
+static_assert(kPiece % 64 == 0, "whole groups of 64 item ids per piece");
 
 __global__ __launch_bounds__(kT) void iota_kernel(int *v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x;
@@ -212,24 +213,37 @@ __global__ __launch_bounds__(kT) void agg_kernel(const bf16_t *__restrict__ dkv,
   const int k = (int)(p - poff[u]);
   const int npu = poff[u + 1] - poff[u];
   const int i0 = seg[u] + k * kPiece;
-  const int i1 = min(i0 + kPiece, seg[u + 1]);
-  for (int f0 = lane * 8; f0 < d2; f0 += 512) {
+  const int n = min(i0 + kPiece, seg[u + 1]) - i0;  // items of this piece, 1 .. kPiece
+  // The piece's item ids, kPiece / 64 per lane, loaded together (ids past
+  // the piece repeat its last one); row q of a group then comes from lane q
+  // by a lane shuffle, so that 16 row loads go out at once.
+  constexpr int PL = kPiece / 64;
+  int tok[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) tok[j] = stok[i0 + min(j * 64 + lane, n - 1)];
+  // every lane runs the loop (the shuffles read all lanes); lanes past the
+  // row's 2d values read column 0 and store nothing
+  for (int c0 = 0; c0 < d2; c0 += 512) {
+    const int f0 = c0 + lane * 8;
+    const bool on = f0 < d2;
+    const int fc = on ? f0 : 0;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int i = i0;
-    for (; i + 4 <= i1; i += 4) {  // four rows in flight
-      bf16x8 x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = ld8(dkv + (int64_t)stok[i + q] * d2 + f0);
+    for (int j = 0; j < PL; ++j) {
+      const int m = min(n - j * 64, 64);  // items of this group of 64
+      for (int b = 0; b < m; b += 16) {
+        bf16x8 x[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 16; ++q) x[q] = ld8(dkv + (int64_t)__shfl(tok[j], min(b + q, m - 1)) * d2 + fc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += bf2f((bf16_t)x[q][e]);
+        for (int q = 0; q < 16; ++q)
+          if (b + q < m) {  // in item order
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += bf2f((bf16_t)x[q][e]);
+          }
+      }
     }
-    for (; i < i1; ++i) {
-      const bf16x8 x = ld8(dkv + (int64_t)stok[i] * d2 + f0);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += bf2f((bf16_t)x[e]);
-    }
+    if (!on) continue;
     if (npu == 1) {
       u32x4 wv;
 #pragma unroll
