@@ -54,7 +54,7 @@ DEV void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int DH, int SCORE>
+template <int DH, int SCORE, bool DD>
 __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
   constexpr int KS = DH / 16;  // 16-deep k-steps over d_h
   constexpr int NN = DH / 32;  // 32-wide output tiles over d_h
@@ -123,26 +123,54 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
 
   bf16_t *kt_w = sKT[w], *p_w = sP[w], *ds_w = sdS[w];
   const bf16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int kb = k_begin + 32 * w; kb < k_end; kb += 128) {
+  // The K / V rows of a wave's next block are loaded while the current one
+  // is worked on (and before its dK | dV stores, which share the in-order
+  // memory counter); with dedup the row ids are fetched one block further
+  // ahead.  Loads are unconditional: keys past the chunk read its last key,
+  // and their rows are zeroed where they are used.
+  auto row_id = [&](int kb) -> int {  // DD (dedup): the key's unique row; else the key
+    const int key = min(kb + l32, k_end - 1);
+    return DD ? a.tok2u[h0 + key] : key;
+  };
+  auto load_kv = [&](int id, bf16x8(&kf)[KS], bf16x8(&vf)[KS]) {
+    const bf16_t *kr, *vr;
+    if (DD) {  // blocked K, row-major V of the unique rows
+      kr = a.k + ((((int64_t)(id >> 5)) * a.H + eta) * 32 + (id & 31)) * DH;
+      vr = a.v + (int64_t)id * d + col0;
+    } else {
+      kr = a.k + (h0 + id) * d + col0;
+      vr = a.v + (h0 + id) * d + col0;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = ld8(kr + 16 * s + 8 * g);
+      vf[s] = ld8(vr + 16 * s + 8 * g);
+    }
+  };
+  // (the block loop runs per wave: its counter is kept wave-uniform, so that
+  // the loop is not a divergent one; it is unrolled by two, the prefetched
+  // rows alternating between two register sets, so that none is copied and
+  // each is waited for only where it is used)
+  const int kb0 = k_begin + 32 * __builtin_amdgcn_readfirstlane(w);
+  bf16x8 kr0[KS], vr0[KS], kr1[KS], vr1[KS];  // the two register sets
+  int idn = 0;  // the row id of the block after the next
+  if (kb0 < k_end) {
+    load_kv(row_id(kb0), kr0, vr0);
+    idn = row_id(kb0 + 128);
+  }
+  auto block = [&](const int kb, const bf16x8(&kc)[KS], const bf16x8(&vc)[KS], bf16x8(&kn)[KS],
+                   bf16x8(&vn)[KS]) {
     const int key = kb + l32;
     const bool kval = key < k_end;
     bf16x8 kf[KS], vf[KS];
-    if (a.tok2u) {  // the item's unique row: blocked K, row-major V
-      const int ui = kval ? a.tok2u[h0 + key] : 0;
-      const bf16_t *kr = a.k + ((((int64_t)(ui >> 5)) * a.H + eta) * 32 + (ui & 31)) * DH;
-      const bf16_t *vr = a.v + (int64_t)ui * d + col0;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        kf[s] = kval ? ld8(kr + 16 * s + 8 * g) : zero8;
-        vf[s] = kval ? ld8(vr + 16 * s + 8 * g) : zero8;
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        kf[s] = kval ? ld8(a.k + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
-        vf[s] = kval ? ld8(a.v + (h0 + key) * d + col0 + 16 * s + 8 * g) : zero8;
-      }
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = kval ? kc[s] : zero8;
+      vf[s] = kval ? vc[s] : zero8;
     }
+    // the next block (past the chunk's end: its last key again, unused)
+    load_kv(idn, kn, vn);
+    idn = row_id(kb + 256);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -236,6 +264,11 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
         *reinterpret_cast<u32x4 *>(row + d + 8) = v1;
       }
     }
+  };
+  for (int kb = kb0; kb < k_end; kb += 256) {
+    block(kb, kr0, vr0, kr1, vr1);
+    if (kb + 128 >= k_end) break;
+    block(kb + 128, kr1, vr1, kr0, vr0);
   }
   // this wave's dQ partial: [64 targets][d_h]
   float *pd = a.part_dq + (((int64_t)c * a.H + eta) * 4 + w) * kMaxTgt * DH;
@@ -278,15 +311,21 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
   }
   if (a.max_chunks > 0 && a.n_hist > 0) {
     const dim3 grid((unsigned)a.max_chunks, (unsigned)a.H);
+#define AB(DH, SC)                                                                        \
+  do {                                                                                    \
+    if (a.tok2u) hipLaunchKernelGGL((attn_bwd_kernel<DH, SC, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((attn_bwd_kernel<DH, SC, false>), grid, dim3(256), 0, s, a);       \
+  } while (0)
     if (a.dh == 32) {
-      if (a.score) hipLaunchKernelGGL((attn_bwd_kernel<32, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_bwd_kernel<32, 0>), grid, dim3(256), 0, s, a);
+      if (a.score) AB(32, 1);
+      else AB(32, 0);
     } else if (a.dh == 64) {
-      if (a.score) hipLaunchKernelGGL((attn_bwd_kernel<64, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((attn_bwd_kernel<64, 0>), grid, dim3(256), 0, s, a);
+      if (a.score) AB(64, 1);
+      else AB(64, 0);
     } else {
       return hipErrorInvalidValue;
     }
+#undef AB
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
