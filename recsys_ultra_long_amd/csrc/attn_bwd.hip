@@ -30,6 +30,9 @@ namespace {
 constexpr int kMaxTgt = 64;
 constexpr int LT = kMaxTgt + 8;  // row stride of [.][target] LDS tiles
 constexpr int LK = 32 + 8;       // row stride of [.][key] LDS tiles
+// p = e^(s - lse) on the hardware base-2 exponential (a few ulp in fp32;
+// p and dS feed bf16 products)
+constexpr float kLog2e = 1.4426950408889634f;
 
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdArgs a) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (target, head)
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
         const bool ok = tval && kb + kr < k_end;
         float p, dsv;
         if (SCORE == 0) {
-          p = ok ? expf(st[r] - lse) : 0.f;
+          p = ok ? __builtin_amdgcn_exp2f((st[r] - lse) * kLog2e) : 0.f;
           dsv = p * (dpt[r] - D);
         } else {
           const bool pos = ok && st[r] > 0.f;
