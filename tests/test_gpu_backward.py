@@ -27,7 +27,8 @@ Checks:
   contributions, which the oracle computes;
 * unique-id dedup (STCA_FLAG_DEDUP): the history backward once per distinct
   id on the summed dK | dV of its items -- against the oracle on every
-  workload above, bitwise repeatable, with out-of-range ids, and at full
+  workload above, bitwise repeatable, with out-of-range ids, with rows whose
+  items fill one, just over one and several 256-item pieces, and at full
   size.
 """
 import numpy as np
@@ -332,6 +333,26 @@ def test_backward_dedup_matches_oracle(k):
     p = I.make_problem(_small(k))
     dz = I.upstream_grad(p.spec, p.n_tgt)
     print(f"[bwd-dedup] workload {k}: n_hist={p.n_hist} unique={len(np.unique(p.hist_ids))}", flush=True)
+    g = gpu_backward(p, dz, dedup=True)
+    ref = OG.backward_problem(p, dz)
+    assert g["status"] == 0
+    compare_all(p, g, ref)
+
+
+def test_backward_dedup_rows_spanning_pieces():
+    """Unique rows whose items fill exactly one 256-item piece, one item more
+    than a piece, and several pieces (their partial sums folded in piece
+    order), scattered over the users: against the oracle."""
+    p = I.make_problem(_small(3, L=700))
+    rng = np.random.default_rng(17)
+    pos = rng.permutation(p.n_hist)
+    p.hist_ids[np.isin(p.hist_ids, [11, 12, 13])] = 14  # the three rows get only the items below
+    for ident, (a, b) in ((11, (0, 256)), (12, (256, 513)), (13, (513, 1113))):
+        p.hist_ids[pos[a:b]] = ident
+    dz = I.upstream_grad(p.spec, p.n_tgt)
+    counts = np.bincount(p.hist_ids[p.hist_ids >= 0], minlength=14)[11:14]
+    print(f"[bwd-dedup] rows spanning pieces: items per hot row {counts.tolist()}", flush=True)
+    assert counts.tolist() == [256, 257, 600]
     g = gpu_backward(p, dz, dedup=True)
     ref = OG.backward_problem(p, dz)
     assert g["status"] == 0
