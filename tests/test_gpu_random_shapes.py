@@ -1,0 +1,77 @@
+"""GPU parity over a seeded random sweep of small problem shapes.
+
+Each case draws, from its own seed: the model width and head width (d 128,
+256 or 512; d_h 32 or 64), the hidden width (d or 2d), the number of layers
+(1-3), the number of users (1-5) with fixed or Beta-ragged lengths, some
+users' histories emptied, the targets per user (1-64), LN after the history
+FFN on or off, a random LN affine, LN on z, a small Zipf table (so that ids
+repeat), the path (staged, or fused where it applies) and unique-id dedup on
+the staged path.  z, every layer's o and attention output are compared with
+the float64 oracle row by row at the bf16 bar (2e-2), the same bar as the
+reduced workload tests; softmax scores only (ReLU chains are held to their
+conditioning bar elsewhere).  The sweep looks for the shape corner the fixed
+cases miss: a tail tile, an empty user at a tile boundary, a width or layer
+count combination no named workload uses.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from parity_util import TOL, compare_forward, gpu_run, oracle_run
+from recsys_ultra_long_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytestmark = [pytest.mark.gpu, pytest.mark.skip(reason="no GPU visible")]
+
+N_CASES = 24
+
+
+def _drop_histories(p, users):
+    """The problem with the histories of ``users`` emptied (ids removed)."""
+    ho = p.hist_offsets.astype(np.int64)
+    keep = np.ones(int(ho[-1]), dtype=bool)
+    lens = np.diff(ho)
+    for u in users:
+        keep[ho[u]:ho[u + 1]] = False
+        lens[u] = 0
+    p.hist_ids = p.hist_ids[keep]
+    p.hist_offsets = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return p
+
+
+def _case(i):
+    r = np.random.default_rng(1000 + i)
+    d, H = [(128, 4), (256, 8), (256, 4), (512, 8), (512, 16)][r.integers(5)]
+    B = int(r.integers(1, 6))
+    ragged = bool(r.integers(2))
+    sp = I.spec(3, name=f"random-{i}", B=B, d=d, H=H, hidden=int(d * r.choice([1, 2])), M=int(r.integers(1, 4)),
+                table_rows=int(r.choice([3000, 20000])), m=int(r.choice([1, 3, 16, 40, 64])),
+                L=None if ragged else int(r.integers(1, 700)), L_max=int(r.integers(40, 700)) if ragged else None,
+                kv_ln=bool(r.integers(4) > 0), z_ln=bool(r.integers(2)), ln_random=bool(r.integers(2)),
+                seed=5000 + i)
+    fused_ok = sp.kv_ln and sp.m <= 64 and ((d == 256 and d // H in (32, 64)) or (d == 128 and d // H == 32))
+    path = "fused" if fused_ok and r.integers(3) == 0 else "staged"
+    dedup = path == "staged" and bool(r.integers(2))
+    drop = [u for u in range(B) if B > 1 and r.integers(4) == 0]
+    return sp, path, dedup, drop
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape_matches_oracle(i):
+    sp, path, dedup, drop = _case(i)
+    p = I.make_problem(sp)
+    if drop:
+        p = _drop_histories(p, drop)
+    print(f"[random {i}] d={sp.d} H={sp.H} hidden={sp.hidden} M={sp.M} B={sp.B} m={sp.m} "
+          f"n_hist={p.n_hist} kv_ln={sp.kv_ln} z_ln={sp.z_ln} ln_random={sp.ln_random} "
+          f"path={path} dedup={dedup} empty={drop}", flush=True)
+    g = gpu_run(p, path=path, dedup=dedup)
+    o = oracle_run(p)
+    errs = compare_forward(g, o, sp.dtype)
+    print(f"[random {i}] errors {errs}", flush=True)
+    assert int(g["status"][0]) == 0
+    assert all(e <= TOL[sp.dtype] for e in errs.values()), errs
