@@ -9,12 +9,13 @@ repeat), the path (staged, or fused where it applies) and unique-id dedup on
 the staged path.  z, every layer's o and attention output are compared with
 the float64 oracle row by row at the bf16 bar (2e-2), the same bar as the
 reduced workload tests; softmax scores only (ReLU chains are held to their
-conditioning bar elsewhere).  The sweep looks for the shape corner the fixed
-cases miss: a tail tile, an empty user at a tile boundary, a width or layer
-count combination no named workload uses.
+conditioning bar elsewhere).  A second sweep does the same on the fp32 path at
+its bar (1e-5) over the widths it takes (any d = 32 H or 64 H up to 512, hidden
+a multiple of 32) and both query modes (the W_C fusion chain, and the linear
+next-query map).  The sweeps look for the shape corner the fixed cases miss: a
+tail tile, an empty user at a tile boundary, a width or layer count
+combination no named workload uses.
 """
-from dataclasses import replace
-
 import numpy as np
 import pytest
 
@@ -73,5 +74,37 @@ def test_random_shape_matches_oracle(i):
     o = oracle_run(p)
     errs = compare_forward(g, o, sp.dtype)
     print(f"[random {i}] errors {errs}", flush=True)
+    assert int(g["status"][0]) == 0
+    assert all(e <= TOL[sp.dtype] for e in errs.values()), errs
+
+
+def _case_f32(i):
+    r = np.random.default_rng(3000 + i)
+    dh = int(r.choice([32, 64]))
+    H = int(r.integers(1, 512 // dh + 1))
+    d = dh * H
+    ragged = bool(r.integers(2))
+    linear = bool(r.integers(3) == 0)
+    sp = I.spec(1, name=f"random-f32-{i}", B=int(r.integers(1, 6)), d=d, H=H, hidden=int(32 * r.integers(1, 17)),
+                M=int(r.integers(1, 4)), table_rows=int(r.choice([3000, 20000])), m=int(r.choice([1, 3, 16, 40, 64])),
+                L=None if ragged else int(r.integers(1, 500)), L_max=int(r.integers(40, 500)) if ragged else None,
+                qmode="linear" if linear else "fusion", kv_ln=bool(r.integers(4) > 0) and not linear,
+                z_ln=bool(r.integers(2)), ln_random=bool(r.integers(2)), ids="zipf", seed=6000 + i)
+    drop = [u for u in range(sp.B) if sp.B > 1 and r.integers(4) == 0]
+    return sp, drop
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shape_f32_matches_oracle(i):
+    sp, drop = _case_f32(i)
+    p = I.make_problem(sp)
+    if drop:
+        p = _drop_histories(p, drop)
+    print(f"[random-f32 {i}] d={sp.d} H={sp.H} hidden={sp.hidden} M={sp.M} B={sp.B} m={sp.m} "
+          f"n_hist={p.n_hist} qmode={sp.qmode} kv_ln={sp.kv_ln} z_ln={sp.z_ln} empty={drop}", flush=True)
+    g = gpu_run(p)
+    o = oracle_run(p)
+    errs = compare_forward(g, o, sp.dtype)
+    print(f"[random-f32 {i}] errors {errs}", flush=True)
     assert int(g["status"][0]) == 0
     assert all(e <= TOL[sp.dtype] for e in errs.values()), errs
