@@ -14,12 +14,16 @@ its bar (1e-5) over the widths it takes (any d = 32 H or 64 H up to 512, hidden
 a multiple of 32) and both query modes (the W_C fusion chain, and the linear
 next-query map).  The sweeps look for the shape corner the fixed cases miss: a
 tail tile, an empty user at a tile boundary, a width or layer count
-combination no named workload uses.
+combination no named workload uses.  A third sweep mixes the modes (bf16,
+staged): softmax or ReLU scores (ReLU held to its conditioning bar), the
+fusion, linear or HyFormer query modes, the LONGER-style encoding, Cross-Mask
+key masks and head maps, the context-similarity score bias and dedup, in the
+combinations the library accepts.
 """
 import numpy as np
 import pytest
 
-from parity_util import TOL, compare_forward, gpu_run, oracle_run
+from parity_util import TOL, compare_forward, end_to_end_bar, gpu_run, oracle_run
 from recsys_ultra_long_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +112,57 @@ def test_random_shape_f32_matches_oracle(i):
     print(f"[random-f32 {i}] errors {errs}", flush=True)
     assert int(g["status"][0]) == 0
     assert all(e <= TOL[sp.dtype] for e in errs.values()), errs
+
+
+def _case_modes(i):
+    r = np.random.default_rng(4000 + i)
+    d, H = [(128, 4), (256, 8), (256, 4), (512, 8), (512, 16)][r.integers(5)]
+    longer = r.integers(4) == 0
+    qmode = ["fusion", "linear", "hyformer"][r.integers(3)]
+    score = "softmax" if longer or r.integers(2) else "relu"
+    ragged = bool(r.integers(2))
+    over = dict(name=f"random-modes-{i}", B=int(r.integers(1, 6)), d=d, H=H, hidden=int(d * r.choice([1, 2])),
+                M=int(r.integers(1, 4)), table_rows=int(r.choice([3000, 20000])), m=int(r.choice([1, 3, 16, 40])),
+                L=None if ragged else int(r.integers(1, 600)), L_max=int(r.integers(40, 600)) if ragged else None,
+                score=score, qmode=qmode, kv_ln=bool(r.integers(4) > 0), z_ln=bool(r.integers(2)),
+                ln_random=bool(r.integers(2)), seed=8000 + i)
+    if qmode == "hyformer":  # the token mixing splits d into m + n_ns equal parts
+        ok = [n for n in range(0, 25) if d % (over["m"] + n) == 0]
+        if ok:
+            over["n_ns"] = int(r.choice(ok))
+        else:
+            over["qmode"] = "fusion"
+    if longer:
+        over.update(encoder="longer", l_short=int(r.integers(1, 600)))
+    sp = I.spec(3, **over)
+    mask = not longer and r.integers(3) == 0
+    hmap = [int(x) for x in r.integers(0, H, size=H)] if mask and H <= 16 and r.integers(2) else None
+    bias = not longer and r.integers(3) == 0
+    dedup = not longer and bool(r.integers(2))
+    drop = [u for u in range(sp.B) if sp.B > 1 and r.integers(5) == 0]
+    return sp, mask, hmap, bias, dedup, drop
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_modes_match_oracle(i):
+    sp, mask, hmap, bias, dedup, drop = _case_modes(i)
+    p = I.make_problem(sp)
+    if drop:
+        p = _drop_histories(p, drop)
+    if mask:
+        p.extra["key_mask"] = I.cross_mask(sp, p.n_hist, sorted({1 % sp.H, (sp.H - 1)}), 0.5, seed=i)
+    if hmap is not None:
+        p.extra["head_map"] = hmap
+    if bias:
+        p.extra["score_bias"] = I.score_bias(sp, p.n_hist)
+    print(f"[random-modes {i}] d={sp.d} H={sp.H} hidden={sp.hidden} M={sp.M} B={sp.B} m={sp.m} "
+          f"n_hist={p.n_hist} score={sp.score} qmode={sp.qmode} n_ns={sp.n_ns} encoder={sp.encoder} "
+          f"l_short={sp.l_short} kv_ln={sp.kv_ln} mask={bool(mask)} map={hmap} bias={bool(bias)} "
+          f"dedup={dedup} empty={drop}", flush=True)
+    g = gpu_run(p, dedup=dedup)
+    o = oracle_run(p)
+    errs = compare_forward(g, o, sp.dtype)
+    bar = end_to_end_bar(p, exact=o)
+    print(f"[random-modes {i}] errors {errs} bar {bar}", flush=True)
+    assert int(g["status"][0]) == 0
+    assert all(errs[k] <= bar[k] for k in errs), (errs, bar)
