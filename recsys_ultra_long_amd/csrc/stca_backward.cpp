@@ -126,7 +126,7 @@ int64_t part_floats_hist(int64_t d, int64_t h, int64_t R) {
 // the events are not recorded by two calls at once.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork[16] = {}, join = nullptr;
+  hipEvent_t fork[16] = {}, prep = nullptr, join = nullptr;
 };
 constexpr int kSideDevices = 64;
 std::mutex g_side_mu;
@@ -143,6 +143,7 @@ hipError_t side_stream(SideStream **out) {
     if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
     for (hipEvent_t &x : ss.fork)
       if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.prep, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
     ss.s = st;
   }
@@ -484,30 +485,25 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     return gemm(n, d, h, dh13 + h, false, 2 * h, 1, f.w3, true, 1, h, dx, d, 1, 1.f, 1.f, kTgt);
   };
 
-  // ---- 3. z head: cz = [o_1..o_M | x_t] W_Z, z = SwiGLU_Z(cz) (+LN)
-  {
-    if ((e = gemm(T, d, MD, ocat, false, MD, 1, w->wz, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("z");
-    if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
-      return hip_err("z");
-    if ((e = ffn_fwd(T, c, w->z, zln, qln))) return hip_err("z ffn");
-    if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc))) return hip_err("z backward");
-    // dW_Z += [o | x_t]^T dcz; d[o | x_t] = dcz W_Z^T
-    if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWz");
-    if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
-      return hip_err("dWz");
-    if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
-    if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, kTgt)))
-      return hip_err("dx_t");
+  // ---- history rows, gathered once (every layer reads the same raw X), the
+  // items sorted by unique row, the weights packed for the history row pass:
+  // none of it depends on the z head, so it runs on the history side's stream
+  // (forked once the forward's outputs are there) while the z head runs here.
+  // The per-layer forks below keep the history work behind it on that stream.
+  hipStream_t hp = s;
+  if (R > 0) {
+    hp = side->s;
+    if ((e = hipEventRecord(side->prep, s)) || (e = hipStreamWaitEvent(hp, side->prep, 0)))
+      return hip_err("history stream fork");
+    forked = true;
   }
-
-  // ---- history rows, gathered once (every layer reads the same raw X)
   bf16_t *X = at<bf16_t>(ws, L.X);
   float *H13 = at<float>(ws, L.H13), *Y = at<float>(ws, L.Y), *ST = at<float>(ws, L.ST), *dXT = at<float>(ws, L.dXT);
   float *dG = at<float>(ws, L.dG);
   bf16_t *G = at<bf16_t>(ws, L.G), *XT = at<bf16_t>(ws, L.XT), *dY = at<bf16_t>(ws, L.dY);
   bf16_t *dH13 = at<bf16_t>(ws, L.dH13);
   const int *hids = L.dedup ? fi.uniq_rows : batch->hist_ids;
-  if (R > 0 && (e = launch_gather_rows(table, cfg->table_rows, hids, Rh, d, X, true, s, hdev)))
+  if (R > 0 && (e = launch_gather_rows(table, cfg->table_rows, hids, Rh, d, X, true, hp, hdev)))
     return hip_err("history gather");
   UniqueSumArgs ua;
   std::memset(&ua, 0, sizeof(ua));
@@ -529,7 +525,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     ua.p2u = at<int>(ws, L.p2u);
     ua.cnt = at<int>(ws, L.cnt);
     ua.out = at<bf16_t>(ws, L.dKVu);
-    if ((e = launch_unique_sort(ua, s))) return hip_err("unique sort");
+    if ((e = launch_unique_sort(ua, hp))) return hip_err("unique sort");
   }
   // operands of the fused history backward, packed for its MFMA fragments
   bf16_t *const bwpack = L.fused_hist ? at<bf16_t>(ws, L.bwpack) : nullptr;
@@ -553,15 +549,31 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       for (const PackDesc &pd : ds) {
         pb.m[n++] = pd;
         if (n == kMaxPacks) {
-          e = launch_pack_batch(pb, n, s);
+          e = launch_pack_batch(pb, n, hp);
           n = 0;
           if (e) break;
         }
       }
     }
-    if (!e && n) e = launch_pack_batch(pb, n, s);
+    if (!e && n) e = launch_pack_batch(pb, n, hp);
     if (e) return hip_err("pack");
   }
+  // ---- 3. z head: cz = [o_1..o_M | x_t] W_Z, z = SwiGLU_Z(cz) (+LN)
+  {
+    if ((e = gemm(T, d, MD, ocat, false, MD, 1, w->wz, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("z");
+    if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
+      return hip_err("z");
+    if ((e = ffn_fwd(T, c, w->z, zln, qln))) return hip_err("z ffn");
+    if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc))) return hip_err("z backward");
+    // dW_Z += [o | x_t]^T dcz; d[o | x_t] = dcz W_Z^T
+    if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWz");
+    if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
+      return hip_err("dWz");
+    if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
+    if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, kTgt)))
+      return hip_err("dx_t");
+  }
+
   if ((e = rec(2))) return hip_err("stage event");
 
   // ---- 4. layers, last to first
