@@ -58,10 +58,10 @@ struct BwdLayout {
   size_t z = 0, o = 0, attn = 0, q = 0, kv = 0, lse = 0;
   size_t plan = 0;
   size_t xt = 0, ocat = 0, docat = 0, dxt = 0;
-  size_t c = 0, h13 = 0, g = 0, y = 0, st = 0, qln = 0, dy = 0, dg = 0, dh13 = 0, dc = 0, da = 0, dq = 0;
+  size_t c = 0, h13 = 0, g = 0, y = 0, st = 0, qln = 0, dy = 0, dg = 0, dh13 = 0, dc = 0, da = 0, dq = 0, dqt = 0;
   size_t da_lo = 0, dsum = 0, part_dq = 0;
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
-  size_t ln_part = 0, gemm_part = 0, ln_part_h = 0, gemm_part_h = 0;
+  size_t ln_part = 0, gemm_part = 0, ln_part_h = 0, gemm_part_h = 0, gemm_part_w = 0;
   // d = 256 with hidden % 128 == 0: one fused launch per layer for the
   // history side (its H1 / H3 scratch and per-layer packed operands)
   bool fused_hist = false;
@@ -120,13 +120,15 @@ int64_t part_floats_hist(int64_t d, int64_t h, int64_t R) {
   return best;
 }
 
-// The history side's stream (one per device, default priority, created on
-// first use) and the events that fork it from the caller's stream per layer
-// and join it back.  Calls on one device are enqueued under a lock, so that
-// the events are not recorded by two calls at once.
+// The history side's stream and the query side's weight-gradient stream (one
+// each per device, default priority, created on first use), and the events
+// that fork them from the caller's stream and join them back.  Calls on one
+// device are enqueued under a lock, so that the events are not recorded by two
+// calls at once.
 struct SideStream {
-  hipStream_t s = nullptr;
+  hipStream_t s = nullptr, w = nullptr;
   hipEvent_t fork[16] = {}, prep = nullptr, join = nullptr;
+  hipEvent_t wfork[2 * 16 + 1] = {}, wdone[16 + 1] = {};
 };
 constexpr int kSideDevices = 64;
 std::mutex g_side_mu;
@@ -139,9 +141,15 @@ hipError_t side_stream(SideStream **out) {
   if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
   SideStream &ss = g_side[dev];
   if (!ss.s) {
-    hipStream_t st = nullptr;
+    hipStream_t st = nullptr, wt = nullptr;
     if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&wt, hipStreamNonBlocking)) != hipSuccess) return e;
+    ss.w = wt;
     for (hipEvent_t &x : ss.fork)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    for (hipEvent_t &x : ss.wfork)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
+    for (hipEvent_t &x : ss.wdone)
       if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.prep, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
@@ -186,7 +194,8 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.dh13 = cv.take(T * 2 * h * 4);
   L.dc = cv.take(T * d * 4);
   L.da = cv.take(T * d * 4);
-  L.dq = cv.take(T * d * 4);
+  L.dq = cv.take(2 * T * d * 4);  // by layer parity: the next layer's attention backward writes the other
+  L.dqt = cv.take(T * d * 4);
   L.da_lo = cv.take(T * d * 2);
   L.dsum = cv.take(T * H * 4);
   L.max_chunks = max_chunks(R, cfg->B, kBwdChunkBlocks);
@@ -227,6 +236,7 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.gemm_part = cv.take((size_t)part_floats_needed(d, h, M, 0, T) * 4);
   L.ln_part_h = cv.take((size_t)2 * ln_part_rows(Rh) * d * 4);  // the history side's own partials
   L.gemm_part_h = cv.take((size_t)part_floats_hist(d, h, Rh) * 4);
+  L.gemm_part_w = cv.take((size_t)part_floats_needed(d, h, M, 0, T) * 4);  // the weight-gradient stream's
   L.total = cv.off;
   return STCA_OK;
 }
@@ -394,6 +404,9 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   }
 
   // ---- GEMM helper: C = alpha * A B + beta * C with explicit strides
+  std::vector<GemmArgs> wq;
+  bool defer_w = false, wforked = false;
+  float *const gpart_w = at<float>(ws, L.gemm_part_w);
   const int *gdev = nullptr;  // device cap applied by gemm(): rows (M) or, for split products, K
   hipStream_t gs = s;         // stream and split-K partials of gemm(): the caller's, or the history side's
   float *gp = gpart;
@@ -431,7 +444,32 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     g.dev_dim = gdev ? (kind == kWgrad ? 2 : 1) : 0;
     g.C2 = C2;
     g.n_split = n_split;
+    if (defer_w && kind == kWgrad) {  // queued for the weight-gradient stream
+      wq.push_back(g);
+      return hipSuccess;
+    }
     return launch_gemm(g, gs);
+  };
+  // The query side's weight gradients (and W_O's, and the z head's) are off
+  // the critical path: nothing reads them before the call returns.  They are
+  // queued while `defer_w` is set and launched by flush_w on the weight-
+  // gradient stream, after event `fork` on the caller's stream, with split-K
+  // partials of their own; `done`, recorded after them, is what the caller's
+  // stream waits for before it overwrites their operands.
+  auto flush_w = [&](hipEvent_t fork, hipEvent_t done) -> hipError_t {
+    hipError_t er = hipSuccess;
+    if (!wq.empty()) {
+      if ((er = hipEventRecord(fork, s)) || (er = hipStreamWaitEvent(side->w, fork, 0))) return er;
+      for (GemmArgs &g : wq) {
+        g.part = gpart_w;
+        g.part_cap = gpart_cap;
+        if ((er = launch_gemm(g, side->w))) return er;
+      }
+      wq.clear();
+      wforked = true;
+    }
+    if (done) er = hipEventRecord(done, side->w);
+    return er;
   };
   // ---- 2. planner for the attention backward (its own chunking)
   Plan plan;
@@ -448,7 +486,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   float *xt = at<float>(ws, L.xt), *ocat = at<float>(ws, L.ocat), *docat = at<float>(ws, L.docat);
   float *c = at<float>(ws, L.c), *h13 = at<float>(ws, L.h13), *g = at<float>(ws, L.g), *y = at<float>(ws, L.y);
   float *st = at<float>(ws, L.st), *qln = at<float>(ws, L.qln), *dy = at<float>(ws, L.dy), *dg = at<float>(ws, L.dg);
-  float *dh13 = at<float>(ws, L.dh13), *dc = at<float>(ws, L.dc), *da = at<float>(ws, L.da), *dq = at<float>(ws, L.dq);
+  float *dh13 = at<float>(ws, L.dh13), *dc = at<float>(ws, L.dc), *da = at<float>(ws, L.da), *dqt = at<float>(ws, L.dqt);
+  float *const dq2 = at<float>(ws, L.dq);  // dQ of layer i at dq2 + (i & 1) T d
   const int64_t MD = (int64_t)M * d;
   if ((e = launch_gather_rows(table, cfg->table_rows, batch->tgt_ids, T, d, xt, false, s))) return hip_err("x_t");
   if ((e = launch_concat_layers(o_all, M, T, d, ocat, s))) return hip_err("concat");
@@ -564,15 +603,19 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
       return hip_err("z");
     if ((e = ffn_fwd(T, c, w->z, zln, qln))) return hip_err("z ffn");
+    defer_w = true;
     if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc))) return hip_err("z backward");
     // dW_Z += [o | x_t]^T dcz; d[o | x_t] = dcz W_Z^T
     if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWz");
     if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
       return hip_err("dWz");
+    defer_w = false;
     if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
     if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, kTgt)))
       return hip_err("dx_t");
+    if ((e = flush_w(side->wfork[2 * M], side->wdone[M]))) return hip_err("weight-gradient stream");
   }
+  hipEvent_t wpending = side->wdone[M];  // the queued products whose operands the next query side overwrites
 
   if ((e = rec(2))) return hip_err("stage event");
 
@@ -584,7 +627,11 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     float *do_i = docat + (size_t)i * d;
     // W_O: da = do W_O^T, dW_O += a^T do
     if ((e = gemm(T, d, d, do_i, false, MD, 1, lw.wo, true, 1, d, da, d, 1, 1.f, 0.f, kTgt))) return hip_err("da");
+    defer_w = true;  // (a and do_i stay as they are: nothing waits for this one)
     if ((e = gemm(d, d, T, a_i, false, 1, d, do_i, false, MD, 1, lg.wo, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWo");
+    defer_w = false;
+    if ((e = flush_w(side->wfork[2 * i], nullptr))) return hip_err("weight-gradient stream");
+    float *const dq = dq2 + (size_t)(i & 1) * T * d;  // this layer's dQ
     if (gr->da_dump && (e = launch_add_rows(da, d, gr->da_dump + (size_t)i * T * d, d, T, d, false, s)))
       return hip_err("da dump");
     // attention backward
@@ -719,7 +766,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       for (int k = 2; k <= 4; ++k)
         if ((e = rec(ev + k))) return hip_err("stage event");
     }
-    // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C
+    // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C;
+    // first, the previous query side's (or the z head's) queued weight
+    // gradients must be done with the buffers it reuses
+    if ((e = hipStreamWaitEvent(s, wpending, 0))) return hip_err("weight-gradient stream");
     const float *cin = xt;
     if (i > 0) {
       const int64_t K1 = (int64_t)i * d;
@@ -730,9 +780,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     }
     if ((e = ffn_fwd(T, cin, lw.q, true, qln))) return hip_err("query ffn");
     // Q = q W_Q / sqrt(d_h): dW_Q += q^T dQ / sqrt(d_h), dq = dQ W_Q^T / sqrt(d_h)
+    defer_w = true;
     if ((e = gemm(d, d, T, qln, false, 1, d, dq, false, d, 1, lg.wq, d, 1, qscale, 1.f, kWgrad))) return hip_err("dWq");
-    if ((e = gemm(T, d, d, dq, false, d, 1, lw.wq, true, 1, d, qln, d, 1, qscale, 0.f, kTgt))) return hip_err("dq");
-    if ((e = ffn_bwd(T, cin, lw.q, lg.q, true, qln, dc))) return hip_err("query backward");
+    if ((e = gemm(T, d, d, dq, false, d, 1, lw.wq, true, 1, d, dqt, d, 1, qscale, 0.f, kTgt))) return hip_err("dq");
+    if ((e = ffn_bwd(T, cin, lw.q, lg.q, true, dqt, dc))) return hip_err("query backward");
     if (i > 0) {
       const int64_t K1 = (int64_t)i * d;
       if ((e = gemm(K1, d, T, ocat, false, 1, MD, dc, false, d, 1, lg.wc, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWc");
@@ -744,13 +795,19 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     } else {
       if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
     }
+    defer_w = false;
+    if ((e = flush_w(side->wfork[2 * i + 1], side->wdone[i]))) return hip_err("weight-gradient stream");
+    wpending = side->wdone[i];
     if ((e = rec(ev + 1))) return hip_err("stage event");
     if ((e = rec(ev + 4))) return hip_err("stage event");
   }
 
-  // ---- 5. row gradients into the table, once the history side is done
+  // ---- 5. row gradients into the table, once the history side is done; the
+  // weight-gradient stream joined too
   if (forked && ((e = hipEventRecord(side->join, side->s)) || (e = hipStreamWaitEvent(s, side->join, 0))))
     return hip_err("history stream join");
+  if (wforked && ((e = hipEventRecord(side->wdone[M], side->w)) || (e = hipStreamWaitEvent(s, side->wdone[M], 0))))
+    return hip_err("weight-gradient stream join");
   if (gr->table) {
     if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev)))
       return hip_err("scatter");
