@@ -61,7 +61,8 @@ struct BwdLayout {
   size_t c = 0, h13 = 0, g = 0, y = 0, st = 0, qln = 0, dy = 0, dg = 0, dh13 = 0, dc = 0, da = 0, dq = 0, dqt = 0;
   size_t da_lo = 0, dsum = 0, part_dq = 0;
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
-  size_t ln_part = 0, gemm_part = 0, ln_part_h = 0, gemm_part_h = 0, gemm_part_w = 0;
+  size_t ln_part = 0, gemm_part = 0, ln_part_h = 0, gemm_part_h = 0, gemm_part_w = 0, gemm_part_r = 0;
+  size_t qf = 0, qf_layer = 0;  // every layer's recomputed query forward (floats per layer)
   // d = 256 with hidden % 128 == 0: one fused launch per layer for the
   // history side (its H1 / H3 scratch and per-layer packed operands)
   bool fused_hist = false;
@@ -120,15 +121,17 @@ int64_t part_floats_hist(int64_t d, int64_t h, int64_t R) {
   return best;
 }
 
-// The history side's stream and the query side's weight-gradient stream (one
-// each per device, default priority, created on first use), and the events
-// that fork them from the caller's stream and join them back.  Calls on one
+// The history side's stream, the query side's weight-gradient stream and the
+// stream that recomputes every layer's query forward ahead of its backward
+// (one each per device, default priority, created on first use), and the
+// events that fork them from the caller's stream and join them back.  Calls on one
 // device are enqueued under a lock, so that the events are not recorded by two
 // calls at once.
 struct SideStream {
-  hipStream_t s = nullptr, w = nullptr;
+  hipStream_t s = nullptr, w = nullptr, r = nullptr;
   hipEvent_t fork[16] = {}, prep = nullptr, join = nullptr;
   hipEvent_t wfork[2 * 16 + 1] = {}, wdone[16 + 1] = {};
+  hipEvent_t rfork = nullptr, rdone[16] = {};
 };
 constexpr int kSideDevices = 64;
 std::mutex g_side_mu;
@@ -141,10 +144,15 @@ hipError_t side_stream(SideStream **out) {
   if (dev < 0 || dev >= kSideDevices) return hipErrorInvalidDevice;
   SideStream &ss = g_side[dev];
   if (!ss.s) {
-    hipStream_t st = nullptr, wt = nullptr;
+    hipStream_t st = nullptr, wt = nullptr, rt = nullptr;
     if ((e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipStreamCreateWithFlags(&wt, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipStreamCreateWithFlags(&rt, hipStreamNonBlocking)) != hipSuccess) return e;
     ss.w = wt;
+    ss.r = rt;
+    if ((e = hipEventCreateWithFlags(&ss.rfork, hipEventDisableTiming)) != hipSuccess) return e;
+    for (hipEvent_t &x : ss.rdone)
+      if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
     for (hipEvent_t &x : ss.fork)
       if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) return e;
     for (hipEvent_t &x : ss.wfork)
@@ -237,6 +245,9 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.ln_part_h = cv.take((size_t)2 * ln_part_rows(Rh) * d * 4);  // the history side's own partials
   L.gemm_part_h = cv.take((size_t)part_floats_hist(d, h, Rh) * 4);
   L.gemm_part_w = cv.take((size_t)part_floats_needed(d, h, M, 0, T) * 4);  // the weight-gradient stream's
+  L.gemm_part_r = cv.take((size_t)part_floats_needed(d, h, M, 0, T) * 4);  // the recompute stream's
+  L.qf_layer = (size_t)T * (3 * d + 3 * h) + (size_t)(2 * T + 3) / 4 * 4;  // c h13 g y qln, st
+  L.qf = cv.take(M * L.qf_layer * 4);
   L.total = cv.off;
   return STCA_OK;
 }
@@ -407,6 +418,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   std::vector<GemmArgs> wq;
   bool defer_w = false, wforked = false;
   float *const gpart_w = at<float>(ws, L.gemm_part_w);
+  float *const gpart_r = at<float>(ws, L.gemm_part_r);
   const int *gdev = nullptr;  // device cap applied by gemm(): rows (M) or, for split products, K
   hipStream_t gs = s;         // stream and split-K partials of gemm(): the caller's, or the history side's
   float *gp = gpart;
@@ -492,30 +504,42 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   if ((e = launch_gather_rows(table, cfg->table_rows, batch->tgt_ids, T, d, xt, false, s))) return hip_err("x_t");
   if ((e = launch_concat_layers(o_all, M, T, d, ocat, s))) return hip_err("concat");
 
-  // SwiGLU FFN (+LN) forward over n rows of x (fp32) with bf16 weights f:
-  // h13 = x [W1 | W3], g = SiLU(h1) h3, y = g W2, out = LN(y) (or y).
-  auto ffn_fwd = [&](int64_t n, const float *x, const stca_ffn &f, bool ln, float *out) -> hipError_t {
+  // A query-side FFN's forward activations: the input c (when it is not x_t),
+  // h13 = c [W1 | W3], g = SiLU(h1) h3, y = g W2, LN statistics, out = LN(y).
+  struct QBuf {
+    float *c, *h13, *g, *y, *st, *out;
+  };
+  const QBuf zb{c, h13, g, y, st, qln};  // the z head's
+  auto qbuf = [&](int i) -> QBuf {      // layer i's, recomputed ahead: c h13 g y out st
+    float *b = at<float>(ws, L.qf) + (size_t)i * L.qf_layer;
+    const size_t td = (size_t)T * d, th = (size_t)T * h;
+    float *qc = b, *qh13 = qc + td, *qg = qh13 + 2 * th, *qy = qg + th, *qout = qy + td, *qst = qout + td;
+    return QBuf{qc, qh13, qg, qy, qst, qout};
+  };
+  // SwiGLU FFN (+LN) forward over n rows of x (fp32) with bf16 weights f,
+  // into q, on stream sq (with gemm()'s stream set to it)
+  auto ffn_fwd = [&](int64_t n, const float *x, const stca_ffn &f, bool ln, const QBuf &q, hipStream_t sq) -> hipError_t {
     hipError_t er;
-    if ((er = gemm(n, h, d, x, false, d, 1, f.w1, true, h, 1, h13, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
-    if ((er = gemm(n, h, d, x, false, d, 1, f.w3, true, h, 1, h13 + h, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
-    if ((er = launch_swiglu_fwd(h13, n, h, g, false, s))) return er;
-    if ((er = gemm(n, d, h, g, false, h, 1, f.w2, true, d, 1, y, d, 1, 1.f, 0.f, kTgt))) return er;
-    if (ln) return launch_ln_fwd(y, n, d, f.ln_g, f.ln_b, out, false, st, s);
+    if ((er = gemm(n, h, d, x, false, d, 1, f.w1, true, h, 1, q.h13, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
+    if ((er = gemm(n, h, d, x, false, d, 1, f.w3, true, h, 1, q.h13 + h, 2 * h, 1, 1.f, 0.f, kTgt))) return er;
+    if ((er = launch_swiglu_fwd(q.h13, n, h, q.g, false, sq))) return er;
+    if ((er = gemm(n, d, h, q.g, false, h, 1, f.w2, true, d, 1, q.y, d, 1, 1.f, 0.f, kTgt))) return er;
+    if (ln) return launch_ln_fwd(q.y, n, d, f.ln_g, f.ln_b, q.out, false, q.st, sq);
     return hipSuccess;
   };
   // its backward from dout [n, d] to dx [n, d] (overwritten), weight grads +=
   auto ffn_bwd = [&](int64_t n, const float *x, const stca_ffn &f, const stca_ffn_grad &fg, bool ln, const float *dout,
-                     float *dx) -> hipError_t {
+                     float *dx, const QBuf &q) -> hipError_t {
     hipError_t er;
     const float *dyv = dout;
     if (ln) {
-      if ((er = launch_ln_bwd(dout, y, st, n, d, f.ln_g, dy, false, fg.ln_g, fg.ln_b, lnpart, s))) return er;
+      if ((er = launch_ln_bwd(dout, q.y, q.st, n, d, f.ln_g, dy, false, fg.ln_g, fg.ln_b, lnpart, s))) return er;
       dyv = dy;
     }
     // dG = dY W2^T; dW2 += G^T dY
     if ((er = gemm(n, h, d, dyv, false, d, 1, f.w2, true, 1, d, dg, h, 1, 1.f, 0.f, kTgt))) return er;
-    if ((er = gemm(h, d, n, g, false, 1, h, dyv, false, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return er;
-    if ((er = launch_swiglu_bwd(dg, h13, n, h, dh13, false, s))) return er;
+    if ((er = gemm(h, d, n, q.g, false, 1, h, dyv, false, d, 1, fg.w2, d, 1, 1.f, 1.f, kWgrad))) return er;
+    if ((er = launch_swiglu_bwd(dg, q.h13, n, h, dh13, false, s))) return er;
     // dW1 += x^T dH1, dW3 += x^T dH3
     if ((er = gemm(d, h, n, x, false, 1, d, dh13, false, 2 * h, 1, fg.w1, h, 1, 1.f, 1.f, kWgrad))) return er;
     if ((er = gemm(d, h, n, x, false, 1, d, dh13 + h, false, 2 * h, 1, fg.w3, h, 1, 1.f, 1.f, kWgrad))) return er;
@@ -523,6 +547,36 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     if ((er = gemm(n, d, h, dh13, false, 2 * h, 1, f.w1, true, 1, h, dx, d, 1, 1.f, 0.f, kTgt))) return er;
     return gemm(n, d, h, dh13 + h, false, 2 * h, 1, f.w3, true, 1, h, dx, d, 1, 1.f, 1.f, kTgt);
   };
+
+  // ---- every layer's query forward, recomputed into buffers of its own on the
+  // recompute stream: c = x_t (layer 0) or [o_1..o_i-1 | x_t] W_C, then the
+  // query FFN and LN.  It reads only forward outputs, so it runs, last layer
+  // first, beside the z head and the attention backward; each layer's query
+  // side waits for its event.
+  {
+    hipStream_t rs = side->r;
+    if ((e = hipEventRecord(side->rfork, s)) || (e = hipStreamWaitEvent(rs, side->rfork, 0)))
+      return hip_err("recompute stream fork");
+    gs = rs;
+    gp = gpart_r;
+    for (int i = M - 1; i >= 0 && !e; --i) {
+      const stca_layer &lw = w->layers[i];
+      const QBuf q = qbuf(i);
+      const float *cin = xt;
+      if (i > 0) {
+        const int64_t K1 = (int64_t)i * d;
+        if ((e = gemm(T, d, K1, ocat, false, MD, 1, lw.wc, true, d, 1, q.c, d, 1, 1.f, 0.f, kTgt))) break;
+        if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, d, 1, q.c, d, 1, 1.f, 1.f, kTgt)))
+          break;
+        cin = q.c;
+      }
+      if ((e = ffn_fwd(T, cin, lw.q, true, q, rs))) break;
+      e = hipEventRecord(side->rdone[i], rs);
+    }
+    gs = s;
+    gp = gpart;
+    if (e) return hip_err("query forward recompute");
+  }
 
   // ---- history rows, gathered once (every layer reads the same raw X), the
   // items sorted by unique row, the weights packed for the history row pass:
@@ -602,9 +656,9 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     if ((e = gemm(T, d, MD, ocat, false, MD, 1, w->wz, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("z");
     if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)w->wz + MD * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
       return hip_err("z");
-    if ((e = ffn_fwd(T, c, w->z, zln, qln))) return hip_err("z ffn");
+    if ((e = ffn_fwd(T, c, w->z, zln, zb, s))) return hip_err("z ffn");
     defer_w = true;
-    if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc))) return hip_err("z backward");
+    if ((e = ffn_bwd(T, c, w->z, gr->z, zln, dz, dc, zb))) return hip_err("z backward");
     // dW_Z += [o | x_t]^T dcz; d[o | x_t] = dcz W_Z^T
     if ((e = gemm(MD, d, T, ocat, false, 1, MD, dc, false, d, 1, gr->wz, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWz");
     if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
@@ -766,24 +820,18 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       for (int k = 2; k <= 4; ++k)
         if ((e = rec(ev + k))) return hip_err("stage event");
     }
-    // query side of layer i, recomputed: c = x_t (i = 0) or [o_1..o_i-1 | x_t] W_C;
+    // query side of layer i, over its recomputed forward (c = x_t for i = 0);
     // first, the previous query side's (or the z head's) queued weight
-    // gradients must be done with the buffers it reuses
+    // gradients must be done with the gradient buffers it reuses
     if ((e = hipStreamWaitEvent(s, wpending, 0))) return hip_err("weight-gradient stream");
-    const float *cin = xt;
-    if (i > 0) {
-      const int64_t K1 = (int64_t)i * d;
-      if ((e = gemm(T, d, K1, ocat, false, MD, 1, lw.wc, true, d, 1, c, d, 1, 1.f, 0.f, kTgt))) return hip_err("wc");
-      if ((e = gemm(T, d, d, xt, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, d, 1, c, d, 1, 1.f, 1.f, kTgt)))
-        return hip_err("wc");
-      cin = c;
-    }
-    if ((e = ffn_fwd(T, cin, lw.q, true, qln))) return hip_err("query ffn");
+    if ((e = hipStreamWaitEvent(s, side->rdone[i], 0))) return hip_err("recompute stream");
+    const QBuf q = qbuf(i);
+    const float *cin = i > 0 ? q.c : xt;
     // Q = q W_Q / sqrt(d_h): dW_Q += q^T dQ / sqrt(d_h), dq = dQ W_Q^T / sqrt(d_h)
     defer_w = true;
-    if ((e = gemm(d, d, T, qln, false, 1, d, dq, false, d, 1, lg.wq, d, 1, qscale, 1.f, kWgrad))) return hip_err("dWq");
+    if ((e = gemm(d, d, T, q.out, false, 1, d, dq, false, d, 1, lg.wq, d, 1, qscale, 1.f, kWgrad))) return hip_err("dWq");
     if ((e = gemm(T, d, d, dq, false, d, 1, lw.wq, true, 1, d, dqt, d, 1, qscale, 0.f, kTgt))) return hip_err("dq");
-    if ((e = ffn_bwd(T, cin, lw.q, lg.q, true, dqt, dc))) return hip_err("query backward");
+    if ((e = ffn_bwd(T, cin, lw.q, lg.q, true, dqt, dc, q))) return hip_err("query backward");
     if (i > 0) {
       const int64_t K1 = (int64_t)i * d;
       if ((e = gemm(K1, d, T, ocat, false, 1, MD, dc, false, d, 1, lg.wc, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWc");
