@@ -202,19 +202,17 @@ struct UniqueSumArgs {
   const int *n_unique;    // device count
   int *keys[2], *vals[2]; // [n] ints each (scratch)
   int *hist;              // sort_hist_ints(n) ints (scratch)
-  int *seg, *poff, *moff; // [max_u + 1] ints each (scratch)
+  int *seg;               // [max_u + 1] ints (scratch): run starts
   const bf16_t *dkv;      // [n, d2]
-  int d2;
-  float *ppart;           // [agg_max_partials(n), d2] (scratch)
-  int *p2u;               // [agg_max_pieces(n, max_u)] (scratch): the unique row of every piece
-  int *cnt;               // [max_u] (scratch): pieces of a row done (zero between calls)
+  int d2;                 // 2d, at most 1024
+  float *ppart;           // [agg_partial_floats(n, d2)] (scratch)
   bf16_t *out;            // [max_u, d2]
   const int *sorted_items;  // set by launch_unique_sort (points into vals)
+  const int *sorted_keys;   // set by launch_unique_sort (points into keys)
 };
-int64_t agg_max_partials(int64_t n);
-int64_t agg_max_pieces(int64_t n, int64_t max_u);
-// Once per batch: the items sorted by (unique row, item) and the run / piece
-// offsets; then per layer: the sums of that layer's dkv.
+int64_t agg_partial_floats(int64_t n, int d2);
+// Once per batch: the items sorted by (unique row, item) and the run starts;
+// then per layer: the sums of that layer's dkv.
 hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s);
 hipError_t launch_unique_sums(const UniqueSumArgs &a, hipStream_t s);
 

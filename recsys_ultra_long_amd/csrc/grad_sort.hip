@@ -10,9 +10,11 @@
 //   1. radix sort (8-bit digits; per pass: block histograms, one scan,
 //      stable scatter that ranks equal digits inside a wave with ballots);
 //   2. run starts seg[u] (every unique index has at least one item);
-//   3. runs cut into pieces of at most kPiece items, one wave per piece;
-//      a run of one piece is written directly, longer runs through per-piece
-//      partials folded in piece order.
+//   3. the sorted items cut into spans of kSpan, one wave per span, which
+//      sums each run (or the part of it inside the span) front to back: a
+//      run inside the span is written directly, one that crosses a span
+//      boundary leaves one partial per span, and a second launch folds them
+//      in span order.
 #include "grad_internal.h"
 
 namespace stca {
@@ -21,8 +23,7 @@ namespace {
 constexpr int kT = 256;
 constexpr int kIPT = 8;                // items per thread per sort block
 constexpr int kIPB = kT * kIPT;        // items per sort block
-constexpr int kPiece = 256;            // items per aggregation piece
-static_assert(kPiece % 64 == 0, "whole groups of 64 item ids per piece");
+constexpr int kSpan = 128;             // sorted items per wave of the run sums (two per lane)
 
 __global__ __launch_bounds__(kT) void iota_kernel(int *v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * kT + threadIdx.x;
@@ -170,113 +171,126 @@ __global__ __launch_bounds__(kT) void seg_kernel(const int *__restrict__ skeys, 
   if (i == 0 || skeys[i - 1] != k) seg[k] = (int)i;
 }
 
-// pieces per unique row (all, and those of rows with more than one piece)
-__global__ __launch_bounds__(kT) void pieces_kernel(const int *__restrict__ seg, const int *n_unique, int64_t max_u,
-                                                    int *np, int *mp) {
-  const int64_t u = (int64_t)blockIdx.x * kT + threadIdx.x;
-  if (u > max_u) return;
-  int a = 0, b = 0;
-  if (u < *n_unique) {
-    const int len = seg[u + 1] - seg[u];
-    a = (len + kPiece - 1) / kPiece;
-    b = a > 1 ? a : 0;
-  }
-  np[u] = a;
-  mp[u] = b;
-}
-
-// The unique row of every piece, and a zero count of finished pieces per row.
-__global__ __launch_bounds__(kT) void p2u_kernel(const int *__restrict__ poff, const int *n_unique, int64_t max_u,
-                                                 int *p2u, int *cnt) {
-  const int64_t u = (int64_t)blockIdx.x * kT + threadIdx.x;
-  if (u >= max_u) return;
-  cnt[u] = 0;
-  if (u >= *n_unique) return;
-  for (int p = poff[u]; p < poff[u + 1]; ++p) p2u[p] = (int)u;
-}
-
-// One wave per piece: the fp32 sum of its items' dK | dV rows (2d bf16
-// values per row, 8 per lane per 512-value chunk), in item order.  A row of
-// one piece is written at once; a row of several leaves one partial per
-// piece, and the wave that finishes the row's last piece (a per-row count,
-// after a device-scope fence) folds them in piece order and clears the count.
-__global__ __launch_bounds__(kT) void agg_kernel(const bf16_t *__restrict__ dkv, const int *__restrict__ stok,
-                                                 const int *__restrict__ seg, const int *__restrict__ poff,
-                                                 const int *__restrict__ moff, const int *__restrict__ p2u,
-                                                 const int *n_unique, int d2, int64_t max_pieces, bf16_t *out,
-                                                 float *ppart, int *cnt) {
+// One wave per span of kSpan consecutive items in (unique row, item) order:
+// the fp32 sum of each run's dK | dV rows over the span (2d bf16 values per
+// row, 8 per lane per 512-value block), in item order.  Rows are loaded 16 at
+// a time across run boundaries (item ids and run keys one per lane, passed
+// round by lane shuffles).  A run that lies inside the span is written as
+// bf16 at once; one that continues from the previous span leaves its partial
+// in slot 2w, one that starts here and continues in slot 2w + 1.
+__global__ __launch_bounds__(kT) void span_sum_kernel(const bf16_t *__restrict__ dkv, const int *__restrict__ skey,
+                                                      const int *__restrict__ stok, int64_t n, int d2, bf16_t *out,
+                                                      float *ppart) {
   const int lane = threadIdx.x & 63;
-  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int U = *n_unique;
-  if (p >= max_pieces || p >= poff[U]) return;
-  const int u = p2u[p];
-  const int k = (int)(p - poff[u]);
-  const int npu = poff[u + 1] - poff[u];
-  const int i0 = seg[u] + k * kPiece;
-  const int n = min(i0 + kPiece, seg[u + 1]) - i0;  // items of this piece, 1 .. kPiece
-  // The piece's item ids, kPiece / 64 per lane, loaded together (ids past
-  // the piece repeat its last one); row q of a group then comes from lane q
-  // by a lane shuffle, so that 16 row loads go out at once.
-  constexpr int PL = kPiece / 64;
-  int tok[PL];
-#pragma unroll
-  for (int j = 0; j < PL; ++j) tok[j] = stok[i0 + min(j * 64 + lane, n - 1)];
-  // every lane runs the loop (the shuffles read all lanes); lanes past the
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t j0 = w * kSpan;
+  if (j0 >= n) return;
+  const int m = (int)min((int64_t)kSpan, n - j0);  // items of this span, 1 .. kSpan
+  const int ia = min(lane, m - 1), ib = min(64 + lane, m - 1);
+  const int key0 = skey[j0 + ia], key1 = skey[j0 + ib];
+  const int tok0 = stok[j0 + ia], tok1 = stok[j0 + ib];
+  const int prev = j0 > 0 ? skey[j0 - 1] : -1;     // the run before the span
+  const int next = j0 + m < n ? skey[j0 + m] : -1;  // the run after it
+  // every lane runs the loops (the shuffles read all lanes); lanes past the
   // row's 2d values read column 0 and store nothing
   for (int c0 = 0; c0 < d2; c0 += 512) {
     const int f0 = c0 + lane * 8;
     const bool on = f0 < d2;
     const int fc = on ? f0 : 0;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int cur = __shfl(key0, 0), start = 0;  // the current run and its first item in the span
+    auto flush = [&](bool cont_next) {
+      const bool cont_prev = start == 0 && cur == prev;
+      if (!on) return;
+      if (!cont_prev && !cont_next) {
+        u32x4 wv;
 #pragma unroll
-    for (int j = 0; j < PL; ++j) {
-      const int m = min(n - j * 64, 64);  // items of this group of 64
-      for (int b = 0; b < m; b += 16) {
-        bf16x8 x[16];
+        for (int e = 0; e < 4; ++e) wv[e] = pack_bf2(acc[2 * e], acc[2 * e + 1]);
+        *reinterpret_cast<u32x4 *>(out + (int64_t)cur * d2 + f0) = wv;
+      } else {
+        float *pp = ppart + (2 * w + (cont_prev ? 0 : 1)) * d2 + f0;
+        *reinterpret_cast<float4 *>(pp) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4 *>(pp + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      }
+    };
+    for (int b = 0; b < m; b += 16) {
+      bf16x8 x[16];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) x[q] = ld8(dkv + (int64_t)__shfl(tok[j], min(b + q, m - 1)) * d2 + fc);
+      for (int q = 0; q < 16; ++q) {
+        const int j = min(b + q, m - 1);
+        x[q] = ld8(dkv + (int64_t)__shfl(j < 64 ? tok0 : tok1, j & 63) * d2 + fc);
+      }
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (b + q < m) {  // in item order
+      for (int q = 0; q < 16; ++q) {
+        const int j = b + q;
+        if (j < m) {
+          const int k = __shfl(j < 64 ? key0 : key1, j & 63);
+          if (k != cur) {  // the run ended at item j - 1
+            flush(false);
+            cur = k;
+            start = j;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += bf2f((bf16_t)x[q][e]);
+            for (int e = 0; e < 8; ++e) acc[e] = 0.f;
           }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += bf2f((bf16_t)x[q][e]);
+        }
       }
     }
-    if (!on) continue;
-    if (npu == 1) {
-      u32x4 wv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) wv[e] = pack_bf2(acc[2 * e], acc[2 * e + 1]);
-      *reinterpret_cast<u32x4 *>(out + (int64_t)u * d2 + f0) = wv;
-    } else {
-      float *pp = ppart + (int64_t)(moff[u] + k) * d2 + f0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pp[e] = acc[e];
-    }
+    flush(cur == next);
   }
-  if (npu == 1) return;
-  __threadfence();  // this piece's partial is visible device-wide
-  int done = 0;
-  if (lane == 0) done = atomicAdd(&cnt[u], 1);
-  done = __shfl(done, 0);
-  if (done != npu - 1) return;
-  __threadfence();
-  // the row's last piece: fold all of its partials in piece order (loads
-  // that bypass this CU's cache: other workgroups wrote them)
-  for (int f0 = lane * 8; f0 < d2; f0 += 512) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < npu; ++q) {
-      const float *pp = ppart + (int64_t)(moff[u] + q) * d2 + f0;
+}
+
+// One workgroup per span w whose last run starts in span w and continues past
+// it: that run's partials (slot 2w + 1, then slot 2c of each later span c it
+// reaches) summed in span order -- eight waves over fixed consecutive groups
+// of them, the group sums then in wave order -- and written as bf16.
+constexpr int kFoldT = 512;
+__global__ __launch_bounds__(kFoldT) void span_fold_kernel(const int *__restrict__ skey, const int *__restrict__ seg,
+                                                           int64_t n, int d2, const float *__restrict__ ppart,
+                                                           bf16_t *out) {
+  __shared__ float red[kFoldT / 64][1024];
+  const int64_t w = blockIdx.x;
+  const int64_t j1 = (w + 1) * kSpan;  // first item after the span
+  if (j1 >= n) return;                 // the last span: nothing continues
+  const int u = skey[j1 - 1];
+  if (skey[j1] != u) return;           // its last run ends inside it
+  if (seg[u] < w * kSpan) return;      // the run started earlier: folded there
+  const int k = (int)((seg[u + 1] - 1) / kSpan - w + 1);  // spans the run reaches
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = (k + kFoldT / 64 - 1) / (kFoldT / 64);
+  const int q0 = min(wave * G, k), q1 = min(q0 + G, k);
+  for (int f0 = lane * 4; f0 < d2; f0 += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int qb = q0; qb < q1; qb += 8) {
+      float4 x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += __hip_atomic_load(pp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < 8; ++r) {
+        const int q = min(qb + r, q1 - 1);
+        const int64_t slot = q == 0 ? 2 * w + 1 : 2 * (w + q);
+        x[r] = *reinterpret_cast<const float4 *>(ppart + slot * d2 + f0);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (qb + r < q1) {
+          acc.x += x[r].x;
+          acc.y += x[r].y;
+          acc.z += x[r].z;
+          acc.w += x[r].w;
+        }
     }
-    u32x4 wv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wv[e] = pack_bf2(acc[2 * e], acc[2 * e + 1]);
-    *reinterpret_cast<u32x4 *>(out + (int64_t)u * d2 + f0) = wv;
+    *reinterpret_cast<float4 *>(&red[wave][f0]) = acc;
   }
-  if (lane == 0) cnt[u] = 0;  // ready for the next layer's sums
+  __syncthreads();
+  for (int f = 2 * threadIdx.x; f < d2; f += 2 * kFoldT) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int g = 0; g < kFoldT / 64; ++g) {
+      a0 += red[g][f];
+      a1 += red[g][f + 1];
+    }
+    *reinterpret_cast<uint32_t *>(out + (int64_t)u * d2 + f) = pack_bf2(a0, a1);
+  }
 }
 
 int bits_for(int64_t n) {
@@ -287,8 +301,7 @@ int bits_for(int64_t n) {
 
 }  // namespace
 
-int64_t agg_max_pieces(int64_t n, int64_t max_u) { return max_u + n / kPiece + 1; }
-int64_t agg_max_partials(int64_t n) { return 2 * (n / kPiece) + 2; }
+int64_t agg_partial_floats(int64_t n, int d2) { return 2 * ((n + kSpan - 1) / kSpan) * (int64_t)d2; }
 
 // scratch of excl_scan over n values: one total per block (the block totals
 // of any scan of up to 256 * n / kIPB + n values fit after the histogram)
@@ -349,21 +362,19 @@ hipError_t launch_unique_sort(UniqueSumArgs &a, hipStream_t s) {
   hipError_t e = launch_radix_sort(a.tok2u, nullptr, n, radix_bits(a.max_u), a.keys, a.vals, a.hist, &rr, s);
   if (e != hipSuccess) return e;
   a.sorted_items = rr.vals;
+  a.sorted_keys = rr.keys;
   hipLaunchKernelGGL(seg_kernel, dim3(g), dim3(kT), 0, s, rr.keys, n, a.n_unique, a.seg);
-  const unsigned gu = (unsigned)((a.max_u + 1 + kT - 1) / kT);
-  hipLaunchKernelGGL(pieces_kernel, dim3(gu), dim3(kT), 0, s, a.seg, a.n_unique, a.max_u, a.poff, a.moff);
-  if ((e = excl_scan(a.poff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
-  if ((e = excl_scan(a.moff, a.max_u + 1, a.hist, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(p2u_kernel, dim3((unsigned)((a.max_u + kT - 1) / kT)), dim3(kT), 0, s, a.poff, a.n_unique,
-                     a.max_u, a.p2u, a.cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_unique_sums(const UniqueSumArgs &a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  const int64_t maxp = agg_max_pieces(a.n, a.max_u);
-  hipLaunchKernelGGL(agg_kernel, dim3((unsigned)((maxp + 3) / 4)), dim3(kT), 0, s, a.dkv, a.sorted_items, a.seg,
-                     a.poff, a.moff, a.p2u, a.n_unique, a.d2, maxp, a.out, a.ppart, a.cnt);
+  if (a.d2 > 1024 || a.d2 % 8) return hipErrorInvalidValue;
+  const int64_t spans = (a.n + kSpan - 1) / kSpan;
+  hipLaunchKernelGGL(span_sum_kernel, dim3((unsigned)((spans + 3) / 4)), dim3(kT), 0, s, a.dkv, a.sorted_keys,
+                     a.sorted_items, a.n, a.d2, a.out, a.ppart);
+  hipLaunchKernelGGL(span_fold_kernel, dim3((unsigned)spans), dim3(kFoldT), 0, s, a.sorted_keys, a.seg, a.n, a.d2,
+                     (const float *)a.ppart, a.out);
   return hipGetLastError();
 }
 

@@ -71,8 +71,7 @@ struct BwdLayout {
   // STCA_FLAG_DEDUP: the history backward runs over Rh = drows unique rows
   bool dedup = false;
   int64_t Rh = 0;
-  size_t keys0 = 0, keys1 = 0, vals0 = 0, vals1 = 0, hist = 0, seg = 0, poff = 0, moff = 0, ppart = 0, dKVu = 0;
-  size_t p2u = 0, cnt = 0;
+  size_t keys0 = 0, keys1 = 0, vals0 = 0, vals1 = 0, hist = 0, seg = 0, ppart = 0, dKVu = 0;
   size_t total = 0;
 };
 
@@ -233,11 +232,7 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
     L.vals1 = cv.take(R * 4);
     L.hist = cv.take((size_t)radix_hist_ints(R) * 4);
     L.seg = cv.take((size_t)(Rh + 1) * 4);
-    L.poff = cv.take((size_t)(Rh + 1) * 4);
-    L.moff = cv.take((size_t)(Rh + 1) * 4);
-    L.ppart = cv.take((size_t)agg_max_partials(R) * 2 * d * 4);
-    L.p2u = cv.take((size_t)agg_max_pieces(R, Rh) * 4);
-    L.cnt = cv.take((size_t)Rh * 4);
+    L.ppart = cv.take((size_t)agg_partial_floats(R, (int)(2 * d)) * 4);
     L.dKVu = cv.take(Rh * 2 * d * 2);
   }
   L.ln_part = cv.take((size_t)2 * ln_part_rows(T) * d * 4);
@@ -611,12 +606,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     ua.vals[1] = at<int>(ws, L.vals1);
     ua.hist = at<int>(ws, L.hist);
     ua.seg = at<int>(ws, L.seg);
-    ua.poff = at<int>(ws, L.poff);
-    ua.moff = at<int>(ws, L.moff);
     ua.d2 = 2 * d;
     ua.ppart = at<float>(ws, L.ppart);
-    ua.p2u = at<int>(ws, L.p2u);
-    ua.cnt = at<int>(ws, L.cnt);
     ua.out = at<bf16_t>(ws, L.dKVu);
     if ((e = launch_unique_sort(ua, hp))) return hip_err("unique sort");
   }

@@ -28,7 +28,7 @@ Checks:
 * unique-id dedup (STCA_FLAG_DEDUP): the history backward once per distinct
   id on the summed dK | dV of its items -- against the oracle on every
   workload above, bitwise repeatable, with out-of-range ids, with rows whose
-  items fill one, just over one and several 256-item pieces, and at full
+  items fill one, just over one and several 128-item spans, and at full
   size.
 """
 import numpy as np
@@ -339,20 +339,22 @@ def test_backward_dedup_matches_oracle(k):
     compare_all(p, g, ref)
 
 
-def test_backward_dedup_rows_spanning_pieces():
-    """Unique rows whose items fill exactly one 256-item piece, one item more
-    than a piece, and several pieces (their partial sums folded in piece
-    order), scattered over the users: against the oracle."""
+def test_backward_dedup_rows_spanning_spans():
+    """Unique rows of exactly one 128-item span's length, one item more, two
+    spans and one, and several spans (their partial sums folded in span
+    order), scattered over the users, beside rows of one or a few items:
+    against the oracle."""
     p = I.make_problem(_small(3, L=700))
     rng = np.random.default_rng(17)
     pos = rng.permutation(p.n_hist)
-    p.hist_ids[np.isin(p.hist_ids, [11, 12, 13])] = 14  # the three rows get only the items below
-    for ident, (a, b) in ((11, (0, 256)), (12, (256, 513)), (13, (513, 1113))):
+    hot = [10, 11, 12, 13]
+    p.hist_ids[np.isin(p.hist_ids, hot)] = 14  # the hot rows get only the items below
+    for ident, (a, b) in zip(hot, ((0, 128), (128, 257), (257, 514), (514, 1114))):
         p.hist_ids[pos[a:b]] = ident
     dz = I.upstream_grad(p.spec, p.n_tgt)
-    counts = np.bincount(p.hist_ids[p.hist_ids >= 0], minlength=14)[11:14]
-    print(f"[bwd-dedup] rows spanning pieces: items per hot row {counts.tolist()}", flush=True)
-    assert counts.tolist() == [256, 257, 600]
+    counts = np.bincount(p.hist_ids[p.hist_ids >= 0], minlength=14)[10:14]
+    print(f"[bwd-dedup] rows spanning spans: items per hot row {counts.tolist()}", flush=True)
+    assert counts.tolist() == [128, 129, 257, 600]
     g = gpu_backward(p, dz, dedup=True)
     ref = OG.backward_problem(p, dz)
     assert g["status"] == 0
