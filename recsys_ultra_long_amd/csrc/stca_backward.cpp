@@ -81,10 +81,13 @@ stca_config forward_cfg(const stca_config *c) {
   return f;
 }
 
-// Split-K choice: weight gradients (K = rows) aim at 2048 workgroups (the
-// rows may be capped on the device, leaving only part of them live); a
-// product over rows with few output tiles is split too (K = the width).
-int split_weight_grad(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 2048, 256); }
+// Split-K choice: weight gradients (K = rows) aim at 1024 workgroups (the
+// rows may be capped on the device, leaving only part of them live): twice
+// that writes and re-reads twice the fp32 partials (a [d, 2d] gradient over
+// 64K rows: 128 MB) for no faster product, half of it leaves the history
+// stream's products long enough to hold up the step; a product over rows
+// with few output tiles is split too (K = the width).
+int split_weight_grad(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 1024, 256); }
 int split_rows(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 512, 64); }
 
 // Largest split-K partial buffer any product of the backward asks for (its
