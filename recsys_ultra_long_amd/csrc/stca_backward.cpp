@@ -85,10 +85,13 @@ stca_config forward_cfg(const stca_config *c) {
 // rows may be capped on the device, leaving only part of them live): twice
 // that writes and re-reads twice the fp32 partials (a [d, 2d] gradient over
 // 64K rows: 128 MB) for no faster product, half of it leaves the history
-// stream's products long enough to hold up the step; a product over rows
-// with few output tiles is split too (K = the width).
+// stream's products long enough to hold up the step.  A product over the
+// target rows with few output tiles is split too (K = the width), into
+// chunks of at least 128: with 64-deep chunks the partials' reduce launches,
+// stretched while the history stream holds the CUs, cost more than the
+// split gains (step 5.10 against 4.99 ms on the training workload).
 int split_weight_grad(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 1024, 256); }
-int split_rows(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 512, 64); }
+int split_rows(int64_t m, int64_t n, int64_t k) { return gemm_split_for(m, n, k, 256, 128); }
 
 // Largest split-K partial buffer any product of the backward asks for (its
 // GEMM refuses a split that would need more).
