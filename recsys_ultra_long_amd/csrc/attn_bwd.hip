@@ -283,6 +283,224 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(AttnBwdArgs a) {
       for (int r = 0; r < 16; ++r) pd[(nt * 32 + c32_row(lane, r)) * DH + nn * 32 + l32] = dq[nt][nn][r];
 }
 
+// The same backward for users of at most 16 targets at d_h = 32 (the training
+// workload's shape), on tiles that match it instead of 32-target tiles with
+// half their columns empty.  Per 32-key block and wave:
+//   S^T, dP^T [keys x targets]:  two 16x16x32 tiles each (keys 0-15, 16-31;
+//                                 k = d_h), A = K / V rows, B = Q / dA rows;
+//   dQ [targets x d_h] += dS K:  16x16x32 per 16 features, A = dS straight
+//                                 from the S^T tiles (lane = target; its 8
+//                                 keys, 4 of each tile, form the k-group in
+//                                 that order), B = K^T from a wave-private LDS
+//                                 copy read in the same key order;
+//   dK^T, dV^T [d_h x keys]:     one 32x32x16 each over the 16 targets, A =
+//                                 Q^T / dA^T, B = dS^T / P^T re-read from
+//                                 wave-private LDS as [key][target].
+constexpr int kT16 = 16;
+constexpr int LT16 = kT16 + 8;  // row stride of [.][target] tiles (48 bytes)
+
+template <int SCORE, bool DD>
+__global__ __launch_bounds__(256) void attn_bwd16_kernel(AttnBwdArgs a) {
+  constexpr int DH = 32;
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[kT16 * (DH + 8)];
+  __shared__ __attribute__((aligned(16))) bf16_t sdA[kT16 * (DH + 8)];
+  __shared__ __attribute__((aligned(16))) bf16_t sQT[DH * LT16];
+  __shared__ __attribute__((aligned(16))) bf16_t sdAT[DH * LT16];
+  __shared__ __attribute__((aligned(16))) bf16_t sKT[4][DH * LK];
+  __shared__ __attribute__((aligned(16))) bf16_t sP[4][32 * LT16];
+  __shared__ __attribute__((aligned(16))) bf16_t sdS[4][32 * LT16];
+  __shared__ float slse[kT16], sD[kT16];
+
+  const Plan P = a.plan;
+  const int c = blockIdx.x, eta = blockIdx.y;
+  if (c >= P.coff[a.B]) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;  // 16x16 operand lanes: row / column, k-group
+  const int l32 = lane & 31, g2 = lane >> 5;  // 32x32 operand lanes
+  const int u = upper_index(P.coff, a.B, c);
+  const int ci = c - P.coff[u];
+  const int64_t h0 = P.hoff[u];
+  const int L = P.hoff[u + 1] - P.hoff[u];
+  const int k_begin = ci * a.nb * 32;
+  const int k_end = min(L, k_begin + a.nb * 32);
+  const int64_t t0 = P.toff[u];
+  const int m = min(P.toff[u + 1] - P.toff[u], kT16);
+  const int d = a.d;
+  const int64_t col0 = (int64_t)eta * DH;
+
+  // the user's Q and dA rows of this head (16 targets x 4 pieces of 8; rows
+  // past m read target 0 and are zeroed)
+  if (tid < kT16 * (DH / 8)) {
+    const int t = tid >> 2, n0 = (tid & 3) * 8;
+    u32x4 q = {0u, 0u, 0u, 0u}, gq = q;
+    if (m > 0) {
+      const int64_t row = (t0 + (t < m ? t : 0)) * d + col0 + n0;
+      q = *reinterpret_cast<const u32x4 *>(a.q + row);
+      gq = *reinterpret_cast<const u32x4 *>(a.da_lo + row);
+      const uint32_t keep = t < m ? 0xffffffffu : 0u;
+      q &= keep;
+      gq &= keep;
+    }
+    *reinterpret_cast<u32x4 *>(sQ + t * (DH + 8) + n0) = q;
+    *reinterpret_cast<u32x4 *>(sdA + t * (DH + 8) + n0) = gq;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      sQT[(n0 + k) * LT16 + t] = (bf16_t)(q[k >> 1] >> (16 * (k & 1)));
+      sdAT[(n0 + k) * LT16 + t] = (bf16_t)(gq[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  if (tid < kT16) {
+    slse[tid] = (SCORE == 0 && tid < m) ? a.lse[(t0 + tid) * a.H + eta] : 0.f;
+    sD[tid] = tid < m ? a.dsum[(t0 + tid) * a.H + eta] : 0.f;
+  }
+  __syncthreads();
+
+  f32x4 dq[2];
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dq[nn][r] = 0.f;
+
+  bf16_t *kt_w = sKT[w], *p_w = sP[w], *ds_w = sdS[w];
+  const bf16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  // Lane l loads, for tile t, key 16 t + l % 16 of the block, features
+  // 8 (l / 16) .. + 7: the 16x16x32 A operand as it comes from memory.  The
+  // next block's rows are loaded while the current one is worked on (with
+  // dedup the row ids one block further ahead); loads are unconditional
+  // (keys past the chunk read its last key, zeroed where used).
+  auto row_ids = [&](int kb, int (&id)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = min(kb + 16 * t + l16, k_end - 1);
+      id[t] = DD ? a.tok2u[h0 + key] : key;
+    }
+  };
+  auto load_kv = [&](const int (&id)[2], bf16x8(&kf)[2], bf16x8(&vf)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16_t *kr, *vr;
+      if (DD) {  // blocked K, row-major V of the unique rows
+        kr = a.k + ((((int64_t)(id[t] >> 5)) * a.H + eta) * 32 + (id[t] & 31)) * DH;
+        vr = a.v + (int64_t)id[t] * d + col0;
+      } else {
+        kr = a.k + (h0 + id[t]) * d + col0;
+        vr = a.v + (h0 + id[t]) * d + col0;
+      }
+      kf[t] = ld8(kr + 8 * g4);
+      vf[t] = ld8(vr + 8 * g4);
+    }
+  };
+  const int kb0 = k_begin + 32 * __builtin_amdgcn_readfirstlane(w);
+  bf16x8 kr0[2], vr0[2], kr1[2], vr1[2];  // the two register sets
+  int idn[2] = {0, 0};                    // the row ids of the block after the next
+  if (kb0 < k_end) {
+    int id0[2];
+    row_ids(kb0, id0);
+    load_kv(id0, kr0, vr0);
+    row_ids(kb0 + 128, idn);
+  }
+  const bf16x8 qb = ld8(sQ + l16 * (DH + 8) + 8 * g4);   // B of S^T: Q[target l16][k-group g4]
+  const bf16x8 gb = ld8(sdA + l16 * (DH + 8) + 8 * g4);  // B of dP^T
+  const bool tval = l16 < m;
+  const float lse = slse[l16], D = sD[l16];
+  auto block = [&](const int kb, const bf16x8(&kc)[2], const bf16x8(&vc)[2], bf16x8(&kn)[2], bf16x8(&vn)[2]) {
+    bf16x8 kf[2], vf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bool kval = kb + 16 * t + l16 < k_end;
+      kf[t] = kval ? kc[t] : zero8;
+      vf[t] = kval ? vc[t] : zero8;
+    }
+    // the next block (past the chunk's end: its last key again, unused)
+    load_kv(idn, kn, vn);
+    row_ids(kb + 256, idn);
+    // K^T [feature][key] for dQ's B operand
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kt_w[(8 * g4 + e) * LK + 16 * t + l16] = (bf16_t)kf[t][e];
+    wave_sync();
+    float ds[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 st = {0.f, 0.f, 0.f, 0.f}, dpt = st;
+      st = mfma16(kf[t], qb, st);
+      dpt = mfma16(vf[t], gb, dpt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 16 * t + 4 * g4 + r;  // key row within the block
+        const bool ok = tval && kb + kr < k_end;
+        float p, dsv;
+        if (SCORE == 0) {
+          p = ok ? __builtin_amdgcn_exp2f((st[r] - lse) * kLog2e) : 0.f;
+          dsv = p * (dpt[r] - D);
+        } else {
+          const bool pos = ok && st[r] > 0.f;
+          p = pos ? st[r] : 0.f;
+          dsv = pos ? dpt[r] : 0.f;
+        }
+        ds[t][r] = dsv;
+        p_w[kr * LT16 + l16] = f2bf(p);
+        ds_w[kr * LT16 + l16] = f2bf(dsv);
+      }
+    }
+    // dQ[targets] += dS K over the block's 32 keys: the lane's k-group g4 is
+    // keys 4 g4 .. + 3 then 16 + 4 g4 .. + 3
+    {
+      bf16x8 af;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        af[r] = (short)f2bf(ds[0][r]);
+        af[4 + r] = (short)f2bf(ds[1][r]);
+      }
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const bf16_t *row = kt_w + (nn * 16 + l16) * LK + 4 * g4;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(row);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(row + 16);
+        u32x4 bw = {lo[0], lo[1], hi[0], hi[1]};
+        dq[nn] = mfma16(af, __builtin_bit_cast(bf16x8, bw), dq[nn]);
+      }
+    }
+    wave_sync();
+    // dK^T = Q^T dS, dV^T = dA^T P over the 16 targets: features as rows,
+    // keys as columns, so each lane ends up with 16 consecutive features of
+    // one key for 16-byte stores
+    f32x16 dk, dv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[r] = 0.f;
+      dv[r] = 0.f;
+    }
+    dk = mfma32(ld8(sQT + l32 * LT16 + 8 * g2), ld8(ds_w + l32 * LT16 + 8 * g2), dk);
+    dv = mfma32(ld8(sdAT + l32 * LT16 + 8 * g2), ld8(p_w + l32 * LT16 + 8 * g2), dv);
+    wave_sync();
+    u32x4 k0, k1, v0, v1;
+    halves16(dk, g2, k0, k1);  // lane (key l32, g2): features 16 g2 .. 16 g2 + 15
+    halves16(dv, g2, v0, v1);
+    const int key = kb + l32;
+    if (key < k_end) {
+      bf16_t *row = a.dkv + (h0 + key) * 2 * d + col0 + 16 * g2;
+      *reinterpret_cast<u32x4 *>(row) = k0;
+      *reinterpret_cast<u32x4 *>(row + 8) = k1;
+      *reinterpret_cast<u32x4 *>(row + d) = v0;
+      *reinterpret_cast<u32x4 *>(row + d + 8) = v1;
+    }
+  };
+  for (int kb = kb0; kb < k_end; kb += 256) {
+    block(kb, kr0, vr0, kr1, vr1);
+    if (kb + 128 >= k_end) break;
+    block(kb + 128, kr1, vr1, kr0, vr0);
+  }
+  // this wave's dQ partial: targets 0..15 of the [64 targets][d_h] slot (the
+  // fold reads no target past the user's count)
+  float *pd = a.part_dq + (((int64_t)c * a.H + eta) * 4 + w) * kMaxTgt * DH;
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pd[(4 * g4 + r) * DH + nn * 16 + l16] = dq[nn][r];
+}
+
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= a.n_tgt * a.d) return;
@@ -319,7 +537,15 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
     if (a.tok2u) hipLaunchKernelGGL((attn_bwd_kernel<DH, SC, true>), grid, dim3(256), 0, s, a); \
     else hipLaunchKernelGGL((attn_bwd_kernel<DH, SC, false>), grid, dim3(256), 0, s, a);       \
   } while (0)
-    if (a.dh == 32) {
+#define AB16(SC)                                                                                  \
+  do {                                                                                            \
+    if (a.tok2u) hipLaunchKernelGGL((attn_bwd16_kernel<SC, true>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((attn_bwd16_kernel<SC, false>), grid, dim3(256), 0, s, a);        \
+  } while (0)
+    if (a.dh == 32 && a.max_tgt <= kT16) {  // every user has at most 16 targets
+      if (a.score) AB16(1);
+      else AB16(0);
+    } else if (a.dh == 32) {
       if (a.score) AB(32, 1);
       else AB(32, 0);
     } else if (a.dh == 64) {
@@ -329,6 +555,7 @@ hipError_t launch_attn_bwd(const AttnBwdArgs &a, hipStream_t s) {
       return hipErrorInvalidValue;
     }
 #undef AB
+#undef AB16
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

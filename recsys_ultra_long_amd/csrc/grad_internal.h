@@ -156,6 +156,7 @@ struct AttnBwdArgs {
   int B;
   int64_t n_hist, n_tgt;
   int nb;  // 32-key blocks per chunk
+  int max_tgt;  // host bound on any user's targets (the planner zeroes users past it)
   Plan plan;
   int64_t max_chunks;
   const bf16_t *q, *k, *v;

@@ -698,6 +698,7 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       ab.n_hist = R;
       ab.n_tgt = T;
       ab.nb = kBwdChunkBlocks;
+      ab.max_tgt = batch->max_tgt_per_user;
       ab.plan = plan;
       ab.max_chunks = L.max_chunks;
       ab.q = q_all + (size_t)i * T * d;

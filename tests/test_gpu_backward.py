@@ -339,12 +339,15 @@ def test_backward_dedup_matches_oracle(k):
     compare_all(p, g, ref)
 
 
-def test_backward_dedup_rows_spanning_spans():
+@pytest.mark.parametrize("k,over", [(3, dict(L=700)), (4, dict(L_max=1400)),
+                                    (3, dict(L=700, d=512, H=8, hidden=1024))], ids=["d256", "d128", "d512"])
+def test_backward_dedup_rows_spanning_spans(k, over):
     """Unique rows of exactly one 128-item span's length, one item more, two
     spans and one, and several spans (their partial sums folded in span
-    order), scattered over the users, beside rows of one or a few items:
-    against the oracle."""
-    p = I.make_problem(_small(3, L=700))
+    order), scattered over the users, beside rows of one or a few items, at
+    d = 256 (the fused row pass), 128 (half of each lane group idle in the
+    sums) and 512 (two 512-value blocks per row): against the oracle."""
+    p = I.make_problem(_small(k, **over))
     rng = np.random.default_rng(17)
     pos = rng.permutation(p.n_hist)
     hot = [10, 11, 12, 13]
