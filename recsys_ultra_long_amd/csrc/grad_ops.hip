@@ -235,16 +235,17 @@ __global__ __launch_bounds__(kT) void concat_kernel(const float *__restrict__ sr
   dst[r * S * d + sidx * d + f] = src[e];
 }
 
-__global__ __launch_bounds__(kT) void scatter_kernel(const float *__restrict__ rows, const int *__restrict__ ids,
-                                                     int64_t R, int d, float *table, int64_t table_rows,
-                                                     const int *dev_rows) {
+__global__ __launch_bounds__(kT) void scatter_kernel(const float *__restrict__ rows, int64_t lds,
+                                                     const int *__restrict__ ids, int64_t R, int d, float *table,
+                                                     int64_t table_rows, const int *dev_rows) {
   if (dev_rows) R = min(R, (int64_t)*dev_rows);
   const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
   if (e >= R * d) return;
   const int64_t r = e / d;
+  const int f = (int)(e % d);
   const int id = ids[r];
   if (id < 0 || (int64_t)id >= table_rows) return;
-  atomicAdd(table + (int64_t)id * d + (e % d), rows[e]);
+  atomicAdd(table + (int64_t)id * d + f, rows[r * lds + f]);
 }
 
 unsigned blocks(int64_t n) { return (unsigned)((n + kT - 1) / kT); }
@@ -336,10 +337,10 @@ hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float
 }
 
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
-                              hipStream_t s, const int *dev_rows) {
+                              hipStream_t s, const int *dev_rows, int64_t lds) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, ids, R, d, table, table_rows,
-                     dev_rows);
+  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, lds > 0 ? lds : (int64_t)d, ids, R,
+                     d, table, table_rows, dev_rows);
   return hipGetLastError();
 }
 

@@ -57,7 +57,7 @@ struct BwdLayout {
   size_t fws = 0, fws_bytes = 0;
   size_t z = 0, o = 0, attn = 0, q = 0, kv = 0, lse = 0;
   size_t plan = 0;
-  size_t xt = 0, ocat = 0, docat = 0, dxt = 0;
+  size_t xt = 0, ocat = 0, docat = 0;
   size_t c = 0, h13 = 0, g = 0, y = 0, st = 0, qln = 0, dy = 0, dg = 0, dh13 = 0, dc = 0, da = 0, dq = 0, dqt = 0;
   size_t da_lo = 0, dsum = 0, part_dq = 0;
   size_t X = 0, H13 = 0, G = 0, Y = 0, ST = 0, XT = 0, dKV = 0, dXT = 0, dY = 0, dG = 0, dH13 = 0, dX = 0;
@@ -109,8 +109,8 @@ int64_t part_floats_needed(int64_t d, int64_t h, int64_t M, int64_t R, int64_t T
   for (int64_t k = 1; k <= M; ++k) {  // fusion and z maps: [o_1..o_k] blocks of width k d
     need(k * d, d, T, true);
     need(T, d, k * d, false);
-    need(T, k * d, d, false);
   }
+  for (int64_t k = 1; k <= M + 1; ++k) need(T, k * d, d, false);  // d[o_1..o_k-1 | x_t] through W_C, W_Z
   // the query side's FFN and projections over the T target rows
   need(T, h, d, false);
   need(T, d, h, false);
@@ -194,8 +194,7 @@ int make_layout(const stca_config *cfg, const stca_batch *b, BwdLayout &L) {
   L.plan = cv.take(4 * sizeof(int) * (size_t)(cfg->B + 1));
   L.xt = cv.take(T * d * 4);
   L.ocat = cv.take(T * M * d * 4);
-  L.docat = cv.take(T * M * d * 4);
-  L.dxt = cv.take(T * d * 4);
+  L.docat = cv.take(T * (M + 1) * d * 4);  // [do_1 .. do_M | dx_t] rows
   L.c = cv.take(T * d * 4);
   L.h13 = cv.take(T * 2 * h * 4);
   L.g = cv.take(T * h * 4);
@@ -390,7 +389,6 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
   const int *hdev = L.dedup ? fi.n_unique : nullptr;  // device cap on the history backward's rows
 
   float *dX = gr->d_hist ? gr->d_hist : at<float>(ws, L.dX);
-  float *dxt = gr->d_tgt ? gr->d_tgt : at<float>(ws, L.dxt);
   float *gpart = at<float>(ws, L.gemm_part);
   const int64_t gpart_cap = part_floats_needed(d, h, M, 0, T);
   float *lnpart = at<float>(ws, L.ln_part);
@@ -497,6 +495,10 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
 
   const bf16_t *table = (const bf16_t *)batch->table;
   float *xt = at<float>(ws, L.xt), *ocat = at<float>(ws, L.ocat), *docat = at<float>(ws, L.docat);
+  // the upstream gradients of [o_1 .. o_M | x_t] as one [T, (M + 1) d] block,
+  // so that every product through W_Z or W_C writes them in one launch
+  const int64_t LD = (int64_t)(M + 1) * d;
+  float *const dxt = docat + (size_t)M * d;
   float *c = at<float>(ws, L.c), *h13 = at<float>(ws, L.h13), *g = at<float>(ws, L.g), *y = at<float>(ws, L.y);
   float *st = at<float>(ws, L.st), *qln = at<float>(ws, L.qln), *dy = at<float>(ws, L.dy), *dg = at<float>(ws, L.dg);
   float *dh13 = at<float>(ws, L.dh13), *dc = at<float>(ws, L.dc), *da = at<float>(ws, L.da), *dqt = at<float>(ws, L.dqt);
@@ -661,9 +663,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, gr->wz + MD * d, d, 1, 1.f, 1.f, kWgrad)))
       return hip_err("dWz");
     defer_w = false;
-    if ((e = gemm(T, MD, d, dc, false, d, 1, w->wz, true, 1, d, docat, MD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
-    if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)w->wz + MD * d, true, 1, d, dxt, d, 1, 1.f, 0.f, kTgt)))
-      return hip_err("dx_t");
+    // d[o_1 .. o_M | x_t] = dcz W_Z^T
+    if ((e = gemm(T, LD, d, dc, false, d, 1, w->wz, true, 1, d, docat, LD, 1, 1.f, 0.f, kTgt))) return hip_err("do");
     if ((e = flush_w(side->wfork[2 * M], side->wdone[M]))) return hip_err("weight-gradient stream");
   }
   hipEvent_t wpending = side->wdone[M];  // the queued products whose operands the next query side overwrites
@@ -677,9 +678,9 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     const float *a_i = a_all + (size_t)i * T * d;
     float *do_i = docat + (size_t)i * d;
     // W_O: da = do W_O^T, dW_O += a^T do
-    if ((e = gemm(T, d, d, do_i, false, MD, 1, lw.wo, true, 1, d, da, d, 1, 1.f, 0.f, kTgt))) return hip_err("da");
+    if ((e = gemm(T, d, d, do_i, false, LD, 1, lw.wo, true, 1, d, da, d, 1, 1.f, 0.f, kTgt))) return hip_err("da");
     defer_w = true;  // (a and do_i stay as they are: nothing waits for this one)
-    if ((e = gemm(d, d, T, a_i, false, 1, d, do_i, false, MD, 1, lg.wo, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWo");
+    if ((e = gemm(d, d, T, a_i, false, 1, d, do_i, false, LD, 1, lg.wo, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWo");
     defer_w = false;
     if ((e = flush_w(side->wfork[2 * i], nullptr))) return hip_err("weight-gradient stream");
     float *const dq = dq2 + (size_t)(i & 1) * T * d;  // this layer's dQ
@@ -835,11 +836,12 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
       if ((e = gemm(K1, d, T, ocat, false, 1, MD, dc, false, d, 1, lg.wc, d, 1, 1.f, 1.f, kWgrad))) return hip_err("dWc");
       if ((e = gemm(d, d, T, xt, false, 1, d, dc, false, d, 1, lg.wc + K1 * d, d, 1, 1.f, 1.f, kWgrad)))
         return hip_err("dWc");
-      if ((e = gemm(T, K1, d, dc, false, d, 1, lw.wc, true, 1, d, docat, MD, 1, 1.f, 1.f, kTgt))) return hip_err("do");
-      if ((e = gemm(T, d, d, dc, false, d, 1, (const bf16_t *)lw.wc + K1 * d, true, 1, d, dxt, d, 1, 1.f, 1.f, kTgt)))
-        return hip_err("dx_t");
+      // d[o_1 .. o_i-1] += dc W_C[:K1]^T, dx_t += dc W_C[K1:]^T: one product,
+      // its columns past K1 going to the dx_t block
+      if ((e = gemm(T, K1 + d, d, dc, false, d, 1, lw.wc, true, 1, d, docat, LD, 1, 1.f, 1.f, kTgt, dxt, K1)))
+        return hip_err("do | dx_t");
     } else {
-      if ((e = launch_add_rows(dc, d, dxt, d, T, d, true, s))) return hip_err("dx_t");
+      if ((e = launch_add_rows(dc, d, dxt, LD, T, d, true, s))) return hip_err("dx_t");
     }
     defer_w = false;
     if ((e = flush_w(side->wfork[2 * i + 1], side->wdone[i]))) return hip_err("weight-gradient stream");
@@ -854,10 +856,12 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     return hip_err("history stream join");
   if (wforked && ((e = hipEventRecord(side->wdone[M], side->w)) || (e = hipStreamWaitEvent(s, side->wdone[M], 0))))
     return hip_err("weight-gradient stream join");
+  if (gr->d_tgt && (e = launch_add_rows(dxt, LD, gr->d_tgt, d, T, d, false, s))) return hip_err("d_tgt");
   if (gr->table) {
     if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev)))
       return hip_err("scatter");
-    if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s))) return hip_err("scatter");
+    if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s, nullptr, LD)))
+      return hip_err("scatter");
   }
   if ((e = rec(3 + 5 * M))) return hip_err("stage event");
   return STCA_OK;
