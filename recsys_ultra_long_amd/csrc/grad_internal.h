@@ -105,10 +105,11 @@ hipError_t launch_add_rows(const float *src, int64_t lds, float *dst, int64_t ld
                            hipStream_t s);
 // dst[t, s*d + f] = src[s][t][f]: layer-major [S][R][d] -> row-major [R][S*d].
 hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float *dst, hipStream_t s);
-// table[ids[r], :] += rows[r, :] (atomic; rows lds apart, lds = 0: d), ids
-// outside the table skipped.
+// table[ids[r], :] += rows[r, :] (rows lds apart, lds = 0: d; d a multiple
+// of 4, rows and table 16-byte aligned), ids outside the table skipped;
+// atomic unless `unique` (no id repeats among the rows).
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
-                              hipStream_t s, const int *dev_rows = nullptr, int64_t lds = 0);
+                              hipStream_t s, const int *dev_rows = nullptr, int64_t lds = 0, bool unique = false);
 
 // ------------------------------------------------------------ history backward (d = 256)
 // One layer of the history encoder's backward on 128-row tiles in one launch

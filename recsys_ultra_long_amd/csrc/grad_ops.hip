@@ -235,17 +235,36 @@ __global__ __launch_bounds__(kT) void concat_kernel(const float *__restrict__ sr
   dst[r * S * d + sidx * d + f] = src[e];
 }
 
+// Four features per thread, grid-stride over the live rows (the grid is
+// sized for the host bound, capped).
+template <bool UNIQUE>
 __global__ __launch_bounds__(kT) void scatter_kernel(const float *__restrict__ rows, int64_t lds,
                                                      const int *__restrict__ ids, int64_t R, int d, float *table,
                                                      int64_t table_rows, const int *dev_rows) {
   if (dev_rows) R = min(R, (int64_t)*dev_rows);
-  const int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x;
-  if (e >= R * d) return;
-  const int64_t r = e / d;
-  const int f = (int)(e % d);
-  const int id = ids[r];
-  if (id < 0 || (int64_t)id >= table_rows) return;
-  atomicAdd(table + (int64_t)id * d + f, rows[r * lds + f]);
+  const int d4 = d / 4;
+  const int64_t n = R * d4, step = (int64_t)gridDim.x * kT;
+  for (int64_t e = (int64_t)blockIdx.x * kT + threadIdx.x; e < n; e += step) {
+    const int64_t r = e / d4;
+    const int f = (int)(e % d4) * 4;
+    const int id = ids[r];
+    if (id < 0 || (int64_t)id >= table_rows) continue;
+    const float4 v = *reinterpret_cast<const float4 *>(rows + r * lds + f);
+    float *t = table + (int64_t)id * d + f;
+    if (UNIQUE) {  // no other row of this launch touches the table row
+      float4 o = *reinterpret_cast<float4 *>(t);
+      o.x += v.x;
+      o.y += v.y;
+      o.z += v.z;
+      o.w += v.w;
+      *reinterpret_cast<float4 *>(t) = o;
+    } else {
+      atomicAdd(t, v.x);
+      atomicAdd(t + 1, v.y);
+      atomicAdd(t + 2, v.z);
+      atomicAdd(t + 3, v.w);
+    }
+  }
 }
 
 unsigned blocks(int64_t n) { return (unsigned)((n + kT - 1) / kT); }
@@ -337,10 +356,16 @@ hipError_t launch_concat_layers(const float *src, int S, int64_t R, int d, float
 }
 
 hipError_t launch_scatter_add(const float *rows, const int *ids, int64_t R, int d, float *table, int64_t table_rows,
-                              hipStream_t s, const int *dev_rows, int64_t lds) {
+                              hipStream_t s, const int *dev_rows, int64_t lds, bool unique) {
   if (R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3(blocks(R * d)), dim3(kT), 0, s, rows, lds > 0 ? lds : (int64_t)d, ids, R,
-                     d, table, table_rows, dev_rows);
+  if (d % 4) return hipErrorInvalidValue;
+  const unsigned g = std::min(blocks(R * (d / 4)), 4096u);
+  const int64_t ld = lds > 0 ? lds : (int64_t)d;
+  if (unique)
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3(g), dim3(kT), 0, s, rows, ld, ids, R, d, table, table_rows, dev_rows);
+  else
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3(g), dim3(kT), 0, s, rows, ld, ids, R, d, table, table_rows,
+                       dev_rows);
   return hipGetLastError();
 }
 

@@ -858,7 +858,8 @@ int stca_backward(const stca_config *cfg, const stca_batch *batch, const stca_we
     return hip_err("weight-gradient stream join");
   if (gr->d_tgt && (e = launch_add_rows(dxt, LD, gr->d_tgt, d, T, d, false, s))) return hip_err("d_tgt");
   if (gr->table) {
-    if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev)))
+    // (with dedup the history rows are the unique ids: no table row twice)
+    if (R > 0 && (e = launch_scatter_add(dX, hids, Rh, d, gr->table, cfg->table_rows, s, hdev, 0, L.dedup)))
       return hip_err("scatter");
     if ((e = launch_scatter_add(dxt, batch->tgt_ids, T, d, gr->table, cfg->table_rows, s, nullptr, LD)))
       return hip_err("scatter");
