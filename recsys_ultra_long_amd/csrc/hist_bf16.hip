@@ -107,20 +107,59 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
   f32x16 y[4];  // Y^T: features 32w .., tokens 32j + l32
   zero16(y);
   f32x4 acc[2][8];  // G^T of one chunk: W1 and W3 rows of this wave's 16 units x 128 tokens
-  auto g_mma = [&](int hc, const Src &nxt) {
+  // Operands from LDS in groups of four fragments: one group is read while
+  // the other group's products run.  `opa` holds the first group of a phase;
+  // a phase's last block reads the first group of the phase that follows
+  // (code `nf`: 0 = a G phase, 1 + c = the Y phase of chunk c; -1 = none),
+  // so that no phase starts on an LDS round trip.
+  bf16x8 opa[4], opb[4];
+  auto load_first = [&](int nf) {
+    if (nf == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) opa[t] = ld8(xrow + t * 16 * kXRLD);
+    } else if (nf > 0) {
+      const bf16_t *g = sm.gs[(nf - 1) & 1] + l32 * kGLD + hi * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) opa[j] = ld8(g + j * 32 * kGLD);
+    }
+  };
+  // G: row tiles 0..3 (opa) and 4..7 (opb) of each k block
+  auto g_mma = [&](int hc, const Src &nxt, bool have, int nf) {
     zero4(acc[0]);
     zero4(acc[1]);
-    run_phase<kD / 32>(ring, src_g(L, hc, w, lane), nxt, true, [&](int kb, int slot) {
+    constexpr int NK = kD / 32;
+    if constexpr (!PIPE) {  // (the fused kernel: no registers to spare)
+      run_phase<NK>(ring, src_g(L, hc, w, lane), nxt, true, [&](int kb, int slot) {
 #pragma unroll
-      for (int t0 = 0; t0 < 8; t0 += 4) {  // four row tiles at a time
-        bf16x8 bx[4];
+        for (int t0 = 0; t0 < 8; t0 += 4) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bx[t] = ld8(xrow + (t0 + t) * 16 * kXRLD + kb * 32);
+          for (int t = 0; t < 4; ++t) opa[t] = ld8(xrow + (t0 + t) * 16 * kXRLD + kb * 32);
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+          for (int f = 0; f < 2; ++f)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], bx[t], acc[f][t0 + t]);
+            for (int t = 0; t < 4; ++t) acc[f][t0 + t] = mfma16(ring.v[slot][f], opa[t], acc[f][t0 + t]);
+        }
+      });
+      return;
+    }
+    if (!have) load_first(0);
+    run_phase<NK>(ring, src_g(L, hc, w, lane), nxt, true, [&](int kb, int slot) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) opb[t] = ld8(xrow + (4 + t) * 16 * kXRLD + kb * 32);
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[f][t] = mfma16(ring.v[slot][f], opa[t], acc[f][t]);
+      if (kb + 1 < NK) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) opa[t] = ld8(xrow + t * 16 * kXRLD + (kb + 1) * 32);
+      } else {
+        load_first(nf);
       }
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[f][4 + t] = mfma16(ring.v[slot][f], opb[t], acc[f][4 + t]);
     });
   };
   // lane: hidden rows 4 g16 + i of token 16 t + c16
@@ -131,19 +170,38 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
     u32x2 v = {pack_bf2(gv[0], gv[1]), pack_bf2(gv[2], gv[3])};
     *reinterpret_cast<u32x2 *>(g + (t * 16 + c16) * kGLD + w * 16 + 4 * g16) = v;
   };
-  // Y^T += W2^T[features 32w.., chunk hc] G^T[chunk, tokens]; with `gnext`,
-  // also the SiLU epilogue of the chunk in acc (two row tiles per block)
-  auto y_mma = [&](int hc, const Src &nxt, bf16_t *gnext) {
-    const bf16_t *g = sm.gs[hc & 1];
-    run_phase<kHC / 32>(ring, src_y(L, hc, w, lane, nkh), nxt, true, [&](int kb, int slot) {
+  // Y^T += W2^T[features 32w.., chunk hc] G^T[chunk, tokens]: the two k
+  // halves of each block (opa, opb); with `gnext`, also the SiLU epilogue of
+  // the chunk in acc (two row tiles per block)
+  auto y_mma = [&](int hc, const Src &nxt, bf16_t *gnext, bool have, int nf) {
+    constexpr int NK = kHC / 32;
+    const bf16_t *g = sm.gs[hc & 1] + l32 * kGLD + hi * 16;
+    if constexpr (!PIPE) {
+      run_phase<NK>(ring, src_y(L, hc, w, lane, nkh), nxt, true, [&](int kb, int slot) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 bg[4];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bg[j] = ld8(g + (j * 32 + l32) * kGLD + kb * 32 + hi * 16 + h * 8);
+          for (int j = 0; j < 4; ++j) opa[j] = ld8(g + j * 32 * kGLD + kb * 32 + h * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], bg[j], y[j]);
+          for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][h], opa[j], y[j]);
+        }
+      });
+      return;
+    }
+    if (!have) load_first(1 + hc);
+    run_phase<NK>(ring, src_y(L, hc, w, lane, nkh), nxt, true, [&](int kb, int slot) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) opb[j] = ld8(g + j * 32 * kGLD + kb * 32 + 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][0], opa[j], y[j]);
+      if (kb + 1 < NK) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) opa[j] = ld8(g + j * 32 * kGLD + (kb + 1) * 32);
+      } else {
+        load_first(nf);
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = mfma32(ring.v[slot][1], opb[j], y[j]);
       if (gnext) {
         silu_store(gnext, 2 * kb);
         silu_store(gnext, 2 * kb + 1);
@@ -152,25 +210,28 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
   };
   static_assert(kHC / 32 * 2 == 8, "two row tiles of the SiLU epilogue per Y block");
   if (PIPE) {
-    g_mma(0, nchunk > 1 ? src_g(L, 1, w, lane) : src_y(L, 0, w, lane, nkh));
+    // G(hc) reads the first group of Y(hc - 1) (written before the last
+    // barrier); Y(hc - 1) that of G(hc + 1) (the raw rows never change).
+    g_mma(0, nchunk > 1 ? src_g(L, 1, w, lane) : src_y(L, 0, w, lane, nkh), false, nchunk > 1 ? 0 : -1);
 #pragma unroll
     for (int t = 0; t < 8; ++t) silu_store(sm.gs[0], t);
     __syncthreads();
 #pragma unroll 1
     for (int hc = 1; hc < nchunk; ++hc) {
-      g_mma(hc, src_y(L, hc - 1, w, lane, nkh));
-      y_mma(hc - 1, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : src_y(L, hc, w, lane, nkh), sm.gs[hc & 1]);
+      g_mma(hc, src_y(L, hc - 1, w, lane, nkh), true, hc);
+      y_mma(hc - 1, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : src_y(L, hc, w, lane, nkh), sm.gs[hc & 1], true,
+            hc + 1 < nchunk ? 0 : -1);
       __syncthreads();
     }
-    y_mma(nchunk - 1, after, nullptr);
+    y_mma(nchunk - 1, after, nullptr, false, -1);
   } else {
 #pragma unroll 1
     for (int hc = 0; hc < nchunk; ++hc) {
-      g_mma(hc, src_y(L, hc, w, lane, nkh));
+      g_mma(hc, src_y(L, hc, w, lane, nkh), false, -1);
 #pragma unroll
       for (int t = 0; t < 8; ++t) silu_store(sm.gs[hc & 1], t);
       __syncthreads();
-      y_mma(hc, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : after, nullptr);
+      y_mma(hc, hc + 1 < nchunk ? src_g(L, hc + 1, w, lane) : after, nullptr, false, -1);
     }
   }
 
@@ -323,22 +384,30 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
         const Layer Ln = layer(li + 1);
         nxt = src_g(Ln, 0, w, lane);
       }
+      // X~ operands of k block kb + 1 are read while block kb's V products
+      // run (each half once its V products are issued).
+      const bf16_t *xo = xt + l32 * kXLD + hi * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bx[h][j] = ld8(xo + j * 32 * kXLD + h * 8);
       run_phase<2 * kD / 32>(ring, src_kv(L, w, lane), nxt, more, [&](int b, int slot) {
         const int kb = b >> 1;
         if ((b & 1) == 0) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bx[h][j] = ld8(xt + (j * 32 + l32) * kXLD + kb * 32 + hi * 16 + h * 8);
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
             for (int j = 0; j < 4; ++j) ka[j] = mfma32(ring.v[slot][h], bx[h][j], ka[j]);
         } else {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+          for (int h = 0; h < 2; ++h) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) va[j] = mfma32(bx[h][j], ring.v[slot][h], va[j]);
+            if (kb + 1 < kD / 32) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) bx[h][j] = ld8(xo + j * 32 * kXLD + (kb + 1) * 32 + h * 8);
+            }
+          }
         }
       });
 #pragma unroll
