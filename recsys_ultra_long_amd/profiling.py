@@ -4,11 +4,15 @@
     python -m recsys_ultra_long_amd.profiling traffic  <fetch.csv> <write.csv> \
         <copy_fetch.csv> <copy_write.csv> <copy_bytes> <out.md> <command...>
     python -m recsys_ultra_long_amd.profiling mfma  <counters.csv> <kernel_trace.csv> <out.md> <command...>
+    python -m recsys_ultra_long_amd.profiling sq  <kernel-substring> <out.md> <counters.csv>... -- <command...>
 
 ``kernels`` condenses a ``--kernel-trace --stats`` run (per-kernel calls and
 average duration).  ``mfma`` turns a ``--pmc MfmaUtil MfmaFlopsBF16
 --kernel-trace`` run into per-kernel MFMA busy percentage and bf16 MFMA
-TFLOP/s (counted operations over the dispatch's own duration).  ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
+TFLOP/s (counted operations over the dispatch's own duration).  ``sq`` lists
+the mean per-dispatch value of every counter in one or more ``--pmc`` runs
+(each within the hardware's per-pass limits) for the kernels whose name
+contains the given substring.  ``traffic`` turns two ``--pmc`` runs (FETCH_SIZE, then
 WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of the profiled
 kernels, each scaled by what the same counter reads for a plain device copy
 of known size (``bench.py --copy-calibration``).  The traffic summary carries
@@ -143,6 +147,40 @@ def read_traffic(path: str):
     return data if data.get("source_hash") == source_hash() else None
 
 
+def write_sq(kernel: str, out: str, csvs, command: str):
+    vals = collections.defaultdict(list)
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if kernel in k:
+                vals[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    lines = ["# SQ counters per dispatch", "", f"Command: `{command}`", "",
+             "Values are means over the profiled dispatches of the counter summed over the device.", "",
+             "| kernel | counter | value |", "|---|---|---|"]
+    means = {kc: sum(v) / len(v) for kc, v in vals.items()}
+    for (k, c), v in sorted(means.items()):
+        lines.append(f"| `{k}` | {c} | {v:.4g} |")
+    lines += ["", "Derived (per kernel):"] + sq_ratios(means)
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+SQ_RATIOS = [
+    ("waves waiting on a memory counter (s_waitcnt: weight-ring loads, LDS reads)", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+    ("waves ready but not issued (the SIMD's other wave holds the MFMA pipe, dependencies)",
+     "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("LDS bank conflicts per active LDS cycle", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+]
+
+
+def sq_ratios(means):
+    out = []
+    for k in sorted({k for k, _ in means}):
+        for text, a, b in SQ_RATIOS:
+            if (k, a) in means and means.get((k, b)):
+                out.append(f"- `{k}`: {text}: {a} / {b} = {means[(k, a)] / means[(k, b)]:.3f}")
+    return out
+
+
 if __name__ == "__main__":
     cmd = sys.argv[1]
     if cmd == "kernels":
@@ -151,6 +189,9 @@ if __name__ == "__main__":
         write_traffic(*sys.argv[2:8], " ".join(sys.argv[8:]))
     elif cmd == "mfma":
         write_mfma(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+    elif cmd == "sq":
+        i = sys.argv.index("--")
+        write_sq(sys.argv[2], sys.argv[3], sys.argv[4:i], " ".join(sys.argv[i + 1:]))
     elif cmd == "hash":
         print(source_hash())
     else:
