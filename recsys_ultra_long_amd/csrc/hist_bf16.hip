@@ -310,15 +310,30 @@ DEV void ffn_ln(Ring &ring, const Layer &L, Smem &sm, bf16_t *xt, int w, int lan
 
 }
 
-template <bool LN>
+template <bool LN, bool PERSIST>
 __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers hl) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;     // 32x32 operand / output roles
   const int c16 = lane & 15, g16 = lane >> 4;    // 16x16 roles
-  const int64_t row0 = (int64_t)blockIdx.x * kR;
   const int total_blocks = a.plan.pblk[a.B];
-  if (row0 >= (int64_t)total_blocks * 32) return;
+  const int tiles = (total_blocks + 3) / 4;
+  // Work units.  One workgroup per tile with all of its layers; or, PERSIST
+  // (a grid of about one workgroup per CU, sized from an upper bound of the
+  // rows: the unique rows of a batch are counted on the device), workgroups
+  // looping over the units, a unit being one tile with all of its layers or,
+  // when that would leave the last round of workgroups mostly idle, one
+  // (tile, layer) pair.  Every row's arithmetic is the same in all three forms.
+  int units = tiles, stride = tiles;
+  bool split = false;
+  if (PERSIST) {
+    const int G = (int)gridDim.x;
+    const int64_t r_all = (int64_t)((tiles + G - 1) / G) * hl.M, r_split = ((int64_t)tiles * hl.M + G - 1) / G;
+    split = r_split < r_all;
+    units = split ? tiles * hl.M : tiles;
+    stride = G;
+  }
+  if ((int)blockIdx.x >= units) return;
   const int nkh = a.hidden / 32, nchunk = a.hidden / kHC;
   const int H = a.H, DH = kD / a.H;
   // optional clock probe: shader-clock and 100 MHz counters at start and end
@@ -342,9 +357,11 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     return L;
   };
 
+  bf16_t *const xt = &sm.gs[0][0];  // LN output, row stride kXLD
+  auto unit = [&](const int64_t row0, const int l0, const int l1) {
   Ring ring;
   {
-    const Layer L0 = layer(0);
+    const Layer L0 = layer(l0);
     const Src s0 = src_g(L0, 0, w, lane);
 #pragma unroll
     for (int kb = 0; kb < 3; ++kb) ring_load(ring, kb, s0, kb);
@@ -352,9 +369,8 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
 
   gather_tile(a, sm, row0, total_blocks, tid, true);
 
-  bf16_t *const xt = &sm.gs[0][0];  // LN output, row stride kXLD
 #pragma unroll 1
-  for (int li = 0; li < hl.M; ++li) {
+  for (int li = l0; li < l1; ++li) {
     // lane quantities re-derived per layer so none is held across layers
     int ltid = tid;
     asm volatile("" : "+v"(ltid));
@@ -364,7 +380,7 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
     Layer L = layer(li);
     // the weight addresses stay loop-variant (no hoisting across layers)
     asm volatile("" : "+s"(L.w1), "+s"(L.w3), "+s"(L.w2), "+s"(L.wp), "+s"(L.ln_g), "+s"(L.ln_b));
-    if (li > 0) __syncthreads();  // the previous layer's projection is done with X~
+    if (li > l0) __syncthreads();  // the previous layer's projection is done with X~
 
     ffn_ln<LN, true>(ring, L, sm, xt, w, lane, nkh, nchunk, src_kv(L, w, lane));
 
@@ -378,7 +394,7 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
       zero16(ka);
       zero16(va);
       bf16x8 bx[2][4];
-      const bool more = li + 1 < hl.M;
+      const bool more = li + 1 < l1;
       Src nxt = src_kv(L, w, lane);  // any valid address when nothing follows
       if (more) {
         const Layer Ln = layer(li + 1);
@@ -434,6 +450,17 @@ __global__ __launch_bounds__(kT, 1) void hist256_kernel(ChainArgs a, HistLayers 
         stnt16(dst, o0);
         stnt16(dst + 8, o1);
       }
+    }
+  }
+  };
+  if (!PERSIST) {
+    unit((int64_t)blockIdx.x * kR, 0, hl.M);
+  } else {
+#pragma unroll 1
+    for (int u = (int)blockIdx.x; u < units; u += stride) {
+      if (u != (int)blockIdx.x) __syncthreads();  // the previous unit is done with the LDS
+      const int l0 = split ? u / tiles : 0;
+      unit((int64_t)(split ? u % tiles : u) * kR, l0, split ? l0 + 1 : hl.M);
     }
   }
   if (hl.clock && blockIdx.x < 8 && tid == 0) {
@@ -691,9 +718,22 @@ hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t 
   if (a.n_rows <= 0 || hl.M <= 0) return hipSuccess;
   if (a.d != kD || hl.M > kMaxLayers || a.hidden % kHC || a.in_mode != IN_GATHER_CSR)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((a.n_rows + kR - 1) / kR)), block(kT);
-  if (a.ln) hipLaunchKernelGGL(hist256_kernel<true>, grid, block, 0, s, a, hl);
-  else hipLaunchKernelGGL(hist256_kernel<false>, grid, block, 0, s, a, hl);
+  int64_t nwg = (a.n_rows + kR - 1) / kR;
+  if (hl.persistent) {  // one workgroup per CU (the LDS allows no more)
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    nwg = std::min<int64_t>(nwg, std::max(cus, 1));
+  }
+  const dim3 grid((unsigned)nwg), block(kT);
+  if (hl.persistent) {
+    if (a.ln) hipLaunchKernelGGL((hist256_kernel<true, true>), grid, block, 0, s, a, hl);
+    else hipLaunchKernelGGL((hist256_kernel<false, true>), grid, block, 0, s, a, hl);
+  } else {
+    if (a.ln) hipLaunchKernelGGL((hist256_kernel<true, false>), grid, block, 0, s, a, hl);
+    else hipLaunchKernelGGL((hist256_kernel<false, false>), grid, block, 0, s, a, hl);
+  }
   return hipGetLastError();
 }
 

@@ -901,6 +901,7 @@ int forward_body(const stca_config *cfg, const stca_batch *batch, const stca_wei
     std::memset(&hl, 0, sizeof(hl));
     hl.M = M;
     hl.clock = reinterpret_cast<unsigned long long *>(out->clock_probe);
+    hl.persistent = L.dedup ? 1 : 0;  // the unique rows are counted on the device
     for (int i = 0; i < M; ++i) {
       const PrepLayer &p = L.pl[i];
       hl.w1[i] = prep + p.kv_w1;

@@ -112,6 +112,7 @@ struct HistLayers {
   void *kbuf[kMaxLayers], *vbuf[kMaxLayers];
   int M;
   unsigned long long *clock;  // optional [8][4]: start / end clock counters of workgroups 0..7
+  int persistent;             // d = 256: about one workgroup per CU looping over the tiles (n_rows an upper bound)
 };
 // d = 256: 128-row tiles on 8 waves (W1, W3 packed with fmt 1).
 hipError_t launch_hist256(const ChainArgs &a, const HistLayers &hl, hipStream_t s);
