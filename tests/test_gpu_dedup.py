@@ -99,3 +99,14 @@ def test_dedup_fullsize_rlb_long():
     p = I.make_problem(I.spec(3), threads=16)
     users = sorted({int(u) for u in np.linspace(0, p.spec.B - 1, 8).round()})
     _same(p, dumps=(), oracle_users=users)
+
+
+def test_dedup_persistent_whole_tiles():
+    """Nearly every id distinct: 385-512 tiles of unique rows at two layers.
+    On 256 CUs the persistent encoder then keeps whole tiles (splitting into
+    (tile, layer) units would save no round) and most workgroups run two of
+    them, the second after re-gathering its rows."""
+    p = I.make_problem(I.spec(2, B=32, L=2048, ids="uniform"), threads=16)
+    tiles = -(-len(np.unique(p.hist_ids)) // 128)
+    assert 384 < tiles <= 512, tiles
+    _same(p, dumps=(), oracle_users=[0, 31])
